@@ -1,0 +1,115 @@
+"""fp64 CPU oracle of the multi-layer, optionally bidirectional LSTM forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product (``layer_lstm_forward_amd``)
+never imports this package, and this package imports nothing from it.
+
+The arithmetic lives in ``lstm_oracle.c`` (plain loops, fp64, built with
+``-O2`` and without fast-math); this module only builds it, converts inputs to
+float64 exactly and calls it.  Which passage of the source pages each step
+follows is stated at the top of the C file.
+
+Inputs may be float32/float64 arrays, or bfloat16 bit patterns held in uint16
+arrays (``bf16=True``); both convert to float64 without rounding.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "lstm_oracle.c")
+_LIB = os.path.join(_DIR, "liblstm_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP) into a .so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # LSTM_ORACLE_LIB lets the mutation test point the pins at a copy of
+        # the oracle built with a planted mistake.
+        path = os.environ.get("LSTM_ORACLE_LIB") or build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_lstm_forward.restype = ctypes.c_int
+        lib.oracle_lstm_forward.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp, ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def as_f64(a, bf16: bool = False) -> np.ndarray:
+    """Exact conversion to float64 (bf16 bit patterns widen by a 16-bit shift)."""
+    a = np.asarray(a)
+    if bf16:
+        assert a.dtype == np.uint16, "bf16 inputs are passed as uint16 bit patterns"
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bool,
+                 h0=None, c0=None, has_bias: bool = True, bf16: bool = False,
+                 c_state_bf16: bool = False, nthreads: int = 1):
+    """Run the oracle.
+
+    x       [T, B, I]
+    params  flat list in (layer, direction, W_ih, W_hh[, b_ih, b_hh]) order
+    h0, c0  [L*D, B, H] or None (zeros); c0 is never bf16 unless c_state_bf16
+    Returns (y [T, B, D*H], h_n [L*D, B, H], c_n [L*D, B, H]) as float64.
+    """
+    lib = _load()
+    x64 = np.ascontiguousarray(as_f64(x, bf16))
+    T, B, I = x64.shape
+    H, L, D = int(hidden_size), int(num_layers), 2 if bidirectional else 1
+    per = 4 if has_bias else 2
+    if len(params) != L * D * per:
+        raise ValueError(f"expected {L * D * per} parameter arrays, got {len(params)}")
+    p64 = [np.ascontiguousarray(as_f64(p, bf16)) for p in params]
+    for idx, p in enumerate(p64):
+        l, rem = divmod(idx, D * per)
+        kind = rem % per
+        in_l = I if l == 0 else D * H
+        want = [(4 * H, in_l), (4 * H, H), (4 * H,), (4 * H,)][kind]
+        if p.shape != want:
+            raise ValueError(f"param {idx} has shape {p.shape}, expected {want}")
+    arr = (ctypes.POINTER(ctypes.c_double) * len(p64))(*[_ptr(p) for p in p64])
+    h064 = None if h0 is None else np.ascontiguousarray(as_f64(h0, bf16))
+    c064 = None if c0 is None else np.ascontiguousarray(as_f64(c0, c_state_bf16))
+    for s in (h064, c064):
+        if s is not None and s.shape != (L * D, B, H):
+            raise ValueError(f"state shape {s.shape} != {(L * D, B, H)}")
+    y = np.empty((T, B, D * H), np.float64)
+    hn = np.empty((L * D, B, H), np.float64)
+    cn = np.empty((L * D, B, H), np.float64)
+    rc = lib.oracle_lstm_forward(
+        T, B, I, H, L, D, _ptr(x64),
+        _ptr(h064) if h064 is not None else None,
+        _ptr(c064) if c064 is not None else None,
+        arr, 1 if has_bias else 0, _ptr(y), _ptr(hn), _ptr(cn), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_lstm_forward failed with {rc}")
+    return y, hn, cn

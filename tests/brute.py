@@ -1,0 +1,78 @@
+"""Per-gate scalar LSTM evaluator for tiny shapes (test helper, pure Python).
+
+An independent formulation of the cell used to pin the oracle: it keeps the
+eight weight matrices W_ii..W_ho and the eight bias vectors b_ii..b_ho as
+separate objects, exactly the symbols of the equation block on the warp-nn
+"Long Short-Term Memory (LSTM)" page (the per-gate buffers of the pulsatrix
+"LSTMModule" class reference are the same idea), and evaluates every scalar
+with Python floats and math.exp / math.tanh.  The stacked row-block layout is
+unpacked here by the page's parameter table: W_ii..W_io are the four H-row
+blocks of weight_ih, in that order, and likewise for weight_hh and the biases.
+"""
+import math
+
+GATES = ("i", "f", "g", "o")
+
+
+def unpack(W_ih, W_hh, b_ih, b_hh, H):
+    """Split stacked parameters into per-gate nested lists (no numpy)."""
+    g = {}
+    for q, name in enumerate(GATES):
+        rows = range(q * H, (q + 1) * H)
+        g["W_i" + name] = [[float(W_ih[r][k]) for k in range(len(W_ih[r]))] for r in rows]
+        g["W_h" + name] = [[float(W_hh[r][k]) for k in range(len(W_hh[r]))] for r in rows]
+        g["b_i" + name] = [float(b_ih[r]) if b_ih is not None else 0.0 for r in rows]
+        g["b_h" + name] = [float(b_hh[r]) if b_hh is not None else 0.0 for r in rows]
+    return g
+
+
+def _sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def _affine(W, v, b):
+    return [sum(W[j][k] * v[k] for k in range(len(v))) + b[j] for j in range(len(W))]
+
+
+def cell(g, x, h, c):
+    """One step of one direction: returns (h_t, c_t) as lists."""
+    a = {n: [u + w for u, w in zip(_affine(g["W_i" + n], x, g["b_i" + n]),
+                                   _affine(g["W_h" + n], h, g["b_h" + n]))]
+         for n in GATES}
+    i = [_sig(z) for z in a["i"]]
+    f = [_sig(z) for z in a["f"]]
+    gg = [math.tanh(z) for z in a["g"]]
+    o = [_sig(z) for z in a["o"]]
+    c_new = [f[j] * c[j] + i[j] * gg[j] for j in range(len(c))]
+    h_new = [o[j] * math.tanh(c_new[j]) for j in range(len(c))]
+    return h_new, c_new
+
+
+def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True):
+    """x: nested [T][B][I]; params flat in (layer, direction, W_ih, W_hh[, b_ih, b_hh]).
+
+    Returns y [T][B][D*H], h_n and c_n [L*D][B][H] as nested lists.
+    """
+    T, B = len(x), len(x[0])
+    per = 4 if has_bias else 2
+    seq = [[list(map(float, x[t][b])) for b in range(B)] for t in range(T)]
+    hn, cn = [], []
+    for l in range(L):
+        out = [[[0.0] * (D * H) for _ in range(B)] for _ in range(T)]
+        for d in range(D):
+            p = params[(l * D + d) * per:(l * D + d + 1) * per]
+            g = unpack(p[0], p[1], p[2] if has_bias else None, p[3] if has_bias else None, H)
+            hl, cl = [], []
+            for b in range(B):
+                h = [float(v) for v in h0[l * D + d][b]] if h0 is not None else [0.0] * H
+                c = [float(v) for v in c0[l * D + d][b]] if c0 is not None else [0.0] * H
+                order = range(T) if d == 0 else range(T - 1, -1, -1)
+                for t in order:
+                    h, c = cell(g, seq[t][b], h, c)
+                    out[t][b][d * H:(d + 1) * H] = h
+                hl.append(h)
+                cl.append(c)
+            hn.append(hl)
+            cn.append(cl)
+        seq = out
+    return seq, hn, cn

@@ -1,0 +1,42 @@
+"""The pins have power: each plausible mistake planted in a copy of the oracle
+(on the CPU, never on a GPU) makes the pin suite fail."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "lstm_oracle.c")
+
+MUTATIONS = {
+    "drop_b_hh": ("acc = b_ih[r] + b_hh[r];", "acc = b_ih[r];"),
+    "swap_i_f": ("const double ig = sigmoid(pb[j]);\n                        const double fg = sigmoid(pb[H + j]);",
+                 "const double ig = sigmoid(pb[H + j]);\n                        const double fg = sigmoid(pb[j]);"),
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
+    "transposed_W_hh": ("acc += wh[k] * hb[k];", "acc += W_hh[(size_t)k * G + r] * hb[k];"),
+    "reverse_at_step_index": ("Y[((size_t)t * B + b)", "Y[((size_t)s * B + b)"),
+    "h0_of_layer0_only": ("h[e] = h0 ? h0[st + e] : 0.0;", "h[e] = h0 ? h0[e] : 0.0;"),
+    "cell_uses_o": ("const double cn = fg * c[e] + ig * gg;", "const double cn = fg * c[e] + ig * og;"),
+    "h_without_o": ("const double hn = og * tanh(cn);", "const double hn = tanh(cn);"),
+    "o_gate_tanh": ("const double og = sigmoid(pb[3 * H + j]);", "const double og = tanh(pb[3 * H + j]);"),
+    "transposed_W_ih": ("acc += wi[k] * xt[k];", "acc += W_ih[(size_t)k * G + r] * xt[k];"),
+    "next_layer_reads_h_not_y": ("in_seq = Xl;", "in_seq = Yl;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut = tmp_path / "lstm_oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liblstm_oracle_mut.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib),
+                           str(mut), "-lm"])
+    env = dict(os.environ, LSTM_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
