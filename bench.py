@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X LSTM forward in timestep-cells/s (B*T*H*L*D per second).
+
+One "step" is one full forward pass (every layer: input projection GEMM and the
+recurrence) over one batch of synthetic, seeded input already resident in HBM.
+Default workload: 2 layers, unidirectional, input 256, hidden 512, T 128,
+batch 64, fp32 -- the running example of the "Complete Trace: nn.LSTM" page
+at a 64-sequence batch.
+
+Prints one JSON line.  Besides throughput it reports
+  roofline      the dominant kernel (the one with the larger share of device
+                time) against its bound, timed live with HIP events recorded on
+                the launch stream inside lstm_forward;
+  cpu_baseline  the fp64 oracle on the host cores over a bounded sample of
+                batch rows of the same workload (rows are independent).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSTM fwd timestep-cells/sec (B·T·H·L·D) at 1 GPU; % of MFMA / LDS-BW roofline"
+DEFAULT = "l2_in256_h512_t128_b64_f32"
+# Published dense peaks of one MI355X.
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def rec_flops_per_launch(spec):
+    """Algorithmic FLOPs of one layer's recurrence: 2*B*T*D*4H*H."""
+    H = spec.hidden_size
+    return 2.0 * spec.B * spec.T * spec.D * 4 * H * H
+
+
+def proj_flops_per_launch(spec):
+    """Average over layers of 2*T*B*D*4H*in_l (one GEMM launch per layer)."""
+    H = spec.hidden_size
+    tot = sum(2.0 * spec.T * spec.B * spec.D * 4 * H * spec.layer_input(l) for l in range(spec.num_layers))
+    return tot / spec.num_layers
+
+
+def cpu_baseline(inp, budget_s):
+    import numpy as np
+    import oracle
+    spec = inp.spec
+    threads = max(1, os.cpu_count() or 1)
+    per_row_flops = spec.flops() / spec.B
+    # calibrate on one row, then size the sample to the time budget
+    rows = [0]
+    t0 = time.perf_counter()
+    sub = inp.rows(rows)
+    oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
+                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads)
+    one = time.perf_counter() - t0
+    n = int(max(1, min(spec.B, budget_s / max(one, 1e-6))))
+    rows = list(np.linspace(0, spec.B - 1, n).astype(int)) if n > 1 else [0]
+    rows = sorted(set(int(r) for r in rows))
+    sub = inp.rows(rows)
+    t0 = time.perf_counter()
+    oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
+                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads)
+    wall = time.perf_counter() - t0
+    cells = len(rows) * spec.T * spec.hidden_size * spec.num_layers * spec.D
+    return {"value": cells / wall, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {spec.B} batch rows, full T={spec.T}, all {spec.num_layers} layers, "
+                      f"fp64, {wall:.1f} s wall ({per_row_flops * len(rows) / wall / 1e9:.2f} GFLOP/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT)
+    ap.add_argument("--recurrence", choices=["auto", "step", "persistent"], default="auto")
+    ap.add_argument("--rec-tile", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the forward pass has no cross-GPU "
+              "component here); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import layer_lstm_forward_amd as pkg
+    from layer_lstm_forward_amd.synth import WORKLOADS, make_inputs
+
+    spec = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {args.workload}: generating inputs")
+    inp = make_inputs(spec)
+    bf = spec.dtype == "bf16"
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if bf and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x = to_dev(inp.x)
+    w = [to_dev(p) for p in inp.params]
+    h0 = to_dev(inp.h0)
+    c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
+    rec = {"auto": pkg.LSTM_REC_AUTO, "step": pkg.LSTM_REC_STEP, "persistent": pkg.LSTM_REC_PERSISTENT}
+    m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
+                 dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile)
+    desc = m.describe(spec.T, spec.B)
+    log(f"schedule: {desc}")
+    out = (torch.empty(spec.T, spec.B, spec.D * spec.hidden_size, dtype=x.dtype, device=dev),
+           torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=x.dtype, device=dev),
+           torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        m.forward(x, w, h0, c0, out=out)
+    torch.cuda.synchronize()
+    rc, flags = m.device_status()
+    if rc != 0:
+        log(f"device status after warmup: {rc} flags {flags}")
+        sys.exit(1)
+    log(f"warmup done ({args.warmup} steps)")
+
+    pkg.lstm_set_option(m.plan, pkg.LSTM_OPT_TIMING, 1)
+    pkg.lstm_read_timing(m.plan, reset=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        m.forward(x, w, h0, c0, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    tm = pkg.lstm_read_timing(m.plan, reset=True)
+    rc, flags = m.device_status()
+    if rc != 0:
+        log(f"device status after timed steps: {rc} flags {flags}")
+        sys.exit(1)
+    ms = total_ms / args.steps
+    value = spec.cells * args.steps / (total_ms / 1e3)
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value / 1e9:.3f} G cells/s; phases {tm}")
+
+    proj_avg = tm["proj_ms"] / max(1, tm["proj_launches"])
+    rec_avg = tm["rec_ms"] / max(1, tm["rec_launches"])
+    if tm["rec_ms"] >= tm["proj_ms"]:
+        kname, flops, avg = "k_rec", rec_flops_per_launch(spec), rec_avg
+        if tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
+            flops /= spec.T
+    else:
+        kname, flops, avg = "k_proj", proj_flops_per_launch(spec), proj_avg
+    achieved = flops / (avg / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[spec.dtype], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS[spec.dtype], 4), "traffic": None, "kernel": kname,
+            "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
+            "phase_ms_per_step": {"proj": round(tm["proj_ms"] / max(1, tm["calls"]), 4),
+                                  "rec": round(tm["rec_ms"] / max(1, tm["calls"]), 4)}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on a row sample")
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+
+    line = {"metric": METRIC, "value": value, "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded; random-init weights)",
+            "config": {"workload": args.workload, "input_size": spec.input_size, "hidden_size": spec.hidden_size,
+                       "num_layers": spec.num_layers, "bidirectional": spec.bidirectional, "T": spec.T,
+                       "B": spec.B, "cells_per_step": spec.cells, "schedule": desc},
+            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

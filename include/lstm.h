@@ -1,0 +1,160 @@
+/*
+ * lstm.h -- C ABI of the MI355X (gfx950) LSTM forward library liblstm_amd.so.
+ *
+ * The operation: a multi-layer, optionally bidirectional LSTM forward pass.
+ * Per layer, direction and time step (warp-nn "Long Short-Term Memory (LSTM)",
+ * the equation block under the class signature):
+ *     i = sigma(W_ii x + b_ii + W_hi h + b_hi)   f = sigma(... f rows ...)
+ *     g = tanh (W_ig x + b_ig + W_hg h + b_hg)   o = sigma(... o rows ...)
+ *     c' = f*c + i*g                             h' = o*tanh(c')
+ * Layer k > 0 reads the D*H-wide output of layer k-1 (same page, the symbol
+ * list); the reverse direction scans from the last element to the first with
+ * its own parameters and its hidden states are concatenated after the
+ * forward ones (same page, the paragraph on bidirectional).  Inputs, outputs
+ * and return values follow the op signature traced on "Complete Trace:
+ * nn.LSTM" (Step 3, lstm.input -> (output, h_n, c_n)) and warp-nn __call__.
+ *
+ * Conventions
+ *   - All tensors are dense, row-major and time-major ([T, B, .]); batch-first
+ *     callers transpose before the call.
+ *   - dtype LSTM_F32: x, weights, biases, h0, y, h_n are float32.
+ *     dtype LSTM_BF16: the same tensors are bfloat16; arithmetic accumulates in
+ *     float32, the cell state c0 / c_n stays float32 in both modes, and the
+ *     hidden state is rounded to bfloat16 (nearest-even) where it is stored.
+ *   - Every tensor pointer is device memory on the current HIP device, owned
+ *     by the caller.  The library allocates no device memory; all scratch
+ *     lives in the caller's workspace.
+ *   - Weight pointer order (warp-nn "Learnable parameters" table, flattened
+ *     layer by layer as "Complete Trace: nn.LSTM" Step 1 flattens them):
+ *         for l in 0..L-1, for d in 0..D-1 (forward, then reverse):
+ *             W_ih [4H, in_l]   in_0 = input_size, in_l = D*H for l > 0
+ *             W_hh [4H, H]
+ *             b_ih [4H]         only when has_bias
+ *             b_hh [4H]         only when has_bias
+ *     with the 4H rows in gate blocks [i; f; g; o] of H rows each.  Both
+ *     biases are added.  Reading weights the caller has not written is the
+ *     caller's undefined behaviour, as on the warp-nn page
+ *     (initialize_parameters=False).
+ *   - State index order of h0, c0, h_n, c_n [L*D, B, H]: l*D + d.  The
+ *     reverse direction's final state is the one after consuming t = 0.
+ *
+ * Errors: every call returns an lstm_status.  Argument checks run on the host
+ * before anything is enqueued; a failed check writes nothing.  Kernel-side
+ * failures are asynchronous and are read back with lstm_device_status.
+ * Nothing is printed and no C++ exception crosses this interface.
+ */
+#ifndef LSTM_AMD_LSTM_H
+#define LSTM_AMD_LSTM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lstm_plan lstm_plan; /* opaque, immutable shape description */
+
+typedef enum { LSTM_F32 = 0, LSTM_BF16 = 1 } lstm_dtype;
+
+typedef enum {
+    LSTM_OK = 0,
+    LSTM_ERR_ARG = -1,         /* NULL/negative argument, num_layers < 1, h0 without c0 */
+    LSTM_ERR_SHAPE = -2,       /* T < 1, B < 1, layers/bidir differ from the plan, size overflow */
+    LSTM_ERR_DTYPE = -3,       /* unknown dtype */
+    LSTM_ERR_DEVICE = -4,      /* a pointer is not device memory of the current device, or no device */
+    LSTM_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than lstm_workspace_size */
+    LSTM_ERR_LAUNCH = -6,      /* a kernel launch was refused by the runtime */
+    LSTM_ERR_UNSUPPORTED = -7, /* option value not supported */
+    LSTM_ERR_DEVICE_TIMEOUT = -8 /* lstm_device_status: a step barrier gave up waiting */
+} lstm_status;
+
+/* Recurrent-phase execution modes (lstm_set_option LSTM_OPT_RECURRENCE). */
+typedef enum {
+    LSTM_REC_AUTO = 0,       /* persistent when the plan's W_hh slices fit on chip, else per step */
+    LSTM_REC_STEP = 1,       /* one launch per time step (no cross-workgroup waits) */
+    LSTM_REC_PERSISTENT = 2  /* one cooperative launch per layer; LSTM_ERR_UNSUPPORTED if it does not fit */
+} lstm_recurrence;
+
+typedef enum {
+    LSTM_OPT_RECURRENCE = 1, /* value: lstm_recurrence */
+    LSTM_OPT_REC_TILE = 2,   /* value: 0 = automatic, else 100*WK + 10*MTW + NT (see lstm_describe) */
+    LSTM_OPT_TIMING = 3      /* value 1: record HIP events around each phase (see lstm_read_timing) */
+} lstm_option;
+
+/* Accumulated per-phase device time of the calls made since the last reset
+ * (LSTM_OPT_TIMING).  A "launch" is one kernel launch of that phase: one
+ * projection GEMM per layer; one recurrent launch per layer when persistent,
+ * T per layer when stepping. */
+typedef struct {
+    double proj_ms;     /* input-projection GEMMs */
+    double rec_ms;      /* recurrent kernels */
+    int calls;          /* lstm_forward calls timed */
+    int proj_launches;
+    int rec_launches;
+} lstm_timing;
+
+/* Create a plan.  input_size, hidden_size >= 1; num_layers >= 1 (warp-nn
+ * "Raises": fewer than one layer is an error); bidirectional and has_bias are
+ * 0 or 1.  Touches no device.  *out receives the handle (NULL on error). */
+lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int num_layers,
+                        int bidirectional, int has_bias, int dtype);
+
+/* Release a plan (NULL is ignored). */
+void lstm_destroy(lstm_plan *plan);
+
+/* Set an execution option.  Options change how the forward is scheduled, not
+ * what it computes. */
+lstm_status lstm_set_option(lstm_plan *plan, int option, int value);
+
+/* Bytes of device workspace lstm_forward needs for sequence length T and batch
+ * B (intermediate layer outputs, the hoisted input projection, cell-state and
+ * synchronisation words).  Touches no device. */
+lstm_status lstm_workspace_size(const lstm_plan *plan, int T, int B, size_t *bytes);
+
+/* Enqueue the forward pass on `stream` (a hipStream_t; NULL = default stream).
+ *   x        [T, B, input_size]            dtype
+ *   h0       [L*D, B, H] dtype, or NULL    NULL means zeros; h0 and c0 are
+ *   c0       [L*D, B, H] float32, or NULL  given together or not at all
+ *   weights  host array of L*D*(has_bias ? 4 : 2) device pointers, order above
+ *   T, B     sequence length and batch size, both >= 1
+ *   layers, bidir  must equal the plan's (checked, not trusted)
+ *   y        [T, B, D*H]                   dtype, written
+ *   h_n      [L*D, B, H] dtype, or NULL    written if not NULL
+ *   c_n      [L*D, B, H] float32, or NULL  written if not NULL
+ *   workspace, workspace_bytes  device scratch of at least lstm_workspace_size
+ *   bytes; its contents are overwritten; it must not be shared by calls that
+ *   can run concurrently.
+ * Returns after enqueueing; results are ready when the stream reaches them.
+ * Inputs must not alias outputs or the workspace. */
+lstm_status lstm_forward(lstm_plan *plan, const void *x, const void *h0, const float *c0,
+                         const void *const *weights, int T, int B, int layers, int bidir,
+                         void *y, void *h_n, float *c_n, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Synchronise `stream` and read the kernel status word a previous
+ * lstm_forward left in `workspace`: *device_flags = 0 if every step barrier
+ * completed.  Returns LSTM_ERR_DEVICE_TIMEOUT when a flag is set (the outputs
+ * of that call are then invalid). */
+lstm_status lstm_device_status(const void *workspace, size_t workspace_bytes, void *stream,
+                               unsigned *device_flags);
+
+/* Wait for the events recorded by timed calls and return their totals; with
+ * reset != 0 the totals restart from zero afterwards.  The timing state
+ * belongs to the plan: time calls from one stream at a time. */
+lstm_status lstm_read_timing(lstm_plan *plan, lstm_timing *out, int reset);
+
+/* Write a one-line, human-readable description of the schedule lstm_forward
+ * would use for (T, B) into buf (kernels, tile, workgroups, mode). */
+lstm_status lstm_describe(const lstm_plan *plan, int T, int B, char *buf, size_t len);
+
+/* Static text for a status code. */
+const char *lstm_strerror(int status);
+
+/* ABI version of this header (major*100 + minor). */
+int lstm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSTM_AMD_LSTM_H */

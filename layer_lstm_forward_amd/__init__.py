@@ -1,0 +1,218 @@
+"""MI355X (gfx950) LSTM forward: thin Python binding of liblstm_amd.so.
+
+The functions below carry the names of the C ABI in include/lstm.h and only
+marshal arguments; every step of the forward pass runs in the HIP kernels of
+the shared library.  There is no fallback: if the library is not built or no
+GPU is present, calls raise.
+
+``LSTM`` is a convenience wrapper that owns a plan and a cached workspace and
+takes/returns torch tensors (torch provides device memory and streams only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblstm_amd.so")
+
+LSTM_F32, LSTM_BF16 = 0, 1
+LSTM_REC_AUTO, LSTM_REC_STEP, LSTM_REC_PERSISTENT = 0, 1, 2
+LSTM_OPT_RECURRENCE, LSTM_OPT_REC_TILE, LSTM_OPT_TIMING = 1, 2, 3
+STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
+          -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
+          -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}
+
+_lib = None
+
+
+class lstm_timing(ctypes.Structure):
+    _fields_ = [("proj_ms", ctypes.c_double), ("rec_ms", ctypes.c_double), ("calls", ctypes.c_int),
+                ("proj_launches", ctypes.c_int), ("rec_launches", ctypes.c_int)]
+
+
+class LSTMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({lstm_strerror(status)})")
+
+
+def load_library():
+    """Load liblstm_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
+                          "or python -m layer_lstm_forward_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.lstm_create.restype = i
+    lib.lstm_create.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i]
+    lib.lstm_destroy.restype = None
+    lib.lstm_destroy.argtypes = [vp]
+    lib.lstm_set_option.restype = i
+    lib.lstm_set_option.argtypes = [vp, i, i]
+    lib.lstm_workspace_size.restype = i
+    lib.lstm_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.lstm_forward.restype = i
+    lib.lstm_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp, sz, vp]
+    lib.lstm_device_status.restype = i
+    lib.lstm_device_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint)]
+    lib.lstm_describe.restype = i
+    lib.lstm_describe.argtypes = [vp, i, i, ctypes.c_char_p, sz]
+    lib.lstm_read_timing.restype = i
+    lib.lstm_read_timing.argtypes = [vp, ctypes.POINTER(lstm_timing), i]
+    lib.lstm_strerror.restype = ctypes.c_char_p
+    lib.lstm_strerror.argtypes = [i]
+    lib.lstm_version.restype = i
+    lib.lstm_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------- C-ABI mirror
+def lstm_strerror(status: int) -> str:
+    return load_library().lstm_strerror(int(status)).decode()
+
+
+def lstm_version() -> int:
+    return int(load_library().lstm_version())
+
+
+def lstm_create(input_size, hidden_size, num_layers, bidirectional, has_bias, dtype):
+    """Returns an opaque plan handle (int)."""
+    h = ctypes.c_void_p()
+    rc = load_library().lstm_create(ctypes.byref(h), int(input_size), int(hidden_size), int(num_layers),
+                                    int(bool(bidirectional)), int(bool(has_bias)), int(dtype))
+    if rc:
+        raise LSTMError(rc, "lstm_create")
+    return h.value
+
+
+def lstm_destroy(plan) -> None:
+    if plan:
+        load_library().lstm_destroy(ctypes.c_void_p(plan))
+
+
+def lstm_set_option(plan, option: int, value: int) -> None:
+    rc = load_library().lstm_set_option(ctypes.c_void_p(plan), int(option), int(value))
+    if rc:
+        raise LSTMError(rc, "lstm_set_option")
+
+
+def lstm_workspace_size(plan, T: int, B: int) -> int:
+    n = ctypes.c_size_t()
+    rc = load_library().lstm_workspace_size(ctypes.c_void_p(plan), int(T), int(B), ctypes.byref(n))
+    if rc:
+        raise LSTMError(rc, "lstm_workspace_size")
+    return int(n.value)
+
+
+def lstm_forward(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                 workspace_bytes, stream) -> int:
+    """Raw call with integer device addresses (0 = NULL); returns the status."""
+    arr = (ctypes.c_void_p * len(weights))(*[int(w) for w in weights])
+    return int(load_library().lstm_forward(
+        ctypes.c_void_p(plan), ctypes.c_void_p(x), ctypes.c_void_p(h0 or None), ctypes.c_void_p(c0 or None),
+        arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
+        ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
+        int(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def lstm_device_status(workspace, workspace_bytes, stream):
+    """Returns (status, flags) after synchronising the stream."""
+    flags = ctypes.c_uint()
+    rc = load_library().lstm_device_status(ctypes.c_void_p(workspace), int(workspace_bytes),
+                                           ctypes.c_void_p(stream or None), ctypes.byref(flags))
+    return int(rc), int(flags.value)
+
+
+def lstm_read_timing(plan, reset: bool = True) -> dict:
+    t = lstm_timing()
+    rc = load_library().lstm_read_timing(ctypes.c_void_p(plan), ctypes.byref(t), int(bool(reset)))
+    if rc:
+        raise LSTMError(rc, "lstm_read_timing")
+    return {f: getattr(t, f) for f, _ in lstm_timing._fields_}
+
+
+def lstm_describe(plan, T: int, B: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().lstm_describe(ctypes.c_void_p(plan), int(T), int(B), buf, 512)
+    if rc:
+        raise LSTMError(rc, "lstm_describe")
+    return buf.value.decode()
+
+
+# ------------------------------------------------------------ torch wrapper
+class LSTM:
+    """A plan plus a cached workspace, taking and returning torch tensors.
+
+    weights: flat list in (layer, direction, W_ih, W_hh[, b_ih, b_hh]) order,
+    contiguous device tensors of the plan's dtype.
+    """
+
+    def __init__(self, input_size, hidden_size, num_layers=1, bidirectional=False, bias=True,
+                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0):
+        self.input_size, self.hidden_size = int(input_size), int(hidden_size)
+        self.num_layers, self.bidirectional, self.bias = int(num_layers), bool(bidirectional), bool(bias)
+        self.dtype = dtype
+        self.D = 2 if self.bidirectional else 1
+        self.plan = lstm_create(input_size, hidden_size, num_layers, bidirectional, bias,
+                                LSTM_BF16 if dtype == "bf16" else LSTM_F32)
+        if recurrence != LSTM_REC_AUTO:
+            lstm_set_option(self.plan, LSTM_OPT_RECURRENCE, recurrence)
+        if rec_tile:
+            lstm_set_option(self.plan, LSTM_OPT_REC_TILE, rec_tile)
+        self._ws = None
+
+    def __del__(self):
+        try:
+            lstm_destroy(self.plan)
+        except Exception:
+            pass
+
+    def describe(self, T, B) -> str:
+        return lstm_describe(self.plan, T, B)
+
+    def workspace(self, T, B, device):
+        import torch
+        n = lstm_workspace_size(self.plan, T, B)
+        if self._ws is None or self._ws.numel() < n or self._ws.device != device:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=device)
+        return self._ws, n
+
+    def forward(self, x, weights, h0=None, c0=None, stream=None, out=None):
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if not x.is_cuda or x.dtype != tdt or not x.is_contiguous() or x.dim() != 3:
+            raise ValueError("x must be a contiguous [T, B, input_size] device tensor of the plan's dtype")
+        for w in weights:
+            if not w.is_cuda or w.dtype != tdt or not w.is_contiguous():
+                raise ValueError("weights must be contiguous device tensors of the plan's dtype")
+        T, B, _ = x.shape
+        H, L, D = self.hidden_size, self.num_layers, self.D
+        if out is None:
+            y = torch.empty(T, B, D * H, dtype=tdt, device=x.device)
+            hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
+            cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
+        else:
+            y, hn, cn = out
+        ws, nbytes = self.workspace(T, B, x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lstm_forward(self.plan, x.data_ptr(), h0.data_ptr() if h0 is not None else 0,
+                          c0.data_ptr() if c0 is not None else 0, [w.data_ptr() for w in weights],
+                          T, B, L, self.bidirectional, y.data_ptr(), hn.data_ptr() if hn is not None else 0,
+                          cn.data_ptr() if cn is not None else 0, ws.data_ptr(), nbytes, stream)
+        if rc:
+            raise LSTMError(rc, "lstm_forward")
+        return y, hn, cn
+
+    def device_status(self, stream=None):
+        import torch
+        if self._ws is None:
+            return 0, 0
+        if stream is None:
+            stream = torch.cuda.current_stream(self._ws.device).cuda_stream
+        return lstm_device_status(self._ws.data_ptr(), self._ws.numel(), stream)

@@ -1,0 +1,68 @@
+// kernels.h -- host-side interface of the gfx950 kernels (internal; the public
+// ABI is include/lstm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace lstm_amd {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// G[m][d*N + n] = sum_k X[m][k] * W_d[n][k] + b_ih_d[n] + b_hh_d[n]
+//   X   [M, K] with row stride ldx (elements), dtype
+//   W_d [N, K] row-major, dtype; N = 4H; d = 0..D-1 (blockIdx.z)
+//   G   [M, D*N] float32
+struct ProjArgs {
+    const void *X;
+    const void *W[2];
+    const void *b_ih[2];
+    const void *b_hh[2];
+    float *G;
+    int M, N, K, ldx, D;
+};
+
+// One layer of the recurrence for all directions and batch rows.
+struct RecArgs {
+    const void *whh[2];      // [4H, H] per direction, dtype
+    const float *G;          // [T, B, D*4H] projection incl. both biases
+    const void *h0;          // [D, B, H] dtype for this layer, or NULL (zeros)
+    const float *c0;         // [D, B, H] or NULL
+    void *Y;                 // [T, B, D*H] dtype, written (also read as h_{t-1})
+    void *hn;                // [D, B, H] dtype or NULL
+    float *cn;               // [D, B, H] or NULL
+    float *cstate;           // [D, B, H] carry between step launches
+    unsigned *ctr;           // team counters, stride kCtrStride words
+    unsigned *status;        // error word
+    int T, B, H, D;
+    int P;                   // workgroups per team (hidden-unit slices)
+    int BG;                  // batch rows per team
+    int NGB;                 // batch groups
+    int kch;                 // K chunks of H
+    int s_begin, s_end;      // steps handled by this launch
+    int persistent;          // 1: all steps in this launch with step barriers
+    int map_xcd;             // 1: place a team's workgroups on the same XCDs
+    int vec;                 // 16-byte vector loads are aligned
+    long long timeout_ticks; // barrier timeout in wall_clock64 ticks
+};
+
+constexpr int kCtrStride = 32;       // 128 bytes between counters
+constexpr int kMaxTeams = 64;        // counters per layer
+
+// Recurrent tile: 4 waves split (4/WK) ways over batch tiles and WK ways over
+// K; each wave owns MTW 16-row batch tiles; NT 16-column tiles of gate rows
+// (4 hidden units each, gates interleaved) make U = 4*NT units per workgroup.
+struct RecTile {
+    int WK, MTW, NT;
+};
+
+size_t rec_smem_bytes(RecTile t, int H, int dtype);
+int rec_rows_per_wg(RecTile t);
+bool rec_tile_supported(RecTile t);
+
+hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s);
+hipError_t launch_rec(const RecArgs &a, RecTile t, int dtype, bool cooperative, hipStream_t s);
+hipError_t rec_max_coresident(RecTile t, int H, int dtype, int *blocks_per_cu);
+hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
+
+}  // namespace lstm_amd

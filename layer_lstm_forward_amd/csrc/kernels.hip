@@ -1,0 +1,405 @@
+// kernels.hip -- gfx950 kernels of the LSTM forward pass.
+//
+//   k_proj  the input projection of one layer for every time step at once:
+//           G = X W_ih^T + b_ih + b_hh, an "NT" GEMM on the matrix cores.
+//           The gate pre-activation splits into a part that depends only on
+//           x_t and a part that depends on h_{t-1} (warp-nn "Long Short-Term
+//           Memory (LSTM)", equation block); the first part carries no
+//           recurrence and is hoisted out of the time loop.  The MXNet blog
+//           "LSTM Forward Computation" ("Basic Operators") concatenates the
+//           four gate matrices into one so that one product serves all gates;
+//           the warp-nn parameter table fixes the [i; f; g; o] row blocks.
+//   k_rec   the recurrence of one layer: per step S = h_{t-1} W_hh^T on the
+//           matrix cores, then the gate nonlinearities and the cell update
+//           (same equation block) fused into the epilogue; the reverse
+//           direction runs in the same launch on its own workgroups.  Either
+//           one launch per step, or one persistent launch per layer with the
+//           W_hh slices resident in LDS and a step barrier between steps.
+//   k_fill  fills synchronisation words.
+#include "device.h"
+#include "kernels.h"
+
+namespace lstm_amd {
+
+// ===========================================================================
+// Projection GEMM.  128x128 output tile per 256-thread workgroup; each of the
+// four waves owns a 64x64 quadrant as 4x4 MFMA tiles of 16x16.  A stage holds
+// 128 bytes of K per row (two chunks), double-buffered in LDS; 16-byte
+// segments are XOR-swizzled by row so that the fragment reads of 16 rows at
+// one K offset spread over the banks.
+// ===========================================================================
+template <class DT, bool VEC>
+__global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 128, BN = 128, SEG = 8;
+    constexpr int KS = SEG * DT::PER16;
+    __shared__ u32x4 sA[2][BM * SEG];
+    __shared__ u32x4 sB[2][BN * SEG];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int d = blockIdx.z;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int M = a.M, N = a.N, K = a.K;
+    const S *X = static_cast<const S *>(a.X);
+    const S *W = static_cast<const S *>(a.W[d]);
+
+    u32x4 ra[4], rb[4];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
+            const int k = k0 + sg * DT::PER16;
+            ra[i] = (m0 + row < M) ? load_frag<DT>(X + (size_t)(m0 + row) * a.ldx, k, K, VEC) : zero;
+            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * K, k, K, VEC) : zero;
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
+            const int pos = row * SEG + (sg ^ ((row >> 1) & 7));
+            sA[buf][pos] = ra[i];
+            sB[buf][pos] = rb[i];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (K + KS - 1) / KS;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * KS);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 af[4], bw[4];
+            const int sg = 4 * c + (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 64 + 16 * i + (lane & 15);
+                af[i] = sA[buf][row * SEG + (sg ^ ((row >> 1) & 7))];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wn * 64 + 16 * j + (lane & 15);
+                bw[j] = sB[buf][row * SEG + (sg ^ ((row >> 1) & 7))];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw[j]);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane l holds rows 4*(l/16)+v, column l%16 of each 16x16 tile.
+    const S *bi = static_cast<const S *>(a.b_ih[d]);
+    const S *bh = static_cast<const S *>(a.b_hh[d]);
+    float bias[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 64 + 16 * j + (lane & 15);
+        bias[j] = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+    }
+    const size_t ldg = (size_t)a.D * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + 16 * j + (lane & 15);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + v;
+                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias[j];
+            }
+        }
+}
+
+// ===========================================================================
+// Recurrence.  A team of P workgroups shares one direction and one group of
+// BG batch rows; workgroup p owns hidden units [p*U, p*U+U) and therefore the
+// 4U rows {q*H + j : q in i,f,g,o} of W_hh, kept in LDS as MFMA fragments
+// (gate rows interleaved: local column n = 4*u + q).  Per step:
+//   1. prefetch the projection G[t] for the cells this thread updates;
+//   2. (persistent) wait until the team has published h_{t-1};
+//   3. S = h_{t-1} W_slice^T: the four waves split over batch tiles and K,
+//      reading h_{t-1} fragments straight from global memory;
+//   4. partial sums meet in LDS; each thread reduces the four gate
+//      pre-activations of its cells, applies sigma/tanh, updates c (kept in
+//      registers across steps) and writes h_t to y (and h_n, c_n at the end);
+//   5. (persistent) publish the step to the team.
+// h_t is exchanged through y itself: the next step reads y[t-1] (forward) or
+// y[t+1] (reverse), so no separate exchange buffer exists.
+// ===========================================================================
+template <class DT, int WK, int MTW, int NT>
+__global__ __launch_bounds__(256) void k_rec(RecArgs a) {
+    using S = typename DT::S;
+    constexpr int WM = 4 / WK;
+    constexpr int MT = WM * MTW;
+    constexpr int ROWS = 16 * MT;
+    constexpr int NCOL = 16 * NT;
+    constexpr int U = 4 * NT;
+    constexpr int PSTR = NCOL + 4;
+    constexpr int CELLS = ROWS * U;
+    constexpr int CPT = (CELLS + 255) / 256;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_flag;
+    u32x4 *Wf = reinterpret_cast<u32x4 *>(smem);
+    float *part = reinterpret_cast<float *>(smem + (size_t)a.kch * NT * 1024);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w / WK, wk = w % WK;
+    const int nteams = a.NGB * a.D;
+    int team, p;
+    {
+        const int bid = blockIdx.x;
+        if (a.map_xcd) {
+            const int X = 8 / nteams;  // XCDs per team (dispatch is round-robin over 8 XCDs)
+            team = (bid & 7) / X;
+            p = (bid >> 3) * X + (bid & 7) % X;
+        } else {
+            team = bid / a.P;
+            p = bid % a.P;
+        }
+    }
+    const int H = a.H, B = a.B, T = a.T, D = a.D;
+    const int d = team % D, gb = team / D;
+    const int b0 = gb * a.BG, rows = min(a.BG, B - b0);
+    const int j0 = p * U, units = min(U, H - j0);
+    const size_t ldy = (size_t)D * H;
+    const size_t ldg = (size_t)D * 4 * H;
+    const bool vec = a.vec != 0;
+
+    // Resident W_hh slice as fragments: [chunk][n-tile][lane] x 16 bytes.
+    {
+        const S *W = static_cast<const S *>(a.whh[d]);
+        const int nfrag = a.kch * NT * 64;
+        for (int f = tid; f < nfrag; f += 256) {
+            const int ln = f & 63, nt = (f >> 6) % NT, c = (f >> 6) / NT;
+            const int n = nt * 16 + (ln & 15), u = n >> 2, q = n & 3;
+            const int k = c * DT::KC + (ln >> 4) * DT::PER16;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (u < units) v = load_frag<DT>(W + (size_t)(q * H + j0 + u) * H, k, H, vec);
+            Wf[f] = v;
+        }
+    }
+
+    int cm[CPT], cu[CPT];
+    bool cv[CPT];
+    float creg[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int e = tid + 256 * i;
+        cm[i] = e / U;
+        cu[i] = e % U;
+        cv[i] = e < CELLS && cm[i] < rows && cu[i] < units;
+        creg[i] = 0.f;
+        if (cv[i]) {
+            const size_t si = ((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i];
+            if (a.s_begin == 0) creg[i] = a.c0 ? a.c0[si] : 0.f;
+            else creg[i] = a.cstate[si];
+        }
+    }
+    __syncthreads();
+
+    unsigned *ctr = a.ctr + team * kCtrStride;
+    const int cpw = (a.kch + WK - 1) / WK;
+    const int cb = wk * cpw, ce = min(a.kch, cb + cpw);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    for (int s = a.s_begin; s < a.s_end; ++s) {
+        const int t = d == 0 ? s : T - 1 - s;
+
+        float g[CPT][4];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const float *gp = a.G + ((size_t)t * B + b0 + cm[i]) * ldg + (size_t)d * 4 * H + j0 + cu[i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[i][q] = cv[i] ? gp[(size_t)q * H] : 0.f;
+        }
+
+        if (a.persistent && s > a.s_begin) {
+            if (!step_wait(ctr, (unsigned)(a.P * (s - a.s_begin)), a.status, a.timeout_ticks, &s_flag))
+                return;
+        }
+
+        const S *hsrc = nullptr;
+        size_t hld = 0;
+        if (s == 0) {
+            if (a.h0) {
+                hsrc = static_cast<const S *>(a.h0) + (size_t)d * B * H;
+                hld = (size_t)H;
+            }
+        } else {
+            const int tp = d == 0 ? t - 1 : t + 1;
+            hsrc = static_cast<const S *>(a.Y) + (size_t)tp * B * ldy + (size_t)d * H;
+            hld = ldy;
+        }
+
+        f32x4 acc[MTW][NT];
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        if (hsrc) {
+            for (int c = cb; c < ce; ++c) {
+                u32x4 af[MTW];
+                const int k = c * DT::KC + (lane >> 4) * DT::PER16;
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) {
+                    const int m = (wm * MTW + i) * 16 + (lane & 15);
+                    af[i] = (m < rows) ? load_frag<DT>(hsrc + (size_t)(b0 + m) * hld, k, H, vec) : zero;
+                }
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const u32x4 bw = Wf[(c * NT + j) * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = (wm * MTW + i) * 16 + 4 * (lane >> 4) + v;
+                    const int n = j * 16 + (lane & 15);
+                    part[(wk * ROWS + m) * PSTR + n] = acc[i][j][v];
+                }
+        __syncthreads();
+
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            if (!cv[i]) continue;
+            f32x4 sum = *reinterpret_cast<const f32x4 *>(&part[(cm[i]) * PSTR + 4 * cu[i]]);
+#pragma unroll
+            for (int kk = 1; kk < WK; ++kk)
+                sum += *reinterpret_cast<const f32x4 *>(&part[(kk * ROWS + cm[i]) * PSTR + 4 * cu[i]]);
+            const float ig = sigmoid_f(sum.x + g[i][0]);
+            const float fg = sigmoid_f(sum.y + g[i][1]);
+            const float gg = tanh_f(sum.z + g[i][2]);
+            const float og = sigmoid_f(sum.w + g[i][3]);
+            const float cn = fg * creg[i] + ig * gg;
+            const float hv = og * tanh_f(cn);
+            creg[i] = cn;
+            const S hs = DT::from_f(hv);
+            const int bb = b0 + cm[i], jj = j0 + cu[i];
+            static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = hs;
+            if (s == T - 1) {
+                const size_t si = ((size_t)d * B + bb) * H + jj;
+                if (a.hn) static_cast<S *>(a.hn)[si] = hs;
+                if (a.cn) a.cn[si] = cn;
+            }
+        }
+
+        if (a.persistent && s + 1 < a.s_end) step_publish(ctr);
+        else __syncthreads();
+    }
+
+    if (a.s_end < T) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            if (cv[i]) a.cstate[((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i]] = creg[i];
+    }
+}
+
+__global__ void k_fill(unsigned *p, size_t n, unsigned v) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// ===========================================================================
+// Host-side launch helpers.
+// ===========================================================================
+hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s) {
+    const int per16 = dtype == DT_BF16 ? 8 : 4;
+    const size_t es = dtype == DT_BF16 ? 2 : 4;
+    bool vec = (a.K % per16 == 0) && (a.ldx % per16 == 0) && ((uintptr_t)a.X % 16 == 0);
+    for (int d = 0; d < a.D; ++d) vec = vec && ((uintptr_t)a.W[d] % 16 == 0);
+    (void)es;
+    dim3 grid((a.N + 127) / 128, (a.M + 127) / 128, a.D), block(256);
+    if (dtype == DT_BF16) {
+        if (vec) hipLaunchKernelGGL((k_proj<BF16, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_proj<BF16, false>), grid, block, 0, s, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_proj<F32, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_proj<F32, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+int rec_rows_per_wg(RecTile t) { return 16 * (4 / t.WK) * t.MTW; }
+
+size_t rec_smem_bytes(RecTile t, int H, int dtype) {
+    const int kc = dtype == DT_BF16 ? 32 : 16;
+    const size_t kch = (size_t)(H + kc - 1) / kc;
+    return kch * t.NT * 1024 + (size_t)t.WK * rec_rows_per_wg(t) * (16 * t.NT + 4) * 4;
+}
+
+#define LSTM_REC_TILES(X) \
+    X(4, 1, 1) X(4, 1, 2) X(4, 1, 4) X(2, 1, 1) X(2, 1, 2) X(2, 1, 4) X(1, 1, 1) X(1, 1, 2) X(1, 1, 4) \
+    X(1, 4, 1) X(1, 4, 2) X(1, 4, 4)
+
+bool rec_tile_supported(RecTile t) {
+#define LSTM_T_OK(wk, mtw, nt) if (t.WK == wk && t.MTW == mtw && t.NT == nt) return true;
+    LSTM_REC_TILES(LSTM_T_OK)
+#undef LSTM_T_OK
+    return false;
+}
+
+template <class DT>
+static const void *rec_kernel_ptr(RecTile t) {
+#define LSTM_T_PTR(wk, mtw, nt) \
+    if (t.WK == wk && t.MTW == mtw && t.NT == nt) return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt>);
+    LSTM_REC_TILES(LSTM_T_PTR)
+#undef LSTM_T_PTR
+    return nullptr;
+}
+
+static const void *rec_kernel(RecTile t, int dtype) {
+    return dtype == DT_BF16 ? rec_kernel_ptr<BF16>(t) : rec_kernel_ptr<F32>(t);
+}
+
+hipError_t rec_max_coresident(RecTile t, int H, int dtype, int *blocks_per_cu) {
+    const void *fn = rec_kernel(t, dtype);
+    if (!fn) return hipErrorInvalidValue;
+    const size_t smem = rec_smem_bytes(t, H, dtype);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256, smem);
+}
+
+hipError_t launch_rec(const RecArgs &a, RecTile t, int dtype, bool cooperative, hipStream_t s) {
+    const void *fn = rec_kernel(t, dtype);
+    if (!fn) return hipErrorInvalidValue;
+    const size_t smem = rec_smem_bytes(t, a.H, dtype);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid(a.NGB * a.D * a.P), block(256);
+    RecArgs copy = a;
+    void *args[] = {&copy};
+    if (cooperative) return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)smem, s);
+    return hipLaunchKernel(fn, grid, block, args, smem, s);
+}
+
+hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(k_fill, dim3(blocks), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace lstm_amd

@@ -1,0 +1,505 @@
+// lstm_api.cpp -- the C ABI declared in include/lstm.h: argument validation,
+// workspace carve-up, the per-layer schedule and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/lstm.h"
+#include "kernels.h"
+
+using namespace lstm_amd;
+
+struct lstm_plan {
+    int I, H, L, D, has_bias, dtype;
+    int rec_mode;  // lstm_recurrence
+    int rec_tile;  // 0 = automatic, else 100*WK + 10*MTW + NT
+    // optional per-phase timing (LSTM_OPT_TIMING)
+    int timing;
+    struct Span {
+        hipEvent_t a, b;
+        int phase;     // 0 projection, 1 recurrence
+        int launches;
+    };
+    std::vector<Span> spans;
+    std::vector<hipEvent_t> pool;
+    lstm_timing acc;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kStatusBytes = 256;
+constexpr size_t kLdsLimit = 160 * 1024 - 64;  // leaves room for static LDS
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t elem_size(int dtype) { return dtype == LSTM_BF16 ? 2 : 4; }
+
+// Checked products; false on size_t overflow.
+bool mul_ok(size_t a, size_t b, size_t *out) {
+    if (a != 0 && b > SIZE_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Layout {
+    size_t status, counters, G, ymid[2], cstate, total;
+    size_t sync_bytes;  // status + counters, zeroed per call
+};
+
+bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
+    size_t tb, g, y, st;
+    if (!mul_ok((size_t)T, (size_t)B, &tb)) return false;
+    if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
+    if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
+    if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
+    const size_t ctr = (size_t)p->L * kMaxTeams * kCtrStride * sizeof(unsigned);
+    size_t off = 0;
+    o->status = off;
+    off += kStatusBytes;
+    o->counters = off;
+    off += align_up(ctr);
+    o->sync_bytes = off;
+    o->G = off;
+    if (g > SIZE_MAX / 2) return false;
+    off += align_up(g);
+    const int nmid = p->L >= 3 ? 2 : (p->L == 2 ? 1 : 0);
+    for (int i = 0; i < 2; ++i) {
+        o->ymid[i] = off;
+        if (i < nmid) off += align_up(y);
+    }
+    o->cstate = off;
+    off += align_up(st);
+    o->total = off;
+    return true;
+}
+
+// ---------------------------------------------------------------- schedule
+struct Sched {
+    bool persistent;
+    RecTile tile;
+    int U, P, BG, NGB, teams, wgs, map_xcd;
+    size_t smem;
+};
+
+struct DevInfo {
+    bool ok;
+    int cus;
+    int wall_khz;
+};
+
+DevInfo dev_info(int dev) {
+    static std::mutex mu;
+    static DevInfo cache[64];
+    static bool have[64];
+    std::lock_guard<std::mutex> g(mu);
+    if (dev < 0 || dev >= 64) return DevInfo{false, 0, 0};
+    if (!have[dev]) {
+        DevInfo d{true, 0, 0};
+        if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+            d.ok = false;
+        if (d.wall_khz <= 0) d.wall_khz = 100000;
+        cache[dev] = d;
+        have[dev] = d.ok;
+        return d;
+    }
+    return cache[dev];
+}
+
+const RecTile kTiles[] = {{4, 1, 4}, {4, 1, 2}, {4, 1, 1}, {2, 1, 4}, {2, 1, 2}, {2, 1, 1},
+                          {1, 1, 4}, {1, 1, 2}, {1, 1, 1}, {1, 4, 4}, {1, 4, 2}, {1, 4, 1}};
+
+bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
+    if (!rec_tile_supported(t)) return false;
+    const int rows = rec_rows_per_wg(t);
+    s->tile = t;
+    s->U = 4 * t.NT;
+    s->P = (p->H + s->U - 1) / s->U;
+    const int ng0 = (B + rows - 1) / rows;
+    s->BG = (B + ng0 - 1) / ng0;
+    s->NGB = (B + s->BG - 1) / s->BG;
+    s->teams = s->NGB * p->D;
+    s->wgs = s->teams * s->P;
+    s->smem = rec_smem_bytes(t, p->H, p->dtype);
+    s->map_xcd = (s->teams <= 8 && 8 % s->teams == 0 && (s->wgs % 8) == 0) ? 1 : 0;
+    return s->teams <= kMaxTeams && s->smem <= kLdsLimit;
+}
+
+// Rough cycles per step of one workgroup: matrix-core work of the busiest
+// wave plus the h_{t-1} fetch at an assumed 64 B/clk per CU.
+double step_cost(const lstm_plan *p, const Sched &s) {
+    const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
+    const int kch = (p->H + kc - 1) / kc;
+    const int cpw = (kch + s.tile.WK - 1) / s.tile.WK;
+    const int live_mtw = (s.BG + 15) / 16 < s.tile.MTW ? (s.BG + 15) / 16 : s.tile.MTW;
+    const double mfma = (double)live_mtw * s.tile.NT * cpw * (p->dtype == LSTM_BF16 ? 16 : 128);
+    const double hbytes = (double)s.BG * p->H * elem_size(p->dtype);
+    return mfma + hbytes / 64.0;
+}
+
+int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
+    const DevInfo di = dev_info(dev);
+    Sched best{};
+    double best_cost = 1e300;
+    bool found = false;
+    const bool want_step = p->rec_mode == LSTM_REC_STEP;
+    for (const RecTile &t : kTiles) {
+        if (p->rec_tile && p->rec_tile != 100 * t.WK + 10 * t.MTW + t.NT) continue;
+        Sched s{};
+        if (!fill_sched(p, B, t, &s)) continue;
+        bool can_persist = false;
+        if (!want_step && di.ok) {
+            int bpc = 0;
+            if (rec_max_coresident(t, p->H, p->dtype, &bpc) == hipSuccess && bpc > 0)
+                can_persist = (long long)bpc * di.cus >= s.wgs;
+            (void)hipGetLastError();
+        }
+        if (p->rec_mode == LSTM_REC_PERSISTENT && !can_persist) continue;
+        s.persistent = can_persist;
+        double cost;
+        if (s.persistent) {
+            cost = step_cost(p, s);
+        } else {
+            // per step launch: every workgroup reloads its W_hh slice
+            cost = 1e12 + (double)s.wgs * (4.0 * s.U + s.BG) * p->H * elem_size(p->dtype);
+        }
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = s;
+            found = true;
+        }
+    }
+    if (!found) return LSTM_ERR_UNSUPPORTED;
+    *out = best;
+    return LSTM_OK;
+}
+
+hipEvent_t take_event(lstm_plan *p) {
+    if (!p->pool.empty()) {
+        hipEvent_t e = p->pool.back();
+        p->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return e;
+}
+
+// Record the start of a timed span on `st`; returns the span index or -1.
+int span_begin(lstm_plan *p, hipStream_t st, int phase) {
+    if (!p->timing) return -1;
+    lstm_plan::Span sp{take_event(p), take_event(p), phase, 0};
+    if (!sp.a || !sp.b || hipEventRecord(sp.a, st) != hipSuccess) {
+        (void)hipGetLastError();
+        if (sp.a) p->pool.push_back(sp.a);
+        if (sp.b) p->pool.push_back(sp.b);
+        return -1;
+    }
+    p->spans.push_back(sp);
+    return (int)p->spans.size() - 1;
+}
+
+void span_end(lstm_plan *p, int idx, hipStream_t st, int launches) {
+    if (idx < 0) return;
+    p->spans[idx].launches = launches;
+    if (hipEventRecord(p->spans[idx].b, st) != hipSuccess) (void)hipGetLastError();
+}
+
+bool is_device_ptr(const void *ptr, int dev) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    const bool dev_mem = attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+    return dev_mem && attr.device == dev;
+}
+
+int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
+             const void *const *weights, int T, int B, int layers, int bidir, const void *y,
+             const void *ws, size_t ws_bytes, Layout *lay) {
+    if (!p) return LSTM_ERR_ARG;
+    if (layers != p->L || (bidir ? 2 : 1) != p->D || (bidir != 0 && bidir != 1)) return LSTM_ERR_SHAPE;
+    if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    if ((long long)T * B > INT_MAX) return LSTM_ERR_SHAPE;
+    if (!x || !y || !weights) return LSTM_ERR_ARG;
+    if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
+    const int per = p->has_bias ? 4 : 2;
+    for (int i = 0; i < p->L * p->D * per; ++i)
+        if (!weights[i]) return LSTM_ERR_ARG;
+    if (!make_layout(p, T, B, lay)) return LSTM_ERR_SHAPE;
+    if (!ws || ws_bytes < lay->total) return LSTM_ERR_WORKSPACE;
+    return LSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lstm_version(void) { return 100; }
+
+const char *lstm_strerror(int s) {
+    switch (s) {
+        case LSTM_OK: return "ok";
+        case LSTM_ERR_ARG: return "invalid argument (NULL pointer, non-positive size, or h0/c0 not given together)";
+        case LSTM_ERR_SHAPE: return "invalid shape (T or B < 1, layers/bidir differ from the plan, or size overflow)";
+        case LSTM_ERR_DTYPE: return "unknown dtype";
+        case LSTM_ERR_DEVICE: return "pointer is not device memory of the current device, or no device";
+        case LSTM_ERR_WORKSPACE: return "workspace missing or smaller than lstm_workspace_size";
+        case LSTM_ERR_LAUNCH: return "kernel launch failed";
+        case LSTM_ERR_UNSUPPORTED: return "unsupported option or schedule";
+        case LSTM_ERR_DEVICE_TIMEOUT: return "a step barrier timed out on the device; outputs are invalid";
+        default: return "unknown status";
+    }
+}
+
+lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int num_layers,
+                        int bidirectional, int has_bias, int dtype) {
+    if (!out) return LSTM_ERR_ARG;
+    *out = nullptr;
+    if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
+    if (input_size < 1 || hidden_size < 1 || num_layers < 1) return LSTM_ERR_ARG;
+    if ((bidirectional != 0 && bidirectional != 1) || (has_bias != 0 && has_bias != 1)) return LSTM_ERR_ARG;
+    // 4H and D*4H index rows and columns as int in the kernels
+    if ((long long)hidden_size * 8 > INT_MAX / 4) return LSTM_ERR_SHAPE;
+    lstm_plan *p = new (std::nothrow) lstm_plan;
+    if (!p) return LSTM_ERR_ARG;
+    p->I = input_size;
+    p->H = hidden_size;
+    p->L = num_layers;
+    p->D = bidirectional ? 2 : 1;
+    p->has_bias = has_bias;
+    p->dtype = dtype;
+    p->rec_mode = LSTM_REC_AUTO;
+    p->rec_tile = 0;
+    p->timing = 0;
+    p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
+    *out = p;
+    return LSTM_OK;
+}
+
+void lstm_destroy(lstm_plan *p) {
+    if (!p) return;
+    for (auto &sp : p->spans) {
+        (void)hipEventSynchronize(sp.b);
+        (void)hipEventDestroy(sp.a);
+        (void)hipEventDestroy(sp.b);
+    }
+    for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
+    (void)hipGetLastError();
+    delete p;
+}
+
+lstm_status lstm_read_timing(lstm_plan *p, lstm_timing *out, int reset) {
+    if (!p || !out) return LSTM_ERR_ARG;
+    for (auto &sp : p->spans) {
+        float ms = 0.f;
+        if (hipEventSynchronize(sp.b) == hipSuccess && hipEventElapsedTime(&ms, sp.a, sp.b) == hipSuccess) {
+            if (sp.phase == 0) {
+                p->acc.proj_ms += ms;
+                p->acc.proj_launches += sp.launches;
+            } else {
+                p->acc.rec_ms += ms;
+                p->acc.rec_launches += sp.launches;
+            }
+        } else {
+            (void)hipGetLastError();
+        }
+        p->pool.push_back(sp.a);
+        p->pool.push_back(sp.b);
+    }
+    p->spans.clear();
+    *out = p->acc;
+    if (reset) p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
+    return LSTM_OK;
+}
+
+lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
+    if (!p) return LSTM_ERR_ARG;
+    switch (option) {
+        case LSTM_OPT_RECURRENCE:
+            if (value < LSTM_REC_AUTO || value > LSTM_REC_PERSISTENT) return LSTM_ERR_UNSUPPORTED;
+            p->rec_mode = value;
+            return LSTM_OK;
+        case LSTM_OPT_TIMING:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->timing = value;
+            return LSTM_OK;
+        case LSTM_OPT_REC_TILE:
+            if (value != 0 && !rec_tile_supported(RecTile{value / 100, (value / 10) % 10, value % 10}))
+                return LSTM_ERR_UNSUPPORTED;
+            p->rec_tile = value;
+            return LSTM_OK;
+        default:
+            return LSTM_ERR_UNSUPPORTED;
+    }
+}
+
+lstm_status lstm_workspace_size(const lstm_plan *p, int T, int B, size_t *bytes) {
+    if (!p || !bytes) return LSTM_ERR_ARG;
+    if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    Layout lay;
+    if (!make_layout(p, T, B, &lay)) return LSTM_ERR_SHAPE;
+    *bytes = lay.total;
+    return LSTM_OK;
+}
+
+lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t len) {
+    if (!p || !buf || len == 0) return LSTM_ERR_ARG;
+    if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    Sched s{};
+    const int rc = choose_sched(p, B, dev, &s);
+    if (rc != LSTM_OK) return (lstm_status)rc;
+    std::snprintf(buf, len,
+                  "proj=k_proj<%s> tile=128x128; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
+                  "NGB=%d teams=%d workgroups=%d lds=%zu map_xcd=%d",
+                  p->dtype == LSTM_BF16 ? "bf16" : "f32", p->dtype == LSTM_BF16 ? "bf16" : "f32", s.tile.WK,
+                  s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P, s.BG, s.NGB, s.teams,
+                  s.wgs, s.smem, s.map_xcd);
+    return LSTM_OK;
+}
+
+lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                         const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream_) {
+    Layout lay;
+    int rc = validate(p, x, h0, c0, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
+    if (rc != LSTM_OK) return (lstm_status)rc;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    const int per = p->has_bias ? 4 : 2;
+    const void *ptrs[] = {x, y, workspace, h0, c0, h_n, c_n};
+    for (const void *q : ptrs)
+        if (q && !is_device_ptr(q, dev)) return LSTM_ERR_DEVICE;
+    for (int i = 0; i < p->L * p->D * per; ++i)
+        if (!is_device_ptr(weights[i], dev)) return LSTM_ERR_DEVICE;
+
+    Sched sch{};
+    rc = choose_sched(p, B, dev, &sch);
+    if (rc != LSTM_OK) return (lstm_status)rc;
+    const DevInfo di = dev_info(dev);
+
+    hipStream_t st = static_cast<hipStream_t>(stream_);
+    char *ws = static_cast<char *>(workspace);
+    unsigned *status = reinterpret_cast<unsigned *>(ws + lay.status);
+    unsigned *counters = reinterpret_cast<unsigned *>(ws + lay.counters);
+    float *G = reinterpret_cast<float *>(ws + lay.G);
+    float *cstate = reinterpret_cast<float *>(ws + lay.cstate);
+    const size_t es = elem_size(p->dtype);
+    const size_t state_elems = (size_t)p->D * B * p->H;
+
+    if (launch_fill_u32(status, lay.sync_bytes / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
+
+    const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
+    const int per16 = p->dtype == LSTM_BF16 ? 8 : 4;
+    for (int l = 0; l < p->L; ++l) {
+        const void *X = l == 0 ? x : static_cast<const void *>(ws + lay.ymid[(l - 1) & 1]);
+        void *Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
+        const int in_l = l == 0 ? p->I : p->D * p->H;
+
+        ProjArgs pa{};
+        pa.X = X;
+        pa.G = G;
+        pa.M = T * B;
+        pa.N = 4 * p->H;
+        pa.K = in_l;
+        pa.ldx = in_l;
+        pa.D = p->D;
+        for (int d = 0; d < p->D; ++d) {
+            const void *const *w = weights + (size_t)(l * p->D + d) * per;
+            pa.W[d] = w[0];
+            pa.b_ih[d] = p->has_bias ? w[2] : nullptr;
+            pa.b_hh[d] = p->has_bias ? w[3] : nullptr;
+        }
+        int span = span_begin(p, st, 0);
+        if (launch_proj(pa, p->dtype, st) != hipSuccess) return LSTM_ERR_LAUNCH;
+        span_end(p, span, st, 1);
+
+        RecArgs ra{};
+        for (int d = 0; d < p->D; ++d) ra.whh[d] = weights[(size_t)(l * p->D + d) * per + 1];
+        ra.G = G;
+        ra.h0 = h0 ? static_cast<const char *>(h0) + (size_t)l * state_elems * es : nullptr;
+        ra.c0 = c0 ? c0 + (size_t)l * state_elems : nullptr;
+        ra.Y = Y;
+        ra.hn = h_n ? static_cast<char *>(h_n) + (size_t)l * state_elems * es : nullptr;
+        ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
+        ra.cstate = cstate;
+        ra.ctr = counters + (size_t)l * kMaxTeams * kCtrStride;
+        ra.status = status;
+        ra.T = T;
+        ra.B = B;
+        ra.H = p->H;
+        ra.D = p->D;
+        ra.P = sch.P;
+        ra.BG = sch.BG;
+        ra.NGB = sch.NGB;
+        ra.kch = (p->H + kc - 1) / kc;
+        ra.map_xcd = sch.map_xcd;
+        ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
+        for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
+        ra.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
+        span = span_begin(p, st, 1);
+        bool stepped = !sch.persistent;
+        if (sch.persistent) {
+            ra.s_begin = 0;
+            ra.s_end = T;
+            ra.persistent = 1;
+            if (launch_rec(ra, sch.tile, p->dtype, true, st) != hipSuccess) {
+                (void)hipGetLastError();
+                // The cooperative launch was refused (nothing ran): in automatic
+                // mode the layer falls back to one launch per step.
+                if (p->rec_mode == LSTM_REC_PERSISTENT) return LSTM_ERR_LAUNCH;
+                stepped = true;
+            }
+        }
+        if (stepped) {
+            ra.persistent = 0;
+            for (int s = 0; s < T; ++s) {
+                ra.s_begin = s;
+                ra.s_end = s + 1;
+                if (launch_rec(ra, sch.tile, p->dtype, false, st) != hipSuccess) {
+                    (void)hipGetLastError();
+                    return LSTM_ERR_LAUNCH;
+                }
+            }
+        }
+        span_end(p, span, st, stepped ? T : 1);
+    }
+    if (p->timing) p->acc.calls += 1;
+    return LSTM_OK;
+}
+
+lstm_status lstm_device_status(const void *workspace, size_t workspace_bytes, void *stream,
+                               unsigned *device_flags) {
+    if (!workspace || !device_flags || workspace_bytes < kStatusBytes) return LSTM_ERR_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    unsigned v = 0;
+    if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    *device_flags = v;
+    return v ? LSTM_ERR_DEVICE_TIMEOUT : LSTM_OK;
+}
+
+}  // extern "C"

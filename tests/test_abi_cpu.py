@@ -1,0 +1,145 @@
+"""The C ABI without a GPU: the library loads, exports every function declared
+in include/lstm.h, and its host-side checks return the documented status codes
+before anything touches a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import layer_lstm_forward_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lstm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pkg.LIB_PATH), reason="liblstm_amd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lstm_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"lstm_create", "lstm_forward", "lstm_destroy", "lstm_workspace_size"} <= set(names)
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in lstm.h but not exported"
+
+
+def test_version_and_strerror():
+    assert pkg.lstm_version() == 100
+    for code in pkg.STATUS:
+        assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
+    assert pkg.lstm_strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("args,code", [
+    ((8, 16, 0, 0, 1, 0), -1),    # fewer than one layer
+    ((0, 16, 1, 0, 1, 0), -1),
+    ((8, 0, 1, 0, 1, 0), -1),
+    ((8, 16, 1, 2, 1, 0), -1),    # bidirectional not 0/1
+    ((8, 16, 1, 0, 3, 0), -1),
+    ((8, 16, 1, 0, 1, 7), -3),    # dtype
+])
+def test_create_errors(args, code):
+    lib = pkg.load_library()
+    h = ctypes.c_void_p(1)
+    assert lib.lstm_create(ctypes.byref(h), *args) == code
+    assert h.value is None
+    assert lib.lstm_create(None, 8, 16, 1, 0, 1, 0) == -1
+
+
+def test_workspace_size_layout():
+    p1 = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    p3 = pkg.lstm_create(8, 16, 3, True, True, pkg.LSTM_BF16)
+    try:
+        a = pkg.lstm_workspace_size(p1, 5, 1)
+        b = pkg.lstm_workspace_size(p1, 10, 1)
+        assert 0 < a < b
+        # G holds T*B*D*4H fp32 values
+        assert b - a >= 5 * 4 * 16 * 4
+        c = pkg.lstm_workspace_size(p3, 5, 2)
+        assert c > 2 * 5 * 2 * 2 * 16 * 2  # two intermediate outputs of [T,B,D*H] bf16
+        with pytest.raises(pkg.LSTMError) as e:
+            pkg.lstm_workspace_size(p1, 0, 1)
+        assert e.value.status == -2
+    finally:
+        pkg.lstm_destroy(p1)
+        pkg.lstm_destroy(p3)
+
+
+def test_set_option():
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        pkg.lstm_set_option(p, pkg.LSTM_OPT_RECURRENCE, pkg.LSTM_REC_STEP)
+        pkg.lstm_set_option(p, pkg.LSTM_OPT_REC_TILE, 412)
+        for opt, val in ((pkg.LSTM_OPT_RECURRENCE, 9), (pkg.LSTM_OPT_REC_TILE, 333), (99, 0)):
+            with pytest.raises(pkg.LSTMError) as e:
+                pkg.lstm_set_option(p, opt, val)
+            assert e.value.status == -7
+    finally:
+        pkg.lstm_destroy(p)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails host validation first
+
+
+def _fwd(plan, **kw):
+    a = dict(x=FAKE, h0=0, c0=0, weights=[FAKE] * 4, T=5, B=1, layers=1, bidir=False, y=FAKE, h_n=0, c_n=0,
+             workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+    a.update(kw)
+    return pkg.lstm_forward(plan, a["x"], a["h0"], a["c0"], a["weights"], a["T"], a["B"], a["layers"],
+                            a["bidir"], a["y"], a["h_n"], a["c_n"], a["workspace"], a["workspace_bytes"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layers=2), -2),
+    (dict(bidir=True), -2),
+    (dict(T=0), -2),
+    (dict(B=0), -2),
+    (dict(B=-3), -2),
+    (dict(x=0), -1),
+    (dict(y=0), -1),
+    (dict(h0=FAKE), -1),             # h0 without c0
+    (dict(c0=FAKE), -1),             # c0 without h0
+    (dict(weights=[FAKE, 0, FAKE, FAKE]), -1),
+    (dict(workspace=0), -5),
+    (dict(workspace_bytes=64), -5),
+])
+def test_forward_host_validation(kw, code):
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        assert _fwd(p, **kw) == code
+    finally:
+        pkg.lstm_destroy(p)
+
+
+def test_forward_null_plan():
+    assert _fwd(None) == -1
+
+
+def test_forward_weights_count_follows_bias_flag():
+    p = pkg.lstm_create(8, 16, 1, False, False, pkg.LSTM_F32)
+    try:
+        # without biases only W_ih and W_hh are read: two entries pass the
+        # NULL check and reach the device check; a NULL second entry does not
+        assert _fwd(p, weights=[FAKE, FAKE]) == -4
+        assert _fwd(p, weights=[FAKE, 0]) == -1
+    finally:
+        pkg.lstm_destroy(p)
+
+
+def test_forward_rejects_non_device_pointers():
+    """Valid shapes but pointers that are not device memory (or no device at
+    all): LSTM_ERR_DEVICE, before any launch."""
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        host = (ctypes.c_float * 64)()
+        addr = ctypes.addressof(host)
+        assert _fwd(p, x=addr, y=addr, workspace=addr, weights=[addr] * 4) == -4
+    finally:
+        pkg.lstm_destroy(p)

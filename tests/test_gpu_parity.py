@@ -1,0 +1,140 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (max-abs over y, h_n, c_n): 1e-4 for fp32 weights, 2e-2 for bf16
+weights with an fp32 cell.  Small shapes span several tiles with ragged tails
+and are checked element by element; the benchmark workloads run at full size
+in the schedule the benchmark times, and the oracle recomputes a sample of
+batch rows (rows are independent, so a row subset run alone is exact).
+"""
+import numpy as np
+import pytest
+
+import layer_lstm_forward_amd as pkg
+from layer_lstm_forward_amd.synth import WORKLOADS, Spec, make_inputs
+from tests.gpu_util import assert_parity, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    Spec(37, 52, 2, True, 9, 19, "f32", 101, "normal0.1"),    # ragged H, I, two batch groups
+    Spec(13, 13, 1, False, 7, 3, "f32", 102, "normal0.1"),    # H % 4 != 0: element-wise loads
+    Spec(70, 40, 3, False, 6, 33, "bf16", 103, "normal0.1"),  # three layers, partial K chunk
+    Spec(64, 96, 2, True, 11, 5, "bf16", 104, "zeros"),
+    Spec(5, 7, 1, True, 4, 2, "f32", 105, "zeros", has_bias=False),
+    Spec(200, 264, 1, False, 12, 40, "f32", 106),
+    Spec(256, 200, 2, True, 8, 70, "bf16", 107, "normal0.1"),
+    Spec(1, 1, 1, False, 1, 1, "f32", 108, "normal0.1"),      # degenerate: one unit, one step
+]
+TILES = [0, 411, 412, 414, 211, 212, 214, 111, 112, 114, 141, 142, 144]
+
+
+def _id(s):
+    return f"{s.dtype}-I{s.input_size}-H{s.hidden_size}-L{s.num_layers}-D{s.D}-T{s.T}-B{s.B}"
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=_id)
+@pytest.mark.parametrize("mode", [pkg.LSTM_REC_STEP, pkg.LSTM_REC_AUTO], ids=["step", "auto"])
+def test_small_shapes(spec, mode):
+    print(f"case {_id(spec)} mode {mode}", flush=True)
+    inp = make_inputs(spec)
+    got, m = run_gpu(inp, recurrence=mode)
+    ref = run_oracle(inp)
+    assert_parity(got, ref, spec.dtype, m.describe(spec.T, spec.B))
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("spec", [Spec(48, 72, 2, True, 7, 37, "f32", 201, "normal0.1"),
+                                  Spec(96, 136, 1, False, 6, 21, "bf16", 202, "normal0.1")], ids=_id)
+def test_every_tile_persistent_equals_step(spec, tile):
+    """Each recurrent tile gives oracle parity, and the persistent launch
+    (step barriers inside one kernel) equals one-launch-per-step bit for bit."""
+    print(f"case {_id(spec)} tile {tile}", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    step, m = run_gpu(inp, recurrence=pkg.LSTM_REC_STEP, rec_tile=tile)
+    assert_parity(step, ref, spec.dtype, m.describe(spec.T, spec.B))
+    try:
+        pers, m2 = run_gpu(inp, recurrence=pkg.LSTM_REC_PERSISTENT, rec_tile=tile)
+    except pkg.LSTMError as e:
+        assert e.status == -7  # this tile does not fit as one persistent launch
+        return
+    assert "persistent" in m2.describe(spec.T, spec.B)
+    for a, b in zip(step, pers):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_repeat_runs_bitwise_identical():
+    spec = Spec(64, 128, 2, True, 10, 20, "bf16", 301, "normal0.1")
+    inp = make_inputs(spec)
+    a, m = run_gpu(inp)
+    b, _ = run_gpu(inp, model=m, repeat=3)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_weights_closed_form_on_gpu(dtype):
+    """All weights zero: c_n = f^n c0 + i g (1 - f^n) / (1 - f), h = o tanh(c)."""
+    spec = Spec(16, 32, 2, True, 6, 4, dtype, 401, "normal0.1")
+    inp = make_inputs(spec)
+    H, D, L, T = 32, 2, 2, 6
+    inp.params = [np.zeros_like(p) if k % 4 < 2 else p for k, p in enumerate(inp.params)]
+    got, _ = run_gpu(inp)
+    if dtype == "bf16":
+        from layer_lstm_forward_amd.synth import bf16_bits_to_f32 as widen
+    else:
+        widen = np.asarray
+    sig = lambda z: 1 / (1 + np.exp(-z))  # noqa: E731
+    c0 = inp.c0.astype(np.float64)
+    y, hn, cn = got
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for l in range(L):
+        for d in range(D):
+            b = widen(inp.params[(l * D + d) * 4 + 2]).astype(np.float64) + \
+                widen(inp.params[(l * D + d) * 4 + 3]).astype(np.float64)
+            i, f, g, o = sig(b[:H]), sig(b[H:2 * H]), np.tanh(b[2 * H:3 * H]), sig(b[3 * H:])
+            for n, t in [(T, None)] + [((t + 1) if d == 0 else (T - t), t) for t in range(T)]:
+                cc = f ** n * c0[l * D + d] + i * g * (1 - f ** n) / (1 - f)
+                if t is None:
+                    np.testing.assert_allclose(cn[l * D + d], cc, atol=tol, rtol=0)
+                    np.testing.assert_allclose(hn[l * D + d], o * np.tanh(cc), atol=tol, rtol=0)
+                elif l == L - 1:
+                    np.testing.assert_allclose(y[t, :, d * H:(d + 1) * H], o * np.tanh(cc), atol=tol, rtol=0)
+
+
+def _full(name, rows):
+    spec = WORKLOADS[name]
+    print(f"case {name} rows {rows}", flush=True)
+    inp = make_inputs(spec)
+    got, m = run_gpu(inp)
+    desc = m.describe(spec.T, spec.B)
+    y, hn, cn = got
+    assert np.all(np.isfinite(y)) and np.all(np.abs(y) <= 1.0)
+    if rows is None:
+        ref = run_oracle(inp)
+        return assert_parity(got, ref, spec.dtype, f"{name}: {desc}")
+    sub = inp.rows(rows)
+    ref = run_oracle(sub)
+    return assert_parity((y[:, rows], hn[:, rows], cn[:, rows]), ref, spec.dtype, f"{name}: {desc}")
+
+
+def test_full_tiny_l1_in8_h16():
+    _full("l1_in8_h16_t5_b1_f32", None)
+
+
+def test_full_l2_in256_h512_b64_f32_sampled_rows():
+    _full("l2_in256_h512_t128_b64_f32", [0, 37, 63])
+
+
+def test_full_l2bi_in512_h1024_b32_bf16_sampled_rows():
+    _full("l2bi_in512_h1024_t256_b32_bf16", [0, 17, 31])
+
+
+@pytest.mark.parametrize("name", ["l1_in1024_h1024_t1024_b1_bf16", "l1_in1024_h1024_t1024_b4_bf16"])
+def test_full_l1_h1024_t1024_small_batch(name):
+    _full(name, None)
+
+
+@pytest.mark.slow
+def test_full_l4_in2048_h2048_b256_bf16_sampled_rows():
+    _full("l4_in2048_h2048_t512_b256_bf16", [0, 201])
