@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--recurrence", choices=["auto", "step", "persistent"], default="auto")
     ap.add_argument("--rec-tile", type=int, default=0)
+    ap.add_argument("--partial-buffers", type=int, default=0)
+    ap.add_argument("--poll-sleep", type=int, default=-1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -116,8 +118,13 @@ def main():
     h0 = to_dev(inp.h0)
     c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
     rec = {"auto": pkg.LSTM_REC_AUTO, "step": pkg.LSTM_REC_STEP, "persistent": pkg.LSTM_REC_PERSISTENT}
+    opts = {}
+    if args.partial_buffers:
+        opts[pkg.LSTM_OPT_PARTIAL_BUFFERS] = args.partial_buffers
+    if args.poll_sleep >= 0:
+        opts[pkg.LSTM_OPT_POLL_SLEEP] = args.poll_sleep
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
-                 dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile)
+                 dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile, options=opts)
     desc = m.describe(spec.T, spec.B)
     log(f"schedule: {desc}")
     out = (torch.empty(spec.T, spec.B, spec.D * spec.hidden_size, dtype=x.dtype, device=dev),

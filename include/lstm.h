@@ -78,7 +78,9 @@ typedef enum {
 typedef enum {
     LSTM_OPT_RECURRENCE = 1, /* value: lstm_recurrence */
     LSTM_OPT_REC_TILE = 2,   /* value: 0 = automatic, else 100*WK + 10*MTW + NT (see lstm_describe) */
-    LSTM_OPT_TIMING = 3      /* value 1: record HIP events around each phase (see lstm_read_timing) */
+    LSTM_OPT_TIMING = 3,     /* value 1: record HIP events around each phase (see lstm_read_timing) */
+    LSTM_OPT_PARTIAL_BUFFERS = 4, /* 1 (default) or 2 LDS partial-sum buffers in the recurrent kernel */
+    LSTM_OPT_POLL_SLEEP = 5  /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset

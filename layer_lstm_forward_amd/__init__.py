@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "liblstm_amd.so")
 LSTM_F32, LSTM_BF16 = 0, 1
 LSTM_REC_AUTO, LSTM_REC_STEP, LSTM_REC_PERSISTENT = 0, 1, 2
 LSTM_OPT_RECURRENCE, LSTM_OPT_REC_TILE, LSTM_OPT_TIMING = 1, 2, 3
+LSTM_OPT_PARTIAL_BUFFERS, LSTM_OPT_POLL_SLEEP = 4, 5
 STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
           -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
           -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}
@@ -153,7 +154,7 @@ class LSTM:
     """
 
     def __init__(self, input_size, hidden_size, num_layers=1, bidirectional=False, bias=True,
-                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0):
+                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None):
         self.input_size, self.hidden_size = int(input_size), int(hidden_size)
         self.num_layers, self.bidirectional, self.bias = int(num_layers), bool(bidirectional), bool(bias)
         self.dtype = dtype
@@ -164,6 +165,8 @@ class LSTM:
             lstm_set_option(self.plan, LSTM_OPT_RECURRENCE, recurrence)
         if rec_tile:
             lstm_set_option(self.plan, LSTM_OPT_REC_TILE, rec_tile)
+        for opt, val in (options or {}).items():
+            lstm_set_option(self.plan, opt, val)
         self._ws = None
 
     def __del__(self):

@@ -1,6 +1,6 @@
 // device.h -- device-side building blocks shared by the gfx950 kernels:
 // element traits, 16-byte fragment loads, MFMA chunk products, the gate
-// nonlinearities and the cross-workgroup step barrier.
+// nonlinearities and the tagged hidden-state exchange between workgroups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,51 +73,37 @@ __device__ inline float sigmoid_f(float z) {
 __device__ inline float tanh_f(float z) { return 2.0f * sigmoid_f(2.0f * z) - 1.0f; }
 
 // ---------------------------------------------------------------------------
-// Step barrier between the workgroups that exchange one direction's hidden
-// state.  Each workgroup adds 1 to its team counter after publishing a step;
-// a consumer waits until the counter reaches (members * steps).  Counters only
-// grow within one launch, so no reset is needed between steps.
-//
-// Memory ordering: every thread that stored part of h_t issues an agent-scope
-// release fence before the workgroup barrier, and thread 0 then bumps the
-// counter; the waiting side observes the counter with agent-scope loads and
-// every thread issues an agent-scope acquire fence before reading h_t.
-//
-// The wait is bounded in wall-clock time: on expiry it raises bit 0 of the
-// status word and every waiter leaves, so a launch always drains.
+// Hidden-state exchange between workgroups.  h_t travels as 64-bit words whose
+// high half is a step tag and whose low half carries the value (one fp32, or
+// two bf16 of adjacent units).  Producers store them with agent-scope atomic
+// stores and consumers read them with agent-scope atomic loads; on gfx950 both
+// are single 64-bit accesses performed at the device coherence point (the
+// "sc1" scope bits), so a word is seen either whole-old or whole-new, from any
+// XCD, without cache write-back or invalidation.  A consumer simply re-reads
+// each word until it carries the tag it expects: the arrival of the data is
+// the synchronisation, and no counter or barrier is involved.
 // ---------------------------------------------------------------------------
-__device__ inline void step_publish(unsigned *ctr) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline unsigned long long xload(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline void xstore(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned long long xword(unsigned tag, uint32_t payload) {
+    return ((unsigned long long)tag << 32) | payload;
+}
+__device__ inline unsigned xtag(unsigned long long w) { return (unsigned)(w >> 32); }
 
-__device__ inline bool step_wait(const unsigned *ctr, unsigned target, unsigned *status,
-                                 long long timeout_ticks, int *s_flag) {
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        unsigned it = 0;
-        const long long t0 = wall_clock64();
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if ((++it & 127u) == 0) {
-                if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                    ok = 0;
-                    break;
-                }
-                if (wall_clock64() - t0 > timeout_ticks) {
-                    __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = 0;
-                    break;
-                }
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        *s_flag = ok;
-    }
-    __syncthreads();
-    const int ok = *s_flag;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return ok != 0;
+// Two adjacent tagged words in one 16-byte agent-scope ("sc1") buffer load.
+// Each 8-byte word carries its own tag, so only 8-byte single-copy atomicity
+// of the halves is relied on.  Offsets at or past the resource size return
+// zeros without a memory access.
+__device__ inline __amdgpu_buffer_rsrc_t xrsrc(const unsigned long long *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned long long *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ inline u32x4 xload2(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1: device scope */);
 }
 
 }  // namespace lstm_amd

@@ -28,26 +28,29 @@ struct RecArgs {
     const float *G;          // [T, B, D*4H] projection incl. both biases
     const void *h0;          // [D, B, H] dtype for this layer, or NULL (zeros)
     const float *c0;         // [D, B, H] or NULL
-    void *Y;                 // [T, B, D*H] dtype, written (also read as h_{t-1})
+    void *Y;                 // [T, B, D*H] dtype, written
     void *hn;                // [D, B, H] dtype or NULL
     float *cn;               // [D, B, H] or NULL
     float *cstate;           // [D, B, H] carry between step launches
-    unsigned *ctr;           // team counters, stride kCtrStride words
+    unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 tagged words
+    unsigned tag_base;       // tags of this layer are tag_base + s + 1
     unsigned *status;        // error word
     int T, B, H, D;
     int P;                   // workgroups per team (hidden-unit slices)
     int BG;                  // batch rows per team
     int NGB;                 // batch groups
     int kch;                 // K chunks of H
+    int kchp;                // chunks resident in LDS (kch padded to whole batches per wave)
+    int nbatch;              // chunk batches per wave
+    int part_bufs;           // 1 or 2 partial-sum buffers in LDS
+    int poll_sleep;          // s_sleep units (64 clocks each) between re-reads of stale words
     int s_begin, s_end;      // steps handled by this launch
-    int persistent;          // 1: all steps in this launch with step barriers
     int map_xcd;             // 1: place a team's workgroups on the same XCDs
     int vec;                 // 16-byte vector loads are aligned
-    long long timeout_ticks; // barrier timeout in wall_clock64 ticks
+    long long timeout_ticks; // wait timeout in wall_clock64 ticks
 };
 
-constexpr int kCtrStride = 32;       // 128 bytes between counters
-constexpr int kMaxTeams = 64;        // counters per layer
+constexpr int kMaxTeams = 64;
 
 // Recurrent tile: 4 waves split (4/WK) ways over batch tiles and WK ways over
 // K; each wave owns MTW 16-row batch tiles; NT 16-column tiles of gate rows
@@ -56,13 +59,20 @@ struct RecTile {
     int WK, MTW, NT;
 };
 
-size_t rec_smem_bytes(RecTile t, int H, int dtype);
+constexpr size_t kRecLdsLimit = 160 * 1024 - 64;  // leaves room for static LDS
+
+// LDS geometry of a recurrent tile for hidden size H.
+struct RecGeom {
+    int kch, kchp, nbatch, part_bufs;
+    size_t smem;
+};
+RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers);
 int rec_rows_per_wg(RecTile t);
 bool rec_tile_supported(RecTile t);
 
 hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s);
-hipError_t launch_rec(const RecArgs &a, RecTile t, int dtype, bool cooperative, hipStream_t s);
-hipError_t rec_max_coresident(RecTile t, int H, int dtype, int *blocks_per_cu);
+hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
 
 }  // namespace lstm_amd

@@ -14,8 +14,9 @@
 //           (same equation block) fused into the epilogue; the reverse
 //           direction runs in the same launch on its own workgroups.  Either
 //           one launch per step, or one persistent launch per layer with the
-//           W_hh slices resident in LDS and a step barrier between steps.
-//   k_fill  fills synchronisation words.
+//           W_hh slices resident in LDS; workgroups hand h_t to each other
+//           through step-tagged words instead of a grid barrier.
+//   k_fill  clears the status word and the exchange buffer.
 #include "device.h"
 #include "kernels.h"
 
@@ -130,19 +131,21 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 // 4U rows {q*H + j : q in i,f,g,o} of W_hh, kept in LDS as MFMA fragments
 // (gate rows interleaved: local column n = 4*u + q).  Per step:
 //   1. prefetch the projection G[t] for the cells this thread updates;
-//   2. (persistent) wait until the team has published h_{t-1};
-//   3. S = h_{t-1} W_slice^T: the four waves split over batch tiles and K,
-//      reading h_{t-1} fragments straight from global memory;
-//   4. partial sums meet in LDS; each thread reduces the four gate
-//      pre-activations of its cells, applies sigma/tanh, updates c (kept in
-//      registers across steps) and writes h_t to y (and h_n, c_n at the end);
-//   5. (persistent) publish the step to the team.
-// h_t is exchanged through y itself: the next step reads y[t-1] (forward) or
-// y[t+1] (reverse), so no separate exchange buffer exists.
+//   2. S = h_{t-1} W_slice^T: the four waves split over batch tiles and K;
+//      each wave fetches its h_{t-1} fragments from the tagged exchange
+//      buffer (re-reading words until they carry step t-1's tag; at t = 0
+//      plain loads of h0) and feeds them to the matrix cores;
+//   3. partial sums meet in LDS; each thread reduces the gate pre-activations
+//      of a pair of adjacent units of one batch row, applies sigma/tanh,
+//      updates c (kept in registers across steps) and writes h_t to y, to the
+//      exchange buffer with the next tag, and at the end to h_n and c_n.
+// One launch can run every step of the layer (persistent: all workgroups must
+// be co-resident, which the cooperative launch guarantees) or just one.
 // ===========================================================================
-template <class DT, int WK, int MTW, int NT>
+template <class DT, int WK, int MTW, int NT, int CB>
 __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     using S = typename DT::S;
+    constexpr bool BF = sizeof(S) == 2;
     constexpr int WM = 4 / WK;
     constexpr int MT = WM * MTW;
     constexpr int ROWS = 16 * MT;
@@ -151,10 +154,12 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     constexpr int PSTR = NCOL + 4;
     constexpr int CELLS = ROWS * U;
     constexpr int CPT = (CELLS + 255) / 256;
+    constexpr int EW = BF ? 2 : 1;  // K values per exchange word
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_flag;
+    __shared__ int s_bad;
     u32x4 *Wf = reinterpret_cast<u32x4 *>(smem);
-    float *part = reinterpret_cast<float *>(smem + (size_t)a.kch * NT * 1024);
+    float *part0 = reinterpret_cast<float *>(smem + (size_t)a.kchp * NT * 1024);
+    const size_t part_stride = (size_t)WK * ROWS * PSTR;  // floats per partial buffer
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w / WK, wk = w % WK;
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             p = bid % a.P;
         }
     }
-    const int H = a.H, B = a.B, T = a.T, D = a.D;
+    const int H = a.H, B = a.B, T = a.T, D = a.D, kch = a.kch;
     const int d = team % D, gb = team / D;
     const int b0 = gb * a.BG, rows = min(a.BG, B - b0);
     const int j0 = p * U, units = min(U, H - j0);
@@ -179,20 +184,23 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     const size_t ldg = (size_t)D * 4 * H;
     const bool vec = a.vec != 0;
 
-    // Resident W_hh slice as fragments: [chunk][n-tile][lane] x 16 bytes.
+    // Resident W_hh slice as fragments: [chunk][n-tile][lane] x 16 bytes,
+    // zero beyond H and for the padding chunks up to kchp.
     {
         const S *W = static_cast<const S *>(a.whh[d]);
-        const int nfrag = a.kch * NT * 64;
+        const int nfrag = a.kchp * NT * 64;
         for (int f = tid; f < nfrag; f += 256) {
             const int ln = f & 63, nt = (f >> 6) % NT, c = (f >> 6) / NT;
             const int n = nt * 16 + (ln & 15), u = n >> 2, q = n & 3;
             const int k = c * DT::KC + (ln >> 4) * DT::PER16;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (u < units) v = load_frag<DT>(W + (size_t)(q * H + j0 + u) * H, k, H, vec);
+            if (u < units && k < H) v = load_frag<DT>(W + (size_t)(q * H + j0 + u) * H, k, H, vec);
             Wf[f] = v;
         }
     }
 
+    // Cells of this thread: (batch row cm, hidden unit cu); adjacent lanes hold
+    // adjacent units of one row.
     int cm[CPT], cu[CPT];
     bool cv[CPT];
     float creg[CPT];
@@ -209,62 +217,160 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             else creg[i] = a.cstate[si];
         }
     }
+    if (tid == 0) s_bad = 0;
+
+    // G[t] of this thread's cells, loaded two steps ahead: older loads hold
+    // up the in-order wait on the exchange loads, so they are issued early.
+    float gcur[CPT][4], gnext[CPT][4];
+    auto load_g = [&](int step, float (&g)[CPT][4]) {
+        const int tg = d == 0 ? step : T - 1 - step;
+        const bool in = step < a.s_end;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const bool ok = in && cv[i];
+            const float *gp = a.G + ((size_t)(ok ? tg : 0) * B + b0 + (ok ? cm[i] : 0)) * ldg + (size_t)d * 4 * H +
+                              j0 + (ok ? cu[i] : 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[i][q] = ok ? gp[(size_t)q * H] : 0.f;
+        }
+    };
+    load_g(a.s_begin, gcur);
+    load_g(a.s_begin + 1, gnext);
     __syncthreads();
 
-    unsigned *ctr = a.ctr + team * kCtrStride;
-    const int cpw = (a.kch + WK - 1) / WK;
-    const int cb = wk * cpw, ce = min(a.kch, cb + cpw);
+    const int nb = a.nbatch;                       // chunk batches per wave
+    const int cw0 = wk * nb * CB;                  // first chunk of this wave
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int mw = wm * MTW * 16 + (lane & 15);    // this lane's team row in tile i: mw + 16 i
+    const int ksub = (lane >> 4) * DT::PER16;      // this lane's K offset inside a chunk
+    const size_t region = (size_t)MT * kch * 256;  // exchange words per team
 
     for (int s = a.s_begin; s < a.s_end; ++s) {
         const int t = d == 0 ? s : T - 1 - s;
-
-        float g[CPT][4];
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const float *gp = a.G + ((size_t)t * B + b0 + cm[i]) * ldg + (size_t)d * 4 * H + j0 + cu[i];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) g[i][q] = cv[i] ? gp[(size_t)q * H] : 0.f;
-        }
-
-        if (a.persistent && s > a.s_begin) {
-            if (!step_wait(ctr, (unsigned)(a.P * (s - a.s_begin)), a.status, a.timeout_ticks, &s_flag))
-                return;
-        }
-
-        const S *hsrc = nullptr;
-        size_t hld = 0;
-        if (s == 0) {
-            if (a.h0) {
-                hsrc = static_cast<const S *>(a.h0) + (size_t)d * B * H;
-                hld = (size_t)H;
-            }
-        } else {
-            const int tp = d == 0 ? t - 1 : t + 1;
-            hsrc = static_cast<const S *>(a.Y) + (size_t)tp * B * ldy + (size_t)d * H;
-            hld = ldy;
-        }
+        float *part = part0 + (a.part_bufs == 2 ? (size_t)(s & 1) * part_stride : 0);
 
         f32x4 acc[MTW][NT];
 #pragma unroll
         for (int i = 0; i < MTW; ++i)
 #pragma unroll
             for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bool wave_ok = true;
 
-        if (hsrc) {
-            for (int c = cb; c < ce; ++c) {
-                u32x4 af[MTW];
-                const int k = c * DT::KC + (lane >> 4) * DT::PER16;
+        if (s == 0) {
+            if (a.h0) {
+                const S *hs = static_cast<const S *>(a.h0) + (size_t)d * B * H;
+                for (int c = cw0; c < cw0 + nb * CB; ++c) {
+                    u32x4 af[MTW];
+                    const int k = c * DT::KC + ksub;
 #pragma unroll
-                for (int i = 0; i < MTW; ++i) {
-                    const int m = (wm * MTW + i) * 16 + (lane & 15);
-                    af[i] = (m < rows) ? load_frag<DT>(hsrc + (size_t)(b0 + m) * hld, k, H, vec) : zero;
+                    for (int i = 0; i < MTW; ++i) {
+                        const int m = mw + 16 * i;
+                        af[i] = (m < rows && k < H) ? load_frag<DT>(hs + (size_t)(b0 + m) * H, k, H, vec) : zero;
+                    }
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const u32x4 bw = Wf[(c * NT + j) * 64 + lane];
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
+                    }
+                }
+            }
+        } else {
+            const unsigned tag = a.tag_base + (unsigned)s;  // written at step s-1
+            const unsigned long long ready = (unsigned long long)tag << 32;
+            const __amdgpu_buffer_rsrc_t xr =
+                xrsrc(a.xbuf + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * region, (unsigned)(region * 8));
+            for (int bi = 0; bi < nb && wave_ok; ++bi) {
+                const int c0 = cw0 + bi * CB;
+                // Each lane reads its fragment as two 16-byte pairs of tagged
+                // words; for a fixed pair index the 64 lanes read 1 KB in a row.
+                // wd[..][eh] holds words e = 2*eh, 2*eh+1 of the fragment.
+                u32x4 wd[CB][MTW][2];
+                unsigned off[CB][MTW][2];
+                bool lv[CB][MTW][4];
+#pragma unroll
+                for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) {
+                        const int c = c0 + ci, m = mw + 16 * i;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lv[ci][i][e] = m < rows && c * DT::KC + ksub + e * EW < H;
+#pragma unroll
+                        for (int eh = 0; eh < 2; ++eh)
+                            off[ci][i][eh] = lv[ci][i][2 * eh]
+                                                 ? (unsigned)(((((wm * MTW + i) * kch + c) * 2 + eh) * 128 + 2 * lane) * 8)
+                                                 : 0x7FFFFFF0u;  // out of range: reads zeros, no memory access
+                    }
+#pragma unroll
+                for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                        for (int eh = 0; eh < 2; ++eh) wd[ci][i][eh] = xload2(xr, off[ci][i][eh]);
+                // a dead word (padding row or K past H) counts as ready and zero
+                auto settle = [&](int ci, int i, int eh) {
+                    if (!lv[ci][i][2 * eh]) { wd[ci][i][eh].x = 0u; wd[ci][i][eh].y = tag; }
+                    if (!lv[ci][i][2 * eh + 1]) { wd[ci][i][eh].z = 0u; wd[ci][i][eh].w = tag; }
+                };
+                auto pair_ok = [&](int ci, int i, int eh) { return wd[ci][i][eh].y == tag && wd[ci][i][eh].w == tag; };
+                bool mine = true;
+#pragma unroll
+                for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                        for (int eh = 0; eh < 2; ++eh) {
+                            settle(ci, i, eh);
+                            mine = mine && pair_ok(ci, i, eh);
+                        }
+                if (!__all(mine)) {
+                    // slow path: back off, then re-read only the pairs that are stale
+                    unsigned spins = 0;
+                    const long long t0 = wall_clock64();
+                    do {
+                        if ((++spins & 31u) == 0) {
+                            const unsigned st = __builtin_amdgcn_readfirstlane(
+                                __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                            if (st != 0u) {
+                                wave_ok = false;
+                                break;
+                            }
+                            if (wall_clock64() - t0 > a.timeout_ticks) {
+                                if (lane == 0)
+                                    __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                                wave_ok = false;
+                                break;
+                            }
+                        }
+                        for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
+                        mine = true;
+#pragma unroll
+                        for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                            for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                                for (int eh = 0; eh < 2; ++eh) {
+                                    if (!pair_ok(ci, i, eh)) {
+                                        wd[ci][i][eh] = xload2(xr, off[ci][i][eh]);
+                                        settle(ci, i, eh);
+                                    }
+                                    mine = mine && pair_ok(ci, i, eh);
+                                }
+                    } while (!__all(mine));
+                    if (!wave_ok) break;
                 }
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const u32x4 bw = Wf[(c * NT + j) * 64 + lane];
+                for (int ci = 0; ci < CB; ++ci) {
+                    u32x4 bw[NT];
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
+                    for (int j = 0; j < NT; ++j) bw[j] = Wf[((c0 + ci) * NT + j) * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) {
+                        const u32x4 af = {wd[ci][i][0].x, wd[ci][i][0].z, wd[ci][i][1].x, wd[ci][i][1].z};
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mma_chunk(DT{}, acc[i][j], af, bw[j]);
+                    }
                 }
             }
         }
@@ -279,34 +385,66 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                     const int n = j * 16 + (lane & 15);
                     part[(wk * ROWS + m) * PSTR + n] = acc[i][j][v];
                 }
+        if (!wave_ok) s_bad = 1;
         __syncthreads();
+        if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
 
+        const unsigned long long tag_out = (unsigned long long)(a.tag_base + (unsigned)s + 1u) << 32;
+        unsigned long long *xo = a.xbuf + ((size_t)((s & 1) * D + d) * a.NGB + gb) * region;
+        const bool publish = s + 1 < T;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            if (!cv[i]) continue;
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(&part[(cm[i]) * PSTR + 4 * cu[i]]);
+            // every lane of the wave takes part in the shuffle below
+            float hv = 0.f;
+            S hs = (S)0;
+            if (cv[i]) {
+                const float *pp = &part[cm[i] * PSTR + 4 * cu[i]];
+                f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
 #pragma unroll
-            for (int kk = 1; kk < WK; ++kk)
-                sum += *reinterpret_cast<const f32x4 *>(&part[(kk * ROWS + cm[i]) * PSTR + 4 * cu[i]]);
-            const float ig = sigmoid_f(sum.x + g[i][0]);
-            const float fg = sigmoid_f(sum.y + g[i][1]);
-            const float gg = tanh_f(sum.z + g[i][2]);
-            const float og = sigmoid_f(sum.w + g[i][3]);
-            const float cn = fg * creg[i] + ig * gg;
-            const float hv = og * tanh_f(cn);
-            creg[i] = cn;
-            const S hs = DT::from_f(hv);
-            const int bb = b0 + cm[i], jj = j0 + cu[i];
-            static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = hs;
-            if (s == T - 1) {
-                const size_t si = ((size_t)d * B + bb) * H + jj;
-                if (a.hn) static_cast<S *>(a.hn)[si] = hs;
-                if (a.cn) a.cn[si] = cn;
+                for (int kk = 1; kk < WK; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
+                const float ig = sigmoid_f(sum.x + gcur[i][0]);
+                const float fg = sigmoid_f(sum.y + gcur[i][1]);
+                const float gg = tanh_f(sum.z + gcur[i][2]);
+                const float og = sigmoid_f(sum.w + gcur[i][3]);
+                const float cn = fg * creg[i] + ig * gg;
+                creg[i] = cn;
+                hv = og * tanh_f(cn);
+                hs = DT::from_f(hv);
+            }
+            // word of (team row m, k) in the consumers' order:
+            // ((tile * kch + chunk) * 2 + e / 2) * 128 + 2 * lane + e % 2, lane = 16 * g + m % 16
+            const int m = cm[i], jj = j0 + cu[i];
+            if (BF) {
+                // units jj (even) and jj + 1 share a word; the even lane stores it
+                const uint32_t mine_bits = (uint32_t)(uint16_t)hs;
+                const uint32_t nb_bits = (uint32_t)__shfl_xor((int)mine_bits, 1);
+                if (publish && cv[i] && (cu[i] & 1) == 0) {
+                    const int c = jj >> 5, g = (jj >> 3) & 3, e = (jj >> 1) & 3;
+                    const uint32_t hi = cu[i] + 1 < units ? nb_bits : 0u;
+                    xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
+                           tag_out | (mine_bits | (hi << 16)));
+                }
+            } else if (publish && cv[i]) {
+                const int c = jj >> 4, g = (jj >> 2) & 3, e = jj & 3;
+                xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
+                       tag_out | __float_as_uint(hv));
+            }
+            if (cv[i]) {
+                const int bb = b0 + m;
+                static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = hs;
+                if (s == T - 1) {
+                    const size_t si = ((size_t)d * B + bb) * H + jj;
+                    if (a.hn) static_cast<S *>(a.hn)[si] = hs;
+                    if (a.cn) a.cn[si] = creg[i];
+                }
             }
         }
-
-        if (a.persistent && s + 1 < a.s_end) step_publish(ctr);
-        else __syncthreads();
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gcur[i][q] = gnext[i][q];
+        load_g(s + 2, gnext);
+        if (a.part_bufs != 2) __syncthreads();  // partials are reused by the next step
     }
 
     if (a.s_end < T) {
@@ -343,10 +481,23 @@ hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s) {
 
 int rec_rows_per_wg(RecTile t) { return 16 * (4 / t.WK) * t.MTW; }
 
-size_t rec_smem_bytes(RecTile t, int H, int dtype) {
+// Chunks fetched per batch by one wave: all of a K-split wave's chunks when
+// they fit in registers, two for the tall batch tiles.
+int rec_chunk_batch(RecTile t) { return t.MTW >= 4 ? 2 : 8; }
+
+RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers) {
+    RecGeom g{};
     const int kc = dtype == DT_BF16 ? 32 : 16;
-    const size_t kch = (size_t)(H + kc - 1) / kc;
-    return kch * t.NT * 1024 + (size_t)t.WK * rec_rows_per_wg(t) * (16 * t.NT + 4) * 4;
+    g.kch = (H + kc - 1) / kc;
+    const int cb = rec_chunk_batch(t);
+    const int cpw = (g.kch + t.WK - 1) / t.WK;
+    g.nbatch = (cpw + cb - 1) / cb;
+    g.kchp = t.WK * g.nbatch * cb;
+    const size_t wbytes = (size_t)g.kchp * t.NT * 1024;
+    const size_t pbytes = (size_t)t.WK * rec_rows_per_wg(t) * (16 * t.NT + 4) * 4;
+    g.part_bufs = (want_two_partial_buffers && wbytes + 2 * pbytes <= kRecLdsLimit) ? 2 : 1;
+    g.smem = wbytes + g.part_bufs * pbytes;
+    return g;
 }
 
 #define LSTM_REC_TILES(X) \
@@ -362,8 +513,9 @@ bool rec_tile_supported(RecTile t) {
 
 template <class DT>
 static const void *rec_kernel_ptr(RecTile t) {
-#define LSTM_T_PTR(wk, mtw, nt) \
-    if (t.WK == wk && t.MTW == mtw && t.NT == nt) return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt>);
+#define LSTM_T_PTR(wk, mtw, nt)                                                                    \
+    if (t.WK == wk && t.MTW == mtw && t.NT == nt)                                                  \
+        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8)>);
     LSTM_REC_TILES(LSTM_T_PTR)
 #undef LSTM_T_PTR
     return nullptr;
@@ -373,19 +525,17 @@ static const void *rec_kernel(RecTile t, int dtype) {
     return dtype == DT_BF16 ? rec_kernel_ptr<BF16>(t) : rec_kernel_ptr<F32>(t);
 }
 
-hipError_t rec_max_coresident(RecTile t, int H, int dtype, int *blocks_per_cu) {
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu) {
     const void *fn = rec_kernel(t, dtype);
     if (!fn) return hipErrorInvalidValue;
-    const size_t smem = rec_smem_bytes(t, H, dtype);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256, smem);
 }
 
-hipError_t launch_rec(const RecArgs &a, RecTile t, int dtype, bool cooperative, hipStream_t s) {
+hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s) {
     const void *fn = rec_kernel(t, dtype);
     if (!fn) return hipErrorInvalidValue;
-    const size_t smem = rec_smem_bytes(t, a.H, dtype);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     dim3 grid(a.NGB * a.D * a.P), block(256);

@@ -19,6 +19,8 @@ struct lstm_plan {
     int I, H, L, D, has_bias, dtype;
     int rec_mode;  // lstm_recurrence
     int rec_tile;  // 0 = automatic, else 100*WK + 10*MTW + NT
+    int part_bufs;   // partial-sum buffers requested (1 or 2)
+    int poll_sleep;  // back-off between re-reads of stale exchange words
     // optional per-phase timing (LSTM_OPT_TIMING)
     int timing;
     struct Span {
@@ -35,7 +37,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kStatusBytes = 256;
-constexpr size_t kLdsLimit = 160 * 1024 - 64;  // leaves room for static LDS
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 size_t elem_size(int dtype) { return dtype == LSTM_BF16 ? 2 : 4; }
@@ -48,22 +49,29 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 }
 
 struct Layout {
-    size_t status, counters, G, ymid[2], cstate, total;
-    size_t sync_bytes;  // status + counters, zeroed per call
+    size_t status, xbuf, G, ymid[2], cstate, total;
+    size_t sync_bytes;  // status + exchange buffer, zeroed per call
 };
 
 bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
-    size_t tb, g, y, st;
+    size_t tb, g, y, st, xb;
     if (!mul_ok((size_t)T, (size_t)B, &tb)) return false;
+    // exchange tags are l*(T+1) + s + 1 and must fit in 32 bits
+    if ((unsigned long long)p->L * ((unsigned long long)T + 1) >= 0xFFFFFFFFull) return false;
+    // exchange buffer: 2 parities x D directions x (padded team rows / 16)
+    // row tiles x kch chunks x 256 words; padded rows of all teams together
+    // never exceed B + 255
+    const size_t kch = (size_t)(p->H + (p->dtype == LSTM_BF16 ? 31 : 15)) / (p->dtype == LSTM_BF16 ? 32 : 16);
+    if (!mul_ok((size_t)2 * p->D * (((size_t)B + 255) / 16 + 1), kch * 256 * sizeof(unsigned long long), &xb))
+        return false;
     if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
-    const size_t ctr = (size_t)p->L * kMaxTeams * kCtrStride * sizeof(unsigned);
     size_t off = 0;
     o->status = off;
     off += kStatusBytes;
-    o->counters = off;
-    off += align_up(ctr);
+    o->xbuf = off;
+    off += align_up(xb);
     o->sync_bytes = off;
     o->G = off;
     if (g > SIZE_MAX / 2) return false;
@@ -83,6 +91,7 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
 struct Sched {
     bool persistent;
     RecTile tile;
+    RecGeom geom;
     int U, P, BG, NGB, teams, wgs, map_xcd;
     size_t smem;
 };
@@ -126,9 +135,10 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
     s->NGB = (B + s->BG - 1) / s->BG;
     s->teams = s->NGB * p->D;
     s->wgs = s->teams * s->P;
-    s->smem = rec_smem_bytes(t, p->H, p->dtype);
+    s->geom = rec_geom(t, p->H, p->dtype, p->part_bufs == 2);
+    s->smem = s->geom.smem;
     s->map_xcd = (s->teams <= 8 && 8 % s->teams == 0 && (s->wgs % 8) == 0) ? 1 : 0;
-    return s->teams <= kMaxTeams && s->smem <= kLdsLimit;
+    return s->teams <= kMaxTeams && s->smem <= kRecLdsLimit;
 }
 
 // Rough cycles per step of one workgroup: matrix-core work of the busiest
@@ -156,7 +166,7 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
         bool can_persist = false;
         if (!want_step && di.ok) {
             int bpc = 0;
-            if (rec_max_coresident(t, p->H, p->dtype, &bpc) == hipSuccess && bpc > 0)
+            if (rec_max_coresident(t, s.smem, p->dtype, &bpc) == hipSuccess && bpc > 0)
                 can_persist = (long long)bpc * di.cus >= s.wgs;
             (void)hipGetLastError();
         }
@@ -282,6 +292,8 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->dtype = dtype;
     p->rec_mode = LSTM_REC_AUTO;
     p->rec_tile = 0;
+    p->part_bufs = 1;
+    p->poll_sleep = 2;
     p->timing = 0;
     p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
     *out = p;
@@ -331,6 +343,14 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             if (value < LSTM_REC_AUTO || value > LSTM_REC_PERSISTENT) return LSTM_ERR_UNSUPPORTED;
             p->rec_mode = value;
             return LSTM_OK;
+        case LSTM_OPT_PARTIAL_BUFFERS:
+            if (value != 1 && value != 2) return LSTM_ERR_UNSUPPORTED;
+            p->part_bufs = value;
+            return LSTM_OK;
+        case LSTM_OPT_POLL_SLEEP:
+            if (value < 0 || value > 1000) return LSTM_ERR_UNSUPPORTED;
+            p->poll_sleep = value;
+            return LSTM_OK;
         case LSTM_OPT_TIMING:
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
             p->timing = value;
@@ -367,10 +387,10 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     if (rc != LSTM_OK) return (lstm_status)rc;
     std::snprintf(buf, len,
                   "proj=k_proj<%s> tile=128x128; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
-                  "NGB=%d teams=%d workgroups=%d lds=%zu map_xcd=%d",
+                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d",
                   p->dtype == LSTM_BF16 ? "bf16" : "f32", p->dtype == LSTM_BF16 ? "bf16" : "f32", s.tile.WK,
                   s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P, s.BG, s.NGB, s.teams,
-                  s.wgs, s.smem, s.map_xcd);
+                  s.wgs, s.smem, s.geom.part_bufs, s.map_xcd);
     return LSTM_OK;
 }
 
@@ -401,7 +421,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
     hipStream_t st = static_cast<hipStream_t>(stream_);
     char *ws = static_cast<char *>(workspace);
     unsigned *status = reinterpret_cast<unsigned *>(ws + lay.status);
-    unsigned *counters = reinterpret_cast<unsigned *>(ws + lay.counters);
+    unsigned long long *xbuf = reinterpret_cast<unsigned long long *>(ws + lay.xbuf);
     float *G = reinterpret_cast<float *>(ws + lay.G);
     float *cstate = reinterpret_cast<float *>(ws + lay.cstate);
     const size_t es = elem_size(p->dtype);
@@ -443,7 +463,8 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.hn = h_n ? static_cast<char *>(h_n) + (size_t)l * state_elems * es : nullptr;
         ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
         ra.cstate = cstate;
-        ra.ctr = counters + (size_t)l * kMaxTeams * kCtrStride;
+        ra.xbuf = xbuf;
+        ra.tag_base = (unsigned)l * (unsigned)(T + 1);
         ra.status = status;
         ra.T = T;
         ra.B = B;
@@ -452,7 +473,11 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.P = sch.P;
         ra.BG = sch.BG;
         ra.NGB = sch.NGB;
-        ra.kch = (p->H + kc - 1) / kc;
+        ra.kch = sch.geom.kch;
+        ra.kchp = sch.geom.kchp;
+        ra.nbatch = sch.geom.nbatch;
+        ra.part_bufs = sch.geom.part_bufs;
+        ra.poll_sleep = p->poll_sleep;
         ra.map_xcd = sch.map_xcd;
         ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
         for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
@@ -462,8 +487,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         if (sch.persistent) {
             ra.s_begin = 0;
             ra.s_end = T;
-            ra.persistent = 1;
-            if (launch_rec(ra, sch.tile, p->dtype, true, st) != hipSuccess) {
+            if (launch_rec(ra, sch.tile, sch.smem, p->dtype, true, st) != hipSuccess) {
                 (void)hipGetLastError();
                 // The cooperative launch was refused (nothing ran): in automatic
                 // mode the layer falls back to one launch per step.
@@ -472,11 +496,10 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
             }
         }
         if (stepped) {
-            ra.persistent = 0;
             for (int s = 0; s < T; ++s) {
                 ra.s_begin = s;
                 ra.s_end = s + 1;
-                if (launch_rec(ra, sch.tile, p->dtype, false, st) != hipSuccess) {
+                if (launch_rec(ra, sch.tile, sch.smem, p->dtype, false, st) != hipSuccess) {
                     (void)hipGetLastError();
                     return LSTM_ERR_LAUNCH;
                 }
