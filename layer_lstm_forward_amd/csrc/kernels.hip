@@ -502,7 +502,7 @@ RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers) {
 
 #define LSTM_REC_TILES(X) \
     X(4, 1, 1) X(4, 1, 2) X(4, 1, 4) X(2, 1, 1) X(2, 1, 2) X(2, 1, 4) X(1, 1, 1) X(1, 1, 2) X(1, 1, 4) \
-    X(1, 4, 1) X(1, 4, 2) X(1, 4, 4)
+    X(1, 4, 1) X(1, 4, 2)
 
 bool rec_tile_supported(RecTile t) {
 #define LSTM_T_OK(wk, mtw, nt) if (t.WK == wk && t.MTW == mtw && t.NT == nt) return true;

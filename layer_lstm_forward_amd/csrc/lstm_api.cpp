@@ -122,7 +122,7 @@ DevInfo dev_info(int dev) {
 }
 
 const RecTile kTiles[] = {{4, 1, 4}, {4, 1, 2}, {4, 1, 1}, {2, 1, 4}, {2, 1, 2}, {2, 1, 1},
-                          {1, 1, 4}, {1, 1, 2}, {1, 1, 1}, {1, 4, 4}, {1, 4, 2}, {1, 4, 1}};
+                          {1, 1, 4}, {1, 1, 2}, {1, 1, 1}, {1, 4, 2}, {1, 4, 1}};
 
 bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
     if (!rec_tile_supported(t)) return false;
@@ -142,15 +142,17 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
 }
 
 // Rough cycles per step of one workgroup: matrix-core work of the busiest
-// wave plus the h_{t-1} fetch at an assumed 64 B/clk per CU.
-double step_cost(const lstm_plan *p, const Sched &s) {
+// wave (times the number of workgroups that share a CU), plus the h_{t-1}
+// fetch as tagged 8-byte words at the ~32 B/clk a CU sustains for it.
+double step_cost(const lstm_plan *p, const Sched &s, int cus) {
     const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
     const int kch = (p->H + kc - 1) / kc;
     const int cpw = (kch + s.tile.WK - 1) / s.tile.WK;
     const int live_mtw = (s.BG + 15) / 16 < s.tile.MTW ? (s.BG + 15) / 16 : s.tile.MTW;
-    const double mfma = (double)live_mtw * s.tile.NT * cpw * (p->dtype == LSTM_BF16 ? 16 : 128);
-    const double hbytes = (double)s.BG * p->H * elem_size(p->dtype);
-    return mfma + hbytes / 64.0;
+    const int share = cus > 0 ? (s.wgs + cus - 1) / cus : 1;
+    const double mfma = (double)live_mtw * s.tile.NT * cpw * (p->dtype == LSTM_BF16 ? 16 : 128) * share;
+    const double xbytes = (double)s.BG * p->H * (p->dtype == LSTM_BF16 ? 4 : 8) * share;
+    return mfma + xbytes / 32.0;
 }
 
 int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
@@ -174,7 +176,7 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
         s.persistent = can_persist;
         double cost;
         if (s.persistent) {
-            cost = step_cost(p, s);
+            cost = step_cost(p, s, di.cus);
         } else {
             // per step launch: every workgroup reloads its W_hh slice
             cost = 1e12 + (double)s.wgs * (4.0 * s.U + s.BG) * p->H * elem_size(p->dtype);

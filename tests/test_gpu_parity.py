@@ -25,7 +25,7 @@ SMALL = [
     Spec(256, 200, 2, True, 8, 70, "bf16", 107, "normal0.1"),
     Spec(1, 1, 1, False, 1, 1, "f32", 108, "normal0.1"),      # degenerate: one unit, one step
 ]
-TILES = [411, 412, 414, 211, 212, 214, 111, 112, 114, 141, 142, 144]
+TILES = [411, 412, 414, 211, 212, 214, 111, 112, 114, 141, 142]
 
 
 def _id(s):
