@@ -74,7 +74,137 @@ def cpu_baseline(inp, budget_s):
                       f"fp64, {wall:.1f} s wall ({per_row_flops * len(rows) / wall / 1e9:.2f} GFLOP/s)"}
 
 
+def summarize_profile(path, command):
+    """Per-kernel duration statistics from a rocprofv3 kernel trace (the
+    rocpd SQLite database or a kernel_trace.csv), as a short text table."""
+    import csv
+    import sqlite3
+    from collections import defaultdict
+    durs = defaultdict(list)
+    counters = defaultdict(lambda: defaultdict(list))
+    if path.endswith(".db"):
+        con = sqlite3.connect(path)
+        for name, dur in con.execute("select name, duration from kernels"):
+            durs[name].append(dur)
+        try:
+            for name, cname, val in con.execute(
+                    "select k.name, p.counter_name, p.value from pmc_events p join kernels k "
+                    "on p.dispatch_id = k.dispatch_id"):
+                counters[name][cname].append(val)
+        except sqlite3.Error:
+            pass
+    else:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name") or row.get("KernelName") or row.get("Name")
+                if "Counter_Name" in row:
+                    counters[name][row["Counter_Name"]].append(float(row["Counter_Value"]))
+                    continue
+                s, e = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+                durs[name].append(e - s)
+    total = sum(sum(v) for v in durs.values()) or 1
+    lines = [f"# rocprofv3 kernel summary", f"# command: {command}", f"# source: {os.path.basename(path)}",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{len(v):6d} {sum(v) / len(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} {max(v) / 1e3:10.2f} "
+                     f"{sum(v) / 1e6:10.3f} {100.0 * sum(v) / total:6.1f}  {name[:140]}")
+    for name, cs in counters.items():
+        for cname, vals in sorted(cs.items()):
+            lines.append(f"# counter {cname} per dispatch: avg {sum(vals) / len(vals):.1f} over {len(vals)} "
+                         f"dispatches of {name[:100]}")
+    return "\n".join(lines)
+
+
+def kernel_source_hash():
+    """sha256 of the kernel sources; a stored counter profile is valid only for
+    the sources it was taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "device.h", "kernels.h"):
+        with open(os.path.join(ROOT, "layer_lstm_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, workload, command):
+    """HBM traffic of `kernel` from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    known size."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(path, want):
+        vals = defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+        for name, v in vals.items():
+            if want in name:
+                return sum(v) / len(v), len(v), name
+        raise SystemExit(f"no dispatch of {want} in {path}")
+
+    cf, _, _ = per_dispatch(copy_fetch_csv, "copyBuffer")
+    cw, _, _ = per_dispatch(copy_write_csv, "copyBuffer")
+    copy_kib = 256 * 1024  # the calibration copy reads and writes 256 MiB
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    kf, nf, name = per_dispatch(fetch_csv, kernel)
+    kw, nw, _ = per_dispatch(write_csv, kernel)
+    fetch_b = kf * 1024 * f_scale
+    write_b = kw * 1024 * w_scale
+    lines = ["# rocprofv3 HBM counters, one dispatch = one launch",
+             f"# command: {command}",
+             f"# workload: {workload}",
+             f"# kernel: {name[:120]}",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"copy_calibration: FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for a 262144 KiB copy "
+             f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+             f"FETCH_SIZE_KiB_per_dispatch: {kf:.1f} (over {nf} dispatches)",
+             f"WRITE_SIZE_KiB_per_dispatch: {kw:.1f} (over {nw} dispatches)",
+             f"fetch_bytes_per_launch: {fetch_b:.0f}",
+             f"write_bytes_per_launch: {write_b:.0f}",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}"]
+    return "\n".join(lines)
+
+
+def stored_traffic(kernel, workload):
+    """traffic_bytes_per_launch from profiles/<kernel>_<workload>_hbm_counters.txt
+    if it was taken from the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of a known size, for scaling the HBM
+    byte counters (the copy moves exactly 2*nbytes: one read, one write)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4, "launches": steps}))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profile":
+        print(summarize_profile(sys.argv[2], " ".join(sys.argv[3:])))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        print(pmc_summary(*sys.argv[2:8], " ".join(sys.argv[8:])))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
+        copy_calibration(int(sys.argv[2]) if len(sys.argv) > 2 else 256 << 20, 5)
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -169,8 +299,12 @@ def main():
     else:
         kname, flops, avg = "k_proj", proj_flops_per_launch(spec), proj_avg
     achieved = flops / (avg / 1e3) / 1e12
+    traffic = stored_traffic(kname, args.workload)
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[spec.dtype], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS[spec.dtype], 4), "traffic": None, "kernel": kname,
+            "frac": round(achieved / PEAK_TFLOPS[spec.dtype], 4),
+            "traffic": None if traffic is None else {"bytes_per_launch": traffic,
+                                                      "GB_per_s": round(traffic / (avg / 1e3) / 1e9, 1)},
+            "kernel": kname,
             "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
             "phase_ms_per_step": {"proj": round(tm["proj_ms"] / max(1, tm["calls"]), 4),
                                   "rec": round(tm["rec_ms"] / max(1, tm["calls"]), 4)}}
