@@ -80,7 +80,9 @@ typedef enum {
     LSTM_OPT_REC_TILE = 2,   /* value: 0 = automatic, else 100*WK + 10*MTW + NT (see lstm_describe) */
     LSTM_OPT_TIMING = 3,     /* value 1: record HIP events around each phase (see lstm_read_timing) */
     LSTM_OPT_PARTIAL_BUFFERS = 4, /* 1 (default) or 2 LDS partial-sum buffers in the recurrent kernel */
-    LSTM_OPT_POLL_SLEEP = 5  /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
+    LSTM_OPT_POLL_SLEEP = 5, /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
+    LSTM_OPT_EXCHANGE = 6,   /* 0 (default): poll the step-tagged h words; 1: wait on per-workgroup flags first */
+    LSTM_OPT_TEAM_ROWS = 7   /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset

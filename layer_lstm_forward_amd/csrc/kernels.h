@@ -33,6 +33,7 @@ struct RecArgs {
     float *cn;               // [D, B, H] or NULL
     float *cstate;           // [D, B, H] carry between step launches
     unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 tagged words
+    unsigned long long *flags;  // per-producer step flags: [2][D][NGB][P] words, or NULL
     unsigned tag_base;       // tags of this layer are tag_base + s + 1
     unsigned *status;        // error word
     int T, B, H, D;

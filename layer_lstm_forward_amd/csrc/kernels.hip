@@ -280,6 +280,44 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             const unsigned long long ready = (unsigned long long)tag << 32;
             const __amdgpu_buffer_rsrc_t xr =
                 xrsrc(a.xbuf + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * region, (unsigned)(region * 8));
+            if (a.flags) {
+                // Wait until every producer of this wave's K range has raised
+                // its flag for step s-1 (one word per producer workgroup, one
+                // lane per producer), so that the bulk loads below are issued
+                // once, after the data is out, instead of re-reading it.  The
+                // words keep their own tags, so correctness does not rest on
+                // the flag: a stale word is still caught and re-read.
+                const int kb = cw0 * DT::KC, ke = min(H, (cw0 + nb * CB) * DT::KC);
+                const int p0 = kb / U, np = kb < ke ? (ke - 1) / U - p0 + 1 : 0;
+                const unsigned long long *fl = a.flags + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * a.P;
+                for (int q0 = 0; q0 < np && wave_ok; q0 += 64) {
+                    const bool mine = q0 + lane < np;
+                    unsigned long long f = mine ? xload(fl + p0 + q0 + lane) : ready;
+                    if (!__all(f == ready)) {
+                        unsigned spins = 0;
+                        const long long t0 = wall_clock64();
+                        do {
+                            if ((++spins & 63u) == 0) {
+                                const unsigned st = __builtin_amdgcn_readfirstlane(
+                                    __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                                if (st != 0u) {
+                                    wave_ok = false;
+                                    break;
+                                }
+                                if (wall_clock64() - t0 > a.timeout_ticks) {
+                                    if (lane == 0)
+                                        __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+                                    wave_ok = false;
+                                    break;
+                                }
+                            }
+                            for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
+                            if (f != ready) f = xload(fl + p0 + q0 + lane);
+                        } while (!__all(f == ready));
+                    }
+                }
+            }
             for (int bi = 0; bi < nb && wave_ok; ++bi) {
                 const int c0 = cw0 + bi * CB;
                 // Each lane reads its fragment as two 16-byte pairs of tagged
@@ -439,12 +477,19 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
             }
         }
+        if (a.flags && publish) {
+            // every thread's exchange stores have completed before the flag
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0)
+                xstore(a.flags + ((size_t)((s & 1) * D + d) * a.NGB + gb) * a.P + p, tag_out);
+        }
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) gcur[i][q] = gnext[i][q];
         load_g(s + 2, gnext);
-        if (a.part_bufs != 2) __syncthreads();  // partials are reused by the next step
+        if (a.part_bufs != 2 && !(a.flags && publish)) __syncthreads();  // partials are reused by the next step
     }
 
     if (a.s_end < T) {

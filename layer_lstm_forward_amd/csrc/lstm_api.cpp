@@ -21,6 +21,8 @@ struct lstm_plan {
     int rec_tile;  // 0 = automatic, else 100*WK + 10*MTW + NT
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
+    int exchange;    // 0: poll the tagged words; 1: poll per-producer flags first
+    int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     // optional per-phase timing (LSTM_OPT_TIMING)
     int timing;
     struct Span {
@@ -49,7 +51,7 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 }
 
 struct Layout {
-    size_t status, xbuf, G, ymid[2], cstate, total;
+    size_t status, xbuf, flags, G, ymid[2], cstate, total;
     size_t sync_bytes;  // status + exchange buffer, zeroed per call
 };
 
@@ -72,6 +74,11 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     off += kStatusBytes;
     o->xbuf = off;
     off += align_up(xb);
+    // producer flags: 2 parities x D x teams x workgroups per team (<= H/4 + 1)
+    size_t fb;
+    if (!mul_ok((size_t)2 * p->D * (((size_t)B + 255) / 16 + 1), ((size_t)p->H / 4 + 1) * 8, &fb)) return false;
+    o->flags = off;
+    off += align_up(fb);
     o->sync_bytes = off;
     o->G = off;
     if (g > SIZE_MAX / 2) return false;
@@ -130,7 +137,8 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
     s->tile = t;
     s->U = 4 * t.NT;
     s->P = (p->H + s->U - 1) / s->U;
-    const int ng0 = (B + rows - 1) / rows;
+    const int cap = p->team_rows > 0 && p->team_rows < rows ? p->team_rows : rows;
+    const int ng0 = (B + cap - 1) / cap;
     s->BG = (B + ng0 - 1) / ng0;
     s->NGB = (B + s->BG - 1) / s->BG;
     s->teams = s->NGB * p->D;
@@ -296,6 +304,8 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->rec_tile = 0;
     p->part_bufs = 1;
     p->poll_sleep = 2;
+    p->exchange = 0;
+    p->team_rows = 0;
     p->timing = 0;
     p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
     *out = p;
@@ -352,6 +362,14 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
         case LSTM_OPT_POLL_SLEEP:
             if (value < 0 || value > 1000) return LSTM_ERR_UNSUPPORTED;
             p->poll_sleep = value;
+            return LSTM_OK;
+        case LSTM_OPT_EXCHANGE:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->exchange = value;
+            return LSTM_OK;
+        case LSTM_OPT_TEAM_ROWS:
+            if (value < 0) return LSTM_ERR_UNSUPPORTED;
+            p->team_rows = value;
             return LSTM_OK;
         case LSTM_OPT_TIMING:
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
@@ -466,6 +484,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
         ra.cstate = cstate;
         ra.xbuf = xbuf;
+        ra.flags = p->exchange == 1 ? reinterpret_cast<unsigned long long *>(ws + lay.flags) : nullptr;
         ra.tag_base = (unsigned)l * (unsigned)(T + 1);
         ra.status = status;
         ra.T = T;
