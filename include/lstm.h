@@ -82,7 +82,8 @@ typedef enum {
     LSTM_OPT_PARTIAL_BUFFERS = 4, /* 1 (default) or 2 LDS partial-sum buffers in the recurrent kernel */
     LSTM_OPT_POLL_SLEEP = 5, /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
     LSTM_OPT_EXCHANGE = 6,   /* 0 (default): poll the step-tagged h words; 1: wait on per-workgroup flags first */
-    LSTM_OPT_TEAM_ROWS = 7   /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
+    LSTM_OPT_TEAM_ROWS = 7,  /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
+    LSTM_OPT_PROJ_TILE = 8   /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset

@@ -51,6 +51,23 @@ __device__ inline f32x4 mma_chunk(BF16, f32x4 acc, u32x4 a, u32x4 b) {
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// acc += A * B^T for one 32x32 output tile over 32 bytes of K per row: lane l
+// feeds row (l % 32) with K sub-range (l / 32) * PER16 .. + PER16 - 1; the
+// result lane l, register v holds row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+__device__ inline f32x16 mma32_chunk(F32, f32x16 acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    return acc;
+}
+__device__ inline f32x16 mma32_chunk(BF16, f32x16 acc, u32x4 a, u32x4 b) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+}
+
 // Load the 16-byte fragment row[k .. k+PER16) with zero fill past kmax.
 // vec: the caller guarantees 16-byte alignment of row + k whenever the whole
 // fragment is in range.

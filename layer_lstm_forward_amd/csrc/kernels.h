@@ -71,7 +71,8 @@ RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers);
 int rec_rows_per_wg(RecTile t);
 bool rec_tile_supported(RecTile t);
 
-hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s);
+// variant: 0 automatic, 1 128x128 tiles, 2 256x256 tiles, 3 256x256 tiles with direct-to-LDS loads
+hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s);
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);

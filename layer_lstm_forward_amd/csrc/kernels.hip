@@ -126,6 +126,221 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 }
 
 // ===========================================================================
+// Projection GEMM, large tiles.  256x256 output tile per 256-thread workgroup;
+// each wave owns a 128x128 quadrant as 4x4 tiles of 32x32 (v_mfma_f32_32x32x16
+// _bf16 / v_mfma_f32_32x32x2_f32), which halves the LDS and L2 bytes per FLOP
+// of the 128x128 kernel.  Stages of 128 bytes of K per row are double-buffered
+// in LDS (128 KiB), with 16-byte segments XOR-swizzled by (row/2) % 8 so that a
+// wave's fragment read of 16 consecutive rows touches 16 distinct bank groups.
+// Tiles are numbered so that each XCD works on a contiguous range (rows of the
+// output advance slowest), keeping an A panel within one XCD's L2.
+// ===========================================================================
+template <class DT, bool VEC>
+__global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 256, BN = 256, SEG = 8;
+    constexpr int KS = SEG * DT::PER16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
+    constexpr int STAGE = (BM + BN) * SEG;  // 16-byte segments per stage
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int d = blockIdx.z;
+    const int M = a.M, N = a.N, K = a.K;
+    const int ntn = (N + BN - 1) / BN;
+    const int ntiles = ((M + BM - 1) / BM) * ntn;
+    int tile = blockIdx.x;
+    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+    const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+    const S *X = static_cast<const S *>(a.X);
+    const S *W = static_cast<const S *>(a.W[d]);
+
+    u32x4 ra[8], rb[8];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
+            const int k = k0 + sg * DT::PER16;
+            ra[i] = (m0 + row < M) ? load_frag<DT>(X + (size_t)(m0 + row) * a.ldx, k, K, VEC) : zero;
+            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * K, k, K, VEC) : zero;
+        }
+    };
+    auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
+    auto sstore = [&](int buf) {
+        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
+            sa[swz(row, sg)] = ra[i];
+            sb[swz(row, sg)] = rb[i];
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (K + KS - 1) / KS;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * KS);
+        const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // 32 bytes of K per row per sub-chunk
+            u32x4 af[4], bw[4];
+            const int sg = 2 * c + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = sa[swz(wm * 128 + 32 * i + (lane & 31), sg)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bw[j] = sb[swz(wn * 128 + 32 * j + (lane & 31), sg)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[i], bw[j]);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    const S *bi = static_cast<const S *>(a.b_ih[d]);
+    const S *bh = static_cast<const S *>(a.b_hh[d]);
+    const size_t ldg = (size_t)a.D * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+            }
+    }
+}
+
+// ===========================================================================
+// Projection GEMM, large tiles fed by direct-to-LDS loads.  Same 256x256 tile,
+// wave split and MFMA work as k_proj_big, but global data goes straight into
+// LDS (buffer_load_dwordx4 ... lds): stage k+1 streams into the other LDS
+// buffer while stage k is multiplied, with no register staging and one
+// barrier per stage.  A load instruction fills 1 KiB of LDS (64 lanes x 16
+// bytes, consecutive), i.e. 8 rows of a stage; each lane fetches the global
+// segment whose swizzled home is its slot.  Rows past M or N and K past K
+// read as zeros (offsets beyond the buffer resource).  Needs K and the row
+// strides to be multiples of 16 bytes.
+// ===========================================================================
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <class DT>
+__global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 256, BN = 256, SEG = 8;
+    constexpr int KS = SEG * DT::PER16;
+    constexpr int STAGE = (BM + BN) * SEG;  // 16-byte segments per stage
+    constexpr unsigned OOR = 0x80000000u;   // past any resource: reads zero
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int d = blockIdx.z;
+    const int M = a.M, N = a.N, K = a.K;
+    const int ntn = (N + BN - 1) / BN;
+    const int ntiles = ((M + BM - 1) / BM) * ntn;
+    int tile = blockIdx.x;
+    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+    const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+    const int es = (int)sizeof(S);
+    const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx;
+    const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * K;
+    const unsigned xbytes = (unsigned)((size_t)min(BM, M - m0) * a.ldx * es);
+    const unsigned wbytes = (unsigned)((size_t)min(BN, N - n0) * K * es);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(X), (short)0, (int)xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
+
+    // this lane's slot in each 1 KiB block: row (lane / 8) of the block, swizzled segment (lane % 8)
+    const int brow = lane >> 3, pseg = lane & 7;
+    auto issue = [&](int kt, int buf) {
+        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int blk = w + 4 * i;  // 32 blocks of 8 rows per operand
+            const int row = blk * 8 + brow;
+            const int lseg = pseg ^ ((row >> 1) & 7);
+            const int k = kt * KS + lseg * DT::PER16;
+            const unsigned ox = k < K ? (unsigned)(((size_t)row * a.ldx + k) * es) : OOR;
+            const unsigned ow = k < K ? (unsigned)(((size_t)row * K + k) * es) : OOR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(sa + blk * 64), 16, ox, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(sb + blk * 64), 16, ow, 0, 0, 0);
+        }
+    };
+    auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (K + KS - 1) / KS;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage kt are in LDS
+        __syncthreads();                 // everyone's are, and stage kt-1 is no longer read
+        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+        const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+        // fragments of sub-chunk c+1 are read while sub-chunk c is multiplied
+        u32x4 af[2][4], bw[2][4];
+        auto frags = [&](int c, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+            const int sg = 2 * c + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = sa[swz(wm * 128 + 32 * i + (lane & 31), sg)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = sb[swz(wn * 128 + 32 * j + (lane & 31), sg)];
+        };
+        frags(0, af[0], bw[0]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (c + 1 < 4) frags(c + 1, af[(c + 1) & 1], bw[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead in front of the products
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[c & 1][i], bw[c & 1][j]);
+        }
+    }
+
+    const S *bi = static_cast<const S *>(a.b_ih[d]);
+    const S *bh = static_cast<const S *>(a.b_hh[d]);
+    const size_t ldg = (size_t)a.D * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+            }
+    }
+}
+
+// ===========================================================================
 // Recurrence.  A team of P workgroups shares one direction and one group of
 // BG batch rows; workgroup p owns hidden units [p*U, p*U+U) and therefore the
 // 4U rows {q*H + j : q in i,f,g,o} of W_hh, kept in LDS as MFMA fragments
@@ -507,21 +722,42 @@ __global__ void k_fill(unsigned *p, size_t n, unsigned v) {
 // ===========================================================================
 // Host-side launch helpers.
 // ===========================================================================
-hipError_t launch_proj(const ProjArgs &a, int dtype, hipStream_t s) {
-    const int per16 = dtype == DT_BF16 ? 8 : 4;
-    const size_t es = dtype == DT_BF16 ? 2 : 4;
-    bool vec = (a.K % per16 == 0) && (a.ldx % per16 == 0) && ((uintptr_t)a.X % 16 == 0);
-    for (int d = 0; d < a.D; ++d) vec = vec && ((uintptr_t)a.W[d] % 16 == 0);
-    (void)es;
-    dim3 grid((a.N + 127) / 128, (a.M + 127) / 128, a.D), block(256);
-    if (dtype == DT_BF16) {
-        if (vec) hipLaunchKernelGGL((k_proj<BF16, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_proj<BF16, false>), grid, block, 0, s, a);
+template <class DT, bool VEC>
+static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, hipStream_t s) {
+    if (big && dma && VEC) {
+        const void *fn = reinterpret_cast<const void *>(&k_proj_dma<DT>);
+        const size_t smem = 2 * (256 + 256) * 8 * 16;
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D);
+        hipLaunchKernelGGL((k_proj_dma<DT>), grid, dim3(256), smem, s, a);
+    } else if (big) {
+        const void *fn = reinterpret_cast<const void *>(&k_proj_big<DT, VEC>);
+        const size_t smem = 2 * (256 + 256) * 8 * 16;
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D);
+        hipLaunchKernelGGL((k_proj_big<DT, VEC>), grid, dim3(256), smem, s, a);
     } else {
-        if (vec) hipLaunchKernelGGL((k_proj<F32, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_proj<F32, false>), grid, block, 0, s, a);
+        dim3 grid((a.N + 127) / 128, (a.M + 127) / 128, a.D);
+        hipLaunchKernelGGL((k_proj<DT, VEC>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s) {
+    const int per16 = dtype == DT_BF16 ? 8 : 4;
+    bool vec = (a.K % per16 == 0) && (a.ldx % per16 == 0) && ((uintptr_t)a.X % 16 == 0);
+    for (int d = 0; d < a.D; ++d) vec = vec && ((uintptr_t)a.W[d] % 16 == 0);
+    // 256x256 tiles once they give every CU at least one tile; otherwise 128x128
+    const long long big_tiles = (long long)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.D;
+    const bool big = variant >= 2 || (variant == 0 && big_tiles >= 256);
+    // direct-to-LDS loads need 16-byte rows; the byte offsets of one tile must fit 31 bits
+    const size_t es = dtype == DT_BF16 ? 2 : 4;
+    const bool dma = variant != 2 && (size_t)256 * a.ldx * es < (1u << 31) && (size_t)256 * a.K * es < (1u << 31);
+    if (dtype == DT_BF16)
+        return vec ? launch_proj_t<BF16, true>(a, big, dma, s) : launch_proj_t<BF16, false>(a, big, dma, s);
+    return vec ? launch_proj_t<F32, true>(a, big, dma, s) : launch_proj_t<F32, false>(a, big, dma, s);
 }
 
 int rec_rows_per_wg(RecTile t) { return 16 * (4 / t.WK) * t.MTW; }

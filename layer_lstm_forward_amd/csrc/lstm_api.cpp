@@ -23,6 +23,7 @@ struct lstm_plan {
     int poll_sleep;  // back-off between re-reads of stale exchange words
     int exchange;    // 0: poll the tagged words; 1: poll per-producer flags first
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
+    int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
     // optional per-phase timing (LSTM_OPT_TIMING)
     int timing;
     struct Span {
@@ -306,6 +307,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->poll_sleep = 2;
     p->exchange = 0;
     p->team_rows = 0;
+    p->proj_tile = 0;
     p->timing = 0;
     p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
     *out = p;
@@ -370,6 +372,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
         case LSTM_OPT_TEAM_ROWS:
             if (value < 0) return LSTM_ERR_UNSUPPORTED;
             p->team_rows = value;
+            return LSTM_OK;
+        case LSTM_OPT_PROJ_TILE:
+            if (value < 0 || value > 3) return LSTM_ERR_UNSUPPORTED;
+            p->proj_tile = value;
             return LSTM_OK;
         case LSTM_OPT_TIMING:
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
@@ -471,7 +477,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
             pa.b_hh[d] = p->has_bias ? w[3] : nullptr;
         }
         int span = span_begin(p, st, 0);
-        if (launch_proj(pa, p->dtype, st) != hipSuccess) return LSTM_ERR_LAUNCH;
+        if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) return LSTM_ERR_LAUNCH;
         span_end(p, span, st, 1);
 
         RecArgs ra{};

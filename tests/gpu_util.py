@@ -22,7 +22,7 @@ def to_dev(a, bf16, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1):
+def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1, options=None):
     """Returns (y, h_n, c_n) as float64 numpy arrays and the model used."""
     import torch
     import layer_lstm_forward_amd as pkg
@@ -30,7 +30,7 @@ def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1
     bf = s.dtype == "bf16"
     if model is None:
         model = pkg.LSTM(s.input_size, s.hidden_size, s.num_layers, s.bidirectional, bias=s.has_bias,
-                         dtype=s.dtype, recurrence=recurrence, rec_tile=rec_tile)
+                         dtype=s.dtype, recurrence=recurrence, rec_tile=rec_tile, options=options)
     x = to_dev(inp.x, bf, device)
     w = [to_dev(p, bf, device) for p in inp.params]
     h0 = to_dev(inp.h0, bf, device)

@@ -42,6 +42,17 @@ def test_small_shapes(spec, mode):
     assert_parity(got, ref, spec.dtype, m.describe(spec.T, spec.B))
 
 
+@pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
+@pytest.mark.parametrize("proj_tile", [1, 2, 3], ids=["proj128", "proj256", "proj256dma"])
+def test_projection_tiles(spec, proj_tile):
+    """Both projection GEMM kernels, forced on shapes with ragged M, N and K."""
+    print(f"case {_id(spec)} proj tile {proj_tile}", flush=True)
+    inp = make_inputs(spec)
+    got, m = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: proj_tile})
+    ref = run_oracle(inp)
+    assert_parity(got, ref, spec.dtype, f"proj tile {proj_tile}")
+
+
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("spec", [Spec(48, 72, 2, True, 7, 37, "f32", 201, "normal0.1"),
                                   Spec(96, 136, 1, False, 6, 21, "bf16", 202, "normal0.1")], ids=_id)
