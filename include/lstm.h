@@ -81,9 +81,12 @@ typedef enum {
     LSTM_OPT_TIMING = 3,     /* value 1: record HIP events around each phase (see lstm_read_timing) */
     LSTM_OPT_PARTIAL_BUFFERS = 4, /* 1 (default) or 2 LDS partial-sum buffers in the recurrent kernel */
     LSTM_OPT_POLL_SLEEP = 5, /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
-    LSTM_OPT_EXCHANGE = 6,   /* 0 (default): poll the step-tagged h words; 1: wait on per-workgroup flags first */
+    /* 6: reserved (no longer accepted) */
     LSTM_OPT_TEAM_ROWS = 7,  /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
-    LSTM_OPT_PROJ_TILE = 8   /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS */
+    LSTM_OPT_PROJ_TILE = 8,  /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS */
+    LSTM_OPT_READ_PACE = 9   /* 0..100000 ns (default 0): delay between a workgroup finishing step t
+                                (its h_t published) and its first read of the other workgroups' h_t;
+                                0 reads as soon as the step ends */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset

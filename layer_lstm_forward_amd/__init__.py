@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_PKG, "liblstm_amd.so")
 LSTM_F32, LSTM_BF16 = 0, 1
 LSTM_REC_AUTO, LSTM_REC_STEP, LSTM_REC_PERSISTENT = 0, 1, 2
 LSTM_OPT_RECURRENCE, LSTM_OPT_REC_TILE, LSTM_OPT_TIMING = 1, 2, 3
-LSTM_OPT_PARTIAL_BUFFERS, LSTM_OPT_POLL_SLEEP, LSTM_OPT_EXCHANGE, LSTM_OPT_TEAM_ROWS = 4, 5, 6, 7
+LSTM_OPT_PARTIAL_BUFFERS, LSTM_OPT_POLL_SLEEP, LSTM_OPT_TEAM_ROWS = 4, 5, 7
 LSTM_OPT_PROJ_TILE = 8
+LSTM_OPT_READ_PACE = 9
 STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
           -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
           -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}

@@ -33,7 +33,6 @@ struct RecArgs {
     float *cn;               // [D, B, H] or NULL
     float *cstate;           // [D, B, H] carry between step launches
     unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 tagged words
-    unsigned long long *flags;  // per-producer step flags: [2][D][NGB][P] words, or NULL
     unsigned tag_base;       // tags of this layer are tag_base + s + 1
     unsigned *status;        // error word
     int T, B, H, D;
@@ -45,6 +44,7 @@ struct RecArgs {
     int nbatch;              // chunk batches per wave
     int part_bufs;           // 1 or 2 partial-sum buffers in LDS
     int poll_sleep;          // s_sleep units (64 clocks each) between re-reads of stale words
+    int pace;                // wall-clock ticks from the end of a step to the first read of the next
     int s_begin, s_end;      // steps handled by this launch
     int map_xcd;             // 1: place a team's workgroups on the same XCDs
     int vec;                 // 16-byte vector loads are aligned
@@ -73,6 +73,9 @@ bool rec_tile_supported(RecTile t);
 
 // variant: 0 automatic, 1 128x128 tiles, 2 256x256 tiles, 3 256x256 tiles with direct-to-LDS loads
 hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s);
+// Name of the projection kernel launch_proj picks for an M x N x K product
+// over D directions, given 16-byte aligned operands.
+const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant);
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);

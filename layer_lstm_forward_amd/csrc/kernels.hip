@@ -459,6 +459,10 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     const int mw = wm * MTW * 16 + (lane & 15);    // this lane's team row in tile i: mw + 16 i
     const int ksub = (lane >> 4) * DT::PER16;      // this lane's K offset inside a chunk
     const size_t region = (size_t)MT * kch * 256;  // exchange words per team
+    // Optional read pacing: every wave waits `pace` wall-clock ticks after the
+    // barrier that ends its workgroup's step s-1 before its first read of the
+    // others' h_{s-1}, so that reads do not reach memory ahead of the data.
+    long long t_pub = 0;
 
     for (int s = a.s_begin; s < a.s_end; ++s) {
         const int t = d == 0 ? s : T - 1 - s;
@@ -492,47 +496,10 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             }
         } else {
             const unsigned tag = a.tag_base + (unsigned)s;  // written at step s-1
-            const unsigned long long ready = (unsigned long long)tag << 32;
             const __amdgpu_buffer_rsrc_t xr =
                 xrsrc(a.xbuf + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * region, (unsigned)(region * 8));
-            if (a.flags) {
-                // Wait until every producer of this wave's K range has raised
-                // its flag for step s-1 (one word per producer workgroup, one
-                // lane per producer), so that the bulk loads below are issued
-                // once, after the data is out, instead of re-reading it.  The
-                // words keep their own tags, so correctness does not rest on
-                // the flag: a stale word is still caught and re-read.
-                const int kb = cw0 * DT::KC, ke = min(H, (cw0 + nb * CB) * DT::KC);
-                const int p0 = kb / U, np = kb < ke ? (ke - 1) / U - p0 + 1 : 0;
-                const unsigned long long *fl = a.flags + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * a.P;
-                for (int q0 = 0; q0 < np && wave_ok; q0 += 64) {
-                    const bool mine = q0 + lane < np;
-                    unsigned long long f = mine ? xload(fl + p0 + q0 + lane) : ready;
-                    if (!__all(f == ready)) {
-                        unsigned spins = 0;
-                        const long long t0 = wall_clock64();
-                        do {
-                            if ((++spins & 63u) == 0) {
-                                const unsigned st = __builtin_amdgcn_readfirstlane(
-                                    __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                                if (st != 0u) {
-                                    wave_ok = false;
-                                    break;
-                                }
-                                if (wall_clock64() - t0 > a.timeout_ticks) {
-                                    if (lane == 0)
-                                        __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
-                                    wave_ok = false;
-                                    break;
-                                }
-                            }
-                            for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
-                            if (f != ready) f = xload(fl + p0 + q0 + lane);
-                        } while (!__all(f == ready));
-                    }
-                }
-            }
+            if (s > a.s_begin && a.pace > 0)
+                while (wall_clock64() - t_pub < a.pace) __builtin_amdgcn_s_sleep(1);
             for (int bi = 0; bi < nb && wave_ok; ++bi) {
                 const int c0 = cw0 + bi * CB;
                 // Each lane reads its fragment as two 16-byte pairs of tagged
@@ -692,19 +659,13 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
             }
         }
-        if (a.flags && publish) {
-            // every thread's exchange stores have completed before the flag
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0)
-                xstore(a.flags + ((size_t)((s & 1) * D + d) * a.NGB + gb) * a.P + p, tag_out);
-        }
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) gcur[i][q] = gnext[i][q];
         load_g(s + 2, gnext);
-        if (a.part_bufs != 2 && !(a.flags && publish)) __syncthreads();  // partials are reused by the next step
+        if (a.part_bufs != 2) __syncthreads();  // partials are reused by the next step
+        t_pub = wall_clock64();
     }
 
     if (a.s_end < T) {
@@ -745,16 +706,30 @@ static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, hipStream
     return hipGetLastError();
 }
 
+// 256x256 tiles once they give every CU at least one tile (or on request);
+// their direct-to-LDS form needs 16-byte rows and the byte offsets of one
+// tile within 31 bits.
+static void proj_choose(int M, int N, int K, int ldx, int D, int dtype, int variant, bool vec, bool *big,
+                        bool *dma) {
+    const long long big_tiles = (long long)((M + 255) / 256) * ((N + 255) / 256) * D;
+    *big = variant >= 2 || (variant == 0 && big_tiles >= 256);
+    const size_t es = dtype == DT_BF16 ? 2 : 4;
+    *dma = *big && vec && variant != 2 && (size_t)256 * ldx * es < (1u << 31) && (size_t)256 * K * es < (1u << 31);
+}
+
+const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant) {
+    const int per16 = dtype == DT_BF16 ? 8 : 4;
+    bool big, dma;
+    proj_choose(M, N, K, K, D, dtype, variant, K % per16 == 0, &big, &dma);
+    return dma ? "k_proj_dma" : big ? "k_proj_big" : "k_proj";
+}
+
 hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s) {
     const int per16 = dtype == DT_BF16 ? 8 : 4;
     bool vec = (a.K % per16 == 0) && (a.ldx % per16 == 0) && ((uintptr_t)a.X % 16 == 0);
     for (int d = 0; d < a.D; ++d) vec = vec && ((uintptr_t)a.W[d] % 16 == 0);
-    // 256x256 tiles once they give every CU at least one tile; otherwise 128x128
-    const long long big_tiles = (long long)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.D;
-    const bool big = variant >= 2 || (variant == 0 && big_tiles >= 256);
-    // direct-to-LDS loads need 16-byte rows; the byte offsets of one tile must fit 31 bits
-    const size_t es = dtype == DT_BF16 ? 2 : 4;
-    const bool dma = variant != 2 && (size_t)256 * a.ldx * es < (1u << 31) && (size_t)256 * a.K * es < (1u << 31);
+    bool big, dma;
+    proj_choose(a.M, a.N, a.K, a.ldx, a.D, dtype, variant, vec, &big, &dma);
     if (dtype == DT_BF16)
         return vec ? launch_proj_t<BF16, true>(a, big, dma, s) : launch_proj_t<BF16, false>(a, big, dma, s);
     return vec ? launch_proj_t<F32, true>(a, big, dma, s) : launch_proj_t<F32, false>(a, big, dma, s);

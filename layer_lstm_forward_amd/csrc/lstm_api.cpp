@@ -21,7 +21,7 @@ struct lstm_plan {
     int rec_tile;  // 0 = automatic, else 100*WK + 10*MTW + NT
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
-    int exchange;    // 0: poll the tagged words; 1: poll per-producer flags first
+    int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
     // optional per-phase timing (LSTM_OPT_TIMING)
@@ -52,8 +52,8 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 }
 
 struct Layout {
-    size_t status, xbuf, flags, G, ymid[2], cstate, total;
-    size_t sync_bytes;  // status + exchange buffer, zeroed per call
+    size_t status, xbuf, G, ymid[2], cstate, total;
+    size_t sync_bytes;  // status word + exchange buffer, zeroed per call
 };
 
 bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
@@ -75,11 +75,6 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     off += kStatusBytes;
     o->xbuf = off;
     off += align_up(xb);
-    // producer flags: 2 parities x D x teams x workgroups per team (<= H/4 + 1)
-    size_t fb;
-    if (!mul_ok((size_t)2 * p->D * (((size_t)B + 255) / 16 + 1), ((size_t)p->H / 4 + 1) * 8, &fb)) return false;
-    o->flags = off;
-    off += align_up(fb);
     o->sync_bytes = off;
     o->G = off;
     if (g > SIZE_MAX / 2) return false;
@@ -152,7 +147,8 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
 
 // Rough cycles per step of one workgroup: matrix-core work of the busiest
 // wave (times the number of workgroups that share a CU), plus the h_{t-1}
-// fetch as tagged 8-byte words at the ~32 B/clk a CU sustains for it.
+// fetch as tagged 8-byte words (one fp32 or two bf16 values each) at the
+// ~32 B/clk a CU sustains for it.
 double step_cost(const lstm_plan *p, const Sched &s, int cus) {
     const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
     const int kch = (p->H + kc - 1) / kc;
@@ -305,7 +301,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->rec_tile = 0;
     p->part_bufs = 1;
     p->poll_sleep = 2;
-    p->exchange = 0;
+    p->read_pace_ns = 0;
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
@@ -365,9 +361,9 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             if (value < 0 || value > 1000) return LSTM_ERR_UNSUPPORTED;
             p->poll_sleep = value;
             return LSTM_OK;
-        case LSTM_OPT_EXCHANGE:
-            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
-            p->exchange = value;
+        case LSTM_OPT_READ_PACE:
+            if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
+            p->read_pace_ns = value;
             return LSTM_OK;
         case LSTM_OPT_TEAM_ROWS:
             if (value < 0) return LSTM_ERR_UNSUPPORTED;
@@ -411,9 +407,11 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     Sched s{};
     const int rc = choose_sched(p, B, dev, &s);
     if (rc != LSTM_OK) return (lstm_status)rc;
+    const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
     std::snprintf(buf, len,
-                  "proj=k_proj<%s> tile=128x128; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
+                  "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
                   "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d",
+                  proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile),
                   p->dtype == LSTM_BF16 ? "bf16" : "f32", p->dtype == LSTM_BF16 ? "bf16" : "f32", s.tile.WK,
                   s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P, s.BG, s.NGB, s.teams,
                   s.wgs, s.smem, s.geom.part_bufs, s.map_xcd);
@@ -490,7 +488,6 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
         ra.cstate = cstate;
         ra.xbuf = xbuf;
-        ra.flags = p->exchange == 1 ? reinterpret_cast<unsigned long long *>(ws + lay.flags) : nullptr;
         ra.tag_base = (unsigned)l * (unsigned)(T + 1);
         ra.status = status;
         ra.T = T;
@@ -505,6 +502,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.nbatch = sch.geom.nbatch;
         ra.part_bufs = sch.geom.part_bufs;
         ra.poll_sleep = p->poll_sleep;
+        ra.pace = (int)((long long)p->read_pace_ns * di.wall_khz / 1000000);
         ra.map_xcd = sch.map_xcd;
         ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
         for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
