@@ -16,6 +16,7 @@ Prints one JSON line.  Besides throughput it reports
 """
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -292,18 +293,20 @@ def main():
 
     proj_avg = tm["proj_ms"] / max(1, tm["proj_launches"])
     rec_avg = tm["rec_ms"] / max(1, tm["rec_launches"])
+    # kernel names as the library reports them: "proj=<name><dtype>; rec=<name><..."
+    names = dict(re.findall(r"(proj|rec)=(k_[a-z_]+)<", desc))
     if tm["rec_ms"] >= tm["proj_ms"]:
-        kname, flops, avg = "k_rec", rec_flops_per_launch(spec), rec_avg
+        kname, flops, avg = names.get("rec", "k_rec"), rec_flops_per_launch(spec), rec_avg
         if tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
             flops /= spec.T
     else:
-        kname, flops, avg = "k_proj", proj_flops_per_launch(spec), proj_avg
+        kname, flops, avg = names.get("proj", "k_proj"), proj_flops_per_launch(spec), proj_avg
     achieved = flops / (avg / 1e3) / 1e12
     traffic = stored_traffic(kname, args.workload)
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[spec.dtype], "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS[spec.dtype], 4),
-            "traffic": None if traffic is None else {"bytes_per_launch": traffic,
-                                                      "GB_per_s": round(traffic / (avg / 1e3) / 1e9, 1)},
+            "traffic": traffic,
+            "traffic_GB_per_s": None if traffic is None else round(traffic / (avg / 1e3) / 1e9, 1),
             "kernel": kname,
             "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
             "phase_ms_per_step": {"proj": round(tm["proj_ms"] / max(1, tm["calls"]), 4),

@@ -70,9 +70,13 @@ typedef enum {
 
 /* Recurrent-phase execution modes (lstm_set_option LSTM_OPT_RECURRENCE). */
 typedef enum {
-    LSTM_REC_AUTO = 0,       /* persistent when the plan's W_hh slices fit on chip, else per step */
-    LSTM_REC_STEP = 1,       /* one launch per time step (no cross-workgroup waits) */
-    LSTM_REC_PERSISTENT = 2  /* one cooperative launch per layer; LSTM_ERR_UNSUPPORTED if it does not fit */
+    LSTM_REC_AUTO = 0,       /* persistent when the plan's W_hh slices fit on chip, else per step as a
+                                GEMM when rows are 16-byte aligned, else per step with the tile kernel */
+    LSTM_REC_STEP = 1,       /* one launch of the tile kernel per time step (no cross-workgroup waits) */
+    LSTM_REC_PERSISTENT = 2, /* one cooperative launch per layer; LSTM_ERR_UNSUPPORTED if it does not fit */
+    LSTM_REC_GEMM = 3        /* one launch per time step of a GEMM-shaped kernel (64 rows x 32 units per
+                                workgroup, cell update fused); needs H*sizeof(dtype) a multiple of 16,
+                                16-byte aligned y, h0 and W_hh, else LSTM_ERR_UNSUPPORTED */
 } lstm_recurrence;
 
 typedef enum {

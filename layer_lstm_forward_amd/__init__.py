@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblstm_amd.so")
 
 LSTM_F32, LSTM_BF16 = 0, 1
-LSTM_REC_AUTO, LSTM_REC_STEP, LSTM_REC_PERSISTENT = 0, 1, 2
+LSTM_REC_AUTO, LSTM_REC_STEP, LSTM_REC_PERSISTENT, LSTM_REC_GEMM = 0, 1, 2, 3
 LSTM_OPT_RECURRENCE, LSTM_OPT_REC_TILE, LSTM_OPT_TIMING = 1, 2, 3
 LSTM_OPT_PARTIAL_BUFFERS, LSTM_OPT_POLL_SLEEP, LSTM_OPT_TEAM_ROWS = 4, 5, 7
 LSTM_OPT_PROJ_TILE = 8

@@ -79,5 +79,10 @@ const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant)
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
+// One recurrent step (a.s_begin) as a GEMM with the cell update fused
+// (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.
+// rec_step_gemm_ok: its alignment and 31-bit offset requirements hold.
+bool rec_step_gemm_ok(const RecArgs &a, int dtype);
+hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s);
 
 }  // namespace lstm_amd

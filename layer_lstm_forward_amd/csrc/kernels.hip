@@ -16,6 +16,8 @@
 //           one launch per step, or one persistent launch per layer with the
 //           W_hh slices resident in LDS; workgroups hand h_t to each other
 //           through step-tagged words instead of a grid barrier.
+//   k_rec_step  one step of the recurrence as a GEMM with the cell update
+//           fused, for layers whose W_hh does not stay on chip.
 //   k_fill  clears the status word and the exchange buffer.
 #include "device.h"
 #include "kernels.h"
@@ -675,6 +677,168 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     }
 }
 
+// ===========================================================================
+// Recurrence, one step as a GEMM.  For layers whose W_hh does not stay on
+// chip, each step is one launch of this kernel: S = h_{t-1} W_hh^T for a block
+// of 64 batch rows and 32 hidden units, followed in the same kernel by the
+// gate nonlinearities and the cell update (the equation block of the
+// warp-nn LSTM page) for those 64 x 32 cells.  h_{t-1} is read from y of the
+// previous step (or h0), which the launch boundary has made visible, so no
+// exchange words are needed.  The block's 128 rows of W_hh are gathered
+// gate-major (row r: gate r / 32, unit u0 + r % 32), so that in the 32x32
+// MFMA output layout each lane holds all four gate pre-activations of its
+// cells and the cell update needs no data exchange.  Operands stream from
+// global memory straight into LDS (128 bytes of K per row per stage,
+// double-buffered, XOR-swizzled 16-byte segments as in k_proj_dma); the four
+// waves are two row halves x two K halves, whose partial sums meet in LDS.
+// c is carried across launches in cstate.
+// ===========================================================================
+template <class DT>
+__global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 64, BR = 128, SEG = 8;  // A rows, W rows per block; segments per row
+    constexpr int KS = SEG * DT::PER16;          // K per stage
+    constexpr int STAGE = (BM + BR) * SEG;       // 16-byte segments per stage
+    constexpr unsigned OOR = 0x80000000u;
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w & 1, wk = w >> 1;
+    const int H = a.H, B = a.B, T = a.T, D = a.D;
+    const int d = blockIdx.z;
+    const int s = a.s_begin;
+    const int t = d == 0 ? s : T - 1 - s;
+    const int nmb = (B + BM - 1) / BM, nub = (H + 31) / 32;
+    int mb, ub;
+    {
+        const int bid = blockIdx.x;
+        if ((nub & 7) == 0) {
+            // the row blocks of one unit block run on the same XCD (round-robin
+            // dispatch), so its W_hh rows are fetched into that XCD's L2 once
+            const int idx = bid >> 3;
+            ub = (bid & 7) + 8 * (idx / nmb);
+            mb = idx % nmb;
+        } else {
+            ub = bid / nmb;
+            mb = bid % nmb;
+        }
+    }
+    const int b0 = mb * BM, u0 = ub * 32;
+    const int es = (int)sizeof(S);
+    const size_t ldy = (size_t)D * H;
+    const size_t ldg = (size_t)D * 4 * H;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+    // h_{t-1}: rows b0.. of y at the previous step, or of h0 at s = 0
+    const S *hsrc = nullptr;
+    size_t lda = 0;
+    if (s > 0) {
+        const int tp = d == 0 ? s - 1 : T - s;
+        hsrc = static_cast<const S *>(a.Y) + ((size_t)tp * B + b0) * ldy + (size_t)d * H;
+        lda = ldy;
+    } else if (a.h0) {
+        hsrc = static_cast<const S *>(a.h0) + ((size_t)d * B + b0) * H;
+        lda = H;
+    }
+    if (hsrc) {
+        const int rows = min(BM, B - b0);
+        const unsigned abytes = (unsigned)((((size_t)rows - 1) * lda + H) * es);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(hsrc), (short)0, (int)abytes, 0x00020000);
+        const S *W = static_cast<const S *>(a.whh[d]);
+        const unsigned wbytes = (unsigned)((size_t)4 * H * H * es);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
+
+        // this lane's slot in each 1 KiB block: row (lane / 8) of the block, swizzled segment (lane % 8)
+        const int brow = lane >> 3, pseg = lane & 7;
+        auto issue = [&](int kt, int buf) {
+            u32x4 *st = lds + buf * STAGE;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int blk = w + 4 * i;  // 8 blocks of A rows, then 16 of W rows
+                const int row = blk * 8 + brow;
+                const int lseg = pseg ^ ((row >> 1) & 7);
+                const int k = kt * KS + lseg * DT::PER16;
+                unsigned off;
+                if (blk < BM / 8) {
+                    off = k < H ? (unsigned)(((size_t)row * lda + k) * es) : OOR;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + blk * 64), 16, off, 0, 0, 0);
+                } else {
+                    const int r = row - BM, u = u0 + (r & 31);
+                    off = (k < H && u < H) ? (unsigned)(((size_t)((r >> 5) * H + u) * H + k) * es) : OOR;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(st + blk * 64), 16, off, 0, 0, 0);
+                }
+            }
+        };
+        auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
+
+        const int nk = (H + KS - 1) / KS;
+        issue(0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt & 1;
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage kt are in LDS
+            __syncthreads();                 // everyone's are, and stage kt-1 is no longer read
+            if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+            const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+            // this wave's two 32-byte sub-chunks of the stage: wk and wk + 2
+            u32x4 af[2], bw[2][4];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int sg = 2 * (wk + 2 * c) + (lane >> 5);
+                af[c] = sa[swz(wm * 32 + (lane & 31), sg)];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bw[c][j] = sb[swz(32 * j + (lane & 31), sg)];
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = mma32_chunk(DT{}, acc[j], af[c], bw[c][j]);
+        }
+        __syncthreads();  // the stage buffers are reused below
+    }
+
+    // The two K halves meet: wave (wm, wk) finishes the result registers
+    // v in [8 wk, 8 wk + 8) and hands the other half to its partner.
+    float *red = reinterpret_cast<float *>(smem);  // [4 waves][32 values][64 lanes]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) red[((size_t)w * 32 + j * 8 + vv) * 64 + lane] = acc[j][8 * (1 - wk) + vv];
+    __syncthreads();
+    const int partner = wm + 2 * (1 - wk);
+    const int u = u0 + (lane & 31);
+    const bool last = s == T - 1;
+#pragma unroll
+    for (int vv = 0; vv < 8; ++vv) {
+        const int v = 8 * wk + vv;
+        const int m = b0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m >= B || u >= H) continue;
+        float pre[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[j] = acc[j][v] + red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane];
+        const float *g = a.G + ((size_t)t * B + m) * ldg + (size_t)d * 4 * H + u;
+        const size_t si = ((size_t)d * B + m) * H + u;
+        const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
+        const float ig = sigmoid_f(pre[0] + g[0]);
+        const float fg = sigmoid_f(pre[1] + g[(size_t)H]);
+        const float gg = tanh_f(pre[2] + g[(size_t)2 * H]);
+        const float og = sigmoid_f(pre[3] + g[(size_t)3 * H]);
+        const float cn = fg * cp + ig * gg;
+        const S hs = DT::from_f(og * tanh_f(cn));
+        a.cstate[si] = cn;
+        static_cast<S *>(a.Y)[((size_t)t * B + m) * ldy + (size_t)d * H + u] = hs;
+        if (last) {
+            if (a.hn) static_cast<S *>(a.hn)[si] = hs;
+            if (a.cn) a.cn[si] = cn;
+        }
+    }
+}
+
 __global__ void k_fill(unsigned *p, size_t n, unsigned v) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -798,6 +962,27 @@ hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool 
     RecArgs copy = a;
     void *args[] = {&copy};
     if (cooperative) return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)smem, s);
+    return hipLaunchKernel(fn, grid, block, args, smem, s);
+}
+
+bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
+    const size_t es = dtype == DT_BF16 ? 2 : 4;
+    bool ok = ((size_t)a.H * es) % 16 == 0 && (size_t)4 * a.H * a.H * es < (1u << 31) &&
+              ((size_t)64 * a.D * a.H * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
+              (!a.h0 || (uintptr_t)a.h0 % 16 == 0);
+    for (int d = 0; d < a.D; ++d) ok = ok && (uintptr_t)a.whh[d] % 16 == 0;
+    return ok;
+}
+
+hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
+    const void *fn = dtype == DT_BF16 ? reinterpret_cast<const void *>(&k_rec_step<BF16>)
+                                      : reinterpret_cast<const void *>(&k_rec_step<F32>);
+    const size_t smem = 2 * (64 + 128) * 8 * 16;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid(((a.B + 63) / 64) * ((a.H + 31) / 32), 1, a.D), block(256);
+    RecArgs copy = a;
+    void *args[] = {&copy};
     return hipLaunchKernel(fn, grid, block, args, smem, s);
 }
 

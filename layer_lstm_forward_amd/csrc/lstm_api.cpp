@@ -165,7 +165,7 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
     Sched best{};
     double best_cost = 1e300;
     bool found = false;
-    const bool want_step = p->rec_mode == LSTM_REC_STEP;
+    const bool want_step = p->rec_mode == LSTM_REC_STEP || p->rec_mode == LSTM_REC_GEMM;
     for (const RecTile &t : kTiles) {
         if (p->rec_tile && p->rec_tile != 100 * t.WK + 10 * t.MTW + t.NT) continue;
         Sched s{};
@@ -195,6 +195,14 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
     if (!found) return LSTM_ERR_UNSUPPORTED;
     *out = best;
     return LSTM_OK;
+}
+
+// Shape conditions of the per-step GEMM kernel (k_rec_step); pointer
+// alignment is checked per call.
+bool gemm_step_shape_ok(const lstm_plan *p) {
+    const size_t es = elem_size(p->dtype);
+    return p->rec_mode != LSTM_REC_STEP && ((size_t)p->H * es) % 16 == 0 &&
+           (size_t)4 * p->H * p->H * es < (1u << 31) && (size_t)64 * p->D * p->H * es < (1u << 31);
 }
 
 hipEvent_t take_event(lstm_plan *p) {
@@ -350,7 +358,7 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
     if (!p) return LSTM_ERR_ARG;
     switch (option) {
         case LSTM_OPT_RECURRENCE:
-            if (value < LSTM_REC_AUTO || value > LSTM_REC_PERSISTENT) return LSTM_ERR_UNSUPPORTED;
+            if (value < LSTM_REC_AUTO || value > LSTM_REC_GEMM) return LSTM_ERR_UNSUPPORTED;
             p->rec_mode = value;
             return LSTM_OK;
         case LSTM_OPT_PARTIAL_BUFFERS:
@@ -408,13 +416,19 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     const int rc = choose_sched(p, B, dev, &s);
     if (rc != LSTM_OK) return (lstm_status)rc;
     const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
+    const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
+    const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
+    if (!s.persistent && gemm_step_shape_ok(p)) {
+        // per-step GEMM (assuming 16-byte aligned operands, as lstm_forward checks)
+        std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_step<%s> mode=gemm-step block=64x32 workgroups=%d launches=T",
+                      proj, dt, dt, ((B + 63) / 64) * ((p->H + 31) / 32) * p->D);
+        return LSTM_OK;
+    }
     std::snprintf(buf, len,
                   "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
                   "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d",
-                  proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile),
-                  p->dtype == LSTM_BF16 ? "bf16" : "f32", p->dtype == LSTM_BF16 ? "bf16" : "f32", s.tile.WK,
-                  s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P, s.BG, s.NGB, s.teams,
-                  s.wgs, s.smem, s.geom.part_bufs, s.map_xcd);
+                  proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
+                  s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd);
     return LSTM_OK;
 }
 
@@ -450,6 +464,20 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
     float *cstate = reinterpret_cast<float *>(ws + lay.cstate);
     const size_t es = elem_size(p->dtype);
     const size_t state_elems = (size_t)p->D * B * p->H;
+
+    // per-step GEMM kernel: usable when the recurrence steps and every layer's
+    // operands meet its alignment (checked before anything is enqueued)
+    bool gemm = !sch.persistent && gemm_step_shape_ok(p);
+    for (int l = 0; l < p->L && gemm; ++l) {
+        RecArgs q{};
+        for (int d = 0; d < p->D; ++d) q.whh[d] = weights[(size_t)(l * p->D + d) * per + 1];
+        q.Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
+        q.h0 = h0 ? static_cast<const char *>(h0) + (size_t)l * state_elems * es : nullptr;
+        q.H = p->H;
+        q.D = p->D;
+        gemm = rec_step_gemm_ok(q, p->dtype);
+    }
+    if (p->rec_mode == LSTM_REC_GEMM && !gemm) return LSTM_ERR_UNSUPPORTED;
 
     if (launch_fill_u32(status, lay.sync_bytes / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
 
@@ -521,10 +549,13 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
             }
         }
         if (stepped) {
+            const bool use_gemm = gemm || (sch.persistent && gemm_step_shape_ok(p) && rec_step_gemm_ok(ra, p->dtype));
             for (int s = 0; s < T; ++s) {
                 ra.s_begin = s;
                 ra.s_end = s + 1;
-                if (launch_rec(ra, sch.tile, sch.smem, p->dtype, false, st) != hipSuccess) {
+                const hipError_t e = use_gemm ? launch_rec_step_gemm(ra, p->dtype, st)
+                                              : launch_rec(ra, sch.tile, sch.smem, p->dtype, false, st);
+                if (e != hipSuccess) {
                     (void)hipGetLastError();
                     return LSTM_ERR_LAUNCH;
                 }

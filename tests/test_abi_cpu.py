@@ -74,11 +74,12 @@ def test_workspace_size_layout():
 def test_set_option():
     p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
     try:
+        pkg.lstm_set_option(p, pkg.LSTM_OPT_RECURRENCE, pkg.LSTM_REC_GEMM)
         pkg.lstm_set_option(p, pkg.LSTM_OPT_RECURRENCE, pkg.LSTM_REC_STEP)
         pkg.lstm_set_option(p, pkg.LSTM_OPT_REC_TILE, 412)
         for v in (0, 1000, 100000):
             pkg.lstm_set_option(p, pkg.LSTM_OPT_READ_PACE, v)
-        for opt, val in ((pkg.LSTM_OPT_RECURRENCE, 9), (pkg.LSTM_OPT_REC_TILE, 333), (6, 0),
+        for opt, val in ((pkg.LSTM_OPT_RECURRENCE, 4), (pkg.LSTM_OPT_REC_TILE, 333), (6, 0),
                          (pkg.LSTM_OPT_READ_PACE, -1), (pkg.LSTM_OPT_READ_PACE, 100001), (99, 0)):
             with pytest.raises(pkg.LSTMError) as e:
                 pkg.lstm_set_option(p, opt, val)

@@ -42,6 +42,44 @@ def test_small_shapes(spec, mode):
     assert_parity(got, ref, spec.dtype, m.describe(spec.T, spec.B))
 
 
+def _gemm_step_shape_ok(spec):
+    return (spec.hidden_size * (2 if spec.dtype == "bf16" else 4)) % 16 == 0
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=_id)
+def test_small_shapes_gemm_step(spec):
+    """The per-step GEMM recurrence (k_rec_step) on the small shapes; shapes
+    whose rows are not 16-byte multiples are refused with LSTM_ERR_UNSUPPORTED."""
+    print(f"case {_id(spec)} gemm step", flush=True)
+    inp = make_inputs(spec)
+    if not _gemm_step_shape_ok(spec):
+        with pytest.raises(pkg.LSTMError) as e:
+            run_gpu(inp, recurrence=pkg.LSTM_REC_GEMM)
+        assert e.value.status == -7
+        return
+    got, m = run_gpu(inp, recurrence=pkg.LSTM_REC_GEMM)
+    assert "gemm-step" in m.describe(spec.T, spec.B)
+    assert_parity(got, run_oracle(inp), spec.dtype, "gemm step")
+
+
+@pytest.mark.parametrize("spec", [
+    Spec(32, 256, 2, False, 6, 130, "bf16", 401, "normal0.1"),   # 8 unit blocks (XCD-grouped), 3 row blocks, ragged
+    Spec(40, 96, 1, True, 5, 70, "f32", 402, "normal0.1"),       # 3 unit blocks, 2 row blocks, both directions
+    Spec(24, 520, 1, False, 4, 64, "f32", 403, "zeros"),         # ragged last unit block, K not a stage multiple
+    Spec(16, 64, 3, True, 3, 1, "bf16", 404, "normal0.1"),       # one batch row, three layers
+], ids=_id)
+def test_gemm_step_blocks(spec):
+    """k_rec_step over several row and unit blocks with ragged edges, against
+    the oracle and against the persistent tile kernel."""
+    print(f"case {_id(spec)} gemm step blocks", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    got, m = run_gpu(inp, recurrence=pkg.LSTM_REC_GEMM)
+    assert_parity(got, ref, spec.dtype, "gemm step")
+    pers, _ = run_gpu(inp, recurrence=pkg.LSTM_REC_AUTO)
+    assert_parity(pers, ref, spec.dtype, "auto")
+
+
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
 @pytest.mark.parametrize("proj_tile", [1, 2, 3], ids=["proj128", "proj256", "proj256dma"])
 def test_projection_tiles(spec, proj_tile):
