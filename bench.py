@@ -297,7 +297,10 @@ def main():
     names = dict(re.findall(r"(proj|rec)=(k_[a-z_]+)<", desc))
     if tm["rec_ms"] >= tm["proj_ms"]:
         kname, flops, avg = names.get("rec", "k_rec"), rec_flops_per_launch(spec), rec_avg
-        if tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
+        if kname == "k_rec_pipe":  # one launch runs every layer, and the input products of layers > 0
+            flops = rec_flops_per_launch(spec) * spec.num_layers + proj_flops_per_launch(spec) * spec.num_layers \
+                - 2.0 * spec.T * spec.B * spec.D * 4 * spec.hidden_size * spec.layer_input(0)
+        elif tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
             flops /= spec.T
     else:
         kname, flops, avg = names.get("proj", "k_proj"), proj_flops_per_launch(spec), proj_avg

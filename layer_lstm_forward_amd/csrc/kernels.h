@@ -53,6 +53,39 @@ struct RecArgs {
 
 constexpr int kMaxTeams = 64;
 
+// All layers of a unidirectional stack in one persistent launch (layer
+// pipeline): layer l > 0 consumes layer l-1's h_t from its exchange buffer in
+// the same step and multiplies [x_t; h_{t-1}] by its resident [W_ih; W_hh]
+// slice, so its input projection is never materialised and the layers' time
+// loops overlap instead of running one after the other.
+constexpr int kMaxPipeLayers = 4;
+struct PipeArgs {
+    const void *whh[kMaxPipeLayers];   // [4H, H] dtype
+    const void *wih[kMaxPipeLayers];   // [4H, H] dtype (layers >= 1; their input width is H)
+    const void *b_ih[kMaxPipeLayers];  // [4H] dtype or NULL (layers >= 1)
+    const void *b_hh[kMaxPipeLayers];
+    const float *G;                    // [T, B, 4H] projection of layer 0 incl. both biases
+    const void *h0;                    // [L, B, H] dtype, or NULL (zeros)
+    const float *c0;                   // [L, B, H] or NULL
+    void *Y;                           // [T, B, H] dtype: output of the last layer
+    void *hn;                          // [L, B, H] dtype or NULL
+    float *cn;                         // [L, B, H] or NULL
+    unsigned long long *xbuf[kMaxPipeLayers];  // per layer: [slots][NGB] regions of (ROWS/16)*kch*256 tagged words
+    int xslots[kMaxPipeLayers];        // T (one slot per step) or 2 (parities, last layer)
+    unsigned tag_base[kMaxPipeLayers]; // tags of layer l are tag_base[l] + s + 1
+    unsigned *status;
+    int L, T, B, H;
+    int P;                             // workgroups per (layer, batch group)
+    int BG, NGB;
+    int kch;                           // K chunks of H
+    int kchp[kMaxPipeLayers];          // resident chunks per layer (padded to whole batches per wave)
+    int kchp_max;
+    int nbatch[kMaxPipeLayers];
+    int poll_sleep;
+    int vec;
+    long long timeout_ticks;
+};
+
 // Recurrent tile: 4 waves split (4/WK) ways over batch tiles and WK ways over
 // K; each wave owns MTW 16-row batch tiles; NT 16-column tiles of gate rows
 // (4 hidden units each, gates interleaved) make U = 4*NT units per workgroup.
@@ -77,12 +110,20 @@ hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s)
 // over D directions, given 16-byte aligned operands.
 const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant);
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
+// Layer pipeline (k_rec_pipe): tiles it is built for, its LDS geometry
+// (kchp/nbatch per layer) and its cooperative launch.
+bool pipe_tile_supported(RecTile t);
+RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch);
+hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
+hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s);
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
 // One recurrent step (a.s_begin) as a GEMM with the cell update fused
 // (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.
 // rec_step_gemm_ok: its alignment and 31-bit offset requirements hold.
 bool rec_step_gemm_ok(const RecArgs &a, int dtype);
+// Batch rows per workgroup of k_rec_step (64 with two K slices, or 128).
+int rec_step_rows(int B);
 hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s);
 
 }  // namespace lstm_amd

@@ -16,6 +16,8 @@
 //           one launch per step, or one persistent launch per layer with the
 //           W_hh slices resident in LDS; workgroups hand h_t to each other
 //           through step-tagged words instead of a grid barrier.
+//   k_rec_pipe  every layer of a unidirectional stack in one persistent
+//           launch, layer l consuming layer l-1's h_t as it is produced.
 //   k_rec_step  one step of the recurrence as a GEMM with the cell update
 //           fused, for layers whose W_hh does not stay on chip.
 //   k_fill  clears the status word and the exchange buffer.
@@ -127,6 +129,27 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
         }
 }
 
+// Output-tile order of the 256x256 GEMM kernels.  Workgroups are dispatched
+// round-robin over the 8 XCDs, each with its own L2.  The 32 workgroups an
+// XCD runs together get a 4x8 block of tiles (4 row bands x 8 column bands),
+// so the 4 A panels and 8 W panels they stream are fetched into that L2 once
+// and shared, instead of every tile of one row band streaming all of W.
+__device__ inline void gemm_tile_order(int bid, int ntm, int ntn, int &tm, int &tn) {
+    const int ntiles = ntm * ntn;
+    if (ntm % 4 == 0 && ntn % 8 == 0 && ntiles % 256 == 0) {
+        const int xcd = bid & 7, li = bid >> 3;
+        const int grp = (li >> 5) * 8 + xcd, pos = li & 31;
+        const int ngc = ntn / 8;
+        tm = (grp / ngc) * 4 + (pos >> 3);
+        tn = (grp % ngc) * 8 + (pos & 7);
+    } else {
+        int tile = bid;
+        if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+        tm = tile / ntn;
+        tn = tile % ntn;
+    }
+}
+
 // ===========================================================================
 // Projection GEMM, large tiles.  256x256 output tile per 256-thread workgroup;
 // each wave owns a 128x128 quadrant as 4x4 tiles of 32x32 (v_mfma_f32_32x32x16
@@ -134,8 +157,7 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 // of the 128x128 kernel.  Stages of 128 bytes of K per row are double-buffered
 // in LDS (128 KiB), with 16-byte segments XOR-swizzled by (row/2) % 8 so that a
 // wave's fragment read of 16 consecutive rows touches 16 distinct bank groups.
-// Tiles are numbered so that each XCD works on a contiguous range (rows of the
-// output advance slowest), keeping an A panel within one XCD's L2.
+// Tiles are ordered by gemm_tile_order: 4x8 tile blocks per XCD.
 // ===========================================================================
 template <class DT, bool VEC>
 __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
@@ -150,11 +172,9 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
     const int wm = w >> 1, wn = w & 1;
     const int d = blockIdx.z;
     const int M = a.M, N = a.N, K = a.K;
-    const int ntn = (N + BN - 1) / BN;
-    const int ntiles = ((M + BM - 1) / BM) * ntn;
-    int tile = blockIdx.x;
-    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
-    const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+    int tm, tn;
+    gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
     const S *X = static_cast<const S *>(a.X);
     const S *W = static_cast<const S *>(a.W[d]);
 
@@ -242,6 +262,7 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
 // strides to be multiples of 16 bytes.
 // ===========================================================================
 typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr unsigned OOR_STEP = 0x80000000u;  // a buffer offset past any resource: reads zero
 
 template <class DT>
 __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
@@ -257,11 +278,9 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
     const int wm = w >> 1, wn = w & 1;
     const int d = blockIdx.z;
     const int M = a.M, N = a.N, K = a.K;
-    const int ntn = (N + BN - 1) / BN;
-    const int ntiles = ((M + BM - 1) / BM) * ntn;
-    int tile = blockIdx.x;
-    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
-    const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+    int tm, tn;
+    gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
     const int es = (int)sizeof(S);
     const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx;
     const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * K;
@@ -678,33 +697,373 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 }
 
 // ===========================================================================
+// Layer pipeline.  All L layers of a unidirectional stack run in one
+// persistent launch.  Workgroup roles: layer l, batch group gb, unit slice p
+// (hidden units [p*U, p*U+U)), as in k_rec.  Layer 0 multiplies h_{t-1} by
+// its W_hh slice and adds the hoisted projection G[t], exactly as k_rec.
+// Layer l > 0 has no hoisted projection: its resident slice is [W_ih; W_hh]
+// (K = 2H; the warp-nn equation block's input and hidden products share one
+// accumulator), the first H of K come from layer l-1's h_t (read from that
+// layer's exchange buffer at the same step) and the rest from its own
+// h_{t-1}; both biases are added in the epilogue.  Layer l's time loop thus
+// trails layer l-1's by about one step instead of starting after it ends,
+// and the input half of its K range is multiplied while its own h_{t-1} is
+// still on the way.  Layers that feed another have one exchange slot per
+// step (nothing is overwritten, so a layer may run ahead of its consumer);
+// the last layer alternates two.
+// ===========================================================================
+template <class DT, int WK, int MTW, int NT, int CB>
+__global__ __launch_bounds__(256) void k_rec_pipe(PipeArgs a) {
+    using S = typename DT::S;
+    constexpr bool BF = sizeof(S) == 2;
+    constexpr int WM = 4 / WK;
+    constexpr int MT = WM * MTW;
+    constexpr int ROWS = 16 * MT;
+    constexpr int NCOL = 16 * NT;
+    constexpr int U = 4 * NT;
+    constexpr int PSTR = NCOL + 4;
+    constexpr int CELLS = ROWS * U;
+    constexpr int CPT = (CELLS + 255) / 256;
+    constexpr int EW = BF ? 2 : 1;  // K values per exchange word
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_bad;
+    u32x4 *Wf = reinterpret_cast<u32x4 *>(smem);
+    float *part = reinterpret_cast<float *>(smem + (size_t)a.kchp_max * NT * 1024);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w / WK, wk = w % WK;
+    const int per_layer = a.NGB * a.P;
+    const int l = blockIdx.x / per_layer;
+    const int gb = (blockIdx.x % per_layer) / a.P, p = blockIdx.x % a.P;
+    const int H = a.H, B = a.B, T = a.T, L = a.L, kch = a.kch;
+    const int b0 = gb * a.BG, rows = min(a.BG, B - b0);
+    const int j0 = p * U, units = min(U, H - j0);
+    const bool vec = a.vec != 0;
+    const int kin = l > 0 ? kch : 0;  // chunks of the input segment
+    const int ktot = kin + kch;
+    const int kchp = a.kchp[l];
+
+    // Resident slice as fragments [chunk][n-tile][lane] x 16 bytes: chunk c < kin
+    // holds W_ih rows, the rest W_hh rows; zero beyond H and in padding chunks.
+    {
+        const S *Wi = static_cast<const S *>(a.wih[l]);
+        const S *Wh = static_cast<const S *>(a.whh[l]);
+        const int nfrag = kchp * NT * 64;
+        for (int f = tid; f < nfrag; f += 256) {
+            const int ln = f & 63, nt = (f >> 6) % NT, c = (f >> 6) / NT;
+            const int n = nt * 16 + (ln & 15), u = n >> 2, q = n & 3;
+            const bool inp = c < kin;
+            const int k = (inp ? c : c - kin) * DT::KC + (ln >> 4) * DT::PER16;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (c < ktot && u < units && k < H)
+                v = load_frag<DT>((inp ? Wi : Wh) + (size_t)(q * H + j0 + u) * H, k, H, vec);
+            Wf[f] = v;
+        }
+    }
+
+    // Cells of this thread: (batch row cm, hidden unit cu).
+    int cm[CPT], cu[CPT];
+    bool cv[CPT];
+    float creg[CPT];
+    float bias[CPT][4];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int e = tid + 256 * i;
+        cm[i] = e / U;
+        cu[i] = e % U;
+        cv[i] = e < CELLS && cm[i] < rows && cu[i] < units;
+        creg[i] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bias[i][q] = 0.f;
+        if (cv[i]) {
+            const size_t si = ((size_t)l * B + b0 + cm[i]) * H + j0 + cu[i];
+            creg[i] = a.c0 ? a.c0[si] : 0.f;
+            if (l > 0 && a.b_ih[l]) {
+                const S *bi = static_cast<const S *>(a.b_ih[l]), *bh = static_cast<const S *>(a.b_hh[l]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = q * H + j0 + cu[i];
+                    bias[i][q] = DT::to_f(bi[r]) + DT::to_f(bh[r]);
+                }
+            }
+        }
+    }
+    if (tid == 0) s_bad = 0;
+
+    // G[t] of layer 0's cells, loaded two steps ahead (as in k_rec).
+    const size_t ldg = (size_t)4 * H;
+    float gcur[CPT][4], gnext[CPT][4];
+    auto load_g = [&](int step, float (&g)[CPT][4]) {
+        const int tg = step;
+        const bool in = step < T && l == 0;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const bool ok = in && cv[i];
+            const float *gp = a.G + ((size_t)(ok ? tg : 0) * B + b0 + (ok ? cm[i] : 0)) * ldg + j0 + (ok ? cu[i] : 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[i][q] = ok ? gp[(size_t)q * H] : 0.f;
+        }
+    };
+    load_g(0, gcur);
+    load_g(1, gnext);
+    __syncthreads();
+
+    const int nb = a.nbatch[l];                    // chunk batches per wave
+    const int cw0 = wk * nb * CB;                  // first chunk of this wave
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int mw = wm * MTW * 16 + (lane & 15);    // this lane's team row in tile i: mw + 16 i
+    const int ksub = (lane >> 4) * DT::PER16;      // this lane's K offset inside a chunk
+    const size_t region = (size_t)MT * kch * 256;  // exchange words per batch group and slot
+    auto xslot = [&](int layer, int step) {
+        const int sl = a.xslots[layer] == 2 ? (step & 1) : step;
+        return a.xbuf[layer] + ((size_t)sl * a.NGB + gb) * region;
+    };
+
+    for (int s = 0; s < T; ++s) {
+        f32x4 acc[MTW][NT];
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bool wave_ok = true;
+
+        // at s = 0 the hidden segment comes from h0 (plain loads) or is zero
+        if (s == 0 && a.h0) {
+            const S *hs = static_cast<const S *>(a.h0) + (size_t)l * B * H;
+            for (int c = max(cw0, kin); c < min(cw0 + nb * CB, ktot); ++c) {
+                u32x4 af[MTW];
+                const int k = (c - kin) * DT::KC + ksub;
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) {
+                    const int m = mw + 16 * i;
+                    af[i] = (m < rows && k < H) ? load_frag<DT>(hs + (size_t)(b0 + m) * H, k, H, vec) : zero;
+                }
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const u32x4 bw = Wf[(c * NT + j) * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
+                }
+            }
+        }
+
+        // exchange segments: input (layer l-1's h_s) and hidden (own h_{s-1})
+        const unsigned tag_in = l > 0 ? a.tag_base[l - 1] + (unsigned)s + 1u : 0u;
+        const unsigned tag_h = a.tag_base[l] + (unsigned)s;
+        const __amdgpu_buffer_rsrc_t xin = xrsrc(l > 0 ? xslot(l - 1, s) : a.xbuf[0], (unsigned)(region * 8));
+        const __amdgpu_buffer_rsrc_t xh = xrsrc(xslot(l, s > 0 ? s - 1 : 0), (unsigned)(region * 8));
+        for (int bi = 0; bi < nb && wave_ok; ++bi) {
+            const int c0 = cw0 + bi * CB;
+            if (c0 >= ktot || (s == 0 && c0 >= kin)) break;  // nothing from the exchange past here
+            // Each lane reads its fragment as two 16-byte pairs of tagged words;
+            // for a fixed pair index the 64 lanes read 1 KB in a row.  A chunk's
+            // source and expected tag are uniform over the wave.
+            u32x4 wd[CB][MTW][2];
+            unsigned off[CB][MTW][2];
+            bool lv[CB][MTW][4];
+            bool isin[CB];
+            unsigned tg[CB];
+#pragma unroll
+            for (int ci = 0; ci < CB; ++ci) {
+                const int c = c0 + ci;
+                isin[ci] = c < kin;
+                tg[ci] = isin[ci] ? tag_in : tag_h;
+                const bool from_x = c < ktot && (isin[ci] || s > 0);
+                const int cc = isin[ci] ? c : c - kin;  // chunk within its source
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) {
+                    const int m = mw + 16 * i;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lv[ci][i][e] = from_x && m < rows && cc * DT::KC + ksub + e * EW < H;
+#pragma unroll
+                    for (int eh = 0; eh < 2; ++eh)
+                        off[ci][i][eh] = lv[ci][i][2 * eh]
+                                             ? (unsigned)(((((wm * MTW + i) * kch + cc) * 2 + eh) * 128 + 2 * lane) * 8)
+                                             : 0x7FFFFFF0u;  // out of range: reads zeros, no memory access
+                }
+            }
+#pragma unroll
+            for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                    for (int eh = 0; eh < 2; ++eh) wd[ci][i][eh] = xload2(isin[ci] ? xin : xh, off[ci][i][eh]);
+            // a dead word (padding row or chunk, K past H) counts as current and zero
+            auto settle = [&](int ci, int i, int eh) {
+                if (!lv[ci][i][2 * eh]) { wd[ci][i][eh].x = 0u; wd[ci][i][eh].y = tg[ci]; }
+                if (!lv[ci][i][2 * eh + 1]) { wd[ci][i][eh].z = 0u; wd[ci][i][eh].w = tg[ci]; }
+            };
+            auto pair_ok = [&](int ci, int i, int eh) {
+                return wd[ci][i][eh].y == tg[ci] && wd[ci][i][eh].w == tg[ci];
+            };
+            bool mine = true;
+#pragma unroll
+            for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                    for (int eh = 0; eh < 2; ++eh) {
+                        settle(ci, i, eh);
+                        mine = mine && pair_ok(ci, i, eh);
+                    }
+            if (!__all(mine)) {
+                // slow path: back off, then re-read only the pairs that are stale
+                unsigned spins = 0;
+                const long long t0 = wall_clock64();
+                do {
+                    if ((++spins & 31u) == 0) {
+                        const unsigned st = __builtin_amdgcn_readfirstlane(
+                            __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                        if (st != 0u) {
+                            wave_ok = false;
+                            break;
+                        }
+                        if (wall_clock64() - t0 > a.timeout_ticks) {
+                            if (lane == 0)
+                                __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            wave_ok = false;
+                            break;
+                        }
+                    }
+                    for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
+                    mine = true;
+#pragma unroll
+                    for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                            for (int eh = 0; eh < 2; ++eh) {
+                                if (!pair_ok(ci, i, eh)) {
+                                    wd[ci][i][eh] = xload2(isin[ci] ? xin : xh, off[ci][i][eh]);
+                                    settle(ci, i, eh);
+                                }
+                                mine = mine && pair_ok(ci, i, eh);
+                            }
+                } while (!__all(mine));
+                if (!wave_ok) break;
+            }
+#pragma unroll
+            for (int ci = 0; ci < CB; ++ci) {
+                u32x4 bw[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) bw[j] = Wf[((c0 + ci) * NT + j) * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) {
+                    const u32x4 af = {wd[ci][i][0].x, wd[ci][i][0].z, wd[ci][i][1].x, wd[ci][i][1].z};
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[i][j] = mma_chunk(DT{}, acc[i][j], af, bw[j]);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = (wm * MTW + i) * 16 + 4 * (lane >> 4) + v;
+                    const int n = j * 16 + (lane & 15);
+                    part[(wk * ROWS + m) * PSTR + n] = acc[i][j][v];
+                }
+        if (!wave_ok) s_bad = 1;
+        __syncthreads();
+        if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+
+        const unsigned long long tag_out = (unsigned long long)(a.tag_base[l] + (unsigned)s + 1u) << 32;
+        unsigned long long *xo = xslot(l, s);
+        const bool publish = s + 1 < T || l + 1 < L;
+        const bool last_layer = l + 1 == L;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            // every lane of the wave takes part in the shuffle below
+            float hv = 0.f;
+            S hs = (S)0;
+            if (cv[i]) {
+                const float *pp = &part[cm[i] * PSTR + 4 * cu[i]];
+                f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
+#pragma unroll
+                for (int kk = 1; kk < WK; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
+                const float ig = sigmoid_f(sum.x + gcur[i][0] + bias[i][0]);
+                const float fg = sigmoid_f(sum.y + gcur[i][1] + bias[i][1]);
+                const float gg = tanh_f(sum.z + gcur[i][2] + bias[i][2]);
+                const float og = sigmoid_f(sum.w + gcur[i][3] + bias[i][3]);
+                const float cn = fg * creg[i] + ig * gg;
+                creg[i] = cn;
+                hv = og * tanh_f(cn);
+                hs = DT::from_f(hv);
+            }
+            // word of (team row m, k) in the consumers' order:
+            // ((tile * kch + chunk) * 2 + e / 2) * 128 + 2 * lane + e % 2, lane = 16 * g + m % 16
+            const int m = cm[i], jj = j0 + cu[i];
+            if (BF) {
+                // units jj (even) and jj + 1 share a word; the even lane stores it
+                const uint32_t mine_bits = (uint32_t)(uint16_t)hs;
+                const uint32_t nb_bits = (uint32_t)__shfl_xor((int)mine_bits, 1);
+                if (publish && cv[i] && (cu[i] & 1) == 0) {
+                    const int c = jj >> 5, g = (jj >> 3) & 3, e = (jj >> 1) & 3;
+                    const uint32_t hi = cu[i] + 1 < units ? nb_bits : 0u;
+                    xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
+                           tag_out | (mine_bits | (hi << 16)));
+                }
+            } else if (publish && cv[i]) {
+                const int c = jj >> 4, g = (jj >> 2) & 3, e = jj & 3;
+                xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
+                       tag_out | __float_as_uint(hv));
+            }
+            if (cv[i]) {
+                const int bb = b0 + m;
+                if (last_layer) static_cast<S *>(a.Y)[((size_t)s * B + bb) * H + jj] = hs;
+                if (s == T - 1) {
+                    const size_t si = ((size_t)l * B + bb) * H + jj;
+                    if (a.hn) static_cast<S *>(a.hn)[si] = hs;
+                    if (a.cn) a.cn[si] = creg[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gcur[i][q] = gnext[i][q];
+        load_g(s + 2, gnext);
+        __syncthreads();  // partials are reused by the next step
+    }
+}
+
+// ===========================================================================
 // Recurrence, one step as a GEMM.  For layers whose W_hh does not stay on
 // chip, each step is one launch of this kernel: S = h_{t-1} W_hh^T for a block
-// of 64 batch rows and 32 hidden units, followed in the same kernel by the
-// gate nonlinearities and the cell update (the equation block of the
-// warp-nn LSTM page) for those 64 x 32 cells.  h_{t-1} is read from y of the
-// previous step (or h0), which the launch boundary has made visible, so no
-// exchange words are needed.  The block's 128 rows of W_hh are gathered
-// gate-major (row r: gate r / 32, unit u0 + r % 32), so that in the 32x32
-// MFMA output layout each lane holds all four gate pre-activations of its
-// cells and the cell update needs no data exchange.  Operands stream from
-// global memory straight into LDS (128 bytes of K per row per stage,
-// double-buffered, XOR-swizzled 16-byte segments as in k_proj_dma); the four
-// waves are two row halves x two K halves, whose partial sums meet in LDS.
-// c is carried across launches in cstate.
+// of BM = 32*WM batch rows and 32 hidden units, followed in the same kernel by
+// the gate nonlinearities and the cell update (the equation block of the
+// warp-nn LSTM page) for those cells.  h_{t-1} is read from y of the previous
+// step (or h0), which the launch boundary has made visible, so no exchange
+// words are needed.  The block's 128 rows of W_hh are gathered gate-major
+// (row r: gate r / 32, unit u0 + r % 32), so that in the 32x32 MFMA output
+// layout each lane holds all four gate pre-activations of its cells and the
+// cell update needs no data exchange.  Operands stream from global memory
+// straight into LDS (128 bytes of K per row per stage, XOR-swizzled 16-byte
+// segments as in k_proj_dma) through a ring of NST stages, so that several
+// stages of loads are in flight while one is multiplied.  The four waves are
+// WM row slices x (4/WM) K slices; K slices' partial sums meet in LDS.  The
+// per-step traffic is bounded by the L2-to-CU bandwidth, (BM + 128) rows of
+// K per workgroup: taller blocks read less in total, shorter ones spread the
+// products over more CUs.  c is carried across launches in cstate.
 // ===========================================================================
-template <class DT>
+template <class DT, int WM>
 __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     using S = typename DT::S;
-    constexpr int BM = 64, BR = 128, SEG = 8;  // A rows, W rows per block; segments per row
+    constexpr int WKS = 4 / WM;                  // K slices
+    constexpr int BM = 32 * WM, BR = 128, SEG = 8;  // A rows, W rows per block; segments per row
     constexpr int KS = SEG * DT::PER16;          // K per stage
     constexpr int STAGE = (BM + BR) * SEG;       // 16-byte segments per stage
-    constexpr unsigned OOR = 0x80000000u;
+    constexpr int NST = WM == 4 ? 4 : 5;         // stages in the LDS ring
+    constexpr int LPS = (BM + BR) / 32;          // 1 KiB loads per wave per stage
     extern __shared__ __align__(16) unsigned char smem[];
     u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w & 1, wk = w >> 1;
+    // the wave index in a scalar register: the operand choice below depends on it
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w % WM, wk = w / WM;
     const int H = a.H, B = a.B, T = a.T, D = a.D;
     const int d = blockIdx.z;
     const int s = a.s_begin;
@@ -759,18 +1118,18 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         auto issue = [&](int kt, int buf) {
             u32x4 *st = lds + buf * STAGE;
 #pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                const int blk = w + 4 * i;  // 8 blocks of A rows, then 16 of W rows
+            for (int i = 0; i < LPS; ++i) {
+                const int blk = w + 4 * i;  // BM/8 blocks of A rows, then 16 of W rows
                 const int row = blk * 8 + brow;
                 const int lseg = pseg ^ ((row >> 1) & 7);
                 const int k = kt * KS + lseg * DT::PER16;
                 unsigned off;
                 if (blk < BM / 8) {
-                    off = k < H ? (unsigned)(((size_t)row * lda + k) * es) : OOR;
+                    off = k < H ? (unsigned)(((size_t)row * lda + k) * es) : OOR_STEP;
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + blk * 64), 16, off, 0, 0, 0);
                 } else {
                     const int r = row - BM, u = u0 + (r & 31);
-                    off = (k < H && u < H) ? (unsigned)(((size_t)((r >> 5) * H + u) * H + k) * es) : OOR;
+                    off = (k < H && u < H) ? (unsigned)(((size_t)((r >> 5) * H + u) * H + k) * es) : OOR_STEP;
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(st + blk * 64), 16, off, 0, 0, 0);
                 }
             }
@@ -778,49 +1137,68 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
 
         const int nk = (H + KS - 1) / KS;
-        issue(0, 0);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage kt are in LDS
-            __syncthreads();                 // everyone's are, and stage kt-1 is no longer read
-            if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
-            const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
-            // this wave's two 32-byte sub-chunks of the stage: wk and wk + 2
-            u32x4 af[2], bw[2][4];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int sg = 2 * (wk + 2 * c) + (lane >> 5);
+        for (int k = 0; k < NST - 1; ++k)
+            if (k < nk) issue(k, k);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt % NST;
+            // this wave's loads of stage kt are in LDS once at most the loads of
+            // the later stages already issued (up to NST-2 of them) are pending
+            constexpr int VM = LPS * (NST - 2);
+            static_assert(VM < 64, "vmcnt field");
+            if (kt + NST - 2 < nk) __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+            else __builtin_amdgcn_s_waitcnt(0);
+            // Everyone's are, and stage kt-1 is no longer read (its fragments were
+            // consumed by the products of the previous iteration).  A bare barrier:
+            // the workgroup fence of __syncthreads would also wait for the loads
+            // of the later stages, which must stay in flight.  The signal fences
+            // keep the compiler from moving LDS accesses across it.
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+            const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+            // this wave's 32-byte sub-chunks of the stage: wk, wk + WKS, ...
+            constexpr int NC = 4 / WKS;
+            u32x4 af[NC], bw[NC][4];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int sg = 2 * (wk + WKS * c) + (lane >> 5);
                 af[c] = sa[swz(wm * 32 + (lane & 31), sg)];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) bw[c][j] = sb[swz(32 * j + (lane & 31), sg)];
             }
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[j] = mma32_chunk(DT{}, acc[j], af[c], bw[c][j]);
         }
         __syncthreads();  // the stage buffers are reused below
     }
 
-    // The two K halves meet: wave (wm, wk) finishes the result registers
+    // With two K slices, wave (wm, wk) finishes the result registers
     // v in [8 wk, 8 wk + 8) and hands the other half to its partner.
+    constexpr int VPW = 16 / WKS;  // result registers finished per wave
     float *red = reinterpret_cast<float *>(smem);  // [4 waves][32 values][64 lanes]
+    const int partner = wm + WM * (1 - wk);
+    if (WKS == 2) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int vv = 0; vv < 8; ++vv) red[((size_t)w * 32 + j * 8 + vv) * 64 + lane] = acc[j][8 * (1 - wk) + vv];
-    __syncthreads();
-    const int partner = wm + 2 * (1 - wk);
+            for (int vv = 0; vv < 8; ++vv) red[((size_t)w * 32 + j * 8 + vv) * 64 + lane] = acc[j][8 * (1 - wk) + vv];
+        __syncthreads();
+    }
     const int u = u0 + (lane & 31);
     const bool last = s == T - 1;
 #pragma unroll
-    for (int vv = 0; vv < 8; ++vv) {
-        const int v = 8 * wk + vv;
+    for (int vv = 0; vv < VPW; ++vv) {
+        const int v = VPW * wk + vv;
         const int m = b0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m >= B || u >= H) continue;
         float pre[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pre[j] = acc[j][v] + red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane];
+        for (int j = 0; j < 4; ++j)
+            pre[j] = acc[j][v] + (WKS == 2 ? red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane] : 0.f);
         const float *g = a.G + ((size_t)t * B + m) * ldg + (size_t)d * 4 * H + u;
         const size_t si = ((size_t)d * B + m) * H + u;
         const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
@@ -953,6 +1331,65 @@ hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256, smem);
 }
 
+#define LSTM_PIPE_TILES(X) X(2, 1, 1) X(2, 1, 2) X(2, 1, 4) X(4, 1, 1) X(4, 1, 2) X(4, 1, 4) X(1, 1, 1) X(1, 1, 2)
+
+bool pipe_tile_supported(RecTile t) {
+#define LSTM_P_OK(wk, mtw, nt) if (t.WK == wk && t.MTW == mtw && t.NT == nt) return true;
+    LSTM_PIPE_TILES(LSTM_P_OK)
+#undef LSTM_P_OK
+    return false;
+}
+
+// LDS geometry of the pipeline: layer 0 holds H of K, the others 2H; the
+// partial sums sit after the largest slice.
+RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch) {
+    RecGeom g{};
+    const int kc = dtype == DT_BF16 ? 32 : 16;
+    g.kch = (H + kc - 1) / kc;
+    const int cb = rec_chunk_batch(t);
+    int kmax = 0;
+    for (int l = 0; l < L; ++l) {
+        const int ktot = (l > 0 ? 2 : 1) * g.kch;
+        const int cpw = (ktot + t.WK - 1) / t.WK;
+        nbatch[l] = (cpw + cb - 1) / cb;
+        kchp[l] = t.WK * nbatch[l] * cb;
+        kmax = kchp[l] > kmax ? kchp[l] : kmax;
+    }
+    g.kchp = kmax;
+    g.part_bufs = 1;
+    g.smem = (size_t)kmax * t.NT * 1024 + (size_t)t.WK * rec_rows_per_wg(t) * (16 * t.NT + 4) * 4;
+    return g;
+}
+
+template <class DT>
+static const void *pipe_kernel_ptr(RecTile t) {
+#define LSTM_P_PTR(wk, mtw, nt)                                                                    \
+    if (t.WK == wk && t.MTW == mtw && t.NT == nt)                                                  \
+        return reinterpret_cast<const void *>(&k_rec_pipe<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8)>);
+    LSTM_PIPE_TILES(LSTM_P_PTR)
+#undef LSTM_P_PTR
+    return nullptr;
+}
+
+hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu) {
+    const void *fn = dtype == DT_BF16 ? pipe_kernel_ptr<BF16>(t) : pipe_kernel_ptr<F32>(t);
+    if (!fn) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256, smem);
+}
+
+hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s) {
+    const void *fn = dtype == DT_BF16 ? pipe_kernel_ptr<BF16>(t) : pipe_kernel_ptr<F32>(t);
+    if (!fn) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid(a.L * a.NGB * a.P), block(256);
+    PipeArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)smem, s);
+}
+
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s) {
     const void *fn = rec_kernel(t, dtype);
     if (!fn) return hipErrorInvalidValue;
@@ -968,22 +1405,32 @@ hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool 
 bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
     const size_t es = dtype == DT_BF16 ? 2 : 4;
     bool ok = ((size_t)a.H * es) % 16 == 0 && (size_t)4 * a.H * a.H * es < (1u << 31) &&
-              ((size_t)64 * a.D * a.H * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
+              ((size_t)128 * a.D * a.H * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
               (!a.h0 || (uintptr_t)a.h0 % 16 == 0);
     for (int d = 0; d < a.D; ++d) ok = ok && (uintptr_t)a.whh[d] % 16 == 0;
     return ok;
 }
 
-hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
-    const void *fn = dtype == DT_BF16 ? reinterpret_cast<const void *>(&k_rec_step<BF16>)
-                                      : reinterpret_cast<const void *>(&k_rec_step<F32>);
-    const size_t smem = 2 * (64 + 128) * 8 * 16;
+// 64-row blocks on all CUs: measured faster than 128-row blocks (which read
+// less in total) at B = 256 -- each CU's load rate is the limit.
+int rec_step_rows(int) { return 64; }
+
+template <class DT, int WM>
+static hipError_t launch_step_t(const RecArgs &a, hipStream_t s) {
+    const void *fn = reinterpret_cast<const void *>(&k_rec_step<DT, WM>);
+    const size_t smem = (size_t)(WM == 4 ? 4 : 5) * (32 * WM + 128) * 8 * 16;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    dim3 grid(((a.B + 63) / 64) * ((a.H + 31) / 32), 1, a.D), block(256);
+    const int bm = 32 * WM;
+    dim3 grid(((a.B + bm - 1) / bm) * ((a.H + 31) / 32), 1, a.D), block(256);
     RecArgs copy = a;
     void *args[] = {&copy};
     return hipLaunchKernel(fn, grid, block, args, smem, s);
+}
+
+hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
+    if (dtype == DT_BF16) return launch_step_t<BF16, 2>(a, s);
+    return launch_step_t<F32, 2>(a, s);
 }
 
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s) {

@@ -22,6 +22,8 @@ struct lstm_plan {
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
     int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next
+    int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
+                       // (off by default: slower than layer by layer on the measured workloads)
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
     // optional per-phase timing (LSTM_OPT_TIMING)
@@ -54,7 +56,15 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 struct Layout {
     size_t status, xbuf, G, ymid[2], cstate, total;
     size_t sync_bytes;  // status word + exchange buffer, zeroed per call
+    size_t pipe_tiles;  // bound on the 16-row tiles of a pipelined schedule
 };
+
+// The layer pipeline applies to unidirectional stacks of 2..kMaxPipeLayers
+// layers in a persistent mode with the option on.
+bool pipe_candidate(const lstm_plan *p) {
+    return p->layer_pipe && p->D == 1 && p->L >= 2 && p->L <= kMaxPipeLayers &&
+           (p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT);
+}
 
 bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     size_t tb, g, y, st, xb;
@@ -67,6 +77,16 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     const size_t kch = (size_t)(p->H + (p->dtype == LSTM_BF16 ? 31 : 15)) / (p->dtype == LSTM_BF16 ? 32 : 16);
     if (!mul_ok((size_t)2 * p->D * (((size_t)B + 255) / 16 + 1), kch * 256 * sizeof(unsigned long long), &xb))
         return false;
+    // the layer pipeline keeps one slot per step for every layer but the last
+    // (pipeline tiles are at most 64 rows, so at most (B + 63) / 16 + 1 tiles)
+    o->pipe_tiles = ((size_t)B + 63) / 16 + 1;
+    if (pipe_candidate(p)) {
+        size_t slots, pb;
+        if (!mul_ok((size_t)T, (size_t)(p->L - 1), &slots) || !mul_ok(slots + 2, o->pipe_tiles, &slots) ||
+            !mul_ok(slots, kch * 256 * sizeof(unsigned long long), &pb))
+            return false;
+        if (pb > xb) xb = pb;
+    }
     if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
@@ -202,7 +222,61 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
 bool gemm_step_shape_ok(const lstm_plan *p) {
     const size_t es = elem_size(p->dtype);
     return p->rec_mode != LSTM_REC_STEP && ((size_t)p->H * es) % 16 == 0 &&
-           (size_t)4 * p->H * p->H * es < (1u << 31) && (size_t)64 * p->D * p->H * es < (1u << 31);
+           (size_t)4 * p->H * p->H * es < (1u << 31) && (size_t)128 * p->D * p->H * es < (1u << 31);
+}
+
+struct PipeSched {
+    RecTile tile;
+    RecGeom geom;
+    int kchp[kMaxPipeLayers], nbatch[kMaxPipeLayers];
+    int U, P, BG, NGB, wgs;
+};
+
+// Pipeline schedule: every (layer, batch group, unit slice) workgroup must be
+// co-resident and layer l > 0's [W_ih; W_hh] slice must fit in LDS.  Among the
+// tiles that fit, take the least matrix-core work per wave on the critical
+// path (the hidden half of a layer l > 0 slice) plus the h fetch.
+bool choose_pipe(const lstm_plan *p, int B, int dev, PipeSched *out) {
+    if (!pipe_candidate(p)) return false;
+    const DevInfo di = dev_info(dev);
+    if (!di.ok) return false;
+    static const RecTile tiles[] = {{2, 1, 2}, {2, 1, 4}, {2, 1, 1}, {4, 1, 2}, {4, 1, 4}, {4, 1, 1}, {1, 1, 2}, {1, 1, 1}};
+    double best = 1e300;
+    bool found = false;
+    for (const RecTile &t : tiles) {
+        if (p->rec_tile && p->rec_tile != 100 * t.WK + 10 * t.MTW + t.NT) continue;
+        if (!pipe_tile_supported(t)) continue;
+        PipeSched s{};
+        s.tile = t;
+        const int rows = rec_rows_per_wg(t);
+        const int cap = p->team_rows > 0 && p->team_rows < rows ? p->team_rows : rows;
+        const int ng0 = (B + cap - 1) / cap;
+        s.BG = (B + ng0 - 1) / ng0;
+        s.NGB = (B + s.BG - 1) / s.BG;
+        s.U = 4 * t.NT;
+        s.P = (p->H + s.U - 1) / s.U;
+        s.wgs = p->L * s.NGB * s.P;
+        // the workspace holds at most (B + 63) / 16 + 1 row tiles per slot
+        if ((size_t)s.NGB * (rows / 16) > ((size_t)B + 63) / 16 + 1) continue;
+        s.geom = pipe_geom(t, p->H, p->dtype, p->L, s.kchp, s.nbatch);
+        if (s.geom.smem > kRecLdsLimit) continue;
+        int bpc = 0;
+        const bool ok = pipe_max_coresident(t, s.geom.smem, p->dtype, &bpc) == hipSuccess && bpc > 0 &&
+                        (long long)bpc * di.cus >= s.wgs;
+        (void)hipGetLastError();
+        if (!ok) continue;
+        const int live_mtw = (s.BG + 15) / 16 < t.MTW ? (s.BG + 15) / 16 : t.MTW;
+        const double mfma = (double)live_mtw * t.NT * ((2.0 * s.geom.kch + t.WK - 1) / t.WK) *
+                            (p->dtype == LSTM_BF16 ? 16 : 128);
+        const double xbytes = (double)s.BG * p->H * (p->dtype == LSTM_BF16 ? 4 : 8) * 2;
+        const double cost = mfma + xbytes / 32.0;
+        if (cost < best) {
+            best = cost;
+            *out = s;
+            found = true;
+        }
+    }
+    return found;
 }
 
 hipEvent_t take_event(lstm_plan *p) {
@@ -310,6 +384,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->part_bufs = 1;
     p->poll_sleep = 2;
     p->read_pace_ns = 0;
+    p->layer_pipe = 0;
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
@@ -369,6 +444,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             if (value < 0 || value > 1000) return LSTM_ERR_UNSUPPORTED;
             p->poll_sleep = value;
             return LSTM_OK;
+        case LSTM_OPT_LAYER_PIPE:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->layer_pipe = value;
+            return LSTM_OK;
         case LSTM_OPT_READ_PACE:
             if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
             p->read_pace_ns = value;
@@ -418,10 +497,20 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
     const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
     const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
+    PipeSched ps{};
+    if (choose_pipe(p, B, dev, &ps)) {
+        std::snprintf(buf, len,
+                      "proj=%s<%s> (layer 0 only); rec=k_rec_pipe<%s,WK=%d,MTW=%d,NT=%d> mode=layer-pipe U=%d P=%d "
+                      "BG=%d NGB=%d layers=%d workgroups=%d lds=%zu",
+                      proj_kernel_name(T * B, 4 * p->H, p->I, 1, p->dtype, p->proj_tile), dt, dt, ps.tile.WK,
+                      ps.tile.MTW, ps.tile.NT, ps.U, ps.P, ps.BG, ps.NGB, p->L, ps.wgs, ps.geom.smem);
+        return LSTM_OK;
+    }
     if (!s.persistent && gemm_step_shape_ok(p)) {
         // per-step GEMM (assuming 16-byte aligned operands, as lstm_forward checks)
-        std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_step<%s> mode=gemm-step block=64x32 workgroups=%d launches=T",
-                      proj, dt, dt, ((B + 63) / 64) * ((p->H + 31) / 32) * p->D);
+        const int bm = rec_step_rows(B);
+        std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_step<%s> mode=gemm-step block=%dx32 workgroups=%d launches=T",
+                      proj, dt, dt, bm, ((B + bm - 1) / bm) * ((p->H + 31) / 32) * p->D);
         return LSTM_OK;
     }
     std::snprintf(buf, len,
@@ -478,6 +567,79 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         gemm = rec_step_gemm_ok(q, p->dtype);
     }
     if (p->rec_mode == LSTM_REC_GEMM && !gemm) return LSTM_ERR_UNSUPPORTED;
+
+    // Layer pipeline: layer 0's projection, then every layer's recurrence in
+    // one cooperative launch.  If the runtime refuses that launch, the
+    // sequential path below redoes the work.
+    PipeSched ps{};
+    if (choose_pipe(p, B, dev, &ps)) {
+        const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
+        const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
+        const size_t slot_words = region_words * ps.NGB;
+        const size_t used_words = slot_words * ((size_t)T * (p->L - 1) + 2);
+        if (launch_fill_u32(status, kStatusBytes / sizeof(unsigned), 0u, st) != hipSuccess ||
+            launch_fill_u32(reinterpret_cast<unsigned *>(xbuf), used_words * 2, 0u, st) != hipSuccess)
+            return LSTM_ERR_LAUNCH;
+        ProjArgs pa{};
+        pa.X = x;
+        pa.G = G;
+        pa.M = T * B;
+        pa.N = 4 * p->H;
+        pa.K = p->I;
+        pa.ldx = p->I;
+        pa.D = 1;
+        pa.W[0] = weights[0];
+        pa.b_ih[0] = p->has_bias ? weights[2] : nullptr;
+        pa.b_hh[0] = p->has_bias ? weights[3] : nullptr;
+        int span = span_begin(p, st, 0);
+        if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) return LSTM_ERR_LAUNCH;
+        span_end(p, span, st, 1);
+
+        PipeArgs qa{};
+        size_t off_words = 0;
+        for (int l = 0; l < p->L; ++l) {
+            const void *const *w = weights + (size_t)l * per;
+            qa.whh[l] = w[1];
+            qa.wih[l] = l > 0 ? w[0] : nullptr;
+            qa.b_ih[l] = (l > 0 && p->has_bias) ? w[2] : nullptr;
+            qa.b_hh[l] = (l > 0 && p->has_bias) ? w[3] : nullptr;
+            qa.xslots[l] = l + 1 < p->L ? T : 2;
+            qa.xbuf[l] = xbuf + off_words;
+            off_words += slot_words * (size_t)qa.xslots[l];
+            qa.tag_base[l] = (unsigned)l * (unsigned)(T + 1);
+            qa.kchp[l] = ps.kchp[l];
+            qa.nbatch[l] = ps.nbatch[l];
+        }
+        qa.G = G;
+        qa.h0 = h0;
+        qa.c0 = c0;
+        qa.Y = y;
+        qa.hn = h_n;
+        qa.cn = c_n;
+        qa.status = status;
+        qa.L = p->L;
+        qa.T = T;
+        qa.B = B;
+        qa.H = p->H;
+        qa.P = ps.P;
+        qa.BG = ps.BG;
+        qa.NGB = ps.NGB;
+        qa.kch = ps.geom.kch;
+        qa.kchp_max = ps.geom.kchp;
+        qa.poll_sleep = p->poll_sleep;
+        qa.vec = (p->H % per16p == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
+        for (int l = 0; l < p->L; ++l)
+            qa.vec = qa.vec && (uintptr_t)qa.whh[l] % 16 == 0 && (!qa.wih[l] || (uintptr_t)qa.wih[l] % 16 == 0);
+        qa.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
+        span = span_begin(p, st, 1);
+        if (launch_pipe(qa, ps.tile, ps.geom.smem, p->dtype, st) == hipSuccess) {
+            span_end(p, span, st, 1);
+            if (p->timing) p->acc.calls += 1;
+            return LSTM_OK;
+        }
+        (void)hipGetLastError();
+        span_end(p, span, st, 0);
+    }
 
     if (launch_fill_u32(status, lay.sync_bytes / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
 

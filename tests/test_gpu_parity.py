@@ -67,10 +67,11 @@ def test_small_shapes_gemm_step(spec):
     Spec(40, 96, 1, True, 5, 70, "f32", 402, "normal0.1"),       # 3 unit blocks, 2 row blocks, both directions
     Spec(24, 520, 1, False, 4, 64, "f32", 403, "zeros"),         # ragged last unit block, K not a stage multiple
     Spec(16, 64, 3, True, 3, 1, "bf16", 404, "normal0.1"),       # one batch row, three layers
+    Spec(48, 160, 2, False, 4, 300, "f32", 405, "normal0.1"),    # 128-row blocks, ragged third
 ], ids=_id)
 def test_gemm_step_blocks(spec):
-    """k_rec_step over several row and unit blocks with ragged edges, against
-    the oracle and against the persistent tile kernel."""
+    """k_rec_step (64- and 128-row blocks) over several row and unit blocks with
+    ragged edges, against the oracle and against the automatic schedule."""
     print(f"case {_id(spec)} gemm step blocks", flush=True)
     inp = make_inputs(spec)
     ref = run_oracle(inp)
@@ -78,6 +79,27 @@ def test_gemm_step_blocks(spec):
     assert_parity(got, ref, spec.dtype, "gemm step")
     pers, _ = run_gpu(inp, recurrence=pkg.LSTM_REC_AUTO)
     assert_parity(pers, ref, spec.dtype, "auto")
+
+
+@pytest.mark.parametrize("spec", [
+    Spec(24, 64, 2, False, 9, 40, "f32", 501, "normal0.1"),     # two layers, two batch groups
+    Spec(33, 52, 3, False, 7, 19, "f32", 502, "zeros"),         # three layers, ragged H (partial unit slice)
+    Spec(40, 96, 4, False, 5, 70, "bf16", 503, "normal0.1"),    # four layers, ragged batch groups
+    Spec(16, 40, 2, False, 6, 3, "bf16", 504, "normal0.1", has_bias=False),
+    Spec(8, 16, 2, False, 1, 1, "f32", 505, "normal0.1"),       # one step, one row
+], ids=_id)
+def test_layer_pipeline(spec):
+    """All layers of a unidirectional stack in one pipelined launch
+    (k_rec_pipe), against the oracle and against the layer-by-layer path."""
+    print(f"case {_id(spec)} layer pipe", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    got, m = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 1})
+    assert "layer-pipe" in m.describe(spec.T, spec.B)
+    assert_parity(got, ref, spec.dtype, "layer pipe")
+    seq, m2 = run_gpu(inp)
+    assert "layer-pipe" not in m2.describe(spec.T, spec.B)
+    assert_parity(seq, ref, spec.dtype, "layer by layer")
 
 
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
@@ -151,11 +173,11 @@ def test_zero_weights_closed_form_on_gpu(dtype):
                     np.testing.assert_allclose(y[t, :, d * H:(d + 1) * H], o * np.tanh(cc), atol=tol, rtol=0)
 
 
-def _full(name, rows):
+def _full(name, rows, options=None):
     spec = WORKLOADS[name]
-    print(f"case {name} rows {rows}", flush=True)
+    print(f"case {name} rows {rows} options {options}", flush=True)
     inp = make_inputs(spec)
-    got, m = run_gpu(inp)
+    got, m = run_gpu(inp, options=options)
     desc = m.describe(spec.T, spec.B)
     y, hn, cn = got
     assert np.all(np.isfinite(y)) and np.all(np.abs(y) <= 1.0)
@@ -173,6 +195,10 @@ def test_full_tiny_l1_in8_h16():
 
 def test_full_l2_in256_h512_b64_f32_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [0, 37, 63])
+
+
+def test_full_l2_in256_h512_b64_f32_layer_pipeline_sampled_rows():
+    _full("l2_in256_h512_t128_b64_f32", [1, 32, 62], options={pkg.LSTM_OPT_LAYER_PIPE: 1})
 
 
 def test_full_l2bi_in512_h1024_b32_bf16_sampled_rows():
