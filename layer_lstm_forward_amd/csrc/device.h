@@ -123,4 +123,44 @@ __device__ inline u32x4 xload2(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1: device scope */);
 }
 
+// ---------------------------------------------------------------------------
+// Compact exchange words (the per-layer recurrence).  A 32-bit word carries
+// the value and a one-bit tag, stored with an agent-scope atomic 32-bit store
+// and read (four words at a time) with the 16-byte sc1 load above; each word
+// is a single-copy atomic unit.  Where the tag lives:
+//   fp32: the least significant mantissa bit.  The value a consumer
+//         multiplies is h or its fp32 neighbour (at most 1 ulp away); NaN
+//         stays NaN.
+//   bf16: bit 30, the top exponent bit of the upper of the two bf16 values.
+//         h = o tanh(c) has |h| <= 1, whose biased exponent is at most 127,
+//         so that bit is always clear in the value itself.  A non-finite h
+//         is sent as a NaN in the lower half (the whole batch row becomes
+//         NaN at the next step either way, as it would with the true value).
+// One bit suffices because each location is written once every two steps
+// and each consumer lane always reads the same locations: the value it last
+// accepted there was the previous write, and read-read coherence of a
+// location forbids it from seeing anything older afterwards, so the only
+// values it can observe are the previous write (tag differs) or the current
+// one.  The host keeps the tag sequence continuous across the layers of a
+// call (the buffer is zeroed once per call, and a zero word carries tag 0).
+// ---------------------------------------------------------------------------
+template <bool BF>
+__device__ inline unsigned xc_shift() { return BF ? 30u : 0u; }
+__device__ inline void xcstore(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline __amdgpu_buffer_rsrc_t xcrsrc(const uint32_t *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// tag bit of the write made at step s into buffer s & 1
+__device__ inline unsigned xc_tag(unsigned xpar, int s) {
+    return (((xpar >> (s & 1)) & 1u) + ((unsigned)s >> 1) + 1u) & 1u;
+}
+// all four words of a 16-byte load carry tag bit tb
+template <bool BF>
+__device__ inline bool xc_ok(const u32x4 &w, unsigned tb) {
+    const unsigned all = w.x & w.y & w.z & w.w, any = w.x | w.y | w.z | w.w;
+    return ((tb ? all : ~any) >> xc_shift<BF>()) & 1u;
+}
+
 }  // namespace lstm_amd

@@ -32,8 +32,8 @@ struct RecArgs {
     void *hn;                // [D, B, H] dtype or NULL
     float *cn;               // [D, B, H] or NULL
     float *cstate;           // [D, B, H] carry between step launches
-    unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 tagged words
-    unsigned tag_base;       // tags of this layer are tag_base + s + 1
+    unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 32-bit words
+    unsigned xpar;           // bit p: parity of the writes buffer p received before this launch
     unsigned *status;        // error word
     int T, B, H, D;
     int P;                   // workgroups per team (hidden-unit slices)

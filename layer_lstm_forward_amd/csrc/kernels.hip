@@ -368,9 +368,10 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 // (gate rows interleaved: local column n = 4*u + q).  Per step:
 //   1. prefetch the projection G[t] for the cells this thread updates;
 //   2. S = h_{t-1} W_slice^T: the four waves split over batch tiles and K;
-//      each wave fetches its h_{t-1} fragments from the tagged exchange
-//      buffer (re-reading words until they carry step t-1's tag; at t = 0
-//      plain loads of h0) and feeds them to the matrix cores;
+//      each wave fetches its h_{t-1} fragments from the exchange buffer of
+//      compact tagged words (re-reading words until they carry step t-1's
+//      tag bit; at t = 0 plain loads of h0) and feeds them to the matrix
+//      cores;
 //   3. partial sums meet in LDS; each thread reduces the gate pre-activations
 //      of a pair of adjacent units of one batch row, applies sigma/tanh,
 //      updates c (kept in registers across steps) and writes h_t to y, to the
@@ -479,7 +480,9 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const int mw = wm * MTW * 16 + (lane & 15);    // this lane's team row in tile i: mw + 16 i
     const int ksub = (lane >> 4) * DT::PER16;      // this lane's K offset inside a chunk
-    const size_t region = (size_t)MT * kch * 256;  // exchange words per team
+    const size_t region = (size_t)MT * kch * 256;  // 32-bit exchange words per team
+    uint32_t *const xb32 = reinterpret_cast<uint32_t *>(a.xbuf);
+    constexpr unsigned XSH = BF ? 30u : 0u;          // tag bit position in a word
     // Optional read pacing: every wave waits `pace` wall-clock ticks after the
     // barrier that ends its workgroup's step s-1 before its first read of the
     // others' h_{s-1}, so that reads do not reach memory ahead of the data.
@@ -516,18 +519,17 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
             }
         } else {
-            const unsigned tag = a.tag_base + (unsigned)s;  // written at step s-1
+            const unsigned tb = xc_tag(a.xpar, s - 1);  // written at step s-1
             const __amdgpu_buffer_rsrc_t xr =
-                xrsrc(a.xbuf + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * region, (unsigned)(region * 8));
+                xcrsrc(xb32 + ((size_t)(((s - 1) & 1) * D + d) * a.NGB + gb) * region, (unsigned)(region * 4));
             if (s > a.s_begin && a.pace > 0)
                 while (wall_clock64() - t_pub < a.pace) __builtin_amdgcn_s_sleep(1);
             for (int bi = 0; bi < nb && wave_ok; ++bi) {
                 const int c0 = cw0 + bi * CB;
-                // Each lane reads its fragment as two 16-byte pairs of tagged
-                // words; for a fixed pair index the 64 lanes read 1 KB in a row.
-                // wd[..][eh] holds words e = 2*eh, 2*eh+1 of the fragment.
-                u32x4 wd[CB][MTW][2];
-                unsigned off[CB][MTW][2];
+                // Each lane reads its fragment (four words) in one 16-byte
+                // load; the 64 lanes of a wave read 1 KB in a row.
+                u32x4 wd[CB][MTW];
+                unsigned off[CB][MTW];
                 bool lv[CB][MTW][4];
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci)
@@ -536,36 +538,33 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                         const int c = c0 + ci, m = mw + 16 * i;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) lv[ci][i][e] = m < rows && c * DT::KC + ksub + e * EW < H;
-#pragma unroll
-                        for (int eh = 0; eh < 2; ++eh)
-                            off[ci][i][eh] = lv[ci][i][2 * eh]
-                                                 ? (unsigned)(((((wm * MTW + i) * kch + c) * 2 + eh) * 128 + 2 * lane) * 8)
-                                                 : 0x7FFFFFF0u;  // out of range: reads zeros, no memory access
+                        off[ci][i] = lv[ci][i][0] ? (unsigned)((((wm * MTW + i) * kch + c) * 64 + lane) * 16)
+                                                  : 0x7FFFFFF0u;  // out of range: reads zeros, no memory access
                     }
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci)
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i)
-#pragma unroll
-                        for (int eh = 0; eh < 2; ++eh) wd[ci][i][eh] = xload2(xr, off[ci][i][eh]);
-                // a dead word (padding row or K past H) counts as ready and zero
-                auto settle = [&](int ci, int i, int eh) {
-                    if (!lv[ci][i][2 * eh]) { wd[ci][i][eh].x = 0u; wd[ci][i][eh].y = tag; }
-                    if (!lv[ci][i][2 * eh + 1]) { wd[ci][i][eh].z = 0u; wd[ci][i][eh].w = tag; }
+                    for (int i = 0; i < MTW; ++i) wd[ci][i] = xload2(xr, off[ci][i]);
+                // a dead word (padding row or K past H) counts as ready; its
+                // value (zero, or the fp32 tag bit alone) meets zero W rows or
+                // a discarded output row
+                const unsigned tpat = tb << XSH;
+                auto settle = [&](int ci, int i) {
+                    if (!lv[ci][i][0]) wd[ci][i].x = tpat;
+                    if (!lv[ci][i][1]) wd[ci][i].y = tpat;
+                    if (!lv[ci][i][2]) wd[ci][i].z = tpat;
+                    if (!lv[ci][i][3]) wd[ci][i].w = tpat;
                 };
-                auto pair_ok = [&](int ci, int i, int eh) { return wd[ci][i][eh].y == tag && wd[ci][i][eh].w == tag; };
                 bool mine = true;
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci)
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i)
-#pragma unroll
-                        for (int eh = 0; eh < 2; ++eh) {
-                            settle(ci, i, eh);
-                            mine = mine && pair_ok(ci, i, eh);
-                        }
+                    for (int i = 0; i < MTW; ++i) {
+                        settle(ci, i);
+                        mine = mine && xc_ok<BF>(wd[ci][i], tb);
+                    }
                 if (!__all(mine)) {
-                    // slow path: back off, then re-read only the pairs that are stale
+                    // slow path: back off, then re-read only the fragments that are stale
                     unsigned spins = 0;
                     const long long t0 = wall_clock64();
                     do {
@@ -589,15 +588,13 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 #pragma unroll
                         for (int ci = 0; ci < CB; ++ci)
 #pragma unroll
-                            for (int i = 0; i < MTW; ++i)
-#pragma unroll
-                                for (int eh = 0; eh < 2; ++eh) {
-                                    if (!pair_ok(ci, i, eh)) {
-                                        wd[ci][i][eh] = xload2(xr, off[ci][i][eh]);
-                                        settle(ci, i, eh);
-                                    }
-                                    mine = mine && pair_ok(ci, i, eh);
+                            for (int i = 0; i < MTW; ++i) {
+                                if (!xc_ok<BF>(wd[ci][i], tb)) {
+                                    wd[ci][i] = xload2(xr, off[ci][i]);
+                                    settle(ci, i);
                                 }
+                                mine = mine && xc_ok<BF>(wd[ci][i], tb);
+                            }
                     } while (!__all(mine));
                     if (!wave_ok) break;
                 }
@@ -608,7 +605,13 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                     for (int j = 0; j < NT; ++j) bw[j] = Wf[((c0 + ci) * NT + j) * 64 + lane];
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) {
-                        const u32x4 af = {wd[ci][i][0].x, wd[ci][i][0].z, wd[ci][i][1].x, wd[ci][i][1].z};
+                        u32x4 af = wd[ci][i];
+                        if (BF) {  // drop the tag bit
+                            af.x &= 0xBFFFFFFFu;
+                            af.y &= 0xBFFFFFFFu;
+                            af.z &= 0xBFFFFFFFu;
+                            af.w &= 0xBFFFFFFFu;
+                        }
 #pragma unroll
                         for (int j = 0; j < NT; ++j) acc[i][j] = mma_chunk(DT{}, acc[i][j], af, bw[j]);
                     }
@@ -630,8 +633,8 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         __syncthreads();
         if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
 
-        const unsigned long long tag_out = (unsigned long long)(a.tag_base + (unsigned)s + 1u) << 32;
-        unsigned long long *xo = a.xbuf + ((size_t)((s & 1) * D + d) * a.NGB + gb) * region;
+        const unsigned tb_out = xc_tag(a.xpar, s);
+        uint32_t *xo = xb32 + ((size_t)((s & 1) * D + d) * a.NGB + gb) * region;
         const bool publish = s + 1 < T;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
@@ -653,7 +656,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 hs = DT::from_f(hv);
             }
             // word of (team row m, k) in the consumers' order:
-            // ((tile * kch + chunk) * 2 + e / 2) * 128 + 2 * lane + e % 2, lane = 16 * g + m % 16
+            // ((tile * kch + chunk) * 64 + lane) * 4 + e, lane = 16 * g + m % 16
             const int m = cm[i], jj = j0 + cu[i];
             if (BF) {
                 // units jj (even) and jj + 1 share a word; the even lane stores it
@@ -662,13 +665,15 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 if (publish && cv[i] && (cu[i] & 1) == 0) {
                     const int c = jj >> 5, g = (jj >> 3) & 3, e = (jj >> 1) & 3;
                     const uint32_t hi = cu[i] + 1 < units ? nb_bits : 0u;
-                    xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
-                           tag_out | (mine_bits | (hi << 16)));
+                    const bool nonfinite = ((mine_bits & 0x7F80u) == 0x7F80u) || ((hi & 0x7F80u) == 0x7F80u);
+                    const uint32_t payload = nonfinite ? 0x7FC0u : (mine_bits | (hi << 16));
+                    xcstore(xo + ((size_t)((m >> 4) * kch + c) * 64 + 16 * g + (m & 15)) * 4 + e,
+                            payload | (tb_out << 30));
                 }
             } else if (publish && cv[i]) {
                 const int c = jj >> 4, g = (jj >> 2) & 3, e = jj & 3;
-                xstore(xo + ((size_t)((m >> 4) * kch + c) * 2 + (e >> 1)) * 128 + 2 * (16 * g + (m & 15)) + (e & 1),
-                       tag_out | __float_as_uint(hv));
+                xcstore(xo + ((size_t)((m >> 4) * kch + c) * 64 + 16 * g + (m & 15)) * 4 + e,
+                        (__float_as_uint(hv) & ~1u) | tb_out);
             }
             if (cv[i]) {
                 const int bb = b0 + m;

@@ -167,7 +167,7 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
 
 // Rough cycles per step of one workgroup: matrix-core work of the busiest
 // wave (times the number of workgroups that share a CU), plus the h_{t-1}
-// fetch as tagged 8-byte words (one fp32 or two bf16 values each) at the
+// fetch as tagged 32-bit words (one fp32 or two bf16 values each) at the
 // ~32 B/clk a CU sustains for it.
 double step_cost(const lstm_plan *p, const Sched &s, int cus) {
     const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
@@ -176,7 +176,7 @@ double step_cost(const lstm_plan *p, const Sched &s, int cus) {
     const int live_mtw = (s.BG + 15) / 16 < s.tile.MTW ? (s.BG + 15) / 16 : s.tile.MTW;
     const int share = cus > 0 ? (s.wgs + cus - 1) / cus : 1;
     const double mfma = (double)live_mtw * s.tile.NT * cpw * (p->dtype == LSTM_BF16 ? 16 : 128) * share;
-    const double xbytes = (double)s.BG * p->H * (p->dtype == LSTM_BF16 ? 4 : 8) * share;
+    const double xbytes = (double)s.BG * p->H * (p->dtype == LSTM_BF16 ? 2 : 4) * share;
     return mfma + xbytes / 32.0;
 }
 
@@ -645,6 +645,11 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
 
     const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
     const int per16 = p->dtype == LSTM_BF16 ? 8 : 4;
+    // Exchange tags are one bit per word: bit p of xpar is the parity of the
+    // writes exchange buffer p has received so far in this call.  A k_rec
+    // layer writes buffer s & 1 at every step s < T - 1.
+    unsigned xpar = 0;
+    const unsigned layer_writes = (unsigned)((T / 2) & 1) | ((unsigned)(((T - 1) / 2) & 1) << 1);
     for (int l = 0; l < p->L; ++l) {
         const void *X = l == 0 ? x : static_cast<const void *>(ws + lay.ymid[(l - 1) & 1]);
         void *Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
@@ -678,7 +683,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
         ra.cstate = cstate;
         ra.xbuf = xbuf;
-        ra.tag_base = (unsigned)l * (unsigned)(T + 1);
+        ra.xpar = xpar;
         ra.status = status;
         ra.T = T;
         ra.B = B;
@@ -710,8 +715,10 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
                 stepped = true;
             }
         }
+        bool use_gemm_layer = false;
         if (stepped) {
             const bool use_gemm = gemm || (sch.persistent && gemm_step_shape_ok(p) && rec_step_gemm_ok(ra, p->dtype));
+            use_gemm_layer = use_gemm;
             for (int s = 0; s < T; ++s) {
                 ra.s_begin = s;
                 ra.s_end = s + 1;
@@ -724,6 +731,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
             }
         }
         span_end(p, span, st, stepped ? T : 1);
+        if (!use_gemm_layer) xpar ^= layer_writes;  // k_rec_step writes no exchange words
     }
     if (p->timing) p->acc.calls += 1;
     return LSTM_OK;

@@ -78,7 +78,7 @@ int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
     const int G = 4 * H;
     const size_t seq_out = (size_t)T * B * D * H;
 
-    double *X = NULL, *Y = NULL;
+    double *Y = NULL;
     double *h = malloc(sizeof(double) * (size_t)B * H);
     double *c = malloc(sizeof(double) * (size_t)B * H);
     double *pre = malloc(sizeof(double) * (size_t)B * G);
