@@ -458,7 +458,12 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 
     // G[t] of this thread's cells, loaded two steps ahead: older loads hold
     // up the in-order wait on the exchange loads, so they are issued early.
-    float gcur[CPT][4], gnext[CPT][4];
+    // Steps alternate between two register sets (the loop below is unrolled
+    // by two) so that no register with a load in flight is ever copied, and
+    // every load is unconditional (a dead cell or a step past the end reads
+    // a valid clamped address and the value is never used): a copy or a
+    // conditional join would make the compiler wait for the loads at once.
+    float gA[CPT][4], gB[CPT][4];
     auto load_g = [&](int step, float (&g)[CPT][4]) {
         const int tg = d == 0 ? step : T - 1 - step;
         const bool in = step < a.s_end;
@@ -468,11 +473,11 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             const float *gp = a.G + ((size_t)(ok ? tg : 0) * B + b0 + (ok ? cm[i] : 0)) * ldg + (size_t)d * 4 * H +
                               j0 + (ok ? cu[i] : 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) g[i][q] = ok ? gp[(size_t)q * H] : 0.f;
+            for (int q = 0; q < 4; ++q) g[i][q] = gp[(size_t)q * H];
         }
     };
-    load_g(a.s_begin, gcur);
-    load_g(a.s_begin + 1, gnext);
+    load_g(a.s_begin, gA);
+    load_g(a.s_begin + 1, gB);
     __syncthreads();
 
     const int nb = a.nbatch;                       // chunk batches per wave
@@ -488,7 +493,8 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     // others' h_{s-1}, so that reads do not reach memory ahead of the data.
     long long t_pub = 0;
 
-    for (int s = a.s_begin; s < a.s_end; ++s) {
+    // one step; false when a wait gave up (the kernel then leaves)
+    auto step = [&](const int s, float (&gcur)[CPT][4]) __attribute__((always_inline)) -> bool {
         const int t = d == 0 ? s : T - 1 - s;
         float *part = part0 + (a.part_bufs == 2 ? (size_t)(s & 1) * part_stride : 0);
 
@@ -584,15 +590,26 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                             }
                         }
                         for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
+                        // re-read the stale fragments; every load is issued
+                        // (a current fragment's goes out of range: zeros, no
+                        // memory access) before any is waited for, so one
+                        // retry costs one round trip however many are stale
+                        bool stale[CB][MTW];
+                        u32x4 re[CB][MTW];
+#pragma unroll
+                        for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                            for (int i = 0; i < MTW; ++i) {
+                                stale[ci][i] = !xc_ok<BF>(wd[ci][i], tb);
+                                re[ci][i] = xload2(xr, stale[ci][i] ? off[ci][i] : 0x7FFFFFF0u);
+                            }
                         mine = true;
 #pragma unroll
                         for (int ci = 0; ci < CB; ++ci)
 #pragma unroll
                             for (int i = 0; i < MTW; ++i) {
-                                if (!xc_ok<BF>(wd[ci][i], tb)) {
-                                    wd[ci][i] = xload2(xr, off[ci][i]);
-                                    settle(ci, i);
-                                }
+                                if (stale[ci][i]) wd[ci][i] = re[ci][i];
+                                settle(ci, i);
                                 mine = mine && xc_ok<BF>(wd[ci][i], tb);
                             }
                     } while (!__all(mine));
@@ -631,7 +648,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
         if (!wave_ok) s_bad = 1;
         __syncthreads();
-        if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+        if (s_bad) return false;  // a wait gave up: leave (every workgroup drains the same way)
 
         const unsigned tb_out = xc_tag(a.xpar, s);
         uint32_t *xo = xb32 + ((size_t)((s & 1) * D + d) * a.NGB + gb) * region;
@@ -685,13 +702,14 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
             }
         }
-#pragma unroll
-        for (int i = 0; i < CPT; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gcur[i][q] = gnext[i][q];
-        load_g(s + 2, gnext);
+        load_g(s + 2, gcur);
         if (a.part_bufs != 2) __syncthreads();  // partials are reused by the next step
         t_pub = wall_clock64();
+        return true;
+    };
+    for (int s = a.s_begin; s < a.s_end; s += 2) {
+        if (!step(s, gA)) return;
+        if (s + 1 < a.s_end && !step(s + 1, gB)) return;
     }
 
     if (a.s_end < T) {

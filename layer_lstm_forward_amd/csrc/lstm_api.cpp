@@ -383,7 +383,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->rec_tile = 0;
     p->part_bufs = 1;
     p->poll_sleep = 2;
-    p->read_pace_ns = 0;
+    p->read_pace_ns = 300;
     p->layer_pipe = 0;
     p->team_rows = 0;
     p->proj_tile = 0;
