@@ -48,6 +48,7 @@ struct RecArgs {
     int s_begin, s_end;      // steps handled by this launch
     int map_xcd;             // 1: place a team's workgroups on the same XCDs
     int vec;                 // 16-byte vector loads are aligned
+    int wreg;                // W_hh fragments in registers (RecGeom::wreg; selects the kernel)
     long long timeout_ticks; // wait timeout in wall_clock64 ticks
 };
 
@@ -98,6 +99,7 @@ constexpr size_t kRecLdsLimit = 160 * 1024 - 64;  // leaves room for static LDS
 // LDS geometry of a recurrent tile for hidden size H.
 struct RecGeom {
     int kch, kchp, nbatch, part_bufs;
+    int wreg;  // 1: each wave holds its W_hh fragments in registers; LDS holds partial sums only
     size_t smem;
 };
 RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers);
@@ -116,7 +118,7 @@ bool pipe_tile_supported(RecTile t);
 RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch);
 hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s);
-hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, int *blocks_per_cu);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
 // One recurrent step (a.s_begin) as a GEMM with the cell update fused
 // (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.

@@ -378,8 +378,12 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 //      exchange buffer with the next tag, and at the end to h_n and c_n.
 // One launch can run every step of the layer (persistent: all workgroups must
 // be co-resident, which the cooperative launch guarantees) or just one.
+// With RW, each wave keeps the W_hh fragments of its own K range in
+// registers for the whole launch (used when that range is one batch of CB
+// chunks): the matrix cores then never wait on LDS, and LDS holds only the
+// partial sums.
 // ===========================================================================
-template <class DT, int WK, int MTW, int NT, int CB>
+template <class DT, int WK, int MTW, int NT, int CB, bool RW>
 __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     using S = typename DT::S;
     constexpr bool BF = sizeof(S) == 2;
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_bad;
     u32x4 *Wf = reinterpret_cast<u32x4 *>(smem);
-    float *part0 = reinterpret_cast<float *>(smem + (size_t)a.kchp * NT * 1024);
+    float *part0 = reinterpret_cast<float *>(smem + (RW ? (size_t)0 : (size_t)a.kchp * NT * 1024));
     const size_t part_stride = (size_t)WK * ROWS * PSTR;  // floats per partial buffer
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -422,8 +426,22 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     const bool vec = a.vec != 0;
 
     // Resident W_hh slice as fragments: [chunk][n-tile][lane] x 16 bytes,
-    // zero beyond H and for the padding chunks up to kchp.
-    {
+    // zero beyond H and for the padding chunks up to kchp; in registers
+    // (this wave's chunks [wk*CB, wk*CB + CB)) or in LDS.
+    u32x4 wreg[RW ? CB : 1][NT];
+    if constexpr (RW) {
+        const S *W = static_cast<const S *>(a.whh[d]);
+#pragma unroll
+        for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = j * 16 + (lane & 15), u = n >> 2, q = n & 3;
+                const int k = (wk * CB + ci) * DT::KC + (lane >> 4) * DT::PER16;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (u < units && k < H) v = load_frag<DT>(W + (size_t)(q * H + j0 + u) * H, k, H, vec);
+                wreg[ci][j] = v;
+            }
+    } else {
         const S *W = static_cast<const S *>(a.whh[d]);
         const int nfrag = a.kchp * NT * 64;
         for (int f = tid; f < nfrag; f += 256) {
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     load_g(a.s_begin + 1, gB);
     __syncthreads();
 
-    const int nb = a.nbatch;                       // chunk batches per wave
+    const int nb = RW ? 1 : a.nbatch;              // chunk batches per wave
     const int cw0 = wk * nb * CB;                  // first chunk of this wave
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const int mw = wm * MTW * 16 + (lane & 15);    // this lane's team row in tile i: mw + 16 i
@@ -508,21 +526,24 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         if (s == 0) {
             if (a.h0) {
                 const S *hs = static_cast<const S *>(a.h0) + (size_t)d * B * H;
-                for (int c = cw0; c < cw0 + nb * CB; ++c) {
-                    u32x4 af[MTW];
-                    const int k = c * DT::KC + ksub;
+                for (int bi = 0; bi < nb; ++bi)
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i) {
-                        const int m = mw + 16 * i;
-                        af[i] = (m < rows && k < H) ? load_frag<DT>(hs + (size_t)(b0 + m) * H, k, H, vec) : zero;
+                    for (int ci = 0; ci < CB; ++ci) {
+                        const int c = cw0 + bi * CB + ci;
+                        u32x4 af[MTW];
+                        const int k = c * DT::KC + ksub;
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i) {
+                            const int m = mw + 16 * i;
+                            af[i] = (m < rows && k < H) ? load_frag<DT>(hs + (size_t)(b0 + m) * H, k, H, vec) : zero;
+                        }
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) {
+                            const u32x4 bw = RW ? wreg[RW ? ci : 0][j] : Wf[(c * NT + j) * 64 + lane];
+#pragma unroll
+                            for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
+                        }
                     }
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) {
-                        const u32x4 bw = Wf[(c * NT + j) * 64 + lane];
-#pragma unroll
-                        for (int i = 0; i < MTW; ++i) acc[i][j] = mma_chunk(DT{}, acc[i][j], af[i], bw);
-                    }
-                }
             }
         } else {
             const unsigned tb = xc_tag(a.xpar, s - 1);  // written at step s-1
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 for (int ci = 0; ci < CB; ++ci) {
                     u32x4 bw[NT];
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) bw[j] = Wf[((c0 + ci) * NT + j) * 64 + lane];
+                    for (int j = 0; j < NT; ++j) bw[j] = RW ? wreg[RW ? ci : 0][j] : Wf[((c0 + ci) * NT + j) * 64 + lane];
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) {
                         u32x4 af = wd[ci][i];
@@ -1314,7 +1335,10 @@ RecGeom rec_geom(RecTile t, int H, int dtype, bool want_two_partial_buffers) {
     const int cpw = (g.kch + t.WK - 1) / t.WK;
     g.nbatch = (cpw + cb - 1) / cb;
     g.kchp = t.WK * g.nbatch * cb;
-    const size_t wbytes = (size_t)g.kchp * t.NT * 1024;
+    // W_hh in registers when a wave's chunks are one batch of at most 32
+    // fragments (128 VGPRs)
+    g.wreg = g.nbatch == 1 && cb * t.NT <= 32 ? 1 : 0;
+    const size_t wbytes = g.wreg ? 0 : (size_t)g.kchp * t.NT * 1024;
     const size_t pbytes = (size_t)t.WK * rec_rows_per_wg(t) * (16 * t.NT + 4) * 4;
     g.part_bufs = (want_two_partial_buffers && wbytes + 2 * pbytes <= kRecLdsLimit) ? 2 : 1;
     g.smem = wbytes + g.part_bufs * pbytes;
@@ -1332,22 +1356,23 @@ bool rec_tile_supported(RecTile t) {
     return false;
 }
 
-template <class DT>
+template <class DT, bool RW>
 static const void *rec_kernel_ptr(RecTile t) {
 #define LSTM_T_PTR(wk, mtw, nt)                                                                    \
     if (t.WK == wk && t.MTW == mtw && t.NT == nt)                                                  \
-        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8)>);
+        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8), RW>);
     LSTM_REC_TILES(LSTM_T_PTR)
 #undef LSTM_T_PTR
     return nullptr;
 }
 
-static const void *rec_kernel(RecTile t, int dtype) {
-    return dtype == DT_BF16 ? rec_kernel_ptr<BF16>(t) : rec_kernel_ptr<F32>(t);
+static const void *rec_kernel(RecTile t, int dtype, bool wreg) {
+    if (dtype == DT_BF16) return wreg ? rec_kernel_ptr<BF16, true>(t) : rec_kernel_ptr<BF16, false>(t);
+    return wreg ? rec_kernel_ptr<F32, true>(t) : rec_kernel_ptr<F32, false>(t);
 }
 
-hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu) {
-    const void *fn = rec_kernel(t, dtype);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, int *blocks_per_cu) {
+    const void *fn = rec_kernel(t, dtype, wreg);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -1414,7 +1439,7 @@ hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hip
 }
 
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s) {
-    const void *fn = rec_kernel(t, dtype);
+    const void *fn = rec_kernel(t, dtype, a.wreg != 0);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;

@@ -193,7 +193,7 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
         bool can_persist = false;
         if (!want_step && di.ok) {
             int bpc = 0;
-            if (rec_max_coresident(t, s.smem, p->dtype, &bpc) == hipSuccess && bpc > 0)
+            if (rec_max_coresident(t, s.smem, p->dtype, s.geom.wreg != 0, &bpc) == hipSuccess && bpc > 0)
                 can_persist = (long long)bpc * di.cus >= s.wgs;
             (void)hipGetLastError();
         }
@@ -515,9 +515,9 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     }
     std::snprintf(buf, len,
                   "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
-                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d",
+                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s",
                   proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
-                  s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd);
+                  s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds");
     return LSTM_OK;
 }
 
@@ -699,6 +699,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.poll_sleep = p->poll_sleep;
         ra.pace = (int)((long long)p->read_pace_ns * di.wall_khz / 1000000);
         ra.map_xcd = sch.map_xcd;
+        ra.wreg = sch.geom.wreg;
         ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
         for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
         ra.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
