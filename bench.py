@@ -302,6 +302,11 @@ def main():
                 - 2.0 * spec.T * spec.B * spec.D * 4 * spec.hidden_size * spec.layer_input(0)
         elif tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
             flops /= spec.T
+        else:  # layers whose input projection runs inside the recurrent launch
+            fused = (re.findall(r"xproj=([a-z,]+)", desc) or [""])[0].split(",")
+            H = spec.hidden_size
+            flops += sum(2.0 * spec.T * spec.B * spec.D * 4 * H * spec.layer_input(l)
+                         for l in range(spec.num_layers) if l < len(fused) and fused[l] == "fused") / spec.num_layers
     else:
         kname, flops, avg = names.get("proj", "k_proj"), proj_flops_per_launch(spec), proj_avg
     achieved = flops / (avg / 1e3) / 1e12

@@ -92,10 +92,13 @@ typedef enum {
                                 (its h_t published) and its first read of the other workgroups' h_t;
                                 0 reads as soon as the step ends. A read that reaches memory before
                                 the data costs a retry round trip; results do not depend on it */
-    LSTM_OPT_LAYER_PIPE = 10 /* 0 (default): layer by layer; 1: a unidirectional stack of 2..4 layers runs
+    LSTM_OPT_LAYER_PIPE = 10, /* 0 (default): layer by layer; 1: a unidirectional stack of 2..4 layers runs
                                 all layers in one pipelined persistent launch when every layer's weights
                                 fit on chip (layer l consumes layer l-1's h_t as it is produced). Changes
                                 lstm_workspace_size. */
+    LSTM_OPT_FUSE_INPUT = 11  /* 1 (default): a layer whose recurrence runs as one persistent launch and
+                                whose W_ih share fits in registers computes x_t W_ih^T + b_ih + b_hh inside
+                                that launch (no projection GEMM, G unused); 0: always hoist the projection */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset

@@ -23,6 +23,7 @@ LSTM_OPT_PARTIAL_BUFFERS, LSTM_OPT_POLL_SLEEP, LSTM_OPT_TEAM_ROWS = 4, 5, 7
 LSTM_OPT_PROJ_TILE = 8
 LSTM_OPT_READ_PACE = 9
 LSTM_OPT_LAYER_PIPE = 10
+LSTM_OPT_FUSE_INPUT = 11
 STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
           -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
           -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}

@@ -49,6 +49,14 @@ struct RecArgs {
     int map_xcd;             // 1: place a team's workgroups on the same XCDs
     int vec;                 // 16-byte vector loads are aligned
     int wreg;                // W_hh fragments in registers (RecGeom::wreg; selects the kernel)
+    // fused input projection (ncx > 0): G is not read; x_t W_ih^T + b_ih + b_hh
+    // is computed in the step from these
+    int ncx;                 // input chunks per wave (0: use G)
+    int I;                   // input width of this layer
+    const void *x;           // [T, B, I] dtype
+    const void *wih[2];      // [4H, I] per direction, dtype
+    const void *b_ih[2];     // [4H] dtype or NULL
+    const void *b_hh[2];
     long long timeout_ticks; // wait timeout in wall_clock64 ticks
 };
 
@@ -118,7 +126,9 @@ bool pipe_tile_supported(RecTile t);
 RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch);
 hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s);
-hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, int *blocks_per_cu);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, int *blocks_per_cu);
+// input chunks per wave of the tile's fused-projection variant (0: none)
+int rec_fused_chunks(RecTile t);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
 // One recurrent step (a.s_begin) as a GEMM with the cell update fused
 // (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.

@@ -382,10 +382,19 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 // registers for the whole launch (used when that range is one batch of CB
 // chunks): the matrix cores then never wait on LDS, and LDS holds only the
 // partial sums.
+// With FX > 0 the input projection is fused instead of hoisted: each wave
+// also keeps the W_ih fragments of its share of the input width in registers
+// (at most FX chunks) and multiplies x_t by them right after issuing the
+// reads of h_{t-1}, i.e. while the matrix cores would otherwise wait for the
+// exchange; both biases are added in the epilogue and G is not used.  The
+// same equation block splits the gate pre-activation into the x_t and h_{t-1}
+// products; here they share one accumulator.
 // ===========================================================================
-template <class DT, int WK, int MTW, int NT, int CB, bool RW>
+template <class DT, int WK, int MTW, int NT, int CB, bool RW, int FX>
 __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     using S = typename DT::S;
+    constexpr bool FUSED = FX > 0;
+    static_assert(!FUSED || RW, "the fused projection keeps W_hh in registers");
     constexpr bool BF = sizeof(S) == 2;
     constexpr int WM = 4 / WK;
     constexpr int MT = WM * MTW;
@@ -454,6 +463,24 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         }
     }
 
+    // Fused projection: W_ih fragments of input chunks [wk*ncx, wk*ncx + ncx)
+    // (ncx <= FX; the chunks past the input width are zero).
+    const int ncx = FUSED ? a.ncx : 0;
+    u32x4 wx[FUSED ? FX : 1][NT];
+    if constexpr (FUSED) {
+        const S *Wi = static_cast<const S *>(a.wih[d]);
+#pragma unroll
+        for (int cx = 0; cx < FX; ++cx)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = j * 16 + (lane & 15), u = n >> 2, q = n & 3;
+                const int k = (wk * ncx + cx) * DT::KC + (lane >> 4) * DT::PER16;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (cx < ncx && u < units && k < a.I) v = load_frag<DT>(Wi + (size_t)(q * H + j0 + u) * a.I, k, a.I, true);
+                wx[cx][j] = v;
+            }
+    }
+
     // Cells of this thread: (batch row cm, hidden unit cu); adjacent lanes hold
     // adjacent units of one row.
     int cm[CPT], cu[CPT];
@@ -473,6 +500,18 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         }
     }
     if (tid == 0) s_bad = 0;
+    // fused projection: b_ih + b_hh of this thread's cells
+    float bias[FUSED ? CPT : 1][4];
+    if constexpr (FUSED) {
+        const S *bi = static_cast<const S *>(a.b_ih[d]), *bh = static_cast<const S *>(a.b_hh[d]);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = q * H + j0 + (cv[i] ? cu[i] : 0);
+                bias[i][q] = bi ? DT::to_f(bi[r]) + DT::to_f(bh[r]) : 0.f;
+            }
+    }
 
     // G[t] of this thread's cells, loaded two steps ahead: older loads hold
     // up the in-order wait on the exchange loads, so they are issued early.
@@ -481,8 +520,8 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     // every load is unconditional (a dead cell or a step past the end reads
     // a valid clamped address and the value is never used): a copy or a
     // conditional join would make the compiler wait for the loads at once.
-    float gA[CPT][4], gB[CPT][4];
-    auto load_g = [&](int step, float (&g)[CPT][4]) {
+    float gA[FUSED ? 1 : CPT][4], gB[FUSED ? 1 : CPT][4];
+    auto load_g = [&](int step, float (&g)[FUSED ? 1 : CPT][4]) {
         const int tg = d == 0 ? step : T - 1 - step;
         const bool in = step < a.s_end;
 #pragma unroll
@@ -494,8 +533,35 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             for (int q = 0; q < 4; ++q) g[i][q] = gp[(size_t)q * H];
         }
     };
-    load_g(a.s_begin, gA);
-    load_g(a.s_begin + 1, gB);
+    // Fused projection: x_t fragments of this wave's rows and input chunks,
+    // loaded two steps ahead in the same way (one buffer resource per time
+    // slice; rows past the batch group and chunks past the input read zeros).
+    const int mw0 = wm * MTW * 16 + (lane & 15);
+    u32x4 xA[FUSED ? FX : 1][MTW], xB[FUSED ? FX : 1][MTW];
+    auto load_x = [&](int step, u32x4 (&xf)[FUSED ? FX : 1][MTW]) {
+        const int st = step < a.s_end ? step : a.s_begin;
+        const int tx = d == 0 ? st : T - 1 - st;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<S *>(static_cast<const S *>(a.x) + (size_t)tx * B * a.I), (short)0,
+            (int)((size_t)B * a.I * sizeof(S)), 0x00020000);
+#pragma unroll
+        for (int cx = 0; cx < FX; ++cx)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                const int m = mw0 + 16 * i;
+                const int k = (wk * ncx + cx) * DT::KC + (lane >> 4) * DT::PER16;
+                const bool ok = cx < ncx && m < rows && k < a.I;
+                xf[cx][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, ok ? (int)((((size_t)(b0 + m)) * a.I + k) * sizeof(S)) : 0x7FFFFFF0, 0, 0);
+            }
+    };
+    if constexpr (FUSED) {
+        load_x(a.s_begin, xA);
+        load_x(a.s_begin + 1, xB);
+    } else {
+        load_g(a.s_begin, gA);
+        load_g(a.s_begin + 1, gB);
+    }
     __syncthreads();
 
     const int nb = RW ? 1 : a.nbatch;              // chunk batches per wave
@@ -512,7 +578,8 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     long long t_pub = 0;
 
     // one step; false when a wait gave up (the kernel then leaves)
-    auto step = [&](const int s, float (&gcur)[CPT][4]) __attribute__((always_inline)) -> bool {
+    auto step = [&](const int s, float (&gcur)[FUSED ? 1 : CPT][4], u32x4 (&xcur)[FUSED ? FX : 1][MTW])
+        __attribute__((always_inline)) -> bool {
         const int t = d == 0 ? s : T - 1 - s;
         float *part = part0 + (a.part_bufs == 2 ? (size_t)(s & 1) * part_stride : 0);
 
@@ -522,8 +589,21 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         bool wave_ok = true;
+        // x_t W_ih^T for this wave's input chunks (fused projection)
+        auto mma_x = [&]() {
+            if constexpr (FUSED) {
+#pragma unroll
+                for (int cx = 0; cx < FX; ++cx)
+                    if (cx < ncx)
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                            for (int j = 0; j < NT; ++j) acc[i][j] = mma_chunk(DT{}, acc[i][j], xcur[cx][i], wx[cx][j]);
+            }
+        };
 
         if (s == 0) {
+            mma_x();
             if (a.h0) {
                 const S *hs = static_cast<const S *>(a.h0) + (size_t)d * B * H;
                 for (int bi = 0; bi < nb; ++bi)
@@ -572,6 +652,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 for (int ci = 0; ci < CB; ++ci)
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) wd[ci][i] = xload2(xr, off[ci][i]);
+                if (bi == 0) mma_x();  // overlaps the reads of h_{t-1}
                 // a dead word (padding row or K past H) counts as ready; its
                 // value (zero, or the fp32 tag bit alone) meets zero W rows or
                 // a discarded output row
@@ -684,10 +765,16 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
 #pragma unroll
                 for (int kk = 1; kk < WK; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
-                const float ig = sigmoid_f(sum.x + gcur[i][0]);
-                const float fg = sigmoid_f(sum.y + gcur[i][1]);
-                const float gg = tanh_f(sum.z + gcur[i][2]);
-                const float og = sigmoid_f(sum.w + gcur[i][3]);
+                float pre[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (FUSED) pre[q] = bias[i][q];
+                    else pre[q] = gcur[i][q];
+                }
+                const float ig = sigmoid_f(sum.x + pre[0]);
+                const float fg = sigmoid_f(sum.y + pre[1]);
+                const float gg = tanh_f(sum.z + pre[2]);
+                const float og = sigmoid_f(sum.w + pre[3]);
                 const float cn = fg * creg[i] + ig * gg;
                 creg[i] = cn;
                 hv = og * tanh_f(cn);
@@ -723,14 +810,15 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 }
             }
         }
-        load_g(s + 2, gcur);
+        if constexpr (FUSED) load_x(s + 2, xcur);
+        else load_g(s + 2, gcur);
         if (a.part_bufs != 2) __syncthreads();  // partials are reused by the next step
         t_pub = wall_clock64();
         return true;
     };
     for (int s = a.s_begin; s < a.s_end; s += 2) {
-        if (!step(s, gA)) return;
-        if (s + 1 < a.s_end && !step(s + 1, gB)) return;
+        if (!step(s, gA, xA)) return;
+        if (s + 1 < a.s_end && !step(s + 1, gB, xB)) return;
     }
 
     if (a.s_end < T) {
@@ -1360,19 +1448,41 @@ template <class DT, bool RW>
 static const void *rec_kernel_ptr(RecTile t) {
 #define LSTM_T_PTR(wk, mtw, nt)                                                                    \
     if (t.WK == wk && t.MTW == mtw && t.NT == nt)                                                  \
-        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8), RW>);
+        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, (mtw >= 4 ? 2 : 8), RW, 0>);
     LSTM_REC_TILES(LSTM_T_PTR)
 #undef LSTM_T_PTR
     return nullptr;
 }
 
-static const void *rec_kernel(RecTile t, int dtype, bool wreg) {
+// Tiles with a fused-projection variant, and its input chunks per wave.
+#define LSTM_REC_FUSED_TILES(X) X(4, 1, 1) X(4, 1, 2) X(4, 1, 4) X(2, 1, 1) X(2, 1, 2) X(2, 1, 4)
+#define LSTM_FX_OF(nt) ((nt) == 4 ? 4 : 8)
+
+int rec_fused_chunks(RecTile t) {
+#define LSTM_F_OK(wk, mtw, nt) if (t.WK == wk && t.MTW == mtw && t.NT == nt) return LSTM_FX_OF(nt);
+    LSTM_REC_FUSED_TILES(LSTM_F_OK)
+#undef LSTM_F_OK
+    return 0;
+}
+
+template <class DT>
+static const void *rec_fused_ptr(RecTile t) {
+#define LSTM_F_PTR(wk, mtw, nt)                                                                    \
+    if (t.WK == wk && t.MTW == mtw && t.NT == nt)                                                  \
+        return reinterpret_cast<const void *>(&k_rec<DT, wk, mtw, nt, 8, true, LSTM_FX_OF(nt)>);
+    LSTM_REC_FUSED_TILES(LSTM_F_PTR)
+#undef LSTM_F_PTR
+    return nullptr;
+}
+
+static const void *rec_kernel(RecTile t, int dtype, bool wreg, bool fused) {
+    if (fused) return wreg ? (dtype == DT_BF16 ? rec_fused_ptr<BF16>(t) : rec_fused_ptr<F32>(t)) : nullptr;
     if (dtype == DT_BF16) return wreg ? rec_kernel_ptr<BF16, true>(t) : rec_kernel_ptr<BF16, false>(t);
     return wreg ? rec_kernel_ptr<F32, true>(t) : rec_kernel_ptr<F32, false>(t);
 }
 
-hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, int *blocks_per_cu) {
-    const void *fn = rec_kernel(t, dtype, wreg);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, int *blocks_per_cu) {
+    const void *fn = rec_kernel(t, dtype, wreg, fused);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -1439,7 +1549,7 @@ hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hip
 }
 
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s) {
-    const void *fn = rec_kernel(t, dtype, a.wreg != 0);
+    const void *fn = rec_kernel(t, dtype, a.wreg != 0, a.ncx > 0);
     if (!fn) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;

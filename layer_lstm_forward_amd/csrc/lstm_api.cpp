@@ -23,6 +23,7 @@ struct lstm_plan {
     int poll_sleep;  // back-off between re-reads of stale exchange words
     int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next
     int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
+    int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
                        // (off by default: slower than layer by layer on the measured workloads)
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
@@ -180,6 +181,35 @@ double step_cost(const lstm_plan *p, const Sched &s, int cus) {
     return mfma + xbytes / 32.0;
 }
 
+// Input chunks per wave when layer input X (width in_l) can use the fused
+// projection of the chosen persistent schedule, else 0: the tile has a fused
+// variant whose register budget covers the wave's share of the input width,
+// rows are 16-byte multiples and aligned, one time slice of X is addressable
+// by a buffer resource, and the fused kernel is co-resident like the plain one.
+int fused_chunks_shape(const lstm_plan *p, const Sched &s, int B, int in_l, const DevInfo &di) {
+    if (!p->fuse_input || !s.persistent || !s.geom.wreg || !di.ok) return 0;
+    const int fx = rec_fused_chunks(s.tile);
+    if (fx == 0) return 0;
+    const size_t es = elem_size(p->dtype);
+    const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
+    const int ncx = ((in_l + kc - 1) / kc + s.tile.WK - 1) / s.tile.WK;
+    if (ncx > fx || ((size_t)in_l * es) % 16 != 0 || (size_t)B * in_l * es >= ((size_t)1 << 31)) return 0;
+    return ncx;
+}
+
+int fused_chunks(const lstm_plan *p, const Sched &s, int B, int in_l, const void *X, const void *const *wih,
+                 const DevInfo &di) {
+    const int ncx = fused_chunks_shape(p, s, B, in_l, di);
+    if (ncx == 0 || (uintptr_t)X % 16 != 0) return 0;
+    for (int d = 0; d < p->D; ++d)
+        if ((uintptr_t)wih[d] % 16 != 0) return 0;
+    int bpc = 0;
+    const bool fits = rec_max_coresident(s.tile, s.smem, p->dtype, true, true, &bpc) == hipSuccess && bpc > 0 &&
+                      (long long)bpc * di.cus >= s.wgs;
+    (void)hipGetLastError();
+    return fits ? ncx : 0;
+}
+
 int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
     const DevInfo di = dev_info(dev);
     Sched best{};
@@ -193,7 +223,7 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
         bool can_persist = false;
         if (!want_step && di.ok) {
             int bpc = 0;
-            if (rec_max_coresident(t, s.smem, p->dtype, s.geom.wreg != 0, &bpc) == hipSuccess && bpc > 0)
+            if (rec_max_coresident(t, s.smem, p->dtype, s.geom.wreg != 0, false, &bpc) == hipSuccess && bpc > 0)
                 can_persist = (long long)bpc * di.cus >= s.wgs;
             (void)hipGetLastError();
         }
@@ -385,6 +415,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->poll_sleep = 2;
     p->read_pace_ns = 300;
     p->layer_pipe = 0;
+    p->fuse_input = 1;
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
@@ -447,6 +478,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
         case LSTM_OPT_LAYER_PIPE:
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
             p->layer_pipe = value;
+            return LSTM_OK;
+        case LSTM_OPT_FUSE_INPUT:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->fuse_input = value;
             return LSTM_OK;
         case LSTM_OPT_READ_PACE:
             if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
@@ -513,11 +548,22 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
                       proj, dt, dt, bm, ((B + bm - 1) / bm) * ((p->H + 31) / 32) * p->D);
         return LSTM_OK;
     }
+    // per layer: is the input projection fused into the recurrence (assuming
+    // 16-byte aligned operands and a co-resident fused kernel)?
+    const DevInfo di = dev_info(dev);
+    char xproj[64] = {0};
+    size_t xl = 0;
+    for (int l = 0; l < p->L && xl + 9 < sizeof(xproj); ++l) {
+        const int in_l = l == 0 ? p->I : p->D * p->H;
+        xl += (size_t)std::snprintf(xproj + xl, sizeof(xproj) - xl, "%s%s", l ? "," : "",
+                                    fused_chunks_shape(p, s, B, in_l, di) ? "fused" : "hoisted");
+    }
     std::snprintf(buf, len,
                   "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
-                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s",
+                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s",
                   proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
-                  s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds");
+                  s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds",
+                  xproj);
     return LSTM_OK;
 }
 
@@ -655,26 +701,47 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         void *Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
         const int in_l = l == 0 ? p->I : p->D * p->H;
 
-        ProjArgs pa{};
-        pa.X = X;
-        pa.G = G;
-        pa.M = T * B;
-        pa.N = 4 * p->H;
-        pa.K = in_l;
-        pa.ldx = in_l;
-        pa.D = p->D;
-        for (int d = 0; d < p->D; ++d) {
-            const void *const *w = weights + (size_t)(l * p->D + d) * per;
-            pa.W[d] = w[0];
-            pa.b_ih[d] = p->has_bias ? w[2] : nullptr;
-            pa.b_hh[d] = p->has_bias ? w[3] : nullptr;
-        }
-        int span = span_begin(p, st, 0);
-        if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) return LSTM_ERR_LAUNCH;
-        span_end(p, span, st, 1);
+        const void *wih[2] = {nullptr, nullptr};
+        for (int d = 0; d < p->D; ++d) wih[d] = weights[(size_t)(l * p->D + d) * per];
+        int ncx = fused_chunks(p, sch, B, in_l, X, wih, di);
+
+        // hoisted projection G = X W_ih^T + b_ih + b_hh (skipped when fused)
+        auto project = [&]() -> bool {
+            ProjArgs pa{};
+            pa.X = X;
+            pa.G = G;
+            pa.M = T * B;
+            pa.N = 4 * p->H;
+            pa.K = in_l;
+            pa.ldx = in_l;
+            pa.D = p->D;
+            for (int d = 0; d < p->D; ++d) {
+                const void *const *w = weights + (size_t)(l * p->D + d) * per;
+                pa.W[d] = w[0];
+                pa.b_ih[d] = p->has_bias ? w[2] : nullptr;
+                pa.b_hh[d] = p->has_bias ? w[3] : nullptr;
+            }
+            const int sp = span_begin(p, st, 0);
+            if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) {
+                (void)hipGetLastError();
+                return false;
+            }
+            span_end(p, sp, st, 1);
+            return true;
+        };
+        if (ncx == 0 && !project()) return LSTM_ERR_LAUNCH;
 
         RecArgs ra{};
-        for (int d = 0; d < p->D; ++d) ra.whh[d] = weights[(size_t)(l * p->D + d) * per + 1];
+        for (int d = 0; d < p->D; ++d) {
+            const void *const *w = weights + (size_t)(l * p->D + d) * per;
+            ra.whh[d] = w[1];
+            ra.wih[d] = w[0];
+            ra.b_ih[d] = p->has_bias ? w[2] : nullptr;
+            ra.b_hh[d] = p->has_bias ? w[3] : nullptr;
+        }
+        ra.ncx = ncx;
+        ra.I = in_l;
+        ra.x = X;
         ra.G = G;
         ra.h0 = h0 ? static_cast<const char *>(h0) + (size_t)l * state_elems * es : nullptr;
         ra.c0 = c0 ? c0 + (size_t)l * state_elems : nullptr;
@@ -703,12 +770,23 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
         for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
         ra.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
-        span = span_begin(p, st, 1);
+        int span = span_begin(p, st, 1);
         bool stepped = !sch.persistent;
         if (sch.persistent) {
             ra.s_begin = 0;
             ra.s_end = T;
-            if (launch_rec(ra, sch.tile, sch.smem, p->dtype, true, st) != hipSuccess) {
+            hipError_t e = launch_rec(ra, sch.tile, sch.smem, p->dtype, true, st);
+            if (e != hipSuccess && ra.ncx > 0) {
+                // the fused launch was refused (nothing ran): hoist the
+                // projection and try the plain kernel
+                (void)hipGetLastError();
+                span_end(p, span, st, 0);
+                ra.ncx = 0;
+                if (!project()) return LSTM_ERR_LAUNCH;
+                span = span_begin(p, st, 1);
+                e = launch_rec(ra, sch.tile, sch.smem, p->dtype, true, st);
+            }
+            if (e != hipSuccess) {
                 (void)hipGetLastError();
                 // The cooperative launch was refused (nothing ran): in automatic
                 // mode the layer falls back to one launch per step.

@@ -79,8 +79,11 @@ def test_set_option():
         pkg.lstm_set_option(p, pkg.LSTM_OPT_REC_TILE, 412)
         for v in (0, 1000, 100000):
             pkg.lstm_set_option(p, pkg.LSTM_OPT_READ_PACE, v)
+        for v in (0, 1):
+            pkg.lstm_set_option(p, pkg.LSTM_OPT_FUSE_INPUT, v)
         for opt, val in ((pkg.LSTM_OPT_RECURRENCE, 4), (pkg.LSTM_OPT_REC_TILE, 333), (6, 0),
-                         (pkg.LSTM_OPT_READ_PACE, -1), (pkg.LSTM_OPT_READ_PACE, 100001), (99, 0)):
+                         (pkg.LSTM_OPT_READ_PACE, -1), (pkg.LSTM_OPT_READ_PACE, 100001),
+                         (pkg.LSTM_OPT_FUSE_INPUT, 2), (99, 0)):
             with pytest.raises(pkg.LSTMError) as e:
                 pkg.lstm_set_option(p, opt, val)
             assert e.value.status == -7

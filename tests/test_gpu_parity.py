@@ -102,13 +102,34 @@ def test_layer_pipeline(spec):
     assert_parity(seq, ref, spec.dtype, "layer by layer")
 
 
+@pytest.mark.parametrize("spec", [
+    Spec(24, 64, 2, False, 9, 40, "f32", 601, "normal0.1"),      # layer 0: one input chunk for four waves
+    Spec(256, 128, 2, True, 7, 37, "f32", 602, "normal0.1"),    # both directions, ragged batch groups
+    Spec(96, 80, 3, False, 5, 16, "bf16", 603, "normal0.1"),    # partial unit slice, three layers
+    Spec(512, 96, 1, True, 4, 20, "bf16", 604, "zeros", has_bias=False),
+    Spec(64, 256, 2, False, 3, 1, "f32", 605, "normal0.1"),     # one batch row
+], ids=_id)
+def test_fused_input_projection(spec):
+    """x_t W_ih^T computed inside the persistent recurrence (fused) against
+    the oracle and against the hoisted projection GEMM."""
+    print(f"case {_id(spec)} fused projection", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    got, m = run_gpu(inp, options={pkg.LSTM_OPT_FUSE_INPUT: 1})
+    assert "fused" in m.describe(spec.T, spec.B)
+    assert_parity(got, ref, spec.dtype, "fused")
+    hoisted, m2 = run_gpu(inp, options={pkg.LSTM_OPT_FUSE_INPUT: 0})
+    assert "fused" not in m2.describe(spec.T, spec.B)
+    assert_parity(hoisted, ref, spec.dtype, "hoisted")
+
+
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
 @pytest.mark.parametrize("proj_tile", [1, 2, 3], ids=["proj128", "proj256", "proj256dma"])
 def test_projection_tiles(spec, proj_tile):
     """Both projection GEMM kernels, forced on shapes with ragged M, N and K."""
     print(f"case {_id(spec)} proj tile {proj_tile}", flush=True)
     inp = make_inputs(spec)
-    got, m = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: proj_tile})
+    got, m = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: proj_tile, pkg.LSTM_OPT_FUSE_INPUT: 0})
     ref = run_oracle(inp)
     assert_parity(got, ref, spec.dtype, f"proj tile {proj_tile}")
 
@@ -118,14 +139,16 @@ def test_projection_tiles(spec, proj_tile):
                                   Spec(96, 136, 1, False, 6, 21, "bf16", 202, "normal0.1")], ids=_id)
 def test_every_tile_persistent_equals_step(spec, tile):
     """Each recurrent tile gives oracle parity, and the persistent launch
-    (step barriers inside one kernel) equals one-launch-per-step bit for bit."""
+    (step barriers inside one kernel) equals one-launch-per-step bit for bit
+    (both with the hoisted projection; the fused one sums in another order)."""
     print(f"case {_id(spec)} tile {tile}", flush=True)
     inp = make_inputs(spec)
     ref = run_oracle(inp)
-    step, m = run_gpu(inp, recurrence=pkg.LSTM_REC_STEP, rec_tile=tile)
+    hoist = {pkg.LSTM_OPT_FUSE_INPUT: 0}  # same projection on both sides: the sum order matches
+    step, m = run_gpu(inp, recurrence=pkg.LSTM_REC_STEP, rec_tile=tile, options=hoist)
     assert_parity(step, ref, spec.dtype, m.describe(spec.T, spec.B))
     try:
-        pers, m2 = run_gpu(inp, recurrence=pkg.LSTM_REC_PERSISTENT, rec_tile=tile)
+        pers, m2 = run_gpu(inp, recurrence=pkg.LSTM_REC_PERSISTENT, rec_tile=tile, options=hoist)
     except pkg.LSTMError as e:
         assert e.status == -7  # this tile does not fit as one persistent launch
         return
@@ -195,6 +218,10 @@ def test_full_tiny_l1_in8_h16():
 
 def test_full_l2_in256_h512_b64_f32_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [0, 37, 63])
+
+
+def test_full_l2_in256_h512_b64_f32_hoisted_projection_sampled_rows():
+    _full("l2_in256_h512_t128_b64_f32", [5, 40], options={pkg.LSTM_OPT_FUSE_INPUT: 0})
 
 
 def test_full_l2_in256_h512_b64_f32_layer_pipeline_sampled_rows():
