@@ -540,7 +540,9 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     u32x4 xA[FUSED ? FX : 1][MTW], xB[FUSED ? FX : 1][MTW];
     auto load_x = [&](int step, u32x4 (&xf)[FUSED ? FX : 1][MTW]) {
         const int st = step < a.s_end ? step : a.s_begin;
-        const int tx = d == 0 ? st : T - 1 - st;
+        // wave-uniform by construction; said explicitly so that the resource
+        // stays in scalar registers (else every load becomes a waterfall loop)
+        const int tx = __builtin_amdgcn_readfirstlane(d == 0 ? st : T - 1 - st);
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<S *>(static_cast<const S *>(a.x) + (size_t)tx * B * a.I), (short)0,
             (int)((size_t)B * a.I * sizeof(S)), 0x00020000);

@@ -413,7 +413,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->rec_tile = 0;
     p->part_bufs = 1;
     p->poll_sleep = 2;
-    p->read_pace_ns = 300;
+    p->read_pace_ns = 450;
     p->layer_pipe = 0;
     p->fuse_input = 1;
     p->team_rows = 0;
