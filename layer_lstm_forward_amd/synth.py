@@ -14,6 +14,11 @@ Recipe (the same for every workload):
   * h0, c0 either absent (zeros) or ~ N(0, 0.1) (standard deviation 0.1);
   * bf16 workloads draw in fp32 and round to nearest-even bf16 once, here;
     the cell state c0 stays fp32.
+  * per-row sequence lengths (variable-length batches), from their own
+    generator ``default_rng(seed + 7919)`` so that the other draws do not
+    change: ``ragged`` is uniform on 1..T, ``mix`` has a quarter of the rows
+    at T and the rest uniform on T/2..T (a padded bucket whose longest row
+    sets T), ``full`` is T for every row.  The pages give no length mix.
 """
 from __future__ import annotations
 
@@ -120,3 +125,18 @@ def make_inputs(spec: Spec) -> Inputs:
     elif spec.state != "zeros":
         raise ValueError(f"unknown state recipe {spec.state!r}")
     return Inputs(spec, x, params, h0, c0)
+
+
+def make_lengths(spec: Spec, mode: str = "mix") -> np.ndarray:
+    """Seeded per-row lengths in 1..T (int32, one per batch row)."""
+    T, B = spec.T, spec.B
+    rng = np.random.default_rng(spec.seed + 7919)
+    if mode == "full":
+        return np.full(B, T, np.int32)
+    if mode == "ragged":
+        return rng.integers(1, T + 1, size=B).astype(np.int32)
+    if mode == "mix":
+        n = rng.integers(max(1, T // 2), T + 1, size=B)
+        n[rng.permutation(B)[:max(1, B // 4)]] = T
+        return n.astype(np.int32)
+    raise ValueError(f"unknown length mode {mode!r}")

@@ -49,6 +49,11 @@ def _load():
         lib.oracle_lstm_forward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp, ctypes.c_int]
+        lib.oracle_lstm_forward_lengths.restype = ctypes.c_int
+        lib.oracle_lstm_forward_lengths.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, ctypes.POINTER(ctypes.c_int), dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp,
+            ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -73,12 +78,14 @@ def _ptr(a):
 
 def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bool,
                  h0=None, c0=None, has_bias: bool = True, bf16: bool = False,
-                 c_state_bf16: bool = False, nthreads: int = 1):
+                 c_state_bf16: bool = False, nthreads: int = 1, lengths=None):
     """Run the oracle.
 
     x       [T, B, I]
     params  flat list in (layer, direction, W_ih, W_hh[, b_ih, b_hh]) order
     h0, c0  [L*D, B, H] or None (zeros); c0 is never bf16 unless c_state_bf16
+    lengths None (every row has T steps) or B ints in 1..T: row b takes part
+            only in steps t < lengths[b] (see the C file)
     Returns (y [T, B, D*H], h_n [L*D, B, H], c_n [L*D, B, H]) as float64.
     """
     lib = _load()
@@ -102,11 +109,17 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     for s in (h064, c064):
         if s is not None and s.shape != (L * D, B, H):
             raise ValueError(f"state shape {s.shape} != {(L * D, B, H)}")
+    len32 = None
+    if lengths is not None:
+        len32 = np.ascontiguousarray(np.asarray(lengths, np.int32))
+        if len32.shape != (B,):
+            raise ValueError(f"lengths shape {len32.shape} != {(B,)}")
     y = np.empty((T, B, D * H), np.float64)
     hn = np.empty((L * D, B, H), np.float64)
     cn = np.empty((L * D, B, H), np.float64)
-    rc = lib.oracle_lstm_forward(
+    rc = lib.oracle_lstm_forward_lengths(
         T, B, I, H, L, D, _ptr(x64),
+        len32.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if len32 is not None else None,
         _ptr(h064) if h064 is not None else None,
         _ptr(c064) if c064 is not None else None,
         arr, 1 if has_bias else 0, _ptr(y), _ptr(hn), _ptr(cn), int(nthreads))

@@ -38,6 +38,15 @@
  *     the reverse output is stored at the time index of the input it has
  *     just consumed, and its "final" state is the one after consuming t = 0.
  *   - Shapes of the returned tensors: warp-nn __call__ "Returns".
+ *   - Variable-length batches (oracle_lstm_forward_lengths): "Complete
+ *     Trace: nn.LSTM", Step 3, lists a packed-sequence overload beside the
+ *     padded one, and the MXNet blog's "Sequence Buckets" pads sequences of
+ *     different lengths and ignores the padded elements.  Reading taken: with
+ *     a length per batch row on the padded [T][B] layout, row b takes part
+ *     only in the steps with t < len_b; elsewhere its state is left as it is
+ *     and its output is zero.  Its final state is therefore the one after
+ *     its last valid step, and the reverse direction starts at t = len_b - 1
+ *     from the initial state.
  *
  * Layouts (all row-major, contiguous, fp64):
  *   x    [T][B][I]                   input sequence, time-major
@@ -64,15 +73,23 @@
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
-/* Returns 0 on success, -1 on a bad argument, -2 if memory runs out. */
-int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
-                        const double *x, const double *h0, const double *c0,
-                        const double *const *params, int has_bias,
-                        double *y, double *h_n, double *c_n, int nthreads)
+/* time index t is past row b's sequence (variable-length batches only) */
+#define PADDED(t, b) (lengths && (t) >= lengths[b])
+
+/* Returns 0 on success, -1 on a bad argument, -2 if memory runs out.
+ * lengths: NULL (every row has T steps) or B values in 1..T. */
+int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
+                                const double *x, const int *lengths,
+                                const double *h0, const double *c0,
+                                const double *const *params, int has_bias,
+                                double *y, double *h_n, double *c_n, int nthreads)
 {
     if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) ||
         !x || !params || !y)
         return -1;
+    if (lengths)
+        for (int b = 0; b < B; ++b)
+            if (lengths[b] < 1 || lengths[b] > T) return -1;
     if (nthreads < 1) nthreads = 1;
     const int per = has_bias ? 4 : 2;
     const int G = 4 * H;
@@ -110,6 +127,7 @@ int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
 #pragma omp parallel for collapse(2) num_threads(nthreads) if (nthreads > 1)
                 for (int b = 0; b < B; ++b) {
                     for (int r = 0; r < G; ++r) {
+                        if (PADDED(t, b)) continue;
                         const double *xt = in_seq + ((size_t)t * B + b) * in_w;
                         const double *wi = W_ih + (size_t)r * in_w;
                         const double *wh = W_hh + (size_t)r * H;
@@ -126,6 +144,8 @@ int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
 #pragma omp parallel for collapse(2) num_threads(nthreads) if (nthreads > 1)
                 for (int b = 0; b < B; ++b) {
                     for (int j = 0; j < H; ++j) {
+                        /* a padded step leaves the state alone; y stays 0 */
+                        if (PADDED(t, b)) continue;
                         const double *pb = pre + (size_t)b * G;
                         const double ig = sigmoid(pb[j]);
                         const double fg = sigmoid(pb[H + j]);
@@ -153,6 +173,16 @@ int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
     memcpy(y, Y, sizeof(double) * seq_out);
     free(h); free(c); free(pre); free(Yl); free(Xl);
     return 0;
+}
+
+/* Every row has all T steps. */
+int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
+                        const double *x, const double *h0, const double *c0,
+                        const double *const *params, int has_bias,
+                        double *y, double *h_n, double *c_n, int nthreads)
+{
+    return oracle_lstm_forward_lengths(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias,
+                                       y, h_n, c_n, nthreads);
 }
 
 /* Number of threads OpenMP would use by default (1 without OpenMP). */

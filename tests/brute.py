@@ -48,9 +48,13 @@ def cell(g, x, h, c):
     return h_new, c_new
 
 
-def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True):
+def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None):
     """x: nested [T][B][I]; params flat in (layer, direction, W_ih, W_hh[, b_ih, b_hh]).
 
+    lengths: None, or the number of valid steps of each row; a row's sequence
+    is then its first lengths[b] time steps only, its padded outputs stay
+    zero, and the reverse direction walks that sequence backwards from its
+    own last element.
     Returns y [T][B][D*H], h_n and c_n [L*D][B][H] as nested lists.
     """
     T, B = len(x), len(x[0])
@@ -66,7 +70,8 @@ def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True):
             for b in range(B):
                 h = [float(v) for v in h0[l * D + d][b]] if h0 is not None else [0.0] * H
                 c = [float(v) for v in c0[l * D + d][b]] if c0 is not None else [0.0] * H
-                order = range(T) if d == 0 else range(T - 1, -1, -1)
+                n = T if lengths is None else lengths[b]
+                order = range(n) if d == 0 else range(n - 1, -1, -1)
                 for t in order:
                     h, c = cell(g, seq[t][b], h, c)
                     out[t][b][d * H:(d + 1) * H] = h

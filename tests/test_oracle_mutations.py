@@ -22,6 +22,12 @@ MUTATIONS = {
     "o_gate_tanh": ("const double og = sigmoid(pb[3 * H + j]);", "const double og = tanh(pb[3 * H + j]);"),
     "transposed_W_ih": ("acc += wi[k] * xt[k];", "acc += W_ih[(size_t)k * G + r] * xt[k];"),
     "next_layer_reads_h_not_y": ("in_seq = Xl;", "in_seq = Yl;"),
+    # variable-length rows: the reverse direction starting at T - 1 instead of
+    # at the row's own end; one step too many per row
+    "varlen_reverse_from_T": ("#define PADDED(t, b) (lengths && (t) >= lengths[b])",
+                              "#define PADDED(t, b) (lengths && d == 0 && (t) >= lengths[b])"),
+    "varlen_one_step_long": ("#define PADDED(t, b) (lengths && (t) >= lengths[b])",
+                             "#define PADDED(t, b) (lengths && (t) > lengths[b])"),
 }
 
 

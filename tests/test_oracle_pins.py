@@ -209,6 +209,53 @@ def test_brute_force_per_gate(I, H, T, B, L, D):
     np.testing.assert_allclose(cn, np.array(cb), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("I,H,T,B,L,D", [(2, 3, 4, 3, 1, 1), (3, 2, 5, 3, 2, 2), (1, 3, 4, 2, 2, 1),
+                                          (3, 1, 3, 2, 1, 2)])
+def test_brute_force_lengths(I, H, T, B, L, D):
+    """Variable-length rows against the per-gate evaluator, which walks each
+    row's own sequence (forward from its start, reverse from its last valid
+    step) and leaves padded outputs at zero."""
+    spec = Spec(I, H, L, D == 2, T, B, "f32", 2000 + I * 100 + H * 10 + T + B + L + D, "normal0.1")
+    inp = make_inputs(spec)
+    inp.params = [p * 3.0 for p in inp.params]
+    lengths = [T] + [1 + (b * 2) % T for b in range(1, B)]
+    y, hn, cn = run(inp, lengths=lengths)
+    yb, hb, cb = brute.lstm(inp.x.astype(np.float64).tolist(),
+                            [p.astype(np.float64).tolist() for p in inp.params], H, L, D,
+                            h0=inp.h0.astype(np.float64).tolist(), c0=inp.c0.astype(np.float64).tolist(),
+                            lengths=lengths)
+    np.testing.assert_allclose(y, np.array(yb), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(hn, np.array(hb), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(cn, np.array(cb), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("L,bidir", [(1, False), (2, True), (3, False)])
+def test_lengths_equal_truncated_rows(L, bidir):
+    """A row with n valid steps gives exactly what the fixed-length forward
+    gives for that row's first n steps alone; padded outputs are zero."""
+    spec = Spec(5, 6, L, bidir, 7, 5, "f32", 3100 + L, "normal0.1")
+    inp = make_inputs(spec)
+    lengths = np.array([7, 1, 4, 6, 3], np.int32)
+    y, hn, cn = run(inp, lengths=lengths)
+    for b, n in enumerate(lengths):
+        sub = inp.rows([b])
+        yt, ht, ct = oracle.lstm_forward(sub.x[:n], sub.params, 6, L, bidir, h0=sub.h0, c0=sub.c0)
+        np.testing.assert_array_equal(y[:n, b], yt[:, 0])
+        np.testing.assert_array_equal(hn[:, b], ht[:, 0])
+        np.testing.assert_array_equal(cn[:, b], ct[:, 0])
+        assert np.all(y[n:, b] == 0.0)
+    full, _, _ = run(inp, lengths=np.full(5, 7, np.int32))
+    plain, _, _ = run(inp)
+    np.testing.assert_array_equal(full, plain)
+
+
+def test_lengths_out_of_range_rejected():
+    inp = make_inputs(Spec(3, 4, 1, False, 5, 2, "f32", 3200, "zeros"))
+    for bad in ([0, 3], [6, 5]):
+        with pytest.raises(RuntimeError):
+            run(inp, lengths=bad)
+
+
 def test_brute_force_without_bias():
     spec = Spec(3, 3, 2, True, 3, 2, "f32", 77, "zeros", has_bias=False)
     inp = make_inputs(spec)
