@@ -151,6 +151,27 @@ lstm_status lstm_forward(lstm_plan *plan, const void *x, const void *h0, const f
                          void *y, void *h_n, float *c_n, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* Variable-length batches: the same forward with a sequence length per
+ * batch row on the padded [T, B, .] layout.  The trace page "Complete Trace:
+ * nn.LSTM" (Step 3) lists a packed-sequence overload beside the padded one,
+ * and the MXNet blog "LSTM Forward Computation" ("Sequence Buckets") pads
+ * sequences of different lengths and ignores the padded elements.
+ *   lengths  HOST array of B int32 values in 1..T (read before the call
+ *            returns; the library copies it into the workspace).  Row b takes
+ *            part only in the steps t < lengths[b]: its state is left as it is
+ *            at the other steps and y[t, b, :] = 0 there; h_n and c_n are the
+ *            state after the row's last valid step, and the reverse direction
+ *            starts at t = lengths[b] - 1 from h0/c0.  (A packed batch_sizes
+ *            tensor of rows sorted by length gives lengths[b] = the number of
+ *            steps t with batch_sizes[t] > b.)
+ * Every other argument, the outputs and the errors are those of lstm_forward;
+ * a NULL lengths or a value outside 1..T is LSTM_ERR_ARG and nothing is
+ * enqueued.  The layer pipeline (LSTM_OPT_LAYER_PIPE) is not used here. */
+lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *lengths, const void *h0,
+                                 const float *c0, const void *const *weights, int T, int B, int layers,
+                                 int bidir, void *y, void *h_n, float *c_n, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Synchronise `stream` and read the kernel status word a previous
  * lstm_forward left in `workspace`: *device_flags = 0 if every step barrier
  * completed.  Returns LSTM_ERR_DEVICE_TIMEOUT when a flag is set (the outputs

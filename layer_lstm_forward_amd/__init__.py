@@ -62,6 +62,9 @@ def load_library():
     lib.lstm_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.lstm_forward.restype = i
     lib.lstm_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp, sz, vp]
+    lib.lstm_forward_lengths.restype = i
+    lib.lstm_forward_lengths.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int), vp, vp, ctypes.POINTER(vp),
+                                         i, i, i, i, vp, vp, vp, vp, sz, vp]
     lib.lstm_device_status.restype = i
     lib.lstm_device_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint)]
     lib.lstm_describe.restype = i
@@ -120,6 +123,18 @@ def lstm_forward(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, wor
     arr = (ctypes.c_void_p * len(weights))(*[int(w) for w in weights])
     return int(load_library().lstm_forward(
         ctypes.c_void_p(plan), ctypes.c_void_p(x), ctypes.c_void_p(h0 or None), ctypes.c_void_p(c0 or None),
+        arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
+        ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
+        int(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def lstm_forward_lengths(plan, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                         workspace_bytes, stream) -> int:
+    """Raw call with per-row lengths (a host sequence of B ints); returns the status."""
+    arr = (ctypes.c_void_p * len(weights))(*[int(w) for w in weights])
+    lens = None if lengths is None else (ctypes.c_int * len(lengths))(*[int(v) for v in lengths])
+    return int(load_library().lstm_forward_lengths(
+        ctypes.c_void_p(plan), ctypes.c_void_p(x), lens, ctypes.c_void_p(h0 or None), ctypes.c_void_p(c0 or None),
         arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
         ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
         int(workspace_bytes), ctypes.c_void_p(stream or None)))
@@ -189,7 +204,8 @@ class LSTM:
             self._ws = torch.empty(n, dtype=torch.uint8, device=device)
         return self._ws, n
 
-    def forward(self, x, weights, h0=None, c0=None, stream=None, out=None):
+    def forward(self, x, weights, h0=None, c0=None, stream=None, out=None, lengths=None):
+        """lengths: None, or B ints in 1..T (per-row sequence lengths, host side)."""
         import torch
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         if not x.is_cuda or x.dtype != tdt or not x.is_contiguous() or x.dim() != 3:
@@ -208,12 +224,16 @@ class LSTM:
         ws, nbytes = self.workspace(T, B, x.device)
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
-        rc = lstm_forward(self.plan, x.data_ptr(), h0.data_ptr() if h0 is not None else 0,
-                          c0.data_ptr() if c0 is not None else 0, [w.data_ptr() for w in weights],
-                          T, B, L, self.bidirectional, y.data_ptr(), hn.data_ptr() if hn is not None else 0,
-                          cn.data_ptr() if cn is not None else 0, ws.data_ptr(), nbytes, stream)
+        args = (h0.data_ptr() if h0 is not None else 0, c0.data_ptr() if c0 is not None else 0,
+                [w.data_ptr() for w in weights], T, B, L, self.bidirectional, y.data_ptr(),
+                hn.data_ptr() if hn is not None else 0, cn.data_ptr() if cn is not None else 0,
+                ws.data_ptr(), nbytes, stream)
+        if lengths is None:
+            rc = lstm_forward(self.plan, x.data_ptr(), *args)
+        else:
+            rc = lstm_forward_lengths(self.plan, x.data_ptr(), [int(v) for v in lengths], *args)
         if rc:
-            raise LSTMError(rc, "lstm_forward")
+            raise LSTMError(rc, "lstm_forward_lengths" if lengths is not None else "lstm_forward")
         return y, hn, cn
 
     def device_status(self, stream=None):

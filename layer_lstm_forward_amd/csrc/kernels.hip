@@ -21,6 +21,7 @@
 //   k_rec_step  one step of the recurrence as a GEMM with the cell update
 //           fused, for layers whose W_hh does not stay on chip.
 //   k_fill  clears the status word and the exchange buffer.
+//   k_mask_padded  zeroes the outputs of padded steps (variable-length rows).
 #include "device.h"
 #include "kernels.h"
 
@@ -483,9 +484,11 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 
     // Cells of this thread: (batch row cm, hidden unit cu); adjacent lanes hold
     // adjacent units of one row.
-    int cm[CPT], cu[CPT];
+    // With per-row lengths a cell is active at time t only if t < its row's
+    // length; otherwise c and h stay as they are (hreg keeps h), y gets 0.
+    int cm[CPT], cu[CPT], clen[CPT];
     bool cv[CPT];
-    float creg[CPT];
+    float creg[CPT], hreg[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int e = tid + 256 * i;
@@ -493,10 +496,18 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         cu[i] = e % U;
         cv[i] = e < CELLS && cm[i] < rows && cu[i] < units;
         creg[i] = 0.f;
+        hreg[i] = 0.f;
+        clen[i] = T;
         if (cv[i]) {
             const size_t si = ((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i];
-            if (a.s_begin == 0) creg[i] = a.c0 ? a.c0[si] : 0.f;
-            else creg[i] = a.cstate[si];
+            if (a.s_begin == 0) {
+                creg[i] = a.c0 ? a.c0[si] : 0.f;
+                if (a.len && a.h0) hreg[i] = DT::to_f(static_cast<const S *>(a.h0)[si]);
+            } else {
+                creg[i] = a.cstate[si];
+                if (a.len) hreg[i] = a.hstate[si];
+            }
+            if (a.len) clen[i] = a.len[b0 + cm[i]];
         }
     }
     if (tid == 0) s_bad = 0;
@@ -777,9 +788,14 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 const float fg = sigmoid_f(sum.y + pre[1]);
                 const float gg = tanh_f(sum.z + pre[2]);
                 const float og = sigmoid_f(sum.w + pre[3]);
-                const float cn = fg * creg[i] + ig * gg;
-                creg[i] = cn;
+                float cn = fg * creg[i] + ig * gg;
                 hv = og * tanh_f(cn);
+                if (t >= clen[i]) {  // padded step of this row: keep the state
+                    cn = creg[i];
+                    hv = hreg[i];
+                }
+                creg[i] = cn;
+                hreg[i] = hv;
                 hs = DT::from_f(hv);
             }
             // word of (team row m, k) in the consumers' order:
@@ -804,7 +820,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             }
             if (cv[i]) {
                 const int bb = b0 + m;
-                static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = hs;
+                static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = t < clen[i] ? hs : (S)0;
                 if (s == T - 1) {
                     const size_t si = ((size_t)d * B + bb) * H + jj;
                     if (a.hn) static_cast<S *>(a.hn)[si] = hs;
@@ -826,7 +842,11 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     if (a.s_end < T) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
-            if (cv[i]) a.cstate[((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i]] = creg[i];
+            if (cv[i]) {
+                const size_t si = ((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i];
+                a.cstate[si] = creg[i];
+                if (a.len) a.hstate[si] = hreg[i];
+            }
     }
 }
 
@@ -1340,14 +1360,32 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         const float fg = sigmoid_f(pre[1] + g[(size_t)H]);
         const float gg = tanh_f(pre[2] + g[(size_t)2 * H]);
         const float og = sigmoid_f(pre[3] + g[(size_t)3 * H]);
-        const float cn = fg * cp + ig * gg;
-        const S hs = DT::from_f(og * tanh_f(cn));
+        float cn = fg * cp + ig * gg;
+        S hs = DT::from_f(og * tanh_f(cn));
+        if (a.len && t >= a.len[m]) {
+            // padded step of this row: the state stays; y carries the unchanged
+            // h because the next step reads h_{t-1} from y (padded outputs are
+            // zeroed after the last layer)
+            cn = cp;
+            hs = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
+        }
         a.cstate[si] = cn;
         static_cast<S *>(a.Y)[((size_t)t * B + m) * ldy + (size_t)d * H + u] = hs;
         if (last) {
             if (a.hn) static_cast<S *>(a.hn)[si] = hs;
             if (a.cn) a.cn[si] = cn;
         }
+    }
+}
+
+// y[t][b][:] = 0 for t >= len[b]; one 16-bit unit per thread (rows of bf16
+// or fp32 values are whole units)
+__global__ void k_mask_padded(uint16_t *y, const int *len, int T, int B, size_t row_units) {
+    const size_t n = (size_t)T * B * row_units;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t row = i / row_units;
+        const int t = (int)(row / B), b = (int)(row % B);
+        if (t >= len[b]) y[i] = 0;
     }
 }
 
@@ -1591,6 +1629,15 @@ static hipError_t launch_step_t(const RecArgs &a, hipStream_t s) {
 hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
     if (dtype == DT_BF16) return launch_step_t<BF16, 2>(a, s);
     return launch_step_t<F32, 2>(a, s);
+}
+
+hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, hipStream_t s) {
+    if (row_bytes % 2 != 0) return hipErrorInvalidValue;
+    const size_t n = (size_t)T * B * (row_bytes / 2);
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_mask_padded, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t *>(y), len, T, B,
+                       row_bytes / 2);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s) {

@@ -55,7 +55,7 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 }
 
 struct Layout {
-    size_t status, xbuf, G, ymid[2], cstate, total;
+    size_t status, xbuf, G, ymid[2], cstate, hstate, lens, total;
     size_t sync_bytes;  // status word + exchange buffer, zeroed per call
     size_t pipe_tiles;  // bound on the 16-row tiles of a pipelined schedule
 };
@@ -107,6 +107,10 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     }
     o->cstate = off;
     off += align_up(st);
+    o->hstate = off;  // h carry of stepped launches with per-row lengths
+    off += align_up(st);
+    o->lens = off;    // per-row lengths, copied from the caller's host array
+    off += align_up((size_t)B * sizeof(int));
     o->total = off;
     return true;
 }
@@ -375,7 +379,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 100; }
+int lstm_version(void) { return 101; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -567,7 +571,13 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     return LSTM_OK;
 }
 
-lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+}  // extern "C"
+
+namespace {
+
+// The forward pass; lengths_h: NULL (every row has T steps) or B host values
+// in 1..T, already validated.
+lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, const void *h0, const float *c0,
                          const void *const *weights, int T, int B, int layers, int bidir, void *y,
                          void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream_) {
     Layout lay;
@@ -597,8 +607,14 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
     unsigned long long *xbuf = reinterpret_cast<unsigned long long *>(ws + lay.xbuf);
     float *G = reinterpret_cast<float *>(ws + lay.G);
     float *cstate = reinterpret_cast<float *>(ws + lay.cstate);
+    float *hstate = reinterpret_cast<float *>(ws + lay.hstate);
+    int *dlen = lengths_h ? reinterpret_cast<int *>(ws + lay.lens) : nullptr;
     const size_t es = elem_size(p->dtype);
     const size_t state_elems = (size_t)p->D * B * p->H;
+    if (dlen && hipMemcpyAsync(dlen, lengths_h, (size_t)B * sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
 
     // per-step GEMM kernel: usable when the recurrence steps and every layer's
     // operands meet its alignment (checked before anything is enqueued)
@@ -618,7 +634,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
     // one cooperative launch.  If the runtime refuses that launch, the
     // sequential path below redoes the work.
     PipeSched ps{};
-    if (choose_pipe(p, B, dev, &ps)) {
+    if (!dlen && choose_pipe(p, B, dev, &ps)) {
         const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
         const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
         const size_t slot_words = region_words * ps.NGB;
@@ -749,6 +765,8 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         ra.hn = h_n ? static_cast<char *>(h_n) + (size_t)l * state_elems * es : nullptr;
         ra.cn = c_n ? c_n + (size_t)l * state_elems : nullptr;
         ra.cstate = cstate;
+        ra.hstate = hstate;
+        ra.len = dlen;
         ra.xbuf = xbuf;
         ra.xpar = xpar;
         ra.status = status;
@@ -811,9 +829,37 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         }
         span_end(p, span, st, stepped ? T : 1);
         if (!use_gemm_layer) xpar ^= layer_writes;  // k_rec_step writes no exchange words
+        // k_rec_step leaves the unchanged h in y at padded steps (the next step
+        // reads it there); the caller sees zeros
+        if (dlen && use_gemm_layer && l == p->L - 1 &&
+            launch_mask_padded(y, dlen, T, B, (size_t)p->D * p->H * es, st) != hipSuccess)
+            return LSTM_ERR_LAUNCH;
     }
     if (p->timing) p->acc.calls += 1;
     return LSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                         const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                        workspace_bytes, stream);
+}
+
+lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths, const void *h0,
+                                 const float *c0, const void *const *weights, int T, int B, int layers,
+                                 int bidir, void *y, void *h_n, float *c_n, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    if (!lengths) return LSTM_ERR_ARG;
+    if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;
+    return forward_impl(p, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                        workspace_bytes, stream);
 }
 
 lstm_status lstm_device_status(const void *workspace, size_t workspace_bytes, void *stream,

@@ -22,7 +22,7 @@ def to_dev(a, bf16, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1, options=None):
+def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1, options=None, lengths=None):
     """Returns (y, h_n, c_n) as float64 numpy arrays and the model used."""
     import torch
     import layer_lstm_forward_amd as pkg
@@ -36,7 +36,7 @@ def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1
     h0 = to_dev(inp.h0, bf, device)
     c0 = to_dev(inp.c0, False, device)
     for _ in range(repeat):
-        y, hn, cn = model.forward(x, w, h0, c0)
+        y, hn, cn = model.forward(x, w, h0, c0, lengths=lengths)
     torch.cuda.synchronize()
     rc, flags = model.device_status()
     assert rc == 0 and flags == 0, f"device status {rc} flags {flags}"
@@ -44,11 +44,11 @@ def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1
     return out, model
 
 
-def run_oracle(inp):
+def run_oracle(inp, lengths=None):
     s = inp.spec
     return oracle.lstm_forward(inp.x, inp.params, s.hidden_size, s.num_layers, s.bidirectional,
                                h0=inp.h0, c0=inp.c0, has_bias=s.has_bias, bf16=s.dtype == "bf16",
-                               nthreads=oracle_threads())
+                               nthreads=oracle_threads(), lengths=lengths)
 
 
 def max_errs(got, ref):

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 100
+    assert pkg.lstm_version() == 101
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -127,6 +127,32 @@ def test_forward_host_validation(kw, code):
 
 def test_forward_null_plan():
     assert _fwd(None) == -1
+
+
+def _fwd_len(plan, lengths, **kw):
+    a = dict(x=FAKE, h0=0, c0=0, weights=[FAKE] * 4, T=5, B=2, layers=1, bidir=False, y=FAKE, h_n=0, c_n=0,
+             workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+    a.update(kw)
+    return pkg.lstm_forward_lengths(plan, a["x"], lengths, a["h0"], a["c0"], a["weights"], a["T"], a["B"],
+                                    a["layers"], a["bidir"], a["y"], a["h_n"], a["c_n"], a["workspace"],
+                                    a["workspace_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("lengths,kw,code", [
+    (None, {}, -1),                   # no lengths
+    ([0, 5], {}, -1),                 # a row without steps
+    ([5, 6], {}, -1),                 # longer than T
+    ([5, -1], {}, -1),
+    ([5, 5], dict(T=0), -2),
+    ([5, 5], dict(layers=3), -2),     # the rest is checked as lstm_forward does
+    ([5, 5], dict(workspace_bytes=64), -5),
+])
+def test_forward_lengths_host_validation(lengths, kw, code):
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        assert _fwd_len(p, lengths, **kw) == code
+    finally:
+        pkg.lstm_destroy(p)
 
 
 def test_forward_weights_count_follows_bias_flag():

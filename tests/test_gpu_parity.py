@@ -123,6 +123,47 @@ def test_fused_input_projection(spec):
     assert_parity(hoisted, ref, spec.dtype, "hoisted")
 
 
+LENGTH_SPECS = [
+    Spec(24, 64, 2, False, 9, 40, "f32", 701, "normal0.1"),      # fused projection
+    Spec(37, 52, 2, True, 9, 19, "f32", 702, "normal0.1"),       # ragged H and I, both directions
+    Spec(70, 40, 3, False, 6, 33, "bf16", 703, "normal0.1"),     # three layers
+    Spec(64, 96, 2, True, 11, 5, "bf16", 704, "zeros"),
+]
+LENGTH_MODES = {"auto": (pkg.LSTM_REC_AUTO, {}), "hoisted": (pkg.LSTM_REC_AUTO, {pkg.LSTM_OPT_FUSE_INPUT: 0}),
+                "step": (pkg.LSTM_REC_STEP, {}), "gemm": (pkg.LSTM_REC_GEMM, {})}
+
+
+@pytest.mark.parametrize("spec", LENGTH_SPECS, ids=_id)
+@pytest.mark.parametrize("mode", sorted(LENGTH_MODES))
+def test_variable_lengths(spec, mode):
+    """Per-row lengths (lstm_forward_lengths) against the oracle in every
+    recurrence mode; padded outputs are exactly zero."""
+    from layer_lstm_forward_amd.synth import make_lengths
+    print(f"case {_id(spec)} lengths {mode}", flush=True)
+    inp = make_inputs(spec)
+    lengths = make_lengths(spec, "ragged")
+    lengths[0] = spec.T
+    lengths[-1] = 1
+    rec, opts = LENGTH_MODES[mode]
+    if mode == "gemm" and not _gemm_step_shape_ok(spec):
+        pytest.skip("rows are not 16-byte multiples: the per-step GEMM refuses this shape")
+    got, m = run_gpu(inp, recurrence=rec, options=opts, lengths=lengths)
+    ref = run_oracle(inp, lengths=lengths)
+    assert_parity(got, ref, spec.dtype, f"lengths {mode}: {m.describe(spec.T, spec.B)}")
+    y = got[0]
+    for b, n in enumerate(lengths):
+        assert np.all(y[n:, b] == 0.0), f"row {b}: padded outputs not zero"
+
+
+def test_lengths_all_full_equal_plain_forward():
+    spec = Spec(48, 72, 2, True, 7, 37, "f32", 705, "normal0.1")
+    inp = make_inputs(spec)
+    a, _ = run_gpu(inp)
+    b, _ = run_gpu(inp, lengths=[spec.T] * spec.B)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
 @pytest.mark.parametrize("proj_tile", [1, 2, 3], ids=["proj128", "proj256", "proj256dma"])
 def test_projection_tiles(spec, proj_tile):
@@ -226,6 +267,19 @@ def test_full_l2_in256_h512_b64_f32_hoisted_projection_sampled_rows():
 
 def test_full_l2_in256_h512_b64_f32_layer_pipeline_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [1, 32, 62], options={pkg.LSTM_OPT_LAYER_PIPE: 1})
+
+
+def test_full_l2_in256_h512_b64_f32_lengths_sampled_rows():
+    """The benchmark workload with a padded-bucket length mix, rows sampled."""
+    from layer_lstm_forward_amd.synth import make_lengths
+    spec = WORKLOADS["l2_in256_h512_t128_b64_f32"]
+    inp = make_inputs(spec)
+    lengths = make_lengths(spec, "mix")
+    got, m = run_gpu(inp, lengths=lengths)
+    rows = [0, 21, 63]
+    ref = run_oracle(inp.rows(rows), lengths=lengths[rows])
+    y, hn, cn = got
+    assert_parity((y[:, rows], hn[:, rows], cn[:, rows]), ref, spec.dtype, m.describe(spec.T, spec.B))
 
 
 def test_full_l2bi_in512_h1024_b32_bf16_sampled_rows():
