@@ -48,7 +48,7 @@ def proj_flops_per_launch(spec):
     return tot / spec.num_layers
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_baseline(inp, budget_s, lengths=None):
     import numpy as np
     import oracle
     spec = inp.spec
@@ -59,7 +59,8 @@ def cpu_baseline(inp, budget_s):
     t0 = time.perf_counter()
     sub = inp.rows(rows)
     oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
-                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads)
+                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads,
+                        lengths=None if lengths is None else lengths[rows])
     one = time.perf_counter() - t0
     n = int(max(1, min(spec.B, budget_s / max(one, 1e-6))))
     rows = list(np.linspace(0, spec.B - 1, n).astype(int)) if n > 1 else [0]
@@ -67,11 +68,15 @@ def cpu_baseline(inp, budget_s):
     sub = inp.rows(rows)
     t0 = time.perf_counter()
     oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
-                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads)
+                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads,
+                        lengths=None if lengths is None else lengths[rows])
     wall = time.perf_counter() - t0
-    cells = len(rows) * spec.T * spec.hidden_size * spec.num_layers * spec.D
+    steps = spec.T * len(rows) if lengths is None else int(np.sum(lengths[rows]))
+    cells = steps * spec.hidden_size * spec.num_layers * spec.D
     return {"value": cells / wall, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {spec.B} batch rows, full T={spec.T}, all {spec.num_layers} layers, "
+            "sample": f"{len(rows)} of {spec.B} batch rows, "
+                      f"{'full T=' + str(spec.T) if lengths is None else 'their valid steps (per-row lengths)'}, "
+                      f"all {spec.num_layers} layers, "
                       f"fp64, {wall:.1f} s wall ({per_row_flops * len(rows) / wall / 1e9:.2f} GFLOP/s)"}
 
 
@@ -217,6 +222,8 @@ def main():
     ap.add_argument("--poll-sleep", type=int, default=-1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lengths", choices=["none", "mix", "ragged"], default="none",
+                    help="variable-length rows (lstm_forward_lengths); the value then counts valid cells only")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -228,13 +235,15 @@ def main():
     import torch
 
     import layer_lstm_forward_amd as pkg
-    from layer_lstm_forward_amd.synth import WORKLOADS, make_inputs
+    from layer_lstm_forward_amd.synth import WORKLOADS, make_inputs, make_lengths
 
     spec = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {args.workload}: generating inputs")
     inp = make_inputs(spec)
+    lengths = None if args.lengths == "none" else make_lengths(spec, args.lengths)
+    cells = spec.cells if lengths is None else int(np.sum(lengths)) * spec.hidden_size * spec.num_layers * spec.D
     bf = spec.dtype == "bf16"
 
     def to_dev(a):
@@ -264,7 +273,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
-        m.forward(x, w, h0, c0, out=out)
+        m.forward(x, w, h0, c0, out=out, lengths=lengths)
     torch.cuda.synchronize()
     rc, flags = m.device_status()
     if rc != 0:
@@ -278,7 +287,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        m.forward(x, w, h0, c0, out=out)
+        m.forward(x, w, h0, c0, out=out, lengths=lengths)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -288,7 +297,7 @@ def main():
         log(f"device status after timed steps: {rc} flags {flags}")
         sys.exit(1)
     ms = total_ms / args.steps
-    value = spec.cells * args.steps / (total_ms / 1e3)
+    value = cells * args.steps / (total_ms / 1e3)
     log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value / 1e9:.3f} G cells/s; phases {tm}")
 
     proj_avg = tm["proj_ms"] / max(1, tm["proj_launches"])
@@ -323,7 +332,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on a row sample")
-        cpu = cpu_baseline(inp, args.cpu_budget)
+        cpu = cpu_baseline(inp, args.cpu_budget, lengths)
         log(f"cpu baseline: {cpu}")
 
     line = {"metric": METRIC, "value": value, "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps,
@@ -331,7 +340,9 @@ def main():
             "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded; random-init weights)",
             "config": {"workload": args.workload, "input_size": spec.input_size, "hidden_size": spec.hidden_size,
                        "num_layers": spec.num_layers, "bidirectional": spec.bidirectional, "T": spec.T,
-                       "B": spec.B, "cells_per_step": spec.cells, "schedule": desc},
+                       "B": spec.B, "cells_per_step": cells, "schedule": desc,
+                       **({} if lengths is None else {"lengths": args.lengths,
+                                                       "valid_steps": int(np.sum(lengths))})},
             "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
