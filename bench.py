@@ -224,6 +224,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lengths", choices=["none", "mix", "ragged"], default="none",
                     help="variable-length rows (lstm_forward_lengths); the value then counts valid cells only")
+    ap.add_argument("--batch-first", action="store_true", help="x [B, T, I] and y [B, T, D*H]")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -253,7 +254,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    x = to_dev(inp.x)
+    x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if args.batch_first else inp.x)
     w = [to_dev(p) for p in inp.params]
     h0 = to_dev(inp.h0)
     c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
@@ -264,10 +265,12 @@ def main():
     if args.poll_sleep >= 0:
         opts[pkg.LSTM_OPT_POLL_SLEEP] = args.poll_sleep
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
-                 dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile, options=opts)
+                 dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile, options=opts,
+                 batch_first=args.batch_first)
     desc = m.describe(spec.T, spec.B)
     log(f"schedule: {desc}")
-    out = (torch.empty(spec.T, spec.B, spec.D * spec.hidden_size, dtype=x.dtype, device=dev),
+    yshape = (spec.B, spec.T) if args.batch_first else (spec.T, spec.B)
+    out = (torch.empty(*yshape, spec.D * spec.hidden_size, dtype=x.dtype, device=dev),
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=x.dtype, device=dev),
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream(dev)
@@ -342,7 +345,8 @@ def main():
                        "num_layers": spec.num_layers, "bidirectional": spec.bidirectional, "T": spec.T,
                        "B": spec.B, "cells_per_step": cells, "schedule": desc,
                        **({} if lengths is None else {"lengths": args.lengths,
-                                                       "valid_steps": int(np.sum(lengths))})},
+                                                       "valid_steps": int(np.sum(lengths))}),
+                       **({"layout": "batch_first"} if args.batch_first else {})},
             "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 

@@ -96,9 +96,13 @@ typedef enum {
                                 all layers in one pipelined persistent launch when every layer's weights
                                 fit on chip (layer l consumes layer l-1's h_t as it is produced). Changes
                                 lstm_workspace_size. */
-    LSTM_OPT_FUSE_INPUT = 11  /* 1 (default): a layer whose recurrence runs as one persistent launch and
+    LSTM_OPT_FUSE_INPUT = 11, /* 1 (default): a layer whose recurrence runs as one persistent launch and
                                 whose W_ih share fits in registers computes x_t W_ih^T + b_ih + b_hh inside
                                 that launch (no projection GEMM, G unused); 0: always hoist the projection */
+    LSTM_OPT_BATCH_FIRST = 12 /* 0 (default): x is [T, B, input_size] and y is [T, B, D*H]; 1: x is
+                                [B, T, input_size] and y is [B, T, D*H] ("batch_first" of the trace page's
+                                op signature, Step 3).  h0, c0, h_n, c_n stay [L*D, B, H].  A layout
+                                option: unlike the others it changes what the pointers mean */
 } lstm_option;
 
 /* Accumulated per-phase device time of the calls made since the last reset
@@ -123,7 +127,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
 void lstm_destroy(lstm_plan *plan);
 
 /* Set an execution option.  Options change how the forward is scheduled, not
- * what it computes. */
+ * what it computes (LSTM_OPT_BATCH_FIRST alone changes the layout of x and y). */
 lstm_status lstm_set_option(lstm_plan *plan, int option, int value);
 
 /* Bytes of device workspace lstm_forward needs for sequence length T and batch

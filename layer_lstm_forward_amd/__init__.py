@@ -24,6 +24,7 @@ LSTM_OPT_PROJ_TILE = 8
 LSTM_OPT_READ_PACE = 9
 LSTM_OPT_LAYER_PIPE = 10
 LSTM_OPT_FUSE_INPUT = 11
+LSTM_OPT_BATCH_FIRST = 12
 STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
           -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
           -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}
@@ -173,10 +174,11 @@ class LSTM:
     """
 
     def __init__(self, input_size, hidden_size, num_layers=1, bidirectional=False, bias=True,
-                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None):
+                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None, batch_first=False):
         self.input_size, self.hidden_size = int(input_size), int(hidden_size)
         self.num_layers, self.bidirectional, self.bias = int(num_layers), bool(bidirectional), bool(bias)
         self.dtype = dtype
+        self.batch_first = bool(batch_first)
         self.D = 2 if self.bidirectional else 1
         self.plan = lstm_create(input_size, hidden_size, num_layers, bidirectional, bias,
                                 LSTM_BF16 if dtype == "bf16" else LSTM_F32)
@@ -184,6 +186,8 @@ class LSTM:
             lstm_set_option(self.plan, LSTM_OPT_RECURRENCE, recurrence)
         if rec_tile:
             lstm_set_option(self.plan, LSTM_OPT_REC_TILE, rec_tile)
+        if self.batch_first:
+            lstm_set_option(self.plan, LSTM_OPT_BATCH_FIRST, 1)
         for opt, val in (options or {}).items():
             lstm_set_option(self.plan, opt, val)
         self._ws = None
@@ -209,14 +213,17 @@ class LSTM:
         import torch
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         if not x.is_cuda or x.dtype != tdt or not x.is_contiguous() or x.dim() != 3:
-            raise ValueError("x must be a contiguous [T, B, input_size] device tensor of the plan's dtype")
+            raise ValueError("x must be a contiguous [T, B, input_size] ([B, T, input_size] with batch_first) "
+                             "device tensor of the plan's dtype")
         for w in weights:
             if not w.is_cuda or w.dtype != tdt or not w.is_contiguous():
                 raise ValueError("weights must be contiguous device tensors of the plan's dtype")
         T, B, _ = x.shape
+        if self.batch_first:
+            B, T = T, B
         H, L, D = self.hidden_size, self.num_layers, self.D
         if out is None:
-            y = torch.empty(T, B, D * H, dtype=tdt, device=x.device)
+            y = torch.empty(*((B, T) if self.batch_first else (T, B)), D * H, dtype=tdt, device=x.device)
             hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
             cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
         else:

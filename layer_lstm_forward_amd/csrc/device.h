@@ -81,6 +81,12 @@ __device__ inline u32x4 load_frag(const typename DT::S *row, int k, int kmax, bo
     return __builtin_bit_cast(u32x4, tmp);
 }
 
+// Row of (time t, batch b) in x, G and y: time-major [T][B] rows, or
+// batch-major [B][T] rows (batch_first).
+__device__ inline size_t trow(int t, int b, int T, int B, bool batch_first) {
+    return batch_first ? (size_t)b * T + t : (size_t)t * B + b;
+}
+
 // sigma(z) = 1 / (1 + e^-z) from the hardware base-2 exponential and
 // reciprocal; exp2 overflows to +inf for very negative z and the reciprocal
 // of +inf is 0, so the saturated ends are exact.  tanh(z) = 2 sigma(2z) - 1.

@@ -34,6 +34,7 @@ struct RecArgs {
     float *cstate;           // [D, B, H] carry between step launches
     float *hstate;           // [D, B, H] h carry between step launches (k_rec with lengths)
     const int *len;          // [B] valid steps per batch row, or NULL (all T)
+    int bfirst;              // x, G, y rows are (b, t) = b*T + t instead of t*B + b
     unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 32-bit words
     unsigned xpar;           // bit p: parity of the writes buffer p received before this launch
     unsigned *status;        // error word
@@ -131,8 +132,8 @@ hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hip
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, int *blocks_per_cu);
 // input chunks per wave of the tile's fused-projection variant (0: none)
 int rec_fused_chunks(RecTile t);
-// Zero y[t][b][:] for every t >= len[b] (padded steps of variable-length rows).
-hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, hipStream_t s);
+// Zero the y row of (t, b) for every t >= len[b] (padded steps of variable-length rows).
+hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first, hipStream_t s);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
 // One recurrent step (a.s_begin) as a GEMM with the cell update fused
 // (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.

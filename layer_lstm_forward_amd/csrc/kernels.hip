@@ -538,8 +538,8 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const bool ok = in && cv[i];
-            const float *gp = a.G + ((size_t)(ok ? tg : 0) * B + b0 + (ok ? cm[i] : 0)) * ldg + (size_t)d * 4 * H +
-                              j0 + (ok ? cu[i] : 0);
+            const float *gp = a.G + trow(ok ? tg : 0, b0 + (ok ? cm[i] : 0), T, B, a.bfirst) * ldg +
+                              (size_t)d * 4 * H + j0 + (ok ? cu[i] : 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) g[i][q] = gp[(size_t)q * H];
         }
@@ -554,9 +554,12 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         // wave-uniform by construction; said explicitly so that the resource
         // stays in scalar registers (else every load becomes a waterfall loop)
         const int tx = __builtin_amdgcn_readfirstlane(d == 0 ? st : T - 1 - st);
+        // rows of batch rows b0.. at time tx: consecutive (time-major) or T
+        // rows apart (batch_first)
+        const size_t xstride = a.bfirst ? (size_t)T * a.I : (size_t)a.I;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<S *>(static_cast<const S *>(a.x) + (size_t)tx * B * a.I), (short)0,
-            (int)((size_t)B * a.I * sizeof(S)), 0x00020000);
+            const_cast<S *>(static_cast<const S *>(a.x) + trow(tx, 0, T, B, a.bfirst) * a.I), (short)0,
+            (int)(((size_t)(B - 1) * xstride + a.I) * sizeof(S)), 0x00020000);
 #pragma unroll
         for (int cx = 0; cx < FX; ++cx)
 #pragma unroll
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                 const int k = (wk * ncx + cx) * DT::KC + (lane >> 4) * DT::PER16;
                 const bool ok = cx < ncx && m < rows && k < a.I;
                 xf[cx][i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    r, ok ? (int)((((size_t)(b0 + m)) * a.I + k) * sizeof(S)) : 0x7FFFFFF0, 0, 0);
+                    r, ok ? (int)((((size_t)(b0 + m)) * xstride + k) * sizeof(S)) : 0x7FFFFFF0, 0, 0);
             }
     };
     if constexpr (FUSED) {
@@ -820,7 +823,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             }
             if (cv[i]) {
                 const int bb = b0 + m;
-                static_cast<S *>(a.Y)[((size_t)t * B + bb) * ldy + (size_t)d * H + jj] = t < clen[i] ? hs : (S)0;
+                static_cast<S *>(a.Y)[trow(t, bb, T, B, a.bfirst) * ldy + (size_t)d * H + jj] = t < clen[i] ? hs : (S)0;
                 if (s == T - 1) {
                     const size_t si = ((size_t)d * B + bb) * H + jj;
                     if (a.hn) static_cast<S *>(a.hn)[si] = hs;
@@ -1253,8 +1256,8 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     size_t lda = 0;
     if (s > 0) {
         const int tp = d == 0 ? s - 1 : T - s;
-        hsrc = static_cast<const S *>(a.Y) + ((size_t)tp * B + b0) * ldy + (size_t)d * H;
-        lda = ldy;
+        hsrc = static_cast<const S *>(a.Y) + trow(tp, b0, T, B, a.bfirst) * ldy + (size_t)d * H;
+        lda = a.bfirst ? (size_t)T * ldy : ldy;
     } else if (a.h0) {
         hsrc = static_cast<const S *>(a.h0) + ((size_t)d * B + b0) * H;
         lda = H;
@@ -1353,7 +1356,7 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             pre[j] = acc[j][v] + (WKS == 2 ? red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane] : 0.f);
-        const float *g = a.G + ((size_t)t * B + m) * ldg + (size_t)d * 4 * H + u;
+        const float *g = a.G + trow(t, m, T, B, a.bfirst) * ldg + (size_t)d * 4 * H + u;
         const size_t si = ((size_t)d * B + m) * H + u;
         const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
         const float ig = sigmoid_f(pre[0] + g[0]);
@@ -1370,7 +1373,7 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             hs = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
         }
         a.cstate[si] = cn;
-        static_cast<S *>(a.Y)[((size_t)t * B + m) * ldy + (size_t)d * H + u] = hs;
+        static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
         if (last) {
             if (a.hn) static_cast<S *>(a.hn)[si] = hs;
             if (a.cn) a.cn[si] = cn;
@@ -1380,11 +1383,12 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
 
 // y[t][b][:] = 0 for t >= len[b]; one 16-bit unit per thread (rows of bf16
 // or fp32 values are whole units)
-__global__ void k_mask_padded(uint16_t *y, const int *len, int T, int B, size_t row_units) {
+__global__ void k_mask_padded(uint16_t *y, const int *len, int T, int B, size_t row_units, int batch_first) {
     const size_t n = (size_t)T * B * row_units;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
         const size_t row = i / row_units;
-        const int t = (int)(row / B), b = (int)(row % B);
+        const int t = batch_first ? (int)(row % T) : (int)(row / B);
+        const int b = batch_first ? (int)(row / T) : (int)(row % B);
         if (t >= len[b]) y[i] = 0;
     }
 }
@@ -1602,8 +1606,11 @@ hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool 
 
 bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
     const size_t es = dtype == DT_BF16 ? 2 : 4;
+    // the A rows of one block (y of the previous step) must be addressable by
+    // one buffer resource: 127 row strides, T rows apart when batch_first
+    const size_t astride = (size_t)a.D * a.H * (a.bfirst ? (size_t)a.T : 1);
     bool ok = ((size_t)a.H * es) % 16 == 0 && (size_t)4 * a.H * a.H * es < (1u << 31) &&
-              ((size_t)128 * a.D * a.H * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
+              ((size_t)128 * astride * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
               (!a.h0 || (uintptr_t)a.h0 % 16 == 0);
     for (int d = 0; d < a.D; ++d) ok = ok && (uintptr_t)a.whh[d] % 16 == 0;
     return ok;
@@ -1631,12 +1638,13 @@ hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
     return launch_step_t<F32, 2>(a, s);
 }
 
-hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, hipStream_t s) {
+hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first,
+                              hipStream_t s) {
     if (row_bytes % 2 != 0) return hipErrorInvalidValue;
     const size_t n = (size_t)T * B * (row_bytes / 2);
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     hipLaunchKernelGGL(k_mask_padded, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t *>(y), len, T, B,
-                       row_bytes / 2);
+                       row_bytes / 2, batch_first ? 1 : 0);
     return hipGetLastError();
 }
 

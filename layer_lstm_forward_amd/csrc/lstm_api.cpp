@@ -24,6 +24,7 @@ struct lstm_plan {
     int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next
     int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
+    int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
                        // (off by default: slower than layer by layer on the measured workloads)
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
@@ -190,20 +191,23 @@ double step_cost(const lstm_plan *p, const Sched &s, int cus) {
 // variant whose register budget covers the wave's share of the input width,
 // rows are 16-byte multiples and aligned, one time slice of X is addressable
 // by a buffer resource, and the fused kernel is co-resident like the plain one.
-int fused_chunks_shape(const lstm_plan *p, const Sched &s, int B, int in_l, const DevInfo &di) {
+int fused_chunks_shape(const lstm_plan *p, const Sched &s, int T, int B, int in_l, const DevInfo &di) {
     if (!p->fuse_input || !s.persistent || !s.geom.wreg || !di.ok) return 0;
     const int fx = rec_fused_chunks(s.tile);
     if (fx == 0) return 0;
     const size_t es = elem_size(p->dtype);
     const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
     const int ncx = ((in_l + kc - 1) / kc + s.tile.WK - 1) / s.tile.WK;
-    if (ncx > fx || ((size_t)in_l * es) % 16 != 0 || (size_t)B * in_l * es >= ((size_t)1 << 31)) return 0;
+    // one buffer resource spans the B rows of one time step: B rows in a row
+    // (time-major) or T rows apart (batch_first)
+    const size_t span = (size_t)B * in_l * es * (p->batch_first ? (size_t)T : 1);
+    if (ncx > fx || ((size_t)in_l * es) % 16 != 0 || span >= ((size_t)1 << 31)) return 0;
     return ncx;
 }
 
-int fused_chunks(const lstm_plan *p, const Sched &s, int B, int in_l, const void *X, const void *const *wih,
-                 const DevInfo &di) {
-    const int ncx = fused_chunks_shape(p, s, B, in_l, di);
+int fused_chunks(const lstm_plan *p, const Sched &s, int T, int B, int in_l, const void *X,
+                 const void *const *wih, const DevInfo &di) {
+    const int ncx = fused_chunks_shape(p, s, T, B, in_l, di);
     if (ncx == 0 || (uintptr_t)X % 16 != 0) return 0;
     for (int d = 0; d < p->D; ++d)
         if ((uintptr_t)wih[d] % 16 != 0) return 0;
@@ -379,7 +383,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 101; }
+int lstm_version(void) { return 102; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -420,6 +424,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->read_pace_ns = 450;
     p->layer_pipe = 0;
     p->fuse_input = 1;
+    p->batch_first = 0;
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
@@ -486,6 +491,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
         case LSTM_OPT_FUSE_INPUT:
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
             p->fuse_input = value;
+            return LSTM_OK;
+        case LSTM_OPT_BATCH_FIRST:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->batch_first = value;
             return LSTM_OK;
         case LSTM_OPT_READ_PACE:
             if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
@@ -560,14 +569,14 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     for (int l = 0; l < p->L && xl + 9 < sizeof(xproj); ++l) {
         const int in_l = l == 0 ? p->I : p->D * p->H;
         xl += (size_t)std::snprintf(xproj + xl, sizeof(xproj) - xl, "%s%s", l ? "," : "",
-                                    fused_chunks_shape(p, s, B, in_l, di) ? "fused" : "hoisted");
+                                    fused_chunks_shape(p, s, T, B, in_l, di) ? "fused" : "hoisted");
     }
     std::snprintf(buf, len,
                   "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
-                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s",
+                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s%s",
                   proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
                   s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds",
-                  xproj);
+                  xproj, p->batch_first ? " layout=batch-first" : "");
     return LSTM_OK;
 }
 
@@ -626,6 +635,8 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         q.h0 = h0 ? static_cast<const char *>(h0) + (size_t)l * state_elems * es : nullptr;
         q.H = p->H;
         q.D = p->D;
+        q.T = T;
+        q.bfirst = p->batch_first;
         gemm = rec_step_gemm_ok(q, p->dtype);
     }
     if (p->rec_mode == LSTM_REC_GEMM && !gemm) return LSTM_ERR_UNSUPPORTED;
@@ -634,7 +645,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     // one cooperative launch.  If the runtime refuses that launch, the
     // sequential path below redoes the work.
     PipeSched ps{};
-    if (!dlen && choose_pipe(p, B, dev, &ps)) {
+    if (!dlen && !p->batch_first && choose_pipe(p, B, dev, &ps)) {
         const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
         const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
         const size_t slot_words = region_words * ps.NGB;
@@ -719,7 +730,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
 
         const void *wih[2] = {nullptr, nullptr};
         for (int d = 0; d < p->D; ++d) wih[d] = weights[(size_t)(l * p->D + d) * per];
-        int ncx = fused_chunks(p, sch, B, in_l, X, wih, di);
+        int ncx = fused_chunks(p, sch, T, B, in_l, X, wih, di);
 
         // hoisted projection G = X W_ih^T + b_ih + b_hh (skipped when fused)
         auto project = [&]() -> bool {
@@ -767,6 +778,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         ra.cstate = cstate;
         ra.hstate = hstate;
         ra.len = dlen;
+        ra.bfirst = p->batch_first;
         ra.xbuf = xbuf;
         ra.xpar = xpar;
         ra.status = status;
@@ -832,7 +844,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         // k_rec_step leaves the unchanged h in y at padded steps (the next step
         // reads it there); the caller sees zeros
         if (dlen && use_gemm_layer && l == p->L - 1 &&
-            launch_mask_padded(y, dlen, T, B, (size_t)p->D * p->H * es, st) != hipSuccess)
+            launch_mask_padded(y, dlen, T, B, (size_t)p->D * p->H * es, p->batch_first != 0, st) != hipSuccess)
             return LSTM_ERR_LAUNCH;
     }
     if (p->timing) p->acc.calls += 1;

@@ -22,7 +22,10 @@ def to_dev(a, bf16, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1, options=None, lengths=None):
+def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1, options=None, lengths=None,
+            batch_first=False):
+    """batch_first: run a batch-first plan on x transposed to [B, T, I] and
+    return y transposed back to [T, B, D*H] (h_n, c_n have one layout)."""
     """Returns (y, h_n, c_n) as float64 numpy arrays and the model used."""
     import torch
     import layer_lstm_forward_amd as pkg
@@ -30,8 +33,9 @@ def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1
     bf = s.dtype == "bf16"
     if model is None:
         model = pkg.LSTM(s.input_size, s.hidden_size, s.num_layers, s.bidirectional, bias=s.has_bias,
-                         dtype=s.dtype, recurrence=recurrence, rec_tile=rec_tile, options=options)
-    x = to_dev(inp.x, bf, device)
+                         dtype=s.dtype, recurrence=recurrence, rec_tile=rec_tile, options=options,
+                         batch_first=batch_first)
+    x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if batch_first else inp.x, bf, device)
     w = [to_dev(p, bf, device) for p in inp.params]
     h0 = to_dev(inp.h0, bf, device)
     c0 = to_dev(inp.c0, False, device)
@@ -41,6 +45,8 @@ def run_gpu(inp, recurrence=0, rec_tile=0, model=None, device="cuda:0", repeat=1
     rc, flags = model.device_status()
     assert rc == 0 and flags == 0, f"device status {rc} flags {flags}"
     out = tuple(t.float().cpu().numpy().astype(np.float64) for t in (y, hn, cn))
+    if batch_first:
+        out = (np.ascontiguousarray(out[0].transpose(1, 0, 2)),) + out[1:]
     return out, model
 
 

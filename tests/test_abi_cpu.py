@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 101
+    assert pkg.lstm_version() == 102
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -81,9 +81,10 @@ def test_set_option():
             pkg.lstm_set_option(p, pkg.LSTM_OPT_READ_PACE, v)
         for v in (0, 1):
             pkg.lstm_set_option(p, pkg.LSTM_OPT_FUSE_INPUT, v)
+            pkg.lstm_set_option(p, pkg.LSTM_OPT_BATCH_FIRST, v)
         for opt, val in ((pkg.LSTM_OPT_RECURRENCE, 4), (pkg.LSTM_OPT_REC_TILE, 333), (6, 0),
                          (pkg.LSTM_OPT_READ_PACE, -1), (pkg.LSTM_OPT_READ_PACE, 100001),
-                         (pkg.LSTM_OPT_FUSE_INPUT, 2), (99, 0)):
+                         (pkg.LSTM_OPT_FUSE_INPUT, 2), (pkg.LSTM_OPT_BATCH_FIRST, -1), (99, 0)):
             with pytest.raises(pkg.LSTMError) as e:
                 pkg.lstm_set_option(p, opt, val)
             assert e.value.status == -7

@@ -155,6 +155,25 @@ def test_variable_lengths(spec, mode):
         assert np.all(y[n:, b] == 0.0), f"row {b}: padded outputs not zero"
 
 
+@pytest.mark.parametrize("spec", LENGTH_SPECS, ids=_id)
+@pytest.mark.parametrize("mode", sorted(LENGTH_MODES))
+@pytest.mark.parametrize("with_lengths", [False, True], ids=["full", "lengths"])
+def test_batch_first(spec, mode, with_lengths):
+    """x [B, T, I] and y [B, T, D*H] (batch_first) in every recurrence mode,
+    with and without per-row lengths, against the oracle on the same data."""
+    from layer_lstm_forward_amd.synth import make_lengths
+    print(f"case {_id(spec)} batch_first {mode} {with_lengths}", flush=True)
+    rec, opts = LENGTH_MODES[mode]
+    if mode == "gemm" and not _gemm_step_shape_ok(spec):
+        pytest.skip("rows are not 16-byte multiples: the per-step GEMM refuses this shape")
+    inp = make_inputs(spec)
+    lengths = make_lengths(spec, "ragged") if with_lengths else None
+    got, m = run_gpu(inp, recurrence=rec, options=opts, lengths=lengths, batch_first=True)
+    assert "batch-first" in m.describe(spec.T, spec.B) or mode == "gemm"
+    ref = run_oracle(inp, lengths=lengths)
+    assert_parity(got, ref, spec.dtype, f"batch_first {mode}: {m.describe(spec.T, spec.B)}")
+
+
 def test_lengths_all_full_equal_plain_forward():
     spec = Spec(48, 72, 2, True, 7, 37, "f32", 705, "normal0.1")
     inp = make_inputs(spec)
