@@ -54,6 +54,10 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             dp, ctypes.POINTER(ctypes.c_int), dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp,
             ctypes.c_int]
+        lib.oracle_lstm_backward.restype = ctypes.c_int
+        lib.oracle_lstm_backward.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -126,3 +130,40 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     if rc != 0:
         raise RuntimeError(f"oracle_lstm_forward failed with {rc}")
     return y, hn, cn
+
+
+def lstm_backward(x, params, hidden_size: int, num_layers: int, bidirectional: bool, dy,
+                  h0=None, c0=None, dh_n=None, dc_n=None, has_bias: bool = True, bf16: bool = False):
+    """Gradients of the forward pass (see the C file).
+
+    dy [T, B, D*H]; dh_n, dc_n [L*D, B, H] or None (zeros).
+    Returns (dx [T, B, I], dh0 [L*D, B, H], dc0 [L*D, B, H], dparams) as
+    float64, dparams in the order and shapes of params.
+    """
+    lib = _load()
+    x64 = np.ascontiguousarray(as_f64(x, bf16))
+    T, B, I = x64.shape
+    H, L, D = int(hidden_size), int(num_layers), 2 if bidirectional else 1
+    per = 4 if has_bias else 2
+    if len(params) != L * D * per:
+        raise ValueError(f"expected {L * D * per} parameter arrays, got {len(params)}")
+    p64 = [np.ascontiguousarray(as_f64(p, bf16)) for p in params]
+    arr = (ctypes.POINTER(ctypes.c_double) * len(p64))(*[_ptr(p) for p in p64])
+    dps = [np.empty_like(p) for p in p64]
+    darr = (ctypes.POINTER(ctypes.c_double) * len(dps))(*[_ptr(p) for p in dps])
+    h064 = None if h0 is None else np.ascontiguousarray(as_f64(h0, bf16))
+    c064 = None if c0 is None else np.ascontiguousarray(as_f64(c0))
+    dy64 = np.ascontiguousarray(np.asarray(dy, np.float64))
+    if dy64.shape != (T, B, D * H):
+        raise ValueError(f"dy shape {dy64.shape} != {(T, B, D * H)}")
+    dhn = None if dh_n is None else np.ascontiguousarray(np.asarray(dh_n, np.float64))
+    dcn = None if dc_n is None else np.ascontiguousarray(np.asarray(dc_n, np.float64))
+    dx = np.empty((T, B, I), np.float64)
+    dh0 = np.empty((L * D, B, H), np.float64)
+    dc0 = np.empty((L * D, B, H), np.float64)
+    opt = lambda a: _ptr(a) if a is not None else None  # noqa: E731
+    rc = lib.oracle_lstm_backward(T, B, I, H, L, D, _ptr(x64), opt(h064), opt(c064), arr, 1 if has_bias else 0,
+                                  _ptr(dy64), opt(dhn), opt(dcn), _ptr(dx), _ptr(dh0), _ptr(dc0), darr)
+    if rc != 0:
+        raise RuntimeError(f"oracle_lstm_backward failed with {rc}")
+    return dx, dh0, dc0, dps

@@ -38,6 +38,15 @@
  *     the reverse output is stored at the time index of the input it has
  *     just consumed, and its "final" state is the one after consuming t = 0.
  *   - Shapes of the returned tensors: warp-nn __call__ "Returns".
+ *   - Backward pass (oracle_lstm_backward): the trace page's "cuDNN
+ *     Backward" section returns the gradients of the input, of the initial
+ *     states and of the weights from the gradients of (output, h_n, c_n) and
+ *     the activations saved by the forward; the pulsatrix "LSTMModule"
+ *     reference describes backpropagation through time across the four gates
+ *     and the cell carry, accumulating every weight and bias gradient over
+ *     all time steps.  The gradients are those of the cell equations above by
+ *     the chain rule, taken step by step in the reverse of each direction's
+ *     scan order (written out in the function).
  *   - Variable-length batches (oracle_lstm_forward_lengths): "Complete
  *     Trace: nn.LSTM", Step 3, lists a packed-sequence overload beside the
  *     padded one, and the MXNet blog's "Sequence Buckets" pads sequences of
@@ -173,6 +182,175 @@ int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
     memcpy(y, Y, sizeof(double) * seq_out);
     free(h); free(c); free(pre); free(Yl); free(Xl);
     return 0;
+}
+
+/* Gradients of the forward pass above (every row has all T steps).
+ *   dy   [T][B][D*H] gradient of y;  dh_n, dc_n [L*D][B][H] or NULL (zeros)
+ * Outputs (each may be NULL when not wanted):
+ *   dx   [T][B][I];  dh0, dc0 [L*D][B][H];
+ *   dparams: same order and shapes as params (W_ih, W_hh[, b_ih, b_hh]),
+ *            overwritten (not accumulated into)
+ * The forward is recomputed here; its per-step activations are kept. */
+int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
+                         const double *x, const double *h0, const double *c0,
+                         const double *const *params, int has_bias,
+                         const double *dy, const double *dh_n, const double *dc_n,
+                         double *dx, double *dh0, double *dc0, double *const *dparams)
+{
+    if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) || !x || !params || !dy)
+        return -1;
+    const int per = has_bias ? 4 : 2;
+    const int G = 4 * H;
+    const size_t BH = (size_t)B * H, TBH = (size_t)T * BH;
+    const int win = I > D * H ? I : D * H;
+    /* saved forward activations, per (layer, direction): gates i,f,g,o and c, h at every t */
+    const size_t nld = (size_t)L * D;
+    double *gi = malloc(sizeof(double) * nld * TBH), *gf = malloc(sizeof(double) * nld * TBH);
+    double *gg = malloc(sizeof(double) * nld * TBH), *go = malloc(sizeof(double) * nld * TBH);
+    double *cs = malloc(sizeof(double) * nld * TBH), *hs = malloc(sizeof(double) * nld * TBH);
+    double *seq = malloc(sizeof(double) * (size_t)(L + 1) * T * B * win);  /* input of each layer */
+    double *dY = malloc(sizeof(double) * (size_t)T * B * win), *dX = malloc(sizeof(double) * (size_t)T * B * win);
+    double *dz = malloc(sizeof(double) * (size_t)B * G);
+    double *dh = malloc(sizeof(double) * BH), *dc = malloc(sizeof(double) * BH), *dhn = malloc(sizeof(double) * BH);
+    double *h = malloc(sizeof(double) * BH), *c = malloc(sizeof(double) * BH);
+    int rc = -2;
+    if (!gi || !gf || !gg || !go || !cs || !hs || !seq || !dY || !dX || !dz || !dh || !dc || !dhn || !h || !c)
+        goto out;
+    /* ---- forward, keeping activations */
+    for (size_t e = 0; e < (size_t)T * B * I; ++e) seq[e] = x[e];
+    for (int l = 0; l < L; ++l) {
+        const int in_w = l == 0 ? I : D * H;
+        const double *in_seq = seq + (size_t)l * T * B * win;
+        double *out_seq = seq + (size_t)(l + 1) * T * B * win;
+        for (int d = 0; d < D; ++d) {
+            const double *const *p = params + (size_t)(l * D + d) * per;
+            const size_t st = (size_t)(l * D + d) * BH, ld = (size_t)(l * D + d) * TBH;
+            for (size_t e = 0; e < BH; ++e) {
+                h[e] = h0 ? h0[st + e] : 0.0;
+                c[e] = c0 ? c0[st + e] : 0.0;
+            }
+            for (int s = 0; s < T; ++s) {
+                const int t = d == 0 ? s : T - 1 - s;
+                for (int b = 0; b < B; ++b) {
+                    const double *xt = in_seq + ((size_t)t * B + b) * in_w;
+                    double pre[4];
+                    for (int j = 0; j < H; ++j) {
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = q * H + j;
+                            double acc = has_bias ? p[2][r] + p[3][r] : 0.0;
+                            for (int k = 0; k < in_w; ++k) acc += p[0][(size_t)r * in_w + k] * xt[k];
+                            for (int k = 0; k < H; ++k) acc += p[1][(size_t)r * H + k] * h[(size_t)b * H + k];
+                            pre[q] = acc;
+                        }
+                        const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
+                        gi[e] = sigmoid(pre[0]);
+                        gf[e] = sigmoid(pre[1]);
+                        gg[e] = tanh(pre[2]);
+                        go[e] = sigmoid(pre[3]);
+                    }
+                    for (int j = 0; j < H; ++j) {
+                        const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
+                        cs[e] = gf[e] * c[(size_t)b * H + j] + gi[e] * gg[e];
+                        hs[e] = go[e] * tanh(cs[e]);
+                    }
+                    for (int j = 0; j < H; ++j) {
+                        const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
+                        c[(size_t)b * H + j] = cs[e];
+                        h[(size_t)b * H + j] = hs[e];
+                        out_seq[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] = hs[e];
+                    }
+                }
+            }
+        }
+    }
+    /* ---- backward, top layer first */
+    for (size_t e = 0; e < (size_t)T * B * D * H; ++e) dY[e] = dy[e];
+    for (int l = L - 1; l >= 0; --l) {
+        const int in_w = l == 0 ? I : D * H;
+        const double *in_seq = seq + (size_t)l * T * B * win;
+        memset(dX, 0, sizeof(double) * (size_t)T * B * in_w);
+        for (int d = 0; d < D; ++d) {
+            const double *const *p = params + (size_t)(l * D + d) * per;
+            double *const *dp = dparams ? dparams + (size_t)(l * D + d) * per : NULL;
+            const size_t st = (size_t)(l * D + d) * BH, ld = (size_t)(l * D + d) * TBH;
+            if (dp) {
+                memset(dp[0], 0, sizeof(double) * (size_t)G * in_w);
+                memset(dp[1], 0, sizeof(double) * (size_t)G * H);
+                if (has_bias) {
+                    memset(dp[2], 0, sizeof(double) * G);
+                    memset(dp[3], 0, sizeof(double) * G);
+                }
+            }
+            /* gradients arriving from after the last step: those of h_n, c_n */
+            for (size_t e = 0; e < BH; ++e) {
+                dhn[e] = dh_n ? dh_n[st + e] : 0.0;
+                dc[e] = dc_n ? dc_n[st + e] : 0.0;
+            }
+            /* walk the scan backwards: s = T-1 is the step the scan took last */
+            for (int s = T - 1; s >= 0; --s) {
+                const int t = d == 0 ? s : T - 1 - s;
+                const int tp = d == 0 ? t - 1 : t + 1; /* time of the scan's previous step */
+                for (int b = 0; b < B; ++b) {
+                    for (int j = 0; j < H; ++j) {
+                        const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
+                        const size_t eb = (size_t)b * H + j;
+                        /* h_t feeds y_t and the next step's products */
+                        const double dht = dY[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] + dhn[eb];
+                        const double tc = tanh(cs[e]);
+                        const double cprev = s == 0 ? (c0 ? c0[st + eb] : 0.0) : cs[ld + (size_t)tp * BH + eb];
+                        /* h = o tanh(c);  c = f c_prev + i g */
+                        const double dct = dc[eb] + dht * go[e] * (1.0 - tc * tc);
+                        dz[(size_t)b * G + 3 * H + j] = dht * tc * go[e] * (1.0 - go[e]);
+                        dz[(size_t)b * G + j] = dct * gg[e] * gi[e] * (1.0 - gi[e]);
+                        dz[(size_t)b * G + 2 * H + j] = dct * gi[e] * (1.0 - gg[e] * gg[e]);
+                        dz[(size_t)b * G + H + j] = dct * cprev * gf[e] * (1.0 - gf[e]);
+                        dc[eb] = dct * gf[e];  /* to c_prev */
+                    }
+                }
+                /* the pre-activations are W_ih x_t + W_hh h_prev + b_ih + b_hh */
+                for (int b = 0; b < B; ++b) {
+                    const double *xt = in_seq + ((size_t)t * B + b) * in_w;
+                    for (int k = 0; k < H; ++k) {
+                        const double hprev = s == 0 ? (h0 ? h0[st + (size_t)b * H + k] : 0.0)
+                                                    : hs[ld + (size_t)tp * BH + (size_t)b * H + k];
+                        h[(size_t)b * H + k] = hprev;
+                    }
+                    for (int k = 0; k < H; ++k) {
+                        double acc = 0.0;
+                        for (int r = 0; r < G; ++r) acc += dz[(size_t)b * G + r] * p[1][(size_t)r * H + k];
+                        dh[(size_t)b * H + k] = acc;
+                    }
+                    for (int k = 0; k < in_w; ++k) {
+                        double acc = 0.0;
+                        for (int r = 0; r < G; ++r) acc += dz[(size_t)b * G + r] * p[0][(size_t)r * in_w + k];
+                        dX[((size_t)t * B + b) * in_w + k] += acc;
+                    }
+                    if (dp) {
+                        for (int r = 0; r < G; ++r) {
+                            const double z = dz[(size_t)b * G + r];
+                            for (int k = 0; k < in_w; ++k) dp[0][(size_t)r * in_w + k] += z * xt[k];
+                            for (int k = 0; k < H; ++k) dp[1][(size_t)r * H + k] += z * h[(size_t)b * H + k];
+                            if (has_bias) {
+                                dp[2][r] += z;
+                                dp[3][r] += z;
+                            }
+                        }
+                    }
+                }
+                for (size_t e = 0; e < BH; ++e) dhn[e] = dh[e];
+            }
+            if (dh0) memcpy(dh0 + st, dhn, sizeof(double) * BH);
+            if (dc0) memcpy(dc0 + st, dc, sizeof(double) * BH);
+        }
+        /* the layer below receives the gradient of its output sequence */
+        memcpy(dY, dX, sizeof(double) * (size_t)T * B * in_w);
+    }
+    if (dx) memcpy(dx, dY, sizeof(double) * (size_t)T * B * I);
+    rc = 0;
+out:
+    free(gi); free(gf); free(gg); free(go); free(cs); free(hs); free(seq); free(dY); free(dX);
+    free(dz); free(dh); free(dc); free(dhn); free(h); free(c);
+    return rc;
 }
 
 /* Every row has all T steps. */

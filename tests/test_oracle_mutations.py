@@ -1,5 +1,6 @@
 """The pins have power: each plausible mistake planted in a copy of the oracle
-(on the CPU, never on a GPU) makes the pin suite fail."""
+(on the CPU, never on a GPU) makes the pin suite fail (the forward pins for
+mistakes in the forward, the backward pins for mistakes in the backward)."""
 import os
 import subprocess
 import sys
@@ -31,9 +32,23 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+# mistakes in the backward pass, checked by tests/test_oracle_backward.py
+BACKWARD_MUTATIONS = {
+    "bwd_drop_cell_carry": ("dc[eb] = dct * gf[e];  /* to c_prev */", "dc[eb] = 0.0 * dct * gf[e];"),
+    "bwd_tanh_derivative": ("const double dct = dc[eb] + dht * go[e] * (1.0 - tc * tc);",
+                            "const double dct = dc[eb] + dht * go[e] * (1.0 - tc);"),
+    "bwd_o_gate_from_cell": ("dz[(size_t)b * G + 3 * H + j] = dht * tc * go[e] * (1.0 - go[e]);",
+                             "dz[(size_t)b * G + 3 * H + j] = dct * tc * go[e] * (1.0 - go[e]);"),
+    "bwd_one_bias_only": ("dp[3][r] += z;", "dp[3][r] += 0.0 * z;"),
+    "bwd_no_recurrent_gradient": ("for (size_t e = 0; e < BH; ++e) dhn[e] = dh[e];",
+                                  "for (size_t e = 0; e < BH; ++e) dhn[e] = 0.0 * dh[e];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(BACKWARD_MUTATIONS))
 def test_planted_mistake_is_caught(name, tmp_path):
-    old, new = MUTATIONS[name]
+    old, new = MUTATIONS[name] if name in MUTATIONS else BACKWARD_MUTATIONS[name]
+    target = "test_oracle_pins.py" if name in MUTATIONS else "test_oracle_backward.py"
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     mut = tmp_path / "lstm_oracle_mut.c"
@@ -43,6 +58,6 @@ def test_planted_mistake_is_caught(name, tmp_path):
                            str(mut), "-lm"])
     env = dict(os.environ, LSTM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", target)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
