@@ -226,8 +226,8 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
             const double *const *p = params + (size_t)(l * D + d) * per;
             const size_t st = (size_t)(l * D + d) * BH, ld = (size_t)(l * D + d) * TBH;
             for (size_t e = 0; e < BH; ++e) {
-                h[e] = h0 ? h0[st + e] : 0.0;
-                c[e] = c0 ? c0[st + e] : 0.0;
+                h[e] = (h0 != NULL) ? h0[st + e] : 0.0;
+                c[e] = (c0 != NULL) ? c0[st + e] : 0.0;
             }
             for (int s = 0; s < T; ++s) {
                 const int t = d == 0 ? s : T - 1 - s;
@@ -295,7 +295,8 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
                         const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
                         const size_t eb = (size_t)b * H + j;
                         /* h_t feeds y_t and the next step's products */
-                        const double dht = dY[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] + dhn[eb];
+                        const size_t ye = ((size_t)t * B + b) * (D * H) + (size_t)d * H + j;
+                        const double dht = dY[ye] + dhn[eb];
                         const double tc = tanh(cs[e]);
                         const double cprev = s == 0 ? (c0 ? c0[st + eb] : 0.0) : cs[ld + (size_t)tp * BH + eb];
                         /* h = o tanh(c);  c = f c_prev + i g */
