@@ -176,6 +176,56 @@ lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *leng
                                  int bidir, void *y, void *h_n, float *c_n, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------ training
+ * Backward pass (backpropagation through time).  The trace page "Complete
+ * Trace: nn.LSTM" ("cuDNN Backward") computes the gradients of the input, of
+ * the initial states and of the weights from the gradients of (output, h_n,
+ * c_n) and a reserve of activations saved by the forward; the pulsatrix
+ * "LSTMModule" reference describes the backpropagation through time across
+ * the four gates and the cell carry.  Time-major layout only (batch_first is
+ * LSTM_ERR_UNSUPPORTED), all rows of length T, no dropout. */
+
+/* Bytes of reserve lstm_forward_train fills for (T, B): per layer the gates
+ * i, f, g, o and the cell state c of every step (fp32), and the outputs of
+ * every layer but the top one (dtype). */
+lstm_status lstm_reserve_size(const lstm_plan *plan, int T, int B, size_t *bytes);
+
+/* lstm_forward, and also fills `reserve` (device memory of at least
+ * lstm_reserve_size bytes, caller-owned) for lstm_backward.  The layer
+ * pipeline is not used.  Errors as lstm_forward; a NULL reserve is
+ * LSTM_ERR_ARG, a short one LSTM_ERR_WORKSPACE. */
+lstm_status lstm_forward_train(lstm_plan *plan, const void *x, const void *h0, const float *c0,
+                               const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                               void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace lstm_backward needs for (T, B) (all fp32: the
+ * pre-activation gradients of a layer and their transpose, transposed
+ * operands, two output-gradient buffers, partial sums). */
+lstm_status lstm_backward_workspace_size(const lstm_plan *plan, int T, int B, size_t *bytes);
+
+/* Gradients of the forward that lstm_forward_train computed with the same x,
+ * h0, c0, weights and reserve.
+ *   y            [T, B, D*H] dtype, the output of that forward
+ *   dy           [T, B, D*H] dtype, gradient of y
+ *   dh_n         [L*D, B, H] dtype, or NULL (zeros)
+ *   dc_n         [L*D, B, H] float32, or NULL (zeros)
+ *   dx           [T, B, input_size] dtype, or NULL (not wanted)
+ *   dh0, dc0     [L*D, B, H] (dtype / float32), or NULL
+ *   dweights     host array of device pointers with the order and shapes of
+ *                `weights` (dtype), overwritten (not accumulated into); both
+ *                bias gradients equal the sum of the gate pre-activation
+ *                gradients
+ *   workspace    at least lstm_backward_workspace_size bytes
+ * Products accumulate in fp32 (bf16 operands are widened exactly); results
+ * are rounded to the output dtype once.  Errors as lstm_forward; a short
+ * reserve or workspace is LSTM_ERR_WORKSPACE. */
+lstm_status lstm_backward(lstm_plan *plan, const void *x, const void *h0, const float *c0,
+                          const void *const *weights, const void *y, const void *dy, const void *dh_n,
+                          const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
+                          int bidir, void *dx, void *dh0, float *dc0, void *const *dweights, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Synchronise `stream` and read the kernel status word a previous
  * lstm_forward left in `workspace`: *device_flags = 0 if every step barrier
  * completed.  Returns LSTM_ERR_DEVICE_TIMEOUT when a flag is set (the outputs

@@ -66,6 +66,15 @@ def load_library():
     lib.lstm_forward_lengths.restype = i
     lib.lstm_forward_lengths.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int), vp, vp, ctypes.POINTER(vp),
                                          i, i, i, i, vp, vp, vp, vp, sz, vp]
+    for fn in ("lstm_reserve_size", "lstm_backward_workspace_size"):
+        getattr(lib, fn).restype = i
+        getattr(lib, fn).argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.lstm_forward_train.restype = i
+    lib.lstm_forward_train.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp, sz, vp, sz,
+                                       vp]
+    lib.lstm_backward.restype = i
+    lib.lstm_backward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp, sz, i, i, i, i, vp, vp,
+                                  vp, ctypes.POINTER(vp), vp, sz, vp]
     lib.lstm_device_status.restype = i
     lib.lstm_device_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint)]
     lib.lstm_describe.restype = i
@@ -139,6 +148,44 @@ def lstm_forward_lengths(plan, x, lengths, h0, c0, weights, T, B, layers, bidir,
         arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
         ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
         int(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def _size_query(fn, plan, T, B) -> int:
+    n = ctypes.c_size_t()
+    rc = getattr(load_library(), fn)(ctypes.c_void_p(plan), int(T), int(B), ctypes.byref(n))
+    if rc:
+        raise LSTMError(rc, fn)
+    return int(n.value)
+
+
+def lstm_reserve_size(plan, T: int, B: int) -> int:
+    return _size_query("lstm_reserve_size", plan, T, B)
+
+
+def lstm_backward_workspace_size(plan, T: int, B: int) -> int:
+    return _size_query("lstm_backward_workspace_size", plan, T, B)
+
+
+def _ptrs(addrs):
+    return (ctypes.c_void_p * len(addrs))(*[int(a) for a in addrs])
+
+
+def lstm_forward_train(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, reserve, reserve_bytes,
+                       workspace, workspace_bytes, stream) -> int:
+    v = ctypes.c_void_p
+    return int(load_library().lstm_forward_train(
+        v(plan), v(x), v(h0 or None), v(c0 or None), _ptrs(weights), int(T), int(B), int(layers), int(bool(bidir)),
+        v(y), v(h_n or None), v(c_n or None), v(reserve), int(reserve_bytes), v(workspace), int(workspace_bytes),
+        v(stream or None)))
+
+
+def lstm_backward(plan, x, h0, c0, weights, y, dy, dh_n, dc_n, reserve, reserve_bytes, T, B, layers, bidir, dx,
+                  dh0, dc0, dweights, workspace, workspace_bytes, stream) -> int:
+    v = ctypes.c_void_p
+    return int(load_library().lstm_backward(
+        v(plan), v(x), v(h0 or None), v(c0 or None), _ptrs(weights), v(y), v(dy), v(dh_n or None), v(dc_n or None),
+        v(reserve), int(reserve_bytes), int(T), int(B), int(layers), int(bool(bidir)), v(dx or None), v(dh0 or None),
+        v(dc0 or None), _ptrs(dweights), v(workspace), int(workspace_bytes), v(stream or None)))
 
 
 def lstm_device_status(workspace, workspace_bytes, stream):
@@ -242,6 +289,51 @@ class LSTM:
         if rc:
             raise LSTMError(rc, "lstm_forward_lengths" if lengths is not None else "lstm_forward")
         return y, hn, cn
+
+    def forward_train(self, x, weights, h0=None, c0=None, stream=None):
+        """Forward that also keeps the reserve for backward(); returns
+        (y, h_n, c_n, reserve)."""
+        import torch
+        T, B, _ = x.shape
+        H, L, D = self.hidden_size, self.num_layers, self.D
+        tdt = x.dtype
+        y = torch.empty(T, B, D * H, dtype=tdt, device=x.device)
+        hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
+        cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
+        rbytes = lstm_reserve_size(self.plan, T, B)
+        reserve = torch.empty(max(rbytes, 1), dtype=torch.uint8, device=x.device)
+        ws, nbytes = self.workspace(T, B, x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lstm_forward_train(self.plan, x.data_ptr(), h0.data_ptr() if h0 is not None else 0,
+                                c0.data_ptr() if c0 is not None else 0, [w.data_ptr() for w in weights], T, B, L,
+                                self.bidirectional, y.data_ptr(), hn.data_ptr(), cn.data_ptr(), reserve.data_ptr(),
+                                rbytes, ws.data_ptr(), nbytes, stream)
+        if rc:
+            raise LSTMError(rc, "lstm_forward_train")
+        return y, hn, cn, reserve
+
+    def backward(self, x, weights, y, reserve, dy, h0=None, c0=None, dh_n=None, dc_n=None, stream=None):
+        """Gradients (dx, dh0, dc0, dweights) of a forward_train() call."""
+        import torch
+        T, B, _ = x.shape
+        H, L, D = self.hidden_size, self.num_layers, self.D
+        dx = torch.empty_like(x)
+        dh0 = torch.empty(L * D, B, H, dtype=x.dtype, device=x.device)
+        dc0 = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
+        dws = [torch.empty_like(w) for w in weights]
+        nbytes = lstm_backward_workspace_size(self.plan, T, B)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        addr = lambda t: t.data_ptr() if t is not None else 0  # noqa: E731
+        rc = lstm_backward(self.plan, x.data_ptr(), addr(h0), addr(c0), [w.data_ptr() for w in weights],
+                           y.data_ptr(), dy.data_ptr(), addr(dh_n), addr(dc_n), reserve.data_ptr(), reserve.numel(),
+                           T, B, L, self.bidirectional, dx.data_ptr(), dh0.data_ptr(), dc0.data_ptr(),
+                           [w.data_ptr() for w in dws], ws.data_ptr(), nbytes, stream)
+        if rc:
+            raise LSTMError(rc, "lstm_backward")
+        return dx, dh0, dc0, dws
 
     def device_status(self, stream=None):
         import torch

@@ -1,0 +1,268 @@
+// backward.hip -- gfx950 kernels of the LSTM backward pass (backpropagation
+// through time).
+//
+// The trace page "Complete Trace: nn.LSTM" ("cuDNN Backward") computes the
+// gradients of the input, of the initial states and of the weights from the
+// gradients of (output, h_n, c_n) and the activations the forward saved; the
+// pulsatrix "LSTMModule" reference walks the four gates and the cell carry
+// backwards through time and accumulates every weight and bias gradient over
+// all steps.  The derivatives are the chain rule of the cell equations on the
+// warp-nn "Long Short-Term Memory (LSTM)" page:
+//   h = o tanh(c),  c = f c_prev + i g
+//   dc   = dc_next + dh o (1 - tanh^2 c)
+//   dz_o = dh tanh(c) o (1 - o),  dz_i = dc g i (1 - i)
+//   dz_g = dc i (1 - g^2),        dz_f = dc c_prev f (1 - f)
+//   dc_prev = dc f,  dh_prev = W_hh^T dz,  dx = W_ih^T dz
+//   dW_ih += dz x^T,  dW_hh += dz h_prev^T,  db_ih = db_hh += dz
+//
+//   k_bwd_cell  one backward step, elementwise: dh, dc, dz for every cell
+//   k_bwd_mm    the recurrent product of that step, dz_t W_hh, as K-split
+//               partial sums on the matrix cores (summed by the next step)
+//   k_bwd_dh0   the last partial sums -> dh0
+//   k_transpose, k_hprev_t, k_rowsum, k_cast_*  operand preparation for the
+//               weight and input gradients, which are plain fp32 "NT" GEMMs
+//               on the projection kernels
+#include "device.h"
+#include "kernels.h"
+
+namespace lstm_amd {
+
+// One backward step for every (direction, batch row, unit).  sb counts the
+// backward steps: sb = 0 is the last step of each direction's scan.
+__global__ void k_bwd_cell(BwdCellArgs a) {
+    const size_t n = (size_t)a.D * a.B * a.H;
+    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int j = (int)(i % a.H);
+    const int b = (int)((i / a.H) % a.B);
+    const int d = (int)(i / ((size_t)a.H * a.B));
+    const int T = a.T, B = a.B, H = a.H, D = a.D;
+    const int sf = T - 1 - a.sb;                 // the forward scan's step
+    const int t = d == 0 ? sf : T - 1 - sf;      // its time index
+    const int tp = d == 0 ? t - 1 : t + 1;       // time of the scan's previous step
+    const size_t dbj = ((size_t)d * B + b) * H + j;
+
+    float dh = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j];
+    float dcn;
+    if (a.sb == 0) {
+        dh += a.dhn ? a.dhn[dbj] : 0.f;
+        dcn = a.dcn ? a.dcn[dbj] : 0.f;
+    } else {
+        float r = 0.f;  // h_t feeds the next step's products: their partial sums
+        for (int p = 0; p < a.NP; ++p) r += a.part[(size_t)p * n + dbj];
+        dh += r;
+        dcn = a.dc[dbj];
+    }
+    const float *ap = a.acts + (((size_t)t * B + b) * D + d) * 5 * H + j;
+    const float ig = ap[0], fg = ap[(size_t)H], gg = ap[(size_t)2 * H], og = ap[(size_t)3 * H];
+    const float c = ap[(size_t)4 * H];
+    const float cprev = sf == 0 ? (a.c0 ? a.c0[dbj] : 0.f)
+                                : a.acts[(((size_t)tp * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
+    const float tc = tanh_f(c);
+    const float dct = dcn + dh * og * (1.f - tc * tc);
+    float *dz = a.dz + (((size_t)t * B + b) * D + d) * 4 * H + j;
+    dz[0] = dct * gg * ig * (1.f - ig);
+    dz[(size_t)H] = dct * cprev * fg * (1.f - fg);
+    dz[(size_t)2 * H] = dct * ig * (1.f - gg * gg);
+    dz[(size_t)3 * H] = dh * tc * og * (1.f - og);
+    a.dc[dbj] = dct * fg;
+}
+
+// part[p][d][b][j] = sum over k in slice p of dz_t[b][d][k] * W_hh[d][k][j]
+// (K = 4H in the stacked gate order), with whT[d][j][k] = W_hh[d][k][j].
+// A workgroup: 32 batch rows x 32 units of one direction and one K slice;
+// wave (wm, wn) computes a 16 x 16 tile with 16x16x4 fp32 MFMAs whose
+// fragments are 16-byte loads of K-contiguous rows.
+__global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w & 1, wn = w >> 1;
+    const int B = a.B, H = a.H, D = a.D, K = 4 * H;
+    const int p = blockIdx.z % a.NP, d = blockIdx.z / a.NP;
+    const int b = blockIdx.x * 32 + wm * 16 + (lane & 15);  // A row of this lane
+    const int j = blockIdx.y * 32 + wn * 16 + (lane & 15);  // B row (unit) of this lane
+    const int k_lo = p * a.KS, k_hi = min(K, k_lo + a.KS);
+    const int sf = a.T - 1 - a.sb;
+    const int t = d == 0 ? sf : a.T - 1 - sf;
+    const float *arow = a.dz + (((size_t)t * B + (b < B ? b : 0)) * D + d) * (size_t)K;
+    const float *brow = a.whT + ((size_t)d * H + (j < H ? j : 0)) * (size_t)K;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int k0 = k_lo; k0 < k_hi; k0 += F32::KC) {
+        const int k = k0 + (lane >> 4) * F32::PER16;
+        // K % 4 == 0 and slices start at multiples of 16: a fragment is whole or absent
+        const u32x4 av = (b < B && k < k_hi) ? *reinterpret_cast<const u32x4 *>(arow + k) : zero;
+        const u32x4 bv = (j < H && k < k_hi) ? *reinterpret_cast<const u32x4 *>(brow + k) : zero;
+        acc = mma_chunk(F32{}, acc, av, bv);
+    }
+    const size_t n = (size_t)D * B * H;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = blockIdx.x * 32 + wm * 16 + 4 * (lane >> 4) + v;
+        const int u = blockIdx.y * 32 + wn * 16 + (lane & 15);
+        if (m < B && u < H) a.part[(size_t)p * n + ((size_t)d * B + m) * H + u] = acc[v];
+    }
+}
+
+// dh0 = the recurrent product of the scan's first step (sum of its partials)
+template <class DT>
+__global__ void k_bwd_dh0(const float *part, int NP, size_t n, typename DT::S *dh0) {
+    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float r = 0.f;
+    for (int p = 0; p < NP; ++p) r += part[(size_t)p * n + i];
+    dh0[i] = DT::from_f(r);
+}
+
+// out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (as fp32)
+template <class DT>
+__global__ void k_transpose(const typename DT::S *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out) {
+    __shared__ float tile[32][33];
+    const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+    for (int rr = threadIdx.y; rr < 32; rr += 8) {
+        const int r = r0 + rr, c = c0 + threadIdx.x;
+        tile[rr][threadIdx.x] = (r < rows && c < cols) ? DT::to_f(in[(size_t)r * ld_in + c]) : 0.f;
+    }
+    __syncthreads();
+    for (int cc = threadIdx.y; cc < 32; cc += 8) {
+        const int c = c0 + cc, r = r0 + threadIdx.x;
+        if (c < cols && r < rows) out[(size_t)c * ld_out + r] = tile[threadIdx.x][cc];
+    }
+}
+
+// out[k][m] = h_prev of direction d for row m = t*B + b (k < H, m < T*B):
+// the layer's output at the time of the scan's previous step, or h0 (NULL =
+// zeros) at the scan's first step.
+template <class DT>
+__global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, int T, int B, int H,
+                          int d, float *out) {
+    __shared__ float tile[32][33];
+    const int m0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+    const int M = T * B;
+    for (int mm = threadIdx.y; mm < 32; mm += 8) {
+        const int m = m0 + mm, k = k0 + threadIdx.x;
+        float v = 0.f;
+        if (m < M && k < H) {
+            const int t = m / B, b = m % B;
+            const int tp = d == 0 ? t - 1 : t + 1;
+            if (tp >= 0 && tp < T) v = DT::to_f(Y[((size_t)tp * B + b) * ldy + (size_t)d * H + k]);
+            else if (h0d) v = DT::to_f(h0d[(size_t)b * H + k]);
+        }
+        tile[mm][threadIdx.x] = v;
+    }
+    __syncthreads();
+    for (int kk = threadIdx.y; kk < 32; kk += 8) {
+        const int k = k0 + kk, m = m0 + threadIdx.x;
+        if (k < H && m < M) out[(size_t)k * M + m] = tile[threadIdx.x][kk];
+    }
+}
+
+// out[r] = sum over c of a[r * ld + c]: one workgroup per row, a fixed tree
+// (deterministic)
+__global__ void k_rowsum(const float *a, size_t ld, int cols, float *out) {
+    __shared__ float red[256];
+    const float *row = a + (size_t)blockIdx.x * ld;
+    float s = 0.f;
+    for (int c = threadIdx.x; c < cols; c += 256) s += row[c];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+}
+
+template <class DT>
+__global__ void k_cast_to(const float *in, typename DT::S *out, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        out[i] = DT::from_f(in[i]);
+}
+
+template <class DT>
+__global__ void k_cast_from(const typename DT::S *in, float *out, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        out[i] = DT::to_f(in[i]);
+}
+
+// ---------------------------------------------------------------- launchers
+static unsigned grid1(size_t n, unsigned cap = 8192) {
+    const size_t g = (n + 255) / 256;
+    return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s) {
+    const size_t n = (size_t)a.D * a.B * a.H;
+    hipLaunchKernelGGL(k_bwd_cell, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_mm(const BwdMmArgs &a, hipStream_t s) {
+    if ((4 * a.H) % 4 != 0 || a.KS % F32::KC != 0) return hipErrorInvalidValue;
+    dim3 grid((a.B + 31) / 32, (a.H + 31) / 32, a.NP * a.D);
+    hipLaunchKernelGGL(k_bwd_mm, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dh0(const float *part, int NP, size_t n, void *dh0, int dtype, hipStream_t s) {
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_bwd_dh0<BF16>, dim3(grid1(n, 1u << 30)), dim3(256), 0, s, part, NP, n,
+                           static_cast<uint16_t *>(dh0));
+    else
+        hipLaunchKernelGGL(k_bwd_dh0<F32>, dim3(grid1(n, 1u << 30)), dim3(256), 0, s, part, NP, n,
+                           static_cast<float *>(dh0));
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out, int dtype,
+                            hipStream_t s) {
+    dim3 grid((cols + 31) / 32, (rows + 31) / 32), block(32, 8);
+    if (grid.y > 65535u) return hipErrorInvalidValue;
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_transpose<BF16>, grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
+                           cols, out, ld_out);
+    else
+        hipLaunchKernelGGL(k_transpose<F32>, grid, block, 0, s, static_cast<const float *>(in), ld_in, rows, cols,
+                           out, ld_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, float *out,
+                          int dtype, hipStream_t s) {
+    dim3 grid(((size_t)T * B + 31) / 32, (H + 31) / 32), block(32, 8);
+    if (grid.y > 65535u) return hipErrorInvalidValue;
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_hprev_t<BF16>, grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
+                           static_cast<const uint16_t *>(h0d), T, B, H, d, out);
+    else
+        hipLaunchKernelGGL(k_hprev_t<F32>, grid, block, 0, s, static_cast<const float *>(Y), ldy,
+                           static_cast<const float *>(h0d), T, B, H, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowsum(const float *a, size_t ld, int rows, int cols, float *out, hipStream_t s) {
+    if (rows < 1) return hipSuccess;
+    hipLaunchKernelGGL(k_rowsum, dim3(rows), dim3(256), 0, s, a, ld, cols, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_cast_to<BF16>, dim3(grid1(n)), dim3(256), 0, s, in, static_cast<uint16_t *>(out), n);
+    else
+        hipLaunchKernelGGL(k_cast_to<F32>, dim3(grid1(n)), dim3(256), 0, s, in, static_cast<float *>(out), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_cast_from<BF16>, dim3(grid1(n)), dim3(256), 0, s, static_cast<const uint16_t *>(in),
+                           out, n);
+    else
+        hipLaunchKernelGGL(k_cast_from<F32>, dim3(grid1(n)), dim3(256), 0, s, static_cast<const float *>(in), out,
+                           n);
+    return hipGetLastError();
+}
+
+}  // namespace lstm_amd

@@ -35,6 +35,7 @@ struct RecArgs {
     float *hstate;           // [D, B, H] h carry between step launches (k_rec with lengths)
     const int *len;          // [B] valid steps per batch row, or NULL (all T)
     int bfirst;              // x, G, y rows are (b, t) = b*T + t instead of t*B + b
+    float *acts;             // training: [T, B, D, 5, H] gates i, f, g, o and c of every step, or NULL
     unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 32-bit words
     unsigned xpar;           // bit p: parity of the writes buffer p received before this launch
     unsigned *status;        // error word
@@ -132,6 +133,40 @@ hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hip
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, int *blocks_per_cu);
 // input chunks per wave of the tile's fused-projection variant (0: none)
 int rec_fused_chunks(RecTile t);
+// ----------------------------------------------------------------- backward
+// One backward step (sb = 0 is the last step of each direction's scan) of one
+// layer, all directions.
+struct BwdCellArgs {
+    const float *acts;  // [T, B, D, 5, H] saved by the training forward (i, f, g, o, c)
+    const float *c0;    // [D, B, H] of this layer, or NULL (zeros)
+    const float *dY;    // [T, B, D*H] gradient of this layer's output
+    const float *dhn;   // [D, B, H] gradient of h_n of this layer, or NULL
+    const float *dcn;   // [D, B, H] gradient of c_n of this layer, or NULL
+    const float *part;  // [NP, D, B, H] recurrent-product partial sums of the previous backward step
+    float *dz;          // [T, B, D, 4H] gradient of the pre-activations, written at this step's time
+    float *dc;          // [D, B, H] cell-state gradient carried backwards (read and written)
+    int T, B, H, D, NP, sb;
+};
+// part[p] = dz_t W_hh over K slice p (KS gate rows, a multiple of 16)
+struct BwdMmArgs {
+    const float *dz;    // [T, B, D, 4H]
+    const float *whT;   // [D, H, 4H] transposed W_hh, fp32
+    float *part;        // [NP, D, B, H]
+    int T, B, H, D, NP, KS, sb;
+};
+hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s);
+hipError_t launch_bwd_mm(const BwdMmArgs &a, hipStream_t s);
+hipError_t launch_bwd_dh0(const float *part, int NP, size_t n, void *dh0, int dtype, hipStream_t s);
+// out[c * ld_out + r] = in[r * ld_in + c] (rows x cols of dtype -> fp32)
+hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out, int dtype,
+                            hipStream_t s);
+// [H][T*B] fp32: h_prev of direction d for every (t, b), from the layer output Y or h0d ([B][H] or NULL)
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, float *out,
+                          int dtype, hipStream_t s);
+hipError_t launch_rowsum(const float *a, size_t ld, int rows, int cols, float *out, hipStream_t s);
+hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s);
+hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s);
+
 // Zero the y row of (t, b) for every t >= len[b] (padded steps of variable-length rows).
 hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first, hipStream_t s);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);

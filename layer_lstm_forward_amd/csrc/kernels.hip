@@ -797,6 +797,14 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                     cn = creg[i];
                     hv = hreg[i];
                 }
+                if (a.acts) {  // training: the activations the backward pass needs
+                    float *ap = a.acts + (((size_t)t * B + b0 + cm[i]) * D + d) * 5 * H + j0 + cu[i];
+                    ap[0] = ig;
+                    ap[(size_t)H] = fg;
+                    ap[(size_t)2 * H] = gg;
+                    ap[(size_t)3 * H] = og;
+                    ap[(size_t)4 * H] = cn;
+                }
                 creg[i] = cn;
                 hreg[i] = hv;
                 hs = DT::from_f(hv);
@@ -1373,6 +1381,14 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             hs = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
         }
         a.cstate[si] = cn;
+        if (a.acts) {  // training: the activations the backward pass needs
+            float *ap = a.acts + (((size_t)t * B + m) * D + d) * 5 * H + u;
+            ap[0] = ig;
+            ap[(size_t)H] = fg;
+            ap[(size_t)2 * H] = gg;
+            ap[(size_t)3 * H] = og;
+            ap[(size_t)4 * H] = cn;
+        }
         static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
         if (last) {
             if (a.hn) static_cast<S *>(a.hn)[si] = hs;

@@ -2,6 +2,7 @@
 // workspace carve-up, the per-layer schedule and the kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstdio>
@@ -112,6 +113,73 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     off += align_up(st);
     o->lens = off;    // per-row lengths, copied from the caller's host array
     off += align_up((size_t)B * sizeof(int));
+    o->total = off;
+    return true;
+}
+
+// Training reserve: per layer the activations [T][B][D][5][H] fp32 (gates i,
+// f, g, o and c of every step), then the outputs of the layers below the top
+// one ([T][B][D*H] dtype) that the backward pass reads again.
+struct ReserveLayout {
+    size_t acts_layer, y_layer, total;
+};
+
+bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
+    size_t tb, a, y;
+    if (T < 1 || B < 1 || !mul_ok((size_t)T, (size_t)B, &tb)) return false;
+    if (!mul_ok(tb, (size_t)p->D * 5 * p->H * sizeof(float), &a)) return false;
+    if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
+    r->acts_layer = align_up(a);
+    r->y_layer = align_up(y);
+    size_t ta, ty;
+    if (!mul_ok(r->acts_layer, (size_t)p->L, &ta) || !mul_ok(r->y_layer, (size_t)(p->L - 1), &ty)) return false;
+    if (ta > SIZE_MAX - ty) return false;
+    r->total = ta + ty;
+    return true;
+}
+
+// Backward workspace (all fp32): dz [T][B][D][4H]; one direction's dz^T
+// [4H][T*B]; the layer input x^T [in][T*B] and h_prev^T [H][T*B]; two output
+// gradient buffers [T*B][max(in, D*H)] (this layer's dY and the dX it
+// produces); the recurrent partial sums [NP][D][B][H]; the cell gradient
+// carry and dh_n [D][B][H]; transposed W_hh [D][H][4H] and W_ih [in][D*4H];
+// one weight gradient [4H][max(in, H)] and one bias gradient [4H].
+struct BwdLayout {
+    size_t dz, dzt, xt, ht, dy[2], part, dc, dhn, wht, wcat, dw, db, total;
+    int NP, KS;
+};
+
+bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
+    if (T < 1 || B < 1) return false;
+    const size_t G4 = (size_t)4 * p->H, H = p->H, D = p->D, f = sizeof(float);
+    const size_t win = std::max((size_t)p->I, D * H);
+    size_t tb;
+    if (!mul_ok((size_t)T, (size_t)B, &tb) || tb > (size_t)INT_MAX) return false;
+    const size_t base = (size_t)((B + 31) / 32) * ((p->H + 31) / 32) * D;
+    int np = (int)std::min<size_t>(std::max<size_t>((256 + base - 1) / base, 1), G4 / 16 > 0 ? G4 / 16 : 1);
+    int ks = (int)(((G4 + np - 1) / np + 15) / 16 * 16);
+    o->KS = ks;
+    o->NP = (int)((G4 + ks - 1) / ks);
+    size_t sz[13];
+    if (!mul_ok(tb, D * G4 * f, &sz[0]) || !mul_ok(tb, G4 * f, &sz[1]) || !mul_ok(tb, win * f, &sz[2]) ||
+        !mul_ok(tb, H * f, &sz[3]) || !mul_ok(tb, win * f, &sz[4]))
+        return false;
+    sz[5] = sz[4];
+    sz[6] = (size_t)o->NP * D * B * H * f;
+    sz[7] = D * B * H * f;
+    sz[8] = sz[7];
+    sz[9] = D * H * G4 * f;
+    sz[10] = win * D * G4 * f;
+    sz[11] = G4 * std::max(win, H) * f;
+    sz[12] = G4 * f;
+    size_t *dst[13] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->part, &o->dc, &o->dhn,
+                       &o->wht, &o->wcat, &o->dw, &o->db};
+    size_t off = 0;
+    for (int i = 0; i < 13; ++i) {
+        *dst[i] = off;
+        if (sz[i] > SIZE_MAX - off - 256) return false;
+        off += align_up(sz[i]);
+    }
     o->total = off;
     return true;
 }
@@ -383,7 +451,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 102; }
+int lstm_version(void) { return 103; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -588,10 +656,13 @@ namespace {
 // in 1..T, already validated.
 lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, const void *h0, const float *c0,
                          const void *const *weights, int T, int B, int layers, int bidir, void *y,
-                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream_) {
+                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream_,
+                         char *reserve = nullptr) {
     Layout lay;
     int rc = validate(p, x, h0, c0, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
     if (rc != LSTM_OK) return (lstm_status)rc;
+    ReserveLayout rl{};
+    if (reserve && !make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -645,7 +716,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     // one cooperative launch.  If the runtime refuses that launch, the
     // sequential path below redoes the work.
     PipeSched ps{};
-    if (!dlen && !p->batch_first && choose_pipe(p, B, dev, &ps)) {
+    if (!dlen && !p->batch_first && !reserve && choose_pipe(p, B, dev, &ps)) {
         const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
         const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
         const size_t slot_words = region_words * ps.NGB;
@@ -724,8 +795,13 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     unsigned xpar = 0;
     const unsigned layer_writes = (unsigned)((T / 2) & 1) | ((unsigned)(((T - 1) / 2) & 1) << 1);
     for (int l = 0; l < p->L; ++l) {
-        const void *X = l == 0 ? x : static_cast<const void *>(ws + lay.ymid[(l - 1) & 1]);
-        void *Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
+        // layer outputs below the top one: workspace ping-pong, or the
+        // training reserve (the backward pass reads them again)
+        auto mid = [&](int k) -> char * {
+            return reserve ? reserve + rl.acts_layer * p->L + rl.y_layer * k : ws + lay.ymid[k & 1];
+        };
+        const void *X = l == 0 ? x : static_cast<const void *>(mid(l - 1));
+        void *Y = l == p->L - 1 ? y : static_cast<void *>(mid(l));
         const int in_l = l == 0 ? p->I : p->D * p->H;
 
         const void *wih[2] = {nullptr, nullptr};
@@ -779,6 +855,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         ra.hstate = hstate;
         ra.len = dlen;
         ra.bfirst = p->batch_first;
+        ra.acts = reserve ? reinterpret_cast<float *>(reserve + rl.acts_layer * l) : nullptr;
         ra.xbuf = xbuf;
         ra.xpar = xpar;
         ra.status = status;
@@ -860,6 +937,195 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
                          void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
     return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                         workspace_bytes, stream);
+}
+
+lstm_status lstm_reserve_size(const lstm_plan *p, int T, int B, size_t *bytes) {
+    if (!p || !bytes) return LSTM_ERR_ARG;
+    ReserveLayout rl{};
+    if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
+    *bytes = rl.total;
+    return LSTM_OK;
+}
+
+lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                               const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                               void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (!p || !reserve) return LSTM_ERR_ARG;
+    if (p->batch_first) return LSTM_ERR_UNSUPPORTED;
+    ReserveLayout rl{};
+    if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
+    if (reserve_bytes < rl.total) return LSTM_ERR_WORKSPACE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    if (!is_device_ptr(reserve, dev)) return LSTM_ERR_DEVICE;
+    return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                        workspace_bytes, stream, static_cast<char *>(reserve));
+}
+
+lstm_status lstm_backward_workspace_size(const lstm_plan *p, int T, int B, size_t *bytes) {
+    if (!p || !bytes) return LSTM_ERR_ARG;
+    BwdLayout bl{};
+    if (!make_bwd_layout(p, T, B, &bl)) return LSTM_ERR_SHAPE;
+    *bytes = bl.total;
+    return LSTM_OK;
+}
+
+lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                          const void *const *weights, const void *y, const void *dy, const void *dh_n,
+                          const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
+                          int bidir, void *dx, void *dh0, float *dc0, void *const *dweights, void *workspace,
+                          size_t workspace_bytes, void *stream_) {
+    if (!p || !x || !weights || !y || !dy || !reserve || !dweights || !workspace) return LSTM_ERR_ARG;
+    if (layers != p->L || (bidir != 0) != (p->D == 2) || T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
+    if (p->batch_first) return LSTM_ERR_UNSUPPORTED;
+    const int per = p->has_bias ? 4 : 2;
+    for (int i = 0; i < p->L * p->D * per; ++i)
+        if (!weights[i] || !dweights[i]) return LSTM_ERR_ARG;
+    ReserveLayout rl{};
+    BwdLayout bl{};
+    if (!make_reserve(p, T, B, &rl) || !make_bwd_layout(p, T, B, &bl)) return LSTM_ERR_SHAPE;
+    if (reserve_bytes < rl.total || workspace_bytes < bl.total) return LSTM_ERR_WORKSPACE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    const void *ptrs[] = {x, h0, c0, y, dy, dh_n, dc_n, reserve, dx, dh0, dc0, workspace};
+    for (const void *q : ptrs)
+        if (q && !is_device_ptr(q, dev)) return LSTM_ERR_DEVICE;
+    for (int i = 0; i < p->L * p->D * per; ++i)
+        if (!is_device_ptr(weights[i], dev) || !is_device_ptr(dweights[i], dev)) return LSTM_ERR_DEVICE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream_);
+    char *ws = static_cast<char *>(workspace);
+    const char *res = static_cast<const char *>(reserve);
+    float *dz = reinterpret_cast<float *>(ws + bl.dz);
+    float *dzt = reinterpret_cast<float *>(ws + bl.dzt);
+    float *xt = reinterpret_cast<float *>(ws + bl.xt);
+    float *ht = reinterpret_cast<float *>(ws + bl.ht);
+    float *dyb[2] = {reinterpret_cast<float *>(ws + bl.dy[0]), reinterpret_cast<float *>(ws + bl.dy[1])};
+    float *part = reinterpret_cast<float *>(ws + bl.part);
+    float *dcb = reinterpret_cast<float *>(ws + bl.dc);
+    float *dhnb = reinterpret_cast<float *>(ws + bl.dhn);
+    float *wht = reinterpret_cast<float *>(ws + bl.wht);
+    float *wcat = reinterpret_cast<float *>(ws + bl.wcat);
+    float *dw = reinterpret_cast<float *>(ws + bl.dw);
+    float *db = reinterpret_cast<float *>(ws + bl.db);
+    const int dt = p->dtype, H = p->H, D = p->D, G4 = 4 * H;
+    const size_t es = elem_size(p->dtype), TB = (size_t)T * B, BH = (size_t)B * H, DBH = (size_t)D * BH;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    auto fail = []() {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    };
+    // the gradient of the top layer's output, as fp32
+    int cur = 0;
+    if (!ok(launch_cast_from(dy, dyb[cur], TB * D * H, dt, st))) return fail();
+    for (int l = p->L - 1; l >= 0; --l) {
+        const int in_l = l == 0 ? p->I : D * H;
+        const void *X = l == 0 ? x : static_cast<const void *>(res + rl.acts_layer * p->L + rl.y_layer * (l - 1));
+        const void *Y = l == p->L - 1 ? y : static_cast<const void *>(res + rl.acts_layer * p->L + rl.y_layer * l);
+        const float *acts = reinterpret_cast<const float *>(res + rl.acts_layer * l);
+        const float *c0l = c0 ? c0 + (size_t)l * DBH : nullptr;
+        const char *h0l = h0 ? static_cast<const char *>(h0) + (size_t)l * DBH * es : nullptr;
+        // W_hh^T per direction for the recurrent products
+        for (int d = 0; d < D; ++d)
+            if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per + 1], H, G4, H, wht + (size_t)d * H * G4,
+                                     G4, dt, st)))
+                return fail();
+        if (dh_n && !ok(launch_cast_from(static_cast<const char *>(dh_n) + (size_t)l * DBH * es, dhnb, DBH, dt, st)))
+            return fail();
+        // the recurrence, backwards: sb = 0 is each direction's last step
+        for (int sb = 0; sb < T; ++sb) {
+            BwdCellArgs ca{};
+            ca.acts = acts;
+            ca.c0 = c0l;
+            ca.dY = dyb[cur];
+            ca.dhn = dh_n ? dhnb : nullptr;
+            ca.dcn = dc_n ? dc_n + (size_t)l * DBH : nullptr;
+            ca.part = part;
+            ca.dz = dz;
+            ca.dc = dcb;
+            ca.T = T;
+            ca.B = B;
+            ca.H = H;
+            ca.D = D;
+            ca.NP = bl.NP;
+            ca.sb = sb;
+            if (!ok(launch_bwd_cell(ca, st))) return fail();
+            BwdMmArgs ma{};
+            ma.dz = dz;
+            ma.whT = wht;
+            ma.part = part;
+            ma.T = T;
+            ma.B = B;
+            ma.H = H;
+            ma.D = D;
+            ma.NP = bl.NP;
+            ma.KS = bl.KS;
+            ma.sb = sb;
+            if (!ok(launch_bwd_mm(ma, st))) return fail();
+        }
+        if (dh0 && !ok(launch_bwd_dh0(part, bl.NP, DBH, static_cast<char *>(dh0) + (size_t)l * DBH * es, dt, st)))
+            return fail();
+        if (dc0 && hipMemcpyAsync(dc0 + (size_t)l * DBH, dcb, DBH * sizeof(float), hipMemcpyDeviceToDevice, st) !=
+                       hipSuccess)
+            return fail();
+        // weight gradients: dW_ih = dz^T x, dW_hh = dz^T h_prev, db = sum of dz
+        if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, st))) return fail();
+        for (int d = 0; d < D; ++d) {
+            void *const *dwd = dweights + (size_t)(l * D + d) * per;
+            if (!ok(launch_transpose(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, dzt, TB, DT_F32, st)) ||
+                !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, T, B, H, d, ht, dt,
+                                   st)))
+                return fail();
+            ProjArgs ga{};
+            ga.X = dzt;
+            ga.W[0] = xt;
+            ga.G = dw;
+            ga.M = G4;
+            ga.N = in_l;
+            ga.K = (int)TB;
+            ga.ldx = (int)TB;
+            ga.D = 1;
+            if (!ok(launch_proj(ga, DT_F32, 0, st)) || !ok(launch_cast_to(dw, dwd[0], (size_t)G4 * in_l, dt, st)))
+                return fail();
+            ga.W[0] = ht;
+            ga.N = H;
+            if (!ok(launch_proj(ga, DT_F32, 0, st)) || !ok(launch_cast_to(dw, dwd[1], (size_t)G4 * H, dt, st)))
+                return fail();
+            if (p->has_bias) {
+                if (!ok(launch_rowsum(dzt, TB, G4, (int)TB, db, st)) || !ok(launch_cast_to(db, dwd[2], G4, dt, st)) ||
+                    !ok(launch_cast_to(db, dwd[3], G4, dt, st)))
+                    return fail();
+            }
+        }
+        // input gradient dX = sum over directions of dz W_ih, the next dY
+        if (l > 0 || dx) {
+            for (int d = 0; d < D; ++d)
+                if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per], in_l, G4, in_l, wcat + (size_t)d * G4,
+                                         (size_t)D * G4, dt, st)))
+                    return fail();
+            ProjArgs xa{};
+            xa.X = dz;
+            xa.W[0] = wcat;
+            xa.G = dyb[cur ^ 1];
+            xa.M = (int)TB;
+            xa.N = in_l;
+            xa.K = D * G4;
+            xa.ldx = D * G4;
+            xa.D = 1;
+            if (!ok(launch_proj(xa, DT_F32, 0, st))) return fail();
+            if (l == 0 && !ok(launch_cast_to(dyb[cur ^ 1], dx, TB * p->I, dt, st))) return fail();
+        }
+        cur ^= 1;
+    }
+    return LSTM_OK;
 }
 
 lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths, const void *h0,
