@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--lengths", choices=["none", "mix", "ragged"], default="none",
                     help="variable-length rows (lstm_forward_lengths); the value then counts valid cells only")
     ap.add_argument("--batch-first", action="store_true", help="x [B, T, I] and y [B, T, D*H]")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step instead: lstm_forward_train + lstm_backward")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -274,6 +276,8 @@ def main():
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=x.dtype, device=dev),
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream(dev)
+    if args.train:
+        return train_bench(args, spec, m, x, w, h0, c0, stream, desc)
 
     for _ in range(args.warmup):
         m.forward(x, w, h0, c0, out=out, lengths=lengths)
@@ -348,6 +352,45 @@ def main():
                                                        "valid_steps": int(np.sum(lengths))}),
                        **({"layout": "batch_first"} if args.batch_first else {})},
             "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
+    """A training step = lstm_forward_train + lstm_backward on the workload
+    (synthetic output gradients); the value counts timestep-cells per second
+    of the whole step.  The forward alone is timed beside it."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(spec.seed + 11)
+    dy = torch.from_numpy(rng.standard_normal((spec.T, spec.B, spec.D * spec.hidden_size)).astype(np.float32))
+    dy = dy.to(x.device).to(x.dtype)
+
+    def step():
+        y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
+        return m.backward(x, w, y, reserve, dy, h0=h0, c0=c0)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1, ev2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    ev0.record(stream)
+    for _ in range(args.steps):
+        m.forward_train(x, w, h0, c0)
+    ev1.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev2.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev1.elapsed_time(ev2) / args.steps
+    value = spec.cells / (ms / 1e3)
+    log(f"training step: {ms:.3f} ms (forward_train {fwd_ms:.3f} ms, backward {ms - fwd_ms:.3f} ms), "
+        f"{value / 1e9:.3f} G cells/s")
+    line = {"metric": "LSTM training step (forward_train + backward) timestep-cells/sec", "value": value,
+            "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+            "data": "synthetic (seeded; random-init weights and output gradients)",
+            "config": {"workload": args.workload, "T": spec.T, "B": spec.B, "forward_train_ms": fwd_ms,
+                       "backward_ms": ms - fwd_ms, "schedule": desc}}
     print(json.dumps(line), flush=True)
 
 

@@ -83,16 +83,33 @@ __global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
     const int k_lo = p * a.KS, k_hi = min(K, k_lo + a.KS);
     const int sf = a.T - 1 - a.sb;
     const int t = d == 0 ? sf : a.T - 1 - sf;
-    const float *arow = a.dz + (((size_t)t * B + (b < B ? b : 0)) * D + d) * (size_t)K;
-    const float *brow = a.whT + ((size_t)d * H + (j < H ? j : 0)) * (size_t)K;
+    // A: dz rows (t, b, d) for b < B; B: whT rows (d, j) for j < H.  Both via
+    // buffer resources: a row past B or H, or a chunk past the slice, gets an
+    // out-of-range offset and reads zeros without a memory access.
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.dz + ((size_t)t * B * D + d) * (size_t)K), (short)0,
+        (int)(((size_t)(B - 1) * D * K + K) * sizeof(float)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.whT + (size_t)d * H * K), (short)0, (int)((size_t)H * K * sizeof(float)), 0x00020000);
+    const unsigned aoff = (unsigned)((size_t)b * D * K * sizeof(float));
+    const unsigned boff = (unsigned)((size_t)j * K * sizeof(float));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int k0 = k_lo; k0 < k_hi; k0 += F32::KC) {
-        const int k = k0 + (lane >> 4) * F32::PER16;
-        // K % 4 == 0 and slices start at multiples of 16: a fragment is whole or absent
-        const u32x4 av = (b < B && k < k_hi) ? *reinterpret_cast<const u32x4 *>(arow + k) : zero;
-        const u32x4 bv = (j < H && k < k_hi) ? *reinterpret_cast<const u32x4 *>(brow + k) : zero;
-        acc = mma_chunk(F32{}, acc, av, bv);
+    // Batches of 8 chunks: all 16 fragment loads are issued before the first
+    // product, so a batch costs about one memory round trip (K % 4 == 0 and
+    // slices start at multiples of 16: a fragment is whole or absent).
+    constexpr int NBAT = 8;
+    constexpr unsigned OOR = 0x7FFFFFF0u;
+    for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * F32::KC) {
+        u32x4 av[NBAT], bv[NBAT];
+#pragma unroll
+        for (int c = 0; c < NBAT; ++c) {
+            const int k = k0 + c * F32::KC + (lane >> 4) * F32::PER16;
+            const bool kin = k < k_hi;
+            av[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + 4u * k : OOR), 0, 0);
+            bv[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + 4u * k : OOR), 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < NBAT; ++c) acc = mma_chunk(F32{}, acc, av[c], bv[c]);
     }
     const size_t n = (size_t)D * B * H;
 #pragma unroll
