@@ -201,6 +201,17 @@ __global__ void k_cast_from(const typename DT::S *in, float *out, size_t n) {
         out[i] = DT::to_f(in[i]);
 }
 
+// Sum of K-split slabs in a fixed order (deterministic), rounded once to the
+// output dtype.
+template <class DT>
+__global__ void k_ksum(const float *part, int ns, size_t slab, size_t n, typename DT::S *out) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        float v = part[i];
+        for (int sp = 1; sp < ns; ++sp) v += part[(size_t)sp * slab + i];
+        out[i] = DT::from_f(v);
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 static unsigned grid1(size_t n, unsigned cap = 8192) {
     const size_t g = (n + 255) / 256;
@@ -268,6 +279,17 @@ hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipSt
         hipLaunchKernelGGL(k_cast_to<BF16>, dim3(grid1(n)), dim3(256), 0, s, in, static_cast<uint16_t *>(out), n);
     else
         hipLaunchKernelGGL(k_cast_to<F32>, dim3(grid1(n)), dim3(256), 0, s, in, static_cast<float *>(out), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_ksum(const float *part, int ns, size_t slab, size_t n, void *out, int dtype, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (ns < 1 || (ns > 1 && slab < n)) return hipErrorInvalidValue;
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_ksum<BF16>, dim3(grid1(n)), dim3(256), 0, s, part, ns, slab, n,
+                           static_cast<uint16_t *>(out));
+    else
+        hipLaunchKernelGGL(k_ksum<F32>, dim3(grid1(n)), dim3(256), 0, s, part, ns, slab, n, static_cast<float *>(out));
     return hipGetLastError();
 }
 

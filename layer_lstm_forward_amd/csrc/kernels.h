@@ -13,6 +13,9 @@ enum DType { DT_F32 = 0, DT_BF16 = 1 };
 //   X   [M, K] with row stride ldx (elements), dtype
 //   W_d [N, K] row-major, dtype; N = 4H; d = 0..D-1 (blockIdx.z)
 //   G   [M, D*N] float32
+//   kchunk > 0 splits K: blockIdx.z = d * nsplit + s, split s sums K range
+//   [s*kchunk, min(K, (s+1)*kchunk)) into its own slab G + s*M*D*N (no bias);
+//   kchunk is a multiple of 64.  W rows keep the stride K.
 struct ProjArgs {
     const void *X;
     const void *W[2];
@@ -20,6 +23,7 @@ struct ProjArgs {
     const void *b_hh[2];
     float *G;
     int M, N, K, ldx, D;
+    int kchunk;
 };
 
 // One layer of the recurrence for all directions and batch rows.
@@ -120,6 +124,11 @@ bool rec_tile_supported(RecTile t);
 
 // variant: 0 automatic, 1 128x128 tiles, 2 256x256 tiles, 3 256x256 tiles with direct-to-LDS loads
 hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s);
+// K-split depth for an fp32 M x N x K product with few output tiles: a chunk
+// (multiple of 64) that gives about one 256x256 tile per CU, or 0 (no split).
+int proj_kchunk(int M, int N, int K);
+// out[i] = sum over s < ns of part[s * slab + i], in the order s = 0, 1, ...; out is dtype
+hipError_t launch_ksum(const float *part, int ns, size_t slab, size_t n, void *out, int dtype, hipStream_t s);
 // Name of the projection kernel launch_proj picks for an M x N x K product
 // over D directions, given 16-byte aligned operands.
 const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant);

@@ -27,6 +27,17 @@
 
 namespace lstm_amd {
 
+// Split of one projection workgroup: direction, K range and output slab.
+struct ProjSplit {
+    int d, kb, kc;  // direction, first K index, K length of this split
+    size_t goff;    // float offset of this split's output slab
+};
+__device__ inline ProjSplit proj_split(const ProjArgs &a) {
+    if (a.kchunk <= 0) return ProjSplit{(int)blockIdx.z, 0, a.K, 0};
+    const int ns = (a.K + a.kchunk - 1) / a.kchunk, z = blockIdx.z, sp = z % ns;
+    return ProjSplit{z / ns, sp * a.kchunk, min(a.K - sp * a.kchunk, a.kchunk), (size_t)sp * a.M * a.D * a.N};
+}
+
 // ===========================================================================
 // Projection GEMM.  128x128 output tile per 256-thread workgroup; each of the
 // four waves owns a 64x64 quadrant as 4x4 MFMA tiles of 16x16.  A stage holds
@@ -44,11 +55,13 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
-    const int d = blockIdx.z;
+    const ProjSplit sp = proj_split(a);
+    const int d = sp.d;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int M = a.M, N = a.N, K = a.K;
-    const S *X = static_cast<const S *>(a.X);
-    const S *W = static_cast<const S *>(a.W[d]);
+    const int M = a.M, N = a.N, K = sp.kc, ldw = a.K;
+    const S *X = static_cast<const S *>(a.X) + sp.kb;
+    const S *W = static_cast<const S *>(a.W[d]) + sp.kb;
+    float *const Gs = a.G + sp.goff;
 
     u32x4 ra[4], rb[4];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -58,7 +71,7 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
             const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
             const int k = k0 + sg * DT::PER16;
             ra[i] = (m0 + row < M) ? load_frag<DT>(X + (size_t)(m0 + row) * a.ldx, k, K, VEC) : zero;
-            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * K, k, K, VEC) : zero;
+            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * ldw, k, K, VEC) : zero;
         }
     };
     auto sstore = [&](int buf) {
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + v;
-                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias[j];
+                if (m < M && n < N) Gs[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias[j];
             }
         }
 }
@@ -171,13 +184,15 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
-    const int d = blockIdx.z;
-    const int M = a.M, N = a.N, K = a.K;
+    const ProjSplit sp = proj_split(a);
+    const int d = sp.d;
+    const int M = a.M, N = a.N, K = sp.kc, ldw = a.K;
     int tm, tn;
     gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const S *X = static_cast<const S *>(a.X);
-    const S *W = static_cast<const S *>(a.W[d]);
+    const S *X = static_cast<const S *>(a.X) + sp.kb;
+    const S *W = static_cast<const S *>(a.W[d]) + sp.kb;
+    float *const Gs = a.G + sp.goff;
 
     u32x4 ra[8], rb[8];
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
             const int seg = tid + 256 * i, row = seg >> 3, sg = seg & 7;
             const int k = k0 + sg * DT::PER16;
             ra[i] = (m0 + row < M) ? load_frag<DT>(X + (size_t)(m0 + row) * a.ldx, k, K, VEC) : zero;
-            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * K, k, K, VEC) : zero;
+            rb[i] = (n0 + row < N) ? load_frag<DT>(W + (size_t)(n0 + row) * ldw, k, K, VEC) : zero;
         }
     };
     auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
@@ -246,7 +261,7 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+                if (m < M && n < N) Gs[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
             }
     }
 }
@@ -277,16 +292,19 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
-    const int d = blockIdx.z;
-    const int M = a.M, N = a.N, K = a.K;
+    const ProjSplit sp = proj_split(a);
+    const int d = sp.d;
+    const int M = a.M, N = a.N, K = sp.kc, ldw = a.K;
     int tm, tn;
     gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int es = (int)sizeof(S);
-    const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx;
-    const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * K;
-    const unsigned xbytes = (unsigned)((size_t)min(BM, M - m0) * a.ldx * es);
-    const unsigned wbytes = (unsigned)((size_t)min(BN, N - n0) * K * es);
+    const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx + sp.kb;
+    const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * ldw + sp.kb;
+    float *const Gs = a.G + sp.goff;
+    // bytes from this split's first element to the end of its last row's K range
+    const unsigned xbytes = (unsigned)(((size_t)(min(BM, M - m0) - 1) * a.ldx + K) * es);
+    const unsigned wbytes = (unsigned)(((size_t)(min(BN, N - n0) - 1) * ldw + K) * es);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(X), (short)0, (int)xbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
 
@@ -301,7 +319,7 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
             const int lseg = pseg ^ ((row >> 1) & 7);
             const int k = kt * KS + lseg * DT::PER16;
             const unsigned ox = k < K ? (unsigned)(((size_t)row * a.ldx + k) * es) : OOR;
-            const unsigned ow = k < K ? (unsigned)(((size_t)row * K + k) * es) : OOR;
+            const unsigned ow = k < K ? (unsigned)(((size_t)row * ldw + k) * es) : OOR;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(sa + blk * 64), 16, ox, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(sb + blk * 64), 16, ow, 0, 0, 0);
         }
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M && n < N) a.G[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+                if (m < M && n < N) Gs[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
             }
     }
 }
@@ -1417,24 +1435,27 @@ __global__ void k_fill(unsigned *p, size_t n, unsigned v) {
 // ===========================================================================
 // Host-side launch helpers.
 // ===========================================================================
+static int proj_nsplit(const ProjArgs &a) { return a.kchunk > 0 ? (a.K + a.kchunk - 1) / a.kchunk : 1; }
+
 template <class DT, bool VEC>
 static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, hipStream_t s) {
+    const int zd = a.D * proj_nsplit(a);
     if (big && dma && VEC) {
         const void *fn = reinterpret_cast<const void *>(&k_proj_dma<DT>);
         const size_t smem = 2 * (256 + 256) * 8 * 16;
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
-        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D);
+        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, zd);
         hipLaunchKernelGGL((k_proj_dma<DT>), grid, dim3(256), smem, s, a);
     } else if (big) {
         const void *fn = reinterpret_cast<const void *>(&k_proj_big<DT, VEC>);
         const size_t smem = 2 * (256 + 256) * 8 * 16;
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
-        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D);
+        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, zd);
         hipLaunchKernelGGL((k_proj_big<DT, VEC>), grid, dim3(256), smem, s, a);
     } else {
-        dim3 grid((a.N + 127) / 128, (a.M + 127) / 128, a.D);
+        dim3 grid((a.N + 127) / 128, (a.M + 127) / 128, zd);
         hipLaunchKernelGGL((k_proj<DT, VEC>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
@@ -1451,6 +1472,16 @@ static void proj_choose(int M, int N, int K, int ldx, int D, int dtype, int vari
     *dma = *big && vec && variant != 2 && (size_t)256 * ldx * es < (1u << 31) && (size_t)256 * K * es < (1u << 31);
 }
 
+int proj_kchunk(int M, int N, int K) {
+    const long long tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles >= 128 || K < 512) return 0;
+    long long ns = 256 / tiles;
+    if (ns > K / 256) ns = K / 256;
+    if (ns < 2) return 0;
+    const int kc = (int)(((K + ns - 1) / ns + 63) / 64 * 64);
+    return kc < K ? kc : 0;
+}
+
 const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant) {
     const int per16 = dtype == DT_BF16 ? 8 : 4;
     bool big, dma;
@@ -1462,8 +1493,10 @@ hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s)
     const int per16 = dtype == DT_BF16 ? 8 : 4;
     bool vec = (a.K % per16 == 0) && (a.ldx % per16 == 0) && ((uintptr_t)a.X % 16 == 0);
     for (int d = 0; d < a.D; ++d) vec = vec && ((uintptr_t)a.W[d] % 16 == 0);
+    if (a.kchunk < 0 || a.kchunk % 64 != 0 || (a.kchunk > 0 && (a.b_ih[0] || a.b_ih[1])))
+        return hipErrorInvalidValue;
     bool big, dma;
-    proj_choose(a.M, a.N, a.K, a.ldx, a.D, dtype, variant, vec, &big, &dma);
+    proj_choose(a.M, a.N, a.K, a.ldx, a.D * proj_nsplit(a), dtype, variant, vec, &big, &dma);
     if (dtype == DT_BF16)
         return vec ? launch_proj_t<BF16, true>(a, big, dma, s) : launch_proj_t<BF16, false>(a, big, dma, s);
     return vec ? launch_proj_t<F32, true>(a, big, dma, s) : launch_proj_t<F32, false>(a, big, dma, s);

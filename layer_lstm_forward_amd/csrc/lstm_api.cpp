@@ -145,9 +145,15 @@ bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
 // carry and dh_n [D][B][H]; transposed W_hh [D][H][4H] and W_ih [in][D*4H];
 // one weight gradient [4H][max(in, H)] and one bias gradient [4H].
 struct BwdLayout {
-    size_t dz, dzt, xt, ht, dy[2], part, dc, dhn, wht, wcat, dw, db, total;
+    size_t dz, dzt, xt, ht, dy[2], part, dc, dhn, wht, wcat, ksp, db, total;
     int NP, KS;
 };
+
+// K-split count of an fp32 M x N x K product (1: not split)
+int ksplit_count(int M, int N, int K) {
+    const int kc = proj_kchunk(M, N, K);
+    return kc ? (K + kc - 1) / kc : 1;
+}
 
 bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     if (T < 1 || B < 1) return false;
@@ -170,10 +176,21 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     sz[8] = sz[7];
     sz[9] = D * H * G4 * f;
     sz[10] = win * D * G4 * f;
-    sz[11] = G4 * std::max(win, H) * f;
+    // K-split slabs (or the unsplit fp32 product) of the weight-gradient
+    // products, and the slabs of a split input-gradient product
+    size_t ksp = 0;
+    for (int l = 0; l < p->L; ++l) {
+        const int in_l = l == 0 ? p->I : (int)(D * H);
+        const size_t kw = std::max((size_t)ksplit_count((int)G4, in_l, (int)tb) * in_l,
+                                   (size_t)ksplit_count((int)G4, (int)H, (int)tb) * H) * G4;
+        ksp = std::max(ksp, kw);
+        const int nx = ksplit_count((int)tb, in_l, (int)(D * G4));
+        if (nx > 1) ksp = std::max(ksp, (size_t)nx * tb * in_l);
+    }
+    if (!mul_ok(ksp, f, &sz[11])) return false;
     sz[12] = G4 * f;
     size_t *dst[13] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->part, &o->dc, &o->dhn,
-                       &o->wht, &o->wcat, &o->dw, &o->db};
+                       &o->wht, &o->wcat, &o->ksp, &o->db};
     size_t off = 0;
     for (int i = 0; i < 13; ++i) {
         *dst[i] = off;
@@ -1014,7 +1031,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     float *dhnb = reinterpret_cast<float *>(ws + bl.dhn);
     float *wht = reinterpret_cast<float *>(ws + bl.wht);
     float *wcat = reinterpret_cast<float *>(ws + bl.wcat);
-    float *dw = reinterpret_cast<float *>(ws + bl.dw);
+    float *ksp = reinterpret_cast<float *>(ws + bl.ksp);
     float *db = reinterpret_cast<float *>(ws + bl.db);
     const int dt = p->dtype, H = p->H, D = p->D, G4 = 4 * H;
     const size_t es = elem_size(p->dtype), TB = (size_t)T * B, BH = (size_t)B * H, DBH = (size_t)D * BH;
@@ -1022,6 +1039,33 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     auto fail = []() {
         (void)hipGetLastError();
         return LSTM_ERR_LAUNCH;
+    };
+    // out[M][N] = A[M][K] Bm[N][K]^T in fp32, rounded once to out_dt; split
+    // over K (slabs in ksp, summed in order) when the product has few output
+    // tiles, else computed into f32 (out itself when out_dt is fp32)
+    auto gemm_nt = [&](const float *A, int lda, const float *Bm, int M, int N, int K, void *out, int out_dt,
+                       float *f32) {
+        ProjArgs g{};
+        g.X = A;
+        g.W[0] = Bm;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.ldx = lda;
+        g.D = 1;
+        g.kchunk = proj_kchunk(M, N, K);
+        const size_t mn = (size_t)M * N;
+        if (g.kchunk) {
+            g.G = ksp;
+            return ok(launch_proj(g, DT_F32, 0, st)) &&
+                   ok(launch_ksum(ksp, (K + g.kchunk - 1) / g.kchunk, mn, mn, out, out_dt, st));
+        }
+        if (out_dt == DT_F32) {
+            g.G = static_cast<float *>(out);
+            return ok(launch_proj(g, DT_F32, 0, st));
+        }
+        g.G = f32;
+        return ok(launch_proj(g, DT_F32, 0, st)) && ok(launch_cast_to(f32, out, mn, out_dt, st));
     };
     // the gradient of the top layer's output, as fp32
     int cur = 0;
@@ -1084,20 +1128,8 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
                 !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, T, B, H, d, ht, dt,
                                    st)))
                 return fail();
-            ProjArgs ga{};
-            ga.X = dzt;
-            ga.W[0] = xt;
-            ga.G = dw;
-            ga.M = G4;
-            ga.N = in_l;
-            ga.K = (int)TB;
-            ga.ldx = (int)TB;
-            ga.D = 1;
-            if (!ok(launch_proj(ga, DT_F32, 0, st)) || !ok(launch_cast_to(dw, dwd[0], (size_t)G4 * in_l, dt, st)))
-                return fail();
-            ga.W[0] = ht;
-            ga.N = H;
-            if (!ok(launch_proj(ga, DT_F32, 0, st)) || !ok(launch_cast_to(dw, dwd[1], (size_t)G4 * H, dt, st)))
+            if (!gemm_nt(dzt, (int)TB, xt, G4, in_l, (int)TB, dwd[0], dt, ksp) ||
+                !gemm_nt(dzt, (int)TB, ht, G4, H, (int)TB, dwd[1], dt, ksp))
                 return fail();
             if (p->has_bias) {
                 if (!ok(launch_rowsum(dzt, TB, G4, (int)TB, db, st)) || !ok(launch_cast_to(db, dwd[2], G4, dt, st)) ||
@@ -1111,17 +1143,10 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
                 if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per], in_l, G4, in_l, wcat + (size_t)d * G4,
                                          (size_t)D * G4, dt, st)))
                     return fail();
-            ProjArgs xa{};
-            xa.X = dz;
-            xa.W[0] = wcat;
-            xa.G = dyb[cur ^ 1];
-            xa.M = (int)TB;
-            xa.N = in_l;
-            xa.K = D * G4;
-            xa.ldx = D * G4;
-            xa.D = 1;
-            if (!ok(launch_proj(xa, DT_F32, 0, st))) return fail();
-            if (l == 0 && !ok(launch_cast_to(dyb[cur ^ 1], dx, TB * p->I, dt, st))) return fail();
+            const bool out_dx = l == 0;
+            if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
+                         dyb[cur ^ 1]))
+                return fail();
         }
         cur ^= 1;
     }

@@ -23,6 +23,11 @@ SPECS = [
     Spec(16, 40, 2, True, 4, 3, "f32", 804, "normal0.1", has_bias=False),
     Spec(64, 96, 2, True, 6, 20, "bf16", 805, "normal0.1"),
     Spec(32, 64, 1, False, 9, 40, "bf16", 806, "zeros"),
+    # weight- and input-gradient products split over K (T*B or D*4H) into slabs:
+    Spec(96, 128, 2, False, 64, 16, "f32", 807, "normal0.1"),   # 128x128 tiles, 4 splits
+    Spec(20, 24, 1, True, 35, 20, "f32", 808, "normal0.1"),     # a ragged last split (384 + 316)
+    Spec(64, 128, 2, True, 48, 24, "bf16", 810, "normal0.1"),   # bf16 weights, 320-deep splits
+    Spec(32, 64, 1, False, 256, 256, "f32", 809, "normal0.1"),  # 256x256 direct-to-LDS tiles, 256 splits
 ]
 
 
