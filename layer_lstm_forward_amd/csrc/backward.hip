@@ -48,8 +48,20 @@ __global__ void k_bwd_cell(BwdCellArgs a) {
         dh += a.dhn ? a.dhn[dbj] : 0.f;
         dcn = a.dcn ? a.dcn[dbj] : 0.f;
     } else {
-        float r = 0.f;  // h_t feeds the next step's products: their partial sums
-        for (int p = 0; p < a.NP; ++p) r += a.part[(size_t)p * n + dbj];
+        // h_t feeds the next step's products: their partial sums, in slice
+        // order, four loads in flight
+        const float *pp = a.part + dbj;
+        float r = 0.f;
+        int p = 0;
+        for (; p + 4 <= a.NP; p += 4) {
+            const float v0 = pp[(size_t)p * n], v1 = pp[(size_t)(p + 1) * n];
+            const float v2 = pp[(size_t)(p + 2) * n], v3 = pp[(size_t)(p + 3) * n];
+            r += v0;
+            r += v1;
+            r += v2;
+            r += v3;
+        }
+        for (; p < a.NP; ++p) r += pp[(size_t)p * n];
         dh += r;
         dcn = a.dc[dbj];
     }
@@ -94,10 +106,12 @@ __global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
     const unsigned aoff = (unsigned)((size_t)b * D * K * sizeof(float));
     const unsigned boff = (unsigned)((size_t)j * K * sizeof(float));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Batches of 8 chunks: all 16 fragment loads are issued before the first
-    // product, so a batch costs about one memory round trip (K % 4 == 0 and
-    // slices start at multiples of 16: a fragment is whole or absent).
-    constexpr int NBAT = 8;
+    // Batches of 16 chunks (a 256-deep slice is one batch): all 32 fragment
+    // loads are issued before the first product of the batch, and a
+    // scheduling barrier keeps the compiler from interleaving them with the
+    // products into a chain of round trips (K % 4 == 0 and slices start at
+    // multiples of 16: a fragment is whole or absent).
+    constexpr int NBAT = 16;
     constexpr unsigned OOR = 0x7FFFFFF0u;
     for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * F32::KC) {
         u32x4 av[NBAT], bv[NBAT];
@@ -108,8 +122,10 @@ __global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
             av[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + 4u * k : OOR), 0, 0);
             bv[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + 4u * k : OOR), 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < NBAT; ++c) acc = mma_chunk(F32{}, acc, av[c], bv[c]);
+        __builtin_amdgcn_sched_barrier(0);
     }
     const size_t n = (size_t)D * B * H;
 #pragma unroll

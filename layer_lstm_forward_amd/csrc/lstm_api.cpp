@@ -161,8 +161,11 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     const size_t win = std::max((size_t)p->I, D * H);
     size_t tb;
     if (!mul_ok((size_t)T, (size_t)B, &tb) || tb > (size_t)INT_MAX) return false;
+    // K slices of the recurrent product: 256 gate rows (one load batch of
+    // the product kernel) while that keeps the grid within about 1024
+    // workgroups, deeper slices beyond
     const size_t base = (size_t)((B + 31) / 32) * ((p->H + 31) / 32) * D;
-    int np = (int)std::min<size_t>(std::max<size_t>((256 + base - 1) / base, 1), G4 / 16 > 0 ? G4 / 16 : 1);
+    int np = (int)std::min<size_t>((G4 + 255) / 256, std::max<size_t>((1024 + base - 1) / base, 1));
     int ks = (int)(((G4 + np - 1) / np + 15) / 16 * 16);
     o->KS = ks;
     o->NP = (int)((G4 + ks - 1) / ks);
