@@ -126,7 +126,7 @@ def kernel_source_hash():
     the sources it was taken from."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "device.h", "kernels.h"):
+    for f in ("kernels.hip", "backward.hip", "device.h", "kernels.h"):
         with open(os.path.join(ROOT, "layer_lstm_forward_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -153,14 +153,24 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, wo
     cw, _, _ = per_dispatch(copy_write_csv, "copyBuffer")
     copy_kib = 256 * 1024  # the calibration copy reads and writes 256 MiB
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
-    kf, nf, name = per_dispatch(fetch_csv, kernel)
-    kw, nw, _ = per_dispatch(write_csv, kernel)
+    # "a+b": one launch is a dispatch of each kernel named; their per-dispatch figures add
+    kf = kw = 0.0
+    nf, nw, names = [], [], []
+    for k in kernel.split("+"):
+        f_, n_, name = per_dispatch(fetch_csv, k)
+        w_, m_, _ = per_dispatch(write_csv, k)
+        kf, kw = kf + f_, kw + w_
+        nf.append(str(n_))
+        nw.append(str(m_))
+        names.append(name[:120])
+    name = " + ".join(names)
+    nf, nw = "+".join(nf), "+".join(nw)
     fetch_b = kf * 1024 * f_scale
     write_b = kw * 1024 * w_scale
     lines = ["# rocprofv3 HBM counters, one dispatch = one launch",
              f"# command: {command}",
              f"# workload: {workload}",
-             f"# kernel: {name[:120]}",
+             f"# kernel: {name}",
              f"kernel_source_sha256: {kernel_source_hash()}",
              f"copy_calibration: FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for a 262144 KiB copy "
              f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
@@ -361,6 +371,7 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     of the whole step.  The forward alone is timed beside it."""
     import numpy as np
     import torch
+    import layer_lstm_forward_amd as pkg
     rng = np.random.default_rng(spec.seed + 11)
     dy = torch.from_numpy(rng.standard_normal((spec.T, spec.B, spec.D * spec.hidden_size)).astype(np.float32))
     dy = dy.to(x.device).to(x.dtype)
@@ -385,13 +396,76 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     value = spec.cells / (ms / 1e3)
     log(f"training step: {ms:.3f} ms (forward_train {fwd_ms:.3f} ms, backward {ms - fwd_ms:.3f} ms), "
         f"{value / 1e9:.3f} G cells/s")
+
+    # The backward's dominant work is its recurrence: per step and layer one
+    # product launch (k_bwd_mm) and one cell launch (k_bwd_cell), timed as a
+    # pair by the library's own events around each layer's loop of T steps,
+    # in separate timed steps.
+    pkg.lstm_set_option(m.plan, pkg.LSTM_OPT_TIMING, 1)
+    pkg.lstm_read_timing(m.plan, reset=True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    tm = pkg.lstm_read_timing(m.plan, reset=True)
+    pkg.lstm_set_option(m.plan, pkg.LSTM_OPT_TIMING, 0)
+    H = spec.hidden_size
+    flops = 2.0 * spec.B * spec.D * 4 * H * H  # dz_t [B, 4H] x W_hh [4H, H] per direction and step
+    avg = tm["bwd_rec_ms"] / max(1, tm["bwd_rec_launches"])
+    achieved = flops / (avg / 1e3) / 1e12
+    traffic = stored_traffic("k_bwd_mm_k_bwd_cell", args.workload)
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS["f32"], 4), "traffic": traffic,
+            "traffic_GB_per_s": None if traffic is None else round(traffic / (avg / 1e3) / 1e9, 1),
+            "kernel": "k_bwd_mm+k_bwd_cell", "launch": "one backward step: a k_bwd_mm and a k_bwd_cell launch",
+            "avg_launch_ms": round(avg, 5), "flops_per_launch": flops,
+            "phase_ms_per_step": {"bwd_rec": round(tm["bwd_rec_ms"] / max(1, tm["bwd_calls"]), 4),
+                                  "bwd_gemm": round(tm["bwd_gemm_ms"] / max(1, tm["bwd_calls"]), 4),
+                                  "bwd_gemm_launches": tm["bwd_gemm_launches"] // max(1, tm["bwd_calls"])}}
+    log(f"backward phases: {tm}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle's forward + backward on a row sample")
+        cpu = cpu_baseline_train(spec, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
     line = {"metric": "LSTM training step (forward_train + backward) timestep-cells/sec", "value": value,
             "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
             "data": "synthetic (seeded; random-init weights and output gradients)",
             "config": {"workload": args.workload, "T": spec.T, "B": spec.B, "forward_train_ms": fwd_ms,
-                       "backward_ms": ms - fwd_ms, "schedule": desc}}
+                       "backward_ms": ms - fwd_ms, "schedule": desc},
+            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_train(spec, budget_s):
+    """The fp64 oracle's forward + backward on a sample of batch rows (rows are
+    independent), sized to the time budget from a one-row calibration."""
+    import numpy as np
+    import oracle
+    from layer_lstm_forward_amd.synth import make_inputs
+    inp = make_inputs(spec)
+    threads = 1  # the oracle's backward runs on one thread
+    rng = np.random.default_rng(spec.seed + 11)
+    dy_all = rng.standard_normal((spec.T, spec.B, spec.D * spec.hidden_size)).astype(np.float32)
+
+    def run(rows):
+        sub = inp.rows(rows)
+        oracle.lstm_backward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
+                             np.ascontiguousarray(dy_all[:, rows]), h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias,
+                             bf16=sub.bf16)
+    t0 = time.perf_counter()
+    run([0])
+    one = time.perf_counter() - t0
+    n = int(max(1, min(spec.B, budget_s / max(one, 1e-6))))
+    rows = sorted(set(int(r) for r in np.linspace(0, spec.B - 1, n).astype(int))) if n > 1 else [0]
+    t0 = time.perf_counter()
+    run(rows)
+    wall = time.perf_counter() - t0
+    cells = spec.T * len(rows) * spec.hidden_size * spec.num_layers * spec.D
+    return {"value": cells / wall, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {spec.B} batch rows, full T={spec.T}, all {spec.num_layers} layers, "
+                      f"forward + backward in fp64 (the oracle's backward recomputes its forward), "
+                      f"{wall:.1f} s wall"}
 
 
 if __name__ == "__main__":

@@ -108,13 +108,21 @@ typedef enum {
 /* Accumulated per-phase device time of the calls made since the last reset
  * (LSTM_OPT_TIMING).  A "launch" is one kernel launch of that phase: one
  * projection GEMM per layer; one recurrent launch per layer when persistent,
- * T per layer when stepping. */
+ * T per layer when stepping.  Backward phases (lstm_backward): a "launch" of
+ * the recurrence is one backward step (its product and cell launches; the
+ * events bracket a layer's whole loop of T steps); one of the gradient
+ * products is one weight or input gradient (GEMM and slab sum). */
 typedef struct {
     double proj_ms;     /* input-projection GEMMs */
     double rec_ms;      /* recurrent kernels */
-    int calls;          /* lstm_forward calls timed */
+    int calls;          /* lstm_forward / lstm_forward_train calls timed */
     int proj_launches;
     int rec_launches;
+    double bwd_rec_ms;  /* backward recurrence: products dz_t W_hh and cell updates */
+    double bwd_gemm_ms; /* backward weight- and input-gradient products */
+    int bwd_calls;      /* lstm_backward calls timed */
+    int bwd_rec_launches;
+    int bwd_gemm_launches;
 } lstm_timing;
 
 /* Create a plan.  input_size, hidden_size >= 1; num_layers >= 1 (warp-nn

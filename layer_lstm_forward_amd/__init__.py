@@ -34,7 +34,9 @@ _lib = None
 
 class lstm_timing(ctypes.Structure):
     _fields_ = [("proj_ms", ctypes.c_double), ("rec_ms", ctypes.c_double), ("calls", ctypes.c_int),
-                ("proj_launches", ctypes.c_int), ("rec_launches", ctypes.c_int)]
+                ("proj_launches", ctypes.c_int), ("rec_launches", ctypes.c_int),
+                ("bwd_rec_ms", ctypes.c_double), ("bwd_gemm_ms", ctypes.c_double), ("bwd_calls", ctypes.c_int),
+                ("bwd_rec_launches", ctypes.c_int), ("bwd_gemm_launches", ctypes.c_int)]
 
 
 class LSTMError(RuntimeError):

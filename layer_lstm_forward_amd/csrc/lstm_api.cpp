@@ -33,7 +33,7 @@ struct lstm_plan {
     int timing;
     struct Span {
         hipEvent_t a, b;
-        int phase;     // 0 projection, 1 recurrence
+        int phase;     // 0 projection, 1 recurrence, 2 backward recurrent product, 3 backward gradient product
         int launches;
     };
     std::vector<Span> spans;
@@ -471,7 +471,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 103; }
+int lstm_version(void) { return 104; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -516,7 +516,7 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
-    p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
+    p->acc = lstm_timing{};
     *out = p;
     return LSTM_OK;
 }
@@ -541,9 +541,15 @@ lstm_status lstm_read_timing(lstm_plan *p, lstm_timing *out, int reset) {
             if (sp.phase == 0) {
                 p->acc.proj_ms += ms;
                 p->acc.proj_launches += sp.launches;
-            } else {
+            } else if (sp.phase == 1) {
                 p->acc.rec_ms += ms;
                 p->acc.rec_launches += sp.launches;
+            } else if (sp.phase == 2) {
+                p->acc.bwd_rec_ms += ms;
+                p->acc.bwd_rec_launches += sp.launches;
+            } else {
+                p->acc.bwd_gemm_ms += ms;
+                p->acc.bwd_gemm_launches += sp.launches;
             }
         } else {
             (void)hipGetLastError();
@@ -553,7 +559,7 @@ lstm_status lstm_read_timing(lstm_plan *p, lstm_timing *out, int reset) {
     }
     p->spans.clear();
     *out = p->acc;
-    if (reset) p->acc = lstm_timing{0.0, 0.0, 0, 0, 0};
+    if (reset) p->acc = lstm_timing{};
     return LSTM_OK;
 }
 
@@ -1058,6 +1064,13 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         g.D = 1;
         g.kchunk = proj_kchunk(M, N, K);
         const size_t mn = (size_t)M * N;
+        const int sp = span_begin(p, st, 3);
+        struct End {
+            lstm_plan *p;
+            int sp;
+            hipStream_t st;
+            ~End() { span_end(p, sp, st, 1); }
+        } end{p, sp, st};
         if (g.kchunk) {
             g.G = ksp;
             return ok(launch_proj(g, DT_F32, 0, st)) &&
@@ -1070,6 +1083,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         g.G = f32;
         return ok(launch_proj(g, DT_F32, 0, st)) && ok(launch_cast_to(f32, out, mn, out_dt, st));
     };
+    if (p->timing) p->acc.bwd_calls += 1;
     // the gradient of the top layer's output, as fp32
     int cur = 0;
     if (!ok(launch_cast_from(dy, dyb[cur], TB * D * H, dt, st))) return fail();
@@ -1087,6 +1101,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
                 return fail();
         if (dh_n && !ok(launch_cast_from(static_cast<const char *>(dh_n) + (size_t)l * DBH * es, dhnb, DBH, dt, st)))
             return fail();
+        const int rec_span = span_begin(p, st, 2);
         // the recurrence, backwards: sb = 0 is each direction's last step
         for (int sb = 0; sb < T; ++sb) {
             BwdCellArgs ca{};
@@ -1118,6 +1133,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
             ma.sb = sb;
             if (!ok(launch_bwd_mm(ma, st))) return fail();
         }
+        span_end(p, rec_span, st, T);
         if (dh0 && !ok(launch_bwd_dh0(part, bl.NP, DBH, static_cast<char *>(dh0) + (size_t)l * DBH * es, dt, st)))
             return fail();
         if (dc0 && hipMemcpyAsync(dc0 + (size_t)l * DBH, dcb, DBH * sizeof(float), hipMemcpyDeviceToDevice, st) !=
