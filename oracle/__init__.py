@@ -54,10 +54,18 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             dp, ctypes.POINTER(ctypes.c_int), dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp,
             ctypes.c_int]
+        u64 = ctypes.c_uint64
+        lib.oracle_lstm_forward_dropout.restype = ctypes.c_int
+        lib.oracle_lstm_forward_dropout.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64, dp, dp, dp, ctypes.c_int]
         lib.oracle_lstm_backward.restype = ctypes.c_int
         lib.oracle_lstm_backward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
+            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
+        lib.oracle_philox4x64_10.restype = None
+        lib.oracle_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64)]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -82,7 +90,7 @@ def _ptr(a):
 
 def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bool,
                  h0=None, c0=None, has_bias: bool = True, bf16: bool = False,
-                 c_state_bf16: bool = False, nthreads: int = 1, lengths=None):
+                 c_state_bf16: bool = False, nthreads: int = 1, lengths=None, dropout=None):
     """Run the oracle.
 
     x       [T, B, I]
@@ -90,6 +98,8 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     h0, c0  [L*D, B, H] or None (zeros); c0 is never bf16 unless c_state_bf16
     lengths None (every row has T steps) or B ints in 1..T: row b takes part
             only in steps t < lengths[b] (see the C file)
+    dropout None, or (p, seed, call): the training forward's dropout between
+            layers (see the C file); not combined with lengths
     Returns (y [T, B, D*H], h_n [L*D, B, H], c_n [L*D, B, H]) as float64.
     """
     lib = _load()
@@ -121,6 +131,17 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     y = np.empty((T, B, D * H), np.float64)
     hn = np.empty((L * D, B, H), np.float64)
     cn = np.empty((L * D, B, H), np.float64)
+    if dropout is not None:
+        if lengths is not None:
+            raise ValueError("dropout with lengths is not supported")
+        dp_, seed, call = dropout
+        rc = lib.oracle_lstm_forward_dropout(
+            T, B, I, H, L, D, _ptr(x64), _ptr(h064) if h064 is not None else None,
+            _ptr(c064) if c064 is not None else None, arr, 1 if has_bias else 0, float(dp_), int(seed), int(call),
+            _ptr(y), _ptr(hn), _ptr(cn), int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_lstm_forward_dropout failed with {rc}")
+        return y, hn, cn
     rc = lib.oracle_lstm_forward_lengths(
         T, B, I, H, L, D, _ptr(x64),
         len32.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if len32 is not None else None,
@@ -133,7 +154,8 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
 
 
 def lstm_backward(x, params, hidden_size: int, num_layers: int, bidirectional: bool, dy,
-                  h0=None, c0=None, dh_n=None, dc_n=None, has_bias: bool = True, bf16: bool = False):
+                  h0=None, c0=None, dh_n=None, dc_n=None, has_bias: bool = True, bf16: bool = False,
+                  dropout=None):
     """Gradients of the forward pass (see the C file).
 
     dy [T, B, D*H]; dh_n, dc_n [L*D, B, H] or None (zeros).
@@ -162,8 +184,19 @@ def lstm_backward(x, params, hidden_size: int, num_layers: int, bidirectional: b
     dh0 = np.empty((L * D, B, H), np.float64)
     dc0 = np.empty((L * D, B, H), np.float64)
     opt = lambda a: _ptr(a) if a is not None else None  # noqa: E731
+    dp_, seed, call = (0.0, 0, 0) if dropout is None else dropout
     rc = lib.oracle_lstm_backward(T, B, I, H, L, D, _ptr(x64), opt(h064), opt(c064), arr, 1 if has_bias else 0,
-                                  _ptr(dy64), opt(dhn), opt(dcn), _ptr(dx), _ptr(dh0), _ptr(dc0), darr)
+                                  float(dp_), int(seed), int(call), _ptr(dy64), opt(dhn), opt(dcn), _ptr(dx), _ptr(dh0), _ptr(dc0), darr)
     if rc != 0:
         raise RuntimeError(f"oracle_lstm_backward failed with {rc}")
     return dx, dh0, dc0, dps
+
+
+def philox4x64_10(counter, key):
+    """One Philox4x64-10 block (four uint64 words) of the oracle's generator."""
+    lib = _load()
+    c = (ctypes.c_uint64 * 4)(*[int(v) for v in counter])
+    k = (ctypes.c_uint64 * 2)(*[int(v) for v in key])
+    out = (ctypes.c_uint64 * 4)()
+    lib.oracle_philox4x64_10(c, k, out)
+    return [int(v) for v in out]

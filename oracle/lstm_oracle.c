@@ -56,6 +56,18 @@
  *     and its output is zero.  Its final state is therefore the one after
  *     its last valid step, and the reverse direction starts at t = len_b - 1
  *     from the initial state.
+ *   - Dropout between layers in training (oracle_lstm_forward_dropout and
+ *     the p argument of oracle_lstm_backward): the trace page's Performance
+ *     Notes apply dropout to the input of every layer above the first during
+ *     training only, and the op signature of its Step 3 carries the
+ *     probability.  Reading taken: element e of layer l's output sequence
+ *     ([T][B][D*H], time-major flat index) reaches layer l + 1 as
+ *     y[e] / (1 - p) when kept and 0 when dropped (all dropped when p = 1).
+ *     The draw is a counter-based generator, Philox4x64-10 (Salmon, Moraes,
+ *     Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011),
+ *     written here from its published definition: the block with counter
+ *     (e / 4, l, call, 0) and key (seed, 0) gives four 64-bit words; word
+ *     e % 4, as u = (word >> 11) * 2^-53, keeps e when u >= p.
  *
  * Layouts (all row-major, contiguous, fp64):
  *   x    [T][B][I]                   input sequence, time-major
@@ -74,6 +86,7 @@
  * on the thread count.
  */
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -82,19 +95,68 @@
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
+/* Philox4x64-10: ten rounds of two 64x64 -> 128-bit products on counter
+ * words 0 and 2, each round mixing the high halves with the other counter
+ * words and the key, the key advanced by the two Weyl constants between
+ * rounds (the constants are the published ones). */
+static void philox_mul(uint64_t a, uint64_t b, uint64_t *hi, uint64_t *lo)
+{
+    const unsigned __int128 p = (unsigned __int128)a * b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+{
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        uint64_t hi0, lo0, hi1, lo1;
+        philox_mul(0xD2E7470EE14C6C93ull, c0, &hi0, &lo0);
+        philox_mul(0xCA5A826395121157ull, c2, &hi1, &lo1);
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Is element e of layer l's output kept by the dropout draw of call `call`? */
+static int dropout_keeps(double p, uint64_t seed, uint64_t call, int l, size_t e)
+{
+    const uint64_t ctr[4] = {(uint64_t)(e / 4), (uint64_t)l, call, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t w[4];
+    oracle_philox4x64_10(ctr, key, w);
+    const double u = (double)(w[e % 4] >> 11) * 0x1p-53;
+    return u >= p;
+}
+
+/* factor that element e of layer l's output carries into layer l + 1 */
+static double dropout_factor(double p, uint64_t seed, uint64_t call, int l, size_t e)
+{
+    if (p <= 0.0) return 1.0;
+    return dropout_keeps(p, seed, call, l, e) ? 1.0 / (1.0 - p) : 0.0;
+}
+
 /* time index t is past row b's sequence (variable-length batches only) */
 #define PADDED(t, b) (lengths && (t) >= lengths[b])
 
 /* Returns 0 on success, -1 on a bad argument, -2 if memory runs out.
- * lengths: NULL (every row has T steps) or B values in 1..T. */
-int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
-                                const double *x, const int *lengths,
-                                const double *h0, const double *c0,
-                                const double *const *params, int has_bias,
-                                double *y, double *h_n, double *c_n, int nthreads)
+ * lengths: NULL (every row has T steps) or B values in 1..T.
+ * drop_p in [0, 1]: dropout between layers (0: none), drawn for (seed, call). */
+static int forward_core(int T, int B, int I, int H, int L, int D,
+                        const double *x, const int *lengths,
+                        const double *h0, const double *c0,
+                        const double *const *params, int has_bias,
+                        double drop_p, uint64_t seed, uint64_t call,
+                        double *y, double *h_n, double *c_n, int nthreads)
 {
     if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) ||
-        !x || !params || !y)
+        !x || !params || !y || !(drop_p >= 0.0 && drop_p <= 1.0))
         return -1;
     if (lengths)
         for (int b = 0; b < B; ++b)
@@ -177,6 +239,9 @@ int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
             double *tmp = Xl; Xl = Yl; Yl = tmp;
             in_seq = Xl;
             in_w = D * H;
+            /* training: dropout on the way up (Xl is this layer's output) */
+            if (drop_p > 0.0)
+                for (size_t e = 0; e < seq_out; ++e) Xl[e] *= dropout_factor(drop_p, seed, call, l, e);
         }
     }
     memcpy(y, Y, sizeof(double) * seq_out);
@@ -190,14 +255,17 @@ int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
  *   dx   [T][B][I];  dh0, dc0 [L*D][B][H];
  *   dparams: same order and shapes as params (W_ih, W_hh[, b_ih, b_hh]),
  *            overwritten (not accumulated into)
+ * drop_p, seed, call: the dropout of the training forward (drop_p = 0: none).
  * The forward is recomputed here; its per-step activations are kept. */
 int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
                          const double *x, const double *h0, const double *c0,
                          const double *const *params, int has_bias,
+                         double drop_p, uint64_t seed, uint64_t call,
                          const double *dy, const double *dh_n, const double *dc_n,
                          double *dx, double *dh0, double *dc0, double *const *dparams)
 {
-    if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) || !x || !params || !dy)
+    if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) || !x || !params || !dy ||
+        !(drop_p >= 0.0 && drop_p <= 1.0))
         return -1;
     const int per = has_bias ? 4 : 2;
     const int G = 4 * H;
@@ -257,7 +325,9 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
                         const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
                         c[(size_t)b * H + j] = cs[e];
                         h[(size_t)b * H + j] = hs[e];
-                        out_seq[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] = hs[e];
+                        /* the next layer's input, through the training dropout */
+                        const size_t oe = ((size_t)t * B + b) * (D * H) + (size_t)d * H + j;
+                        out_seq[oe] = l + 1 < L ? hs[e] * dropout_factor(drop_p, seed, call, l, oe) : hs[e];
                     }
                 }
             }
@@ -343,8 +413,10 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
             if (dh0) memcpy(dh0 + st, dhn, sizeof(double) * BH);
             if (dc0) memcpy(dc0 + st, dc, sizeof(double) * BH);
         }
-        /* the layer below receives the gradient of its output sequence */
-        memcpy(dY, dX, sizeof(double) * (size_t)T * B * in_w);
+        /* the layer below receives the gradient of its output sequence,
+         * through the dropout factor that output was sent up with */
+        for (size_t e = 0; e < (size_t)T * B * in_w; ++e)
+            dY[e] = l > 0 ? dX[e] * dropout_factor(drop_p, seed, call, l - 1, e) : dX[e];
     }
     if (dx) memcpy(dx, dY, sizeof(double) * (size_t)T * B * I);
     rc = 0;
@@ -354,14 +426,35 @@ out:
     return rc;
 }
 
+int oracle_lstm_forward_lengths(int T, int B, int I, int H, int L, int D,
+                                const double *x, const int *lengths,
+                                const double *h0, const double *c0,
+                                const double *const *params, int has_bias,
+                                double *y, double *h_n, double *c_n, int nthreads)
+{
+    return forward_core(T, B, I, H, L, D, x, lengths, h0, c0, params, has_bias, 0.0, 0, 0,
+                        y, h_n, c_n, nthreads);
+}
+
 /* Every row has all T steps. */
 int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
                         const double *x, const double *h0, const double *c0,
                         const double *const *params, int has_bias,
                         double *y, double *h_n, double *c_n, int nthreads)
 {
-    return oracle_lstm_forward_lengths(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias,
-                                       y, h_n, c_n, nthreads);
+    return forward_core(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias, 0.0, 0, 0,
+                        y, h_n, c_n, nthreads);
+}
+
+/* Training forward: dropout with probability p between layers. */
+int oracle_lstm_forward_dropout(int T, int B, int I, int H, int L, int D,
+                                const double *x, const double *h0, const double *c0,
+                                const double *const *params, int has_bias,
+                                double p, uint64_t seed, uint64_t call,
+                                double *y, double *h_n, double *c_n, int nthreads)
+{
+    return forward_core(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias, p, seed, call,
+                        y, h_n, c_n, nthreads);
 }
 
 /* Number of threads OpenMP would use by default (1 without OpenMP). */

@@ -48,8 +48,11 @@ def cell(g, x, h, c):
     return h_new, c_new
 
 
-def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None):
+def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None, between=None):
     """x: nested [T][B][I]; params flat in (layer, direction, W_ih, W_hh[, b_ih, b_hh]).
+
+    between: None, or between[l][t][b][k], a factor that element (t, b, k) of
+    layer l's output carries into layer l + 1 (training dropout).
 
     lengths: None, or the number of valid steps of each row; a row's sequence
     is then its first lengths[b] time steps only, its padded outputs stay
@@ -80,4 +83,7 @@ def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None):
             hn.append(hl)
             cn.append(cl)
         seq = out
-    return seq, hn, cn
+        if between is not None and l + 1 < L:
+            seq = [[[out[t][b][k] * between[l][t][b][k] for k in range(D * H)] for b in range(B)]
+                   for t in range(T)]
+    return out, hn, cn

@@ -45,10 +45,28 @@ BACKWARD_MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(BACKWARD_MUTATIONS))
+# mistakes in the training dropout and its generator, checked by tests/test_oracle_dropout.py
+DROPOUT_MUTATIONS = {
+    "dropout_no_rescale": ("return dropout_keeps(p, seed, call, l, e) ? 1.0 / (1.0 - p) : 0.0;",
+                           "return dropout_keeps(p, seed, call, l, e) ? 1.0 : 0.0;"),
+    "dropout_keep_inverted": ("return u >= p;", "return u < p;"),
+    "dropout_next_layer_index": ("Xl[e] *= dropout_factor(drop_p, seed, call, l, e);",
+                                 "Xl[e] *= dropout_factor(drop_p, seed, call, l + 1, e);"),
+    "dropout_first_word_only": ("(double)(w[e % 4] >> 11)", "(double)(w[0] >> 11)"),
+    "philox_key_not_advanced": ("k1 += 0xBB67AE8584CAA73Bull;", "k1 += 0;"),
+    "dropout_gradient_unmasked": ("dY[e] = l > 0 ? dX[e] * dropout_factor(drop_p, seed, call, l - 1, e) : dX[e];",
+                                  "dY[e] = dX[e];"),
+}
+TARGET = {**{n: "test_oracle_pins.py" for n in MUTATIONS},
+          **{n: "test_oracle_backward.py" for n in BACKWARD_MUTATIONS},
+          **{n: "test_oracle_dropout.py" for n in DROPOUT_MUTATIONS}}
+ALL = {**MUTATIONS, **BACKWARD_MUTATIONS, **DROPOUT_MUTATIONS}
+
+
+@pytest.mark.parametrize("name", sorted(ALL))
 def test_planted_mistake_is_caught(name, tmp_path):
-    old, new = MUTATIONS[name] if name in MUTATIONS else BACKWARD_MUTATIONS[name]
-    target = "test_oracle_pins.py" if name in MUTATIONS else "test_oracle_backward.py"
+    old, new = ALL[name]
+    target = TARGET[name]
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     mut = tmp_path / "lstm_oracle_mut.c"
