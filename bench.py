@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--poll-sleep", type=int, default=-1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="with --train: dropout probability between layers (seed 1234)")
     ap.add_argument("--lengths", choices=["none", "mix", "ragged"], default="none",
                     help="variable-length rows (lstm_forward_lengths); the value then counts valid cells only")
     ap.add_argument("--batch-first", action="store_true", help="x [B, T, I] and y [B, T, D*H]")
@@ -287,6 +289,8 @@ def main():
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev))
     stream = torch.cuda.current_stream(dev)
     if args.train:
+        if args.dropout:
+            m.set_dropout(args.dropout, 1234, 0)
         return train_bench(args, spec, m, x, w, h0, c0, stream, desc)
 
     for _ in range(args.warmup):
@@ -425,19 +429,19 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle's forward + backward on a row sample")
-        cpu = cpu_baseline_train(spec, args.cpu_budget)
+        cpu = cpu_baseline_train(spec, args.cpu_budget, args.dropout)
         log(f"cpu baseline: {cpu}")
     line = {"metric": "LSTM training step (forward_train + backward) timestep-cells/sec", "value": value,
             "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
             "data": "synthetic (seeded; random-init weights and output gradients)",
             "config": {"workload": args.workload, "T": spec.T, "B": spec.B, "forward_train_ms": fwd_ms,
-                       "backward_ms": ms - fwd_ms, "schedule": desc},
+                       "backward_ms": ms - fwd_ms, "dropout": args.dropout, "schedule": desc},
             "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_train(spec, budget_s):
+def cpu_baseline_train(spec, budget_s, dropout=0.0):
     """The fp64 oracle's forward + backward on a sample of batch rows (rows are
     independent), sized to the time budget from a one-row calibration."""
     import numpy as np
@@ -452,7 +456,7 @@ def cpu_baseline_train(spec, budget_s):
         sub = inp.rows(rows)
         oracle.lstm_backward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
                              np.ascontiguousarray(dy_all[:, rows]), h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias,
-                             bf16=sub.bf16)
+                             bf16=sub.bf16, dropout=(dropout, 1234, 0) if dropout else None)
     t0 = time.perf_counter()
     run([0])
     one = time.perf_counter() - t0

@@ -191,11 +191,30 @@ lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *leng
  * c_n) and a reserve of activations saved by the forward; the pulsatrix
  * "LSTMModule" reference describes the backpropagation through time across
  * the four gates and the cell carry.  Time-major layout only (batch_first is
- * LSTM_ERR_UNSUPPORTED), all rows of length T, no dropout. */
+ * LSTM_ERR_UNSUPPORTED), all rows of length T. */
+
+/* Training dropout between layers.  The trace page's Performance Notes apply
+ * dropout to the input of every layer above the first, in training only
+ * (lstm_forward never drops); its Step 3 op signature carries the
+ * probability.  With probability prob in [0, 1] (0: none, the default),
+ * element e of layer l's output ([T, B, D*H] flat, time-major) reaches layer
+ * l + 1 as y * 1/(1 - prob) when kept and as 0 when dropped (all dropped when
+ * prob = 1).  The draw is Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011): the block with
+ * counter (e / 4, l, call, 0) and key (seed, 0) gives four 64-bit words, and
+ * word e % 4 keeps e when (word >> 11) * 2^-53 >= prob.  `call` is the index
+ * used by the next lstm_forward_train; each successful call with dropout
+ * advances it by one.  Set it before lstm_reserve_size (the reserve then also
+ * holds each dropped layer input and its keep bytes) and keep it unchanged
+ * between a lstm_forward_train and its lstm_backward.  prob outside [0, 1]
+ * (or NaN) is LSTM_ERR_ARG. */
+lstm_status lstm_set_dropout(lstm_plan *plan, double prob, unsigned long long seed, unsigned long long call);
 
 /* Bytes of reserve lstm_forward_train fills for (T, B): per layer the gates
  * i, f, g, o and the cell state c of every step (fp32), and the outputs of
- * every layer but the top one (dtype). */
+ * every layer but the top one (dtype); with dropout also, for every layer but
+ * the top one, its output after dropout (dtype) and one keep byte per
+ * element. */
 lstm_status lstm_reserve_size(const lstm_plan *plan, int T, int B, size_t *bytes);
 
 /* lstm_forward, and also fills `reserve` (device memory of at least

@@ -61,6 +61,8 @@ def load_library():
     lib.lstm_destroy.argtypes = [vp]
     lib.lstm_set_option.restype = i
     lib.lstm_set_option.argtypes = [vp, i, i]
+    lib.lstm_set_dropout.restype = i
+    lib.lstm_set_dropout.argtypes = [vp, ctypes.c_double, ctypes.c_ulonglong, ctypes.c_ulonglong]
     lib.lstm_workspace_size.restype = i
     lib.lstm_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.lstm_forward.restype = i
@@ -119,6 +121,12 @@ def lstm_set_option(plan, option: int, value: int) -> None:
     rc = load_library().lstm_set_option(ctypes.c_void_p(plan), int(option), int(value))
     if rc:
         raise LSTMError(rc, "lstm_set_option")
+
+
+def lstm_set_dropout(plan, prob: float, seed: int = 0, call: int = 0) -> None:
+    rc = load_library().lstm_set_dropout(ctypes.c_void_p(plan), float(prob), int(seed), int(call))
+    if rc:
+        raise LSTMError(rc, "lstm_set_dropout")
 
 
 def lstm_workspace_size(plan, T: int, B: int) -> int:
@@ -223,7 +231,8 @@ class LSTM:
     """
 
     def __init__(self, input_size, hidden_size, num_layers=1, bidirectional=False, bias=True,
-                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None, batch_first=False):
+                 dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None, batch_first=False, dropout=0.0,
+                 dropout_seed=0):
         self.input_size, self.hidden_size = int(input_size), int(hidden_size)
         self.num_layers, self.bidirectional, self.bias = int(num_layers), bool(bidirectional), bool(bias)
         self.dtype = dtype
@@ -239,7 +248,14 @@ class LSTM:
             lstm_set_option(self.plan, LSTM_OPT_BATCH_FIRST, 1)
         for opt, val in (options or {}).items():
             lstm_set_option(self.plan, opt, val)
+        if dropout:
+            lstm_set_dropout(self.plan, dropout, dropout_seed, 0)
         self._ws = None
+
+    def set_dropout(self, prob, seed=0, call=0):
+        """Training dropout between layers; `call` is the draw index of the
+        next forward_train (each one advances it)."""
+        lstm_set_dropout(self.plan, prob, seed, call)
 
     def __del__(self):
         try:

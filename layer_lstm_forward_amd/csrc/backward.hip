@@ -22,6 +22,11 @@
 //   k_transpose, k_hprev_t, k_rowsum, k_cast_*  operand preparation for the
 //               weight and input gradients, which are plain fp32 "NT" GEMMs
 //               on the projection kernels
+//   k_dropout_fwd, k_dropout_bwd  training dropout between layers: the trace
+//               page's Performance Notes apply it to the input of every
+//               layer above the first in training only; the draw is
+//               Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+//               numbers: as easy as 1, 2, 3", SC 2011)
 #include "device.h"
 #include "kernels.h"
 
@@ -228,6 +233,57 @@ __global__ void k_ksum(const float *part, int ns, size_t slab, size_t n, typenam
     }
 }
 
+// Philox4x64-10 block: ten rounds, each two 64 x 64 -> 128-bit products of
+// counter words 0 and 2 by the published multipliers, mixed with the other
+// two words and the key; the key advances by the published Weyl constants
+// after every round.
+__device__ inline void philox4x64_10(unsigned long long (&c)[4], unsigned long long k0, unsigned long long k1) {
+    constexpr unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const unsigned long long hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+        const unsigned long long hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+        const unsigned long long n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+}
+
+// Training dropout of layer `layer`'s output y (n elements, flat index e over
+// [T][B][D*H]): the block with counter (e / 4, layer, call, 0) and key
+// (seed, 0) gives four words; word e % 4 keeps e when (word >> 11) >= thr,
+// i.e. (word >> 11) * 2^-53 >= p with thr = ceil(p * 2^53), an exact integer
+// form of the comparison.  xd = kept ? y * scale : 0 (the next layer's
+// input), keep = the decision (read again by the backward pass).
+template <class DT>
+__global__ void k_dropout_fwd(const typename DT::S *y, typename DT::S *xd, unsigned char *keep, size_t n,
+                              unsigned long long seed, unsigned long long call, int layer, unsigned long long thr,
+                              float scale) {
+    const size_t nblk = (n + 3) / 4;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < nblk; i += (size_t)gridDim.x * blockDim.x) {
+        unsigned long long c[4] = {(unsigned long long)i, (unsigned long long)layer, call, 0ull};
+        philox4x64_10(c, seed, 0ull);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const size_t e = 4 * i + q;
+            if (e >= n) break;
+            const bool kept = (c[q] >> 11) >= thr;
+            xd[e] = DT::from_f(kept ? DT::to_f(y[e]) * scale : 0.f);
+            keep[e] = kept ? 1 : 0;
+        }
+    }
+}
+
+// The gradient reaching layer `layer`'s output through the dropout.
+__global__ void k_dropout_bwd(float *g, const unsigned char *keep, size_t n, float scale) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        g[e] = keep[e] ? g[e] * scale : 0.f;
+}
+
 // ---------------------------------------------------------------- launchers
 static unsigned grid1(size_t n, unsigned cap = 8192) {
     const size_t g = (n + 255) / 256;
@@ -306,6 +362,26 @@ hipError_t launch_ksum(const float *part, int ns, size_t slab, size_t n, void *o
                            static_cast<uint16_t *>(out));
     else
         hipLaunchKernelGGL(k_ksum<F32>, dim3(grid1(n)), dim3(256), 0, s, part, ns, slab, n, static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, size_t n, unsigned long long seed,
+                              unsigned long long call, int layer, unsigned long long thr, float scale, int dtype,
+                              hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const unsigned g = grid1((n + 3) / 4);
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_dropout_fwd<BF16>, dim3(g), dim3(256), 0, s, static_cast<const uint16_t *>(y),
+                           static_cast<uint16_t *>(xd), keep, n, seed, call, layer, thr, scale);
+    else
+        hipLaunchKernelGGL(k_dropout_fwd<F32>, dim3(g), dim3(256), 0, s, static_cast<const float *>(y),
+                           static_cast<float *>(xd), keep, n, seed, call, layer, thr, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_dropout_bwd(float *g, const unsigned char *keep, size_t n, float scale, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_dropout_bwd, dim3(grid1(n)), dim3(256), 0, s, g, keep, n, scale);
     return hipGetLastError();
 }
 

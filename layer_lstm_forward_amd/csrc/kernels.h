@@ -175,6 +175,14 @@ hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int
 hipError_t launch_rowsum(const float *a, size_t ld, int rows, int cols, float *out, hipStream_t s);
 hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s);
 hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s);
+// Training dropout of one layer's output y (n elements of dtype): xd = the
+// next layer's input, keep = one byte per element; thr = ceil(p * 2^53),
+// scale = 1 / (1 - p) (0 when p = 1).
+hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, size_t n, unsigned long long seed,
+                              unsigned long long call, int layer, unsigned long long thr, float scale, int dtype,
+                              hipStream_t s);
+// g[e] = keep[e] ? g[e] * scale : 0
+hipError_t launch_dropout_bwd(float *g, const unsigned char *keep, size_t n, float scale, hipStream_t s);
 
 // Zero the y row of (t, b) for every t >= len[b] (padded steps of variable-length rows).
 hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first, hipStream_t s);

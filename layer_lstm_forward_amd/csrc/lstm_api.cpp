@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -26,6 +27,10 @@ struct lstm_plan {
     int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
+    // training dropout between layers (lstm_set_dropout)
+    double dropout;                 // probability, 0 = none
+    unsigned long long drop_seed;   // generator key
+    unsigned long long drop_call;   // call index of the next lstm_forward_train
                        // (off by default: slower than layer by layer on the measured workloads)
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
     int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
@@ -119,9 +124,18 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
 
 // Training reserve: per layer the activations [T][B][D][5][H] fp32 (gates i,
 // f, g, o and c of every step), then the outputs of the layers below the top
-// one ([T][B][D*H] dtype) that the backward pass reads again.
+// one ([T][B][D*H] dtype) that the backward pass reads again; with dropout,
+// per layer below the top one also the next layer's input (the output after
+// dropout, dtype) and the keep decisions (one byte per element).
 struct ReserveLayout {
-    size_t acts_layer, y_layer, total;
+    size_t acts_layer, y_layer, xd_layer, keep_layer, total;
+    bool dropout;
+    // layer l's output (l < L - 1), the next layer's input after dropout, and the keep bytes
+    size_t y(const lstm_plan *p, int l) const { return acts_layer * p->L + y_layer * l; }
+    size_t xd(const lstm_plan *p, int l) const {
+        return acts_layer * p->L + y_layer * (p->L - 1) + (xd_layer + keep_layer) * l;
+    }
+    size_t keep(const lstm_plan *p, int l) const { return xd(p, l) + xd_layer; }
 };
 
 bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
@@ -131,10 +145,15 @@ bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     r->acts_layer = align_up(a);
     r->y_layer = align_up(y);
-    size_t ta, ty;
-    if (!mul_ok(r->acts_layer, (size_t)p->L, &ta) || !mul_ok(r->y_layer, (size_t)(p->L - 1), &ty)) return false;
-    if (ta > SIZE_MAX - ty) return false;
-    r->total = ta + ty;
+    r->dropout = p->dropout > 0.0 && p->L > 1;
+    r->xd_layer = r->dropout ? r->y_layer : 0;
+    r->keep_layer = r->dropout ? align_up(y / elem_size(p->dtype)) : 0;
+    size_t ta, ty, td;
+    if (!mul_ok(r->acts_layer, (size_t)p->L, &ta) || !mul_ok(r->y_layer, (size_t)(p->L - 1), &ty) ||
+        !mul_ok(r->xd_layer + r->keep_layer, (size_t)(p->L - 1), &td))
+        return false;
+    if (ta > SIZE_MAX - ty || ta + ty > SIZE_MAX - td) return false;
+    r->total = ta + ty + td;
     return true;
 }
 
@@ -471,7 +490,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 104; }
+int lstm_version(void) { return 105; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -513,6 +532,9 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->layer_pipe = 0;
     p->fuse_input = 1;
     p->batch_first = 0;
+    p->dropout = 0.0;
+    p->drop_seed = 0;
+    p->drop_call = 0;
     p->team_rows = 0;
     p->proj_tile = 0;
     p->timing = 0;
@@ -560,6 +582,14 @@ lstm_status lstm_read_timing(lstm_plan *p, lstm_timing *out, int reset) {
     p->spans.clear();
     *out = p->acc;
     if (reset) p->acc = lstm_timing{};
+    return LSTM_OK;
+}
+
+lstm_status lstm_set_dropout(lstm_plan *p, double prob, unsigned long long seed, unsigned long long call) {
+    if (!p || !(prob >= 0.0 && prob <= 1.0)) return LSTM_ERR_ARG;
+    p->dropout = prob;
+    p->drop_seed = seed;
+    p->drop_call = call;
     return LSTM_OK;
 }
 
@@ -823,10 +853,11 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     for (int l = 0; l < p->L; ++l) {
         // layer outputs below the top one: workspace ping-pong, or the
         // training reserve (the backward pass reads them again)
-        auto mid = [&](int k) -> char * {
-            return reserve ? reserve + rl.acts_layer * p->L + rl.y_layer * k : ws + lay.ymid[k & 1];
-        };
-        const void *X = l == 0 ? x : static_cast<const void *>(mid(l - 1));
+        auto mid = [&](int k) -> char * { return reserve ? reserve + rl.y(p, k) : ws + lay.ymid[k & 1]; };
+        // training with dropout: a layer above the first reads the output below after dropout
+        const bool drop = reserve && rl.dropout;
+        const void *X = l == 0 ? x : drop ? static_cast<const void *>(reserve + rl.xd(p, l - 1))
+                                          : static_cast<const void *>(mid(l - 1));
         void *Y = l == p->L - 1 ? y : static_cast<void *>(mid(l));
         const int in_l = l == 0 ? p->I : p->D * p->H;
 
@@ -949,6 +980,17 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         if (dlen && use_gemm_layer && l == p->L - 1 &&
             launch_mask_padded(y, dlen, T, B, (size_t)p->D * p->H * es, p->batch_first != 0, st) != hipSuccess)
             return LSTM_ERR_LAUNCH;
+        if (drop && l + 1 < p->L) {
+            const double q = p->dropout;
+            const unsigned long long thr = q >= 1.0 ? (1ull << 53) : (unsigned long long)std::ceil(q * 0x1p53);
+            const float scale = q >= 1.0 ? 0.f : (float)(1.0 / (1.0 - q));
+            if (launch_dropout_fwd(Y, reserve + rl.xd(p, l), reinterpret_cast<unsigned char *>(reserve + rl.keep(p, l)),
+                                   (size_t)T * B * p->D * p->H, p->drop_seed, p->drop_call, l, thr, scale, p->dtype,
+                                   st) != hipSuccess) {
+                (void)hipGetLastError();
+                return LSTM_ERR_LAUNCH;
+            }
+        }
     }
     if (p->timing) p->acc.calls += 1;
     return LSTM_OK;
@@ -988,8 +1030,10 @@ lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, cons
         return LSTM_ERR_DEVICE;
     }
     if (!is_device_ptr(reserve, dev)) return LSTM_ERR_DEVICE;
-    return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
-                        workspace_bytes, stream, static_cast<char *>(reserve));
+    const lstm_status s = forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                                       workspace_bytes, stream, static_cast<char *>(reserve));
+    if (s == LSTM_OK && rl.dropout) p->drop_call += 1;  // the next call draws a fresh mask
+    return s;
 }
 
 lstm_status lstm_backward_workspace_size(const lstm_plan *p, int T, int B, size_t *bytes) {
@@ -1089,8 +1133,8 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     if (!ok(launch_cast_from(dy, dyb[cur], TB * D * H, dt, st))) return fail();
     for (int l = p->L - 1; l >= 0; --l) {
         const int in_l = l == 0 ? p->I : D * H;
-        const void *X = l == 0 ? x : static_cast<const void *>(res + rl.acts_layer * p->L + rl.y_layer * (l - 1));
-        const void *Y = l == p->L - 1 ? y : static_cast<const void *>(res + rl.acts_layer * p->L + rl.y_layer * l);
+        const void *X = l == 0 ? x : static_cast<const void *>(res + (rl.dropout ? rl.xd(p, l - 1) : rl.y(p, l - 1)));
+        const void *Y = l == p->L - 1 ? y : static_cast<const void *>(res + rl.y(p, l));
         const float *acts = reinterpret_cast<const float *>(res + rl.acts_layer * l);
         const float *c0l = c0 ? c0 + (size_t)l * DBH : nullptr;
         const char *h0l = h0 ? static_cast<const char *>(h0) + (size_t)l * DBH * es : nullptr;
@@ -1166,6 +1210,13 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
             if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
                          dyb[cur ^ 1]))
                 return fail();
+            // through the dropout the layer below's output was sent up with
+            if (!out_dx && rl.dropout) {
+                const float scale = p->dropout >= 1.0 ? 0.f : (float)(1.0 / (1.0 - p->dropout));
+                if (!ok(launch_dropout_bwd(dyb[cur ^ 1], reinterpret_cast<const unsigned char *>(res + rl.keep(p, l - 1)),
+                                           TB * in_l, scale, st)))
+                    return fail();
+            }
         }
         cur ^= 1;
     }

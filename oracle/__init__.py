@@ -64,6 +64,9 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
+        lib.oracle_dropout_keep.restype = None
+        lib.oracle_dropout_keep.argtypes = [ctypes.c_double, u64, u64, ctypes.c_int, ctypes.c_size_t,
+                                            ctypes.POINTER(ctypes.c_ubyte)]
         lib.oracle_philox4x64_10.restype = None
         lib.oracle_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64)]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -200,3 +203,13 @@ def philox4x64_10(counter, key):
     out = (ctypes.c_uint64 * 4)()
     lib.oracle_philox4x64_10(c, k, out)
     return [int(v) for v in out]
+
+
+def dropout_keep(p, seed, call, layer, n):
+    """The training dropout's keep decisions (uint8, 1 = kept) of elements
+    0..n-1 of layer `layer`'s output for draw (seed, call)."""
+    lib = _load()
+    out = np.zeros(int(n), np.uint8)
+    lib.oracle_dropout_keep(float(p), int(seed), int(call), int(layer), int(n),
+                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)))
+    return out

@@ -135,6 +135,12 @@ static int dropout_keeps(double p, uint64_t seed, uint64_t call, int l, size_t e
     return u >= p;
 }
 
+/* keep decisions of elements 0..n-1 of layer l's output (1 kept, 0 dropped) */
+void oracle_dropout_keep(double p, uint64_t seed, uint64_t call, int l, size_t n, unsigned char *keep)
+{
+    for (size_t e = 0; e < n; ++e) keep[e] = (unsigned char)dropout_keeps(p, seed, call, l, e);
+}
+
 /* factor that element e of layer l's output carries into layer l + 1 */
 static double dropout_factor(double p, uint64_t seed, uint64_t call, int l, size_t e)
 {

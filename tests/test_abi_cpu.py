@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 104
+    assert pkg.lstm_version() == 105
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -175,5 +175,34 @@ def test_forward_rejects_non_device_pointers():
         host = (ctypes.c_float * 64)()
         addr = ctypes.addressof(host)
         assert _fwd(p, x=addr, y=addr, workspace=addr, weights=[addr] * 4) == -4
+    finally:
+        pkg.lstm_destroy(p)
+
+
+def test_dropout_settings_and_reserve_size():
+    # prob in [0, 1]; the reserve grows by each dropped layer input and its keep bytes
+    for dtype, es in (("f32", 4), ("bf16", 2)):
+        p = pkg.lstm_create(24, 32, 3, True, True, pkg.LSTM_BF16 if dtype == "bf16" else pkg.LSTM_F32)
+        try:
+            T, B, D, H = 7, 5, 2, 32
+            base = pkg.lstm_reserve_size(p, T, B)
+            for bad in (-0.1, 1.5, float("nan")):
+                with pytest.raises(pkg.LSTMError):
+                    pkg.lstm_set_dropout(p, bad, 1, 0)
+            assert pkg.lstm_reserve_size(p, T, B) == base
+            pkg.lstm_set_dropout(p, 0.25, 99, 3)
+            n = T * B * D * H
+            up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+            assert pkg.lstm_reserve_size(p, T, B) == base + 2 * (up(n * es) + up(n))
+            pkg.lstm_set_dropout(p, 0.0, 99, 3)
+            assert pkg.lstm_reserve_size(p, T, B) == base
+        finally:
+            pkg.lstm_destroy(p)
+    # one layer: nothing to drop
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        base = pkg.lstm_reserve_size(p, 4, 2)
+        pkg.lstm_set_dropout(p, 0.5, 1, 0)
+        assert pkg.lstm_reserve_size(p, 4, 2) == base
     finally:
         pkg.lstm_destroy(p)

@@ -53,6 +53,13 @@ def test_philox_matches_numpy(counter, key):
     assert oracle.philox4x64_10(counter, key) == numpy_philox_block(counter, key)
 
 
+@pytest.mark.parametrize("p,seed,call,layer,n", [(0.3, 7, 0, 0, 1001), (0.5, 1 << 60, 9, 2, 4096),
+                                                  (0.999, 3, 1, 1, 777), (1.0, 5, 0, 0, 64), (0.0, 5, 0, 0, 64)])
+def test_oracle_keep_decisions_match_numpy(p, seed, call, layer, n):
+    want = numpy_keep_mask(p, seed, call, layer, n).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.dropout_keep(p, seed, call, layer, n), want)
+
+
 def test_numpy_mask_keep_fraction():
     # the test's own mask helper: keeps about 1 - p (binomial, 6 sigma)
     n, p = 200000, 0.3
