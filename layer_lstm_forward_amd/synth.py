@@ -12,6 +12,8 @@ Recipe (the same for every workload):
     table (biases included);
   * x ~ N(0, 1) drawn as float32;
   * h0, c0 either absent (zeros) or ~ N(0, 0.1) (standard deviation 0.1);
+    c0 is drawn for every mode (the GRU and the RNNs do not read it);
+  * the gate blocks per parameter are 4 (LSTM), 3 (GRU) or 1 (RNN);
   * bf16 workloads draw in fp32 and round to nearest-even bf16 once, here;
     the cell state c0 stays fp32.
   * per-row sequence lengths (variable-length batches), from their own
@@ -39,6 +41,12 @@ class Spec:
     seed: int = 0
     state: str = "zeros"        # "zeros" (h0 = c0 = None) or "normal0.1"
     has_bias: bool = True
+    mode: str = "lstm"          # "lstm", "gru", "rnn_tanh" or "rnn_relu"
+
+    @property
+    def gates(self) -> int:
+        """Gate blocks of H rows in W_ih, W_hh and the biases."""
+        return {"lstm": 4, "gru": 3, "rnn_tanh": 1, "rnn_relu": 1}[self.mode]
 
     @property
     def D(self) -> int:
@@ -53,9 +61,9 @@ class Spec:
         return self.input_size if l == 0 else self.D * self.hidden_size
 
     def flops(self) -> int:
-        """Multiply-add FLOPs of the two products, 8*(in_l + H) per cell per layer."""
+        """Multiply-add FLOPs of the two products, 2*gates*(in_l + H) per cell per layer."""
         H = self.hidden_size
-        return sum(8 * (self.layer_input(l) + H) * self.B * self.T * H * self.D
+        return sum(2 * self.gates * (self.layer_input(l) + H) * self.B * self.T * H * self.D
                    for l in range(self.num_layers))
 
 
@@ -109,11 +117,12 @@ def make_inputs(spec: Spec) -> Inputs:
     k = 1.0 / np.sqrt(H)
     cast = f32_to_bf16_bits if spec.dtype == "bf16" else (lambda a: a)
     params = []
+    G = spec.gates * H
     for l in range(L):
         for _d in range(D):
-            shapes = [(4 * H, spec.layer_input(l)), (4 * H, H)]
+            shapes = [(G, spec.layer_input(l)), (G, H)]
             if spec.has_bias:
-                shapes += [(4 * H,), (4 * H,)]
+                shapes += [(G,), (G,)]
             for shp in shapes:
                 params.append(cast(rng.uniform(-k, k, size=shp).astype(np.float32)))
     x = cast(rng.standard_normal(size=(spec.T, spec.B, spec.input_size), dtype=np.float32))

@@ -64,6 +64,10 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
+        lib.oracle_rnn_forward.restype = ctypes.c_int
+        lib.oracle_rnn_forward.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, ctypes.c_int]
         lib.oracle_dropout_keep.restype = None
         lib.oracle_dropout_keep.argtypes = [ctypes.c_double, u64, u64, ctypes.c_int, ctypes.c_size_t,
                                             ctypes.POINTER(ctypes.c_ubyte)]
@@ -213,3 +217,41 @@ def dropout_keep(p, seed, call, layer, n):
     lib.oracle_dropout_keep(float(p), int(seed), int(call), int(layer), int(n),
                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)))
     return out
+
+
+MODES = {"gru": 1, "rnn_tanh": 2, "rnn_relu": 3}
+
+
+def rnn_forward(mode, x, params, hidden_size: int, num_layers: int, bidirectional: bool, h0=None,
+                has_bias: bool = True, bf16: bool = False, nthreads: int = 1):
+    """The other recurrent modes ("gru", "rnn_tanh", "rnn_relu"; see the C
+    file).  params in (layer, direction, W_ih, W_hh[, b_ih, b_hh]) order with
+    3H (GRU) or H gate rows.  Returns (y [T, B, D*H], h_n [L*D, B, H]) as
+    float64."""
+    lib = _load()
+    m = MODES[mode]
+    x64 = np.ascontiguousarray(as_f64(x, bf16))
+    T, B, I = x64.shape
+    H, L, D = int(hidden_size), int(num_layers), 2 if bidirectional else 1
+    per = 4 if has_bias else 2
+    ng = 3 if m == 1 else 1
+    if len(params) != L * D * per:
+        raise ValueError(f"expected {L * D * per} parameter arrays, got {len(params)}")
+    p64 = [np.ascontiguousarray(as_f64(p, bf16)) for p in params]
+    for idx, p in enumerate(p64):
+        l, rem = divmod(idx, D * per)
+        in_l = I if l == 0 else D * H
+        want = [(ng * H, in_l), (ng * H, H), (ng * H,), (ng * H,)][rem % per]
+        if p.shape != want:
+            raise ValueError(f"param {idx} has shape {p.shape}, expected {want}")
+    arr = (ctypes.POINTER(ctypes.c_double) * len(p64))(*[_ptr(p) for p in p64])
+    h064 = None if h0 is None else np.ascontiguousarray(as_f64(h0, bf16))
+    if h064 is not None and h064.shape != (L * D, B, H):
+        raise ValueError(f"h0 shape {h064.shape} != {(L * D, B, H)}")
+    y = np.empty((T, B, D * H), np.float64)
+    hn = np.empty((L * D, B, H), np.float64)
+    rc = lib.oracle_rnn_forward(m, T, B, I, H, L, D, _ptr(x64), _ptr(h064) if h064 is not None else None, arr,
+                                1 if has_bias else 0, _ptr(y), _ptr(hn), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_rnn_forward failed with {rc}")
+    return y, hn

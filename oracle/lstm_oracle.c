@@ -69,6 +69,18 @@
  *     (e / 4, l, call, 0) and key (seed, 0) gives four 64-bit words; word
  *     e % 4, as u = (word >> 11) * 2^-53, keeps e when u >= p.
  *
+ *   - Other recurrent modes (oracle_rnn_forward): the trace page's RNNBase
+ *     ("Complete Trace: nn.LSTM", Step 1) takes a mode among 'LSTM', 'GRU',
+ *     'RNN_TANH' and 'RNN_RELU' but gives only the LSTM's equations.  Reading
+ *     taken: the definitions of the framework whose RNNBase that page
+ *     reproduces.  With gi = W_ih x_t + b_ih and gh = W_hh h + b_hh split
+ *     into H-row blocks (GRU: [r; z; n], RNN: one block):
+ *         GRU:  r = sigma(gi_r + gh_r),  z = sigma(gi_z + gh_z),
+ *               n = tanh(gi_n + r * gh_n),  h' = (1 - z) * n + z * h
+ *         RNN_TANH: h' = tanh(gi + gh);  RNN_RELU: h' = max(0, gi + gh)
+ *     Stacking, directions and shapes as for the LSTM, with 3H (GRU) or H
+ *     (RNN) gate rows instead of 4H and no cell state.
+ *
  * Layouts (all row-major, contiguous, fp64):
  *   x    [T][B][I]                   input sequence, time-major
  *   h0   [L*D][B][H] or NULL (zeros) index l*D + d, forward before reverse
@@ -461,6 +473,83 @@ int oracle_lstm_forward_dropout(int T, int B, int I, int H, int L, int D,
 {
     return forward_core(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias, p, seed, call,
                         y, h_n, c_n, nthreads);
+}
+
+/* Forward pass of the other recurrent modes: mode 1 GRU, 2 RNN_TANH, 3
+ * RNN_RELU.  Parameters per (layer, direction): W_ih [NG*H][in_l],
+ * W_hh [NG*H][H] (and b_ih, b_hh [NG*H] when has_bias), NG = 3 for the GRU
+ * and 1 for the RNNs.  h0, h_n [L*D][B][H] as for the LSTM; no cell state.
+ * Returns 0, -1 on a bad argument, -2 if memory runs out. */
+int oracle_rnn_forward(int mode, int T, int B, int I, int H, int L, int D,
+                       const double *x, const double *h0, const double *const *params, int has_bias,
+                       double *y, double *h_n, int nthreads)
+{
+    if (mode < 1 || mode > 3 || T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) ||
+        !x || !params || !y)
+        return -1;
+    if (nthreads < 1) nthreads = 1;
+    const int per = has_bias ? 4 : 2;
+    const int NG = mode == 1 ? 3 : 1, R = NG * H;
+    const size_t nseq = (size_t)T * B * D * H;
+    double *state = malloc(sizeof(double) * (size_t)B * H);
+    double *gin = malloc(sizeof(double) * (size_t)B * R), *ghid = malloc(sizeof(double) * (size_t)B * R);
+    double *cur = malloc(sizeof(double) * nseq), *below = malloc(sizeof(double) * nseq);
+    if (!state || !gin || !ghid || !cur || !below) {
+        free(state); free(gin); free(ghid); free(cur); free(below);
+        return -2;
+    }
+    const double *src = x;
+    int width = I;
+    for (int l = 0; l < L; ++l) {
+        memset(cur, 0, sizeof(double) * nseq);
+        for (int d = 0; d < D; ++d) {
+            const double *const *w = params + (size_t)(l * D + d) * per;
+            const size_t base = (size_t)(l * D + d) * B * H;
+            for (size_t q = 0; q < (size_t)B * H; ++q) state[q] = h0 ? h0[base + q] : 0.0;
+            for (int s = 0; s < T; ++s) {
+                const int t = d == 0 ? s : T - 1 - s;
+                /* the input and the hidden contributions of every gate row, kept apart */
+#pragma omp parallel for collapse(2) num_threads(nthreads) if (nthreads > 1)
+                for (int b = 0; b < B; ++b) {
+                    for (int r = 0; r < R; ++r) {
+                        const double *xv = src + ((size_t)t * B + b) * width;
+                        double a = has_bias ? w[2][r] : 0.0, c = has_bias ? w[3][r] : 0.0;
+                        for (int k = 0; k < width; ++k) a += w[0][(size_t)r * width + k] * xv[k];
+                        for (int k = 0; k < H; ++k) c += w[1][(size_t)r * H + k] * state[(size_t)b * H + k];
+                        gin[(size_t)b * R + r] = a;
+                        ghid[(size_t)b * R + r] = c;
+                    }
+                }
+                for (int b = 0; b < B; ++b) {
+                    for (int j = 0; j < H; ++j) {
+                        const double *gi = gin + (size_t)b * R, *gh = ghid + (size_t)b * R;
+                        double hv;
+                        if (mode == 1) {
+                            const double rg = sigmoid(gi[j] + gh[j]);
+                            const double zg = sigmoid(gi[H + j] + gh[H + j]);
+                            const double ng = tanh(gi[2 * H + j] + rg * gh[2 * H + j]);
+                            hv = (1.0 - zg) * ng + zg * state[(size_t)b * H + j];
+                        } else {
+                            const double v = gi[j] + gh[j];
+                            hv = mode == 2 ? tanh(v) : (v > 0.0 ? v : 0.0);
+                        }
+                        cur[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] = hv;
+                    }
+                    /* every gate row of row b has read the old state: replace it */
+                    for (int j = 0; j < H; ++j)
+                        state[(size_t)b * H + j] = cur[((size_t)t * B + b) * (D * H) + (size_t)d * H + j];
+                }
+            }
+            if (h_n) memcpy(h_n + base, state, sizeof(double) * (size_t)B * H);
+        }
+        /* the layer above reads this layer's output sequence */
+        double *swap = below; below = cur; cur = swap;
+        src = below;
+        width = D * H;
+    }
+    memcpy(y, below, sizeof(double) * nseq);
+    free(state); free(gin); free(ghid); free(cur); free(below);
+    return 0;
 }
 
 /* Number of threads OpenMP would use by default (1 without OpenMP). */

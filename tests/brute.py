@@ -87,3 +87,49 @@ def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None, betw
             seq = [[[out[t][b][k] * between[l][t][b][k] for k in range(D * H)] for b in range(B)]
                    for t in range(T)]
     return out, hn, cn
+
+
+def rnn(mode, x, params, H, L, D, h0=None, has_bias=True):
+    """The GRU ("gru", gate blocks r, z, n) and the plain RNNs ("rnn_tanh",
+    "rnn_relu") in the same per-gate scalar style: every gate keeps its own
+    W_i*, W_h*, b_i*, b_h*; the GRU's candidate applies r to the hidden
+    contribution including its bias.  Returns y [T][B][D*H] and h_n
+    [L*D][B][H] as nested lists."""
+    T, B = len(x), len(x[0])
+    per = 4 if has_bias else 2
+    names = ("r", "z", "n") if mode == "gru" else ("a",)
+    seq = [[list(map(float, x[t][b])) for b in range(B)] for t in range(T)]
+    hn = []
+    out = seq
+    for l in range(L):
+        out = [[[0.0] * (D * H) for _ in range(B)] for _ in range(T)]
+        for d in range(D):
+            p = params[(l * D + d) * per:(l * D + d + 1) * per]
+            g = {}
+            for q, nm in enumerate(names):
+                rows = range(q * H, (q + 1) * H)
+                g["Wi" + nm] = [[float(v) for v in p[0][r]] for r in rows]
+                g["Wh" + nm] = [[float(v) for v in p[1][r]] for r in rows]
+                g["bi" + nm] = [float(p[2][r]) if has_bias else 0.0 for r in rows]
+                g["bh" + nm] = [float(p[3][r]) if has_bias else 0.0 for r in rows]
+            hl = []
+            for b in range(B):
+                h = [float(v) for v in h0[l * D + d][b]] if h0 is not None else [0.0] * H
+                order = range(T) if d == 0 else range(T - 1, -1, -1)
+                for t in order:
+                    xi = {nm: _affine(g["Wi" + nm], seq[t][b], g["bi" + nm]) for nm in names}
+                    hh = {nm: _affine(g["Wh" + nm], h, g["bh" + nm]) for nm in names}
+                    if mode == "gru":
+                        r = [_sig(xi["r"][j] + hh["r"][j]) for j in range(H)]
+                        z = [_sig(xi["z"][j] + hh["z"][j]) for j in range(H)]
+                        n = [math.tanh(xi["n"][j] + r[j] * hh["n"][j]) for j in range(H)]
+                        h = [(1.0 - z[j]) * n[j] + z[j] * h[j] for j in range(H)]
+                    elif mode == "rnn_tanh":
+                        h = [math.tanh(xi["a"][j] + hh["a"][j]) for j in range(H)]
+                    else:
+                        h = [max(0.0, xi["a"][j] + hh["a"][j]) for j in range(H)]
+                    out[t][b][d * H:(d + 1) * H] = h
+                hl.append(h)
+            hn.append(hl)
+        seq = out
+    return out, hn

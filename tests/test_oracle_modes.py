@@ -1,0 +1,77 @@
+"""Pins of the oracle's other recurrent modes (GRU, RNN_TANH, RNN_RELU).
+
+The pages name these modes (the trace page's RNNBase takes a mode) without
+their equations; the oracle follows the definitions of the framework whose
+RNNBase that page reproduces.  Pinned by (1) the per-gate scalar brute force
+of tests/brute.py, an independent formulation, and (2) torch.nn.GRU and
+torch.nn.RNN in float64, the framework's own implementations, on stacked
+bidirectional shapes; plus the relu case's closed form without recurrence.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from layer_lstm_forward_amd.synth import Spec, make_inputs
+from tests import brute
+
+MODES = ("gru", "rnn_tanh", "rnn_relu")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("I,H,T,B,L,bidir,bias,state", [(3, 4, 5, 2, 1, False, True, "normal0.1"),
+                                                         (2, 3, 4, 3, 2, True, True, "normal0.1"),
+                                                         (4, 2, 3, 2, 3, True, False, "zeros")])
+def test_modes_match_brute_force(mode, I, H, T, B, L, bidir, bias, state):
+    spec = Spec(I, H, L, bidir, T, B, "f32", 7000 + I + 10 * H + 100 * L, state, has_bias=bias, mode=mode)
+    inp = make_inputs(spec)
+    scale = 2.0  # gates well inside their non-linear ranges
+    params = [p.astype(np.float64) * scale for p in inp.params]
+    y, hn = oracle.rnn_forward(mode, inp.x, params, H, L, bidir, h0=inp.h0, has_bias=bias)
+    ry, rhn = brute.rnn(mode, inp.x.tolist(), [p.tolist() for p in params], H, L, spec.D,
+                        h0=None if inp.h0 is None else inp.h0.tolist(), has_bias=bias)
+    np.testing.assert_allclose(y, np.array(ry), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hn, np.array(rhn), rtol=0, atol=1e-13)
+
+
+def test_relu_without_recurrence_is_a_dense_product():
+    # W_hh = 0, b_hh = 0: every step is relu(W_ih x_t + b_ih), one layer at a time
+    spec = Spec(5, 6, 2, True, 4, 3, "f32", 7101, "normal0.1", mode="rnn_relu")
+    inp = make_inputs(spec)
+    params = [p.astype(np.float64) for p in inp.params]
+    for i in range(len(params)):
+        if i % 4 in (1, 3):
+            params[i] = np.zeros_like(params[i])
+    y, _ = oracle.rnn_forward("rnn_relu", inp.x, params, 6, 2, True, h0=inp.h0)
+    seq = inp.x.astype(np.float64)
+    for l in range(2):
+        outs = [np.maximum(0.0, seq @ params[(2 * l + d) * 4].T + params[(2 * l + d) * 4 + 2]) for d in range(2)]
+        seq = np.concatenate(outs, axis=-1)
+    np.testing.assert_allclose(y, seq, rtol=0, atol=1e-14)
+
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("L,bidir,bias", [(1, False, True), (2, True, True), (3, False, False)])
+def test_modes_match_torch_fp64(mode, L, bidir, bias):
+    I, H, T, B = 7, 9, 6, 4
+    spec = Spec(I, H, L, bidir, T, B, "f32", 7200 + L, "normal0.1", has_bias=bias, mode=mode)
+    inp = make_inputs(spec)
+    if mode == "gru":
+        net = torch.nn.GRU(I, H, L, bias=bias, bidirectional=bidir, dtype=torch.float64)
+    else:
+        net = torch.nn.RNN(I, H, L, nonlinearity=mode[4:], bias=bias, bidirectional=bidir, dtype=torch.float64)
+    per = 4 if bias else 2
+    with torch.no_grad():
+        for l in range(L):
+            for d in range(spec.D):
+                sfx = f"_l{l}" + ("_reverse" if d else "")
+                names = ["weight_ih", "weight_hh"] + (["bias_ih", "bias_hh"] if bias else [])
+                for k, nm in enumerate(names):
+                    getattr(net, nm + sfx).copy_(torch.from_numpy(inp.params[(l * spec.D + d) * per + k]
+                                                                  .astype(np.float64)))
+        ty, thn = net(torch.from_numpy(inp.x.astype(np.float64)), torch.from_numpy(inp.h0.astype(np.float64)))
+    y, hn = oracle.rnn_forward(mode, inp.x, inp.params, H, L, bidir, h0=inp.h0, has_bias=bias)
+    np.testing.assert_allclose(y, ty.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hn, thn.numpy(), rtol=0, atol=1e-12)

@@ -57,10 +57,23 @@ DROPOUT_MUTATIONS = {
     "dropout_gradient_unmasked": ("dY[e] = l > 0 ? dX[e] * dropout_factor(drop_p, seed, call, l - 1, e) : dX[e];",
                                   "dY[e] = dX[e];"),
 }
+# mistakes in the other recurrent modes, checked by tests/test_oracle_modes.py
+MODE_MUTATIONS = {
+    "gru_reset_outside_hidden": ("const double ng = tanh(gi[2 * H + j] + rg * gh[2 * H + j]);",
+                                 "const double ng = tanh(rg * (gi[2 * H + j] + gh[2 * H + j]));"),
+    "gru_update_swapped": ("hv = (1.0 - zg) * ng + zg * state[(size_t)b * H + j];",
+                           "hv = zg * ng + (1.0 - zg) * state[(size_t)b * H + j];"),
+    "gru_r_reads_z_block": ("const double rg = sigmoid(gi[j] + gh[j]);",
+                            "const double rg = sigmoid(gi[H + j] + gh[H + j]);"),
+    "relu_is_identity": ("hv = mode == 2 ? tanh(v) : (v > 0.0 ? v : 0.0);", "hv = mode == 2 ? tanh(v) : v;"),
+    "rnn_hidden_bias_dropped": ("double a = has_bias ? w[2][r] : 0.0, c = has_bias ? w[3][r] : 0.0;",
+                                "double a = has_bias ? w[2][r] : 0.0, c = 0.0;"),
+}
 TARGET = {**{n: "test_oracle_pins.py" for n in MUTATIONS},
+          **{n: "test_oracle_modes.py" for n in MODE_MUTATIONS},
           **{n: "test_oracle_backward.py" for n in BACKWARD_MUTATIONS},
           **{n: "test_oracle_dropout.py" for n in DROPOUT_MUTATIONS}}
-ALL = {**MUTATIONS, **BACKWARD_MUTATIONS, **DROPOUT_MUTATIONS}
+ALL = {**MUTATIONS, **BACKWARD_MUTATIONS, **DROPOUT_MUTATIONS, **MODE_MUTATIONS}
 
 
 @pytest.mark.parametrize("name", sorted(ALL))
