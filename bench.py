@@ -15,6 +15,7 @@ Prints one JSON line.  Besides throughput it reports
                 batch rows of the same workload (rows are independent).
 """
 import argparse
+import dataclasses
 import json
 import re
 import os
@@ -38,19 +39,31 @@ def log(msg):
 def rec_flops_per_launch(spec):
     """Algorithmic FLOPs of one layer's recurrence: 2*B*T*D*4H*H."""
     H = spec.hidden_size
-    return 2.0 * spec.B * spec.T * spec.D * 4 * H * H
+    return 2.0 * spec.B * spec.T * spec.D * spec.gates * H * H
 
 
 def proj_flops_per_launch(spec):
     """Average over layers of 2*T*B*D*4H*in_l (one GEMM launch per layer)."""
     H = spec.hidden_size
-    tot = sum(2.0 * spec.T * spec.B * spec.D * 4 * H * spec.layer_input(l) for l in range(spec.num_layers))
+    tot = sum(2.0 * spec.T * spec.B * spec.D * spec.gates * H * spec.layer_input(l)
+              for l in range(spec.num_layers))
     return tot / spec.num_layers
+
+
+def run_oracle(sub, threads, lengths):
+    import oracle
+    spec = sub.spec
+    if spec.mode != "lstm":
+        return oracle.rnn_forward(spec.mode, sub.x, sub.params, spec.hidden_size, spec.num_layers,
+                                  spec.bidirectional, h0=sub.h0, has_bias=spec.has_bias, bf16=sub.bf16,
+                                  nthreads=threads)
+    return oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
+                               h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads,
+                               lengths=lengths)
 
 
 def cpu_baseline(inp, budget_s, lengths=None):
     import numpy as np
-    import oracle
     spec = inp.spec
     threads = max(1, os.cpu_count() or 1)
     per_row_flops = spec.flops() / spec.B
@@ -58,18 +71,14 @@ def cpu_baseline(inp, budget_s, lengths=None):
     rows = [0]
     t0 = time.perf_counter()
     sub = inp.rows(rows)
-    oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
-                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads,
-                        lengths=None if lengths is None else lengths[rows])
+    run_oracle(sub, threads, None if lengths is None else lengths[rows])
     one = time.perf_counter() - t0
     n = int(max(1, min(spec.B, budget_s / max(one, 1e-6))))
     rows = list(np.linspace(0, spec.B - 1, n).astype(int)) if n > 1 else [0]
     rows = sorted(set(int(r) for r in rows))
     sub = inp.rows(rows)
     t0 = time.perf_counter()
-    oracle.lstm_forward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
-                        h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias, bf16=sub.bf16, nthreads=threads,
-                        lengths=None if lengths is None else lengths[rows])
+    run_oracle(sub, threads, None if lengths is None else lengths[rows])
     wall = time.perf_counter() - t0
     steps = spec.T * len(rows) if lengths is None else int(np.sum(lengths[rows]))
     cells = steps * spec.hidden_size * spec.num_layers * spec.D
@@ -237,6 +246,8 @@ def main():
     ap.add_argument("--lengths", choices=["none", "mix", "ragged"], default="none",
                     help="variable-length rows (lstm_forward_lengths); the value then counts valid cells only")
     ap.add_argument("--batch-first", action="store_true", help="x [B, T, I] and y [B, T, D*H]")
+    ap.add_argument("--mode", choices=["lstm", "gru", "rnn_tanh", "rnn_relu"], default="lstm",
+                    help="recurrent mode (the workload's shape with another cell; forward only)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: lstm_forward_train + lstm_backward")
     args = ap.parse_args()
@@ -253,6 +264,10 @@ def main():
     from layer_lstm_forward_amd.synth import WORKLOADS, make_inputs, make_lengths
 
     spec = WORKLOADS[args.workload]
+    if args.mode != "lstm":
+        if args.train or args.lengths != "none":
+            raise SystemExit("--mode other than lstm: forward only, without --lengths")
+        spec = dataclasses.replace(spec, mode=args.mode)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {args.workload}: generating inputs")
@@ -271,7 +286,7 @@ def main():
     x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if args.batch_first else inp.x)
     w = [to_dev(p) for p in inp.params]
     h0 = to_dev(inp.h0)
-    c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
+    c0 = None if inp.c0 is None or spec.mode != "lstm" else torch.from_numpy(inp.c0).to(dev)
     rec = {"auto": pkg.LSTM_REC_AUTO, "step": pkg.LSTM_REC_STEP, "persistent": pkg.LSTM_REC_PERSISTENT}
     opts = {}
     if args.partial_buffers:
@@ -280,13 +295,14 @@ def main():
         opts[pkg.LSTM_OPT_POLL_SLEEP] = args.poll_sleep
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
                  dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile, options=opts,
-                 batch_first=args.batch_first)
+                 batch_first=args.batch_first, mode=spec.mode)
     desc = m.describe(spec.T, spec.B)
     log(f"schedule: {desc}")
     yshape = (spec.B, spec.T) if args.batch_first else (spec.T, spec.B)
     out = (torch.empty(*yshape, spec.D * spec.hidden_size, dtype=x.dtype, device=dev),
            torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=x.dtype, device=dev),
-           torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev))
+           torch.empty(spec.num_layers * spec.D, spec.B, spec.hidden_size, dtype=torch.float32, device=dev)
+           if spec.mode == "lstm" else None)
     stream = torch.cuda.current_stream(dev)
     if args.train:
         if args.dropout:
@@ -356,7 +372,8 @@ def main():
         cpu = cpu_baseline(inp, args.cpu_budget, lengths)
         log(f"cpu baseline: {cpu}")
 
-    line = {"metric": METRIC, "value": value, "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps,
+    metric = METRIC if spec.mode == "lstm" else METRIC.replace("LSTM", spec.mode.upper(), 1)
+    line = {"metric": metric, "value": value, "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded; random-init weights)",
             "config": {"workload": args.workload, "input_size": spec.input_size, "hidden_size": spec.hidden_size,
@@ -364,7 +381,8 @@ def main():
                        "B": spec.B, "cells_per_step": cells, "schedule": desc,
                        **({} if lengths is None else {"lengths": args.lengths,
                                                        "valid_steps": int(np.sum(lengths))}),
-                       **({"layout": "batch_first"} if args.batch_first else {})},
+                       **({"layout": "batch_first"} if args.batch_first else {}),
+                       **({"cell": spec.mode} if spec.mode != "lstm" else {})},
             "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 

@@ -56,6 +56,18 @@ typedef struct lstm_plan lstm_plan; /* opaque, immutable shape description */
 
 typedef enum { LSTM_F32 = 0, LSTM_BF16 = 1 } lstm_dtype;
 
+/* Recurrent modes.  The trace page's RNNBase ("Complete Trace: nn.LSTM",
+ * Step 1) takes a mode among LSTM, GRU, RNN_TANH and RNN_RELU, and gives the
+ * equations of the LSTM only; the others follow the definitions of the
+ * framework whose RNNBase that page reproduces.  With gi = W_ih x_t + b_ih
+ * and gh = W_hh h + b_hh in H-row blocks:
+ *   GRU (blocks r, z, n):  r = sigma(gi_r + gh_r), z = sigma(gi_z + gh_z),
+ *                          n = tanh(gi_n + r * gh_n), h' = (1 - z) n + z h
+ *   RNN_TANH: h' = tanh(gi + gh);   RNN_RELU: h' = max(0, gi + gh)
+ * W_ih, W_hh and the biases have 3H (GRU) or H (RNN) rows instead of 4H;
+ * there is no cell state. */
+typedef enum { LSTM_MODE_LSTM = 0, LSTM_MODE_GRU = 1, LSTM_MODE_RNN_TANH = 2, LSTM_MODE_RNN_RELU = 3 } lstm_mode;
+
 typedef enum {
     LSTM_OK = 0,
     LSTM_ERR_ARG = -1,         /* NULL/negative argument, num_layers < 1, h0 without c0 */
@@ -130,6 +142,16 @@ typedef struct {
  * 0 or 1.  Touches no device.  *out receives the handle (NULL on error). */
 lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int num_layers,
                         int bidirectional, int has_bias, int dtype);
+
+/* lstm_create for any lstm_mode (lstm_create is mode LSTM_MODE_LSTM); a mode
+ * outside the enum is LSTM_ERR_ARG.  For the GRU and the RNNs, lstm_forward
+ * takes h0 alone (c0 and c_n must be NULL, else LSTM_ERR_ARG), runs one
+ * hoisted projection GEMM and T recurrent-step launches per layer, and needs
+ * hidden_size * element size to be a multiple of 16 bytes and 16-byte aligned
+ * x, y, h0 and weights (LSTM_ERR_UNSUPPORTED otherwise); lstm_forward_lengths,
+ * the training entry points and their size queries are LSTM_ERR_UNSUPPORTED. */
+lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidden_size, int num_layers,
+                             int bidirectional, int has_bias, int dtype);
 
 /* Release a plan (NULL is ignored). */
 void lstm_destroy(lstm_plan *plan);

@@ -57,6 +57,8 @@ def load_library():
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.lstm_create.restype = i
     lib.lstm_create.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i]
+    lib.lstm_create_mode.restype = i
+    lib.lstm_create_mode.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i, i]
     lib.lstm_destroy.restype = None
     lib.lstm_destroy.argtypes = [vp]
     lib.lstm_set_option.restype = i
@@ -109,6 +111,20 @@ def lstm_create(input_size, hidden_size, num_layers, bidirectional, has_bias, dt
                                     int(bool(bidirectional)), int(bool(has_bias)), int(dtype))
     if rc:
         raise LSTMError(rc, "lstm_create")
+    return h.value
+
+
+LSTM_MODE_LSTM, LSTM_MODE_GRU, LSTM_MODE_RNN_TANH, LSTM_MODE_RNN_RELU = 0, 1, 2, 3
+MODES = {"lstm": LSTM_MODE_LSTM, "gru": LSTM_MODE_GRU, "rnn_tanh": LSTM_MODE_RNN_TANH, "rnn_relu": LSTM_MODE_RNN_RELU}
+
+
+def lstm_create_mode(mode, input_size, hidden_size, num_layers, bidirectional, has_bias, dtype):
+    """lstm_create for a recurrent mode (LSTM_MODE_*); returns the plan handle."""
+    h = ctypes.c_void_p()
+    rc = load_library().lstm_create_mode(ctypes.byref(h), int(mode), int(input_size), int(hidden_size),
+                                         int(num_layers), int(bool(bidirectional)), int(bool(has_bias)), int(dtype))
+    if rc:
+        raise LSTMError(rc, "lstm_create_mode")
     return h.value
 
 
@@ -232,14 +248,15 @@ class LSTM:
 
     def __init__(self, input_size, hidden_size, num_layers=1, bidirectional=False, bias=True,
                  dtype="f32", recurrence=LSTM_REC_AUTO, rec_tile=0, options=None, batch_first=False, dropout=0.0,
-                 dropout_seed=0):
+                 dropout_seed=0, mode="lstm"):
         self.input_size, self.hidden_size = int(input_size), int(hidden_size)
         self.num_layers, self.bidirectional, self.bias = int(num_layers), bool(bidirectional), bool(bias)
         self.dtype = dtype
         self.batch_first = bool(batch_first)
         self.D = 2 if self.bidirectional else 1
-        self.plan = lstm_create(input_size, hidden_size, num_layers, bidirectional, bias,
-                                LSTM_BF16 if dtype == "bf16" else LSTM_F32)
+        self.mode = mode
+        self.plan = lstm_create_mode(MODES[mode], input_size, hidden_size, num_layers, bidirectional, bias,
+                                     LSTM_BF16 if dtype == "bf16" else LSTM_F32)
         if recurrence != LSTM_REC_AUTO:
             lstm_set_option(self.plan, LSTM_OPT_RECURRENCE, recurrence)
         if rec_tile:
@@ -290,7 +307,8 @@ class LSTM:
         if out is None:
             y = torch.empty(*((B, T) if self.batch_first else (T, B)), D * H, dtype=tdt, device=x.device)
             hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
-            cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
+            # the GRU and the RNNs have no cell state
+            cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device) if self.mode == "lstm" else None
         else:
             y, hn, cn = out
         ws, nbytes = self.workspace(T, B, x.device)

@@ -66,6 +66,7 @@ struct RecArgs {
     const void *b_ih[2];     // [4H] dtype or NULL
     const void *b_hh[2];
     long long timeout_ticks; // wait timeout in wall_clock64 ticks
+    int mode;                // recurrent mode of k_rec_step: 0 LSTM, 1 GRU, 2 RNN_TANH, 3 RNN_RELU
 };
 
 constexpr int kMaxTeams = 64;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_proj(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + wn * 64 + 16 * j + (lane & 15);
-        bias[j] = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+        bias[j] = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
     }
     const size_t ldg = (size_t)a.D * N;
 #pragma unroll
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void k_proj_big(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + wn * 128 + 32 * j + (lane & 31);
-        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + wn * 128 + 32 * j + (lane & 31);
-        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + DT::to_f(bh[n]) : 0.f;
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1231,12 +1231,20 @@ __global__ __launch_bounds__(256) void k_rec_pipe(PipeArgs a) {
 // per-step traffic is bounded by the L2-to-CU bandwidth, (BM + 128) rows of
 // K per workgroup: taller blocks read less in total, shorter ones spread the
 // products over more CUs.  c is carried across launches in cstate.
+//
+// The other recurrent modes of the trace page's RNNBase (MODE 1 GRU, 2
+// RNN_TANH, 3 RNN_RELU) run through the same kernel with NG = 3 or 1 gate
+// blocks (BR = 32 NG rows of W_hh per block) and their own update: G holds
+// x W_ih^T + b_ih only, and b_hh is added here, because the GRU's candidate
+// multiplies its hidden contribution, bias included, by the reset gate.
+// Their state is h alone, read back from y of the previous step.
 // ===========================================================================
-template <class DT, int WM>
+template <class DT, int WM, int MODE>
 __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     using S = typename DT::S;
+    constexpr int NG = MODE == 0 ? 4 : MODE == 1 ? 3 : 1;  // gate blocks
     constexpr int WKS = 4 / WM;                  // K slices
-    constexpr int BM = 32 * WM, BR = 128, SEG = 8;  // A rows, W rows per block; segments per row
+    constexpr int BM = 32 * WM, BR = 32 * NG, SEG = 8;  // A rows, W rows per block; segments per row
     constexpr int KS = SEG * DT::PER16;          // K per stage
     constexpr int STAGE = (BM + BR) * SEG;       // 16-byte segments per stage
     constexpr int NST = WM == 4 ? 4 : 5;         // stages in the LDS ring
@@ -1269,11 +1277,11 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     const int b0 = mb * BM, u0 = ub * 32;
     const int es = (int)sizeof(S);
     const size_t ldy = (size_t)D * H;
-    const size_t ldg = (size_t)D * 4 * H;
+    const size_t ldg = (size_t)D * NG * H;
 
-    f32x16 acc[4];
+    f32x16 acc[NG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NG; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 
@@ -1293,7 +1301,7 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         const unsigned abytes = (unsigned)((((size_t)rows - 1) * lda + H) * es);
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(hsrc), (short)0, (int)abytes, 0x00020000);
         const S *W = static_cast<const S *>(a.whh[d]);
-        const unsigned wbytes = (unsigned)((size_t)4 * H * H * es);
+        const unsigned wbytes = (unsigned)((size_t)NG * H * H * es);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
 
         // this lane's slot in each 1 KiB block: row (lane / 8) of the block, swizzled segment (lane % 8)
@@ -1343,18 +1351,18 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
             // this wave's 32-byte sub-chunks of the stage: wk, wk + WKS, ...
             constexpr int NC = 4 / WKS;
-            u32x4 af[NC], bw[NC][4];
+            u32x4 af[NC], bw[NC][NG];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int sg = 2 * (wk + WKS * c) + (lane >> 5);
                 af[c] = sa[swz(wm * 32 + (lane & 31), sg)];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bw[c][j] = sb[swz(32 * j + (lane & 31), sg)];
+                for (int j = 0; j < NG; ++j) bw[c][j] = sb[swz(32 * j + (lane & 31), sg)];
             }
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = mma32_chunk(DT{}, acc[j], af[c], bw[c][j]);
+                for (int j = 0; j < NG; ++j) acc[j] = mma32_chunk(DT{}, acc[j], af[c], bw[c][j]);
         }
         __syncthreads();  // the stage buffers are reused below
     }
@@ -1366,7 +1374,7 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     const int partner = wm + WM * (1 - wk);
     if (WKS == 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NG; ++j)
 #pragma unroll
             for (int vv = 0; vv < 8; ++vv) red[((size_t)w * 32 + j * 8 + vv) * 64 + lane] = acc[j][8 * (1 - wk) + vv];
         __syncthreads();
@@ -1378,39 +1386,61 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         const int v = VPW * wk + vv;
         const int m = b0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m >= B || u >= H) continue;
-        float pre[4];
+        float pre[NG];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NG; ++j)
             pre[j] = acc[j][v] + (WKS == 2 ? red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane] : 0.f);
-        const float *g = a.G + trow(t, m, T, B, a.bfirst) * ldg + (size_t)d * 4 * H + u;
+        const float *g = a.G + trow(t, m, T, B, a.bfirst) * ldg + (size_t)d * NG * H + u;
         const size_t si = ((size_t)d * B + m) * H + u;
-        const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
-        const float ig = sigmoid_f(pre[0] + g[0]);
-        const float fg = sigmoid_f(pre[1] + g[(size_t)H]);
-        const float gg = tanh_f(pre[2] + g[(size_t)2 * H]);
-        const float og = sigmoid_f(pre[3] + g[(size_t)3 * H]);
-        float cn = fg * cp + ig * gg;
-        S hs = DT::from_f(og * tanh_f(cn));
-        if (a.len && t >= a.len[m]) {
-            // padded step of this row: the state stays; y carries the unchanged
-            // h because the next step reads h_{t-1} from y (padded outputs are
-            // zeroed after the last layer)
-            cn = cp;
-            hs = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
-        }
-        a.cstate[si] = cn;
-        if (a.acts) {  // training: the activations the backward pass needs
-            float *ap = a.acts + (((size_t)t * B + m) * D + d) * 5 * H + u;
-            ap[0] = ig;
-            ap[(size_t)H] = fg;
-            ap[(size_t)2 * H] = gg;
-            ap[(size_t)3 * H] = og;
-            ap[(size_t)4 * H] = cn;
-        }
-        static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
-        if (last) {
-            if (a.hn) static_cast<S *>(a.hn)[si] = hs;
-            if (a.cn) a.cn[si] = cn;
+        if constexpr (MODE != 0) {
+            // hidden contributions with b_hh; h_{t-1} of this cell for the GRU
+            const S *bh = static_cast<const S *>(a.b_hh[d]);
+#pragma unroll
+            for (int j = 0; j < NG; ++j) pre[j] += bh ? DT::to_f(bh[(size_t)j * H + u]) : 0.f;
+            const S hprev = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
+            float hv;
+            if constexpr (MODE == 1) {
+                const float rg = sigmoid_f(g[0] + pre[0]);
+                const float zg = sigmoid_f(g[(size_t)H] + pre[1]);
+                const float ng = tanh_f(g[(size_t)2 * H] + rg * pre[2]);
+                hv = (1.f - zg) * ng + zg * DT::to_f(hprev);
+            } else if constexpr (MODE == 2) {
+                hv = tanh_f(g[0] + pre[0]);
+            } else {
+                hv = fmaxf(g[0] + pre[0], 0.f);
+            }
+            const S hs = DT::from_f(hv);
+            static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
+            if (last && a.hn) static_cast<S *>(a.hn)[si] = hs;
+        } else {
+            const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
+            const float ig = sigmoid_f(pre[0] + g[0]);
+            const float fg = sigmoid_f(pre[1] + g[(size_t)H]);
+            const float gg = tanh_f(pre[2] + g[(size_t)2 * H]);
+            const float og = sigmoid_f(pre[3] + g[(size_t)3 * H]);
+            float cn = fg * cp + ig * gg;
+            S hs = DT::from_f(og * tanh_f(cn));
+            if (a.len && t >= a.len[m]) {
+                // padded step of this row: the state stays; y carries the unchanged
+                // h because the next step reads h_{t-1} from y (padded outputs are
+                // zeroed after the last layer)
+                cn = cp;
+                hs = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
+            }
+            a.cstate[si] = cn;
+            if (a.acts) {  // training: the activations the backward pass needs
+                float *ap = a.acts + (((size_t)t * B + m) * D + d) * 5 * H + u;
+                ap[0] = ig;
+                ap[(size_t)H] = fg;
+                ap[(size_t)2 * H] = gg;
+                ap[(size_t)3 * H] = og;
+                ap[(size_t)4 * H] = cn;
+            }
+            static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
+            if (last) {
+                if (a.hn) static_cast<S *>(a.hn)[si] = hs;
+                if (a.cn) a.cn[si] = cn;
+            }
         }
     }
 }
@@ -1658,7 +1688,8 @@ bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
     // the A rows of one block (y of the previous step) must be addressable by
     // one buffer resource: 127 row strides, T rows apart when batch_first
     const size_t astride = (size_t)a.D * a.H * (a.bfirst ? (size_t)a.T : 1);
-    bool ok = ((size_t)a.H * es) % 16 == 0 && (size_t)4 * a.H * a.H * es < (1u << 31) &&
+    const size_t ng = a.mode == 0 ? 4 : a.mode == 1 ? 3 : 1;
+    bool ok = ((size_t)a.H * es) % 16 == 0 && ng * a.H * a.H * es < (1u << 31) &&
               ((size_t)128 * astride * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
               (!a.h0 || (uintptr_t)a.h0 % 16 == 0);
     for (int d = 0; d < a.D; ++d) ok = ok && (uintptr_t)a.whh[d] % 16 == 0;
@@ -1669,10 +1700,14 @@ bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
 // less in total) at B = 256 -- each CU's load rate is the limit.
 int rec_step_rows(int) { return 64; }
 
-template <class DT, int WM>
+template <class DT, int WM, int MODE>
 static hipError_t launch_step_t(const RecArgs &a, hipStream_t s) {
-    const void *fn = reinterpret_cast<const void *>(&k_rec_step<DT, WM>);
-    const size_t smem = (size_t)(WM == 4 ? 4 : 5) * (32 * WM + 128) * 8 * 16;
+    const void *fn = reinterpret_cast<const void *>(&k_rec_step<DT, WM, MODE>);
+    constexpr int NG = MODE == 0 ? 4 : MODE == 1 ? 3 : 1;
+    // the stage ring, and at least the K-slice exchange of the epilogue
+    const size_t ring = (size_t)(WM == 4 ? 4 : 5) * (32 * WM + 32 * NG) * 8 * 16;
+    const size_t red = WM == 2 ? (size_t)4 * 32 * 64 * sizeof(float) : 0;
+    const size_t smem = ring > red ? ring : red;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     const int bm = 32 * WM;
@@ -1682,9 +1717,20 @@ static hipError_t launch_step_t(const RecArgs &a, hipStream_t s) {
     return hipLaunchKernel(fn, grid, block, args, smem, s);
 }
 
+template <class DT>
+static hipError_t launch_step_mode(const RecArgs &a, hipStream_t s) {
+    switch (a.mode) {
+        case 0: return launch_step_t<DT, 2, 0>(a, s);
+        case 1: return launch_step_t<DT, 2, 1>(a, s);
+        case 2: return launch_step_t<DT, 2, 2>(a, s);
+        case 3: return launch_step_t<DT, 2, 3>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s) {
-    if (dtype == DT_BF16) return launch_step_t<BF16, 2>(a, s);
-    return launch_step_t<F32, 2>(a, s);
+    if (dtype == DT_BF16) return launch_step_mode<BF16>(a, s);
+    return launch_step_mode<F32>(a, s);
 }
 
 hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first,

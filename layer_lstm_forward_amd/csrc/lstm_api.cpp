@@ -27,6 +27,8 @@ struct lstm_plan {
     int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
+    int mode;          // LSTM_MODE_*
+    int NG;            // gate blocks of H rows: 4 (LSTM), 3 (GRU), 1 (RNN)
     // training dropout between layers (lstm_set_dropout)
     double dropout;                 // probability, 0 = none
     unsigned long long drop_seed;   // generator key
@@ -95,7 +97,7 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
             return false;
         if (pb > xb) xb = pb;
     }
-    if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
+    if (!mul_ok(tb, (size_t)p->D * p->NG * p->H * sizeof(float), &g)) return false;
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
     size_t off = 0;
@@ -477,7 +479,8 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
     if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
     if ((long long)T * B > INT_MAX) return LSTM_ERR_SHAPE;
     if (!x || !y || !weights) return LSTM_ERR_ARG;
-    if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
+    // the LSTM's initial state is a pair; the other modes have no cell state
+    if (p->mode == LSTM_MODE_LSTM ? (h0 == nullptr) != (c0 == nullptr) : c0 != nullptr) return LSTM_ERR_ARG;
     const int per = p->has_bias ? 4 : 2;
     for (int i = 0; i < p->L * p->D * per; ++i)
         if (!weights[i]) return LSTM_ERR_ARG;
@@ -490,7 +493,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 105; }
+int lstm_version(void) { return 106; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -509,8 +512,15 @@ const char *lstm_strerror(int s) {
 
 lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int num_layers,
                         int bidirectional, int has_bias, int dtype) {
+    return lstm_create_mode(out, LSTM_MODE_LSTM, input_size, hidden_size, num_layers, bidirectional, has_bias,
+                            dtype);
+}
+
+lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidden_size, int num_layers,
+                             int bidirectional, int has_bias, int dtype) {
     if (!out) return LSTM_ERR_ARG;
     *out = nullptr;
+    if (mode < LSTM_MODE_LSTM || mode > LSTM_MODE_RNN_RELU) return LSTM_ERR_ARG;
     if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
     if (input_size < 1 || hidden_size < 1 || num_layers < 1) return LSTM_ERR_ARG;
     if ((bidirectional != 0 && bidirectional != 1) || (has_bias != 0 && has_bias != 1)) return LSTM_ERR_ARG;
@@ -532,6 +542,8 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
     p->layer_pipe = 0;
     p->fuse_input = 1;
     p->batch_first = 0;
+    p->mode = mode;
+    p->NG = mode == LSTM_MODE_LSTM ? 4 : mode == LSTM_MODE_GRU ? 3 : 1;
     p->dropout = 0.0;
     p->drop_seed = 0;
     p->drop_call = 0;
@@ -663,11 +675,20 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
         (void)hipGetLastError();
         return LSTM_ERR_DEVICE;
     }
+    const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
+    const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
+    if (p->mode != LSTM_MODE_LSTM) {
+        static const char *names[] = {"lstm", "gru", "rnn_tanh", "rnn_relu"};
+        const int bm = rec_step_rows(B);
+        std::snprintf(buf, len,
+                      "cell=%s proj=%s<%s>; rec=k_rec_step<%s> mode=gemm-step block=%dx32 workgroups=%d launches=T%s",
+                      names[p->mode], proj_kernel_name(T * B, p->NG * p->H, in0, p->D, p->dtype, p->proj_tile), dt, dt,
+                      bm, ((B + bm - 1) / bm) * ((p->H + 31) / 32) * p->D, p->batch_first ? " layout=batch-first" : "");
+        return LSTM_OK;
+    }
     Sched s{};
     const int rc = choose_sched(p, B, dev, &s);
     if (rc != LSTM_OK) return (lstm_status)rc;
-    const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
-    const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
     const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
     PipeSched ps{};
     if (choose_pipe(p, B, dev, &ps)) {
@@ -996,6 +1017,91 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     return LSTM_OK;
 }
 
+// The forward pass of the GRU and the plain RNNs: per layer the hoisted
+// projection G = X W_ih^T + b_ih (both directions), then one k_rec_step launch
+// per step, which adds W_hh h_{t-1} + b_hh and applies the mode's update.
+lstm_status forward_modes(lstm_plan *p, const void *x, const void *h0, const void *const *weights, int T, int B,
+                          int layers, int bidir, void *y, void *h_n, const float *c_n, void *workspace,
+                          size_t workspace_bytes, void *stream_) {
+    Layout lay;
+    int rc = validate(p, x, h0, nullptr, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
+    if (rc != LSTM_OK) return (lstm_status)rc;
+    if (c_n) return LSTM_ERR_ARG;  // no cell state
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    const int per = p->has_bias ? 4 : 2;
+    const void *ptrs[] = {x, y, workspace, h0, h_n};
+    for (const void *q : ptrs)
+        if (q && !is_device_ptr(q, dev)) return LSTM_ERR_DEVICE;
+    for (int i = 0; i < p->L * p->D * per; ++i)
+        if (!is_device_ptr(weights[i], dev)) return LSTM_ERR_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream_);
+    char *ws = static_cast<char *>(workspace);
+    float *G = reinterpret_cast<float *>(ws + lay.G);
+    const size_t es = elem_size(p->dtype), state_elems = (size_t)p->D * B * p->H;
+    auto layer_args = [&](int l) {
+        RecArgs ra{};
+        for (int d = 0; d < p->D; ++d) {
+            const void *const *w = weights + (size_t)(l * p->D + d) * per;
+            ra.whh[d] = w[1];
+            ra.b_hh[d] = p->has_bias ? w[3] : nullptr;
+        }
+        ra.G = G;
+        ra.h0 = h0 ? static_cast<const char *>(h0) + (size_t)l * state_elems * es : nullptr;
+        ra.Y = l == p->L - 1 ? y : static_cast<void *>(ws + lay.ymid[l & 1]);
+        ra.hn = h_n ? static_cast<char *>(h_n) + (size_t)l * state_elems * es : nullptr;
+        ra.T = T;
+        ra.B = B;
+        ra.H = p->H;
+        ra.D = p->D;
+        ra.bfirst = p->batch_first;
+        ra.mode = p->mode;
+        return ra;
+    };
+    // every layer's operands must suit the per-step kernel: checked before anything is enqueued
+    for (int l = 0; l < p->L; ++l)
+        if (!rec_step_gemm_ok(layer_args(l), p->dtype)) return LSTM_ERR_UNSUPPORTED;
+    for (int l = 0; l < p->L; ++l) {
+        const void *X = l == 0 ? x : static_cast<const void *>(ws + lay.ymid[(l - 1) & 1]);
+        const int in_l = l == 0 ? p->I : p->D * p->H;
+        ProjArgs pa{};
+        pa.X = X;
+        pa.G = G;
+        pa.M = T * B;
+        pa.N = p->NG * p->H;
+        pa.K = in_l;
+        pa.ldx = in_l;
+        pa.D = p->D;
+        for (int d = 0; d < p->D; ++d) {
+            const void *const *w = weights + (size_t)(l * p->D + d) * per;
+            pa.W[d] = w[0];
+            pa.b_ih[d] = p->has_bias ? w[2] : nullptr;  // b_hh joins in the step
+        }
+        int span = span_begin(p, st, 0);
+        if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return LSTM_ERR_LAUNCH;
+        }
+        span_end(p, span, st, 1);
+        RecArgs ra = layer_args(l);
+        span = span_begin(p, st, 1);
+        for (int s = 0; s < T; ++s) {
+            ra.s_begin = s;
+            ra.s_end = s + 1;
+            if (launch_rec_step_gemm(ra, p->dtype, st) != hipSuccess) {
+                (void)hipGetLastError();
+                return LSTM_ERR_LAUNCH;
+            }
+        }
+        span_end(p, span, st, T);
+    }
+    if (p->timing) p->acc.calls += 1;
+    return LSTM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1003,12 +1109,18 @@ extern "C" {
 lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
                          const void *const *weights, int T, int B, int layers, int bidir, void *y,
                          void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
+    if (p && p->mode != LSTM_MODE_LSTM) {
+        if (c0) return LSTM_ERR_ARG;  // no cell state
+        return forward_modes(p, x, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace, workspace_bytes,
+                             stream);
+    }
     return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                         workspace_bytes, stream);
 }
 
 lstm_status lstm_reserve_size(const lstm_plan *p, int T, int B, size_t *bytes) {
     if (!p || !bytes) return LSTM_ERR_ARG;
+    if (p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     ReserveLayout rl{};
     if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
     *bytes = rl.total;
@@ -1020,7 +1132,7 @@ lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, cons
                                void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
                                size_t workspace_bytes, void *stream) {
     if (!p || !reserve) return LSTM_ERR_ARG;
-    if (p->batch_first) return LSTM_ERR_UNSUPPORTED;
+    if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     ReserveLayout rl{};
     if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
     if (reserve_bytes < rl.total) return LSTM_ERR_WORKSPACE;
@@ -1038,6 +1150,7 @@ lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, cons
 
 lstm_status lstm_backward_workspace_size(const lstm_plan *p, int T, int B, size_t *bytes) {
     if (!p || !bytes) return LSTM_ERR_ARG;
+    if (p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     BwdLayout bl{};
     if (!make_bwd_layout(p, T, B, &bl)) return LSTM_ERR_SHAPE;
     *bytes = bl.total;
@@ -1052,7 +1165,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     if (!p || !x || !weights || !y || !dy || !reserve || !dweights || !workspace) return LSTM_ERR_ARG;
     if (layers != p->L || (bidir != 0) != (p->D == 2) || T < 1 || B < 1) return LSTM_ERR_SHAPE;
     if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
-    if (p->batch_first) return LSTM_ERR_UNSUPPORTED;
+    if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     const int per = p->has_bias ? 4 : 2;
     for (int i = 0; i < p->L * p->D * per; ++i)
         if (!weights[i] || !dweights[i]) return LSTM_ERR_ARG;
@@ -1228,6 +1341,7 @@ lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths
                                  int bidir, void *y, void *h_n, float *c_n, void *workspace,
                                  size_t workspace_bytes, void *stream) {
     if (!lengths) return LSTM_ERR_ARG;
+    if (p && p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
     for (int b = 0; b < B; ++b)
         if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;

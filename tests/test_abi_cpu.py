@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 105
+    assert pkg.lstm_version() == 106
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -206,3 +206,35 @@ def test_dropout_settings_and_reserve_size():
         assert pkg.lstm_reserve_size(p, 4, 2) == base
     finally:
         pkg.lstm_destroy(p)
+
+
+def test_modes_create_and_validate():
+    # mode outside the enum; the GRU's projection is 3H wide, the RNNs' H
+    h = ctypes.c_void_p()
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    assert lib.lstm_create_mode(ctypes.byref(h), 4, 8, 16, 1, 0, 1, 0) == -1
+    assert lib.lstm_create_mode(ctypes.byref(h), -1, 8, 16, 1, 0, 1, 0) == -1
+    sizes = {}
+    for name, mode in pkg.MODES.items():
+        p = pkg.lstm_create_mode(mode, 24, 32, 2, True, True, pkg.LSTM_F32)
+        try:
+            sizes[name] = pkg.lstm_workspace_size(p, 10, 8)
+            if mode != pkg.LSTM_MODE_LSTM:
+                FAKE = 0x10000
+                # c0 (and c_n) belong to the LSTM only; validation precedes any device access
+                rc = pkg.lstm_forward(p, FAKE, FAKE, FAKE, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0, FAKE, 1 << 40, 0)
+                assert rc == -1
+                rc = pkg.lstm_forward_lengths(p, FAKE, [3] * 8, 0, 0, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0, FAKE,
+                                              1 << 40, 0)
+                assert rc == -7
+                with pytest.raises(pkg.LSTMError):
+                    pkg.lstm_reserve_size(p, 10, 8)
+                with pytest.raises(pkg.LSTMError):
+                    pkg.lstm_backward_workspace_size(p, 10, 8)
+        finally:
+            pkg.lstm_destroy(p)
+    # G is [T*B, D*NG*H] fp32: the workspaces differ by exactly that
+    g = 10 * 8 * 2 * 32 * 4
+    assert sizes["lstm"] - sizes["gru"] == g
+    assert sizes["gru"] - sizes["rnn_tanh"] == 2 * g
+    assert sizes["rnn_tanh"] == sizes["rnn_relu"]

@@ -1,0 +1,106 @@
+"""The GRU, RNN_TANH and RNN_RELU forward (lstm_create_mode, through the C ABI)
+against the fp64 oracle's oracle_rnn_forward on the same seeded inputs.
+
+Max-abs error relative to the output's scale, max(1, max|ref|) (the relu RNN
+is unbounded): 1e-4 for fp32, 2e-2 for bf16, the LSTM forward's bounds.
+"""
+import numpy as np
+import pytest
+
+import layer_lstm_forward_amd as pkg
+import oracle
+from layer_lstm_forward_amd.synth import Spec, make_inputs
+from tests.gpu_util import oracle_threads, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+MODES = ("gru", "rnn_tanh", "rnn_relu")
+
+SHAPES = [  # input, hidden, layers, bidirectional, T, B, dtype, state, bias
+    (24, 32, 1, False, 9, 11, "f32", "normal0.1", True),
+    (40, 64, 2, True, 13, 70, "f32", "normal0.1", True),     # rows over two 64-row blocks, two layers
+    (16, 40, 3, True, 5, 3, "f32", "zeros", False),          # three layers, no bias, no initial state
+    (64, 96, 2, False, 7, 20, "bf16", "normal0.1", True),
+    (32, 136, 1, True, 6, 130, "bf16", "zeros", True),       # units over five 32-unit blocks, ragged
+]
+
+
+def _run(spec, inp, batch_first=False, rows=None):
+    import torch
+    bf = spec.dtype == "bf16"
+    dev = "cuda:0"
+    m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
+                 dtype=spec.dtype, mode=spec.mode, batch_first=batch_first)
+    x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if batch_first else inp.x, bf, dev)
+    w = [to_dev(p, bf, dev) for p in inp.params]
+    h0 = to_dev(inp.h0, bf, dev)
+    y, hn, cn = m.forward(x, w, h0)
+    torch.cuda.synchronize()
+    assert cn is None
+    y = y.float().cpu().numpy().astype(np.float64)
+    if batch_first:
+        y = np.ascontiguousarray(y.transpose(1, 0, 2))
+    return y, hn.float().cpu().numpy().astype(np.float64)
+
+
+def _check(got, ref, dtype, what):
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= TOL[dtype] * scale, f"{what}: max-abs error {err:.3g} > {TOL[dtype]} x {scale:.3g}"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[6]}-I{s[0]}-H{s[1]}-L{s[2]}-D{2 if s[3] else 1}"
+                                                        f"-T{s[4]}-B{s[5]}")
+def test_mode_matches_oracle(mode, shape):
+    I, H, L, bidir, T, B, dtype, state, bias = shape
+    spec = Spec(I, H, L, bidir, T, B, dtype, 900 + H + L, state, has_bias=bias, mode=mode)
+    print(f"case {mode} {shape}", flush=True)
+    inp = make_inputs(spec)
+    y, hn = _run(spec, inp)
+    ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, H, L, bidir, h0=inp.h0, has_bias=bias,
+                                 bf16=dtype == "bf16", nthreads=oracle_threads())
+    _check(y, ry, dtype, "y")
+    _check(hn, rhn, dtype, "h_n")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mode_batch_first(mode):
+    spec = Spec(24, 64, 2, True, 7, 21, "f32", 960, "normal0.1", mode=mode)
+    print(f"case {mode} batch_first", flush=True)
+    inp = make_inputs(spec)
+    y, hn = _run(spec, inp, batch_first=True)
+    ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, 64, 2, True, h0=inp.h0, nthreads=oracle_threads())
+    _check(y, ry, "f32", "y")
+    _check(hn, rhn, "f32", "h_n")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mode_full_size_sampled_rows(mode):
+    # the benchmark workload's shape (in 256, H 512, T 128, B 64, two layers,
+    # fp32) in the GRU / RNN mode, checked on a sample of batch rows (rows
+    # are independent), in the launch configuration the benchmark times
+    spec = Spec(256, 512, 2, False, 128, 64, "f32", 1002, "normal0.1", mode=mode)
+    print(f"case {mode} full size", flush=True)
+    inp = make_inputs(spec)
+    y, hn = _run(spec, inp)
+    rows = [0, 17, 42, 63]
+    sub = inp.rows(rows)
+    ry, rhn = oracle.rnn_forward(mode, sub.x, sub.params, 512, 2, False, h0=sub.h0, nthreads=oracle_threads())
+    _check(y[:, rows], ry, "f32", "y")
+    _check(hn[:, rows], rhn, "f32", "h_n")
+
+
+def test_mode_rejects_cell_state_and_lengths():
+    import torch
+    spec = Spec(8, 32, 1, False, 4, 2, "f32", 970, "normal0.1", mode="gru")
+    inp = make_inputs(spec)
+    m = pkg.LSTM(8, 32, 1, False, mode="gru")
+    x = to_dev(inp.x, False, "cuda:0")
+    w = [to_dev(p, False, "cuda:0") for p in inp.params]
+    h0 = to_dev(inp.h0, False, "cuda:0")
+    c0 = torch.zeros(1, 2, 32, device="cuda:0")
+    with pytest.raises(pkg.LSTMError):
+        m.forward(x, w, h0, c0)
+    with pytest.raises(pkg.LSTMError):
+        m.forward(x, w, h0, lengths=[4, 2])
