@@ -188,6 +188,14 @@ hipError_t launch_dropout_bwd(float *g, const unsigned char *keep, size_t n, flo
 // Zero the y row of (t, b) for every t >= len[b] (padded steps of variable-length rows).
 hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_bytes, bool batch_first, hipStream_t s);
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s);
+// Row-padded parameter copies: dst (rows x cols, dtype) = the first `valid`
+// rows of src (row-major, cols wide), zeros below.  Any number of jobs.
+struct PadJob {
+    const void *src;
+    void *dst;
+    int valid, rows, cols;
+};
+hipError_t launch_pad_rows(const PadJob *jobs, int n, int dtype, hipStream_t s);
 // One recurrent step (a.s_begin) as a GEMM with the cell update fused
 // (k_rec_step); reads h_{t-1} from a.Y / a.h0 and carries c in a.cstate.
 // rec_step_gemm_ok: its alignment and 31-bit offset requirements hold.

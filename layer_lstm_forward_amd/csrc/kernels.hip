@@ -504,9 +504,11 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
     // adjacent units of one row.
     // With per-row lengths a cell is active at time t only if t < its row's
     // length; otherwise c and h stay as they are (hreg keeps h), y gets 0.
+    // The GRU (a.mode 1) also needs its cell's h_{t-1} in hreg, and b_hn.
     int cm[CPT], cu[CPT], clen[CPT];
     bool cv[CPT];
-    float creg[CPT], hreg[CPT];
+    float creg[CPT], hreg[CPT], bhn[CPT];
+    const bool keep_h = a.len || a.mode == 1;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int e = tid + 256 * i;
@@ -515,17 +517,19 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
         cv[i] = e < CELLS && cm[i] < rows && cu[i] < units;
         creg[i] = 0.f;
         hreg[i] = 0.f;
+        bhn[i] = 0.f;
         clen[i] = T;
         if (cv[i]) {
             const size_t si = ((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i];
             if (a.s_begin == 0) {
                 creg[i] = a.c0 ? a.c0[si] : 0.f;
-                if (a.len && a.h0) hreg[i] = DT::to_f(static_cast<const S *>(a.h0)[si]);
+                if (keep_h && a.h0) hreg[i] = DT::to_f(static_cast<const S *>(a.h0)[si]);
             } else {
                 creg[i] = a.cstate[si];
-                if (a.len) hreg[i] = a.hstate[si];
+                if (keep_h) hreg[i] = a.hstate[si];
             }
             if (a.len) clen[i] = a.len[b0 + cm[i]];
+            if (a.mode == 1 && a.b_hh[d]) bhn[i] = DT::to_f(static_cast<const S *>(a.b_hh[d])[(size_t)2 * H + j0 + cu[i]]);
         }
     }
     if (tid == 0) s_bad = 0;
@@ -805,12 +809,26 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                     if constexpr (FUSED) pre[q] = bias[i][q];
                     else pre[q] = gcur[i][q];
                 }
-                const float ig = sigmoid_f(sum.x + pre[0]);
-                const float fg = sigmoid_f(sum.y + pre[1]);
-                const float gg = tanh_f(sum.z + pre[2]);
-                const float og = sigmoid_f(sum.w + pre[3]);
-                float cn = fg * creg[i] + ig * gg;
-                hv = og * tanh_f(cn);
+                float ig = 0.f, fg = 0.f, gg = 0.f, og = 0.f, cn = creg[i];
+                if (a.mode == 0) {
+                    ig = sigmoid_f(sum.x + pre[0]);
+                    fg = sigmoid_f(sum.y + pre[1]);
+                    gg = tanh_f(sum.z + pre[2]);
+                    og = sigmoid_f(sum.w + pre[3]);
+                    cn = fg * creg[i] + ig * gg;
+                    hv = og * tanh_f(cn);
+                } else if (a.mode == 1) {
+                    // GRU on gate slots r, z, n (the fourth is empty): G holds
+                    // x W_ih^T + b_ih + (b_hr, b_hz, 0); b_hn joins the hidden term
+                    const float rg = sigmoid_f(sum.x + pre[0]);
+                    const float zg = sigmoid_f(sum.y + pre[1]);
+                    const float ng = tanh_f(pre[2] + rg * (sum.z + bhn[i]));
+                    hv = (1.f - zg) * ng + zg * hreg[i];
+                } else {
+                    // plain RNN on the first gate slot
+                    const float v = sum.x + pre[0];
+                    hv = a.mode == 2 ? tanh_f(v) : fmaxf(v, 0.f);
+                }
                 if (t >= clen[i]) {  // padded step of this row: keep the state
                     cn = creg[i];
                     hv = hreg[i];
@@ -874,7 +892,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             if (cv[i]) {
                 const size_t si = ((size_t)d * B + b0 + cm[i]) * H + j0 + cu[i];
                 a.cstate[si] = creg[i];
-                if (a.len) a.hstate[si] = hreg[i];
+                if (keep_h) a.hstate[si] = hreg[i];
             }
     }
 }
@@ -1741,6 +1759,45 @@ hipError_t launch_mask_padded(void *y, const int *len, int T, int B, size_t row_
     hipLaunchKernelGGL(k_mask_padded, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t *>(y), len, T, B,
                        row_bytes / 2, batch_first ? 1 : 0);
     return hipGetLastError();
+}
+
+// Parameter copies padded with zero rows (the GRU and the plain RNNs run on
+// the LSTM's four gate slots): job blockIdx.y copies its first valid*cols
+// elements and zeroes the rest of rows*cols.
+constexpr int kPadJobs = 32;
+struct PadBatch {
+    PadJob j[kPadJobs];
+};
+template <class DT>
+__global__ void k_pad_rows(PadBatch a) {
+    using S = typename DT::S;
+    const PadJob jb = a.j[blockIdx.y];
+    const S *src = static_cast<const S *>(jb.src);
+    S *dst = static_cast<S *>(jb.dst);
+    const size_t n = (size_t)jb.rows * jb.cols, nv = (size_t)jb.valid * jb.cols;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        dst[e] = e < nv ? src[e] : (S)0;
+}
+
+hipError_t launch_pad_rows(const PadJob *jobs, int n, int dtype, hipStream_t s) {
+    for (int j0 = 0; j0 < n; j0 += kPadJobs) {
+        PadBatch b{};
+        const int m = n - j0 < kPadJobs ? n - j0 : kPadJobs;
+        size_t most = 0;
+        for (int k = 0; k < m; ++k) {
+            b.j[k] = jobs[j0 + k];
+            if (b.j[k].valid < 0 || b.j[k].valid > b.j[k].rows) return hipErrorInvalidValue;
+            const size_t e = (size_t)b.j[k].rows * b.j[k].cols;
+            most = e > most ? e : most;
+        }
+        const unsigned gx = (unsigned)((most + 255) / 256 < 1024 ? (most + 255) / 256 : 1024);
+        dim3 grid(gx < 1 ? 1 : gx, (unsigned)m);
+        if (dtype == DT_BF16) hipLaunchKernelGGL(k_pad_rows<BF16>, grid, dim3(256), 0, s, b);
+        else hipLaunchKernelGGL(k_pad_rows<F32>, grid, dim3(256), 0, s, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fill_u32(unsigned *p, size_t n, unsigned v, hipStream_t s) {

@@ -54,6 +54,7 @@ constexpr size_t kAlign = 256;
 constexpr size_t kStatusBytes = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool use_persistent_for_mode(const lstm_plan *p, int B);
 size_t elem_size(int dtype) { return dtype == LSTM_BF16 ? 2 : 4; }
 
 // Checked products; false on size_t overflow.
@@ -64,7 +65,7 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 }
 
 struct Layout {
-    size_t status, xbuf, G, ymid[2], cstate, hstate, lens, total;
+    size_t status, xbuf, G, ymid[2], cstate, hstate, lens, wpad, total;
     size_t sync_bytes;  // status word + exchange buffer, zeroed per call
     size_t pipe_tiles;  // bound on the 16-row tiles of a pipelined schedule
 };
@@ -74,6 +75,37 @@ struct Layout {
 bool pipe_candidate(const lstm_plan *p) {
     return p->layer_pipe && p->D == 1 && p->L >= 2 && p->L <= kMaxPipeLayers &&
            (p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT);
+}
+
+// Padded parameters of the GRU and the RNNs, per (layer, direction): W_ih
+// [4H][in_l], W_hh [4H][H], b_ih [4H], b_hh [4H] (dtype), each 256-byte
+// aligned; fn(l, d, k, offset, rows of the original, columns) for each.
+template <class F>
+bool walk_padded_params(const lstm_plan *p, F fn) {
+    const size_t es = elem_size(p->dtype), G4 = (size_t)4 * p->H;
+    size_t off = 0;
+    for (int l = 0; l < p->L; ++l)
+        for (int d = 0; d < p->D; ++d) {
+            const size_t cols[4] = {(size_t)(l == 0 ? p->I : p->D * p->H), (size_t)p->H, 1, 1};
+            for (int k = 0; k < 4; ++k) {
+                size_t b;
+                if (!mul_ok(G4 * cols[k], es, &b) || b > SIZE_MAX / 4 - off) return false;
+                fn(l, d, k, off, cols[k]);
+                off += align_up(b);
+            }
+        }
+    return true;
+}
+
+bool padded_params_bytes(const lstm_plan *p, size_t *bytes) {
+    size_t last = 0, last_cols = 0;
+    const bool ok = walk_padded_params(p, [&](int, int, int, size_t off, size_t cols) {
+        last = off;
+        last_cols = cols;
+    });
+    if (!ok) return false;
+    *bytes = last + align_up((size_t)4 * p->H * last_cols * elem_size(p->dtype));
+    return true;
 }
 
 bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
@@ -97,7 +129,9 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
             return false;
         if (pb > xb) xb = pb;
     }
-    if (!mul_ok(tb, (size_t)p->D * p->NG * p->H * sizeof(float), &g)) return false;
+    // G is [T*B][D][4H] for every mode: the GRU and the RNNs use it with
+    // their gate blocks padded to four when they run on the persistent kernel
+    if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
     size_t off = 0;
@@ -120,6 +154,12 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     off += align_up(st);
     o->lens = off;    // per-row lengths, copied from the caller's host array
     off += align_up((size_t)B * sizeof(int));
+    o->wpad = off;    // the GRU's and the RNNs' parameters padded to four gate blocks
+    if (p->mode != LSTM_MODE_LSTM) {
+        size_t wp = 0;
+        if (!padded_params_bytes(p, &wp)) return false;
+        off += wp;
+    }
     o->total = off;
     return true;
 }
@@ -677,8 +717,9 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     }
     const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
     const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
-    if (p->mode != LSTM_MODE_LSTM) {
-        static const char *names[] = {"lstm", "gru", "rnn_tanh", "rnn_relu"};
+    static const char *names[] = {"lstm", "gru", "rnn_tanh", "rnn_relu"};
+    const bool mode_persistent = p->mode != LSTM_MODE_LSTM && use_persistent_for_mode(p, B);
+    if (p->mode != LSTM_MODE_LSTM && !mode_persistent) {
         const int bm = rec_step_rows(B);
         std::snprintf(buf, len,
                       "cell=%s proj=%s<%s>; rec=k_rec_step<%s> mode=gemm-step block=%dx32 workgroups=%d launches=T%s",
@@ -691,7 +732,7 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     if (rc != LSTM_OK) return (lstm_status)rc;
     const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
     PipeSched ps{};
-    if (choose_pipe(p, B, dev, &ps)) {
+    if (!mode_persistent && choose_pipe(p, B, dev, &ps)) {
         std::snprintf(buf, len,
                       "proj=%s<%s> (layer 0 only); rec=k_rec_pipe<%s,WK=%d,MTW=%d,NT=%d> mode=layer-pipe U=%d P=%d "
                       "BG=%d NGB=%d layers=%d workgroups=%d lds=%zu",
@@ -714,12 +755,15 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     for (int l = 0; l < p->L && xl + 9 < sizeof(xproj); ++l) {
         const int in_l = l == 0 ? p->I : p->D * p->H;
         xl += (size_t)std::snprintf(xproj + xl, sizeof(xproj) - xl, "%s%s", l ? "," : "",
-                                    fused_chunks_shape(p, s, T, B, in_l, di) ? "fused" : "hoisted");
+                                    p->mode != LSTM_MODE_GRU && fused_chunks_shape(p, s, T, B, in_l, di) ? "fused"
+                                                                                                       : "hoisted");
     }
+    char cell[64] = {0};
+    if (mode_persistent) std::snprintf(cell, sizeof(cell), "cell=%s gate_slots=4 ", names[p->mode]);
     std::snprintf(buf, len,
-                  "proj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
+                  "%sproj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
                   "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s%s",
-                  proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
+                  cell, proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
                   s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds",
                   xproj, p->batch_first ? " layout=batch-first" : "");
     return LSTM_OK;
@@ -760,6 +804,37 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
 
     hipStream_t st = static_cast<hipStream_t>(stream_);
     char *ws = static_cast<char *>(workspace);
+
+    // The GRU and the plain RNNs run on the LSTM's four gate slots: their
+    // parameters are copied with zero rows up to four gate blocks (the GRU's
+    // b_hh keeps only its r and z blocks: b_hn is added inside the reset
+    // product by the kernel, from the caller's b_hh).
+    const bool padded = p->mode != LSTM_MODE_LSTM;
+    std::vector<const void *> wpad_ptrs;
+    const void *const *wts = weights;
+    int wper = per;
+    bool bias_on = p->has_bias != 0;
+    if (padded) {
+        if (!sch.persistent || lengths_h || reserve) return LSTM_ERR_UNSUPPORTED;
+        wpad_ptrs.assign((size_t)p->L * p->D * 4, nullptr);
+        std::vector<PadJob> jobs;
+        const int rows = p->NG * p->H;
+        walk_padded_params(p, [&](int l, int d, int k, size_t off, size_t cols) {
+            void *dst = ws + lay.wpad + off;
+            wpad_ptrs[(size_t)(l * p->D + d) * 4 + k] = dst;
+            const void *src = (k < 2 || p->has_bias) ? weights[(size_t)(l * p->D + d) * per + k] : nullptr;
+            int valid = src ? rows : 0;
+            if (k == 3 && p->mode == LSTM_MODE_GRU && src) valid = 2 * p->H;
+            jobs.push_back(PadJob{src ? src : dst, dst, valid, 4 * p->H, (int)cols});
+        });
+        if (launch_pad_rows(jobs.data(), (int)jobs.size(), p->dtype, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return LSTM_ERR_LAUNCH;
+        }
+        wts = wpad_ptrs.data();
+        wper = 4;
+        bias_on = true;
+    }
     unsigned *status = reinterpret_cast<unsigned *>(ws + lay.status);
     unsigned long long *xbuf = reinterpret_cast<unsigned long long *>(ws + lay.xbuf);
     float *G = reinterpret_cast<float *>(ws + lay.G);
@@ -793,7 +868,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     // one cooperative launch.  If the runtime refuses that launch, the
     // sequential path below redoes the work.
     PipeSched ps{};
-    if (!dlen && !p->batch_first && !reserve && choose_pipe(p, B, dev, &ps)) {
+    if (!padded && !dlen && !p->batch_first && !reserve && choose_pipe(p, B, dev, &ps)) {
         const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
         const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
         const size_t slot_words = region_words * ps.NGB;
@@ -883,8 +958,9 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         const int in_l = l == 0 ? p->I : p->D * p->H;
 
         const void *wih[2] = {nullptr, nullptr};
-        for (int d = 0; d < p->D; ++d) wih[d] = weights[(size_t)(l * p->D + d) * per];
-        int ncx = fused_chunks(p, sch, T, B, in_l, X, wih, di);
+        for (int d = 0; d < p->D; ++d) wih[d] = wts[(size_t)(l * p->D + d) * wper];
+        // the GRU needs x W_in^T apart from W_hn h (reset product): never fused
+        int ncx = p->mode == LSTM_MODE_GRU ? 0 : fused_chunks(p, sch, T, B, in_l, X, wih, di);
 
         // hoisted projection G = X W_ih^T + b_ih + b_hh (skipped when fused)
         auto project = [&]() -> bool {
@@ -897,10 +973,10 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
             pa.ldx = in_l;
             pa.D = p->D;
             for (int d = 0; d < p->D; ++d) {
-                const void *const *w = weights + (size_t)(l * p->D + d) * per;
+                const void *const *w = wts + (size_t)(l * p->D + d) * wper;
                 pa.W[d] = w[0];
-                pa.b_ih[d] = p->has_bias ? w[2] : nullptr;
-                pa.b_hh[d] = p->has_bias ? w[3] : nullptr;
+                pa.b_ih[d] = bias_on ? w[2] : nullptr;
+                pa.b_hh[d] = bias_on ? w[3] : nullptr;
             }
             const int sp = span_begin(p, st, 0);
             if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) {
@@ -914,12 +990,16 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
 
         RecArgs ra{};
         for (int d = 0; d < p->D; ++d) {
-            const void *const *w = weights + (size_t)(l * p->D + d) * per;
+            const void *const *w = wts + (size_t)(l * p->D + d) * wper;
             ra.whh[d] = w[1];
             ra.wih[d] = w[0];
-            ra.b_ih[d] = p->has_bias ? w[2] : nullptr;
-            ra.b_hh[d] = p->has_bias ? w[3] : nullptr;
+            ra.b_ih[d] = bias_on ? w[2] : nullptr;
+            ra.b_hh[d] = bias_on ? w[3] : nullptr;
+            // the GRU's b_hn: from the caller's b_hh
+            if (p->mode == LSTM_MODE_GRU)
+                ra.b_hh[d] = p->has_bias ? weights[(size_t)(l * p->D + d) * per + 3] : nullptr;
         }
+        ra.mode = p->mode;
         ra.ncx = ncx;
         ra.I = in_l;
         ra.x = X;
@@ -981,7 +1061,9 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         }
         bool use_gemm_layer = false;
         if (stepped) {
-            const bool use_gemm = gemm || (sch.persistent && gemm_step_shape_ok(p) && rec_step_gemm_ok(ra, p->dtype));
+            // (k_rec_step's LSTM instance needs real LSTM parameters: not for the padded modes)
+            const bool use_gemm = !padded && (gemm || (sch.persistent && gemm_step_shape_ok(p) &&
+                                                       rec_step_gemm_ok(ra, p->dtype)));
             use_gemm_layer = use_gemm;
             for (int s = 0; s < T; ++s) {
                 ra.s_begin = s;
@@ -1015,6 +1097,20 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     }
     if (p->timing) p->acc.calls += 1;
     return LSTM_OK;
+}
+
+// The GRU and the RNNs take the persistent recurrence when its schedule
+// applies (unless the caller asked for stepping) and the per-step GEMM kernel
+// otherwise.
+bool use_persistent_for_mode(const lstm_plan *p, int B) {
+    if (p->rec_mode == LSTM_REC_STEP || p->rec_mode == LSTM_REC_GEMM || B < 1) return false;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    Sched s{};
+    return choose_sched(p, B, dev, &s) == LSTM_OK && s.persistent;
 }
 
 // The forward pass of the GRU and the plain RNNs: per layer the hoisted
@@ -1110,7 +1206,11 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
                          const void *const *weights, int T, int B, int layers, int bidir, void *y,
                          void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
     if (p && p->mode != LSTM_MODE_LSTM) {
-        if (c0) return LSTM_ERR_ARG;  // no cell state
+        if (c0 || c_n) return LSTM_ERR_ARG;  // no cell state
+        // the persistent kernel on padded gate slots where the schedule allows, else one launch per step
+        if (use_persistent_for_mode(p, B))
+            return forward_impl(p, x, nullptr, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
+                                workspace, workspace_bytes, stream);
         return forward_modes(p, x, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace, workspace_bytes,
                              stream);
     }

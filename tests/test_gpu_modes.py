@@ -1,5 +1,7 @@
 """The GRU, RNN_TANH and RNN_RELU forward (lstm_create_mode, through the C ABI)
-against the fp64 oracle's oracle_rnn_forward on the same seeded inputs.
+against the fp64 oracle's oracle_rnn_forward on the same seeded inputs, on
+both paths: the persistent recurrence on padded gate slots (the default where
+its schedule applies) and one GEMM-step launch per step (LSTM_REC_STEP).
 
 Max-abs error relative to the output's scale, max(1, max|ref|) (the relu RNN
 is unbounded): 1e-4 for fp32, 2e-2 for bf16, the LSTM forward's bounds.
@@ -25,12 +27,17 @@ SHAPES = [  # input, hidden, layers, bidirectional, T, B, dtype, state, bias
 ]
 
 
-def _run(spec, inp, batch_first=False, rows=None):
+PATHS = {"auto": pkg.LSTM_REC_AUTO, "step": pkg.LSTM_REC_STEP}
+
+
+def _run(spec, inp, batch_first=False, path="auto"):
     import torch
     bf = spec.dtype == "bf16"
     dev = "cuda:0"
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
-                 dtype=spec.dtype, mode=spec.mode, batch_first=batch_first)
+                 dtype=spec.dtype, mode=spec.mode, batch_first=batch_first, recurrence=PATHS[path])
+    desc = m.describe(spec.T, spec.B)
+    assert ("k_rec_step" in desc) == (path == "step"), desc
     x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if batch_first else inp.x, bf, dev)
     w = [to_dev(p, bf, dev) for p in inp.params]
     h0 = to_dev(inp.h0, bf, dev)
@@ -49,41 +56,44 @@ def _check(got, ref, dtype, what):
     assert err <= TOL[dtype] * scale, f"{what}: max-abs error {err:.3g} > {TOL[dtype]} x {scale:.3g}"
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[6]}-I{s[0]}-H{s[1]}-L{s[2]}-D{2 if s[3] else 1}"
                                                         f"-T{s[4]}-B{s[5]}")
-def test_mode_matches_oracle(mode, shape):
+def test_mode_matches_oracle(mode, shape, path):
     I, H, L, bidir, T, B, dtype, state, bias = shape
     spec = Spec(I, H, L, bidir, T, B, dtype, 900 + H + L, state, has_bias=bias, mode=mode)
-    print(f"case {mode} {shape}", flush=True)
+    print(f"case {mode} {shape} {path}", flush=True)
     inp = make_inputs(spec)
-    y, hn = _run(spec, inp)
+    y, hn = _run(spec, inp, path=path)
     ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, H, L, bidir, h0=inp.h0, has_bias=bias,
                                  bf16=dtype == "bf16", nthreads=oracle_threads())
     _check(y, ry, dtype, "y")
     _check(hn, rhn, dtype, "h_n")
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("mode", MODES)
-def test_mode_batch_first(mode):
+def test_mode_batch_first(mode, path):
     spec = Spec(24, 64, 2, True, 7, 21, "f32", 960, "normal0.1", mode=mode)
-    print(f"case {mode} batch_first", flush=True)
+    print(f"case {mode} batch_first {path}", flush=True)
     inp = make_inputs(spec)
-    y, hn = _run(spec, inp, batch_first=True)
+    y, hn = _run(spec, inp, batch_first=True, path=path)
     ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, 64, 2, True, h0=inp.h0, nthreads=oracle_threads())
     _check(y, ry, "f32", "y")
     _check(hn, rhn, "f32", "h_n")
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("mode", MODES)
-def test_mode_full_size_sampled_rows(mode):
+def test_mode_full_size_sampled_rows(mode, path):
     # the benchmark workload's shape (in 256, H 512, T 128, B 64, two layers,
     # fp32) in the GRU / RNN mode, checked on a sample of batch rows (rows
     # are independent), in the launch configuration the benchmark times
     spec = Spec(256, 512, 2, False, 128, 64, "f32", 1002, "normal0.1", mode=mode)
-    print(f"case {mode} full size", flush=True)
+    print(f"case {mode} full size {path}", flush=True)
     inp = make_inputs(spec)
-    y, hn = _run(spec, inp)
+    y, hn = _run(spec, inp, path=path)
     rows = [0, 17, 42, 63]
     sub = inp.rows(rows)
     ry, rhn = oracle.rnn_forward(mode, sub.x, sub.params, 512, 2, False, h0=sub.h0, nthreads=oracle_threads())
