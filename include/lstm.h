@@ -145,11 +145,14 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
 
 /* lstm_create for any lstm_mode (lstm_create is mode LSTM_MODE_LSTM); a mode
  * outside the enum is LSTM_ERR_ARG.  For the GRU and the RNNs, lstm_forward
- * takes h0 alone (c0 and c_n must be NULL, else LSTM_ERR_ARG), runs one
- * hoisted projection GEMM and T recurrent-step launches per layer, and needs
- * hidden_size * element size to be a multiple of 16 bytes and 16-byte aligned
- * x, y, h0 and weights (LSTM_ERR_UNSUPPORTED otherwise); lstm_forward_lengths,
- * the training entry points and their size queries are LSTM_ERR_UNSUPPORTED. */
+ * takes h0 alone (c0 and c_n must be NULL, else LSTM_ERR_ARG).  Where an LSTM
+ * of the same shape gets a persistent recurrence, they run on it with their
+ * gate blocks copied into the workspace padded to four; otherwise (or with
+ * LSTM_REC_STEP / LSTM_REC_GEMM) one projection GEMM and T recurrent-step
+ * launches per layer, which need hidden_size * element size to be a multiple
+ * of 16 bytes and 16-byte aligned x, y, h0 and weights
+ * (LSTM_ERR_UNSUPPORTED otherwise).  lstm_forward_lengths, the training entry
+ * points and their size queries are LSTM_ERR_UNSUPPORTED. */
 lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidden_size, int num_layers,
                              int bidirectional, int has_bias, int dtype);
 
