@@ -420,9 +420,9 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
         f"{value / 1e9:.3f} G cells/s")
 
     # The backward's dominant work is its recurrence: per step and layer one
-    # product launch (k_bwd_mm) and one cell launch (k_bwd_cell), timed as a
-    # pair by the library's own events around each layer's loop of T steps,
-    # in separate timed steps.
+    # k_bwd_step launch (the recurrent product and the next step's cell
+    # update), timed by the library's own events around each layer's loop of
+    # T steps, in separate timed steps.
     pkg.lstm_set_option(m.plan, pkg.LSTM_OPT_TIMING, 1)
     pkg.lstm_read_timing(m.plan, reset=True)
     for _ in range(args.steps):
@@ -434,11 +434,11 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     flops = 2.0 * spec.B * spec.D * 4 * H * H  # dz_t [B, 4H] x W_hh [4H, H] per direction and step
     avg = tm["bwd_rec_ms"] / max(1, tm["bwd_rec_launches"])
     achieved = flops / (avg / 1e3) / 1e12
-    traffic = stored_traffic("k_bwd_mm_k_bwd_cell", args.workload)
+    traffic = stored_traffic("k_bwd_step", args.workload)
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS["f32"], 4), "traffic": traffic,
             "traffic_GB_per_s": None if traffic is None else round(traffic / (avg / 1e3) / 1e9, 1),
-            "kernel": "k_bwd_mm+k_bwd_cell", "launch": "one backward step: a k_bwd_mm and a k_bwd_cell launch",
+            "kernel": "k_bwd_step", "launch": "one backward step",
             "avg_launch_ms": round(avg, 5), "flops_per_launch": flops,
             "phase_ms_per_step": {"bwd_rec": round(tm["bwd_rec_ms"] / max(1, tm["bwd_calls"]), 4),
                                   "bwd_gemm": round(tm["bwd_gemm_ms"] / max(1, tm["bwd_calls"]), 4),

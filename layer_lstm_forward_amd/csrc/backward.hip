@@ -15,10 +15,10 @@
 //   dc_prev = dc f,  dh_prev = W_hh^T dz,  dx = W_ih^T dz
 //   dW_ih += dz x^T,  dW_hh += dz h_prev^T,  db_ih = db_hh += dz
 //
-//   k_bwd_cell  one backward step, elementwise: dh, dc, dz for every cell
-//   k_bwd_mm    the recurrent product of that step, dz_t W_hh, as K-split
-//               partial sums on the matrix cores (summed by the next step)
-//   k_bwd_dh0   the last partial sums -> dh0
+//   k_bwd_cell  the first backward step of a scan, elementwise: dh, dc, dz
+//   k_bwd_step  each backward step: the recurrent product dz_t W_hh of a
+//               tile over the whole K on the matrix cores, then the cell
+//               update of the step before it (or dh0 after the last)
 //   k_transpose, k_hprev_t, k_rowsum, k_cast_*  operand preparation for the
 //               weight and input gradients, which are plain fp32 "NT" GEMMs
 //               on the projection kernels
@@ -32,42 +32,23 @@
 
 namespace lstm_amd {
 
-// One backward step for every (direction, batch row, unit).  sb counts the
-// backward steps: sb = 0 is the last step of each direction's scan.
-__global__ void k_bwd_cell(BwdCellArgs a) {
-    const size_t n = (size_t)a.D * a.B * a.H;
-    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int j = (int)(i % a.H);
-    const int b = (int)((i / a.H) % a.B);
-    const int d = (int)(i / ((size_t)a.H * a.B));
+// The cell part of backward step sb (sb = 0 is the last step of each
+// direction's scan) at (d, b, j): from dh = dY + dh_rec (the recurrent
+// product of the step after it) and the carried dc, the pre-activation
+// gradients dz of the four gates and dc for the step before it.
+__device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int b, int j, float dh_rec) {
     const int T = a.T, B = a.B, H = a.H, D = a.D;
-    const int sf = T - 1 - a.sb;                 // the forward scan's step
+    const int sf = T - 1 - sb;                   // the forward scan's step
     const int t = d == 0 ? sf : T - 1 - sf;      // its time index
     const int tp = d == 0 ? t - 1 : t + 1;       // time of the scan's previous step
     const size_t dbj = ((size_t)d * B + b) * H + j;
 
-    float dh = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j];
+    float dh = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j] + dh_rec;
     float dcn;
-    if (a.sb == 0) {
+    if (sb == 0) {
         dh += a.dhn ? a.dhn[dbj] : 0.f;
         dcn = a.dcn ? a.dcn[dbj] : 0.f;
     } else {
-        // h_t feeds the next step's products: their partial sums, in slice
-        // order, four loads in flight
-        const float *pp = a.part + dbj;
-        float r = 0.f;
-        int p = 0;
-        for (; p + 4 <= a.NP; p += 4) {
-            const float v0 = pp[(size_t)p * n], v1 = pp[(size_t)(p + 1) * n];
-            const float v2 = pp[(size_t)(p + 2) * n], v3 = pp[(size_t)(p + 3) * n];
-            r += v0;
-            r += v1;
-            r += v2;
-            r += v3;
-        }
-        for (; p < a.NP; ++p) r += pp[(size_t)p * n];
-        dh += r;
         dcn = a.dc[dbj];
     }
     const float *ap = a.acts + (((size_t)t * B + b) * D + d) * 5 * H + j;
@@ -85,24 +66,37 @@ __global__ void k_bwd_cell(BwdCellArgs a) {
     a.dc[dbj] = dct * fg;
 }
 
-// part[p][d][b][j] = sum over k in slice p of dz_t[b][d][k] * W_hh[d][k][j]
-// (K = 4H in the stacked gate order), with whT[d][j][k] = W_hh[d][k][j].
-// A workgroup: 32 batch rows x 32 units of one direction and one K slice;
-// wave (wm, wn) computes a 16 x 16 tile with 16x16x4 fp32 MFMAs whose
-// fragments are 16-byte loads of K-contiguous rows.
-__global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w & 1, wn = w >> 1;
+// The first backward step of every (direction, batch row, unit): dh = dY + dh_n.
+__global__ void k_bwd_cell(BwdCellArgs a) {
+    const size_t n = (size_t)a.D * a.B * a.H;
+    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    bwd_cell_update(a, 0, (int)(i / ((size_t)a.H * a.B)), (int)((i / a.H) % a.B), (int)(i % a.H), 0.f);
+}
+
+// Backward step sb: the recurrent product dh_prev = dz_t W_hh of step sb for
+// one tile of 16 batch rows x 16 units of one direction, over the whole
+// K = 4H (stacked gate order), then the cell update of step sb + 1 for the
+// tile's cells -- or, after the scan's first step (sb = T - 1), dh0.
+//   whT[d][j][k] = W_hh[d][k][j]: K-contiguous rows, as are dz's
+// The four waves take a quarter of K each (16x16x4 fp32 MFMAs whose
+// fragments are 16-byte loads); their tiles meet in LDS, one output per
+// thread.  A whole tile's K lives in one workgroup, so no partial sums leave
+// it and nothing waits on another workgroup.
+template <class DT>
+__global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, typename DT::S *dh0) {
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.B, H = a.H, D = a.D, K = 4 * H;
-    const int p = blockIdx.z % a.NP, d = blockIdx.z / a.NP;
-    const int b = blockIdx.x * 32 + wm * 16 + (lane & 15);  // A row of this lane
-    const int j = blockIdx.y * 32 + wn * 16 + (lane & 15);  // B row (unit) of this lane
-    const int k_lo = p * a.KS, k_hi = min(K, k_lo + a.KS);
+    const int d = blockIdx.z, b0 = blockIdx.x * 16, u0 = blockIdx.y * 16;
+    const int b = b0 + (lane & 15);  // A row (batch row) of this lane
+    const int j = u0 + (lane & 15);  // B row (unit) of this lane
+    const int kq = (K + 63) / 64 * 16;  // K per wave, whole 16-chunks
+    const int k_lo = w * kq, k_hi = min(K, k_lo + kq);
     const int sf = a.T - 1 - a.sb;
     const int t = d == 0 ? sf : a.T - 1 - sf;
-    // A: dz rows (t, b, d) for b < B; B: whT rows (d, j) for j < H.  Both via
-    // buffer resources: a row past B or H, or a chunk past the slice, gets an
-    // out-of-range offset and reads zeros without a memory access.
+    // dz rows (t, b, d) for b < B and whT rows (d, j) for j < H through buffer
+    // resources: a row past B or H, or a chunk past the wave's K range, gets
+    // an out-of-range offset and reads zeros without a memory access
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.dz + ((size_t)t * B * D + d) * (size_t)K), (short)0,
         (int)(((size_t)(B - 1) * D * K + K) * sizeof(float)), 0x00020000);
@@ -111,44 +105,36 @@ __global__ __launch_bounds__(256) void k_bwd_mm(BwdMmArgs a) {
     const unsigned aoff = (unsigned)((size_t)b * D * K * sizeof(float));
     const unsigned boff = (unsigned)((size_t)j * K * sizeof(float));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Batches of 16 chunks (a 256-deep slice is one batch): all 32 fragment
-    // loads are issued before the first product of the batch, and a
-    // scheduling barrier keeps the compiler from interleaving them with the
-    // products into a chain of round trips (K % 4 == 0 and slices start at
-    // multiples of 16: a fragment is whole or absent).
+    // batches of 16 chunks: all 32 fragment loads are issued before the first
+    // product of the batch; scheduling barriers keep the compiler from
+    // interleaving them with the products into a chain of round trips
     constexpr int NBAT = 16;
     constexpr unsigned OOR = 0x7FFFFFF0u;
     for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * F32::KC) {
         u32x4 av[NBAT], bv[NBAT];
 #pragma unroll
-        for (int c = 0; c < NBAT; ++c) {
-            const int k = k0 + c * F32::KC + (lane >> 4) * F32::PER16;
+        for (int q = 0; q < NBAT; ++q) {
+            const int k = k0 + q * F32::KC + (lane >> 4) * F32::PER16;
             const bool kin = k < k_hi;
-            av[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + 4u * k : OOR), 0, 0);
-            bv[c] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + 4u * k : OOR), 0, 0);
+            av[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + 4u * k : OOR), 0, 0);
+            bv[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + 4u * k : OOR), 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < NBAT; ++c) acc = mma_chunk(F32{}, acc, av[c], bv[c]);
+        for (int q = 0; q < NBAT; ++q) acc = mma_chunk(F32{}, acc, av[q], bv[q]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    const size_t n = (size_t)D * B * H;
+    // lane l, register v: batch row 4 (l / 16) + v, unit l % 16 of the tile
+    __shared__ float red[4][16][17];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int m = blockIdx.x * 32 + wm * 16 + 4 * (lane >> 4) + v;
-        const int u = blockIdx.y * 32 + wn * 16 + (lane & 15);
-        if (m < B && u < H) a.part[(size_t)p * n + ((size_t)d * B + m) * H + u] = acc[v];
-    }
-}
-
-// dh0 = the recurrent product of the scan's first step (sum of its partials)
-template <class DT>
-__global__ void k_bwd_dh0(const float *part, int NP, size_t n, typename DT::S *dh0) {
-    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float r = 0.f;
-    for (int p = 0; p < NP; ++p) r += part[(size_t)p * n + i];
-    dh0[i] = DT::from_f(r);
+    for (int v = 0; v < 4; ++v) red[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
+    __syncthreads();
+    const int rb_ = tid >> 4, ru = tid & 15;
+    const int m = b0 + rb_, u = u0 + ru;
+    if (m >= B || u >= H) return;
+    const float r = red[0][rb_][ru] + red[1][rb_][ru] + red[2][rb_][ru] + red[3][rb_][ru];
+    if (a.sb + 1 < a.T) bwd_cell_update(c, a.sb + 1, d, m, u, r);
+    else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r);
 }
 
 // out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (as fp32)
@@ -296,20 +282,13 @@ hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_mm(const BwdMmArgs &a, hipStream_t s) {
-    if ((4 * a.H) % 4 != 0 || a.KS % F32::KC != 0) return hipErrorInvalidValue;
-    dim3 grid((a.B + 31) / 32, (a.H + 31) / 32, a.NP * a.D);
-    hipLaunchKernelGGL(k_bwd_mm, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_bwd_dh0(const float *part, int NP, size_t n, void *dh0, int dtype, hipStream_t s) {
+hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int dtype, hipStream_t s) {
+    if (c.dz != a.dz || c.T != a.T || c.B != a.B || c.H != a.H || c.D != a.D) return hipErrorInvalidValue;
+    dim3 grid((a.B + 15) / 16, (a.H + 15) / 16, a.D);
     if (dtype == DT_BF16)
-        hipLaunchKernelGGL(k_bwd_dh0<BF16>, dim3(grid1(n, 1u << 30)), dim3(256), 0, s, part, NP, n,
-                           static_cast<uint16_t *>(dh0));
+        hipLaunchKernelGGL(k_bwd_step<BF16>, grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
     else
-        hipLaunchKernelGGL(k_bwd_dh0<F32>, dim3(grid1(n, 1u << 30)), dim3(256), 0, s, part, NP, n,
-                           static_cast<float *>(dh0));
+        hipLaunchKernelGGL(k_bwd_step<F32>, grid, dim3(256), 0, s, a, c, static_cast<float *>(dh0));
     return hipGetLastError();
 }
 

@@ -152,21 +152,21 @@ struct BwdCellArgs {
     const float *dY;    // [T, B, D*H] gradient of this layer's output
     const float *dhn;   // [D, B, H] gradient of h_n of this layer, or NULL
     const float *dcn;   // [D, B, H] gradient of c_n of this layer, or NULL
-    const float *part;  // [NP, D, B, H] recurrent-product partial sums of the previous backward step
-    float *dz;          // [T, B, D, 4H] gradient of the pre-activations, written at this step's time
+    float *dz;          // [T, B, D, 4H] gradient of the pre-activations, written at each step's time
     float *dc;          // [D, B, H] cell-state gradient carried backwards (read and written)
-    int T, B, H, D, NP, sb;
+    int T, B, H, D;
 };
-// part[p] = dz_t W_hh over K slice p (KS gate rows, a multiple of 16)
+// the recurrent product of step sb: dz_t W_hh
 struct BwdMmArgs {
     const float *dz;    // [T, B, D, 4H]
     const float *whT;   // [D, H, 4H] transposed W_hh, fp32
-    float *part;        // [NP, D, B, H]
-    int T, B, H, D, NP, KS, sb;
+    int T, B, H, D, sb;
 };
+// The first backward step of a layer (dh = dY + dh_n), elementwise.
 hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s);
-hipError_t launch_bwd_mm(const BwdMmArgs &a, hipStream_t s);
-hipError_t launch_bwd_dh0(const float *part, int NP, size_t n, void *dh0, int dtype, hipStream_t s);
+// Backward step a.sb: the recurrent product, then the cell update of step
+// a.sb + 1, or dh0 ([D, B, H], dtype; NULL = not wanted) after the last step.
+hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int dtype, hipStream_t s);
 // out[c * ld_out + r] = in[r * ld_in + c] (rows x cols of dtype -> fp32)
 hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out, int dtype,
                             hipStream_t s);

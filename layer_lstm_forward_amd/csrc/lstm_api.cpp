@@ -202,12 +202,11 @@ bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
 // Backward workspace (all fp32): dz [T][B][D][4H]; one direction's dz^T
 // [4H][T*B]; the layer input x^T [in][T*B] and h_prev^T [H][T*B]; two output
 // gradient buffers [T*B][max(in, D*H)] (this layer's dY and the dX it
-// produces); the recurrent partial sums [NP][D][B][H]; the cell gradient
-// carry and dh_n [D][B][H]; transposed W_hh [D][H][4H] and W_ih [in][D*4H];
-// one weight gradient [4H][max(in, H)] and one bias gradient [4H].
+// produces); the cell gradient carry and dh_n [D][B][H]; transposed W_hh
+// [D][H][4H] and W_ih [in][D*4H]; the K-split slabs of the gradient products;
+// one bias gradient [4H].
 struct BwdLayout {
-    size_t dz, dzt, xt, ht, dy[2], part, dc, dhn, wht, wcat, ksp, db, total;
-    int NP, KS;
+    size_t dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, total;
 };
 
 // K-split count of an fp32 M x N x K product (1: not split)
@@ -222,24 +221,15 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     const size_t win = std::max((size_t)p->I, D * H);
     size_t tb;
     if (!mul_ok((size_t)T, (size_t)B, &tb) || tb > (size_t)INT_MAX) return false;
-    // K slices of the recurrent product: 256 gate rows (one load batch of
-    // the product kernel) while that keeps the grid within about 1024
-    // workgroups, deeper slices beyond
-    const size_t base = (size_t)((B + 31) / 32) * ((p->H + 31) / 32) * D;
-    int np = (int)std::min<size_t>((G4 + 255) / 256, std::max<size_t>((1024 + base - 1) / base, 1));
-    int ks = (int)(((G4 + np - 1) / np + 15) / 16 * 16);
-    o->KS = ks;
-    o->NP = (int)((G4 + ks - 1) / ks);
-    size_t sz[13];
+    size_t sz[12];
     if (!mul_ok(tb, D * G4 * f, &sz[0]) || !mul_ok(tb, G4 * f, &sz[1]) || !mul_ok(tb, win * f, &sz[2]) ||
         !mul_ok(tb, H * f, &sz[3]) || !mul_ok(tb, win * f, &sz[4]))
         return false;
     sz[5] = sz[4];
-    sz[6] = (size_t)o->NP * D * B * H * f;
-    sz[7] = D * B * H * f;
-    sz[8] = sz[7];
-    sz[9] = D * H * G4 * f;
-    sz[10] = win * D * G4 * f;
+    sz[6] = D * B * H * f;
+    sz[7] = sz[6];
+    sz[8] = D * H * G4 * f;
+    sz[9] = win * D * G4 * f;
     // K-split slabs (or the unsplit fp32 product) of the weight-gradient
     // products, and the slabs of a split input-gradient product
     size_t ksp = 0;
@@ -251,12 +241,12 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
         const int nx = ksplit_count((int)tb, in_l, (int)(D * G4));
         if (nx > 1) ksp = std::max(ksp, (size_t)nx * tb * in_l);
     }
-    if (!mul_ok(ksp, f, &sz[11])) return false;
-    sz[12] = G4 * f;
-    size_t *dst[13] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->part, &o->dc, &o->dhn,
+    if (!mul_ok(ksp, f, &sz[10])) return false;
+    sz[11] = G4 * f;
+    size_t *dst[12] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
                        &o->wht, &o->wcat, &o->ksp, &o->db};
     size_t off = 0;
-    for (int i = 0; i < 13; ++i) {
+    for (int i = 0; i < 12; ++i) {
         *dst[i] = off;
         if (sz[i] > SIZE_MAX - off - 256) return false;
         off += align_up(sz[i]);
@@ -939,7 +929,6 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
 
     if (launch_fill_u32(status, lay.sync_bytes / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
 
-    const int kc = p->dtype == LSTM_BF16 ? 32 : 16;
     const int per16 = p->dtype == LSTM_BF16 ? 8 : 4;
     // Exchange tags are one bit per word: bit p of xpar is the parity of the
     // writes exchange buffer p has received so far in this call.  A k_rec
@@ -1292,7 +1281,6 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     float *xt = reinterpret_cast<float *>(ws + bl.xt);
     float *ht = reinterpret_cast<float *>(ws + bl.ht);
     float *dyb[2] = {reinterpret_cast<float *>(ws + bl.dy[0]), reinterpret_cast<float *>(ws + bl.dy[1])};
-    float *part = reinterpret_cast<float *>(ws + bl.part);
     float *dcb = reinterpret_cast<float *>(ws + bl.dc);
     float *dhnb = reinterpret_cast<float *>(ws + bl.dhn);
     float *wht = reinterpret_cast<float *>(ws + bl.wht);
@@ -1359,40 +1347,34 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         if (dh_n && !ok(launch_cast_from(static_cast<const char *>(dh_n) + (size_t)l * DBH * es, dhnb, DBH, dt, st)))
             return fail();
         const int rec_span = span_begin(p, st, 2);
-        // the recurrence, backwards: sb = 0 is each direction's last step
+        // the recurrence, backwards: sb = 0 is each direction's last step;
+        // launch sb multiplies step sb's dz by W_hh and runs step sb + 1's cell
+        BwdCellArgs ca{};
+        ca.acts = acts;
+        ca.c0 = c0l;
+        ca.dY = dyb[cur];
+        ca.dhn = dh_n ? dhnb : nullptr;
+        ca.dcn = dc_n ? dc_n + (size_t)l * DBH : nullptr;
+        ca.dz = dz;
+        ca.dc = dcb;
+        ca.T = T;
+        ca.B = B;
+        ca.H = H;
+        ca.D = D;
+        if (!ok(launch_bwd_cell(ca, st))) return fail();
+        void *dh0l = dh0 ? static_cast<char *>(dh0) + (size_t)l * DBH * es : nullptr;
         for (int sb = 0; sb < T; ++sb) {
-            BwdCellArgs ca{};
-            ca.acts = acts;
-            ca.c0 = c0l;
-            ca.dY = dyb[cur];
-            ca.dhn = dh_n ? dhnb : nullptr;
-            ca.dcn = dc_n ? dc_n + (size_t)l * DBH : nullptr;
-            ca.part = part;
-            ca.dz = dz;
-            ca.dc = dcb;
-            ca.T = T;
-            ca.B = B;
-            ca.H = H;
-            ca.D = D;
-            ca.NP = bl.NP;
-            ca.sb = sb;
-            if (!ok(launch_bwd_cell(ca, st))) return fail();
             BwdMmArgs ma{};
             ma.dz = dz;
             ma.whT = wht;
-            ma.part = part;
             ma.T = T;
             ma.B = B;
             ma.H = H;
             ma.D = D;
-            ma.NP = bl.NP;
-            ma.KS = bl.KS;
             ma.sb = sb;
-            if (!ok(launch_bwd_mm(ma, st))) return fail();
+            if (!ok(launch_bwd_step(ma, ca, dh0l, dt, st))) return fail();
         }
         span_end(p, rec_span, st, T);
-        if (dh0 && !ok(launch_bwd_dh0(part, bl.NP, DBH, static_cast<char *>(dh0) + (size_t)l * DBH * es, dt, st)))
-            return fail();
         if (dc0 && hipMemcpyAsync(dc0 + (size_t)l * DBH, dcb, DBH * sizeof(float), hipMemcpyDeviceToDevice, st) !=
                        hipSuccess)
             return fail();
