@@ -19,9 +19,10 @@
 //   k_bwd_step  each backward step: the recurrent product dz_t W_hh of a
 //               tile over the whole K on the matrix cores, then the cell
 //               update of the step before it (or dh0 after the last)
-//   k_transpose, k_hprev_t, k_rowsum, k_cast_*  operand preparation for the
-//               weight and input gradients, which are plain fp32 "NT" GEMMs
-//               on the projection kernels
+//   k_transpose, k_hprev_t, k_cast_*  operand preparation for the weight
+//               and input gradients, which are "NT" GEMMs on the projection
+//               kernels (bf16 operands for bf16 parameters, else fp32)
+//   k_colsum_part  the bias gradients, column sums of dz in fixed chunks
 //   k_dropout_fwd, k_dropout_bwd  training dropout between layers: the trace
 //               page's Performance Notes apply it to the input of every
 //               layer above the first in training only; the draw is
@@ -137,19 +138,20 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
     else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r);
 }
 
-// out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (as fp32)
-template <class DT>
-__global__ void k_transpose(const typename DT::S *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out) {
+// out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (DI in, DO out)
+template <class DI, class DO>
+__global__ void k_transpose(const typename DI::S *in, size_t ld_in, int rows, int cols, typename DO::S *out,
+                            size_t ld_out) {
     __shared__ float tile[32][33];
     const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
     for (int rr = threadIdx.y; rr < 32; rr += 8) {
         const int r = r0 + rr, c = c0 + threadIdx.x;
-        tile[rr][threadIdx.x] = (r < rows && c < cols) ? DT::to_f(in[(size_t)r * ld_in + c]) : 0.f;
+        tile[rr][threadIdx.x] = (r < rows && c < cols) ? DI::to_f(in[(size_t)r * ld_in + c]) : 0.f;
     }
     __syncthreads();
     for (int cc = threadIdx.y; cc < 32; cc += 8) {
         const int c = c0 + cc, r = r0 + threadIdx.x;
-        if (c < cols && r < rows) out[(size_t)c * ld_out + r] = tile[threadIdx.x][cc];
+        if (c < cols && r < rows) out[(size_t)c * ld_out + r] = DO::from_f(tile[threadIdx.x][cc]);
     }
 }
 
@@ -158,7 +160,7 @@ __global__ void k_transpose(const typename DT::S *in, size_t ld_in, int rows, in
 // zeros) at the scan's first step.
 template <class DT>
 __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, int T, int B, int H,
-                          int d, float *out) {
+                          int d, typename DT::S *out) {
     __shared__ float tile[32][33];
     const int m0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int M = T * B;
@@ -176,24 +178,28 @@ __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT
     __syncthreads();
     for (int kk = threadIdx.y; kk < 32; kk += 8) {
         const int k = k0 + kk, m = m0 + threadIdx.x;
-        if (k < H && m < M) out[(size_t)k * M + m] = tile[threadIdx.x][kk];
+        if (k < H && m < M) out[(size_t)k * M + m] = DT::from_f(tile[threadIdx.x][kk]);
     }
 }
 
-// out[r] = sum over c of a[r * ld + c]: one workgroup per row, a fixed tree
-// (deterministic)
-__global__ void k_rowsum(const float *a, size_t ld, int cols, float *out) {
-    __shared__ float red[256];
-    const float *row = a + (size_t)blockIdx.x * ld;
+// Column sums in fixed row chunks: part[c][col] = sum over rows r in chunk c
+// (rows c*chunk .. ) of a[r * ld + col], each summed in row order; the
+// chunks are then added in order by k_ksum (deterministic).
+__global__ void k_colsum_part(const float *a, size_t ld, int rows, int cols, int chunk, float *part) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= cols) return;
+    const int r0 = blockIdx.y * chunk, r1 = min(rows, r0 + chunk);
     float s = 0.f;
-    for (int c = threadIdx.x; c < cols; c += 256) s += row[c];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-        __syncthreads();
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {  // eight loads in flight, added in row order
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * ld + col];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v[q];
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+    for (; r < r1; ++r) s += a[(size_t)r * ld + col];
+    part[(size_t)blockIdx.y * cols + col] = s;
 }
 
 template <class DT>
@@ -214,7 +220,15 @@ template <class DT>
 __global__ void k_ksum(const float *part, int ns, size_t slab, size_t n, typename DT::S *out) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
         float v = part[i];
-        for (int sp = 1; sp < ns; ++sp) v += part[(size_t)sp * slab + i];
+        int sp = 1;
+        for (; sp + 8 <= ns; sp += 8) {  // eight loads in flight, added in slab order
+            float w[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) w[q] = part[(size_t)(sp + q) * slab + i];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v += w[q];
+        }
+        for (; sp < ns; ++sp) v += part[(size_t)sp * slab + i];
         out[i] = DT::from_f(v);
     }
 }
@@ -292,35 +306,45 @@ hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, 
     return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out, int dtype,
-                            hipStream_t s) {
+hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
+                            int out_dtype, hipStream_t s) {
     dim3 grid((cols + 31) / 32, (rows + 31) / 32), block(32, 8);
     if (grid.y > 65535u) return hipErrorInvalidValue;
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(k_transpose<BF16>, grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
-                           cols, out, ld_out);
+    const bool bi = in_dtype == DT_BF16, bo = out_dtype == DT_BF16;
+    if (bi && bo)
+        hipLaunchKernelGGL((k_transpose<BF16, BF16>), grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
+                           cols, static_cast<uint16_t *>(out), ld_out);
+    else if (bi)
+        hipLaunchKernelGGL((k_transpose<BF16, F32>), grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
+                           cols, static_cast<float *>(out), ld_out);
+    else if (bo)
+        hipLaunchKernelGGL((k_transpose<F32, BF16>), grid, block, 0, s, static_cast<const float *>(in), ld_in, rows,
+                           cols, static_cast<uint16_t *>(out), ld_out);
     else
-        hipLaunchKernelGGL(k_transpose<F32>, grid, block, 0, s, static_cast<const float *>(in), ld_in, rows, cols,
-                           out, ld_out);
+        hipLaunchKernelGGL((k_transpose<F32, F32>), grid, block, 0, s, static_cast<const float *>(in), ld_in, rows,
+                           cols, static_cast<float *>(out), ld_out);
     return hipGetLastError();
 }
 
-hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, float *out,
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
                           int dtype, hipStream_t s) {
     dim3 grid(((size_t)T * B + 31) / 32, (H + 31) / 32), block(32, 8);
     if (grid.y > 65535u) return hipErrorInvalidValue;
     if (dtype == DT_BF16)
         hipLaunchKernelGGL(k_hprev_t<BF16>, grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
-                           static_cast<const uint16_t *>(h0d), T, B, H, d, out);
+                           static_cast<const uint16_t *>(h0d), T, B, H, d, static_cast<uint16_t *>(out));
     else
         hipLaunchKernelGGL(k_hprev_t<F32>, grid, block, 0, s, static_cast<const float *>(Y), ldy,
-                           static_cast<const float *>(h0d), T, B, H, d, out);
+                           static_cast<const float *>(h0d), T, B, H, d, static_cast<float *>(out));
     return hipGetLastError();
 }
 
-hipError_t launch_rowsum(const float *a, size_t ld, int rows, int cols, float *out, hipStream_t s) {
-    if (rows < 1) return hipSuccess;
-    hipLaunchKernelGGL(k_rowsum, dim3(rows), dim3(256), 0, s, a, ld, cols, out);
+hipError_t launch_colsum_part(const float *a, size_t ld, int rows, int cols, int nchunks, float *part,
+                              hipStream_t s) {
+    if (rows < 1 || cols < 1 || nchunks < 1) return hipErrorInvalidValue;
+    const int chunk = (rows + nchunks - 1) / nchunks;
+    dim3 grid((cols + 255) / 256, (unsigned)((rows + chunk - 1) / chunk));
+    hipLaunchKernelGGL(k_colsum_part, grid, dim3(256), 0, s, a, ld, rows, cols, chunk, part);
     return hipGetLastError();
 }
 

@@ -167,13 +167,18 @@ hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s);
 // Backward step a.sb: the recurrent product, then the cell update of step
 // a.sb + 1, or dh0 ([D, B, H], dtype; NULL = not wanted) after the last step.
 hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int dtype, hipStream_t s);
-// out[c * ld_out + r] = in[r * ld_in + c] (rows x cols of dtype -> fp32)
-hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, float *out, size_t ld_out, int dtype,
-                            hipStream_t s);
-// [H][T*B] fp32: h_prev of direction d for every (t, b), from the layer output Y or h0d ([B][H] or NULL)
-hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, float *out,
+// out[c * ld_out + r] = in[r * ld_in + c] (rows x cols, in_dtype -> out_dtype)
+hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
+                            int out_dtype, hipStream_t s);
+// [H][T*B] in dtype: h_prev of direction d for every (t, b), from the layer
+// output Y or h0d ([B][H] or NULL)
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
                           int dtype, hipStream_t s);
-hipError_t launch_rowsum(const float *a, size_t ld, int rows, int cols, float *out, hipStream_t s);
+// part[c][col] (c < the chunk count launched, at most nchunks) = sum over
+// the rows of chunk c of a[r * ld + col]; rows split into ceil(rows /
+// nchunks)-row chunks, each summed in row order
+hipError_t launch_colsum_part(const float *a, size_t ld, int rows, int cols, int nchunks, float *part,
+                              hipStream_t s);
 hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s);
 hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s);
 // Training dropout of one layer's output y (n elements of dtype): xd = the

@@ -209,6 +209,9 @@ struct BwdLayout {
     size_t dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, total;
 };
 
+// row chunks of the bias-gradient column sums
+constexpr int kBiasChunks = 128;
+
 // K-split count of an fp32 M x N x K product (1: not split)
 int ksplit_count(int M, int N, int K) {
     const int kc = proj_kchunk(M, N, K);
@@ -242,7 +245,7 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
         if (nx > 1) ksp = std::max(ksp, (size_t)nx * tb * in_l);
     }
     if (!mul_ok(ksp, f, &sz[10])) return false;
-    sz[11] = G4 * f;
+    sz[11] = (size_t)kBiasChunks * G4 * f;  // bias-gradient partial sums
     size_t *dst[12] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
                        &o->wht, &o->wcat, &o->ksp, &o->db};
     size_t off = 0;
@@ -1277,14 +1280,18 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     char *ws = static_cast<char *>(workspace);
     const char *res = static_cast<const char *>(reserve);
     float *dz = reinterpret_cast<float *>(ws + bl.dz);
-    float *dzt = reinterpret_cast<float *>(ws + bl.dzt);
-    float *xt = reinterpret_cast<float *>(ws + bl.xt);
-    float *ht = reinterpret_cast<float *>(ws + bl.ht);
+    // operands of the gradient products, in gdt: bf16 for bf16 parameters
+    // (fp32 accumulation, results rounded once), fp32 otherwise; the
+    // recurrence itself stays fp32
+    const int gdt = p->dtype;
+    char *dzt = ws + bl.dzt;   // one direction's dz^T, or (after the weight products) dz in gdt
+    char *xt = ws + bl.xt;
+    char *ht = ws + bl.ht;
     float *dyb[2] = {reinterpret_cast<float *>(ws + bl.dy[0]), reinterpret_cast<float *>(ws + bl.dy[1])};
     float *dcb = reinterpret_cast<float *>(ws + bl.dc);
     float *dhnb = reinterpret_cast<float *>(ws + bl.dhn);
     float *wht = reinterpret_cast<float *>(ws + bl.wht);
-    float *wcat = reinterpret_cast<float *>(ws + bl.wcat);
+    char *wcat = ws + bl.wcat;
     float *ksp = reinterpret_cast<float *>(ws + bl.ksp);
     float *db = reinterpret_cast<float *>(ws + bl.db);
     const int dt = p->dtype, H = p->H, D = p->D, G4 = 4 * H;
@@ -1297,7 +1304,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     // out[M][N] = A[M][K] Bm[N][K]^T in fp32, rounded once to out_dt; split
     // over K (slabs in ksp, summed in order) when the product has few output
     // tiles, else computed into f32 (out itself when out_dt is fp32)
-    auto gemm_nt = [&](const float *A, int lda, const float *Bm, int M, int N, int K, void *out, int out_dt,
+    auto gemm_nt = [&](const void *A, int lda, const void *Bm, int M, int N, int K, void *out, int out_dt,
                        float *f32) {
         ProjArgs g{};
         g.X = A;
@@ -1318,15 +1325,15 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         } end{p, sp, st};
         if (g.kchunk) {
             g.G = ksp;
-            return ok(launch_proj(g, DT_F32, 0, st)) &&
+            return ok(launch_proj(g, gdt, 0, st)) &&
                    ok(launch_ksum(ksp, (K + g.kchunk - 1) / g.kchunk, mn, mn, out, out_dt, st));
         }
         if (out_dt == DT_F32) {
             g.G = static_cast<float *>(out);
-            return ok(launch_proj(g, DT_F32, 0, st));
+            return ok(launch_proj(g, gdt, 0, st));
         }
         g.G = f32;
-        return ok(launch_proj(g, DT_F32, 0, st)) && ok(launch_cast_to(f32, out, mn, out_dt, st));
+        return ok(launch_proj(g, gdt, 0, st)) && ok(launch_cast_to(f32, out, mn, out_dt, st));
     };
     if (p->timing) p->acc.bwd_calls += 1;
     // the gradient of the top layer's output, as fp32
@@ -1342,7 +1349,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         // W_hh^T per direction for the recurrent products
         for (int d = 0; d < D; ++d)
             if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per + 1], H, G4, H, wht + (size_t)d * H * G4,
-                                     G4, dt, st)))
+                                     G4, dt, DT_F32, st)))
                 return fail();
         if (dh_n && !ok(launch_cast_from(static_cast<const char *>(dh_n) + (size_t)l * DBH * es, dhnb, DBH, dt, st)))
             return fail();
@@ -1378,11 +1385,12 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         if (dc0 && hipMemcpyAsync(dc0 + (size_t)l * DBH, dcb, DBH * sizeof(float), hipMemcpyDeviceToDevice, st) !=
                        hipSuccess)
             return fail();
-        // weight gradients: dW_ih = dz^T x, dW_hh = dz^T h_prev, db = sum of dz
-        if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, st))) return fail();
+        // weight gradients: dW_ih = dz^T x, dW_hh = dz^T h_prev (operands in
+        // gdt), db = sum of dz (fp32 column sums in fixed chunks, then in order)
+        if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, gdt, st))) return fail();
         for (int d = 0; d < D; ++d) {
             void *const *dwd = dweights + (size_t)(l * D + d) * per;
-            if (!ok(launch_transpose(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, dzt, TB, DT_F32, st)) ||
+            if (!ok(launch_transpose(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, dzt, TB, DT_F32, gdt, st)) ||
                 !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, T, B, H, d, ht, dt,
                                    st)))
                 return fail();
@@ -1390,19 +1398,27 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
                 !gemm_nt(dzt, (int)TB, ht, G4, H, (int)TB, dwd[1], dt, ksp))
                 return fail();
             if (p->has_bias) {
-                if (!ok(launch_rowsum(dzt, TB, G4, (int)TB, db, st)) || !ok(launch_cast_to(db, dwd[2], G4, dt, st)) ||
-                    !ok(launch_cast_to(db, dwd[3], G4, dt, st)))
+                const int chunk = (int)((TB + kBiasChunks - 1) / kBiasChunks);
+                const int nch = (int)((TB + chunk - 1) / chunk);
+                if (!ok(launch_colsum_part(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, kBiasChunks, db, st)) ||
+                    !ok(launch_ksum(db, nch, G4, G4, dwd[2], dt, st)) || !ok(launch_ksum(db, nch, G4, G4, dwd[3], dt, st)))
                     return fail();
             }
         }
         // input gradient dX = sum over directions of dz W_ih, the next dY
         if (l > 0 || dx) {
             for (int d = 0; d < D; ++d)
-                if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per], in_l, G4, in_l, wcat + (size_t)d * G4,
-                                         (size_t)D * G4, dt, st)))
+                if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per], in_l, G4, in_l,
+                                         wcat + (size_t)d * G4 * elem_size(gdt), (size_t)D * G4, dt, gdt, st)))
                     return fail();
+            // dz as the product's A operand: itself (fp32), or a gdt copy in dzt's space
+            const void *dzA = dz;
+            if (gdt != DT_F32) {
+                if (!ok(launch_cast_to(dz, dzt, TB * D * G4, gdt, st))) return fail();
+                dzA = dzt;
+            }
             const bool out_dx = l == 0;
-            if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
+            if (!gemm_nt(dzA, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
                          dyb[cur ^ 1]))
                 return fail();
             // through the dropout the layer below's output was sent up with
