@@ -37,6 +37,7 @@ namespace lstm_amd {
 // direction's scan) at (d, b, j): from dh = dY + dh_rec (the recurrent
 // product of the step after it) and the carried dc, the pre-activation
 // gradients dz of the four gates and dc for the step before it.
+template <class G>
 __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int b, int j, float dh_rec) {
     const int T = a.T, B = a.B, H = a.H, D = a.D;
     const int sf = T - 1 - sb;                   // the forward scan's step
@@ -59,20 +60,21 @@ __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int 
                                 : a.acts[(((size_t)tp * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
     const float tc = tanh_f(c);
     const float dct = dcn + dh * og * (1.f - tc * tc);
-    float *dz = a.dz + (((size_t)t * B + b) * D + d) * 4 * H + j;
-    dz[0] = dct * gg * ig * (1.f - ig);
-    dz[(size_t)H] = dct * cprev * fg * (1.f - fg);
-    dz[(size_t)2 * H] = dct * ig * (1.f - gg * gg);
-    dz[(size_t)3 * H] = dh * tc * og * (1.f - og);
+    typename G::S *dz = static_cast<typename G::S *>(a.dz) + (((size_t)t * B + b) * D + d) * 4 * H + j;
+    dz[0] = G::from_f(dct * gg * ig * (1.f - ig));
+    dz[(size_t)H] = G::from_f(dct * cprev * fg * (1.f - fg));
+    dz[(size_t)2 * H] = G::from_f(dct * ig * (1.f - gg * gg));
+    dz[(size_t)3 * H] = G::from_f(dh * tc * og * (1.f - og));
     a.dc[dbj] = dct * fg;
 }
 
 // The first backward step of every (direction, batch row, unit): dh = dY + dh_n.
+template <class G>
 __global__ void k_bwd_cell(BwdCellArgs a) {
     const size_t n = (size_t)a.D * a.B * a.H;
     const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
-    bwd_cell_update(a, 0, (int)(i / ((size_t)a.H * a.B)), (int)((i / a.H) % a.B), (int)(i % a.H), 0.f);
+    bwd_cell_update<G>(a, 0, (int)(i / ((size_t)a.H * a.B)), (int)((i / a.H) % a.B), (int)(i % a.H), 0.f);
 }
 
 // Backward step sb: the recurrent product dh_prev = dz_t W_hh of step sb for
@@ -80,49 +82,52 @@ __global__ void k_bwd_cell(BwdCellArgs a) {
 // K = 4H (stacked gate order), then the cell update of step sb + 1 for the
 // tile's cells -- or, after the scan's first step (sb = T - 1), dh0.
 //   whT[d][j][k] = W_hh[d][k][j]: K-contiguous rows, as are dz's
-// The four waves take a quarter of K each (16x16x4 fp32 MFMAs whose
-// fragments are 16-byte loads); their tiles meet in LDS, one output per
-// thread.  A whole tile's K lives in one workgroup, so no partial sums leave
-// it and nothing waits on another workgroup.
-template <class DT>
+// The four waves take a quarter of K each (16x16 MFMAs in the gradient
+// dtype G, fp32 accumulation, fragments of 16-byte loads); their tiles meet
+// in LDS, one output per thread.  A whole tile's K lives in one workgroup, so
+// no partial sums leave it and nothing waits on another workgroup.
+template <class G, class DT>
 __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, typename DT::S *dh0) {
+    using S = typename G::S;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.B, H = a.H, D = a.D, K = 4 * H;
     const int d = blockIdx.z, b0 = blockIdx.x * 16, u0 = blockIdx.y * 16;
     const int b = b0 + (lane & 15);  // A row (batch row) of this lane
     const int j = u0 + (lane & 15);  // B row (unit) of this lane
-    const int kq = (K + 63) / 64 * 16;  // K per wave, whole 16-chunks
+    const int kq = (K + 4 * G::KC - 1) / (4 * G::KC) * G::KC;  // K per wave, whole chunks
     const int k_lo = w * kq, k_hi = min(K, k_lo + kq);
     const int sf = a.T - 1 - a.sb;
     const int t = d == 0 ? sf : a.T - 1 - sf;
+    constexpr unsigned es = sizeof(S);
     // dz rows (t, b, d) for b < B and whT rows (d, j) for j < H through buffer
     // resources: a row past B or H, or a chunk past the wave's K range, gets
     // an out-of-range offset and reads zeros without a memory access
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.dz + ((size_t)t * B * D + d) * (size_t)K), (short)0,
-        (int)(((size_t)(B - 1) * D * K + K) * sizeof(float)), 0x00020000);
+        const_cast<S *>(static_cast<const S *>(a.dz) + ((size_t)t * B * D + d) * (size_t)K), (short)0,
+        (int)(((size_t)(B - 1) * D * K + K) * es), 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.whT + (size_t)d * H * K), (short)0, (int)((size_t)H * K * sizeof(float)), 0x00020000);
-    const unsigned aoff = (unsigned)((size_t)b * D * K * sizeof(float));
-    const unsigned boff = (unsigned)((size_t)j * K * sizeof(float));
+        const_cast<S *>(static_cast<const S *>(a.whT) + (size_t)d * H * K), (short)0, (int)((size_t)H * K * es),
+        0x00020000);
+    const unsigned aoff = (unsigned)((size_t)b * D * K * es);
+    const unsigned boff = (unsigned)((size_t)j * K * es);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     // batches of 16 chunks: all 32 fragment loads are issued before the first
     // product of the batch; scheduling barriers keep the compiler from
     // interleaving them with the products into a chain of round trips
     constexpr int NBAT = 16;
     constexpr unsigned OOR = 0x7FFFFFF0u;
-    for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * F32::KC) {
+    for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * G::KC) {
         u32x4 av[NBAT], bv[NBAT];
 #pragma unroll
         for (int q = 0; q < NBAT; ++q) {
-            const int k = k0 + q * F32::KC + (lane >> 4) * F32::PER16;
+            const int k = k0 + q * G::KC + (lane >> 4) * G::PER16;
             const bool kin = k < k_hi;
-            av[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + 4u * k : OOR), 0, 0);
-            bv[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + 4u * k : OOR), 0, 0);
+            av[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + es * k : OOR), 0, 0);
+            bv[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + es * k : OOR), 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < NBAT; ++q) acc = mma_chunk(F32{}, acc, av[q], bv[q]);
+        for (int q = 0; q < NBAT; ++q) acc = mma_chunk(G{}, acc, av[q], bv[q]);
         __builtin_amdgcn_sched_barrier(0);
     }
     // lane l, register v: batch row 4 (l / 16) + v, unit l % 16 of the tile
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
     const int m = b0 + rb_, u = u0 + ru;
     if (m >= B || u >= H) return;
     const float r = red[0][rb_][ru] + red[1][rb_][ru] + red[2][rb_][ru] + red[3][rb_][ru];
-    if (a.sb + 1 < a.T) bwd_cell_update(c, a.sb + 1, d, m, u, r);
+    if (a.sb + 1 < a.T) bwd_cell_update<G>(c, a.sb + 1, d, m, u, r);
     else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r);
 }
 
@@ -158,9 +163,9 @@ __global__ void k_transpose(const typename DI::S *in, size_t ld_in, int rows, in
 // out[k][m] = h_prev of direction d for row m = t*B + b (k < H, m < T*B):
 // the layer's output at the time of the scan's previous step, or h0 (NULL =
 // zeros) at the scan's first step.
-template <class DT>
+template <class DT, class DO>
 __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, int T, int B, int H,
-                          int d, typename DT::S *out) {
+                          int d, typename DO::S *out) {
     __shared__ float tile[32][33];
     const int m0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int M = T * B;
@@ -178,14 +183,15 @@ __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT
     __syncthreads();
     for (int kk = threadIdx.y; kk < 32; kk += 8) {
         const int k = k0 + kk, m = m0 + threadIdx.x;
-        if (k < H && m < M) out[(size_t)k * M + m] = DT::from_f(tile[threadIdx.x][kk]);
+        if (k < H && m < M) out[(size_t)k * M + m] = DO::from_f(tile[threadIdx.x][kk]);
     }
 }
 
 // Column sums in fixed row chunks: part[c][col] = sum over rows r in chunk c
 // (rows c*chunk .. ) of a[r * ld + col], each summed in row order; the
 // chunks are then added in order by k_ksum (deterministic).
-__global__ void k_colsum_part(const float *a, size_t ld, int rows, int cols, int chunk, float *part) {
+template <class DT>
+__global__ void k_colsum_part(const typename DT::S *a, size_t ld, int rows, int cols, int chunk, float *part) {
     const int col = blockIdx.x * blockDim.x + threadIdx.x;
     if (col >= cols) return;
     const int r0 = blockIdx.y * chunk, r1 = min(rows, r0 + chunk);
@@ -194,11 +200,11 @@ __global__ void k_colsum_part(const float *a, size_t ld, int rows, int cols, int
     for (; r + 8 <= r1; r += 8) {  // eight loads in flight, added in row order
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * ld + col];
+        for (int q = 0; q < 8; ++q) v[q] = DT::to_f(a[(size_t)(r + q) * ld + col]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) s += v[q];
     }
-    for (; r < r1; ++r) s += a[(size_t)r * ld + col];
+    for (; r < r1; ++r) s += DT::to_f(a[(size_t)r * ld + col]);
     part[(size_t)blockIdx.y * cols + col] = s;
 }
 
@@ -290,19 +296,26 @@ static unsigned grid1(size_t n, unsigned cap = 8192) {
     return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 
-hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s) {
+hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s) {
     const size_t n = (size_t)a.D * a.B * a.H;
-    hipLaunchKernelGGL(k_bwd_cell, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (gdt == DT_BF16) hipLaunchKernelGGL(k_bwd_cell<BF16>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_bwd_cell<F32>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int dtype, hipStream_t s) {
+hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s) {
     if (c.dz != a.dz || c.T != a.T || c.B != a.B || c.H != a.H || c.D != a.D) return hipErrorInvalidValue;
+    if (gdt == DT_BF16 && a.H % 2 != 0) return hipErrorInvalidValue;  // whole bf16 fragments over K = 4H
     dim3 grid((a.B + 15) / 16, (a.H + 15) / 16, a.D);
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(k_bwd_step<BF16>, grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
+    if (gdt == DT_BF16 && dtype == DT_BF16)
+        hipLaunchKernelGGL((k_bwd_step<BF16, BF16>), grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
+    else if (gdt == DT_BF16)
+        return hipErrorInvalidValue;
+    else if (dtype == DT_BF16)
+        hipLaunchKernelGGL((k_bwd_step<F32, BF16>), grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
     else
-        hipLaunchKernelGGL(k_bwd_step<F32>, grid, dim3(256), 0, s, a, c, static_cast<float *>(dh0));
+        hipLaunchKernelGGL((k_bwd_step<F32, F32>), grid, dim3(256), 0, s, a, c, static_cast<float *>(dh0));
     return hipGetLastError();
 }
 
@@ -327,24 +340,34 @@ hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, vo
 }
 
 hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
-                          int dtype, hipStream_t s) {
+                          int dtype, int out_dtype, hipStream_t s) {
     dim3 grid(((size_t)T * B + 31) / 32, (H + 31) / 32), block(32, 8);
     if (grid.y > 65535u) return hipErrorInvalidValue;
-    if (dtype == DT_BF16)
-        hipLaunchKernelGGL(k_hprev_t<BF16>, grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
+    if (dtype == DT_BF16 && out_dtype == DT_BF16)
+        hipLaunchKernelGGL((k_hprev_t<BF16, BF16>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
                            static_cast<const uint16_t *>(h0d), T, B, H, d, static_cast<uint16_t *>(out));
-    else
-        hipLaunchKernelGGL(k_hprev_t<F32>, grid, block, 0, s, static_cast<const float *>(Y), ldy,
+    else if (dtype == DT_BF16)
+        hipLaunchKernelGGL((k_hprev_t<BF16, F32>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
+                           static_cast<const uint16_t *>(h0d), T, B, H, d, static_cast<float *>(out));
+    else if (out_dtype == DT_F32)
+        hipLaunchKernelGGL((k_hprev_t<F32, F32>), grid, block, 0, s, static_cast<const float *>(Y), ldy,
                            static_cast<const float *>(h0d), T, B, H, d, static_cast<float *>(out));
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_colsum_part(const float *a, size_t ld, int rows, int cols, int nchunks, float *part,
+hipError_t launch_colsum_part(const void *a, size_t ld, int rows, int cols, int nchunks, float *part, int dtype,
                               hipStream_t s) {
     if (rows < 1 || cols < 1 || nchunks < 1) return hipErrorInvalidValue;
     const int chunk = (rows + nchunks - 1) / nchunks;
     dim3 grid((cols + 255) / 256, (unsigned)((rows + chunk - 1) / chunk));
-    hipLaunchKernelGGL(k_colsum_part, grid, dim3(256), 0, s, a, ld, rows, cols, chunk, part);
+    if (dtype == DT_BF16)
+        hipLaunchKernelGGL(k_colsum_part<BF16>, grid, dim3(256), 0, s, static_cast<const uint16_t *>(a), ld, rows,
+                           cols, chunk, part);
+    else
+        hipLaunchKernelGGL(k_colsum_part<F32>, grid, dim3(256), 0, s, static_cast<const float *>(a), ld, rows, cols,
+                           chunk, part);
     return hipGetLastError();
 }
 

@@ -152,32 +152,35 @@ struct BwdCellArgs {
     const float *dY;    // [T, B, D*H] gradient of this layer's output
     const float *dhn;   // [D, B, H] gradient of h_n of this layer, or NULL
     const float *dcn;   // [D, B, H] gradient of c_n of this layer, or NULL
-    float *dz;          // [T, B, D, 4H] gradient of the pre-activations, written at each step's time
+    void *dz;           // [T, B, D, 4H] gradient of the pre-activations (gradient dtype), written at each step's time
     float *dc;          // [D, B, H] cell-state gradient carried backwards (read and written)
     int T, B, H, D;
 };
 // the recurrent product of step sb: dz_t W_hh
 struct BwdMmArgs {
-    const float *dz;    // [T, B, D, 4H]
-    const float *whT;   // [D, H, 4H] transposed W_hh, fp32
+    const void *dz;     // [T, B, D, 4H], gradient dtype
+    const void *whT;    // [D, H, 4H] transposed W_hh, gradient dtype
     int T, B, H, D, sb;
 };
+// The backward pass stores dz and multiplies it in the gradient dtype gdt:
+// bf16 (fp32 accumulation; the cell math stays fp32) for bf16 parameters
+// with an even H (whole 16-byte fragments over K = 4H), fp32 otherwise.
 // The first backward step of a layer (dh = dY + dh_n), elementwise.
-hipError_t launch_bwd_cell(const BwdCellArgs &a, hipStream_t s);
+hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s);
 // Backward step a.sb: the recurrent product, then the cell update of step
 // a.sb + 1, or dh0 ([D, B, H], dtype; NULL = not wanted) after the last step.
-hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int dtype, hipStream_t s);
+hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s);
 // out[c * ld_out + r] = in[r * ld_in + c] (rows x cols, in_dtype -> out_dtype)
 hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
                             int out_dtype, hipStream_t s);
-// [H][T*B] in dtype: h_prev of direction d for every (t, b), from the layer
-// output Y or h0d ([B][H] or NULL)
+// [H][T*B] in out_dtype: h_prev of direction d for every (t, b), from the
+// layer output Y or h0d ([B][H] or NULL), both dtype (bf16 -> fp32 allowed)
 hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
-                          int dtype, hipStream_t s);
+                          int dtype, int out_dtype, hipStream_t s);
 // part[c][col] (c < the chunk count launched, at most nchunks) = sum over
 // the rows of chunk c of a[r * ld + col]; rows split into ceil(rows /
 // nchunks)-row chunks, each summed in row order
-hipError_t launch_colsum_part(const float *a, size_t ld, int rows, int cols, int nchunks, float *part,
+hipError_t launch_colsum_part(const void *a, size_t ld, int rows, int cols, int nchunks, float *part, int dtype,
                               hipStream_t s);
 hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s);
 hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s);

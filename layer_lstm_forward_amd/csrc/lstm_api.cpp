@@ -1279,18 +1279,19 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
     hipStream_t st = static_cast<hipStream_t>(stream_);
     char *ws = static_cast<char *>(workspace);
     const char *res = static_cast<const char *>(reserve);
-    float *dz = reinterpret_cast<float *>(ws + bl.dz);
-    // operands of the gradient products, in gdt: bf16 for bf16 parameters
-    // (fp32 accumulation, results rounded once), fp32 otherwise; the
-    // recurrence itself stays fp32
-    const int gdt = p->dtype;
-    char *dzt = ws + bl.dzt;   // one direction's dz^T, or (after the weight products) dz in gdt
+    char *dz = ws + bl.dz;
+    // dz and the operands of every backward product, in the gradient dtype
+    // gdt: bf16 for bf16 parameters with an even H (fp32 accumulation, the
+    // cell math and the carries stay fp32, results rounded once), else fp32
+    const int gdt = p->dtype == LSTM_BF16 && p->H % 2 == 0 ? DT_BF16 : DT_F32;
+    const size_t ges = gdt == DT_BF16 ? 2 : 4;
+    char *dzt = ws + bl.dzt;   // one direction's dz^T
     char *xt = ws + bl.xt;
     char *ht = ws + bl.ht;
     float *dyb[2] = {reinterpret_cast<float *>(ws + bl.dy[0]), reinterpret_cast<float *>(ws + bl.dy[1])};
     float *dcb = reinterpret_cast<float *>(ws + bl.dc);
     float *dhnb = reinterpret_cast<float *>(ws + bl.dhn);
-    float *wht = reinterpret_cast<float *>(ws + bl.wht);
+    char *wht = ws + bl.wht;
     char *wcat = ws + bl.wcat;
     float *ksp = reinterpret_cast<float *>(ws + bl.ksp);
     float *db = reinterpret_cast<float *>(ws + bl.db);
@@ -1348,8 +1349,8 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         const char *h0l = h0 ? static_cast<const char *>(h0) + (size_t)l * DBH * es : nullptr;
         // W_hh^T per direction for the recurrent products
         for (int d = 0; d < D; ++d)
-            if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per + 1], H, G4, H, wht + (size_t)d * H * G4,
-                                     G4, dt, DT_F32, st)))
+            if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per + 1], H, G4, H, wht + (size_t)d * H * G4 * ges,
+                                     G4, dt, gdt, st)))
                 return fail();
         if (dh_n && !ok(launch_cast_from(static_cast<const char *>(dh_n) + (size_t)l * DBH * es, dhnb, DBH, dt, st)))
             return fail();
@@ -1368,7 +1369,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         ca.B = B;
         ca.H = H;
         ca.D = D;
-        if (!ok(launch_bwd_cell(ca, st))) return fail();
+        if (!ok(launch_bwd_cell(ca, gdt, st))) return fail();
         void *dh0l = dh0 ? static_cast<char *>(dh0) + (size_t)l * DBH * es : nullptr;
         for (int sb = 0; sb < T; ++sb) {
             BwdMmArgs ma{};
@@ -1379,7 +1380,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
             ma.H = H;
             ma.D = D;
             ma.sb = sb;
-            if (!ok(launch_bwd_step(ma, ca, dh0l, dt, st))) return fail();
+            if (!ok(launch_bwd_step(ma, ca, dh0l, gdt, dt, st))) return fail();
         }
         span_end(p, rec_span, st, T);
         if (dc0 && hipMemcpyAsync(dc0 + (size_t)l * DBH, dcb, DBH * sizeof(float), hipMemcpyDeviceToDevice, st) !=
@@ -1390,9 +1391,9 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, gdt, st))) return fail();
         for (int d = 0; d < D; ++d) {
             void *const *dwd = dweights + (size_t)(l * D + d) * per;
-            if (!ok(launch_transpose(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, dzt, TB, DT_F32, gdt, st)) ||
+            if (!ok(launch_transpose(dz + (size_t)d * G4 * ges, (size_t)D * G4, (int)TB, G4, dzt, TB, gdt, gdt, st)) ||
                 !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, T, B, H, d, ht, dt,
-                                   st)))
+                                   gdt, st)))
                 return fail();
             if (!gemm_nt(dzt, (int)TB, xt, G4, in_l, (int)TB, dwd[0], dt, ksp) ||
                 !gemm_nt(dzt, (int)TB, ht, G4, H, (int)TB, dwd[1], dt, ksp))
@@ -1400,7 +1401,8 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
             if (p->has_bias) {
                 const int chunk = (int)((TB + kBiasChunks - 1) / kBiasChunks);
                 const int nch = (int)((TB + chunk - 1) / chunk);
-                if (!ok(launch_colsum_part(dz + (size_t)d * G4, (size_t)D * G4, (int)TB, G4, kBiasChunks, db, st)) ||
+                if (!ok(launch_colsum_part(dz + (size_t)d * G4 * ges, (size_t)D * G4, (int)TB, G4, kBiasChunks, db, gdt,
+                                           st)) ||
                     !ok(launch_ksum(db, nch, G4, G4, dwd[2], dt, st)) || !ok(launch_ksum(db, nch, G4, G4, dwd[3], dt, st)))
                     return fail();
             }
@@ -1409,16 +1411,10 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         if (l > 0 || dx) {
             for (int d = 0; d < D; ++d)
                 if (!ok(launch_transpose(weights[(size_t)(l * D + d) * per], in_l, G4, in_l,
-                                         wcat + (size_t)d * G4 * elem_size(gdt), (size_t)D * G4, dt, gdt, st)))
+                                         wcat + (size_t)d * G4 * ges, (size_t)D * G4, dt, gdt, st)))
                     return fail();
-            // dz as the product's A operand: itself (fp32), or a gdt copy in dzt's space
-            const void *dzA = dz;
-            if (gdt != DT_F32) {
-                if (!ok(launch_cast_to(dz, dzt, TB * D * G4, gdt, st))) return fail();
-                dzA = dzt;
-            }
             const bool out_dx = l == 0;
-            if (!gemm_nt(dzA, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
+            if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
                          dyb[cur ^ 1]))
                 return fail();
             // through the dropout the layer below's output was sent up with

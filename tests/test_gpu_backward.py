@@ -3,7 +3,8 @@ ABI) against the fp64 oracle's backward on the same seeded inputs.
 
 Gradients are compared by max-abs error relative to the gradient's own scale,
 max(1, max|reference|): 1e-4 for fp32, 3e-2 for bf16 (the bf16 forward rounds h
-to bf16 where it is stored, and the backward reuses those stored outputs).
+to bf16 where it is stored, and the backward reuses those stored outputs; with
+an even H it also keeps dz in bf16 for its products, fp32 accumulation).
 """
 import numpy as np
 import pytest
@@ -28,6 +29,8 @@ SPECS = [
     Spec(20, 24, 1, True, 35, 20, "f32", 808, "normal0.1"),     # a ragged last split (384 + 316)
     Spec(64, 128, 2, True, 48, 24, "bf16", 810, "normal0.1"),   # bf16 weights, 320-deep splits
     Spec(32, 64, 1, False, 256, 256, "f32", 809, "normal0.1"),  # 256x256 direct-to-LDS tiles, 256 splits
+    # bf16 parameters with an odd H: dz and the backward products stay fp32
+    Spec(30, 37, 2, True, 6, 9, "bf16", 811, "normal0.1"),
 ]
 
 
