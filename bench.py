@@ -130,13 +130,23 @@ def summarize_profile(path, command):
     return "\n".join(lines)
 
 
-def kernel_source_hash():
-    """sha256 of the kernel sources; a stored counter profile is valid only for
-    the sources it was taken from."""
+def kernel_source_hash(kernel):
+    """sha256 of the sources of `kernel` (its .hip file and the shared device
+    headers; "a+b": of each kernel's); a stored counter profile is valid only
+    for the sources it was taken from."""
     import hashlib
+    import re as _re
+    csrc = os.path.join(ROOT, "layer_lstm_forward_amd", "csrc")
+    files = set()
+    for k in kernel.split("+"):
+        for name in ("backward.hip", "kernels.hip"):
+            with open(os.path.join(csrc, name)) as fh:
+                if _re.search(r"\b" + _re.escape(k.strip()) + r"\s*\(", fh.read()):
+                    files.add(name)
+                    break
     h = hashlib.sha256()
-    for f in ("kernels.hip", "backward.hip", "device.h", "kernels.h"):
-        with open(os.path.join(ROOT, "layer_lstm_forward_amd", "csrc", f), "rb") as fh:
+    for f in sorted(files) + ["device.h", "kernels.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -180,7 +190,7 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, wo
              f"# command: {command}",
              f"# workload: {workload}",
              f"# kernel: {name}",
-             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"kernel_source_sha256: {kernel_source_hash(kernel)}",
              f"copy_calibration: FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for a 262144 KiB copy "
              f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
              f"FETCH_SIZE_KiB_per_dispatch: {kf:.1f} (over {nf} dispatches)",
@@ -203,7 +213,7 @@ def stored_traffic(kernel, workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(kernel):
         return None
     return float(fields["traffic_bytes_per_launch"])
 
