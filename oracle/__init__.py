@@ -62,7 +62,7 @@ def _load():
         lib.oracle_lstm_backward.restype = ctypes.c_int
         lib.oracle_lstm_backward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
+            dp, ctypes.POINTER(ctypes.c_int), dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(dp)]
         lib.oracle_rnn_forward.restype = ctypes.c_int
         lib.oracle_rnn_forward.argtypes = [
@@ -162,7 +162,7 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
 
 def lstm_backward(x, params, hidden_size: int, num_layers: int, bidirectional: bool, dy,
                   h0=None, c0=None, dh_n=None, dc_n=None, has_bias: bool = True, bf16: bool = False,
-                  dropout=None):
+                  dropout=None, lengths=None):
     """Gradients of the forward pass (see the C file).
 
     dy [T, B, D*H]; dh_n, dc_n [L*D, B, H] or None (zeros).
@@ -192,7 +192,13 @@ def lstm_backward(x, params, hidden_size: int, num_layers: int, bidirectional: b
     dc0 = np.empty((L * D, B, H), np.float64)
     opt = lambda a: _ptr(a) if a is not None else None  # noqa: E731
     dp_, seed, call = (0.0, 0, 0) if dropout is None else dropout
-    rc = lib.oracle_lstm_backward(T, B, I, H, L, D, _ptr(x64), opt(h064), opt(c064), arr, 1 if has_bias else 0,
+    len32 = None
+    if lengths is not None:
+        len32 = np.ascontiguousarray(np.asarray(lengths, np.int32))
+        if len32.shape != (B,):
+            raise ValueError(f"lengths shape {len32.shape} != {(B,)}")
+    lenp = len32.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if len32 is not None else None
+    rc = lib.oracle_lstm_backward(T, B, I, H, L, D, _ptr(x64), lenp, opt(h064), opt(c064), arr, 1 if has_bias else 0,
                                   float(dp_), int(seed), int(call), _ptr(dy64), opt(dhn), opt(dcn), _ptr(dx), _ptr(dh0), _ptr(dc0), darr)
     if rc != 0:
         raise RuntimeError(f"oracle_lstm_backward failed with {rc}")

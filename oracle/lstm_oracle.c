@@ -274,9 +274,13 @@ static int forward_core(int T, int B, int I, int H, int L, int D,
  *   dparams: same order and shapes as params (W_ih, W_hh[, b_ih, b_hh]),
  *            overwritten (not accumulated into)
  * drop_p, seed, call: the dropout of the training forward (drop_p = 0: none).
+ * lengths: NULL or per-row lengths as in oracle_lstm_forward_lengths.  At a
+ * padded step the forward left h and c alone and output 0, so there the
+ * pre-activation gradients are 0, and the cell-state gradient and the
+ * gradient of h pass on to the step before unchanged.
  * The forward is recomputed here; its per-step activations are kept. */
 int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
-                         const double *x, const double *h0, const double *c0,
+                         const double *x, const int *lengths, const double *h0, const double *c0,
                          const double *const *params, int has_bias,
                          double drop_p, uint64_t seed, uint64_t call,
                          const double *dy, const double *dh_n, const double *dc_n,
@@ -285,6 +289,9 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
     if (T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) || !x || !params || !dy ||
         !(drop_p >= 0.0 && drop_p <= 1.0))
         return -1;
+    if (lengths)
+        for (int b = 0; b < B; ++b)
+            if (lengths[b] < 1 || lengths[b] > T) return -1;
     const int per = has_bias ? 4 : 2;
     const int G = 4 * H;
     const size_t BH = (size_t)B * H, TBH = (size_t)T * BH;
@@ -318,6 +325,16 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
             for (int s = 0; s < T; ++s) {
                 const int t = d == 0 ? s : T - 1 - s;
                 for (int b = 0; b < B; ++b) {
+                    if (PADDED(t, b)) {  /* the state stays; the output is 0 */
+                        for (int j = 0; j < H; ++j) {
+                            const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
+                            gi[e] = gf[e] = gg[e] = go[e] = 0.0;
+                            cs[e] = c[(size_t)b * H + j];
+                            hs[e] = h[(size_t)b * H + j];
+                            out_seq[((size_t)t * B + b) * (D * H) + (size_t)d * H + j] = 0.0;
+                        }
+                        continue;
+                    }
                     const double *xt = in_seq + ((size_t)t * B + b) * in_w;
                     double pre[4];
                     for (int j = 0; j < H; ++j) {
@@ -379,6 +396,10 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
                 const int t = d == 0 ? s : T - 1 - s;
                 const int tp = d == 0 ? t - 1 : t + 1; /* time of the scan's previous step */
                 for (int b = 0; b < B; ++b) {
+                    if (PADDED(t, b)) {  /* no gate took part: dc (and dh, below) pass on unchanged */
+                        for (int r = 0; r < G; ++r) dz[(size_t)b * G + r] = 0.0;
+                        continue;
+                    }
                     for (int j = 0; j < H; ++j) {
                         const size_t e = ld + (size_t)t * BH + (size_t)b * H + j;
                         const size_t eb = (size_t)b * H + j;
@@ -407,7 +428,8 @@ int oracle_lstm_backward(int T, int B, int I, int H, int L, int D,
                     for (int k = 0; k < H; ++k) {
                         double acc = 0.0;
                         for (int r = 0; r < G; ++r) acc += dz[(size_t)b * G + r] * p[1][(size_t)r * H + k];
-                        dh[(size_t)b * H + k] = acc;
+                        /* a padded step's h was its predecessor's: its gradient passes through */
+                        dh[(size_t)b * H + k] = PADDED(t, b) ? dhn[(size_t)b * H + k] : acc;
                     }
                     for (int k = 0; k < in_w; ++k) {
                         double acc = 0.0;

@@ -94,3 +94,55 @@ def test_backward_matches_torch_autograd_fp64():
     np.testing.assert_allclose(dc0, c0t.grad.numpy(), rtol=0, atol=1e-11)
     for k, p in enumerate(m._flat_weights):
         np.testing.assert_allclose(dps[k], p.grad.numpy(), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("L,bidir,lens", [(1, False, [3, 1, 4]), (2, True, [2, 4, 1]), (2, False, [4, 4, 2])])
+def test_backward_with_lengths_matches_finite_differences(L, bidir, lens):
+    # per-row lengths: padded steps leave the state alone and output 0, so the
+    # gradients must flow around them; checked against finite differences of
+    # the lengths forward (itself pinned by the brute force)
+    spec = Spec(2, 2, L, bidir, 4, 3, "f32", 4500 + L, "normal0.1")
+    inp = make_inputs(spec)
+    H = spec.hidden_size
+    params = [p.astype(np.float64) * 3.0 for p in inp.params]
+    x, h0, c0 = (a.astype(np.float64) for a in (inp.x, inp.h0, inp.c0))
+    wy, whn, wcn = _weights(spec, 23)
+    lengths = np.array(lens, np.int32)
+    dx, dh0, dc0, dps = oracle.lstm_backward(x, params, H, L, bidir, wy, h0=h0, c0=c0, dh_n=whn, dc_n=wcn,
+                                             lengths=lengths)
+
+    def loss():
+        y, hn, cn = oracle.lstm_forward(x, params, H, L, bidir, h0=h0, c0=c0, lengths=lengths)
+        return float(np.sum(wy * y) + np.sum(whn * hn) + np.sum(wcn * cn))
+
+    eps = 1e-6
+
+    def fd(arr):
+        g = np.empty_like(arr)
+        for idx in np.ndindex(arr.shape):
+            v = arr[idx]
+            arr[idx] = v + eps
+            lp = loss()
+            arr[idx] = v - eps
+            lm = loss()
+            arr[idx] = v
+            g[idx] = (lp - lm) / (2 * eps)
+        return g
+
+    np.testing.assert_allclose(dx, fd(x), rtol=0, atol=2e-7)
+    np.testing.assert_allclose(dh0, fd(h0), rtol=0, atol=2e-7)
+    np.testing.assert_allclose(dc0, fd(c0), rtol=0, atol=2e-7)
+    for k, q in enumerate(params):
+        np.testing.assert_allclose(dps[k], fd(q), rtol=0, atol=2e-7, err_msg=f"param {k}")
+
+
+def test_backward_with_full_lengths_is_the_plain_backward():
+    spec = Spec(3, 4, 2, True, 5, 3, "f32", 4600, "normal0.1")
+    inp = make_inputs(spec)
+    dy = np.random.default_rng(3).standard_normal((5, 3, 8))
+    a = oracle.lstm_backward(inp.x, inp.params, 4, 2, True, dy, h0=inp.h0, c0=inp.c0)
+    b = oracle.lstm_backward(inp.x, inp.params, 4, 2, True, dy, h0=inp.h0, c0=inp.c0, lengths=[5, 5, 5])
+    for u, v in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(u, v)
+    for u, v in zip(a[3], b[3]):
+        np.testing.assert_array_equal(u, v)

@@ -42,6 +42,11 @@ BACKWARD_MUTATIONS = {
     "bwd_one_bias_only": ("dp[3][r] += z;", "dp[3][r] += 0.0 * z;"),
     "bwd_no_recurrent_gradient": ("for (size_t e = 0; e < BH; ++e) dhn[e] = dh[e];",
                                   "for (size_t e = 0; e < BH; ++e) dhn[e] = 0.0 * dh[e];"),
+    # per-row lengths: the gradient of h dropped at a padded step; the state
+    # before the reverse scan's first valid step taken as zero
+    "bwd_padded_dh_dropped": ("dh[(size_t)b * H + k] = PADDED(t, b) ? dhn[(size_t)b * H + k] : acc;",
+                              "dh[(size_t)b * H + k] = acc;"),
+    "bwd_padded_state_lost": ("hs[e] = h[(size_t)b * H + j];", "hs[e] = 0.0;"),
 }
 
 
