@@ -216,7 +216,7 @@ lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *leng
  * c_n) and a reserve of activations saved by the forward; the pulsatrix
  * "LSTMModule" reference describes the backpropagation through time across
  * the four gates and the cell carry.  Time-major layout only (batch_first is
- * LSTM_ERR_UNSUPPORTED), all rows of length T. */
+ * LSTM_ERR_UNSUPPORTED); per-row lengths through the _lengths variants. */
 
 /* Training dropout between layers.  The trace page's Performance Notes apply
  * dropout to the input of every layer above the first, in training only
@@ -251,6 +251,15 @@ lstm_status lstm_forward_train(lstm_plan *plan, const void *x, const void *h0, c
                                void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* lstm_forward_train over per-row lengths (B host values in 1..T, as for
+ * lstm_forward_lengths): the reserve then also serves lstm_backward_lengths
+ * with the same lengths.  NULL lengths or a length outside 1..T is
+ * LSTM_ERR_ARG. */
+lstm_status lstm_forward_train_lengths(lstm_plan *plan, const void *x, const int *lengths, const void *h0,
+                                       const float *c0, const void *const *weights, int T, int B, int layers,
+                                       int bidir, void *y, void *h_n, float *c_n, void *reserve,
+                                       size_t reserve_bytes, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace lstm_backward needs for (T, B) (all fp32: the
  * pre-activation gradients of a layer and their transpose, transposed
  * operands, two output-gradient buffers, partial sums). */
@@ -277,6 +286,17 @@ lstm_status lstm_backward(lstm_plan *plan, const void *x, const void *h0, const 
                           const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
                           int bidir, void *dx, void *dh0, float *dc0, void *const *dweights, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* lstm_backward of a lstm_forward_train_lengths call, with the same lengths.
+ * At a padded step (t >= length of the row) the forward left h and c alone
+ * and output 0, so no gate gradient arises there and the gradients of h and
+ * c pass on unchanged to the step before; dy at padded steps is ignored and
+ * dx there is 0.  NULL lengths or a length outside 1..T is LSTM_ERR_ARG. */
+lstm_status lstm_backward_lengths(lstm_plan *plan, const void *x, const int *lengths, const void *h0,
+                                  const float *c0, const void *const *weights, const void *y, const void *dy,
+                                  const void *dh_n, const float *dc_n, const void *reserve, size_t reserve_bytes,
+                                  int T, int B, int layers, int bidir, void *dx, void *dh0, float *dc0,
+                                  void *const *dweights, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronise `stream` and read the kernel status word a previous
  * lstm_forward left in `workspace`: *device_flags = 0 if every step barrier

@@ -81,6 +81,13 @@ def load_library():
     lib.lstm_backward.restype = i
     lib.lstm_backward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp, sz, i, i, i, i, vp, vp,
                                   vp, ctypes.POINTER(vp), vp, sz, vp]
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.lstm_forward_train_lengths.restype = i
+    lib.lstm_forward_train_lengths.argtypes = [vp, vp, ip, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp,
+                                               sz, vp, sz, vp]
+    lib.lstm_backward_lengths.restype = i
+    lib.lstm_backward_lengths.argtypes = [vp, vp, ip, vp, vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp, sz, i, i, i,
+                                          i, vp, vp, vp, ctypes.POINTER(vp), vp, sz, vp]
     lib.lstm_device_status.restype = i
     lib.lstm_device_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint)]
     lib.lstm_describe.restype = i
@@ -196,22 +203,34 @@ def _ptrs(addrs):
     return (ctypes.c_void_p * len(addrs))(*[int(a) for a in addrs])
 
 
+def _lens(lengths):
+    return None if lengths is None else (ctypes.c_int * len(lengths))(*[int(v) for v in lengths])
+
+
 def lstm_forward_train(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, reserve, reserve_bytes,
-                       workspace, workspace_bytes, stream) -> int:
+                       workspace, workspace_bytes, stream, lengths=None) -> int:
+    """lengths: None, or B host ints (lstm_forward_train_lengths)."""
     v = ctypes.c_void_p
-    return int(load_library().lstm_forward_train(
-        v(plan), v(x), v(h0 or None), v(c0 or None), _ptrs(weights), int(T), int(B), int(layers), int(bool(bidir)),
-        v(y), v(h_n or None), v(c_n or None), v(reserve), int(reserve_bytes), v(workspace), int(workspace_bytes),
-        v(stream or None)))
+    lib = load_library()
+    common = (v(h0 or None), v(c0 or None), _ptrs(weights), int(T), int(B), int(layers), int(bool(bidir)), v(y),
+              v(h_n or None), v(c_n or None), v(reserve), int(reserve_bytes), v(workspace), int(workspace_bytes),
+              v(stream or None))
+    if lengths is None:
+        return int(lib.lstm_forward_train(v(plan), v(x), *common))
+    return int(lib.lstm_forward_train_lengths(v(plan), v(x), _lens(lengths), *common))
 
 
 def lstm_backward(plan, x, h0, c0, weights, y, dy, dh_n, dc_n, reserve, reserve_bytes, T, B, layers, bidir, dx,
-                  dh0, dc0, dweights, workspace, workspace_bytes, stream) -> int:
+                  dh0, dc0, dweights, workspace, workspace_bytes, stream, lengths=None) -> int:
+    """lengths: None, or B host ints (lstm_backward_lengths)."""
     v = ctypes.c_void_p
-    return int(load_library().lstm_backward(
-        v(plan), v(x), v(h0 or None), v(c0 or None), _ptrs(weights), v(y), v(dy), v(dh_n or None), v(dc_n or None),
-        v(reserve), int(reserve_bytes), int(T), int(B), int(layers), int(bool(bidir)), v(dx or None), v(dh0 or None),
-        v(dc0 or None), _ptrs(dweights), v(workspace), int(workspace_bytes), v(stream or None)))
+    lib = load_library()
+    common = (v(h0 or None), v(c0 or None), _ptrs(weights), v(y), v(dy), v(dh_n or None), v(dc_n or None),
+              v(reserve), int(reserve_bytes), int(T), int(B), int(layers), int(bool(bidir)), v(dx or None),
+              v(dh0 or None), v(dc0 or None), _ptrs(dweights), v(workspace), int(workspace_bytes), v(stream or None))
+    if lengths is None:
+        return int(lib.lstm_backward(v(plan), v(x), *common))
+    return int(lib.lstm_backward_lengths(v(plan), v(x), _lens(lengths), *common))
 
 
 def lstm_device_status(workspace, workspace_bytes, stream):
@@ -326,9 +345,9 @@ class LSTM:
             raise LSTMError(rc, "lstm_forward_lengths" if lengths is not None else "lstm_forward")
         return y, hn, cn
 
-    def forward_train(self, x, weights, h0=None, c0=None, stream=None):
+    def forward_train(self, x, weights, h0=None, c0=None, stream=None, lengths=None):
         """Forward that also keeps the reserve for backward(); returns
-        (y, h_n, c_n, reserve)."""
+        (y, h_n, c_n, reserve).  lengths: None or B per-row lengths (host ints)."""
         import torch
         T, B, _ = x.shape
         H, L, D = self.hidden_size, self.num_layers, self.D
@@ -344,13 +363,14 @@ class LSTM:
         rc = lstm_forward_train(self.plan, x.data_ptr(), h0.data_ptr() if h0 is not None else 0,
                                 c0.data_ptr() if c0 is not None else 0, [w.data_ptr() for w in weights], T, B, L,
                                 self.bidirectional, y.data_ptr(), hn.data_ptr(), cn.data_ptr(), reserve.data_ptr(),
-                                rbytes, ws.data_ptr(), nbytes, stream)
+                                rbytes, ws.data_ptr(), nbytes, stream, lengths=lengths)
         if rc:
             raise LSTMError(rc, "lstm_forward_train")
         return y, hn, cn, reserve
 
-    def backward(self, x, weights, y, reserve, dy, h0=None, c0=None, dh_n=None, dc_n=None, stream=None):
-        """Gradients (dx, dh0, dc0, dweights) of a forward_train() call."""
+    def backward(self, x, weights, y, reserve, dy, h0=None, c0=None, dh_n=None, dc_n=None, stream=None,
+                 lengths=None):
+        """Gradients (dx, dh0, dc0, dweights) of a forward_train() call (with the same lengths)."""
         import torch
         T, B, _ = x.shape
         H, L, D = self.hidden_size, self.num_layers, self.D
@@ -366,7 +386,7 @@ class LSTM:
         rc = lstm_backward(self.plan, x.data_ptr(), addr(h0), addr(c0), [w.data_ptr() for w in weights],
                            y.data_ptr(), dy.data_ptr(), addr(dh_n), addr(dc_n), reserve.data_ptr(), reserve.numel(),
                            T, B, L, self.bidirectional, dx.data_ptr(), dh0.data_ptr(), dc0.data_ptr(),
-                           [w.data_ptr() for w in dws], ws.data_ptr(), nbytes, stream)
+                           [w.data_ptr() for w in dws], ws.data_ptr(), nbytes, stream, lengths=lengths)
         if rc:
             raise LSTMError(rc, "lstm_backward")
         return dx, dh0, dc0, dws

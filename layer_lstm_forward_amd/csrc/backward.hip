@@ -44,6 +44,22 @@ __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int 
     const int t = d == 0 ? sf : T - 1 - sf;      // its time index
     const int tp = d == 0 ? t - 1 : t + 1;       // time of the scan's previous step
     const size_t dbj = ((size_t)d * B + b) * H + j;
+    typename G::S *dz = static_cast<typename G::S *>(a.dz) + (((size_t)t * B + b) * D + d) * 4 * H + j;
+    // With per-row lengths, a padded step (the forward left h and c alone
+    // there and output 0) has zero dz; dc stays, and the gradient of h it
+    // received goes on to the step before in a.dhc, joining that step's dh.
+    if (a.len) {
+        const float carried = sb == 0 ? (a.dhn ? a.dhn[dbj] : 0.f) : a.dhc[dbj];
+        if (t >= a.len[b]) {
+            if (sb == 0) a.dc[dbj] = a.dcn ? a.dcn[dbj] : 0.f;
+            a.dhc[dbj] = dh_rec + carried;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dz[(size_t)q * H] = G::from_f(0.f);
+            return;
+        }
+        a.dhc[dbj] = 0.f;
+        if (sb > 0) dh_rec += carried;  // at sb = 0, dh_n joins below
+    }
 
     float dh = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j] + dh_rec;
     float dcn;
@@ -60,7 +76,6 @@ __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int 
                                 : a.acts[(((size_t)tp * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
     const float tc = tanh_f(c);
     const float dct = dcn + dh * og * (1.f - tc * tc);
-    typename G::S *dz = static_cast<typename G::S *>(a.dz) + (((size_t)t * B + b) * D + d) * 4 * H + j;
     dz[0] = G::from_f(dct * gg * ig * (1.f - ig));
     dz[(size_t)H] = G::from_f(dct * cprev * fg * (1.f - fg));
     dz[(size_t)2 * H] = G::from_f(dct * ig * (1.f - gg * gg));
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
     if (m >= B || u >= H) return;
     const float r = red[0][rb_][ru] + red[1][rb_][ru] + red[2][rb_][ru] + red[3][rb_][ru];
     if (a.sb + 1 < a.T) bwd_cell_update<G>(c, a.sb + 1, d, m, u, r);
-    else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r);
+    else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r + (c.len ? c.dhc[((size_t)d * B + m) * H + u] : 0.f));
 }
 
 // out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (DI in, DO out)
@@ -164,8 +179,8 @@ __global__ void k_transpose(const typename DI::S *in, size_t ld_in, int rows, in
 // the layer's output at the time of the scan's previous step, or h0 (NULL =
 // zeros) at the scan's first step.
 template <class DT, class DO>
-__global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, int T, int B, int H,
-                          int d, typename DO::S *out) {
+__global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, const int *len, int T,
+                          int B, int H, int d, typename DO::S *out) {
     __shared__ float tile[32][33];
     const int m0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int M = T * B;
@@ -175,7 +190,8 @@ __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT
         if (m < M && k < H) {
             const int t = m / B, b = m % B;
             const int tp = d == 0 ? t - 1 : t + 1;
-            if (tp >= 0 && tp < T) v = DT::to_f(Y[((size_t)tp * B + b) * ldy + (size_t)d * H + k]);
+            if (tp >= 0 && tp < T && !(len && tp >= len[b]))  // a padded predecessor kept h0
+                v = DT::to_f(Y[((size_t)tp * B + b) * ldy + (size_t)d * H + k]);
             else if (h0d) v = DT::to_f(h0d[(size_t)b * H + k]);
         }
         tile[mm][threadIdx.x] = v;
@@ -339,19 +355,19 @@ hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, vo
     return hipGetLastError();
 }
 
-hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
-                          int dtype, int out_dtype, hipStream_t s) {
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, const int *len, int T, int B, int H, int d,
+                          void *out, int dtype, int out_dtype, hipStream_t s) {
     dim3 grid(((size_t)T * B + 31) / 32, (H + 31) / 32), block(32, 8);
     if (grid.y > 65535u) return hipErrorInvalidValue;
     if (dtype == DT_BF16 && out_dtype == DT_BF16)
         hipLaunchKernelGGL((k_hprev_t<BF16, BF16>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
-                           static_cast<const uint16_t *>(h0d), T, B, H, d, static_cast<uint16_t *>(out));
+                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, static_cast<uint16_t *>(out));
     else if (dtype == DT_BF16)
         hipLaunchKernelGGL((k_hprev_t<BF16, F32>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
-                           static_cast<const uint16_t *>(h0d), T, B, H, d, static_cast<float *>(out));
+                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, static_cast<float *>(out));
     else if (out_dtype == DT_F32)
         hipLaunchKernelGGL((k_hprev_t<F32, F32>), grid, block, 0, s, static_cast<const float *>(Y), ldy,
-                           static_cast<const float *>(h0d), T, B, H, d, static_cast<float *>(out));
+                           static_cast<const float *>(h0d), len, T, B, H, d, static_cast<float *>(out));
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -154,6 +154,8 @@ struct BwdCellArgs {
     const float *dcn;   // [D, B, H] gradient of c_n of this layer, or NULL
     void *dz;           // [T, B, D, 4H] gradient of the pre-activations (gradient dtype), written at each step's time
     float *dc;          // [D, B, H] cell-state gradient carried backwards (read and written)
+    const int *len;     // [B] valid steps per row, or NULL (all T)
+    float *dhc;         // [D, B, H] with len: the gradient of h carried through padded steps
     int T, B, H, D;
 };
 // the recurrent product of step sb: dz_t W_hh
@@ -174,9 +176,10 @@ hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, 
 hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
                             int out_dtype, hipStream_t s);
 // [H][T*B] in out_dtype: h_prev of direction d for every (t, b), from the
-// layer output Y or h0d ([B][H] or NULL), both dtype (bf16 -> fp32 allowed)
-hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, int T, int B, int H, int d, void *out,
-                          int dtype, int out_dtype, hipStream_t s);
+// layer output Y or h0d ([B][H] or NULL), both dtype (bf16 -> fp32 allowed);
+// with per-row lengths (len, or NULL) a padded predecessor's h is h0d's
+hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, const int *len, int T, int B, int H, int d,
+                          void *out, int dtype, int out_dtype, hipStream_t s);
 // part[c][col] (c < the chunk count launched, at most nchunks) = sum over
 // the rows of chunk c of a[r * ld + col]; rows split into ceil(rows /
 // nchunks)-row chunks, each summed in row order

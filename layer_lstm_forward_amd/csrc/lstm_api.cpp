@@ -206,7 +206,7 @@ bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
 // [D][H][4H] and W_ih [in][D*4H]; the K-split slabs of the gradient products;
 // one bias gradient [4H].
 struct BwdLayout {
-    size_t dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, total;
+    size_t dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, lens, dhc, total;
 };
 
 // row chunks of the bias-gradient column sums
@@ -224,7 +224,7 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     const size_t win = std::max((size_t)p->I, D * H);
     size_t tb;
     if (!mul_ok((size_t)T, (size_t)B, &tb) || tb > (size_t)INT_MAX) return false;
-    size_t sz[12];
+    size_t sz[14];
     if (!mul_ok(tb, D * G4 * f, &sz[0]) || !mul_ok(tb, G4 * f, &sz[1]) || !mul_ok(tb, win * f, &sz[2]) ||
         !mul_ok(tb, H * f, &sz[3]) || !mul_ok(tb, win * f, &sz[4]))
         return false;
@@ -246,10 +246,12 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     }
     if (!mul_ok(ksp, f, &sz[10])) return false;
     sz[11] = (size_t)kBiasChunks * G4 * f;  // bias-gradient partial sums
-    size_t *dst[12] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
-                       &o->wht, &o->wcat, &o->ksp, &o->db};
+    sz[12] = (size_t)B * sizeof(int);        // per-row lengths
+    sz[13] = D * B * H * f;                  // gradient of h carried through padded steps
+    size_t *dst[14] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
+                       &o->wht, &o->wcat, &o->ksp, &o->db, &o->lens, &o->dhc};
     size_t off = 0;
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 14; ++i) {
         *dst[i] = off;
         if (sz[i] > SIZE_MAX - off - 256) return false;
         off += align_up(sz[i]);
@@ -526,7 +528,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 106; }
+int lstm_version(void) { return 107; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -1219,11 +1221,16 @@ lstm_status lstm_reserve_size(const lstm_plan *p, int T, int B, size_t *bytes) {
     return LSTM_OK;
 }
 
-lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, const float *c0,
-                               const void *const *weights, int T, int B, int layers, int bidir, void *y,
-                               void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+static lstm_status forward_train_impl(lstm_plan *p, const void *x, const int *lengths, const void *h0,
+                                      const float *c0, const void *const *weights, int T, int B, int layers,
+                                      int bidir, void *y, void *h_n, float *c_n, void *reserve, size_t reserve_bytes,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
     if (!p || !reserve) return LSTM_ERR_ARG;
+    if (lengths) {
+        if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
+        for (int b = 0; b < B; ++b)
+            if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;
+    }
     if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     ReserveLayout rl{};
     if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
@@ -1234,10 +1241,27 @@ lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, cons
         return LSTM_ERR_DEVICE;
     }
     if (!is_device_ptr(reserve, dev)) return LSTM_ERR_DEVICE;
-    const lstm_status s = forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+    const lstm_status s = forward_impl(p, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                                        workspace_bytes, stream, static_cast<char *>(reserve));
     if (s == LSTM_OK && rl.dropout) p->drop_call += 1;  // the next call draws a fresh mask
     return s;
+}
+
+lstm_status lstm_forward_train(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                               const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                               void *h_n, float *c_n, void *reserve, size_t reserve_bytes, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return forward_train_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, reserve,
+                              reserve_bytes, workspace, workspace_bytes, stream);
+}
+
+lstm_status lstm_forward_train_lengths(lstm_plan *p, const void *x, const int *lengths, const void *h0,
+                                       const float *c0, const void *const *weights, int T, int B, int layers,
+                                       int bidir, void *y, void *h_n, float *c_n, void *reserve, size_t reserve_bytes,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!lengths) return LSTM_ERR_ARG;
+    return forward_train_impl(p, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, reserve,
+                              reserve_bytes, workspace, workspace_bytes, stream);
 }
 
 lstm_status lstm_backward_workspace_size(const lstm_plan *p, int T, int B, size_t *bytes) {
@@ -1249,13 +1273,17 @@ lstm_status lstm_backward_workspace_size(const lstm_plan *p, int T, int B, size_
     return LSTM_OK;
 }
 
-lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const float *c0,
-                          const void *const *weights, const void *y, const void *dy, const void *dh_n,
-                          const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
-                          int bidir, void *dx, void *dh0, float *dc0, void *const *dweights, void *workspace,
-                          size_t workspace_bytes, void *stream_) {
+// lengths_h: NULL (every row has T steps) or B host values, validated here
+static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths_h, const void *h0, const float *c0,
+                                 const void *const *weights, const void *y, const void *dy, const void *dh_n,
+                                 const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B,
+                                 int layers, int bidir, void *dx, void *dh0, float *dc0, void *const *dweights,
+                                 void *workspace, size_t workspace_bytes, void *stream_) {
     if (!p || !x || !weights || !y || !dy || !reserve || !dweights || !workspace) return LSTM_ERR_ARG;
     if (layers != p->L || (bidir != 0) != (p->D == 2) || T < 1 || B < 1) return LSTM_ERR_SHAPE;
+    if (lengths_h)
+        for (int b = 0; b < B; ++b)
+            if (lengths_h[b] < 1 || lengths_h[b] > T) return LSTM_ERR_ARG;
     if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
     if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     const int per = p->has_bias ? 4 : 2;
@@ -1337,6 +1365,12 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         return ok(launch_proj(g, gdt, 0, st)) && ok(launch_cast_to(f32, out, mn, out_dt, st));
     };
     if (p->timing) p->acc.bwd_calls += 1;
+    // per-row lengths on the device, and the gradient of h carried through padded steps
+    int *dlen = lengths_h ? reinterpret_cast<int *>(ws + bl.lens) : nullptr;
+    if (dlen && hipMemcpyAsync(dlen, lengths_h, (size_t)B * sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
     // the gradient of the top layer's output, as fp32
     int cur = 0;
     if (!ok(launch_cast_from(dy, dyb[cur], TB * D * H, dt, st))) return fail();
@@ -1365,6 +1399,8 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         ca.dcn = dc_n ? dc_n + (size_t)l * DBH : nullptr;
         ca.dz = dz;
         ca.dc = dcb;
+        ca.len = dlen;
+        ca.dhc = reinterpret_cast<float *>(ws + bl.dhc);
         ca.T = T;
         ca.B = B;
         ca.H = H;
@@ -1392,7 +1428,7 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         for (int d = 0; d < D; ++d) {
             void *const *dwd = dweights + (size_t)(l * D + d) * per;
             if (!ok(launch_transpose(dz + (size_t)d * G4 * ges, (size_t)D * G4, (int)TB, G4, dzt, TB, gdt, gdt, st)) ||
-                !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, T, B, H, d, ht, dt,
+                !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, dlen, T, B, H, d, ht, dt,
                                    gdt, st)))
                 return fail();
             if (!gemm_nt(dzt, (int)TB, xt, G4, in_l, (int)TB, dwd[0], dt, ksp) ||
@@ -1428,6 +1464,25 @@ lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const flo
         cur ^= 1;
     }
     return LSTM_OK;
+}
+
+lstm_status lstm_backward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                          const void *const *weights, const void *y, const void *dy, const void *dh_n,
+                          const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
+                          int bidir, void *dx, void *dh0, float *dc0, void *const *dweights, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return backward_impl(p, x, nullptr, h0, c0, weights, y, dy, dh_n, dc_n, reserve, reserve_bytes, T, B, layers,
+                         bidir, dx, dh0, dc0, dweights, workspace, workspace_bytes, stream);
+}
+
+lstm_status lstm_backward_lengths(lstm_plan *p, const void *x, const int *lengths, const void *h0, const float *c0,
+                                  const void *const *weights, const void *y, const void *dy, const void *dh_n,
+                                  const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B,
+                                  int layers, int bidir, void *dx, void *dh0, float *dc0, void *const *dweights,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    if (!lengths) return LSTM_ERR_ARG;
+    return backward_impl(p, x, lengths, h0, c0, weights, y, dy, dh_n, dc_n, reserve, reserve_bytes, T, B, layers,
+                         bidir, dx, dh0, dc0, dweights, workspace, workspace_bytes, stream);
 }
 
 lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths, const void *h0,

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 106
+    assert pkg.lstm_version() == 107
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -239,3 +239,26 @@ def test_modes_create_and_validate():
     pad = sum(2 * (up(128 * in_l * 4) + up(128 * 32 * 4) + 2 * up(128 * 4)) for in_l in (24, 64))
     for name in ("gru", "rnn_tanh", "rnn_relu"):
         assert sizes[name] - sizes["lstm"] == pad
+
+
+def test_training_lengths_validated_on_the_host():
+    # NULL lengths and lengths outside 1..T are argument errors, before any device access
+    FAKE = 0x10000
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    try:
+        common = dict(h0=0, c0=0, weights=[FAKE] * 4, T=5, B=2, layers=1, bidir=False, y=FAKE, h_n=0, c_n=0,
+                      reserve=FAKE, reserve_bytes=1 << 40, workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+        for bad in ([0, 3], [6, 1]):
+            assert pkg.lstm_forward_train(p, FAKE, lengths=bad, **common) == -1
+        v = ctypes.c_void_p
+        assert lib.lstm_forward_train_lengths(v(p), v(FAKE), None, None, None, pkg._ptrs([FAKE] * 4), 5, 2, 1, 0,
+                                              v(FAKE), None, None, v(FAKE), ctypes.c_size_t(1 << 40), v(FAKE),
+                                              ctypes.c_size_t(1 << 40), None) == -1
+        bargs = dict(h0=0, c0=0, weights=[FAKE] * 4, y=FAKE, dy=FAKE, dh_n=0, dc_n=0, reserve=FAKE,
+                     reserve_bytes=1 << 40, T=5, B=2, layers=1, bidir=False, dx=0, dh0=0, dc0=0,
+                     dweights=[FAKE] * 4, workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+        for bad in ([0, 3], [6, 1]):
+            assert pkg.lstm_backward(p, FAKE, lengths=bad, **bargs) == -1
+    finally:
+        pkg.lstm_destroy(p)

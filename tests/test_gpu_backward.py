@@ -186,3 +186,57 @@ def test_dropout_training_matches_oracle(spec, p, seed, call):
                                     has_bias=spec.has_bias, bf16=bf, dropout=(p, seed, call + 1))
     err = float(np.max(np.abs(cpu(y2) - ry2)))
     assert err <= FWD_TOL[spec.dtype], f"second call y: max-abs error {err:.3g}"
+
+
+# per-row lengths (lstm_forward_train_lengths + lstm_backward_lengths):
+# (spec, length mix, recurrence option)
+LEN_SPECS = [
+    (Spec(24, 32, 1, False, 9, 11, "f32", 831, "normal0.1"), "ragged", None),
+    (Spec(37, 52, 2, True, 7, 19, "f32", 832, "normal0.1"), "ragged", None),
+    (Spec(40, 48, 3, False, 5, 33, "f32", 833, "zeros"), "mix", None),
+    (Spec(64, 96, 2, True, 6, 20, "bf16", 834, "normal0.1"), "mix", None),
+    (Spec(32, 64, 2, True, 6, 21, "f32", 835, "normal0.1"), "ragged", "gemm"),  # one GEMM-step launch per step
+]
+
+
+@pytest.mark.parametrize("spec,mode,rec", LEN_SPECS, ids=lambda v: _id(v) if isinstance(v, Spec) else str(v))
+def test_backward_with_lengths_matches_oracle(spec, mode, rec):
+    import torch
+    from layer_lstm_forward_amd.synth import make_lengths
+    print(f"case {_id(spec)} lengths {mode} rec {rec}", flush=True)
+    inp = make_inputs(spec)
+    lens = make_lengths(spec, mode)
+    bf = spec.dtype == "bf16"
+    dev = "cuda:0"
+    dy, dhn, dcn = _grads(spec, spec.seed + 5)
+    if bf:
+        from layer_lstm_forward_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+        dy_b, dhn_b = f32_to_bf16_bits(dy), f32_to_bf16_bits(dhn)
+        dy, dhn = bf16_bits_to_f32(dy_b), bf16_bits_to_f32(dhn_b)
+    m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
+                 dtype=spec.dtype, recurrence=pkg.LSTM_REC_GEMM if rec == "gemm" else pkg.LSTM_REC_AUTO)
+    x = to_dev(inp.x, bf, dev)
+    w = [to_dev(p, bf, dev) for p in inp.params]
+    h0 = to_dev(inp.h0, bf, dev)
+    c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
+    y, hn, cn, reserve = m.forward_train(x, w, h0, c0, lengths=lens)
+    y_plain, hn_plain, cn_plain = m.forward(x, w, h0, c0, lengths=lens)
+    torch.cuda.synchronize()
+    # keeping the activations changes nothing
+    np.testing.assert_array_equal(y.float().cpu().numpy(), y_plain.float().cpu().numpy())
+    np.testing.assert_array_equal(cn.cpu().numpy(), cn_plain.cpu().numpy())
+    dy_d = to_dev(dy_b if bf else dy, bf, dev)
+    dhn_d = to_dev(dhn_b if bf else dhn, bf, dev)
+    dcn_d = torch.from_numpy(dcn).to(dev)
+    dx, dh0, dc0, dws = m.backward(x, w, y, reserve, dy_d, h0=h0, c0=c0, dh_n=dhn_d, dc_n=dcn_d, lengths=lens)
+    torch.cuda.synchronize()
+    rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, spec.hidden_size, spec.num_layers,
+                                                 spec.bidirectional, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn, dc_n=dcn,
+                                                 has_bias=spec.has_bias, bf16=bf, lengths=lens)
+    cpu = lambda t: t.float().cpu().numpy()  # noqa: E731
+    _check(cpu(dx), rdx, spec.dtype, "dx")
+    if inp.h0 is not None:
+        _check(cpu(dh0), rdh0, spec.dtype, "dh0")
+        _check(cpu(dc0), rdc0, spec.dtype, "dc0")
+    for k, (g, r) in enumerate(zip(dws, rdps)):
+        _check(cpu(g), r, spec.dtype, f"dweights[{k}]")
