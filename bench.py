@@ -317,7 +317,7 @@ def main():
     if args.train:
         if args.dropout:
             m.set_dropout(args.dropout, 1234, 0)
-        return train_bench(args, spec, m, x, w, h0, c0, stream, desc)
+        return train_bench(args, spec, m, x, w, h0, c0, stream, desc, lengths)
 
     for _ in range(args.warmup):
         m.forward(x, w, h0, c0, out=out, lengths=lengths)
@@ -397,7 +397,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
+def train_bench(args, spec, m, x, w, h0, c0, stream, desc, lengths=None):
     """A training step = lstm_forward_train + lstm_backward on the workload
     (synthetic output gradients); the value counts timestep-cells per second
     of the whole step.  The forward alone is timed beside it."""
@@ -408,16 +408,18 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     dy = torch.from_numpy(rng.standard_normal((spec.T, spec.B, spec.D * spec.hidden_size)).astype(np.float32))
     dy = dy.to(x.device).to(x.dtype)
 
+    lens = None if lengths is None else [int(v) for v in lengths]
+
     def step():
-        y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
-        return m.backward(x, w, y, reserve, dy, h0=h0, c0=c0)
+        y, hn, cn, reserve = m.forward_train(x, w, h0, c0, lengths=lens)
+        return m.backward(x, w, y, reserve, dy, h0=h0, c0=c0, lengths=lens)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ev0, ev1, ev2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     ev0.record(stream)
     for _ in range(args.steps):
-        m.forward_train(x, w, h0, c0)
+        m.forward_train(x, w, h0, c0, lengths=lens)
     ev1.record(stream)
     for _ in range(args.steps):
         step()
@@ -425,7 +427,8 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     torch.cuda.synchronize()
     fwd_ms = ev0.elapsed_time(ev1) / args.steps
     ms = ev1.elapsed_time(ev2) / args.steps
-    value = spec.cells / (ms / 1e3)
+    cells = spec.cells if lengths is None else int(np.sum(lengths)) * spec.hidden_size * spec.num_layers * spec.D
+    value = cells / (ms / 1e3)
     log(f"training step: {ms:.3f} ms (forward_train {fwd_ms:.3f} ms, backward {ms - fwd_ms:.3f} ms), "
         f"{value / 1e9:.3f} G cells/s")
 
@@ -459,7 +462,7 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle's forward + backward on a row sample")
-        cpu = cpu_baseline_train(spec, args.cpu_budget, args.dropout)
+        cpu = cpu_baseline_train(spec, args.cpu_budget, args.dropout, lengths)
         log(f"cpu baseline: {cpu}")
     line = {"metric": "LSTM training step (forward_train + backward) timestep-cells/sec", "value": value,
             "unit": "timestep-cells/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -471,7 +474,7 @@ def train_bench(args, spec, m, x, w, h0, c0, stream, desc):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_train(spec, budget_s, dropout=0.0):
+def cpu_baseline_train(spec, budget_s, dropout=0.0, lengths=None):
     """The fp64 oracle's forward + backward on a sample of batch rows (rows are
     independent), sized to the time budget from a one-row calibration."""
     import numpy as np
@@ -486,7 +489,8 @@ def cpu_baseline_train(spec, budget_s, dropout=0.0):
         sub = inp.rows(rows)
         oracle.lstm_backward(sub.x, sub.params, spec.hidden_size, spec.num_layers, spec.bidirectional,
                              np.ascontiguousarray(dy_all[:, rows]), h0=sub.h0, c0=sub.c0, has_bias=spec.has_bias,
-                             bf16=sub.bf16, dropout=(dropout, 1234, 0) if dropout else None)
+                             bf16=sub.bf16, dropout=(dropout, 1234, 0) if dropout else None,
+                             lengths=None if lengths is None else lengths[rows])
     t0 = time.perf_counter()
     run([0])
     one = time.perf_counter() - t0
@@ -495,7 +499,8 @@ def cpu_baseline_train(spec, budget_s, dropout=0.0):
     t0 = time.perf_counter()
     run(rows)
     wall = time.perf_counter() - t0
-    cells = spec.T * len(rows) * spec.hidden_size * spec.num_layers * spec.D
+    steps = spec.T * len(rows) if lengths is None else int(np.sum(lengths[rows]))
+    cells = steps * spec.hidden_size * spec.num_layers * spec.D
     return {"value": cells / wall, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {spec.B} batch rows, full T={spec.T}, all {spec.num_layers} layers, "
                       f"forward + backward in fp64 (the oracle's backward recomputes its forward), "

@@ -58,7 +58,8 @@ def _load():
         lib.oracle_lstm_forward_dropout.restype = ctypes.c_int
         lib.oracle_lstm_forward_dropout.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            dp, dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64, dp, dp, dp, ctypes.c_int]
+            dp, ctypes.POINTER(ctypes.c_int), dp, dp, ctypes.POINTER(dp), ctypes.c_int, ctypes.c_double, u64, u64,
+            dp, dp, dp, ctypes.c_int]
         lib.oracle_lstm_backward.restype = ctypes.c_int
         lib.oracle_lstm_backward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -106,7 +107,7 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     lengths None (every row has T steps) or B ints in 1..T: row b takes part
             only in steps t < lengths[b] (see the C file)
     dropout None, or (p, seed, call): the training forward's dropout between
-            layers (see the C file); not combined with lengths
+            layers (see the C file)
     Returns (y [T, B, D*H], h_n [L*D, B, H], c_n [L*D, B, H]) as float64.
     """
     lib = _load()
@@ -139,11 +140,11 @@ def lstm_forward(x, params, hidden_size: int, num_layers: int, bidirectional: bo
     hn = np.empty((L * D, B, H), np.float64)
     cn = np.empty((L * D, B, H), np.float64)
     if dropout is not None:
-        if lengths is not None:
-            raise ValueError("dropout with lengths is not supported")
         dp_, seed, call = dropout
         rc = lib.oracle_lstm_forward_dropout(
-            T, B, I, H, L, D, _ptr(x64), _ptr(h064) if h064 is not None else None,
+            T, B, I, H, L, D, _ptr(x64),
+            len32.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if len32 is not None else None,
+            _ptr(h064) if h064 is not None else None,
             _ptr(c064) if c064 is not None else None, arr, 1 if has_bias else 0, float(dp_), int(seed), int(call),
             _ptr(y), _ptr(hn), _ptr(cn), int(nthreads))
         if rc != 0:

@@ -486,14 +486,15 @@ int oracle_lstm_forward(int T, int B, int I, int H, int L, int D,
                         y, h_n, c_n, nthreads);
 }
 
-/* Training forward: dropout with probability p between layers. */
+/* Training forward: dropout with probability p between layers; lengths as
+ * for oracle_lstm_forward_lengths, or NULL. */
 int oracle_lstm_forward_dropout(int T, int B, int I, int H, int L, int D,
-                                const double *x, const double *h0, const double *c0,
+                                const double *x, const int *lengths, const double *h0, const double *c0,
                                 const double *const *params, int has_bias,
                                 double p, uint64_t seed, uint64_t call,
                                 double *y, double *h_n, double *c_n, int nthreads)
 {
-    return forward_core(T, B, I, H, L, D, x, NULL, h0, c0, params, has_bias, p, seed, call,
+    return forward_core(T, B, I, H, L, D, x, lengths, h0, c0, params, has_bias, p, seed, call,
                         y, h_n, c_n, nthreads);
 }
 

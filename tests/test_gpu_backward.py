@@ -240,3 +240,39 @@ def test_backward_with_lengths_matches_oracle(spec, mode, rec):
         _check(cpu(dc0), rdc0, spec.dtype, "dc0")
     for k, (g, r) in enumerate(zip(dws, rdps)):
         _check(cpu(g), r, spec.dtype, f"dweights[{k}]")
+
+
+def test_dropout_with_lengths_matches_oracle():
+    import torch
+    from layer_lstm_forward_amd.synth import make_lengths
+    spec = Spec(20, 48, 3, True, 7, 19, "f32", 841, "normal0.1")
+    p, seed, call = 0.35, 12345, 4
+    print(f"case {_id(spec)} dropout {p} with ragged lengths", flush=True)
+    inp = make_inputs(spec)
+    lens = make_lengths(spec, "ragged")
+    H, L, bidir, dev = spec.hidden_size, spec.num_layers, spec.bidirectional, "cuda:0"
+    m = pkg.LSTM(spec.input_size, H, L, bidir)
+    m.set_dropout(p, seed, call)
+    x = to_dev(inp.x, False, dev)
+    w = [to_dev(q, False, dev) for q in inp.params]
+    h0 = to_dev(inp.h0, False, dev)
+    c0 = torch.from_numpy(inp.c0).to(dev)
+    y, hn, cn, reserve = m.forward_train(x, w, h0, c0, lengths=lens)
+    torch.cuda.synchronize()
+    ry, rhn, rcn = oracle.lstm_forward(inp.x, inp.params, H, L, bidir, h0=inp.h0, c0=inp.c0, dropout=(p, seed, call),
+                                       lengths=lens)
+    cpu = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for got, ref, what in ((y, ry, "y"), (hn, rhn, "h_n"), (cn, rcn, "c_n")):
+        err = float(np.max(np.abs(cpu(got) - ref)))
+        assert err <= FWD_TOL["f32"], f"{what}: max-abs error {err:.3g}"
+    dy, dhn, dcn = _grads(spec, spec.seed + 5)
+    dx, dh0, dc0, dws = m.backward(x, w, y, reserve, torch.from_numpy(dy).to(dev), h0=h0, c0=c0,
+                                   dh_n=torch.from_numpy(dhn).to(dev), dc_n=torch.from_numpy(dcn).to(dev), lengths=lens)
+    torch.cuda.synchronize()
+    rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, H, L, bidir, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn,
+                                                 dc_n=dcn, dropout=(p, seed, call), lengths=lens)
+    _check(cpu(dx), rdx, "f32", "dx")
+    _check(cpu(dh0), rdh0, "f32", "dh0")
+    _check(cpu(dc0), rdc0, "f32", "dc0")
+    for k, (g, r) in enumerate(zip(dws, rdps)):
+        _check(cpu(g), r, "f32", f"dweights[{k}]")

@@ -157,3 +157,24 @@ def test_backward_with_dropout_matches_finite_differences(L, bidir, p):
     np.testing.assert_allclose(dc0, fd(c0), rtol=0, atol=2e-7)
     for k, q in enumerate(params):
         np.testing.assert_allclose(dps[k], fd(q), rtol=0, atol=2e-7, err_msg=f"param {k}")
+
+
+@pytest.mark.parametrize("L,bidir", [(2, False), (3, True)])
+def test_dropout_with_lengths_matches_brute_force(L, bidir):
+    # per-row lengths and dropout together: padded outputs are 0 before and after the mask
+    spec = _spec(L=L, bidir=bidir, T=5, B=3)
+    inp = make_inputs(spec)
+    H, D, T, B = spec.hidden_size, spec.D, spec.T, spec.B
+    p, seed, call = 0.4, 99, 7
+    lengths = [5, 2, 3]
+    between = []
+    for l in range(L - 1):
+        keep = numpy_keep_mask(p, seed, call, l, T * B * D * H).reshape(T, B, D * H)
+        between.append((keep / (1.0 - p)).tolist())
+    ref_y, ref_hn, ref_cn = brute.lstm(inp.x.tolist(), [q.tolist() for q in inp.params], H, L, D,
+                                       h0=inp.h0.tolist(), c0=inp.c0.tolist(), lengths=lengths, between=between)
+    y, hn, cn = oracle.lstm_forward(inp.x, inp.params, H, L, bidir, h0=inp.h0, c0=inp.c0, dropout=(p, seed, call),
+                                    lengths=lengths)
+    np.testing.assert_allclose(y, np.array(ref_y), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hn, np.array(ref_hn), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cn, np.array(ref_cn), rtol=0, atol=1e-13)
