@@ -215,8 +215,9 @@ lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *leng
  * the initial states and of the weights from the gradients of (output, h_n,
  * c_n) and a reserve of activations saved by the forward; the pulsatrix
  * "LSTMModule" reference describes the backpropagation through time across
- * the four gates and the cell carry.  Time-major layout only (batch_first is
- * LSTM_ERR_UNSUPPORTED); per-row lengths through the _lengths variants. */
+ * the four gates and the cell carry.  Both layouts (with LSTM_OPT_BATCH_FIRST
+ * x, y, dy and dx are [B, T, .]); per-row lengths through the _lengths
+ * variants; the LSTM mode only (others: LSTM_ERR_UNSUPPORTED). */
 
 /* Training dropout between layers.  The trace page's Performance Notes apply
  * dropout to the input of every layer above the first, in training only

@@ -350,9 +350,11 @@ class LSTM:
         (y, h_n, c_n, reserve).  lengths: None or B per-row lengths (host ints)."""
         import torch
         T, B, _ = x.shape
+        if self.batch_first:
+            B, T = T, B
         H, L, D = self.hidden_size, self.num_layers, self.D
         tdt = x.dtype
-        y = torch.empty(T, B, D * H, dtype=tdt, device=x.device)
+        y = torch.empty(*((B, T) if self.batch_first else (T, B)), D * H, dtype=tdt, device=x.device)
         hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
         cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device)
         rbytes = lstm_reserve_size(self.plan, T, B)
@@ -373,6 +375,8 @@ class LSTM:
         """Gradients (dx, dh0, dc0, dweights) of a forward_train() call (with the same lengths)."""
         import torch
         T, B, _ = x.shape
+        if self.batch_first:
+            B, T = T, B
         H, L, D = self.hidden_size, self.num_layers, self.D
         dx = torch.empty_like(x)
         dh0 = torch.empty(L * D, B, H, dtype=x.dtype, device=x.device)

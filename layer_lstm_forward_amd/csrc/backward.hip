@@ -158,15 +158,18 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
     else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r + (c.len ? c.dhc[((size_t)d * B + m) * H + u] : 0.f));
 }
 
-// out[c * ld_out + r] = in[r * ld_in + c] for r < rows, c < cols (DI in, DO out)
+// out[c * ld_out + r] = in[r' * ld_in + c] for r < rows, c < cols (DI in, DO
+// out), r' = r, or with bT > 0 the batch-first row of time-major row r =
+// t*bB + b, i.e. b*bT + t
 template <class DI, class DO>
 __global__ void k_transpose(const typename DI::S *in, size_t ld_in, int rows, int cols, typename DO::S *out,
-                            size_t ld_out) {
+                            size_t ld_out, int bT, int bB) {
     __shared__ float tile[32][33];
     const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
     for (int rr = threadIdx.y; rr < 32; rr += 8) {
         const int r = r0 + rr, c = c0 + threadIdx.x;
-        tile[rr][threadIdx.x] = (r < rows && c < cols) ? DI::to_f(in[(size_t)r * ld_in + c]) : 0.f;
+        const size_t ri = bT > 0 ? (size_t)(r % bB) * bT + r / bB : (size_t)r;
+        tile[rr][threadIdx.x] = (r < rows && c < cols) ? DI::to_f(in[ri * ld_in + c]) : 0.f;
     }
     __syncthreads();
     for (int cc = threadIdx.y; cc < 32; cc += 8) {
@@ -180,7 +183,7 @@ __global__ void k_transpose(const typename DI::S *in, size_t ld_in, int rows, in
 // zeros) at the scan's first step.
 template <class DT, class DO>
 __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT::S *h0d, const int *len, int T,
-                          int B, int H, int d, typename DO::S *out) {
+                          int B, int H, int d, int bfirst, typename DO::S *out) {
     __shared__ float tile[32][33];
     const int m0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int M = T * B;
@@ -191,7 +194,7 @@ __global__ void k_hprev_t(const typename DT::S *Y, size_t ldy, const typename DT
             const int t = m / B, b = m % B;
             const int tp = d == 0 ? t - 1 : t + 1;
             if (tp >= 0 && tp < T && !(len && tp >= len[b]))  // a padded predecessor kept h0
-                v = DT::to_f(Y[((size_t)tp * B + b) * ldy + (size_t)d * H + k]);
+                v = DT::to_f(Y[trow(tp, b, T, B, bfirst != 0) * ldy + (size_t)d * H + k]);
             else if (h0d) v = DT::to_f(h0d[(size_t)b * H + k]);
         }
         tile[mm][threadIdx.x] = v;
@@ -284,7 +287,7 @@ __device__ inline void philox4x64_10(unsigned long long (&c)[4], unsigned long l
 template <class DT>
 __global__ void k_dropout_fwd(const typename DT::S *y, typename DT::S *xd, unsigned char *keep, size_t n,
                               unsigned long long seed, unsigned long long call, int layer, unsigned long long thr,
-                              float scale) {
+                              float scale, int T, int B, int width, int bfirst) {
     const size_t nblk = (n + 3) / 4;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < nblk; i += (size_t)gridDim.x * blockDim.x) {
         unsigned long long c[4] = {(unsigned long long)i, (unsigned long long)layer, call, 0ull};
@@ -294,7 +297,13 @@ __global__ void k_dropout_fwd(const typename DT::S *y, typename DT::S *xd, unsig
             const size_t e = 4 * i + q;
             if (e >= n) break;
             const bool kept = (c[q] >> 11) >= thr;
-            xd[e] = DT::from_f(kept ? DT::to_f(y[e]) * scale : 0.f);
+            // e counts time-major ([T][B][width]); y and xd may be batch-first
+            size_t ye = e;
+            if (bfirst) {
+                const size_t r = e / width;
+                ye = trow((int)(r / B), (int)(r % B), T, B, true) * width + e % width;
+            }
+            xd[ye] = DT::from_f(kept ? DT::to_f(y[ye]) * scale : 0.f);
             keep[e] = kept ? 1 : 0;
         }
     }
@@ -336,38 +345,74 @@ hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, 
 }
 
 hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
-                            int out_dtype, hipStream_t s) {
+                            int out_dtype, hipStream_t s, int bT, int bB) {
     dim3 grid((cols + 31) / 32, (rows + 31) / 32), block(32, 8);
-    if (grid.y > 65535u) return hipErrorInvalidValue;
+    if (grid.y > 65535u || (bT > 0 && (long long)bT * bB != rows)) return hipErrorInvalidValue;
     const bool bi = in_dtype == DT_BF16, bo = out_dtype == DT_BF16;
     if (bi && bo)
         hipLaunchKernelGGL((k_transpose<BF16, BF16>), grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
-                           cols, static_cast<uint16_t *>(out), ld_out);
+                           cols, static_cast<uint16_t *>(out), ld_out, bT, bB);
     else if (bi)
         hipLaunchKernelGGL((k_transpose<BF16, F32>), grid, block, 0, s, static_cast<const uint16_t *>(in), ld_in, rows,
-                           cols, static_cast<float *>(out), ld_out);
+                           cols, static_cast<float *>(out), ld_out, bT, bB);
     else if (bo)
         hipLaunchKernelGGL((k_transpose<F32, BF16>), grid, block, 0, s, static_cast<const float *>(in), ld_in, rows,
-                           cols, static_cast<uint16_t *>(out), ld_out);
+                           cols, static_cast<uint16_t *>(out), ld_out, bT, bB);
     else
         hipLaunchKernelGGL((k_transpose<F32, F32>), grid, block, 0, s, static_cast<const float *>(in), ld_in, rows,
-                           cols, static_cast<float *>(out), ld_out);
+                           cols, static_cast<float *>(out), ld_out, bT, bB);
+    return hipGetLastError();
+}
+
+// Rows of width elements between the time-major [T][B] and batch-first
+// [B][T] orders (to_tm: batch-first in, time-major out), with a dtype change.
+template <class DI, class DO>
+__global__ void k_permute_rows(const typename DI::S *in, typename DO::S *out, int T, int B, int width, int to_tm) {
+    const size_t n = (size_t)T * B * width;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = e / width, k = e % width;
+        const int t = (int)(r / B), b = (int)(r % B);  // time-major row r = t*B + b
+        const size_t rb = (size_t)b * T + t;
+        if (to_tm) out[e] = DO::from_f(DI::to_f(in[rb * width + k]));
+        else out[rb * width + k] = DO::from_f(DI::to_f(in[e]));
+    }
+}
+
+hipError_t launch_permute_rows(const void *in, void *out, int T, int B, int width, int in_dtype, int out_dtype,
+                               bool to_time_major, hipStream_t s) {
+    const size_t n = (size_t)T * B * width;
+    if (n == 0) return hipSuccess;
+    const unsigned g = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+    const int tm = to_time_major ? 1 : 0;
+    const bool bi = in_dtype == DT_BF16, bo = out_dtype == DT_BF16;
+    if (bi && !bo)
+        hipLaunchKernelGGL((k_permute_rows<BF16, F32>), dim3(g), dim3(256), 0, s, static_cast<const uint16_t *>(in),
+                           static_cast<float *>(out), T, B, width, tm);
+    else if (!bi && bo)
+        hipLaunchKernelGGL((k_permute_rows<F32, BF16>), dim3(g), dim3(256), 0, s, static_cast<const float *>(in),
+                           static_cast<uint16_t *>(out), T, B, width, tm);
+    else if (!bi && !bo)
+        hipLaunchKernelGGL((k_permute_rows<F32, F32>), dim3(g), dim3(256), 0, s, static_cast<const float *>(in),
+                           static_cast<float *>(out), T, B, width, tm);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, const int *len, int T, int B, int H, int d,
-                          void *out, int dtype, int out_dtype, hipStream_t s) {
+                          void *out, int dtype, int out_dtype, hipStream_t s, bool batch_first) {
+    const int bf = batch_first ? 1 : 0;
     dim3 grid(((size_t)T * B + 31) / 32, (H + 31) / 32), block(32, 8);
     if (grid.y > 65535u) return hipErrorInvalidValue;
     if (dtype == DT_BF16 && out_dtype == DT_BF16)
         hipLaunchKernelGGL((k_hprev_t<BF16, BF16>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
-                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, static_cast<uint16_t *>(out));
+                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, bf, static_cast<uint16_t *>(out));
     else if (dtype == DT_BF16)
         hipLaunchKernelGGL((k_hprev_t<BF16, F32>), grid, block, 0, s, static_cast<const uint16_t *>(Y), ldy,
-                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, static_cast<float *>(out));
+                           static_cast<const uint16_t *>(h0d), len, T, B, H, d, bf, static_cast<float *>(out));
     else if (out_dtype == DT_F32)
         hipLaunchKernelGGL((k_hprev_t<F32, F32>), grid, block, 0, s, static_cast<const float *>(Y), ldy,
-                           static_cast<const float *>(h0d), len, T, B, H, d, static_cast<float *>(out));
+                           static_cast<const float *>(h0d), len, T, B, H, d, bf, static_cast<float *>(out));
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -407,17 +452,19 @@ hipError_t launch_ksum(const float *part, int ns, size_t slab, size_t n, void *o
     return hipGetLastError();
 }
 
-hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, size_t n, unsigned long long seed,
-                              unsigned long long call, int layer, unsigned long long thr, float scale, int dtype,
-                              hipStream_t s) {
+hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, int T, int B, int width,
+                              unsigned long long seed, unsigned long long call, int layer, unsigned long long thr,
+                              float scale, int dtype, bool batch_first, hipStream_t s) {
+    const size_t n = (size_t)T * B * width;
     if (n == 0) return hipSuccess;
     const unsigned g = grid1((n + 3) / 4);
+    const int bf = batch_first ? 1 : 0;
     if (dtype == DT_BF16)
         hipLaunchKernelGGL(k_dropout_fwd<BF16>, dim3(g), dim3(256), 0, s, static_cast<const uint16_t *>(y),
-                           static_cast<uint16_t *>(xd), keep, n, seed, call, layer, thr, scale);
+                           static_cast<uint16_t *>(xd), keep, n, seed, call, layer, thr, scale, T, B, width, bf);
     else
         hipLaunchKernelGGL(k_dropout_fwd<F32>, dim3(g), dim3(256), 0, s, static_cast<const float *>(y),
-                           static_cast<float *>(xd), keep, n, seed, call, layer, thr, scale);
+                           static_cast<float *>(xd), keep, n, seed, call, layer, thr, scale, T, B, width, bf);
     return hipGetLastError();
 }
 

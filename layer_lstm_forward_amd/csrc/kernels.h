@@ -172,14 +172,20 @@ hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s);
 // Backward step a.sb: the recurrent product, then the cell update of step
 // a.sb + 1, or dh0 ([D, B, H], dtype; NULL = not wanted) after the last step.
 hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s);
-// out[c * ld_out + r] = in[r * ld_in + c] (rows x cols, in_dtype -> out_dtype)
+// out[c * ld_out + r] = in[r * ld_in + c] (rows x cols, in_dtype -> out_dtype);
+// with bT > 0 (rows = bT * bB) the input rows are batch-first: row r = t*bB + b
+// of the result reads input row b*bT + t
 hipError_t launch_transpose(const void *in, size_t ld_in, int rows, int cols, void *out, size_t ld_out, int in_dtype,
-                            int out_dtype, hipStream_t s);
+                            int out_dtype, hipStream_t s, int bT = 0, int bB = 0);
+// rows of width elements between [B][T] and [T][B] order (to_time_major:
+// batch-first in, time-major out), converting in_dtype -> out_dtype
+hipError_t launch_permute_rows(const void *in, void *out, int T, int B, int width, int in_dtype, int out_dtype,
+                               bool to_time_major, hipStream_t s);
 // [H][T*B] in out_dtype: h_prev of direction d for every (t, b), from the
 // layer output Y or h0d ([B][H] or NULL), both dtype (bf16 -> fp32 allowed);
 // with per-row lengths (len, or NULL) a padded predecessor's h is h0d's
 hipError_t launch_hprev_t(const void *Y, size_t ldy, const void *h0d, const int *len, int T, int B, int H, int d,
-                          void *out, int dtype, int out_dtype, hipStream_t s);
+                          void *out, int dtype, int out_dtype, hipStream_t s, bool batch_first = false);
 // part[c][col] (c < the chunk count launched, at most nchunks) = sum over
 // the rows of chunk c of a[r * ld + col]; rows split into ceil(rows /
 // nchunks)-row chunks, each summed in row order
@@ -187,12 +193,13 @@ hipError_t launch_colsum_part(const void *a, size_t ld, int rows, int cols, int 
                               hipStream_t s);
 hipError_t launch_cast_to(const float *in, void *out, size_t n, int dtype, hipStream_t s);
 hipError_t launch_cast_from(const void *in, float *out, size_t n, int dtype, hipStream_t s);
-// Training dropout of one layer's output y (n elements of dtype): xd = the
-// next layer's input, keep = one byte per element; thr = ceil(p * 2^53),
-// scale = 1 / (1 - p) (0 when p = 1).
-hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, size_t n, unsigned long long seed,
-                              unsigned long long call, int layer, unsigned long long thr, float scale, int dtype,
-                              hipStream_t s);
+// Training dropout of one layer's output y ([T][B][width] of dtype, or
+// [B][T][width] when batch_first): xd = the next layer's input in y's layout,
+// keep = one byte per element in time-major order (the order of the draw's
+// element index); thr = ceil(p * 2^53), scale = 1 / (1 - p) (0 when p = 1).
+hipError_t launch_dropout_fwd(const void *y, void *xd, unsigned char *keep, int T, int B, int width,
+                              unsigned long long seed, unsigned long long call, int layer, unsigned long long thr,
+                              float scale, int dtype, bool batch_first, hipStream_t s);
 // g[e] = keep[e] ? g[e] * scale : 0
 hipError_t launch_dropout_bwd(float *g, const unsigned char *keep, size_t n, float scale, hipStream_t s);
 

@@ -528,7 +528,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 107; }
+int lstm_version(void) { return 108; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -1082,8 +1082,8 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
             const unsigned long long thr = q >= 1.0 ? (1ull << 53) : (unsigned long long)std::ceil(q * 0x1p53);
             const float scale = q >= 1.0 ? 0.f : (float)(1.0 / (1.0 - q));
             if (launch_dropout_fwd(Y, reserve + rl.xd(p, l), reinterpret_cast<unsigned char *>(reserve + rl.keep(p, l)),
-                                   (size_t)T * B * p->D * p->H, p->drop_seed, p->drop_call, l, thr, scale, p->dtype,
-                                   st) != hipSuccess) {
+                                   T, B, p->D * p->H, p->drop_seed, p->drop_call, l, thr, scale, p->dtype,
+                                   p->batch_first != 0, st) != hipSuccess) {
                 (void)hipGetLastError();
                 return LSTM_ERR_LAUNCH;
             }
@@ -1231,7 +1231,7 @@ static lstm_status forward_train_impl(lstm_plan *p, const void *x, const int *le
         for (int b = 0; b < B; ++b)
             if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;
     }
-    if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
+    if (p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     ReserveLayout rl{};
     if (!make_reserve(p, T, B, &rl)) return LSTM_ERR_SHAPE;
     if (reserve_bytes < rl.total) return LSTM_ERR_WORKSPACE;
@@ -1285,7 +1285,7 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
         for (int b = 0; b < B; ++b)
             if (lengths_h[b] < 1 || lengths_h[b] > T) return LSTM_ERR_ARG;
     if ((h0 == nullptr) != (c0 == nullptr)) return LSTM_ERR_ARG;
-    if (p->batch_first || p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
+    if (p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     const int per = p->has_bias ? 4 : 2;
     for (int i = 0; i < p->L * p->D * per; ++i)
         if (!weights[i] || !dweights[i]) return LSTM_ERR_ARG;
@@ -1373,7 +1373,11 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
     }
     // the gradient of the top layer's output, as fp32
     int cur = 0;
-    if (!ok(launch_cast_from(dy, dyb[cur], TB * D * H, dt, st))) return fail();
+    // batch-first x, y, dy, dx: the internal gradient buffers stay time-major
+    const bool bfirst = p->batch_first != 0;
+    if (!ok(bfirst ? launch_permute_rows(dy, dyb[cur], T, B, D * H, dt, DT_F32, true, st)
+                   : launch_cast_from(dy, dyb[cur], TB * D * H, dt, st)))
+        return fail();
     for (int l = p->L - 1; l >= 0; --l) {
         const int in_l = l == 0 ? p->I : D * H;
         const void *X = l == 0 ? x : static_cast<const void *>(res + (rl.dropout ? rl.xd(p, l - 1) : rl.y(p, l - 1)));
@@ -1424,12 +1428,12 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
             return fail();
         // weight gradients: dW_ih = dz^T x, dW_hh = dz^T h_prev (operands in
         // gdt), db = sum of dz (fp32 column sums in fixed chunks, then in order)
-        if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, gdt, st))) return fail();
+        if (!ok(launch_transpose(X, in_l, (int)TB, in_l, xt, TB, dt, gdt, st, bfirst ? T : 0, B))) return fail();
         for (int d = 0; d < D; ++d) {
             void *const *dwd = dweights + (size_t)(l * D + d) * per;
             if (!ok(launch_transpose(dz + (size_t)d * G4 * ges, (size_t)D * G4, (int)TB, G4, dzt, TB, gdt, gdt, st)) ||
                 !ok(launch_hprev_t(Y, (size_t)D * H, h0l ? h0l + (size_t)d * BH * es : nullptr, dlen, T, B, H, d, ht, dt,
-                                   gdt, st)))
+                                   gdt, st, bfirst)))
                 return fail();
             if (!gemm_nt(dzt, (int)TB, xt, G4, in_l, (int)TB, dwd[0], dt, ksp) ||
                 !gemm_nt(dzt, (int)TB, ht, G4, H, (int)TB, dwd[1], dt, ksp))
@@ -1450,9 +1454,14 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
                                          wcat + (size_t)d * G4 * ges, (size_t)D * G4, dt, gdt, st)))
                     return fail();
             const bool out_dx = l == 0;
-            if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1], out_dx ? dt : DT_F32,
-                         dyb[cur ^ 1]))
+            if (out_dx && bfirst) {  // time-major rows in fp32, then into dx's batch-first rows
+                if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, dyb[cur ^ 1], DT_F32, dyb[cur ^ 1]) ||
+                    !ok(launch_permute_rows(dyb[cur ^ 1], dx, T, B, in_l, DT_F32, dt, false, st)))
+                    return fail();
+            } else if (!gemm_nt(dz, D * G4, wcat, (int)TB, in_l, D * G4, out_dx ? dx : dyb[cur ^ 1],
+                                out_dx ? dt : DT_F32, dyb[cur ^ 1])) {
                 return fail();
+            }
             // through the dropout the layer below's output was sent up with
             if (!out_dx && rl.dropout) {
                 const float scale = p->dropout >= 1.0 ? 0.f : (float)(1.0 / (1.0 - p->dropout));
