@@ -68,7 +68,7 @@ def _load():
         lib.oracle_rnn_forward.restype = ctypes.c_int
         lib.oracle_rnn_forward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            dp, dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, ctypes.c_int]
+            dp, ctypes.POINTER(ctypes.c_int), dp, ctypes.POINTER(dp), ctypes.c_int, dp, dp, ctypes.c_int]
         lib.oracle_dropout_keep.restype = None
         lib.oracle_dropout_keep.argtypes = [ctypes.c_double, u64, u64, ctypes.c_int, ctypes.c_size_t,
                                             ctypes.POINTER(ctypes.c_ubyte)]
@@ -230,7 +230,7 @@ MODES = {"gru": 1, "rnn_tanh": 2, "rnn_relu": 3}
 
 
 def rnn_forward(mode, x, params, hidden_size: int, num_layers: int, bidirectional: bool, h0=None,
-                has_bias: bool = True, bf16: bool = False, nthreads: int = 1):
+                has_bias: bool = True, bf16: bool = False, nthreads: int = 1, lengths=None):
     """The other recurrent modes ("gru", "rnn_tanh", "rnn_relu"; see the C
     file).  params in (layer, direction, W_ih, W_hh[, b_ih, b_hh]) order with
     3H (GRU) or H gate rows.  Returns (y [T, B, D*H], h_n [L*D, B, H]) as
@@ -257,7 +257,12 @@ def rnn_forward(mode, x, params, hidden_size: int, num_layers: int, bidirectiona
         raise ValueError(f"h0 shape {h064.shape} != {(L * D, B, H)}")
     y = np.empty((T, B, D * H), np.float64)
     hn = np.empty((L * D, B, H), np.float64)
-    rc = lib.oracle_rnn_forward(m, T, B, I, H, L, D, _ptr(x64), _ptr(h064) if h064 is not None else None, arr,
+    len32 = None if lengths is None else np.ascontiguousarray(np.asarray(lengths, np.int32))
+    if len32 is not None and len32.shape != (B,):
+        raise ValueError(f"lengths shape {len32.shape} != {(B,)}")
+    rc = lib.oracle_rnn_forward(m, T, B, I, H, L, D, _ptr(x64),
+                                len32.ctypes.data_as(ctypes.POINTER(ctypes.c_int)) if len32 is not None else None,
+                                _ptr(h064) if h064 is not None else None, arr,
                                 1 if has_bias else 0, _ptr(y), _ptr(hn), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_rnn_forward failed with {rc}")

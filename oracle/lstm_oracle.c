@@ -502,14 +502,19 @@ int oracle_lstm_forward_dropout(int T, int B, int I, int H, int L, int D,
  * RNN_RELU.  Parameters per (layer, direction): W_ih [NG*H][in_l],
  * W_hh [NG*H][H] (and b_ih, b_hh [NG*H] when has_bias), NG = 3 for the GRU
  * and 1 for the RNNs.  h0, h_n [L*D][B][H] as for the LSTM; no cell state.
+ * lengths: NULL or per-row lengths with the LSTM's reading (a padded step
+ * leaves h alone and outputs 0).
  * Returns 0, -1 on a bad argument, -2 if memory runs out. */
 int oracle_rnn_forward(int mode, int T, int B, int I, int H, int L, int D,
-                       const double *x, const double *h0, const double *const *params, int has_bias,
-                       double *y, double *h_n, int nthreads)
+                       const double *x, const int *lengths, const double *h0, const double *const *params,
+                       int has_bias, double *y, double *h_n, int nthreads)
 {
     if (mode < 1 || mode > 3 || T < 1 || B < 1 || I < 1 || H < 1 || L < 1 || (D != 1 && D != 2) ||
         !x || !params || !y)
         return -1;
+    if (lengths)
+        for (int b = 0; b < B; ++b)
+            if (lengths[b] < 1 || lengths[b] > T) return -1;
     if (nthreads < 1) nthreads = 1;
     const int per = has_bias ? 4 : 2;
     const int NG = mode == 1 ? 3 : 1, R = NG * H;
@@ -544,6 +549,7 @@ int oracle_rnn_forward(int mode, int T, int B, int I, int H, int L, int D,
                     }
                 }
                 for (int b = 0; b < B; ++b) {
+                    if (PADDED(t, b)) continue;  /* h stays, y stays 0 */
                     for (int j = 0; j < H; ++j) {
                         const double *gi = gin + (size_t)b * R, *gh = ghid + (size_t)b * R;
                         double hv;

@@ -89,11 +89,12 @@ def lstm(x, params, H, L, D, h0=None, c0=None, has_bias=True, lengths=None, betw
     return out, hn, cn
 
 
-def rnn(mode, x, params, H, L, D, h0=None, has_bias=True):
+def rnn(mode, x, params, H, L, D, h0=None, has_bias=True, lengths=None):
     """The GRU ("gru", gate blocks r, z, n) and the plain RNNs ("rnn_tanh",
     "rnn_relu") in the same per-gate scalar style: every gate keeps its own
     W_i*, W_h*, b_i*, b_h*; the GRU's candidate applies r to the hidden
-    contribution including its bias.  Returns y [T][B][D*H] and h_n
+    contribution including its bias.  lengths: as for lstm() (a row's own
+    sequence only; padded outputs stay zero).  Returns y [T][B][D*H] and h_n
     [L*D][B][H] as nested lists."""
     T, B = len(x), len(x[0])
     per = 4 if has_bias else 2
@@ -115,7 +116,8 @@ def rnn(mode, x, params, H, L, D, h0=None, has_bias=True):
             hl = []
             for b in range(B):
                 h = [float(v) for v in h0[l * D + d][b]] if h0 is not None else [0.0] * H
-                order = range(T) if d == 0 else range(T - 1, -1, -1)
+                n = T if lengths is None else lengths[b]
+                order = range(n) if d == 0 else range(n - 1, -1, -1)
                 for t in order:
                     xi = {nm: _affine(g["Wi" + nm], seq[t][b], g["bi" + nm]) for nm in names}
                     hh = {nm: _affine(g["Wh" + nm], h, g["bh" + nm]) for nm in names}

@@ -75,3 +75,31 @@ def test_modes_match_torch_fp64(mode, L, bidir, bias):
     y, hn = oracle.rnn_forward(mode, inp.x, inp.params, H, L, bidir, h0=inp.h0, has_bias=bias)
     np.testing.assert_allclose(y, ty.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(hn, thn.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("L,bidir", [(1, True), (2, True), (3, False)])
+def test_modes_with_lengths_match_brute_force(mode, L, bidir):
+    spec = Spec(3, 4, L, bidir, 6, 4, "f32", 7300 + L, "normal0.1", mode=mode)
+    inp = make_inputs(spec)
+    params = [p.astype(np.float64) * 2.0 for p in inp.params]
+    lengths = [6, 2, 4, 1]
+    y, hn = oracle.rnn_forward(mode, inp.x, params, 4, L, bidir, h0=inp.h0, lengths=lengths)
+    ry, rhn = brute.rnn(mode, inp.x.tolist(), [p.tolist() for p in params], 4, L, spec.D, h0=inp.h0.tolist(),
+                        lengths=lengths)
+    np.testing.assert_allclose(y, np.array(ry), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hn, np.array(rhn), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mode_row_with_n_steps_is_the_row_alone(mode):
+    # a row of length n equals, bit for bit, the fixed-length oracle on its first n steps alone
+    spec = Spec(5, 6, 2, True, 7, 3, "f32", 7400, "normal0.1", mode=mode)
+    inp = make_inputs(spec)
+    lengths = [7, 3, 5]
+    y, hn = oracle.rnn_forward(mode, inp.x, inp.params, 6, 2, True, h0=inp.h0, lengths=lengths)
+    for b, n in enumerate(lengths):
+        yb, hb = oracle.rnn_forward(mode, inp.x[:n, b:b + 1], inp.params, 6, 2, True, h0=inp.h0[:, b:b + 1])
+        np.testing.assert_array_equal(y[:n, b], yb[:, 0])
+        assert not np.any(y[n:, b])
+        np.testing.assert_array_equal(hn[:, b], hb[:, 0])
