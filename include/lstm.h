@@ -151,8 +151,9 @@ lstm_status lstm_create(lstm_plan **out, int input_size, int hidden_size, int nu
  * LSTM_REC_STEP / LSTM_REC_GEMM) one projection GEMM and T recurrent-step
  * launches per layer, which need hidden_size * element size to be a multiple
  * of 16 bytes and 16-byte aligned x, y, h0 and weights
- * (LSTM_ERR_UNSUPPORTED otherwise).  lstm_forward_lengths, the training entry
- * points and their size queries are LSTM_ERR_UNSUPPORTED. */
+ * (LSTM_ERR_UNSUPPORTED otherwise).  lstm_forward_lengths takes them on either
+ * path: a padded step keeps the row's h and writes zeros to y, as for the LSTM.
+ * The training entry points and their size queries are LSTM_ERR_UNSUPPORTED. */
 lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidden_size, int num_layers,
                              int bidirectional, int has_bias, int dtype);
 

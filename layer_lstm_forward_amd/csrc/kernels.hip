@@ -1427,7 +1427,9 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             } else {
                 hv = fmaxf(g[0] + pre[0], 0.f);
             }
-            const S hs = DT::from_f(hv);
+            // a padded step of this row keeps h, which y carries to the next
+            // step (padded outputs are zeroed after the last layer)
+            const S hs = (a.len && t >= a.len[m]) ? hprev : DT::from_f(hv);
             static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
             if (last && a.hn) static_cast<S *>(a.hn)[si] = hs;
         } else {

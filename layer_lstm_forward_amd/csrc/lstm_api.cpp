@@ -810,7 +810,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     int wper = per;
     bool bias_on = p->has_bias != 0;
     if (padded) {
-        if (!sch.persistent || lengths_h || reserve) return LSTM_ERR_UNSUPPORTED;
+        if (!sch.persistent || reserve) return LSTM_ERR_UNSUPPORTED;
         wpad_ptrs.assign((size_t)p->L * p->D * 4, nullptr);
         std::vector<PadJob> jobs;
         const int rows = p->NG * p->H;
@@ -1110,9 +1110,9 @@ bool use_persistent_for_mode(const lstm_plan *p, int B) {
 // The forward pass of the GRU and the plain RNNs: per layer the hoisted
 // projection G = X W_ih^T + b_ih (both directions), then one k_rec_step launch
 // per step, which adds W_hh h_{t-1} + b_hh and applies the mode's update.
-lstm_status forward_modes(lstm_plan *p, const void *x, const void *h0, const void *const *weights, int T, int B,
-                          int layers, int bidir, void *y, void *h_n, const float *c_n, void *workspace,
-                          size_t workspace_bytes, void *stream_) {
+lstm_status forward_modes(lstm_plan *p, const void *x, const int *lengths_h, const void *h0,
+                          const void *const *weights, int T, int B, int layers, int bidir, void *y, void *h_n,
+                          const float *c_n, void *workspace, size_t workspace_bytes, void *stream_) {
     Layout lay;
     int rc = validate(p, x, h0, nullptr, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
     if (rc != LSTM_OK) return (lstm_status)rc;
@@ -1132,6 +1132,7 @@ lstm_status forward_modes(lstm_plan *p, const void *x, const void *h0, const voi
     char *ws = static_cast<char *>(workspace);
     float *G = reinterpret_cast<float *>(ws + lay.G);
     const size_t es = elem_size(p->dtype), state_elems = (size_t)p->D * B * p->H;
+    int *dlen = lengths_h ? reinterpret_cast<int *>(ws + lay.lens) : nullptr;
     auto layer_args = [&](int l) {
         RecArgs ra{};
         for (int d = 0; d < p->D; ++d) {
@@ -1149,11 +1150,16 @@ lstm_status forward_modes(lstm_plan *p, const void *x, const void *h0, const voi
         ra.D = p->D;
         ra.bfirst = p->batch_first;
         ra.mode = p->mode;
+        ra.len = dlen;
         return ra;
     };
     // every layer's operands must suit the per-step kernel: checked before anything is enqueued
     for (int l = 0; l < p->L; ++l)
         if (!rec_step_gemm_ok(layer_args(l), p->dtype)) return LSTM_ERR_UNSUPPORTED;
+    if (dlen && hipMemcpyAsync(dlen, lengths_h, (size_t)B * sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
     for (int l = 0; l < p->L; ++l) {
         const void *X = l == 0 ? x : static_cast<const void *>(ws + lay.ymid[(l - 1) & 1]);
         const int in_l = l == 0 ? p->I : p->D * p->H;
@@ -1188,6 +1194,11 @@ lstm_status forward_modes(lstm_plan *p, const void *x, const void *h0, const voi
         }
         span_end(p, span, st, T);
     }
+    // padded steps carried h in y for the next step; the caller sees zeros
+    if (dlen && launch_mask_padded(y, dlen, T, B, (size_t)p->D * p->H * es, p->batch_first != 0, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
     if (p->timing) p->acc.calls += 1;
     return LSTM_OK;
 }
@@ -1205,8 +1216,8 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
         if (use_persistent_for_mode(p, B))
             return forward_impl(p, x, nullptr, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
                                 workspace, workspace_bytes, stream);
-        return forward_modes(p, x, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace, workspace_bytes,
-                             stream);
+        return forward_modes(p, x, nullptr, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                             workspace_bytes, stream);
     }
     return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                         workspace_bytes, stream);
@@ -1499,10 +1510,17 @@ lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths
                                  int bidir, void *y, void *h_n, float *c_n, void *workspace,
                                  size_t workspace_bytes, void *stream) {
     if (!lengths) return LSTM_ERR_ARG;
-    if (p && p->mode != LSTM_MODE_LSTM) return LSTM_ERR_UNSUPPORTED;
     if (T < 1 || B < 1) return LSTM_ERR_SHAPE;
     for (int b = 0; b < B; ++b)
         if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;
+    if (p && p->mode != LSTM_MODE_LSTM) {
+        if (c0 || c_n) return LSTM_ERR_ARG;  // no cell state
+        if (use_persistent_for_mode(p, B))
+            return forward_impl(p, x, lengths, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
+                                workspace, workspace_bytes, stream);
+        return forward_modes(p, x, lengths, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
+                             workspace_bytes, stream);
+    }
     return forward_impl(p, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                         workspace_bytes, stream);
 }

@@ -224,9 +224,12 @@ def test_modes_create_and_validate():
                 # c0 (and c_n) belong to the LSTM only; validation precedes any device access
                 rc = pkg.lstm_forward(p, FAKE, FAKE, FAKE, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0, FAKE, 1 << 40, 0)
                 assert rc == -1
-                rc = pkg.lstm_forward_lengths(p, FAKE, [3] * 8, 0, 0, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0, FAKE,
-                                              1 << 40, 0)
-                assert rc == -7
+                rc = pkg.lstm_forward_lengths(p, FAKE, [3] * 8, 0, FAKE, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0,
+                                              FAKE, 1 << 40, 0)
+                assert rc == -1
+                rc = pkg.lstm_forward_lengths(p, FAKE, [3] * 7 + [11], 0, 0, [FAKE] * 8, 10, 8, 2, True, FAKE, 0, 0,
+                                              FAKE, 1 << 40, 0)
+                assert rc == -1
                 with pytest.raises(pkg.LSTMError):
                     pkg.lstm_reserve_size(p, 10, 8)
                 with pytest.raises(pkg.LSTMError):

@@ -30,7 +30,7 @@ SHAPES = [  # input, hidden, layers, bidirectional, T, B, dtype, state, bias
 PATHS = {"auto": pkg.LSTM_REC_AUTO, "step": pkg.LSTM_REC_STEP}
 
 
-def _run(spec, inp, batch_first=False, path="auto"):
+def _run(spec, inp, batch_first=False, path="auto", lengths=None):
     import torch
     bf = spec.dtype == "bf16"
     dev = "cuda:0"
@@ -41,7 +41,7 @@ def _run(spec, inp, batch_first=False, path="auto"):
     x = to_dev(np.ascontiguousarray(inp.x.transpose(1, 0, 2)) if batch_first else inp.x, bf, dev)
     w = [to_dev(p, bf, dev) for p in inp.params]
     h0 = to_dev(inp.h0, bf, dev)
-    y, hn, cn = m.forward(x, w, h0)
+    y, hn, cn = m.forward(x, w, h0, lengths=lengths)
     torch.cuda.synchronize()
     assert cn is None
     y = y.float().cpu().numpy().astype(np.float64)
@@ -101,7 +101,54 @@ def test_mode_full_size_sampled_rows(mode, path):
     _check(hn[:, rows], rhn, "f32", "h_n")
 
 
-def test_mode_rejects_cell_state_and_lengths():
+LEN_SHAPES = [  # input, hidden, layers, bidirectional, T, B, dtype, length mix
+    (24, 32, 1, False, 9, 11, "f32", "ragged"),
+    (40, 64, 2, True, 13, 70, "f32", "ragged"),   # reverse direction starts at each row's last step
+    (64, 96, 2, True, 7, 20, "bf16", "mix"),
+]
+
+
+@pytest.mark.parametrize("batch_first", [False, True], ids=["tmajor", "bfirst"])
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", LEN_SHAPES, ids=lambda s: f"{s[6]}-H{s[1]}-L{s[2]}-D{2 if s[3] else 1}-{s[7]}")
+def test_mode_lengths_match_oracle(mode, shape, path, batch_first):
+    # per-row lengths: padded steps keep h and output zeros, h_n is each
+    # row's state after its own last step (the reverse direction's after t=0)
+    from layer_lstm_forward_amd.synth import make_lengths
+    I, H, L, bidir, T, B, dtype, mix = shape
+    spec = Spec(I, H, L, bidir, T, B, dtype, 940 + H + L, "normal0.1", mode=mode)
+    print(f"case {mode} lengths {shape} {path} batch_first={batch_first}", flush=True)
+    inp = make_inputs(spec)
+    lengths = make_lengths(spec, mix)
+    y, hn = _run(spec, inp, batch_first=batch_first, path=path, lengths=lengths)
+    ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, H, L, bidir, h0=inp.h0, bf16=dtype == "bf16",
+                                 nthreads=oracle_threads(), lengths=lengths)
+    _check(y, ry, dtype, "y")
+    _check(hn, rhn, dtype, "h_n")
+    for b in range(B):  # exact zeros past each row's end
+        assert not np.any(y[lengths[b]:, b]), f"row {b}: nonzero output past length {lengths[b]}"
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("mode", MODES)
+def test_mode_full_size_lengths_sampled_rows(mode, path):
+    # the benchmark workload's shape with the seeded length mix, sampled rows
+    from layer_lstm_forward_amd.synth import make_lengths
+    spec = Spec(256, 512, 2, False, 128, 64, "f32", 1003, "normal0.1", mode=mode)
+    print(f"case {mode} full size lengths {path}", flush=True)
+    inp = make_inputs(spec)
+    lengths = make_lengths(spec, "mix")
+    y, hn = _run(spec, inp, path=path, lengths=lengths)
+    rows = [int(np.argmin(lengths)), 5, 33, 63]
+    sub = inp.rows(rows)
+    ry, rhn = oracle.rnn_forward(mode, sub.x, sub.params, 512, 2, False, h0=sub.h0, nthreads=oracle_threads(),
+                                 lengths=lengths[rows])
+    _check(y[:, rows], ry, "f32", "y")
+    _check(hn[:, rows], rhn, "f32", "h_n")
+
+
+def test_mode_rejects_cell_state():
     import torch
     spec = Spec(8, 32, 1, False, 4, 2, "f32", 970, "normal0.1", mode="gru")
     inp = make_inputs(spec)
@@ -113,4 +160,4 @@ def test_mode_rejects_cell_state_and_lengths():
     with pytest.raises(pkg.LSTMError):
         m.forward(x, w, h0, c0)
     with pytest.raises(pkg.LSTMError):
-        m.forward(x, w, h0, lengths=[4, 2])
+        m.forward(x, w, h0, c0, lengths=[4, 2])
