@@ -36,22 +36,69 @@ namespace lstm_amd {
 // The cell part of backward step sb (sb = 0 is the last step of each
 // direction's scan) at (d, b, j): from dh = dY + dh_rec (the recurrent
 // product of the step after it) and the carried dc, the pre-activation
-// gradients dz of the four gates and dc for the step before it.
+// gradients dz of the four gates and dc for the step before it.  It is split
+// in two: CellIn holds what it reads besides the recurrent product.  None of
+// that depends on the product, so a step kernel issues these loads before its
+// product and they overlap its round trips.
+struct CellIn {
+    float dY, dhn, dhc, dcn, dc;         // dhn, dhc, dcn: 0 where the array is NULL
+    float ig, fg, gg, og, c, c0, cpa;    // cpa: c of the scan's previous step (clamped time)
+    int len;                             // 0 where lengths are NULL
+};
+
+// a[i] through a buffer resource: NULL (no records) reads 0 without a branch
+__device__ inline float ld_or0(const float *a, size_t i) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a), (short)0, a ? 0x7FFFFFFF : 0, 0x00020000);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4), 0, 0));
+}
+
+// Every load is unconditional (any choice between them waits for the
+// compiler's join of the paths, i.e. for the loads), and the choices are
+// made in bwd_cell_store.  sb, b and j must be in range.
 template <class G>
-__device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int b, int j, float dh_rec) {
+__device__ inline CellIn bwd_cell_load(const BwdCellArgs &a, int sb, int d, int b, int j) {
     const int T = a.T, B = a.B, H = a.H, D = a.D;
     const int sf = T - 1 - sb;                   // the forward scan's step
     const int t = d == 0 ? sf : T - 1 - sf;      // its time index
     const int tp = d == 0 ? t - 1 : t + 1;       // time of the scan's previous step
+    const int tpc = tp < 0 ? 0 : tp >= T ? T - 1 : tp;
+    const size_t dbj = ((size_t)d * B + b) * H + j;
+    CellIn v;
+    v.len = (int)__float_as_uint(ld_or0(reinterpret_cast<const float *>(a.len), (size_t)b));
+    v.dhn = ld_or0(a.dhn, dbj);
+    v.dhc = ld_or0(a.dhc, dbj);
+    v.dcn = ld_or0(a.dcn, dbj);
+    v.dc = a.dc[dbj];
+    v.dY = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j];
+    const float *ap = a.acts + (((size_t)t * B + b) * D + d) * 5 * H + j;
+    v.ig = ap[0];
+    v.fg = ap[(size_t)H];
+    v.gg = ap[(size_t)2 * H];
+    v.og = ap[(size_t)3 * H];
+    v.c = ap[(size_t)4 * H];
+    v.c0 = ld_or0(a.c0, dbj);
+    v.cpa = a.acts[(((size_t)tpc * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
+    return v;
+}
+
+// The update itself, with v from bwd_cell_load (dz in the gradient dtype G).
+template <class G>
+__device__ inline void bwd_cell_store(const BwdCellArgs &a, int sb, int d, int b, int j, float dh_rec,
+                                      const CellIn &v) {
+    const int T = a.T, B = a.B, H = a.H, D = a.D;
+    const int sf = T - 1 - sb;
+    const int t = d == 0 ? sf : T - 1 - sf;
     const size_t dbj = ((size_t)d * B + b) * H + j;
     typename G::S *dz = static_cast<typename G::S *>(a.dz) + (((size_t)t * B + b) * D + d) * 4 * H + j;
+    const float dcn = sb == 0 ? v.dcn : v.dc;  // the dc carried in (dc_n at the scan's last step)
     // With per-row lengths, a padded step (the forward left h and c alone
     // there and output 0) has zero dz; dc stays, and the gradient of h it
     // received goes on to the step before in a.dhc, joining that step's dh.
     if (a.len) {
-        const float carried = sb == 0 ? (a.dhn ? a.dhn[dbj] : 0.f) : a.dhc[dbj];
-        if (t >= a.len[b]) {
-            if (sb == 0) a.dc[dbj] = a.dcn ? a.dcn[dbj] : 0.f;
+        const float carried = sb == 0 ? v.dhn : v.dhc;
+        if (t >= v.len) {
+            if (sb == 0) a.dc[dbj] = dcn;
             a.dhc[dbj] = dh_rec + carried;
 #pragma unroll
             for (int q = 0; q < 4; ++q) dz[(size_t)q * H] = G::from_f(0.f);
@@ -60,27 +107,22 @@ __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int 
         a.dhc[dbj] = 0.f;
         if (sb > 0) dh_rec += carried;  // at sb = 0, dh_n joins below
     }
-
-    float dh = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j] + dh_rec;
-    float dcn;
-    if (sb == 0) {
-        dh += a.dhn ? a.dhn[dbj] : 0.f;
-        dcn = a.dcn ? a.dcn[dbj] : 0.f;
-    } else {
-        dcn = a.dc[dbj];
-    }
-    const float *ap = a.acts + (((size_t)t * B + b) * D + d) * 5 * H + j;
-    const float ig = ap[0], fg = ap[(size_t)H], gg = ap[(size_t)2 * H], og = ap[(size_t)3 * H];
-    const float c = ap[(size_t)4 * H];
-    const float cprev = sf == 0 ? (a.c0 ? a.c0[dbj] : 0.f)
-                                : a.acts[(((size_t)tp * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
-    const float tc = tanh_f(c);
+    float dh = v.dY + dh_rec;
+    if (sb == 0) dh += v.dhn;
+    const float ig = v.ig, fg = v.fg, gg = v.gg, og = v.og;
+    const float cprev = sf == 0 ? v.c0 : v.cpa;
+    const float tc = tanh_f(v.c);
     const float dct = dcn + dh * og * (1.f - tc * tc);
     dz[0] = G::from_f(dct * gg * ig * (1.f - ig));
     dz[(size_t)H] = G::from_f(dct * cprev * fg * (1.f - fg));
     dz[(size_t)2 * H] = G::from_f(dct * ig * (1.f - gg * gg));
     dz[(size_t)3 * H] = G::from_f(dh * tc * og * (1.f - og));
     a.dc[dbj] = dct * fg;
+}
+
+template <class G>
+__device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int b, int j, float dh_rec) {
+    bwd_cell_store<G>(a, sb, d, b, j, dh_rec, bwd_cell_load<G>(a, sb, d, b, j));
 }
 
 // The first backward step of every (direction, batch row, unit): dh = dY + dh_n.
@@ -97,19 +139,41 @@ __global__ void k_bwd_cell(BwdCellArgs a) {
 // K = 4H (stacked gate order), then the cell update of step sb + 1 for the
 // tile's cells -- or, after the scan's first step (sb = T - 1), dh0.
 //   whT[d][j][k] = W_hh[d][k][j]: K-contiguous rows, as are dz's
-// The four waves take a quarter of K each (16x16 MFMAs in the gradient
+// The BWD_WAVES waves take equal slices of K (16x16 MFMAs in the gradient
 // dtype G, fp32 accumulation, fragments of 16-byte loads); their tiles meet
-// in LDS, one output per thread.  A whole tile's K lives in one workgroup, so
-// no partial sums leave it and nothing waits on another workgroup.
+// in LDS, one output per thread of the first 256.  The cell update's own
+// inputs are loaded before the product, so their round trip overlaps it.  A
+// whole tile's K lives in one workgroup, so no partial sums leave it and
+// nothing waits on another workgroup.  (Eight waves, two per SIMD, doubled
+// the loads in flight and measured no faster: the fp32 product chain and the
+// launch dominate a step.)
+constexpr int BWD_WAVES = 4;
+
 template <class G, class DT>
-__global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, typename DT::S *dh0) {
+__global__ __launch_bounds__(BWD_WAVES * 64) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, typename DT::S *dh0) {
     using S = typename G::S;
+    constexpr int NW = BWD_WAVES;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.B, H = a.H, D = a.D, K = 4 * H;
-    const int d = blockIdx.z, b0 = blockIdx.x * 16, u0 = blockIdx.y * 16;
+    const int d = blockIdx.z;
+    int mb, ub;
+    {
+        // the row blocks of one unit block run on the same XCD (round-robin
+        // dispatch), so its W_hh^T rows are fetched into that XCD's L2 once
+        const int bid = blockIdx.x, nmb = (B + 15) / 16, nub = (H + 15) / 16;
+        if ((nub & 7) == 0) {
+            const int idx = bid >> 3;
+            ub = (bid & 7) + 8 * (idx / nmb);
+            mb = idx % nmb;
+        } else {
+            ub = bid / nmb;
+            mb = bid % nmb;
+        }
+    }
+    const int b0 = mb * 16, u0 = ub * 16;
     const int b = b0 + (lane & 15);  // A row (batch row) of this lane
     const int j = u0 + (lane & 15);  // B row (unit) of this lane
-    const int kq = (K + 4 * G::KC - 1) / (4 * G::KC) * G::KC;  // K per wave, whole chunks
+    const int kq = (K + NW * G::KC - 1) / (NW * G::KC) * G::KC;  // K per wave, whole chunks
     const int k_lo = w * kq, k_hi = min(K, k_lo + kq);
     const int sf = a.T - 1 - a.sb;
     const int t = d == 0 ? sf : a.T - 1 - sf;
@@ -125,6 +189,11 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
         0x00020000);
     const unsigned aoff = (unsigned)((size_t)b * D * K * es);
     const unsigned boff = (unsigned)((size_t)j * K * es);
+    // the cell update's own inputs (one cell per thread of the first 256)
+    const int rb_ = (tid >> 4) & 15, ru = tid & 15;
+    const int m = b0 + rb_, u = u0 + ru;
+    const bool cell = tid < 256 && m < B && u < H && a.sb + 1 < a.T;
+    const CellIn cin = bwd_cell_load<G>(c, min(a.sb + 1, a.T - 1), d, min(m, B - 1), min(u, H - 1));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     // batches of 16 chunks: all 32 fragment loads are issued before the first
     // product of the batch; scheduling barriers keep the compiler from
@@ -146,15 +215,15 @@ __global__ __launch_bounds__(256) void k_bwd_step(BwdMmArgs a, BwdCellArgs c, ty
         __builtin_amdgcn_sched_barrier(0);
     }
     // lane l, register v: batch row 4 (l / 16) + v, unit l % 16 of the tile
-    __shared__ float red[4][16][17];
+    __shared__ float red[NW][16][17];
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
     __syncthreads();
-    const int rb_ = tid >> 4, ru = tid & 15;
-    const int m = b0 + rb_, u = u0 + ru;
-    if (m >= B || u >= H) return;
-    const float r = red[0][rb_][ru] + red[1][rb_][ru] + red[2][rb_][ru] + red[3][rb_][ru];
-    if (a.sb + 1 < a.T) bwd_cell_update<G>(c, a.sb + 1, d, m, u, r);
+    if (tid >= 256 || m >= B || u >= H) return;
+    float r = red[0][rb_][ru];  // the waves' K slices, added in order
+#pragma unroll
+    for (int q = 1; q < NW; ++q) r += red[q][rb_][ru];
+    if (cell) bwd_cell_store<G>(c, a.sb + 1, d, m, u, r, cin);
     else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r + (c.len ? c.dhc[((size_t)d * B + m) * H + u] : 0.f));
 }
 
@@ -332,15 +401,15 @@ hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s) {
 hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s) {
     if (c.dz != a.dz || c.T != a.T || c.B != a.B || c.H != a.H || c.D != a.D) return hipErrorInvalidValue;
     if (gdt == DT_BF16 && a.H % 2 != 0) return hipErrorInvalidValue;  // whole bf16 fragments over K = 4H
-    dim3 grid((a.B + 15) / 16, (a.H + 15) / 16, a.D);
+    dim3 grid(((a.B + 15) / 16) * ((a.H + 15) / 16), 1, a.D);
     if (gdt == DT_BF16 && dtype == DT_BF16)
-        hipLaunchKernelGGL((k_bwd_step<BF16, BF16>), grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
+        hipLaunchKernelGGL((k_bwd_step<BF16, BF16>), grid, dim3(BWD_WAVES * 64), 0, s, a, c, static_cast<uint16_t *>(dh0));
     else if (gdt == DT_BF16)
         return hipErrorInvalidValue;
     else if (dtype == DT_BF16)
-        hipLaunchKernelGGL((k_bwd_step<F32, BF16>), grid, dim3(256), 0, s, a, c, static_cast<uint16_t *>(dh0));
+        hipLaunchKernelGGL((k_bwd_step<F32, BF16>), grid, dim3(BWD_WAVES * 64), 0, s, a, c, static_cast<uint16_t *>(dh0));
     else
-        hipLaunchKernelGGL((k_bwd_step<F32, F32>), grid, dim3(256), 0, s, a, c, static_cast<float *>(dh0));
+        hipLaunchKernelGGL((k_bwd_step<F32, F32>), grid, dim3(BWD_WAVES * 64), 0, s, a, c, static_cast<float *>(dh0));
     return hipGetLastError();
 }
 

@@ -1483,13 +1483,148 @@ __global__ void k_fill(unsigned *p, size_t n, unsigned v) {
 }
 
 // ===========================================================================
+// Projection GEMM, 256x256 tiles fed through a ring of NST direct-to-LDS
+// stages.  The double buffer of k_proj_dma drains every load before each
+// stage's barrier, so each wave keeps at most one stage of loads in flight
+// and the next stage must land within one stage of products.  Here a stage
+// holds 64 bytes of K per row (32 KiB for both operands), NST - 1 stages are
+// issued ahead, and the wait before a stage's barrier lets the later stages'
+// loads stay pending (a vmcnt bound instead of a full drain).
+// Each 1 KiB load fills 16 rows of 4 segments; segment s of row r sits at
+// r * 4 + (s ^ ((r / 4) % 4)), so 16 consecutive rows reading one segment
+// touch 16 distinct 16-byte bank groups.  The products and the epilogue are
+// those of k_proj_dma.
+// ===========================================================================
+template <class DT, int NST>
+__global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 256, BN = 256, SEG = 4;
+    constexpr int KS = SEG * DT::PER16;
+    constexpr int STAGE = (BM + BN) * SEG;       // 16-byte segments per stage
+    constexpr int LPS = (BM + BN) / 16 / 4;      // 1 KiB loads per wave per stage
+    constexpr unsigned OOR = 0x80000000u;        // past any resource: reads zero
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const ProjSplit sp = proj_split(a);
+    const int d = sp.d;
+    const int M = a.M, N = a.N, K = sp.kc, ldw = a.K;
+    int tm, tn;
+    gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int es = (int)sizeof(S);
+    const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx + sp.kb;
+    const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * ldw + sp.kb;
+    float *const Gs = a.G + sp.goff;
+    const unsigned xbytes = (unsigned)(((size_t)(min(BM, M - m0) - 1) * a.ldx + K) * es);
+    const unsigned wbytes = (unsigned)(((size_t)(min(BN, N - n0) - 1) * ldw + K) * es);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(X), (short)0, (int)xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
+
+    // this lane's slot in each 1 KiB block: row (lane / 4) of the block, swizzled segment (lane % 4)
+    const int brow = lane >> 2, pseg = lane & 3;
+    auto issue = [&](int kt, int buf) {
+        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+#pragma unroll
+        for (int i = 0; i < LPS / 2; ++i) {
+            const int blk = w + 4 * i;  // 16 blocks of 16 rows per operand
+            const int row = blk * 16 + brow;
+            const int lseg = pseg ^ ((row >> 2) & 3);
+            const int k = kt * KS + lseg * DT::PER16;
+            const unsigned ox = k < K ? (unsigned)(((size_t)row * a.ldx + k) * es) : OOR;
+            const unsigned ow = k < K ? (unsigned)(((size_t)row * ldw + k) * es) : OOR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(sa + blk * 64), 16, ox, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(sb + blk * 64), 16, ow, 0, 0, 0);
+        }
+    };
+    auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 2) & 3)); };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (K + KS - 1) / KS;
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k)
+        if (k < nk) issue(k, k);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt % NST;
+        // this wave's loads of stage kt are in LDS once at most the loads of
+        // the later stages already issued (up to NST-2 of them) are pending
+        constexpr int VM = LPS * (NST - 2);
+        static_assert(VM < 64, "vmcnt field");
+        if (kt + NST - 2 < nk) __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+        else __builtin_amdgcn_s_waitcnt(0);
+        // everyone's are, and stage kt-1 is no longer read; a bare barrier, so
+        // that the later stages' loads stay in flight
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+        const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+        u32x4 af[2][4], bw[2][4];
+        auto frags = [&](int c, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+            const int sg = 2 * c + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = sa[swz(wm * 128 + 32 * i + (lane & 31), sg)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = sb[swz(wn * 128 + 32 * j + (lane & 31), sg)];
+        };
+        frags(0, af[0], bw[0]);
+        frags(1, af[1], bw[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[c][i], bw[c][j]);
+    }
+
+    const S *bi = static_cast<const S *>(a.b_ih[d]);
+    const S *bh = static_cast<const S *>(a.b_hh[d]);
+    const size_t ldg = (size_t)a.D * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) Gs[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+            }
+    }
+}
+
+// ===========================================================================
 // Host-side launch helpers.
 // ===========================================================================
 static int proj_nsplit(const ProjArgs &a) { return a.kchunk > 0 ? (a.K + a.kchunk - 1) / a.kchunk : 1; }
 
+template <class DT, int NST>
+static hipError_t launch_proj_ring(const ProjArgs &a, hipStream_t s) {
+    const void *fn = reinterpret_cast<const void *>(&k_proj_ring<DT, NST>);
+    const size_t smem = (size_t)NST * (256 + 256) * 4 * 16;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D * proj_nsplit(a));
+    hipLaunchKernelGGL((k_proj_ring<DT, NST>), grid, dim3(256), smem, s, a);
+    return hipGetLastError();
+}
+
 template <class DT, bool VEC>
-static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, hipStream_t s) {
+static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, int ring, hipStream_t s) {
     const int zd = a.D * proj_nsplit(a);
+    if (big && dma && VEC && ring == 4) return launch_proj_ring<DT, 4>(a, s);
+    if (big && dma && VEC && ring == 5) return launch_proj_ring<DT, 5>(a, s);
     if (big && dma && VEC) {
         const void *fn = reinterpret_cast<const void *>(&k_proj_dma<DT>);
         const size_t smem = 2 * (256 + 256) * 8 * 16;
@@ -1522,6 +1657,9 @@ static void proj_choose(int M, int N, int K, int ldx, int D, int dtype, int vari
     *dma = *big && vec && variant != 2 && (size_t)256 * ldx * es < (1u << 31) && (size_t)256 * K * es < (1u << 31);
 }
 
+// stages of the direct-to-LDS ring (0: the double-buffered k_proj_dma)
+static int proj_ring(int variant) { return variant == 4 ? 4 : variant == 5 ? 5 : 0; }
+
 int proj_kchunk(int M, int N, int K) {
     const long long tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);
     if (tiles >= 128 || K < 512) return 0;
@@ -1536,7 +1674,7 @@ const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant)
     const int per16 = dtype == DT_BF16 ? 8 : 4;
     bool big, dma;
     proj_choose(M, N, K, K, D, dtype, variant, K % per16 == 0, &big, &dma);
-    return dma ? "k_proj_dma" : big ? "k_proj_big" : "k_proj";
+    return dma ? (proj_ring(variant) ? "k_proj_ring" : "k_proj_dma") : big ? "k_proj_big" : "k_proj";
 }
 
 hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s) {
@@ -1547,9 +1685,10 @@ hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s)
         return hipErrorInvalidValue;
     bool big, dma;
     proj_choose(a.M, a.N, a.K, a.ldx, a.D * proj_nsplit(a), dtype, variant, vec, &big, &dma);
+    const int ring = proj_ring(variant);
     if (dtype == DT_BF16)
-        return vec ? launch_proj_t<BF16, true>(a, big, dma, s) : launch_proj_t<BF16, false>(a, big, dma, s);
-    return vec ? launch_proj_t<F32, true>(a, big, dma, s) : launch_proj_t<F32, false>(a, big, dma, s);
+        return vec ? launch_proj_t<BF16, true>(a, big, dma, ring, s) : launch_proj_t<BF16, false>(a, big, dma, ring, s);
+    return vec ? launch_proj_t<F32, true>(a, big, dma, ring, s) : launch_proj_t<F32, false>(a, big, dma, ring, s);
 }
 
 int rec_rows_per_wg(RecTile t) { return 16 * (4 / t.WK) * t.MTW; }
