@@ -35,7 +35,7 @@ struct lstm_plan {
     unsigned long long drop_call;   // call index of the next lstm_forward_train
                        // (off by default: slower than layer by layer on the measured workloads)
     int team_rows;   // 0 = as many batch rows per team as the tile holds, else at most this many
-    int proj_tile;   // projection GEMM tile: 0 automatic, 1 128x128, 2 256x256
+    int proj_tile;   // projection GEMM (LSTM_OPT_PROJ_TILE): 0 automatic, 1..5 forced
     // optional per-phase timing (LSTM_OPT_TIMING)
     int timing;
     struct Span {
