@@ -283,7 +283,12 @@ lstm_status lstm_backward_workspace_size(const lstm_plan *plan, int T, int B, si
  *   workspace    at least lstm_backward_workspace_size bytes
  * Products accumulate in fp32 (bf16 operands are widened exactly); results
  * are rounded to the output dtype once.  Errors as lstm_forward; a short
- * reserve or workspace is LSTM_ERR_WORKSPACE. */
+ * reserve or workspace is LSTM_ERR_WORKSPACE, and B * D * 5 * hidden_size * 4
+ * bytes (one step's saved activations) of 2^31 or more LSTM_ERR_UNSUPPORTED.
+ * When the recurrent products' tiles would leave CUs idle, each tile's
+ * product is split between two workgroups that meet through the workspace;
+ * lstm_device_status on this workspace then reports a wait that gave up
+ * (flag 2; the outputs are invalid). */
 lstm_status lstm_backward(lstm_plan *plan, const void *x, const void *h0, const float *c0,
                           const void *const *weights, const void *y, const void *dy, const void *dh_n,
                           const float *dc_n, const void *reserve, size_t reserve_bytes, int T, int B, int layers,
@@ -302,8 +307,8 @@ lstm_status lstm_backward_lengths(lstm_plan *plan, const void *x, const int *len
                                   void *const *dweights, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronise `stream` and read the kernel status word a previous
- * lstm_forward left in `workspace`: *device_flags = 0 if every step barrier
- * completed.  Returns LSTM_ERR_DEVICE_TIMEOUT when a flag is set (the outputs
+ * lstm_forward (or lstm_backward, with its own workspace) left in
+ * `workspace`: *device_flags = 0 if every step barrier completed.  Returns LSTM_ERR_DEVICE_TIMEOUT when a flag is set (the outputs
  * of that call are then invalid). */
 lstm_status lstm_device_status(const void *workspace, size_t workspace_bytes, void *stream,
                                unsigned *device_flags);

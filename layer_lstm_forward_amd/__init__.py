@@ -393,7 +393,17 @@ class LSTM:
                            [w.data_ptr() for w in dws], ws.data_ptr(), nbytes, stream, lengths=lengths)
         if rc:
             raise LSTMError(rc, "lstm_backward")
+        self._bws = ws
         return dx, dh0, dc0, dws
+
+    def backward_status(self, stream=None):
+        """lstm_device_status on the last backward call's workspace (a K-split step's wait gave up: flag 2)."""
+        import torch
+        if getattr(self, "_bws", None) is None:
+            return 0, 0
+        if stream is None:
+            stream = torch.cuda.current_stream(self._bws.device).cuda_stream
+        return lstm_device_status(self._bws.data_ptr(), self._bws.numel(), stream)
 
     def device_status(self, stream=None):
         import torch

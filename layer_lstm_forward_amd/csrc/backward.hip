@@ -46,39 +46,51 @@ struct CellIn {
     int len;                             // 0 where lengths are NULL
 };
 
-// a[i] through a buffer resource: NULL (no records) reads 0 without a branch
-__device__ inline float ld_or0(const float *a, size_t i) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a), (short)0, a ? 0x7FFFFFFF : 0, 0x00020000);
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4), 0, 0));
+// The float at byte offset off of a buffer of nbytes bytes through a buffer
+// resource: NULL (no records) reads 0, without a branch.
+__device__ inline float bld(const void *base, unsigned nbytes, unsigned off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                                                       base ? (int)nbytes : 0, 0x00020000);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
 // Every load is unconditional (any choice between them waits for the
 // compiler's join of the paths, i.e. for the loads), and the choices are
-// made in bwd_cell_store.  sb, b and j must be in range.
+// made in bwd_cell_store.  All of them are buffer loads with 32-bit offsets
+// from wave-uniform bases (the step's time slices of acts and dY, the
+// [D, B, H] arrays whole; the host keeps each within 2^31 bytes): 64-bit
+// address arithmetic among the loads had the compiler pass a loaded register
+// as a don't-care operand, i.e. wait for that load before the product's own
+// loads went out.  sb and d must be uniform, b and j in range.
 template <class G>
 __device__ inline CellIn bwd_cell_load(const BwdCellArgs &a, int sb, int d, int b, int j) {
-    const int T = a.T, B = a.B, H = a.H, D = a.D;
+    const int T = a.T;
+    const unsigned B = a.B, H = a.H, D = a.D;
     const int sf = T - 1 - sb;                   // the forward scan's step
-    const int t = d == 0 ? sf : T - 1 - sf;      // its time index
+    const int t = __builtin_amdgcn_readfirstlane(d == 0 ? sf : T - 1 - sf);  // its time index
     const int tp = d == 0 ? t - 1 : t + 1;       // time of the scan's previous step
-    const int tpc = tp < 0 ? 0 : tp >= T ? T - 1 : tp;
-    const size_t dbj = ((size_t)d * B + b) * H + j;
+    const int tpc = __builtin_amdgcn_readfirstlane(tp < 0 ? 0 : tp >= T ? T - 1 : tp);
+    const unsigned ud = (unsigned)d, ub = (unsigned)b, uj = (unsigned)j;
+    const unsigned sbytes = D * B * H * 4u, so = ((ud * B + ub) * H + uj) * 4u;  // [D, B, H]
+    const unsigned arow = B * D * 5u * H;                                     // acts floats per step
+    const unsigned ao = ((ub * D + ud) * 5u * H + uj) * 4u;
+    const unsigned yrow = B * D * H;                                           // dY floats per step
+    const unsigned yo = ((ub * D + ud) * H + uj) * 4u;
+    const float *at = a.acts + (size_t)t * arow, *ap = a.acts + (size_t)tpc * arow;
     CellIn v;
-    v.len = (int)__float_as_uint(ld_or0(reinterpret_cast<const float *>(a.len), (size_t)b));
-    v.dhn = ld_or0(a.dhn, dbj);
-    v.dhc = ld_or0(a.dhc, dbj);
-    v.dcn = ld_or0(a.dcn, dbj);
-    v.dc = a.dc[dbj];
-    v.dY = a.dY[((size_t)t * B + b) * ((size_t)D * H) + (size_t)d * H + j];
-    const float *ap = a.acts + (((size_t)t * B + b) * D + d) * 5 * H + j;
-    v.ig = ap[0];
-    v.fg = ap[(size_t)H];
-    v.gg = ap[(size_t)2 * H];
-    v.og = ap[(size_t)3 * H];
-    v.c = ap[(size_t)4 * H];
-    v.c0 = ld_or0(a.c0, dbj);
-    v.cpa = a.acts[(((size_t)tpc * B + b) * D + d) * 5 * H + (size_t)4 * H + j];
+    v.len = (int)__float_as_uint(bld(a.len, B * 4u, ub * 4u));
+    v.dhn = bld(a.dhn, sbytes, so);
+    v.dhc = bld(a.dhc, sbytes, so);
+    v.dcn = bld(a.dcn, sbytes, so);
+    v.dc = bld(a.dc, sbytes, so);
+    v.dY = bld(a.dY + (size_t)t * yrow, yrow * 4u, yo);
+    v.ig = bld(at, arow * 4u, ao);
+    v.fg = bld(at, arow * 4u, ao + H * 4u);
+    v.gg = bld(at, arow * 4u, ao + 2u * H * 4u);
+    v.og = bld(at, arow * 4u, ao + 3u * H * 4u);
+    v.c = bld(at, arow * 4u, ao + 4u * H * 4u);
+    v.c0 = bld(a.c0, sbytes, so);
+    v.cpa = bld(ap, arow * 4u, ao + 4u * H * 4u);
     return v;
 }
 
@@ -128,10 +140,10 @@ __device__ inline void bwd_cell_update(const BwdCellArgs &a, int sb, int d, int 
 // The first backward step of every (direction, batch row, unit): dh = dY + dh_n.
 template <class G>
 __global__ void k_bwd_cell(BwdCellArgs a) {
-    const size_t n = (size_t)a.D * a.B * a.H;
+    const size_t n = (size_t)a.B * a.H;
     const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
-    bwd_cell_update<G>(a, 0, (int)(i / ((size_t)a.H * a.B)), (int)((i / a.H) % a.B), (int)(i % a.H), 0.f);
+    bwd_cell_update<G>(a, 0, (int)blockIdx.z, (int)(i / a.H), (int)(i % a.H), 0.f);
 }
 
 // Backward step sb: the recurrent product dh_prev = dz_t W_hh of step sb for
@@ -156,11 +168,17 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void k_bwd_step(BwdMmArgs a, BwdCel
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.B, H = a.H, D = a.D, K = 4 * H;
     const int d = blockIdx.z;
+    const int nmb = (B + 15) / 16, nub = (H + 15) / 16, ntile = nmb * nub;
+    // with a K split, workgroups [0, ntile) own their tiles and finish them;
+    // [ntile, 2 ntile) are their helpers (the same tile order, so a helper
+    // runs on its owner's XCD when ntile is a multiple of 8)
+    const int half = (int)blockIdx.x >= ntile ? 1 : 0;
+    const int tile = (int)blockIdx.x - half * ntile;
     int mb, ub;
     {
         // the row blocks of one unit block run on the same XCD (round-robin
         // dispatch), so its W_hh^T rows are fetched into that XCD's L2 once
-        const int bid = blockIdx.x, nmb = (B + 15) / 16, nub = (H + 15) / 16;
+        const int bid = tile;
         if ((nub & 7) == 0) {
             const int idx = bid >> 3;
             ub = (bid & 7) + 8 * (idx / nmb);
@@ -173,8 +191,11 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void k_bwd_step(BwdMmArgs a, BwdCel
     const int b0 = mb * 16, u0 = ub * 16;
     const int b = b0 + (lane & 15);  // A row (batch row) of this lane
     const int j = u0 + (lane & 15);  // B row (unit) of this lane
-    const int kq = (K + NW * G::KC - 1) / (NW * G::KC) * G::KC;  // K per wave, whole chunks
-    const int k_lo = w * kq, k_hi = min(K, k_lo + kq);
+    // this workgroup's K range (whole chunks), then each wave's
+    const int kseg = (K + a.ksplit * G::KC - 1) / (a.ksplit * G::KC) * G::KC;
+    const int kb = half * kseg, ke = min(K, kb + kseg);
+    const int kq = (ke - kb + NW * G::KC - 1) / (NW * G::KC) * G::KC;
+    const int k_lo = kb + w * kq, k_hi = min(ke, k_lo + kq);
     const int sf = a.T - 1 - a.sb;
     const int t = d == 0 ? sf : a.T - 1 - sf;
     constexpr unsigned es = sizeof(S);
@@ -189,19 +210,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void k_bwd_step(BwdMmArgs a, BwdCel
         0x00020000);
     const unsigned aoff = (unsigned)((size_t)b * D * K * es);
     const unsigned boff = (unsigned)((size_t)j * K * es);
-    // the cell update's own inputs (one cell per thread of the first 256)
-    const int rb_ = (tid >> 4) & 15, ru = tid & 15;
-    const int m = b0 + rb_, u = u0 + ru;
-    const bool cell = tid < 256 && m < B && u < H && a.sb + 1 < a.T;
-    const CellIn cin = bwd_cell_load<G>(c, min(a.sb + 1, a.T - 1), d, min(m, B - 1), min(u, H - 1));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     // batches of 16 chunks: all 32 fragment loads are issued before the first
     // product of the batch; scheduling barriers keep the compiler from
     // interleaving them with the products into a chain of round trips
     constexpr int NBAT = 16;
     constexpr unsigned OOR = 0x7FFFFFF0u;
-    for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * G::KC) {
-        u32x4 av[NBAT], bv[NBAT];
+    auto issue = [&](int k0, u32x4 (&av)[NBAT], u32x4 (&bv)[NBAT]) {
 #pragma unroll
         for (int q = 0; q < NBAT; ++q) {
             const int k = k0 + q * G::KC + (lane >> 4) * G::PER16;
@@ -209,20 +224,57 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void k_bwd_step(BwdMmArgs a, BwdCel
             av[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(kin && b < B ? aoff + es * k : OOR), 0, 0);
             bv[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(kin && j < H ? boff + es * k : OOR), 0, 0);
         }
+    };
+    auto multiply = [&](const u32x4 (&av)[NBAT], const u32x4 (&bv)[NBAT]) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NBAT; ++q) acc = mma_chunk(G{}, acc, av[q], bv[q]);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // the cell update's own inputs (one cell per thread of the first 256)
+    const int rb_ = (tid >> 4) & 15, ru = tid & 15;
+    const int m = b0 + rb_, u = u0 + ru;
+    const bool cell = tid < 256 && m < B && u < H && a.sb + 1 < a.T;
+    const CellIn cin = bwd_cell_load<G>(c, min(a.sb + 1, a.T - 1), d, min(m, B - 1), min(u, H - 1));
+    for (int k0 = k_lo; k0 < k_hi; k0 += NBAT * G::KC) {
+        u32x4 av[NBAT], bv[NBAT];
+        issue(k0, av, bv);
+        multiply(av, bv);
     }
     // lane l, register v: batch row 4 (l / 16) + v, unit l % 16 of the tile
     __shared__ float red[NW][16][17];
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
     __syncthreads();
-    if (tid >= 256 || m >= B || u >= H) return;
+    if (tid >= 256) return;
     float r = red[0][rb_][ru];  // the waves' K slices, added in order
 #pragma unroll
     for (int q = 1; q < NW; ++q) r += red[q][rb_][ru];
+    unsigned long long *pw = a.ksplit == 2 ? a.pbuf + ((size_t)d * ntile + tile) * 256 + tid : nullptr;
+    const unsigned long long want = (unsigned long long)a.tag << 32;
+    if (half) {  // helper: hand the partial sum over (every word, dead cells too)
+        __hip_atomic_store(pw, want | __float_as_uint(r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (m >= B || u >= H) return;
+    if (a.ksplit == 2) {  // owner: the helper's half of K, added after this one's
+        unsigned long long v = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & 0xFFFFFFFF00000000ull) != want) {
+            const long long t0 = wall_clock64();
+            do {
+                __builtin_amdgcn_s_sleep(1);
+                v = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((v & 0xFFFFFFFF00000000ull) == want) break;
+                // an earlier wait gave up: the outputs are invalid, do not wait again
+                if (wall_clock64() - t0 > a.timeout_ticks ||
+                    (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2u)) {
+                    __hip_atomic_fetch_or(a.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            } while (true);
+        }
+        r += __uint_as_float((unsigned)v);
+    }
     if (cell) bwd_cell_store<G>(c, a.sb + 1, d, m, u, r, cin);
     else if (dh0) dh0[((size_t)d * B + m) * H + u] = DT::from_f(r + (c.len ? c.dhc[((size_t)d * B + m) * H + u] : 0.f));
 }
@@ -391,8 +443,8 @@ static unsigned grid1(size_t n, unsigned cap = 8192) {
 }
 
 hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s) {
-    const size_t n = (size_t)a.D * a.B * a.H;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    const size_t n = (size_t)a.B * a.H;
+    const dim3 grid((unsigned)((n + 255) / 256), 1, a.D);
     if (gdt == DT_BF16) hipLaunchKernelGGL(k_bwd_cell<BF16>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_bwd_cell<F32>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
@@ -401,7 +453,8 @@ hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s) {
 hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s) {
     if (c.dz != a.dz || c.T != a.T || c.B != a.B || c.H != a.H || c.D != a.D) return hipErrorInvalidValue;
     if (gdt == DT_BF16 && a.H % 2 != 0) return hipErrorInvalidValue;  // whole bf16 fragments over K = 4H
-    dim3 grid(((a.B + 15) / 16) * ((a.H + 15) / 16), 1, a.D);
+    if (a.ksplit != 1 && (a.ksplit != 2 || !a.pbuf || !a.status || a.tag == 0)) return hipErrorInvalidValue;
+    dim3 grid(((a.B + 15) / 16) * ((a.H + 15) / 16) * a.ksplit, 1, a.D);
     if (gdt == DT_BF16 && dtype == DT_BF16)
         hipLaunchKernelGGL((k_bwd_step<BF16, BF16>), grid, dim3(BWD_WAVES * 64), 0, s, a, c, static_cast<uint16_t *>(dh0));
     else if (gdt == DT_BF16)

@@ -163,6 +163,16 @@ struct BwdMmArgs {
     const void *dz;     // [T, B, D, 4H], gradient dtype
     const void *whT;    // [D, H, 4H] transposed W_hh, gradient dtype
     int T, B, H, D, sb;
+    // ksplit 2: each 16x16 tile's K = 4H is split between two workgroups; the
+    // second hands its partial sums to the first through pbuf ([D][tiles]
+    // [256] words of (tag << 32 | fp32 bits), zeroed before the first launch
+    // of a call), tagged with this launch's tag (unique within the call, not
+    // 0); a wait that outlasts timeout_ticks sets bit 1 of *status
+    int ksplit;
+    unsigned tag;
+    unsigned long long *pbuf;
+    unsigned *status;
+    long long timeout_ticks;
 };
 // The backward pass stores dz and multiplies it in the gradient dtype gdt:
 // bf16 (fp32 accumulation; the cell math stays fp32) for bf16 parameters
@@ -171,6 +181,8 @@ struct BwdMmArgs {
 hipError_t launch_bwd_cell(const BwdCellArgs &a, int gdt, hipStream_t s);
 // Backward step a.sb: the recurrent product, then the cell update of step
 // a.sb + 1, or dh0 ([D, B, H], dtype; NULL = not wanted) after the last step.
+// With a.ksplit = 2 every workgroup of the launch must be resident at once
+// (two per tile; the caller keeps the grid within one per CU).
 hipError_t launch_bwd_step(const BwdMmArgs &a, const BwdCellArgs &c, void *dh0, int gdt, int dtype, hipStream_t s);
 // out[c * ld_out + r] = in[r * ld_in + c] (rows x cols, in_dtype -> out_dtype);
 // with bT > 0 (rows = bT * bB) the input rows are batch-first: row r = t*bB + b

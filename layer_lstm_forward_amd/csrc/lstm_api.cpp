@@ -206,7 +206,7 @@ bool make_reserve(const lstm_plan *p, int T, int B, ReserveLayout *r) {
 // [D][H][4H] and W_ih [in][D*4H]; the K-split slabs of the gradient products;
 // one bias gradient [4H].
 struct BwdLayout {
-    size_t dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, lens, dhc, total;
+    size_t status, pbuf, dz, dzt, xt, ht, dy[2], dc, dhn, wht, wcat, ksp, db, lens, dhc, total;
 };
 
 // row chunks of the bias-gradient column sums
@@ -224,7 +224,10 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     const size_t win = std::max((size_t)p->I, D * H);
     size_t tb;
     if (!mul_ok((size_t)T, (size_t)B, &tb) || tb > (size_t)INT_MAX) return false;
-    size_t sz[14];
+    size_t sz[16];
+    sz[14] = kStatusBytes;  // status word first, as in the forward's workspace
+    // partial sums handed between the two halves of a K-split backward step
+    sz[15] = D * (size_t)((B + 15) / 16) * ((H + 15) / 16) * 256 * sizeof(unsigned long long);
     if (!mul_ok(tb, D * G4 * f, &sz[0]) || !mul_ok(tb, G4 * f, &sz[1]) || !mul_ok(tb, win * f, &sz[2]) ||
         !mul_ok(tb, H * f, &sz[3]) || !mul_ok(tb, win * f, &sz[4]))
         return false;
@@ -248,10 +251,11 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
     sz[11] = (size_t)kBiasChunks * G4 * f;  // bias-gradient partial sums
     sz[12] = (size_t)B * sizeof(int);        // per-row lengths
     sz[13] = D * B * H * f;                  // gradient of h carried through padded steps
-    size_t *dst[14] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
-                       &o->wht, &o->wcat, &o->ksp, &o->db, &o->lens, &o->dhc};
+    size_t *dst[16] = {&o->dz, &o->dzt, &o->xt, &o->ht, &o->dy[0], &o->dy[1], &o->dc, &o->dhn,
+                       &o->wht, &o->wcat, &o->ksp, &o->db, &o->lens, &o->dhc, &o->status, &o->pbuf};
+    const int order[16] = {14, 15, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13};
     size_t off = 0;
-    for (int i = 0; i < 14; ++i) {
+    for (int i : order) {
         *dst[i] = off;
         if (sz[i] > SIZE_MAX - off - 256) return false;
         off += align_up(sz[i]);
@@ -1304,6 +1308,9 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
     BwdLayout bl{};
     if (!make_reserve(p, T, B, &rl) || !make_bwd_layout(p, T, B, &bl)) return LSTM_ERR_SHAPE;
     if (reserve_bytes < rl.total || workspace_bytes < bl.total) return LSTM_ERR_WORKSPACE;
+    // the backward cell reads one step's activations ([B, D, 5H] floats) and
+    // the [D, B, H] state arrays with 32-bit byte offsets
+    if ((size_t)B * p->D * 5 * p->H * sizeof(float) >= ((size_t)1 << 31)) return LSTM_ERR_UNSUPPORTED;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
@@ -1382,6 +1389,19 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
         (void)hipGetLastError();
         return LSTM_ERR_LAUNCH;
     }
+    // The recurrent product of a backward step: a 16x16 tile per workgroup
+    // over the whole K = 4H, or, when those tiles leave CUs idle, its K split
+    // between two workgroups (all resident at once: at most one per CU).
+    // The status word and the hand-over buffer start at zero in every call,
+    // and each step launch gets a tag of its own.
+    const DevInfo di = dev_info(dev);
+    const long long tiles = (long long)((B + 15) / 16) * ((H + 15) / 16) * D;
+    const int ksplit = di.ok && 2 * tiles <= di.cus ? 2 : 1;
+    unsigned *bstatus = reinterpret_cast<unsigned *>(ws + bl.status);
+    auto *pbuf = reinterpret_cast<unsigned long long *>(ws + bl.pbuf);
+    const long long timeout_ticks = (long long)(di.ok ? di.wall_khz : 100000) * 1000LL * 2;  // two seconds
+    unsigned step_tag = 0;
+    if (launch_fill_u32(bstatus, (bl.dz - bl.status) / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
     // the gradient of the top layer's output, as fp32
     int cur = 0;
     // batch-first x, y, dy, dx: the internal gradient buffers stay time-major
@@ -1431,6 +1451,11 @@ static lstm_status backward_impl(lstm_plan *p, const void *x, const int *lengths
             ma.H = H;
             ma.D = D;
             ma.sb = sb;
+            ma.ksplit = ksplit;
+            ma.tag = ++step_tag;
+            ma.pbuf = pbuf;
+            ma.status = bstatus;
+            ma.timeout_ticks = timeout_ticks;
             if (!ok(launch_bwd_step(ma, ca, dh0l, gdt, dt, st))) return fail();
         }
         span_end(p, rec_span, st, T);

@@ -31,6 +31,10 @@ SPECS = [
     Spec(32, 64, 1, False, 256, 256, "f32", 809, "normal0.1"),  # 256x256 direct-to-LDS tiles, 256 splits
     # bf16 parameters with an odd H: dz and the backward products stay fp32
     Spec(30, 37, 2, True, 6, 9, "bf16", 811, "normal0.1"),
+    # 256 recurrent 16x16 tiles fill the CUs: K stays whole in one workgroup
+    # (every case above has at most 128 and splits K between two)
+    Spec(64, 1024, 1, True, 4, 32, "f32", 812, "normal0.1"),
+    Spec(32, 1024, 1, True, 3, 32, "bf16", 813, "zeros"),
 ]
 
 
@@ -336,3 +340,49 @@ def test_batch_first_training_matches_oracle(spec, mode, p):
         _check(cpu(dc0), rdc0, spec.dtype, "dc0")
     for k, (g, r) in enumerate(zip(dws, rdps)):
         _check(cpu(g), r, spec.dtype, f"dweights[{k}]")
+
+
+FULL_TRAIN = [
+    # the training benchmark's workload: (spec, sampled batch rows); its 128
+    # recurrent 16x16 tiles leave half the CUs idle, so K is split between
+    # two workgroups.  (The bidirectional bf16 workload would take the oracle
+    # about 100 s per row; its 256-tile schedule is checked at a smaller T.)
+    (Spec(256, 512, 2, False, 128, 64, "f32", 1101, "normal0.1"), [0, 29, 63]),
+]
+
+
+@pytest.mark.parametrize("spec,rows", FULL_TRAIN, ids=lambda v: _id(v) if isinstance(v, Spec) else "")
+def test_full_size_training_sampled_rows(spec, rows):
+    # Rows are independent given their own dy, dh_n and dc_n, so dx, dh0 and
+    # dc0 of a few rows of the full-size launch are checked against the
+    # oracle run on those rows alone.  (The weight gradients sum over every
+    # row; the smaller cases above check them element by element.)
+    import torch
+    print(f"case {_id(spec)} full-size training, rows {rows}", flush=True)
+    inp = make_inputs(spec)
+    bf = spec.dtype == "bf16"
+    dev = "cuda:0"
+    dy, dhn, dcn = _grads(spec, spec.seed + 5)
+    if bf:
+        from layer_lstm_forward_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+        dy_b, dhn_b = f32_to_bf16_bits(dy), f32_to_bf16_bits(dhn)
+        dy, dhn = bf16_bits_to_f32(dy_b), bf16_bits_to_f32(dhn_b)
+    m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, dtype=spec.dtype)
+    x = to_dev(inp.x, bf, dev)
+    w = [to_dev(p, bf, dev) for p in inp.params]
+    h0 = None if inp.h0 is None else to_dev(inp.h0, bf, dev)
+    c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
+    y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
+    dx, dh0, dc0, dws = m.backward(x, w, y, reserve, to_dev(dy_b if bf else dy, bf, dev), h0=h0, c0=c0,
+                                   dh_n=to_dev(dhn_b if bf else dhn, bf, dev), dc_n=torch.from_numpy(dcn).to(dev))
+    torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)
+    sub = inp.rows(rows)
+    rdx, rdh0, rdc0, _ = oracle.lstm_backward(sub.x, sub.params, spec.hidden_size, spec.num_layers,
+                                              spec.bidirectional, np.ascontiguousarray(dy[:, rows]), h0=sub.h0,
+                                              c0=sub.c0, dh_n=np.ascontiguousarray(dhn[:, rows]),
+                                              dc_n=np.ascontiguousarray(dcn[:, rows]), bf16=bf)
+    cpu = lambda t: t.float().cpu().numpy()  # noqa: E731
+    _check(cpu(dx)[:, rows], rdx, spec.dtype, "dx")
+    _check(cpu(dh0)[:, rows], rdh0, spec.dtype, "dh0")
+    _check(cpu(dc0)[:, rows], rdc0, spec.dtype, "dc0")
