@@ -265,3 +265,19 @@ def test_training_lengths_validated_on_the_host():
             assert pkg.lstm_backward(p, FAKE, lengths=bad, **bargs) == -1
     finally:
         pkg.lstm_destroy(p)
+
+
+def test_backward_rejects_steps_past_32_bit_offsets():
+    # one step's saved activations (B * D * 5H floats) must stay under 2^31
+    # bytes: the backward cell reads them with 32-bit offsets; checked on the
+    # host before any device access
+    FAKE = 0x10000
+    p = pkg.lstm_create(8, 2048, 1, True, True, pkg.LSTM_F32)
+    try:
+        bargs = dict(h0=0, c0=0, weights=[FAKE] * 8, y=FAKE, dy=FAKE, dh_n=0, dc_n=0, reserve=FAKE,
+                     reserve_bytes=1 << 60, T=1, B=32768, layers=1, bidir=True, dx=0, dh0=0, dc0=0,
+                     dweights=[FAKE] * 8, workspace=FAKE, workspace_bytes=1 << 60, stream=0)
+        assert pkg.lstm_backward(p, FAKE, **bargs) == -7          # 32768 * 2 * 5 * 2048 * 4 = 2^31 bytes
+        assert pkg.lstm_backward(p, FAKE, **dict(bargs, B=0)) == -2
+    finally:
+        pkg.lstm_destroy(p)
