@@ -46,14 +46,6 @@ struct CellIn {
     int len;                             // 0 where lengths are NULL
 };
 
-// The float at byte offset off of a buffer of nbytes bytes through a buffer
-// resource: NULL (no records) reads 0, without a branch.
-__device__ inline float bld(const void *base, unsigned nbytes, unsigned off) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                                                       base ? (int)nbytes : 0, 0x00020000);
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-}
-
 // Every load is unconditional (any choice between them waits for the
 // compiler's join of the paths, i.e. for the loads), and the choices are
 // made in bwd_cell_store.  All of them are buffer loads with 32-bit offsets
@@ -78,19 +70,19 @@ __device__ inline CellIn bwd_cell_load(const BwdCellArgs &a, int sb, int d, int 
     const unsigned yo = ((ub * D + ud) * H + uj) * 4u;
     const float *at = a.acts + (size_t)t * arow, *ap = a.acts + (size_t)tpc * arow;
     CellIn v;
-    v.len = (int)__float_as_uint(bld(a.len, B * 4u, ub * 4u));
-    v.dhn = bld(a.dhn, sbytes, so);
-    v.dhc = bld(a.dhc, sbytes, so);
-    v.dcn = bld(a.dcn, sbytes, so);
-    v.dc = bld(a.dc, sbytes, so);
-    v.dY = bld(a.dY + (size_t)t * yrow, yrow * 4u, yo);
-    v.ig = bld(at, arow * 4u, ao);
-    v.fg = bld(at, arow * 4u, ao + H * 4u);
-    v.gg = bld(at, arow * 4u, ao + 2u * H * 4u);
-    v.og = bld(at, arow * 4u, ao + 3u * H * 4u);
-    v.c = bld(at, arow * 4u, ao + 4u * H * 4u);
-    v.c0 = bld(a.c0, sbytes, so);
-    v.cpa = bld(ap, arow * 4u, ao + 4u * H * 4u);
+    v.len = (int)__float_as_uint(load_f32_or0(a.len, B * 4u, ub * 4u));
+    v.dhn = load_f32_or0(a.dhn, sbytes, so);
+    v.dhc = load_f32_or0(a.dhc, sbytes, so);
+    v.dcn = load_f32_or0(a.dcn, sbytes, so);
+    v.dc = load_f32_or0(a.dc, sbytes, so);
+    v.dY = load_f32_or0(a.dY + (size_t)t * yrow, yrow * 4u, yo);
+    v.ig = load_f32_or0(at, arow * 4u, ao);
+    v.fg = load_f32_or0(at, arow * 4u, ao + H * 4u);
+    v.gg = load_f32_or0(at, arow * 4u, ao + 2u * H * 4u);
+    v.og = load_f32_or0(at, arow * 4u, ao + 3u * H * 4u);
+    v.c = load_f32_or0(at, arow * 4u, ao + 4u * H * 4u);
+    v.c0 = load_f32_or0(a.c0, sbytes, so);
+    v.cpa = load_f32_or0(ap, arow * 4u, ao + 4u * H * 4u);
     return v;
 }
 

@@ -169,4 +169,13 @@ __device__ inline bool xc_ok(const u32x4 &w, unsigned tb) {
     return ((tb ? all : ~any) >> xc_shift<BF>()) & 1u;
 }
 
+// The float at byte offset off of a buffer of nbytes bytes, through a buffer
+// resource: a NULL base (no records) reads 0, without a branch (a branch
+// around a load makes the compiler wait for it where the paths join).
+__device__ inline float load_f32_or0(const void *base, unsigned nbytes, unsigned off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                                                       base ? (int)nbytes : 0, 0x00020000);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 }  // namespace lstm_amd

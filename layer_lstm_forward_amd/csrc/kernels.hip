@@ -1295,13 +1295,35 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
     const int b0 = mb * BM, u0 = ub * 32;
     const int es = (int)sizeof(S);
     const size_t ldy = (size_t)D * H;
-    const size_t ldg = (size_t)D * NG * H;
 
     f32x16 acc[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+    // G of the cells this lane finishes (below): independent of the product,
+    // so they are loaded while it runs (streamed once: non-temporal).  Cells
+    // past B or H read a clamped valid address; their values go unused.
+    constexpr int VPW = 16 / WKS;  // result registers finished per wave
+    const size_t ldg = (size_t)D * NG * H;
+    // The LSTM's carried c (c0 at the first step, NULL: zeros) likewise.
+    float gv[VPW][NG], cpv[VPW];
+    auto load_gv = [&]() {
+        const int uc = min(u0 + (lane & 31), H - 1);
+        const float *cb = s == 0 ? a.c0 : a.cstate;
+#pragma unroll
+        for (int vv = 0; vv < VPW; ++vv) {
+            const int v = VPW * wk + vv;
+            const int mc = min(b0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), B - 1);
+            const float *g = a.G + trow(t, mc, T, B, a.bfirst) * ldg + (size_t)d * NG * H + uc;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) gv[vv][j] = __builtin_nontemporal_load(g + (size_t)j * H);
+            if constexpr (MODE == 0)
+                cpv[vv] = load_f32_or0(cb, (unsigned)((size_t)D * B * H * 4),
+                                       (unsigned)((((size_t)d * B + mc) * H + uc) * 4));
+        }
+    };
 
     // h_{t-1}: rows b0.. of y at the previous step, or of h0 at s = 0
     const S *hsrc = nullptr;
@@ -1349,6 +1371,11 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
 #pragma unroll
         for (int k = 0; k < NST - 1; ++k)
             if (k < nk) issue(k, k);
+        // after the first stages (a wait the compiler may place among these
+        // loads then covers loads the first products need anyway); the stage
+        // waits below stay conservative: the extra loads only make the first
+        // stages wait for them as well
+        load_gv();
         for (int kt = 0; kt < nk; ++kt) {
             const int buf = kt % NST;
             // this wave's loads of stage kt are in LDS once at most the loads of
@@ -1385,9 +1412,10 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         __syncthreads();  // the stage buffers are reused below
     }
 
+    if (!hsrc) load_gv();  // no product at this step
+
     // With two K slices, wave (wm, wk) finishes the result registers
     // v in [8 wk, 8 wk + 8) and hands the other half to its partner.
-    constexpr int VPW = 16 / WKS;  // result registers finished per wave
     float *red = reinterpret_cast<float *>(smem);  // [4 waves][32 values][64 lanes]
     const int partner = wm + WM * (1 - wk);
     if (WKS == 2) {
@@ -1408,7 +1436,7 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
 #pragma unroll
         for (int j = 0; j < NG; ++j)
             pre[j] = acc[j][v] + (WKS == 2 ? red[((size_t)partner * 32 + j * 8 + vv) * 64 + lane] : 0.f);
-        const float *g = a.G + trow(t, m, T, B, a.bfirst) * ldg + (size_t)d * NG * H + u;
+        const float *g = gv[vv];  // G of gate block j at g[j]
         const size_t si = ((size_t)d * B + m) * H + u;
         if constexpr (MODE != 0) {
             // hidden contributions with b_hh; h_{t-1} of this cell for the GRU
@@ -1419,8 +1447,8 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             float hv;
             if constexpr (MODE == 1) {
                 const float rg = sigmoid_f(g[0] + pre[0]);
-                const float zg = sigmoid_f(g[(size_t)H] + pre[1]);
-                const float ng = tanh_f(g[(size_t)2 * H] + rg * pre[2]);
+                const float zg = sigmoid_f(g[1] + pre[1]);
+                const float ng = tanh_f(g[2] + rg * pre[2]);
                 hv = (1.f - zg) * ng + zg * DT::to_f(hprev);
             } else if constexpr (MODE == 2) {
                 hv = tanh_f(g[0] + pre[0]);
@@ -1433,11 +1461,11 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             static_cast<S *>(a.Y)[trow(t, m, T, B, a.bfirst) * ldy + (size_t)d * H + u] = hs;
             if (last && a.hn) static_cast<S *>(a.hn)[si] = hs;
         } else {
-            const float cp = s == 0 ? (a.c0 ? a.c0[si] : 0.f) : a.cstate[si];
+            const float cp = cpv[vv];
             const float ig = sigmoid_f(pre[0] + g[0]);
-            const float fg = sigmoid_f(pre[1] + g[(size_t)H]);
-            const float gg = tanh_f(pre[2] + g[(size_t)2 * H]);
-            const float og = sigmoid_f(pre[3] + g[(size_t)3 * H]);
+            const float fg = sigmoid_f(pre[1] + g[1]);
+            const float gg = tanh_f(pre[2] + g[2]);
+            const float og = sigmoid_f(pre[3] + g[3]);
             float cn = fg * cp + ig * gg;
             S hs = DT::from_f(og * tanh_f(cn));
             if (a.len && t >= a.len[m]) {
@@ -1849,7 +1877,8 @@ bool rec_step_gemm_ok(const RecArgs &a, int dtype) {
     const size_t astride = (size_t)a.D * a.H * (a.bfirst ? (size_t)a.T : 1);
     const size_t ng = a.mode == 0 ? 4 : a.mode == 1 ? 3 : 1;
     bool ok = ((size_t)a.H * es) % 16 == 0 && ng * a.H * a.H * es < (1u << 31) &&
-              ((size_t)128 * astride * es) < (1u << 31) && (uintptr_t)a.Y % 16 == 0 &&
+              ((size_t)128 * astride * es) < (1u << 31) && (size_t)a.D * a.B * a.H * 4 < (1u << 31) &&
+              (uintptr_t)a.Y % 16 == 0 &&
               (!a.h0 || (uintptr_t)a.h0 % 16 == 0);
     for (int d = 0; d < a.D; ++d) ok = ok && (uintptr_t)a.whh[d] % 16 == 0;
     return ok;
