@@ -178,4 +178,15 @@ __device__ inline float load_f32_or0(const void *base, unsigned nbytes, unsigned
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
+// The same for an element of the storage type of DT (bf16 or fp32), widened.
+template <class DT>
+__device__ inline float load_s_or0(const void *base, unsigned nbytes, unsigned off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                                                       base ? (int)nbytes : 0, 0x00020000);
+    if constexpr (sizeof(typename DT::S) == 2)
+        return DT::to_f((typename DT::S)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+    else
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 }  // namespace lstm_amd

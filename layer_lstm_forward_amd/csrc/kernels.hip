@@ -1302,13 +1302,28 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 
+    // h_{t-1}: rows b0.. of y at the previous step, or of h0 at s = 0
+    const S *hsrc = nullptr;
+    size_t lda = 0;
+    if (s > 0) {
+        const int tp = d == 0 ? s - 1 : T - s;
+        hsrc = static_cast<const S *>(a.Y) + trow(tp, b0, T, B, a.bfirst) * ldy + (size_t)d * H;
+        lda = a.bfirst ? (size_t)T * ldy : ldy;
+    } else if (a.h0) {
+        hsrc = static_cast<const S *>(a.h0) + ((size_t)d * B + b0) * H;
+        lda = H;
+    }
+
     // G of the cells this lane finishes (below): independent of the product,
     // so they are loaded while it runs (streamed once: non-temporal).  Cells
     // past B or H read a clamped valid address; their values go unused.
     constexpr int VPW = 16 / WKS;  // result registers finished per wave
     const size_t ldg = (size_t)D * NG * H;
-    // The LSTM's carried c (c0 at the first step, NULL: zeros) likewise.
-    float gv[VPW][NG], cpv[VPW];
+    // bytes of h_{t-1} this block may read (its rows of y or h0)
+    const unsigned hbytes = hsrc ? (unsigned)((((size_t)min(BM, B - b0) - 1) * lda + H) * sizeof(S)) : 0u;
+    // The LSTM's carried c (c0 at the first step, NULL: zeros) likewise, and
+    // for the other modes b_hh and the cell's h_{t-1} (NULL: zeros).
+    float gv[VPW][NG], cpv[VPW], hpv[VPW], bhv[NG];
     auto load_gv = [&]() {
         const int uc = min(u0 + (lane & 31), H - 1);
         const float *cb = s == 0 ? a.c0 : a.cstate;
@@ -1322,20 +1337,16 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
             if constexpr (MODE == 0)
                 cpv[vv] = load_f32_or0(cb, (unsigned)((size_t)D * B * H * 4),
                                        (unsigned)((((size_t)d * B + mc) * H + uc) * 4));
+            else
+                hpv[vv] = load_s_or0<DT>(hsrc, hbytes, (unsigned)(((size_t)(mc - b0) * lda + uc) * sizeof(S)));
         }
+        if constexpr (MODE != 0)
+#pragma unroll
+            for (int j = 0; j < NG; ++j)
+                bhv[j] = load_s_or0<DT>(a.b_hh[d], (unsigned)((size_t)NG * H * sizeof(S)),
+                                        (unsigned)(((size_t)j * H + uc) * sizeof(S)));
     };
 
-    // h_{t-1}: rows b0.. of y at the previous step, or of h0 at s = 0
-    const S *hsrc = nullptr;
-    size_t lda = 0;
-    if (s > 0) {
-        const int tp = d == 0 ? s - 1 : T - s;
-        hsrc = static_cast<const S *>(a.Y) + trow(tp, b0, T, B, a.bfirst) * ldy + (size_t)d * H;
-        lda = a.bfirst ? (size_t)T * ldy : ldy;
-    } else if (a.h0) {
-        hsrc = static_cast<const S *>(a.h0) + ((size_t)d * B + b0) * H;
-        lda = H;
-    }
     if (hsrc) {
         const int rows = min(BM, B - b0);
         const unsigned abytes = (unsigned)((((size_t)rows - 1) * lda + H) * es);
@@ -1440,16 +1451,15 @@ __global__ __launch_bounds__(256) void k_rec_step(RecArgs a) {
         const size_t si = ((size_t)d * B + m) * H + u;
         if constexpr (MODE != 0) {
             // hidden contributions with b_hh; h_{t-1} of this cell for the GRU
-            const S *bh = static_cast<const S *>(a.b_hh[d]);
 #pragma unroll
-            for (int j = 0; j < NG; ++j) pre[j] += bh ? DT::to_f(bh[(size_t)j * H + u]) : 0.f;
-            const S hprev = hsrc ? hsrc[(size_t)(m - b0) * lda + u] : (S)0;
+            for (int j = 0; j < NG; ++j) pre[j] += bhv[j];
+            const S hprev = DT::from_f(hpv[vv]);  // exact: an S value widened
             float hv;
             if constexpr (MODE == 1) {
                 const float rg = sigmoid_f(g[0] + pre[0]);
                 const float zg = sigmoid_f(g[1] + pre[1]);
                 const float ng = tanh_f(g[2] + rg * pre[2]);
-                hv = (1.f - zg) * ng + zg * DT::to_f(hprev);
+                hv = (1.f - zg) * ng + zg * hpv[vv];
             } else if constexpr (MODE == 2) {
                 hv = tanh_f(g[0] + pre[0]);
             } else {
