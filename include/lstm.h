@@ -100,7 +100,8 @@ typedef enum {
     /* 6: reserved (no longer accepted) */
     LSTM_OPT_TEAM_ROWS = 7,  /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
     LSTM_OPT_PROJ_TILE = 8,  /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS,
-                                4 / 5 256x256 direct-to-LDS through a ring of 4 / 5 stages */
+                                4 / 5 256x256 direct-to-LDS through a ring of 4 / 5 stages, 6 256x128
+                                through a ring of 3 stages (two workgroups per CU) */
     LSTM_OPT_READ_PACE = 9,  /* 0..100000 ns (default 450): delay between a workgroup finishing step t
                                 (its h_t published) and its first read of the other workgroups' h_t;
                                 0 reads as soon as the step ends. A read that reaches memory before

@@ -1531,15 +1531,19 @@ __global__ void k_fill(unsigned *p, size_t n, unsigned v) {
 // Each 1 KiB load fills 16 rows of 4 segments; segment s of row r sits at
 // r * 4 + (s ^ ((r / 4) % 4)), so 16 consecutive rows reading one segment
 // touch 16 distinct 16-byte bank groups.  The products and the epilogue are
-// those of k_proj_dma.
+// those of k_proj_dma.  With BN = 128 (each wave a 128x64 quadrant) and three
+// stages a workgroup takes 72 KiB of LDS, so two share a CU and one's waits
+// overlap the other's products.
 // ===========================================================================
-template <class DT, int NST>
-__global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
+template <class DT, int NST, int BN>
+__global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_proj_ring(ProjArgs a) {
     using S = typename DT::S;
-    constexpr int BM = 256, BN = 256, SEG = 4;
+    constexpr int BM = 256, SEG = 4;
+    constexpr int NJ = BN / 64;                  // 32-column tiles per wave
     constexpr int KS = SEG * DT::PER16;
     constexpr int STAGE = (BM + BN) * SEG;       // 16-byte segments per stage
     constexpr int LPS = (BM + BN) / 16 / 4;      // 1 KiB loads per wave per stage
+    static_assert((BM + BN) % 64 == 0, "whole loads per wave");
     constexpr unsigned OOR = 0x80000000u;        // past any resource: reads zero
     extern __shared__ __align__(16) unsigned char smem[];
     u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
@@ -1564,26 +1568,25 @@ __global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
     // this lane's slot in each 1 KiB block: row (lane / 4) of the block, swizzled segment (lane % 4)
     const int brow = lane >> 2, pseg = lane & 3;
     auto issue = [&](int kt, int buf) {
-        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+        u32x4 *st = lds + buf * STAGE;
 #pragma unroll
-        for (int i = 0; i < LPS / 2; ++i) {
-            const int blk = w + 4 * i;  // 16 blocks of 16 rows per operand
-            const int row = blk * 16 + brow;
+        for (int i = 0; i < LPS; ++i) {
+            const int blk = w + 4 * i;  // BM/16 blocks of 16 X rows, then BN/16 of W rows
+            const bool isx = blk < BM / 16;
+            const int row = (isx ? blk : blk - BM / 16) * 16 + brow;
             const int lseg = pseg ^ ((row >> 2) & 3);
             const int k = kt * KS + lseg * DT::PER16;
-            const unsigned ox = k < K ? (unsigned)(((size_t)row * a.ldx + k) * es) : OOR;
-            const unsigned ow = k < K ? (unsigned)(((size_t)row * ldw + k) * es) : OOR;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(sa + blk * 64), 16, ox, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(sb + blk * 64), 16, ow, 0, 0, 0);
+            const unsigned off = k < K ? (unsigned)(((size_t)row * (isx ? a.ldx : ldw) + k) * es) : OOR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : rw, (lds_void_t *)(st + blk * 64), 16, off, 0, 0, 0);
         }
     };
     auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 2) & 3)); };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -1606,13 +1609,13 @@ __global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
         const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
-        u32x4 af[2][4], bw[2][4];
-        auto frags = [&](int c, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+        u32x4 af[2][4], bw[2][NJ];
+        auto frags = [&](int c, u32x4 (&fa)[4], u32x4 (&fb)[NJ]) {
             const int sg = 2 * c + (lane >> 5);
 #pragma unroll
             for (int i = 0; i < 4; ++i) fa[i] = sa[swz(wm * 128 + 32 * i + (lane & 31), sg)];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = sb[swz(wn * 128 + 32 * j + (lane & 31), sg)];
+            for (int j = 0; j < NJ; ++j) fb[j] = sb[swz(wn * (BN / 2) + 32 * j + (lane & 31), sg)];
         };
         frags(0, af[0], bw[0]);
         frags(1, af[1], bw[1]);
@@ -1622,15 +1625,15 @@ __global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[c][i], bw[c][j]);
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[c][i], bw[c][j]);
     }
 
     const S *bi = static_cast<const S *>(a.b_ih[d]);
     const S *bh = static_cast<const S *>(a.b_hh[d]);
     const size_t ldg = (size_t)a.D * N;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
         const float bias = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1647,22 +1650,23 @@ __global__ __launch_bounds__(256) void k_proj_ring(ProjArgs a) {
 // ===========================================================================
 static int proj_nsplit(const ProjArgs &a) { return a.kchunk > 0 ? (a.K + a.kchunk - 1) / a.kchunk : 1; }
 
-template <class DT, int NST>
+template <class DT, int NST, int BN>
 static hipError_t launch_proj_ring(const ProjArgs &a, hipStream_t s) {
-    const void *fn = reinterpret_cast<const void *>(&k_proj_ring<DT, NST>);
-    const size_t smem = (size_t)NST * (256 + 256) * 4 * 16;
+    const void *fn = reinterpret_cast<const void *>(&k_proj_ring<DT, NST, BN>);
+    const size_t smem = (size_t)NST * (256 + BN) * 4 * 16;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, a.D * proj_nsplit(a));
-    hipLaunchKernelGGL((k_proj_ring<DT, NST>), grid, dim3(256), smem, s, a);
+    dim3 grid(((a.M + 255) / 256) * ((a.N + BN - 1) / BN), 1, a.D * proj_nsplit(a));
+    hipLaunchKernelGGL((k_proj_ring<DT, NST, BN>), grid, dim3(256), smem, s, a);
     return hipGetLastError();
 }
 
 template <class DT, bool VEC>
 static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, int ring, hipStream_t s) {
     const int zd = a.D * proj_nsplit(a);
-    if (big && dma && VEC && ring == 4) return launch_proj_ring<DT, 4>(a, s);
-    if (big && dma && VEC && ring == 5) return launch_proj_ring<DT, 5>(a, s);
+    if (big && dma && VEC && ring == 4) return launch_proj_ring<DT, 4, 256>(a, s);
+    if (big && dma && VEC && ring == 5) return launch_proj_ring<DT, 5, 256>(a, s);
+    if (big && dma && VEC && ring == 6) return launch_proj_ring<DT, 3, 128>(a, s);
     if (big && dma && VEC) {
         const void *fn = reinterpret_cast<const void *>(&k_proj_dma<DT>);
         const size_t smem = 2 * (256 + 256) * 8 * 16;
@@ -1695,8 +1699,9 @@ static void proj_choose(int M, int N, int K, int ldx, int D, int dtype, int vari
     *dma = *big && vec && variant != 2 && (size_t)256 * ldx * es < (1u << 31) && (size_t)256 * K * es < (1u << 31);
 }
 
-// stages of the direct-to-LDS ring (0: the double-buffered k_proj_dma)
-static int proj_ring(int variant) { return variant == 4 ? 4 : variant == 5 ? 5 : 0; }
+// the direct-to-LDS ring variant: 4 / 5 stages of 256x256 tiles, 6: three
+// stages of 256x128 tiles (0: the double-buffered k_proj_dma)
+static int proj_ring(int variant) { return variant >= 4 && variant <= 6 ? variant : 0; }
 
 int proj_kchunk(int M, int N, int K) {
     const long long tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);

@@ -680,7 +680,7 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             p->team_rows = value;
             return LSTM_OK;
         case LSTM_OPT_PROJ_TILE:
-            if (value < 0 || value > 5) return LSTM_ERR_UNSUPPORTED;
+            if (value < 0 || value > 6) return LSTM_ERR_UNSUPPORTED;
             p->proj_tile = value;
             return LSTM_OK;
         case LSTM_OPT_TIMING:

@@ -184,7 +184,8 @@ def test_lengths_all_full_equal_plain_forward():
 
 
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
-@pytest.mark.parametrize("proj_tile", [1, 2, 3, 4, 5], ids=["proj128", "proj256", "proj256dma", "ring4", "ring5"])
+@pytest.mark.parametrize("proj_tile", [1, 2, 3, 4, 5, 6],
+                         ids=["proj128", "proj256", "proj256dma", "ring4", "ring5", "ring3x128"])
 def test_projection_tiles(spec, proj_tile):
     """Both projection GEMM kernels, forced on shapes with ragged M, N and K."""
     print(f"case {_id(spec)} proj tile {proj_tile}", flush=True)
