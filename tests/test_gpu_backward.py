@@ -83,6 +83,7 @@ def test_backward_matches_oracle(spec):
     dcn_d = torch.from_numpy(dcn).to(dev)
     dx, dh0, dc0, dws = m.backward(x, w, y, reserve, dy_d, h0=h0, c0=c0, dh_n=dhn_d, dc_n=dcn_d)
     torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)  # no hand-over wait gave up
     rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, spec.hidden_size, spec.num_layers,
                                                  spec.bidirectional, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn, dc_n=dcn,
                                                  has_bias=spec.has_bias, bf16=bf)
@@ -173,6 +174,7 @@ def test_dropout_training_matches_oracle(spec, p, seed, call):
     dcn_d = torch.from_numpy(dcn).to(dev)
     dx, dh0, dc0, dws = m.backward(x, w, y, reserve, dy_d, h0=h0, c0=c0, dh_n=dhn_d, dc_n=dcn_d)
     torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)  # no hand-over wait gave up
     rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, H, L, bidir, dy, h0=inp.h0, c0=inp.c0,
                                                  dh_n=dhn, dc_n=dcn, has_bias=spec.has_bias, bf16=bf,
                                                  dropout=(p, seed, call))
@@ -234,6 +236,7 @@ def test_backward_with_lengths_matches_oracle(spec, mode, rec):
     dcn_d = torch.from_numpy(dcn).to(dev)
     dx, dh0, dc0, dws = m.backward(x, w, y, reserve, dy_d, h0=h0, c0=c0, dh_n=dhn_d, dc_n=dcn_d, lengths=lens)
     torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)  # no hand-over wait gave up
     rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, spec.hidden_size, spec.num_layers,
                                                  spec.bidirectional, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn, dc_n=dcn,
                                                  has_bias=spec.has_bias, bf16=bf, lengths=lens)
@@ -273,6 +276,7 @@ def test_dropout_with_lengths_matches_oracle():
     dx, dh0, dc0, dws = m.backward(x, w, y, reserve, torch.from_numpy(dy).to(dev), h0=h0, c0=c0,
                                    dh_n=torch.from_numpy(dhn).to(dev), dc_n=torch.from_numpy(dcn).to(dev), lengths=lens)
     torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)  # no hand-over wait gave up
     rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, H, L, bidir, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn,
                                                  dc_n=dcn, dropout=(p, seed, call), lengths=lens)
     _check(cpu(dx), rdx, "f32", "dx")
@@ -331,6 +335,7 @@ def test_batch_first_training_matches_oracle(spec, mode, p):
     dx, dh0, dc0, dws = m.backward(x, w, y, reserve, dy_d, h0=h0, c0=c0, dh_n=dhn_d,
                                    dc_n=torch.from_numpy(dcn).to(dev), lengths=lens)
     torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)  # no hand-over wait gave up
     rdx, rdh0, rdc0, rdps = oracle.lstm_backward(inp.x, inp.params, H, L, bidir, dy, h0=inp.h0, c0=inp.c0, dh_n=dhn,
                                                  dc_n=dcn, has_bias=spec.has_bias, bf16=bf, dropout=drop,
                                                  lengths=lens)
