@@ -249,6 +249,7 @@ def main():
     ap.add_argument("--rec-tile", type=int, default=0)
     ap.add_argument("--proj-tile", type=int, default=0, help="LSTM_OPT_PROJ_TILE (0 automatic)")
     ap.add_argument("--layer-pipe", action="store_true", help="LSTM_OPT_LAYER_PIPE = 1")
+    ap.add_argument("--read-pace", type=int, default=-1, help="LSTM_OPT_READ_PACE in ns (-1: the default)")
     ap.add_argument("--partial-buffers", type=int, default=0)
     ap.add_argument("--poll-sleep", type=int, default=-1)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
@@ -309,6 +310,8 @@ def main():
         opts[pkg.LSTM_OPT_PROJ_TILE] = args.proj_tile
     if args.layer_pipe:
         opts[pkg.LSTM_OPT_LAYER_PIPE] = 1
+    if args.read_pace >= 0:
+        opts[pkg.LSTM_OPT_READ_PACE] = args.read_pace
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
                  dtype=spec.dtype, recurrence=rec[args.recurrence], rec_tile=args.rec_tile, options=opts,
                  batch_first=args.batch_first, mode=spec.mode)

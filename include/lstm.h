@@ -102,10 +102,11 @@ typedef enum {
     LSTM_OPT_PROJ_TILE = 8,  /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS,
                                 4 / 5 256x256 direct-to-LDS through a ring of 4 / 5 stages, 6 256x128
                                 through a ring of 3 stages (two workgroups per CU) */
-    LSTM_OPT_READ_PACE = 9,  /* 0..100000 ns (default 450): delay between a workgroup finishing step t
-                                (its h_t published) and its first read of the other workgroups' h_t;
-                                0 reads as soon as the step ends. A read that reaches memory before
-                                the data costs a retry round trip; results do not depend on it */
+    LSTM_OPT_READ_PACE = 9,  /* 0..100000 ns (default: 300 to 450 by schedule): delay between a workgroup
+                                finishing step t (its h_t published) and its first read of the other
+                                workgroups' h_t; 0 reads as soon as the step ends. A read that reaches
+                                memory before the data costs a retry round trip; results do not depend
+                                on it */
     LSTM_OPT_LAYER_PIPE = 10, /* 0 (default): layer by layer; 1: a unidirectional stack of 2..4 layers runs
                                 all layers in one pipelined persistent launch when every layer's weights
                                 fit on chip (layer l consumes layer l-1's h_t as it is produced). Changes

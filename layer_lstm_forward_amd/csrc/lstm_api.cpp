@@ -23,7 +23,7 @@ struct lstm_plan {
     int rec_tile;  // 0 = automatic, else 100*WK + 10*MTW + NT
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
-    int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next
+    int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next (-1: by schedule)
     int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
@@ -272,6 +272,19 @@ struct Sched {
     int U, P, BG, NGB, teams, wgs, map_xcd;
     size_t smem;
 };
+
+// The read pace of a persistent schedule (LSTM_OPT_READ_PACE unless set).
+// A read of the others' h_t that reaches memory before the data costs a
+// retry round trip, one that waits too long idles.  Measured optima: 450 ns
+// when one team spans every XCD (P = 256: the latency-bound B = 1 and 4
+// workloads), ~375 ns for 8-unit slices (the fp32 benchmark, 0.991 -> 0.975
+// ms against 450), ~300 ns for 16-unit slices, whose own step is longer (the
+// bidirectional bf16 workload, 1.742 -> 1.674 ms).
+int read_pace_for(const lstm_plan *p, const Sched &s) {
+    if (p->read_pace_ns >= 0) return p->read_pace_ns;
+    if (s.P >= 256) return 450;
+    return s.U >= 16 ? 300 : 375;
+}
 
 struct DevInfo {
     bool ok;
@@ -577,7 +590,7 @@ lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidd
     p->rec_tile = 0;
     p->part_bufs = 1;
     p->poll_sleep = 2;
-    p->read_pace_ns = 450;
+    p->read_pace_ns = -1;
     p->layer_pipe = 0;
     p->fuse_input = 1;
     p->batch_first = 0;
@@ -1027,7 +1040,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         ra.nbatch = sch.geom.nbatch;
         ra.part_bufs = sch.geom.part_bufs;
         ra.poll_sleep = p->poll_sleep;
-        ra.pace = (int)((long long)p->read_pace_ns * di.wall_khz / 1000000);
+        ra.pace = (int)((long long)read_pace_for(p, sch) * di.wall_khz / 1000000);
         ra.map_xcd = sch.map_xcd;
         ra.wreg = sch.geom.wreg;
         ra.vec = (p->H % per16 == 0) && ((uintptr_t)Y % 16 == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
