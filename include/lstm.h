@@ -213,6 +213,29 @@ lstm_status lstm_forward_lengths(lstm_plan *plan, const void *x, const int *leng
                                  int bidir, void *y, void *h_n, float *c_n, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* Packed sequences, the other overload the trace page "Complete Trace:
+ * nn.LSTM" (Step 3) lists: x is [N, input_size] (dtype), the rows of step t
+ * being rows o_t .. o_t + batch_sizes[t] - 1 with o_t = the sum of the
+ * earlier batch_sizes, one per sequence still running at t; sequences are in
+ * order of non-increasing length, so batch_sizes is non-increasing.
+ *   batch_sizes  HOST array of T int32 values, batch_sizes[0] = B (the
+ *                number of sequences) >= batch_sizes[1] >= ... >= 1;
+ *                N = their sum.  Read before the call returns.
+ *   y            [N, D*H] dtype, packed like x
+ *   h_n, c_n     [L*D, B, H] as lstm_forward, rows in the packed sequence
+ *                order (h0 and c0 likewise)
+ *   workspace    at least lstm_packed_workspace_size bytes
+ * The result equals lstm_forward_lengths on the padded [T, B, .] layout with
+ * lengths[b] = the number of steps t with batch_sizes[t] > b: the rows are
+ * gathered into a zero-padded buffer in the workspace, that forward runs, and
+ * y is scattered back.  A NULL batch_sizes, an increasing or a non-positive
+ * entry is LSTM_ERR_ARG; a plan with LSTM_OPT_BATCH_FIRST set is
+ * LSTM_ERR_UNSUPPORTED; other errors as lstm_forward_lengths. */
+lstm_status lstm_packed_workspace_size(const lstm_plan *plan, const int *batch_sizes, int T, size_t *bytes);
+lstm_status lstm_forward_packed(lstm_plan *plan, const void *x, const int *batch_sizes, int T, const void *h0,
+                                const float *c0, const void *const *weights, int layers, int bidir, void *y,
+                                void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ training
  * Backward pass (backpropagation through time).  The trace page "Complete
  * Trace: nn.LSTM" ("cuDNN Backward") computes the gradients of the input, of

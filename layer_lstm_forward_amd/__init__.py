@@ -72,6 +72,11 @@ def load_library():
     lib.lstm_forward_lengths.restype = i
     lib.lstm_forward_lengths.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int), vp, vp, ctypes.POINTER(vp),
                                          i, i, i, i, vp, vp, vp, vp, sz, vp]
+    lib.lstm_packed_workspace_size.restype = i
+    lib.lstm_packed_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_int), i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lstm_forward_packed.restype = i
+    lib.lstm_forward_packed.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int), i, vp, vp, ctypes.POINTER(vp), i, i,
+                                        vp, vp, vp, vp, sz, vp]
     for fn in ("lstm_reserve_size", "lstm_backward_workspace_size"):
         getattr(lib, fn).restype = i
         getattr(lib, fn).argtypes = [vp, i, i, ctypes.POINTER(sz)]
@@ -179,6 +184,33 @@ def lstm_forward_lengths(plan, x, lengths, h0, c0, weights, T, B, layers, bidir,
     return int(load_library().lstm_forward_lengths(
         ctypes.c_void_p(plan), ctypes.c_void_p(x), lens, ctypes.c_void_p(h0 or None), ctypes.c_void_p(c0 or None),
         arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
+        ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
+        int(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def _int_array(values):
+    return None if values is None else (ctypes.c_int * len(values))(*[int(v) for v in values])
+
+
+def lstm_packed_workspace_size(plan, batch_sizes) -> int:
+    """Workspace bytes of lstm_forward_packed for these batch_sizes (host ints)."""
+    n = ctypes.c_size_t()
+    rc = load_library().lstm_packed_workspace_size(ctypes.c_void_p(plan), _int_array(batch_sizes),
+                                                   len(batch_sizes) if batch_sizes is not None else 0,
+                                                   ctypes.byref(n))
+    if rc:
+        raise LSTMError(rc, "lstm_packed_workspace_size")
+    return int(n.value)
+
+
+def lstm_forward_packed(plan, x, batch_sizes, h0, c0, weights, layers, bidir, y, h_n, c_n, workspace,
+                        workspace_bytes, stream, T=None) -> int:
+    """Raw call on packed rows (batch_sizes: a host sequence of T ints); returns the status."""
+    arr = (ctypes.c_void_p * len(weights))(*[int(w) for w in weights])
+    T = len(batch_sizes) if T is None else T
+    return int(load_library().lstm_forward_packed(
+        ctypes.c_void_p(plan), ctypes.c_void_p(x), _int_array(batch_sizes), int(T), ctypes.c_void_p(h0 or None),
+        ctypes.c_void_p(c0 or None), arr, int(layers), int(bool(bidir)), ctypes.c_void_p(y),
         ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
         int(workspace_bytes), ctypes.c_void_p(stream or None)))
 
@@ -343,6 +375,32 @@ class LSTM:
             rc = lstm_forward_lengths(self.plan, x.data_ptr(), [int(v) for v in lengths], *args)
         if rc:
             raise LSTMError(rc, "lstm_forward_lengths" if lengths is not None else "lstm_forward")
+        return y, hn, cn
+
+    def forward_packed(self, x, batch_sizes, weights, h0=None, c0=None, stream=None):
+        """Packed sequences: x [N, input_size] with the rows of step t after those of
+        the earlier steps, batch_sizes the T host ints (non-increasing).  Returns
+        (y [N, D*H], h_n, c_n) with h_n, c_n rows in the packed sequence order."""
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if not x.is_cuda or x.dtype != tdt or not x.is_contiguous() or x.dim() != 2:
+            raise ValueError("x must be a contiguous [N, input_size] device tensor of the plan's dtype")
+        bs = [int(v) for v in batch_sizes]
+        B, H, L, D = bs[0], self.hidden_size, self.num_layers, self.D
+        y = torch.empty(x.shape[0], D * H, dtype=tdt, device=x.device)
+        hn = torch.empty(L * D, B, H, dtype=tdt, device=x.device)
+        cn = torch.empty(L * D, B, H, dtype=torch.float32, device=x.device) if self.mode == "lstm" else None
+        nbytes = lstm_packed_workspace_size(self.plan, bs)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lstm_forward_packed(self.plan, x.data_ptr(), bs, h0.data_ptr() if h0 is not None else 0,
+                                 c0.data_ptr() if c0 is not None else 0, [w.data_ptr() for w in weights], L,
+                                 self.bidirectional, y.data_ptr(), hn.data_ptr(),
+                                 cn.data_ptr() if cn is not None else 0, ws.data_ptr(), nbytes, stream)
+        if rc:
+            raise LSTMError(rc, "lstm_forward_packed")
+        self._pws = ws  # kept until the next call: the stream may still be using it
         return y, hn, cn
 
     def forward_train(self, x, weights, h0=None, c0=None, stream=None, lengths=None):

@@ -12,7 +12,7 @@ LIB = os.path.join(PKG, "liblstm_amd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["lstm_api.cpp", "kernels.hip", "backward.hip"]
+SOURCES = ["lstm_api.cpp", "kernels.hip", "backward.hip", "pack.hip"]
 # Packed-fp32 VALU ops stay off: the device code uses plain fp32 arithmetic.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

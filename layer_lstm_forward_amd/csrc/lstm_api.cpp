@@ -14,6 +14,7 @@
 
 #include "../../include/lstm.h"
 #include "kernels.h"
+#include "pack.h"
 
 using namespace lstm_amd;
 
@@ -545,7 +546,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 108; }
+int lstm_version(void) { return 109; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -1561,6 +1562,95 @@ lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths
     }
     return forward_impl(p, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
                         workspace_bytes, stream);
+}
+
+// Packed sequences: the padded buffers and the row map after the forward's
+// own workspace.  batch_sizes as documented in lstm.h.
+struct PackLayout {
+    size_t fwd, xpad, ypad, map, total;
+    int B;
+    size_t N;
+};
+
+static lstm_status pack_layout(const lstm_plan *p, const int *batch_sizes, int T, PackLayout *o) {
+    if (!p || !batch_sizes) return LSTM_ERR_ARG;
+    if (T < 1) return LSTM_ERR_SHAPE;
+    if (batch_sizes[0] < 1) return LSTM_ERR_ARG;
+    size_t n = 0;
+    for (int t = 0; t < T; ++t) {
+        if (batch_sizes[t] < 1 || (t > 0 && batch_sizes[t] > batch_sizes[t - 1])) return LSTM_ERR_ARG;
+        n += (size_t)batch_sizes[t];
+    }
+    if (n > (size_t)INT_MAX) return LSTM_ERR_SHAPE;
+    o->B = batch_sizes[0];
+    o->N = n;
+    size_t fwd = 0;
+    const lstm_status rc = lstm_workspace_size(p, T, o->B, &fwd);
+    if (rc != LSTM_OK) return rc;
+    const size_t es = elem_size(p->dtype), rows = (size_t)T * o->B;
+    size_t xb, yb;
+    if (!mul_ok(rows, (size_t)p->I * es, &xb) || !mul_ok(rows, (size_t)p->D * p->H * es, &yb)) return LSTM_ERR_SHAPE;
+    o->fwd = fwd;
+    o->xpad = align_up(fwd);
+    o->ypad = o->xpad + align_up(xb);
+    o->map = o->ypad + align_up(yb);
+    o->total = o->map + align_up(n * sizeof(int));
+    return LSTM_OK;
+}
+
+lstm_status lstm_packed_workspace_size(const lstm_plan *p, const int *batch_sizes, int T, size_t *bytes) {
+    if (!bytes) return LSTM_ERR_ARG;
+    PackLayout pl{};
+    const lstm_status rc = pack_layout(p, batch_sizes, T, &pl);
+    if (rc != LSTM_OK) return rc;
+    *bytes = pl.total;
+    return LSTM_OK;
+}
+
+lstm_status lstm_forward_packed(lstm_plan *p, const void *x, const int *batch_sizes, int T, const void *h0,
+                                const float *c0, const void *const *weights, int layers, int bidir, void *y,
+                                void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
+    PackLayout pl{};
+    lstm_status rc = pack_layout(p, batch_sizes, T, &pl);
+    if (rc != LSTM_OK) return rc;
+    if (!x || !y || !workspace) return LSTM_ERR_ARG;
+    if (p->batch_first) return LSTM_ERR_UNSUPPORTED;  // the packed layout is time-major
+    if (workspace_bytes < pl.total) return LSTM_ERR_WORKSPACE;
+    const int B = pl.B;
+    // row length of each sequence, and the padded row (t*B + b) of every packed row
+    std::vector<int> lengths((size_t)B, 0), map(pl.N);
+    size_t r = 0;
+    for (int t = 0; t < T; ++t)
+        for (int b = 0; b < batch_sizes[t]; ++b) {
+            lengths[(size_t)b] = t + 1;
+            map[r++] = t * B + b;
+        }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_DEVICE;
+    }
+    if (!is_device_ptr(x, dev) || !is_device_ptr(y, dev) || !is_device_ptr(workspace, dev)) return LSTM_ERR_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    int *dmap = reinterpret_cast<int *>(ws + pl.map);
+    const size_t es = elem_size(p->dtype);
+    const size_t xrow = (size_t)p->I * es, yrow = (size_t)p->D * p->H * es;
+    const size_t xwords = (pl.ypad - pl.xpad) / sizeof(unsigned);  // the padded x region, 256-byte aligned
+    if (hipMemcpyAsync(dmap, map.data(), pl.N * sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess ||
+        launch_fill_u32(reinterpret_cast<unsigned *>(ws + pl.xpad), xwords, 0u, st) != hipSuccess ||
+        launch_copy_rows(x, ws + pl.xpad, dmap, (int)pl.N, xrow, true, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
+    rc = lstm_forward_lengths(p, ws + pl.xpad, lengths.data(), h0, c0, weights, T, B, layers, bidir, ws + pl.ypad,
+                              h_n, c_n, workspace, pl.fwd, stream);
+    if (rc != LSTM_OK) return rc;
+    if (launch_copy_rows(ws + pl.ypad, y, dmap, (int)pl.N, yrow, false, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSTM_ERR_LAUNCH;
+    }
+    return LSTM_OK;
 }
 
 lstm_status lstm_device_status(const void *workspace, size_t workspace_bytes, void *stream,

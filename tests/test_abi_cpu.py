@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 108
+    assert pkg.lstm_version() == 109
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
@@ -281,3 +281,30 @@ def test_backward_rejects_steps_past_32_bit_offsets():
         assert pkg.lstm_backward(p, FAKE, **dict(bargs, B=0)) == -2
     finally:
         pkg.lstm_destroy(p)
+
+
+def test_packed_batch_sizes_validated_on_the_host():
+    # batch_sizes must be non-increasing and positive (B = batch_sizes[0]);
+    # checked before any device access
+    FAKE = 0x10000
+    p = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        n = pkg.lstm_packed_workspace_size(p, [3, 2, 2, 1])
+        assert n >= pkg.lstm_workspace_size(p, 4, 3)
+        for bad in ([2, 3], [3, 0], [0], [3, -1, 1]):
+            with pytest.raises(pkg.LSTMError):
+                pkg.lstm_packed_workspace_size(p, bad)
+            assert pkg.lstm_forward_packed(p, FAKE, bad, 0, 0, [FAKE] * 4, 1, False, FAKE, 0, 0, FAKE, 1 << 40,
+                                           0) == -1
+        assert pkg.lstm_forward_packed(p, FAKE, None, 0, 0, [FAKE] * 4, 1, False, FAKE, 0, 0, FAKE, 1 << 40, 0,
+                                       T=2) == -1
+        assert pkg.lstm_forward_packed(p, FAKE, [3, 2], 0, 0, [FAKE] * 4, 1, False, FAKE, 0, 0, FAKE, 16, 0) == -5
+    finally:
+        pkg.lstm_destroy(p)
+    q = pkg.lstm_create(8, 16, 1, False, True, pkg.LSTM_F32)
+    try:
+        pkg.lstm_set_option(q, pkg.LSTM_OPT_BATCH_FIRST, 1)  # raises on failure
+        assert pkg.lstm_forward_packed(q, FAKE, [2, 1], 0, 0, [FAKE] * 4, 1, False, FAKE, 0, 0, FAKE, 1 << 40,
+                                       0) == -7
+    finally:
+        pkg.lstm_destroy(q)
