@@ -266,7 +266,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the forward pass has no cross-GPU "
+        print("bench.py: the benchmark runs on exactly one GPU (the forward pass has no cross-GPU "
               "component here); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
