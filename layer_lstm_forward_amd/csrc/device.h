@@ -131,17 +131,26 @@ __device__ inline u32x4 xload2(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
 
 // ---------------------------------------------------------------------------
 // Compact exchange words (the per-layer recurrence).  A 32-bit word carries
-// the value and a one-bit tag, stored with an agent-scope atomic 32-bit store
-// and read (four words at a time) with the 16-byte sc1 load above; each word
-// is a single-copy atomic unit.  Where the tag lives:
-//   fp32: the least significant mantissa bit.  The value a consumer
-//         multiplies is h or its fp32 neighbour (at most 1 ulp away); NaN
-//         stays NaN.
-//   bf16: bit 30, the top exponent bit of the upper of the two bf16 values.
-//         h = o tanh(c) has |h| <= 1, whose biased exponent is at most 127,
-//         so that bit is always clear in the value itself.  A non-finite h
-//         is sent as a NaN in the lower half (the whole batch row becomes
-//         NaN at the next step either way, as it would with the true value).
+// the value and a one-bit step tag, stored with an agent-scope atomic 32-bit
+// store and read (four words at a time) with the 16-byte sc1 load above; each
+// word is a single-copy atomic unit.  Three word formats:
+//   fp32:      one value; the tag is the least significant mantissa bit.  The
+//              value a consumer multiplies is h or its fp32 neighbour (at most
+//              1 ulp away); NaN stays NaN.  Any h.
+//   bf16 pair: two bf16 values of adjacent units (low half: the even unit);
+//              the tag is bit 30, the top exponent bit of the upper value.
+//              That bit is clear in the value itself only while |h| < 2 (a
+//              bf16 of magnitude >= 2 has a biased exponent >= 128), so this
+//              format is only for values bounded by 1: the LSTM's o tanh(c)
+//              and the tanh RNN's output.  A non-finite h is sent as a NaN in
+//              the lower half (the batch row becomes NaN at the next step
+//              either way, as it would with the true value).
+//   bf16 wide: one bf16 value in the upper half, the tag in bit 0 (the word
+//              is the value's exact fp32 form plus the tag in a bit that is
+//              zero in every bf16).  Any h, at twice the bytes of the pair
+//              format: used wherever a published h may reach 2 in magnitude
+//              (the relu RNN, the GRU started from a caller's h0, and padded
+//              steps that republish a caller's h0).
 // One bit suffices because each location is written once every two steps
 // and each consumer lane always reads the same locations: the value it last
 // accepted there was the previous write, and read-read coherence of a
@@ -149,9 +158,27 @@ __device__ inline u32x4 xload2(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
 // values it can observe are the previous write (tag differs) or the current
 // one.  The host keeps the tag sequence continuous across the layers of a
 // call (the buffer is zeroed once per call, and a zero word carries tag 0).
+// The word functions are host-callable so that the formats can be checked on
+// the CPU.
 // ---------------------------------------------------------------------------
-template <bool BF>
-__device__ inline unsigned xc_shift() { return BF ? 30u : 0u; }
+enum XFmt { XF_F32 = 0, XF_PAIR = 1, XF_WIDE = 2 };
+// bit position of the tag in a word of format f
+__host__ __device__ constexpr unsigned xc_shift(int f) { return f == XF_PAIR ? 30u : 0u; }
+__host__ __device__ inline uint32_t xc_word_f32(uint32_t hbits, unsigned tb) { return (hbits & ~1u) | tb; }
+__host__ __device__ inline uint32_t xc_word_pair(uint16_t lo, uint16_t hi, unsigned tb) {
+    const bool nonfinite = ((lo & 0x7F80u) == 0x7F80u) || ((hi & 0x7F80u) == 0x7F80u);
+    const uint32_t payload = nonfinite ? 0x7FC0u : ((uint32_t)lo | ((uint32_t)hi << 16));
+    return payload | (tb << 30);
+}
+__host__ __device__ inline uint32_t xc_word_wide(uint16_t h, unsigned tb) { return ((uint32_t)h << 16) | tb; }
+// the tag bit a word of format f carries
+__host__ __device__ inline unsigned xc_word_tag(uint32_t w, int f) { return (w >> xc_shift(f)) & 1u; }
+// the value bits of a pair word with its tag removed (two bf16)
+__host__ __device__ inline uint32_t xc_pair_value(uint32_t w) { return w & 0xBFFFFFFFu; }
+// two wide words (values e and e + 1) as one bf16 pair, value e in the low half
+__host__ __device__ inline uint32_t xc_wide_pair(uint32_t w0, uint32_t w1) {
+    return (w0 >> 16) | (w1 & 0xFFFF0000u);
+}
 __device__ inline void xcstore(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -159,14 +186,14 @@ __device__ inline __amdgpu_buffer_rsrc_t xcrsrc(const uint32_t *base, unsigned b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(base), (short)0, (int)bytes, 0x00020000);
 }
 // tag bit of the write made at step s into buffer s & 1
-__device__ inline unsigned xc_tag(unsigned xpar, int s) {
+__host__ __device__ inline unsigned xc_tag(unsigned xpar, int s) {
     return (((xpar >> (s & 1)) & 1u) + ((unsigned)s >> 1) + 1u) & 1u;
 }
 // all four words of a 16-byte load carry tag bit tb
-template <bool BF>
-__device__ inline bool xc_ok(const u32x4 &w, unsigned tb) {
+template <int F>
+__host__ __device__ inline bool xc_ok(const u32x4 &w, unsigned tb) {
     const unsigned all = w.x & w.y & w.z & w.w, any = w.x | w.y | w.z | w.w;
-    return ((tb ? all : ~any) >> xc_shift<BF>()) & 1u;
+    return ((tb ? all : ~any) >> xc_shift(F)) & 1u;
 }
 
 // The float at byte offset off of a buffer of nbytes bytes, through a buffer

@@ -40,8 +40,9 @@ struct RecArgs {
     const int *len;          // [B] valid steps per batch row, or NULL (all T)
     int bfirst;              // x, G, y rows are (b, t) = b*T + t instead of t*B + b
     float *acts;             // training: [T, B, D, 5, H] gates i, f, g, o and c of every step, or NULL
-    unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 32-bit words
+    unsigned long long *xbuf;  // h exchange: [2][D][NGB] regions of (ROWS/16)*kch*256 32-bit words (twice that when xwide)
     unsigned xpar;           // bit p: parity of the writes buffer p received before this launch
+    int xwide;               // bf16: one value per exchange word (any h), else pairs (|h| < 2 only)
     unsigned *status;        // error word
     int T, B, H, D;
     int P;                   // workgroups per team (hidden-unit slices)
@@ -140,9 +141,15 @@ bool pipe_tile_supported(RecTile t);
 RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch);
 hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
 hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s);
-hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, int *blocks_per_cu);
+hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, bool wide,
+                              int *blocks_per_cu);
 // input chunks per wave of the tile's fused-projection variant (0: none)
 int rec_fused_chunks(RecTile t);
+// The k_rec instance for tile t (rec_f32.hip, rec_bf16.hip, rec_bf16_wide.hip):
+// W_hh in registers or LDS, fused or hoisted projection; nullptr if none.
+const void *rec_kernel_f32(RecTile t, bool wreg, bool fused);
+const void *rec_kernel_bf16(RecTile t, bool wreg, bool fused);
+const void *rec_kernel_bf16_wide(RecTile t, bool wreg, bool fused);
 // ----------------------------------------------------------------- backward
 // One backward step (sb = 0 is the last step of each direction's scan) of one
 // layer, all directions.

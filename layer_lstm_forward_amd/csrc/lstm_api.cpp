@@ -55,7 +55,7 @@ constexpr size_t kAlign = 256;
 constexpr size_t kStatusBytes = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-bool use_persistent_for_mode(const lstm_plan *p, int B);
+bool use_persistent_for_mode(const lstm_plan *p, int B, bool wide);
 size_t elem_size(int dtype) { return dtype == LSTM_BF16 ? 2 : 4; }
 
 // Checked products; false on size_t overflow.
@@ -268,6 +268,7 @@ bool make_bwd_layout(const lstm_plan *p, int T, int B, BwdLayout *o) {
 // ---------------------------------------------------------------- schedule
 struct Sched {
     bool persistent;
+    bool wide;  // bf16 exchange in wide words (one value per word)
     RecTile tile;
     RecGeom geom;
     int U, P, BG, NGB, teams, wgs, map_xcd;
@@ -330,7 +331,23 @@ bool fill_sched(const lstm_plan *p, int B, RecTile t, Sched *s) {
     s->geom = rec_geom(t, p->H, p->dtype, p->part_bufs == 2);
     s->smem = s->geom.smem;
     s->map_xcd = (s->teams <= 8 && 8 % s->teams == 0 && (s->wgs % 8) == 0) ? 1 : 0;
-    return s->teams <= kMaxTeams && s->smem <= kRecLdsLimit;
+    // the exchange buffer (make_layout) holds (B + 255) / 16 + 1 row tiles of
+    // 8-byte words per direction and parity, i.e. that many tiles of wide
+    // words: the teams' padded row tiles must fit (a small LSTM_OPT_TEAM_ROWS
+    // makes many teams of mostly padding rows)
+    const bool fits_xbuf = (size_t)s->NGB * (rows / 16) <= ((size_t)B + 255) / 16 + 1;
+    return fits_xbuf && s->teams <= kMaxTeams && s->smem <= kRecLdsLimit;
+}
+
+// bf16 recurrences whose exchanged h may reach 2 in magnitude take the wide
+// exchange words: the relu RNN (unbounded), the GRU from a caller's h0 (h
+// moves from h0 towards values in [-1, 1] without a bound of 1), and per-row
+// lengths with a caller's h0 (the reverse scan republishes h0 on its leading
+// padded steps).  The LSTM's o tanh(c) and the tanh RNN's output are bounded
+// by 1 otherwise.
+bool needs_wide_exchange(const lstm_plan *p, bool have_h0, bool have_lengths) {
+    if (p->dtype != LSTM_BF16) return false;
+    return p->mode == LSTM_MODE_RNN_RELU || (have_h0 && (p->mode == LSTM_MODE_GRU || have_lengths));
 }
 
 // Rough cycles per step of one workgroup: matrix-core work of the busiest
@@ -374,13 +391,13 @@ int fused_chunks(const lstm_plan *p, const Sched &s, int T, int B, int in_l, con
     for (int d = 0; d < p->D; ++d)
         if ((uintptr_t)wih[d] % 16 != 0) return 0;
     int bpc = 0;
-    const bool fits = rec_max_coresident(s.tile, s.smem, p->dtype, true, true, &bpc) == hipSuccess && bpc > 0 &&
+    const bool fits = rec_max_coresident(s.tile, s.smem, p->dtype, true, true, s.wide, &bpc) == hipSuccess && bpc > 0 &&
                       (long long)bpc * di.cus >= s.wgs;
     (void)hipGetLastError();
     return fits ? ncx : 0;
 }
 
-int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
+int choose_sched(const lstm_plan *p, int B, int dev, Sched *out, bool wide) {
     const DevInfo di = dev_info(dev);
     Sched best{};
     double best_cost = 1e300;
@@ -390,10 +407,11 @@ int choose_sched(const lstm_plan *p, int B, int dev, Sched *out) {
         if (p->rec_tile && p->rec_tile != 100 * t.WK + 10 * t.MTW + t.NT) continue;
         Sched s{};
         if (!fill_sched(p, B, t, &s)) continue;
+        s.wide = wide;
         bool can_persist = false;
         if (!want_step && di.ok) {
             int bpc = 0;
-            if (rec_max_coresident(t, s.smem, p->dtype, s.geom.wreg != 0, false, &bpc) == hipSuccess && bpc > 0)
+            if (rec_max_coresident(t, s.smem, p->dtype, s.geom.wreg != 0, false, wide, &bpc) == hipSuccess && bpc > 0)
                 can_persist = (long long)bpc * di.cus >= s.wgs;
             (void)hipGetLastError();
         }
@@ -731,7 +749,9 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     const int in0 = p->I > p->D * p->H ? p->I : p->D * p->H;  // widest layer input
     const char *dt = p->dtype == LSTM_BF16 ? "bf16" : "f32";
     static const char *names[] = {"lstm", "gru", "rnn_tanh", "rnn_relu"};
-    const bool mode_persistent = p->mode != LSTM_MODE_LSTM && use_persistent_for_mode(p, B);
+    // (describes a call without h0 or lengths)
+    const bool wide = needs_wide_exchange(p, false, false);
+    const bool mode_persistent = p->mode != LSTM_MODE_LSTM && use_persistent_for_mode(p, B, wide);
     if (p->mode != LSTM_MODE_LSTM && !mode_persistent) {
         const int bm = rec_step_rows(B);
         std::snprintf(buf, len,
@@ -741,7 +761,7 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
         return LSTM_OK;
     }
     Sched s{};
-    const int rc = choose_sched(p, B, dev, &s);
+    const int rc = choose_sched(p, B, dev, &s, wide);
     if (rc != LSTM_OK) return (lstm_status)rc;
     const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
     PipeSched ps{};
@@ -775,10 +795,11 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     if (mode_persistent) std::snprintf(cell, sizeof(cell), "cell=%s gate_slots=4 ", names[p->mode]);
     std::snprintf(buf, len,
                   "%sproj=%s<%s>; rec=k_rec<%s,WK=%d,MTW=%d,NT=%d> mode=%s U=%d P=%d BG=%d "
-                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s%s",
+                  "NGB=%d teams=%d workgroups=%d lds=%zu partial_bufs=%d map_xcd=%d w_hh=%s xproj=%s xwords=%s%s",
                   cell, proj, dt, dt, s.tile.WK, s.tile.MTW, s.tile.NT, s.persistent ? "persistent" : "step", s.U, s.P,
                   s.BG, s.NGB, s.teams, s.wgs, s.smem, s.geom.part_bufs, s.map_xcd, s.geom.wreg ? "regs" : "lds",
-                  xproj, p->batch_first ? " layout=batch-first" : "");
+                  xproj, p->dtype != LSTM_BF16 ? "f32" : s.wide ? "wide" : "pair",
+                  p->batch_first ? " layout=batch-first" : "");
     return LSTM_OK;
 }
 
@@ -811,7 +832,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         if (!is_device_ptr(weights[i], dev)) return LSTM_ERR_DEVICE;
 
     Sched sch{};
-    rc = choose_sched(p, B, dev, &sch);
+    rc = choose_sched(p, B, dev, &sch, needs_wide_exchange(p, h0 != nullptr, lengths_h != nullptr));
     if (rc != LSTM_OK) return (lstm_status)rc;
     const DevInfo di = dev_info(dev);
 
@@ -1028,6 +1049,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         ra.acts = reserve ? reinterpret_cast<float *>(reserve + rl.acts_layer * l) : nullptr;
         ra.xbuf = xbuf;
         ra.xpar = xpar;
+        ra.xwide = sch.wide ? 1 : 0;
         ra.status = status;
         ra.T = T;
         ra.B = B;
@@ -1114,7 +1136,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
 // The GRU and the RNNs take the persistent recurrence when its schedule
 // applies (unless the caller asked for stepping) and the per-step GEMM kernel
 // otherwise.
-bool use_persistent_for_mode(const lstm_plan *p, int B) {
+bool use_persistent_for_mode(const lstm_plan *p, int B, bool wide) {
     if (p->rec_mode == LSTM_REC_STEP || p->rec_mode == LSTM_REC_GEMM || B < 1) return false;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -1122,7 +1144,7 @@ bool use_persistent_for_mode(const lstm_plan *p, int B) {
         return false;
     }
     Sched s{};
-    return choose_sched(p, B, dev, &s) == LSTM_OK && s.persistent;
+    return choose_sched(p, B, dev, &s, wide) == LSTM_OK && s.persistent;
 }
 
 // The forward pass of the GRU and the plain RNNs: per layer the hoisted
@@ -1231,7 +1253,7 @@ lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const floa
     if (p && p->mode != LSTM_MODE_LSTM) {
         if (c0 || c_n) return LSTM_ERR_ARG;  // no cell state
         // the persistent kernel on padded gate slots where the schedule allows, else one launch per step
-        if (use_persistent_for_mode(p, B))
+        if (use_persistent_for_mode(p, B, needs_wide_exchange(p, h0 != nullptr, false)))
             return forward_impl(p, x, nullptr, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
                                 workspace, workspace_bytes, stream);
         return forward_modes(p, x, nullptr, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
@@ -1554,7 +1576,7 @@ lstm_status lstm_forward_lengths(lstm_plan *p, const void *x, const int *lengths
         if (lengths[b] < 1 || lengths[b] > T) return LSTM_ERR_ARG;
     if (p && p->mode != LSTM_MODE_LSTM) {
         if (c0 || c_n) return LSTM_ERR_ARG;  // no cell state
-        if (use_persistent_for_mode(p, B))
+        if (use_persistent_for_mode(p, B, needs_wide_exchange(p, h0 != nullptr, true)))
             return forward_impl(p, x, lengths, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
                                 workspace, workspace_bytes, stream);
         return forward_modes(p, x, lengths, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,

@@ -43,6 +43,8 @@ def _run(spec, inp, batch_first=False, path="auto", lengths=None):
     h0 = to_dev(inp.h0, bf, dev)
     y, hn, cn = m.forward(x, w, h0, lengths=lengths)
     torch.cuda.synchronize()
+    rc, flags = m.device_status()
+    assert rc == 0 and flags == 0, f"device status {rc} flags {flags}: {desc}"
     assert cn is None
     y = y.float().cpu().numpy().astype(np.float64)
     if batch_first:
@@ -146,6 +148,53 @@ def test_mode_full_size_lengths_sampled_rows(mode, path):
                                  lengths=lengths[rows])
     _check(y[:, rows], ry, "f32", "y")
     _check(hn[:, rows], rhn, "f32", "h_n")
+
+
+def _scaled(a, factor, bf):
+    """a * factor as the same storage type (bf16 bits rounded once, like every input)."""
+    from layer_lstm_forward_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+    if a is None:
+        return None
+    if bf:
+        return f32_to_bf16_bits(bf16_bits_to_f32(a) * np.float32(factor))
+    return (a * np.float32(factor)).astype(np.float32)
+
+
+LARGE_H = [  # mode, weight factor, h0 factor, lengths, bidirectional
+    ("rnn_relu", 4.0, 1.0, None, True),       # relu outputs well above 2 from the first step
+    ("rnn_relu", 4.0, 40.0, "ragged", True),  # ... with lengths and a large h0
+    ("gru", 1.0, 40.0, None, True),           # h moves from |h0| ~ 4 towards [-1, 1]
+    ("gru", 1.0, 40.0, "ragged", False),
+    ("rnn_tanh", 1.0, 40.0, "ragged", True),  # the reverse scan republishes h0 on padded steps
+]
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("case", LARGE_H, ids=lambda c: f"{c[0]}-w{c[1]:g}-h0x{c[2]:g}-{c[3] or 'full'}-D{2 if c[4] else 1}")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mode_large_h_exchange(case, path, dtype):
+    """Hidden states of magnitude 2 and more pass between the workgroups of
+    the persistent recurrence intact (bf16: the wide exchange words), with
+    every wait ending (device status clean), against the oracle."""
+    from layer_lstm_forward_amd.synth import make_lengths
+    mode, wf, hf, lmix, bidir = case
+    spec = Spec(32, 64, 2, bidir, 6, 20, dtype, 980, "normal0.1", mode=mode)
+    print(f"case large h {case} {path} {dtype}", flush=True)
+    inp = make_inputs(spec)
+    bf = dtype == "bf16"
+    inp.params = [_scaled(p, wf, bf) for p in inp.params]
+    inp.h0 = _scaled(inp.h0, hf, bf)
+    lengths = None if lmix is None else make_lengths(spec, lmix)
+    y, hn = _run(spec, inp, path=path, lengths=lengths)
+    ry, rhn = oracle.rnn_forward(mode, inp.x, inp.params, 64, 2, bidir, h0=inp.h0, bf16=bf,
+                                 nthreads=oracle_threads(), lengths=lengths)
+    # the case reaches the range it is about: in the outputs, or in the h0
+    # that padded steps republish (their outputs are zeros)
+    from layer_lstm_forward_amd.synth import bf16_bits_to_f32
+    h0 = bf16_bits_to_f32(inp.h0) if bf else inp.h0
+    assert max(np.max(np.abs(ry)), np.max(np.abs(rhn)), np.max(np.abs(h0)) if hf > 1 else 0.0) >= 2.0
+    _check(y, ry, dtype, "y")
+    _check(hn, rhn, dtype, "h_n")
 
 
 def test_mode_rejects_cell_state():

@@ -174,6 +174,100 @@ def test_batch_first(spec, mode, with_lengths):
     assert_parity(got, ref, spec.dtype, f"batch_first {mode}: {m.describe(spec.T, spec.B)}")
 
 
+def _scaled(a, factor, bf):
+    """a * factor in the same storage type (bf16 bits rounded once, like every input)."""
+    from layer_lstm_forward_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+    if a is None:
+        return None
+    if bf:
+        return f32_to_bf16_bits(bf16_bits_to_f32(a) * np.float32(factor))
+    return (a * np.float32(factor)).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", sorted(LENGTH_MODES))
+def test_lengths_large_h0(dtype, mode):
+    """Per-row lengths with a caller's h0 of magnitude up to ~10 (N(0, 0.1) x
+    40): the reverse scan republishes h0 on its leading padded steps, so
+    values of magnitude 2 and more pass between workgroups (bf16: the wide
+    exchange words).  Every wait ends and the outputs match the oracle."""
+    from layer_lstm_forward_amd.synth import make_lengths
+    spec = Spec(40, 64, 2, True, 9, 20, dtype, 710, "normal0.1")
+    print(f"case lengths large h0 {dtype} {mode}", flush=True)
+    inp = make_inputs(spec)
+    bf = dtype == "bf16"
+    inp.h0 = _scaled(inp.h0, 40.0, bf)
+    lengths = make_lengths(spec, "ragged")
+    lengths[0] = 1
+    rec, opts = LENGTH_MODES[mode]
+    got, m = run_gpu(inp, recurrence=rec, options=opts, lengths=lengths)
+    ref = run_oracle(inp, lengths=lengths)
+    # the reverse scan of a row shorter than T republishes h0 on its padded
+    # steps and multiplies it at its first valid step: h0 reaches the range
+    from layer_lstm_forward_amd.synth import bf16_bits_to_f32
+    assert np.max(np.abs(bf16_bits_to_f32(inp.h0) if bf else inp.h0)) >= 2.0 and min(lengths) < spec.T
+    assert_parity(got, ref, dtype, f"lengths, large h0, {mode}: {m.describe(spec.T, spec.B)}")
+
+
+def _saturating(spec):
+    """Inputs whose every gate sits at a saturated end: b_ih of i and o +30
+    (sigma = 1 exactly in fp32), of g +-30 (tanh = +-1), of f +30 or -100
+    (sigma = 0 exactly: exp2 overflows to +inf and its reciprocal is 0);
+    b_hh = 0; weights as drawn.  c then moves by exactly +-1 per step where
+    f = 1, so h = o tanh(c) reaches +-1 exactly after a few steps, and the
+    saturated gates make the recurrence contract instead of amplifying
+    rounding differences."""
+    from layer_lstm_forward_amd.synth import f32_to_bf16_bits
+    inp = make_inputs(spec)
+    H, bf = spec.hidden_size, spec.dtype == "bf16"
+    rng = np.random.default_rng(spec.seed + 1)
+    for k in range(len(inp.params)):
+        if k % 4 == 2:
+            b = np.empty(4 * H, np.float32)
+            b[:H] = 30.0
+            b[H:2 * H] = np.where(rng.random(H) < 0.3, -100.0, 30.0)
+            b[2 * H:3 * H] = np.where(rng.random(H) < 0.5, 30.0, -30.0)
+            b[3 * H:] = 30.0
+            inp.params[k] = f32_to_bf16_bits(b) if bf else b
+        elif k % 4 == 3:
+            inp.params[k] = np.zeros_like(inp.params[k])
+    return inp
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", sorted(LENGTH_MODES))
+def test_saturated_gates(dtype, mode):
+    """Every gate saturated (the ends of the sigmoid and tanh of the [warp-nn]
+    equation block), |h| = 1 exactly on many cells (in the bf16 exchange word
+    too), on the persistent (fused and hoisted), stepped and GEMM-step paths."""
+    spec = Spec(32, 64, 2, True, 16, 20, dtype, 720, "normal0.1")
+    print(f"case saturated gates {dtype} {mode}", flush=True)
+    inp = _saturating(spec)
+    rec, opts = LENGTH_MODES[mode]
+    got, m = run_gpu(inp, recurrence=rec, options=opts)
+    y, hn, cn = got
+    assert np.all(np.abs(y) <= 1.0) and np.all(np.isfinite(cn))
+    assert np.mean(np.abs(y) == 1.0) > 0.1, "the case should drive h to +-1 exactly"
+    assert_parity(got, run_oracle(inp), dtype, f"saturated {mode}: {m.describe(spec.T, spec.B)}")
+
+
+@pytest.mark.parametrize("mode", sorted(LENGTH_MODES))
+def test_large_weights_few_steps(mode):
+    """Weights x40 (the invariant pin's saturating draw) over three steps of one
+    bidirectional layer in fp32: most pre-activations are far into the
+    saturated ends.  (Over more steps such weights make the recurrence
+    chaotic: fp32 and fp64 runs of the same inputs drift apart by more than
+    any fixed tolerance, whatever the implementation.)"""
+    spec = Spec(32, 64, 1, True, 3, 20, "f32", 730, "normal0.1")
+    print(f"case large weights {mode}", flush=True)
+    inp = make_inputs(spec)
+    inp.params = [_scaled(p, 40.0, False) for p in inp.params]
+    rec, opts = LENGTH_MODES[mode]
+    got, m = run_gpu(inp, recurrence=rec, options=opts)
+    assert np.all(np.abs(got[0]) <= 1.0)
+    assert_parity(got, run_oracle(inp), "f32", f"x40 weights {mode}: {m.describe(spec.T, spec.B)}")
+
+
 def test_lengths_all_full_equal_plain_forward():
     spec = Spec(48, 72, 2, True, 7, 37, "f32", 705, "normal0.1")
     inp = make_inputs(spec)
@@ -302,8 +396,8 @@ def test_full_l2_in256_h512_b64_f32_lengths_sampled_rows():
     assert_parity((y[:, rows], hn[:, rows], cn[:, rows]), ref, spec.dtype, m.describe(spec.T, spec.B))
 
 
-def test_full_l2bi_in512_h1024_b32_bf16_sampled_rows():
-    _full("l2bi_in512_h1024_t256_b32_bf16", [0, 17, 31])
+def test_full_l2bi_in512_h1024_b32_bf16_all_rows():
+    _full("l2bi_in512_h1024_t256_b32_bf16", None)
 
 
 @pytest.mark.parametrize("name", ["l1_in1024_h1024_t1024_b1_bf16", "l1_in1024_h1024_t1024_b4_bf16"])
@@ -313,4 +407,7 @@ def test_full_l1_h1024_t1024_small_batch(name):
 
 @pytest.mark.slow
 def test_full_l4_in2048_h2048_b256_bf16_sampled_rows():
-    _full("l4_in2048_h2048_t512_b256_bf16", [0, 201])
+    # the first row, the last row (the end of the last 64-row block) and one
+    # seeded random row, over the full T and all four layers
+    rnd = int(np.random.default_rng(1006).integers(1, 255))
+    _full("l4_in2048_h2048_t512_b256_bf16", [0, rnd, 255])
