@@ -23,7 +23,8 @@
  *     hidden state is rounded to bfloat16 (nearest-even) where it is stored.
  *   - Every tensor pointer is device memory on the current HIP device, owned
  *     by the caller.  The library allocates no device memory; all scratch
- *     lives in the caller's workspace.
+ *     lives in the caller's workspace (lstm_forward_static: in the library's
+ *     own file-scope device array).
  *   - Weight pointer order (warp-nn "Learnable parameters" table, flattened
  *     layer by layer as "Complete Trace: nn.LSTM" Step 1 flattens them):
  *         for l in 0..L-1, for d in 0..D-1 (forward, then reverse):
@@ -191,6 +192,31 @@ lstm_status lstm_forward(lstm_plan *plan, const void *x, const void *h0, const f
                          const void *const *weights, int T, int B, int layers, int bidir,
                          void *y, void *h_n, float *c_n, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* lstm_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture into a graph, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a file-scope device
+ * array of LSTM_STATIC_WORKSPACE_BYTES inside the library: one copy on each
+ * device the library runs on, held until the process ends, its address looked
+ * up once per device.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *   x .. c_n, stream  as lstm_forward
+ *   device_status     device memory for one unsigned, or NULL: after the
+ *                     forward, a one-thread kernel on `stream` copies the
+ *                     kernel status word there (0: every step barrier
+ *                     completed; non-zero: a wait gave up and the outputs are
+ *                     invalid), what lstm_device_status reads for lstm_forward
+ * Errors as lstm_forward; a (T, B) whose lstm_workspace_size exceeds
+ * LSTM_STATIC_WORKSPACE_BYTES is LSTM_ERR_WORKSPACE, with nothing enqueued.
+ * Every call on one device shares that device's array, and each call
+ * overwrites it (the synchronisation words are cleared at the start of each
+ * call, on its stream): calls that can overlap on one device -- on different
+ * streams, or from several threads -- race and must be serialised by the
+ * caller. */
+#define LSTM_STATIC_WORKSPACE_BYTES ((size_t)96 << 20)
+lstm_status lstm_forward_static(lstm_plan *plan, const void *x, const void *h0, const float *c0,
+                                const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                                void *h_n, float *c_n, unsigned *device_status, void *stream);
 
 /* Variable-length batches: the same forward with a sequence length per
  * batch row on the padded [T, B, .] layout.  The trace page "Complete Trace:

@@ -69,6 +69,8 @@ def load_library():
     lib.lstm_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.lstm_forward.restype = i
     lib.lstm_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp, sz, vp]
+    lib.lstm_forward_static.restype = i
+    lib.lstm_forward_static.argtypes = [vp, vp, vp, vp, ctypes.POINTER(vp), i, i, i, i, vp, vp, vp, vp, vp]
     lib.lstm_forward_lengths.restype = i
     lib.lstm_forward_lengths.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int), vp, vp, ctypes.POINTER(vp),
                                          i, i, i, i, vp, vp, vp, vp, sz, vp]
@@ -174,6 +176,21 @@ def lstm_forward(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, wor
         arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
         ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(workspace),
         int(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+LSTM_STATIC_WORKSPACE_BYTES = 96 << 20
+
+
+def lstm_forward_static(plan, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, device_status, stream) -> int:
+    """Raw call of the forward on the library's own workspace (integer device
+    addresses, 0 = NULL; device_status: device address of one unsigned, or 0);
+    returns the status."""
+    arr = (ctypes.c_void_p * len(weights))(*[int(w) for w in weights])
+    return int(load_library().lstm_forward_static(
+        ctypes.c_void_p(plan), ctypes.c_void_p(x), ctypes.c_void_p(h0 or None), ctypes.c_void_p(c0 or None),
+        arr, int(T), int(B), int(layers), int(bool(bidir)), ctypes.c_void_p(y),
+        ctypes.c_void_p(h_n or None), ctypes.c_void_p(c_n or None), ctypes.c_void_p(device_status or None),
+        ctypes.c_void_p(stream or None)))
 
 
 def lstm_forward_lengths(plan, x, lengths, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "../../include/lstm.h"
+
 namespace lstm_amd {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
@@ -240,5 +242,12 @@ bool rec_step_gemm_ok(const RecArgs &a, int dtype);
 // Batch rows per workgroup of k_rec_step (64 with two K slices, or 128).
 int rec_step_rows(int B);
 hipError_t launch_rec_step_gemm(const RecArgs &a, int dtype, hipStream_t s);
+
+// The forward pass behind lstm_forward (every recurrent mode); own_ws: the
+// workspace is the library's own device array (lstm_forward_static) rather
+// than caller memory, so it is not checked as caller memory.
+lstm_status forward_dispatch(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                             const void *const *weights, int T, int B, int layers, int bidir, void *y, void *h_n,
+                             float *c_n, void *workspace, size_t workspace_bytes, void *stream, bool own_ws);
 
 }  // namespace lstm_amd

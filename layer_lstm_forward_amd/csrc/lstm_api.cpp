@@ -564,7 +564,7 @@ int validate(const lstm_plan *p, const void *x, const void *h0, const float *c0,
 
 extern "C" {
 
-int lstm_version(void) { return 109; }
+int lstm_version(void) { return 110; }
 
 const char *lstm_strerror(int s) {
     switch (s) {
@@ -809,10 +809,12 @@ namespace {
 
 // The forward pass; lengths_h: NULL (every row has T steps) or B host values
 // in 1..T, already validated.
+// own_ws: the workspace is the library's own device array (lstm_forward_static),
+// not caller memory, and is not checked as one.
 lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, const void *h0, const float *c0,
                          const void *const *weights, int T, int B, int layers, int bidir, void *y,
                          void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream_,
-                         char *reserve = nullptr) {
+                         char *reserve = nullptr, bool own_ws = false) {
     Layout lay;
     int rc = validate(p, x, h0, c0, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
     if (rc != LSTM_OK) return (lstm_status)rc;
@@ -825,7 +827,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         return LSTM_ERR_DEVICE;
     }
     const int per = p->has_bias ? 4 : 2;
-    const void *ptrs[] = {x, y, workspace, h0, c0, h_n, c_n};
+    const void *ptrs[] = {x, y, own_ws ? nullptr : workspace, h0, c0, h_n, c_n};
     for (const void *q : ptrs)
         if (q && !is_device_ptr(q, dev)) return LSTM_ERR_DEVICE;
     for (int i = 0; i < p->L * p->D * per; ++i)
@@ -1152,7 +1154,8 @@ bool use_persistent_for_mode(const lstm_plan *p, int B, bool wide) {
 // per step, which adds W_hh h_{t-1} + b_hh and applies the mode's update.
 lstm_status forward_modes(lstm_plan *p, const void *x, const int *lengths_h, const void *h0,
                           const void *const *weights, int T, int B, int layers, int bidir, void *y, void *h_n,
-                          const float *c_n, void *workspace, size_t workspace_bytes, void *stream_) {
+                          const float *c_n, void *workspace, size_t workspace_bytes, void *stream_,
+                          bool own_ws = false) {
     Layout lay;
     int rc = validate(p, x, h0, nullptr, weights, T, B, layers, bidir, y, workspace, workspace_bytes, &lay);
     if (rc != LSTM_OK) return (lstm_status)rc;
@@ -1163,7 +1166,7 @@ lstm_status forward_modes(lstm_plan *p, const void *x, const int *lengths_h, con
         return LSTM_ERR_DEVICE;
     }
     const int per = p->has_bias ? 4 : 2;
-    const void *ptrs[] = {x, y, workspace, h0, h_n};
+    const void *ptrs[] = {x, y, own_ws ? nullptr : workspace, h0, h_n};
     for (const void *q : ptrs)
         if (q && !is_device_ptr(q, dev)) return LSTM_ERR_DEVICE;
     for (int i = 0; i < p->L * p->D * per; ++i)
@@ -1245,22 +1248,30 @@ lstm_status forward_modes(lstm_plan *p, const void *x, const int *lengths_h, con
 
 }  // namespace
 
-extern "C" {
-
-lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
-                         const void *const *weights, int T, int B, int layers, int bidir, void *y,
-                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
+lstm_status lstm_amd::forward_dispatch(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                                       const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                                       void *h_n, float *c_n, void *workspace, size_t workspace_bytes,
+                                       void *stream, bool own_ws) {
     if (p && p->mode != LSTM_MODE_LSTM) {
         if (c0 || c_n) return LSTM_ERR_ARG;  // no cell state
         // the persistent kernel on padded gate slots where the schedule allows, else one launch per step
         if (use_persistent_for_mode(p, B, needs_wide_exchange(p, h0 != nullptr, false)))
             return forward_impl(p, x, nullptr, h0, nullptr, weights, T, B, layers, bidir, y, h_n, nullptr,
-                                workspace, workspace_bytes, stream);
+                                workspace, workspace_bytes, stream, nullptr, own_ws);
         return forward_modes(p, x, nullptr, h0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
-                             workspace_bytes, stream);
+                             workspace_bytes, stream, own_ws);
     }
     return forward_impl(p, x, nullptr, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, nullptr, own_ws);
+}
+
+extern "C" {
+
+lstm_status lstm_forward(lstm_plan *p, const void *x, const void *h0, const float *c0,
+                         const void *const *weights, int T, int B, int layers, int bidir, void *y,
+                         void *h_n, float *c_n, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_dispatch(p, x, h0, c0, weights, T, B, layers, bidir, y, h_n, c_n, workspace, workspace_bytes,
+                            stream, false);
 }
 
 lstm_status lstm_reserve_size(const lstm_plan *p, int T, int B, size_t *bytes) {

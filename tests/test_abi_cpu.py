@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert pkg.lstm_version() == 109
+    assert pkg.lstm_version() == 110
     for code in pkg.STATUS:
         assert pkg.lstm_strerror(code) and pkg.lstm_strerror(code) != "unknown status"
     assert pkg.lstm_strerror(12345) == "unknown status"
