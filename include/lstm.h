@@ -170,7 +170,10 @@ lstm_status lstm_set_option(lstm_plan *plan, int option, int value);
 
 /* Bytes of device workspace lstm_forward needs for sequence length T and batch
  * B (intermediate layer outputs, the hoisted input projection, cell-state and
- * synchronisation words).  Touches no device. */
+ * synchronisation words).  Touches no device.  The caller queries the size,
+ * allocates the workspace and passes it to the forward call, the sequence the
+ * trace page "Complete Trace: nn.LSTM" (Step 5, the fused-library path) shows
+ * for its workspace. */
 lstm_status lstm_workspace_size(const lstm_plan *plan, int T, int B, size_t *bytes);
 
 /* Enqueue the forward pass on `stream` (a hipStream_t; NULL = default stream).
