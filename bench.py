@@ -62,31 +62,62 @@ def run_oracle(sub, threads, lengths):
                                lengths=lengths)
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_threads():
+    """The host threads this run may use: OMP_NUM_THREADS when set (a share of
+    a larger machine), else every CPU the process sees."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, n if n > 0 else (os.cpu_count() or 1))
+
+
 def cpu_baseline(inp, budget_s, lengths=None):
+    """The fp64 oracle timed on the host cores, on a bounded sample of batch
+    rows of the same workload (rows are independent): once on one thread and
+    once on every thread this run may use, each sized from a one-row
+    calibration to about budget_s / 2 seconds."""
     import numpy as np
     spec = inp.spec
-    threads = max(1, os.cpu_count() or 1)
     per_row_flops = spec.flops() / spec.B
-    # calibrate on one row, then size the sample to the time budget
-    rows = [0]
-    t0 = time.perf_counter()
-    sub = inp.rows(rows)
-    run_oracle(sub, threads, None if lengths is None else lengths[rows])
-    one = time.perf_counter() - t0
-    n = int(max(1, min(spec.B, budget_s / max(one, 1e-6))))
-    rows = list(np.linspace(0, spec.B - 1, n).astype(int)) if n > 1 else [0]
-    rows = sorted(set(int(r) for r in rows))
-    sub = inp.rows(rows)
-    t0 = time.perf_counter()
-    run_oracle(sub, threads, None if lengths is None else lengths[rows])
-    wall = time.perf_counter() - t0
-    steps = spec.T * len(rows) if lengths is None else int(np.sum(lengths[rows]))
-    cells = steps * spec.hidden_size * spec.num_layers * spec.D
-    return {"value": cells / wall, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {spec.B} batch rows, "
-                      f"{'full T=' + str(spec.T) if lengths is None else 'their valid steps (per-row lengths)'}, "
-                      f"all {spec.num_layers} layers, "
-                      f"fp64, {wall:.1f} s wall ({per_row_flops * len(rows) / wall / 1e9:.2f} GFLOP/s)"}
+
+    def timed(threads):
+        t0 = time.perf_counter()
+        run_oracle(inp.rows([0]), threads, None if lengths is None else lengths[[0]])
+        one = time.perf_counter() - t0
+        n = int(max(1, min(spec.B, (budget_s / 2) / max(one, 1e-6))))
+        rows = sorted(set(int(r) for r in np.linspace(0, spec.B - 1, n).astype(int))) if n > 1 else [0]
+        t0 = time.perf_counter()
+        run_oracle(inp.rows(rows), threads, None if lengths is None else lengths[rows])
+        wall = time.perf_counter() - t0
+        steps = spec.T * len(rows) if lengths is None else int(np.sum(lengths[rows]))
+        cells = steps * spec.hidden_size * spec.num_layers * spec.D
+        return cells / wall, rows, wall
+
+    threads = host_threads()
+    v1, rows1, wall1 = timed(1)
+    vn, rowsn, walln = timed(threads)
+    what = f"full T={spec.T}" if lengths is None else "their valid steps (per-row lengths)"
+    return {"value": vn, "unit": "timestep-cells/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rowsn)} of {spec.B} batch rows, {what}, all {spec.num_layers} layers, fp64, "
+                      f"{walln:.1f} s wall on {threads} threads ({per_row_flops * len(rowsn) / walln / 1e9:.2f} "
+                      f"GFLOP/s)",
+            "single_thread": {"value": v1, "cores": 1,
+                              "sample": f"{len(rows1)} of {spec.B} batch rows, {what}, {wall1:.1f} s wall "
+                                        f"({per_row_flops * len(rows1) / wall1 / 1e9:.2f} GFLOP/s)"},
+            "cpu_model": cpu_model(), "cpus_visible": os.cpu_count()}
 
 
 def summarize_profile(path, command):
@@ -374,16 +405,29 @@ def main():
                          for l in range(spec.num_layers) if l < len(fused) and fused[l] == "fused") / spec.num_layers
     else:
         kname, flops, avg = names.get("proj", "k_proj"), proj_flops_per_launch(spec), proj_avg
-    achieved = flops / (avg / 1e3) / 1e12
+    stepping = tm["rec_launches"] > tm["calls"] * spec.num_layers
+    nbytes = alg_bytes_per_launch(spec, kname, desc, stepping)
+    tflops = flops / (avg / 1e3) / 1e12
+    gbs = None if nbytes is None else nbytes / (avg / 1e3) / 1e9
+    # the bound is the resource whose time at peak is the larger for this launch
+    hbm_bound = gbs is not None and nbytes / PEAK_HBM_GBS > flops / (PEAK_TFLOPS[spec.dtype] * 1e3)
+    if hbm_bound:
+        bound, achieved, peak, unit = "hbm", gbs, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", tflops, PEAK_TFLOPS[spec.dtype], "TFLOP/s"
     traffic = stored_traffic(kname, args.workload)
-    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[spec.dtype], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS[spec.dtype], 4),
+    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "traffic_GB_per_s": None if traffic is None else round(traffic / (avg / 1e3) / 1e9, 1),
             "kernel": kname,
-            "avg_launch_ms": round(avg, 4), "flops_per_launch": flops,
+            "avg_launch_ms": round(avg, 4), "flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
+            "mfma_frac": round(tflops / PEAK_TFLOPS[spec.dtype], 4),
+            "hbm_frac": None if gbs is None else round(gbs / PEAK_HBM_GBS, 4),
             "phase_ms_per_step": {"proj": round(tm["proj_ms"] / max(1, tm["calls"]), 4),
                                   "rec": round(tm["rec_ms"] / max(1, tm["calls"]), 4)}}
+
+    recurrence = recurrence_roofline(spec, desc, tm, args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -402,8 +446,82 @@ def main():
                                                        "valid_steps": int(np.sum(lengths))}),
                        **({"layout": "batch_first"} if args.batch_first else {}),
                        **({"cell": spec.mode} if spec.mode != "lstm" else {})},
-            "roofline": roof, "cpu_baseline": cpu}
+            "roofline": roof, "recurrence": recurrence, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
+    # release the plan while the runtime is fully up, not from a finaliser at exit
+    del m
+    torch.cuda.synchronize()
+
+
+PEAK_LDS_GBS = 78643.2  # 128 B per clock per CU, 256 CUs, 2.4 GHz
+
+
+def alg_bytes_per_launch(spec, kname, desc, stepping):
+    """Algorithmic HBM bytes of one launch of the dominant kernel (the
+    per-unit figures times the units one launch covers), or None where no
+    such figure is kept (the layer pipeline).  Every array read or written
+    once per launch:
+      k_proj*      x [T*B, in_l] + W_ih [D*4H, in_l] read, G [T*B, D*4H] fp32
+                   written (mean over layers)
+      k_rec        per layer: W_hh [D*4H, H], y [T, B, D*H] written, h0/c0 and
+                   h_n/c_n, and either G read (hoisted) or x and W_ih read
+                   (fused) (mean over layers)
+      k_rec_step   one step: W_hh, G [B, D*4H] fp32, h_{t-1} [B, D*H] read, c
+                   read and written, y [B, D*H] written"""
+    H, B, T, D, L = spec.hidden_size, spec.B, spec.T, spec.D, spec.num_layers
+    s = 2 if spec.dtype == "bf16" else 4
+    G4 = spec.gates * H
+    fused = (re.findall(r"xproj=([a-z,]+)", desc) or [""])[0].split(",")
+    if kname.startswith("k_proj"):
+        return sum(T * B * spec.layer_input(l) * s + D * G4 * spec.layer_input(l) * s + T * B * D * G4 * 4
+                   for l in range(L)) / L
+    states = 2 * D * B * H * (s + 4)  # h0, c0 read; h_n, c_n written
+    if kname == "k_rec_step" or (kname == "k_rec" and stepping):
+        return D * G4 * H * s + B * D * G4 * 4 + B * D * H * s + 2 * B * D * H * 4 + B * D * H * s
+    if kname == "k_rec":
+        tot = 0.0
+        for l in range(L):
+            io = (T * B * spec.layer_input(l) * s + D * G4 * spec.layer_input(l) * s
+                  if l < len(fused) and fused[l] == "fused" else T * B * D * G4 * 4)
+            tot += D * G4 * H * s + T * B * D * H * s + states + io
+        return tot / L
+    return None
+
+
+def recurrence_roofline(spec, desc, tm, workload):
+    """The recurrent phase against its own roofline: the larger of (a) its
+    matrix-core time at the dtype's peak (the recurrent products, plus the
+    input products when they run inside the recurrent launch), (b) W_hh read
+    once per step from where it lives (registers: no bound; LDS at the LDS
+    peak; streamed from HBM by the per-step GEMM kernel) and (c) its HBM
+    traffic (the hoisted G read and y written).  frac = roofline time /
+    measured time; per_step_us = measured time / sequential step slots."""
+    H, B, T, D, L = spec.hidden_size, spec.B, spec.T, spec.D, spec.num_layers
+    s = 2 if spec.dtype == "bf16" else 4
+    G4 = spec.gates * H
+    fused = (re.findall(r"xproj=([a-z,]+)", desc) or [""])[0].split(",")
+    is_fused = [l < len(fused) and fused[l] == "fused" for l in range(L)]
+    flops = sum(2.0 * B * T * D * G4 * (H + (spec.layer_input(l) if is_fused[l] else 0)) for l in range(L))
+    rec_ms = tm["rec_ms"] / max(1, tm["calls"])
+    pipe = "k_rec_pipe" in desc
+    slots = T + L - 1 if pipe else T * L
+    if "k_rec_step" in desc or "mode=gemm-step" in desc:
+        w_level, w_bw = "hbm", PEAK_HBM_GBS
+    elif "w_hh=lds" in desc or pipe:
+        w_level, w_bw = "lds", PEAK_LDS_GBS
+    else:
+        w_level, w_bw = "registers", None
+    w_bytes = T * L * D * G4 * H * s
+    hbm_bytes = sum((0 if is_fused[l] else T * B * D * G4 * 4) + T * B * D * H * s for l in range(L))
+    terms = {"mfma_us": flops / (PEAK_TFLOPS[spec.dtype] * 1e12) * 1e6,
+             "w_hh_us": None if w_bw is None else w_bytes / (w_bw * 1e9) * 1e6,
+             "hbm_us": hbm_bytes / (PEAK_HBM_GBS * 1e9) * 1e6}
+    bound = max((k for k in terms if terms[k] is not None), key=lambda k: terms[k])
+    t_roof = terms[bound]
+    return {"per_step_us": round(rec_ms * 1e3 / slots, 3), "slots": slots, "ms": round(rec_ms, 4),
+            "w_hh_from": w_level, "bound": bound.replace("_us", ""),
+            "terms_us": {k: None if v is None else round(v, 2) for k, v in terms.items()},
+            "frac": round(t_roof / (rec_ms * 1e3), 4)}
 
 
 def train_bench(args, spec, m, x, w, h0, c0, stream, desc, lengths=None):

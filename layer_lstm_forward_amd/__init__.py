@@ -343,6 +343,11 @@ class LSTM:
         lstm_set_dropout(self.plan, prob, seed, call)
 
     def __del__(self):
+        # at interpreter shutdown the plan's host memory goes with the process;
+        # no runtime call is made from a finaliser then
+        import sys
+        if sys.is_finalizing():
+            return
         try:
             lstm_destroy(self.plan)
         except Exception:
