@@ -393,9 +393,8 @@ def main():
     names = dict(re.findall(r"(proj|rec)=(k_[a-z_]+)<", desc))
     if tm["rec_ms"] >= tm["proj_ms"]:
         kname, flops, avg = names.get("rec", "k_rec"), rec_flops_per_launch(spec), rec_avg
-        if kname == "k_rec_pipe":  # one launch runs every layer, and the input products of layers > 0
-            flops = rec_flops_per_launch(spec) * spec.num_layers + proj_flops_per_launch(spec) * spec.num_layers \
-                - 2.0 * spec.T * spec.B * spec.D * 4 * spec.hidden_size * spec.layer_input(0)
+        if kname == "k_rec_wave":  # one launch runs every layer with its input products
+            flops = (rec_flops_per_launch(spec) + proj_flops_per_launch(spec)) * spec.num_layers
         elif tm["rec_launches"] > tm["calls"] * spec.num_layers:  # stepping: a "launch" is one step
             flops /= spec.T
         else:  # layers whose input projection runs inside the recurrent launch
@@ -467,7 +466,9 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
                    h_n/c_n, and either G read (hoisted) or x and W_ih read
                    (fused) (mean over layers)
       k_rec_step   one step: W_hh, G [B, D*4H] fp32, h_{t-1} [B, D*H] read, c
-                   read and written, y [B, D*H] written"""
+                   read and written, y [B, D*H] written
+      k_rec_wave   the whole stack: every layer's W_ih and W_hh, x, the top
+                   layer's y, each layer's h0/c0 and h_n/c_n"""
     H, B, T, D, L = spec.hidden_size, spec.B, spec.T, spec.D, spec.num_layers
     s = 2 if spec.dtype == "bf16" else 4
     G4 = spec.gates * H
@@ -476,6 +477,9 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
         return sum(T * B * spec.layer_input(l) * s + D * G4 * spec.layer_input(l) * s + T * B * D * G4 * 4
                    for l in range(L)) / L
     states = 2 * D * B * H * (s + 4)  # h0, c0 read; h_n, c_n written
+    if kname == "k_rec_wave":  # every layer in one launch: all weights, x, the top layer's y, states
+        return (sum(D * G4 * (H + spec.layer_input(l)) * s for l in range(L)) + T * B * spec.input_size * s
+                + T * B * D * H * s + L * 2 * D * B * H * (s + 4))
     if kname == "k_rec_step" or (kname == "k_rec" and stepping):
         return D * G4 * H * s + B * D * G4 * 4 + B * D * H * s + 2 * B * D * H * 4 + B * D * H * s
     if kname == "k_rec":
@@ -503,7 +507,7 @@ def recurrence_roofline(spec, desc, tm, workload):
     is_fused = [l < len(fused) and fused[l] == "fused" for l in range(L)]
     flops = sum(2.0 * B * T * D * G4 * (H + (spec.layer_input(l) if is_fused[l] else 0)) for l in range(L))
     rec_ms = tm["rec_ms"] / max(1, tm["calls"])
-    pipe = "k_rec_pipe" in desc
+    pipe = "k_rec_wave" in desc
     slots = T + L - 1 if pipe else T * L
     if "k_rec_step" in desc or "mode=gemm-step" in desc:
         w_level, w_bw = "hbm", PEAK_HBM_GBS

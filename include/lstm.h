@@ -108,9 +108,12 @@ typedef enum {
                                 workgroups' h_t; 0 reads as soon as the step ends. A read that reaches
                                 memory before the data costs a retry round trip; results do not depend
                                 on it */
-    LSTM_OPT_LAYER_PIPE = 10, /* 0 (default): layer by layer; 1: a unidirectional stack of 2..4 layers runs
-                                all layers in one pipelined persistent launch when every layer's weights
-                                fit on chip (layer l consumes layer l-1's h_t as it is produced). Changes
+    LSTM_OPT_LAYER_PIPE = 10, /* 1 (default): a unidirectional LSTM stack of 2..4 layers in the time-major
+                                layout runs every layer in one persistent launch (the layer wavefront: layer
+                                l consumes layer l-1's h_t as it is produced, two workgroups per CU) when its
+                                tiles fit (H and the input width at most 128 fp32 / 256 bf16 values per wave
+                                and whole 16-byte rows) and all its workgroups are co-resident; 0: layer by
+                                layer.  Not used with per-row lengths or in training. Changes
                                 lstm_workspace_size. */
     LSTM_OPT_FUSE_INPUT = 11, /* 1 (default): a layer whose recurrence runs as one persistent launch and
                                 whose W_ih share fits in registers computes x_t W_ih^T + b_ih + b_hh inside

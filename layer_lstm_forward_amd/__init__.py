@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblstm_amd.so")
@@ -342,11 +343,10 @@ class LSTM:
         next forward_train (each one advances it)."""
         lstm_set_dropout(self.plan, prob, seed, call)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # at interpreter shutdown the plan's host memory goes with the process;
         # no runtime call is made from a finaliser then
-        import sys
-        if sys.is_finalizing():
+        if _finalizing():
             return
         try:
             lstm_destroy(self.plan)

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #include "../../include/lstm.h"
 
@@ -74,38 +75,39 @@ struct RecArgs {
 
 constexpr int kMaxTeams = 64;
 
-// All layers of a unidirectional stack in one persistent launch (layer
-// pipeline): layer l > 0 consumes layer l-1's h_t from its exchange buffer in
-// the same step and multiplies [x_t; h_{t-1}] by its resident [W_ih; W_hh]
-// slice, so its input projection is never materialised and the layers' time
-// loops overlap instead of running one after the other.
+// The layer wavefront (rec_wave.hip): every layer of a unidirectional stack in
+// one persistent launch, two workgroups per CU, layer l > 0 multiplying layer
+// l-1's h_t (read from its exchange words) as its input; layer 0 multiplies
+// x_t.  Teams of at most 16 batch rows, U = 4 NT units per workgroup.
 constexpr int kMaxPipeLayers = 4;
-struct PipeArgs {
-    const void *whh[kMaxPipeLayers];   // [4H, H] dtype
-    const void *wih[kMaxPipeLayers];   // [4H, H] dtype (layers >= 1; their input width is H)
-    const void *b_ih[kMaxPipeLayers];  // [4H] dtype or NULL (layers >= 1)
+struct WaveArgs {
+    const void *x;                          // [T, B, I] dtype: layer 0's input
+    const void *wih[kMaxPipeLayers];        // [4H, in_l] dtype (in_0 = I, else H)
+    const void *whh[kMaxPipeLayers];        // [4H, H] dtype
+    const void *b_ih[kMaxPipeLayers];       // [4H] dtype or NULL (no bias)
     const void *b_hh[kMaxPipeLayers];
-    const float *G;                    // [T, B, 4H] projection of layer 0 incl. both biases
-    const void *h0;                    // [L, B, H] dtype, or NULL (zeros)
-    const float *c0;                   // [L, B, H] or NULL
-    void *Y;                           // [T, B, H] dtype: output of the last layer
-    void *hn;                          // [L, B, H] dtype or NULL
-    float *cn;                         // [L, B, H] or NULL
-    unsigned long long *xbuf[kMaxPipeLayers];  // per layer: [slots][NGB] regions of (ROWS/16)*kch*256 tagged words
-    int xslots[kMaxPipeLayers];        // T (one slot per step) or 2 (parities, last layer)
-    unsigned tag_base[kMaxPipeLayers]; // tags of layer l are tag_base[l] + s + 1
+    const void *h0;                         // [L, B, H] dtype, or NULL (zeros)
+    const float *c0;                        // [L, B, H] or NULL
+    void *Y;                                // [T, B, H] dtype: output of the last layer
+    void *hn;                               // [L, B, H] dtype or NULL
+    float *cn;                              // [L, B, H] or NULL
+    uint32_t *xbuf[kMaxPipeLayers];         // per layer: [slots][NGB][kch * 256] exchange words, zeroed;
+                                            // T slots, or 2 for the last layer
     unsigned *status;
-    int L, T, B, H;
-    int P;                             // workgroups per (layer, batch group)
-    int BG, NGB;
-    int kch;                           // K chunks of H
-    int kchp[kMaxPipeLayers];          // resident chunks per layer (padded to whole batches per wave)
-    int kchp_max;
-    int nbatch[kMaxPipeLayers];
-    int poll_sleep;
-    int vec;
+    int L, T, B, H, I;
+    int P, BG, NGB, kch;
+    int ncx0;                               // layer 0's input chunks per wave
+    int map_xcd;                            // 1: a team's workgroups on 8 / NGB XCDs
+    int poll_sleep, pace, vec;
     long long timeout_ticks;
 };
+// The wavefront applies when W_hh's K fits 4 waves x 8 chunks, layer 0's
+// input width fits 8 chunks per wave (ncx0: its chunks per wave), and H and
+// the input width are multiples of 16 bytes.
+bool wave_shape_ok(int H, int I, int dtype, int *ncx0);
+// nt: 4 nt units per workgroup (1, 2 or 4)
+hipError_t wave_max_coresident(int nt, int dtype, int *blocks_per_cu);
+hipError_t launch_wave(const WaveArgs &a, int nt, int dtype, hipStream_t s);
 
 // Recurrent tile: 4 waves split (4/WK) ways over batch tiles and WK ways over
 // K; each wave owns MTW 16-row batch tiles; NT 16-column tiles of gate rows
@@ -137,12 +139,6 @@ hipError_t launch_ksum(const float *part, int ns, size_t slab, size_t n, void *o
 // over D directions, given 16-byte aligned operands.
 const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant);
 hipError_t launch_rec(const RecArgs &a, RecTile t, size_t smem, int dtype, bool cooperative, hipStream_t s);
-// Layer pipeline (k_rec_pipe): tiles it is built for, its LDS geometry
-// (kchp/nbatch per layer) and its cooperative launch.
-bool pipe_tile_supported(RecTile t);
-RecGeom pipe_geom(RecTile t, int H, int dtype, int L, int *kchp, int *nbatch);
-hipError_t pipe_max_coresident(RecTile t, size_t smem, int dtype, int *blocks_per_cu);
-hipError_t launch_pipe(const PipeArgs &a, RecTile t, size_t smem, int dtype, hipStream_t s);
 hipError_t rec_max_coresident(RecTile t, size_t smem, int dtype, bool wreg, bool fused, bool wide,
                               int *blocks_per_cu);
 // input chunks per wave of the tile's fused-projection variant (0: none)

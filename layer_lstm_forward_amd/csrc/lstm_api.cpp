@@ -25,7 +25,7 @@ struct lstm_plan {
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
     int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next (-1: by schedule)
-    int layer_pipe;    // 1: run a unidirectional stack's layers in one pipelined launch when it fits
+    int layer_pipe;    // 1 (default): run a unidirectional stack's layers in one wavefront launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
     int mode;          // LSTM_MODE_*
@@ -68,15 +68,22 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 struct Layout {
     size_t status, xbuf, G, ymid[2], cstate, hstate, lens, wpad, total;
     size_t sync_bytes;  // status word + exchange buffer, zeroed per call
-    size_t pipe_tiles;  // bound on the 16-row tiles of a pipelined schedule
 };
 
-// The layer pipeline applies to unidirectional stacks of 2..kMaxPipeLayers
-// layers in a persistent mode with the option on.
-bool pipe_candidate(const lstm_plan *p) {
-    return p->layer_pipe && p->D == 1 && p->L >= 2 && p->L <= kMaxPipeLayers &&
-           (p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT);
+// The layer wavefront (rec_wave.hip) applies to unidirectional LSTM stacks of
+// 2..kMaxPipeLayers layers in the time-major layout, in a persistent mode with
+// its option and the fused input projection on (it computes every input
+// product in its launch), whose W_hh and layer-0 input widths fit its tiles.
+bool wave_candidate(const lstm_plan *p) {
+    int ncx0 = 0;
+    return p->layer_pipe && p->fuse_input && p->mode == LSTM_MODE_LSTM && p->D == 1 && p->L >= 2 &&
+           p->L <= kMaxPipeLayers &&
+           !p->batch_first && (p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT) &&
+           wave_shape_ok(p->H, p->I, p->dtype, &ncx0);
 }
+
+// Teams of the wavefront: at most 16 batch rows each.
+int wave_teams(int B) { return (B + 15) / 16; }
 
 // Padded parameters of the GRU and the RNNs, per (layer, direction): W_ih
 // [4H][in_l], W_hh [4H][H], b_ih [4H], b_hh [4H] (dtype), each 256-byte
@@ -120,19 +127,20 @@ bool make_layout(const lstm_plan *p, int T, int B, Layout *o) {
     const size_t kch = (size_t)(p->H + (p->dtype == LSTM_BF16 ? 31 : 15)) / (p->dtype == LSTM_BF16 ? 32 : 16);
     if (!mul_ok((size_t)2 * p->D * (((size_t)B + 255) / 16 + 1), kch * 256 * sizeof(unsigned long long), &xb))
         return false;
-    // the layer pipeline keeps one slot per step for every layer but the last
-    // (pipeline tiles are at most 64 rows, so at most (B + 63) / 16 + 1 tiles)
-    o->pipe_tiles = ((size_t)B + 63) / 16 + 1;
-    if (pipe_candidate(p)) {
-        size_t slots, pb;
-        if (!mul_ok((size_t)T, (size_t)(p->L - 1), &slots) || !mul_ok(slots + 2, o->pipe_tiles, &slots) ||
-            !mul_ok(slots, kch * 256 * sizeof(unsigned long long), &pb))
-            return false;
-        if (pb > xb) xb = pb;
-    }
     // G is [T*B][D][4H] for every mode: the GRU and the RNNs use it with
     // their gate blocks padded to four when they run on the persistent kernel
     if (!mul_ok(tb, (size_t)p->D * 4 * p->H * sizeof(float), &g)) return false;
+    // The layer wavefront has no G (every input product runs in its launch)
+    // and keeps its exchange words in G's place: one slot per step for every
+    // layer but the last, which keeps two; a slot holds kch * 256 32-bit
+    // words per team.
+    if (wave_candidate(p)) {
+        size_t slots, wb;
+        if (!mul_ok((size_t)T, (size_t)(p->L - 1), &slots) || !mul_ok(slots + 2, (size_t)wave_teams(B), &slots) ||
+            !mul_ok(slots, kch * 256 * sizeof(uint32_t), &wb))
+            return false;
+        if (wb > g) g = wb;
+    }
     if (!mul_ok(tb, (size_t)p->D * p->H * elem_size(p->dtype), &y)) return false;
     if (!mul_ok((size_t)p->D * B, (size_t)p->H * sizeof(float), &st)) return false;
     size_t off = 0;
@@ -443,58 +451,39 @@ bool gemm_step_shape_ok(const lstm_plan *p) {
            (size_t)4 * p->H * p->H * es < (1u << 31) && (size_t)128 * p->D * p->H * es < (1u << 31);
 }
 
-struct PipeSched {
-    RecTile tile;
-    RecGeom geom;
-    int kchp[kMaxPipeLayers], nbatch[kMaxPipeLayers];
-    int U, P, BG, NGB, wgs;
+struct WaveSched {
+    int NT, U, P, BG, NGB, wgs, ncx0, map_xcd;
 };
 
-// Pipeline schedule: every (layer, batch group, unit slice) workgroup must be
-// co-resident and layer l > 0's [W_ih; W_hh] slice must fit in LDS.  Among the
-// tiles that fit, take the least matrix-core work per wave on the critical
-// path (the hidden half of a layer l > 0 slice) plus the h fetch.
-bool choose_pipe(const lstm_plan *p, int B, int dev, PipeSched *out) {
-    if (!pipe_candidate(p)) return false;
+// Wavefront schedule: teams of at most 16 rows, U = 4 NT units per
+// workgroup; every (layer, team, unit slice) workgroup must be co-resident.
+// The smallest NT that fits spreads the work over the most workgroups.
+bool choose_wave(const lstm_plan *p, int B, int dev, WaveSched *out) {
+    if (!wave_candidate(p)) return false;
     const DevInfo di = dev_info(dev);
     if (!di.ok) return false;
-    static const RecTile tiles[] = {{2, 1, 2}, {2, 1, 4}, {2, 1, 1}, {4, 1, 2}, {4, 1, 4}, {4, 1, 1}, {1, 1, 2}, {1, 1, 1}};
-    double best = 1e300;
-    bool found = false;
-    for (const RecTile &t : tiles) {
-        if (p->rec_tile && p->rec_tile != 100 * t.WK + 10 * t.MTW + t.NT) continue;
-        if (!pipe_tile_supported(t)) continue;
-        PipeSched s{};
-        s.tile = t;
-        const int rows = rec_rows_per_wg(t);
-        const int cap = p->team_rows > 0 && p->team_rows < rows ? p->team_rows : rows;
-        const int ng0 = (B + cap - 1) / cap;
-        s.BG = (B + ng0 - 1) / ng0;
-        s.NGB = (B + s.BG - 1) / s.BG;
-        s.U = 4 * t.NT;
-        s.P = (p->H + s.U - 1) / s.U;
-        s.wgs = p->L * s.NGB * s.P;
-        // the workspace holds at most (B + 63) / 16 + 1 row tiles per slot
-        if ((size_t)s.NGB * (rows / 16) > ((size_t)B + 63) / 16 + 1) continue;
-        s.geom = pipe_geom(t, p->H, p->dtype, p->L, s.kchp, s.nbatch);
-        if (s.geom.smem > kRecLdsLimit) continue;
+    for (int nt = 1; nt <= 4; nt *= 2) {
+        if (p->rec_tile && p->rec_tile != 410 + nt) continue;
+        WaveSched w{};
+        w.NT = nt;
+        w.U = 4 * nt;
+        w.P = (p->H + w.U - 1) / w.U;
+        w.NGB = wave_teams(B);
+        w.BG = (B + w.NGB - 1) / w.NGB;
+        w.wgs = p->L * w.NGB * w.P;
+        wave_shape_ok(p->H, p->I, p->dtype, &w.ncx0);
+        const int per_layer = w.NGB * w.P;
+        w.map_xcd = (w.NGB <= 8 && 8 % w.NGB == 0 && per_layer % 8 == 0) ? 1 : 0;
         int bpc = 0;
-        const bool ok = pipe_max_coresident(t, s.geom.smem, p->dtype, &bpc) == hipSuccess && bpc > 0 &&
-                        (long long)bpc * di.cus >= s.wgs;
+        const bool ok = wave_max_coresident(nt, p->dtype, &bpc) == hipSuccess && bpc > 0 &&
+                        (long long)bpc * di.cus >= w.wgs;
         (void)hipGetLastError();
-        if (!ok) continue;
-        const int live_mtw = (s.BG + 15) / 16 < t.MTW ? (s.BG + 15) / 16 : t.MTW;
-        const double mfma = (double)live_mtw * t.NT * ((2.0 * s.geom.kch + t.WK - 1) / t.WK) *
-                            (p->dtype == LSTM_BF16 ? 16 : 128);
-        const double xbytes = (double)s.BG * p->H * (p->dtype == LSTM_BF16 ? 4 : 8) * 2;
-        const double cost = mfma + xbytes / 32.0;
-        if (cost < best) {
-            best = cost;
-            *out = s;
-            found = true;
+        if (ok) {
+            *out = w;
+            return true;
         }
     }
-    return found;
+    return false;
 }
 
 hipEvent_t take_event(lstm_plan *p) {
@@ -610,7 +599,7 @@ lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidd
     p->part_bufs = 1;
     p->poll_sleep = 2;
     p->read_pace_ns = -1;
-    p->layer_pipe = 0;
+    p->layer_pipe = 1;
     p->fuse_input = 1;
     p->batch_first = 0;
     p->mode = mode;
@@ -764,13 +753,13 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     const int rc = choose_sched(p, B, dev, &s, wide);
     if (rc != LSTM_OK) return (lstm_status)rc;
     const char *proj = proj_kernel_name(T * B, 4 * p->H, in0, p->D, p->dtype, p->proj_tile);
-    PipeSched ps{};
-    if (!mode_persistent && choose_pipe(p, B, dev, &ps)) {
+    WaveSched ws{};
+    if (!mode_persistent && choose_wave(p, B, dev, &ws)) {
         std::snprintf(buf, len,
-                      "proj=%s<%s> (layer 0 only); rec=k_rec_pipe<%s,WK=%d,MTW=%d,NT=%d> mode=layer-pipe U=%d P=%d "
-                      "BG=%d NGB=%d layers=%d workgroups=%d lds=%zu",
-                      proj_kernel_name(T * B, 4 * p->H, p->I, 1, p->dtype, p->proj_tile), dt, dt, ps.tile.WK,
-                      ps.tile.MTW, ps.tile.NT, ps.U, ps.P, ps.BG, ps.NGB, p->L, ps.wgs, ps.geom.smem);
+                      "rec=k_rec_wave<%s,NT=%d> mode=wavefront U=%d P=%d BG=%d NGB=%d layers=%d workgroups=%d "
+                      "map_xcd=%d w_hh=regs xproj=%s",
+                      dt, ws.NT, ws.U, ws.P, ws.BG, ws.NGB, p->L, ws.wgs, ws.map_xcd,
+                      p->L == 2 ? "fused,fused" : p->L == 3 ? "fused,fused,fused" : "fused,fused,fused,fused");
         return LSTM_OK;
     }
     if (!s.persistent && gemm_step_shape_ok(p)) {
@@ -900,49 +889,30 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     }
     if (p->rec_mode == LSTM_REC_GEMM && !gemm) return LSTM_ERR_UNSUPPORTED;
 
-    // Layer pipeline: layer 0's projection, then every layer's recurrence in
-    // one cooperative launch.  If the runtime refuses that launch, the
-    // sequential path below redoes the work.
-    PipeSched ps{};
-    if (!padded && !dlen && !p->batch_first && !reserve && choose_pipe(p, B, dev, &ps)) {
-        const int per16p = p->dtype == LSTM_BF16 ? 8 : 4;
-        const size_t region_words = (size_t)(rec_rows_per_wg(ps.tile) / 16) * ps.geom.kch * 256;
-        const size_t slot_words = region_words * ps.NGB;
+    // Layer wavefront: every layer's recurrence (input products included) in
+    // one cooperative launch.  If the runtime refuses that launch (nothing
+    // ran), the layer-by-layer path below does the work.
+    WaveSched wsch{};
+    if (!padded && !dlen && !reserve && choose_wave(p, B, dev, &wsch)) {
+        const size_t slot_words = (size_t)wsch.NGB * (size_t)((p->H + (p->dtype == LSTM_BF16 ? 31 : 15)) /
+                                                              (p->dtype == LSTM_BF16 ? 32 : 16)) * 256;
         const size_t used_words = slot_words * ((size_t)T * (p->L - 1) + 2);
+        uint32_t *xw = reinterpret_cast<uint32_t *>(ws + lay.G);  // the exchange slots live in G's place
         if (launch_fill_u32(status, kStatusBytes / sizeof(unsigned), 0u, st) != hipSuccess ||
-            launch_fill_u32(reinterpret_cast<unsigned *>(xbuf), used_words * 2, 0u, st) != hipSuccess)
+            launch_fill_u32(xw, used_words, 0u, st) != hipSuccess)
             return LSTM_ERR_LAUNCH;
-        ProjArgs pa{};
-        pa.X = x;
-        pa.G = G;
-        pa.M = T * B;
-        pa.N = 4 * p->H;
-        pa.K = p->I;
-        pa.ldx = p->I;
-        pa.D = 1;
-        pa.W[0] = weights[0];
-        pa.b_ih[0] = p->has_bias ? weights[2] : nullptr;
-        pa.b_hh[0] = p->has_bias ? weights[3] : nullptr;
-        int span = span_begin(p, st, 0);
-        if (launch_proj(pa, p->dtype, p->proj_tile, st) != hipSuccess) return LSTM_ERR_LAUNCH;
-        span_end(p, span, st, 1);
-
-        PipeArgs qa{};
+        WaveArgs qa{};
         size_t off_words = 0;
         for (int l = 0; l < p->L; ++l) {
             const void *const *w = weights + (size_t)l * per;
+            qa.wih[l] = w[0];
             qa.whh[l] = w[1];
-            qa.wih[l] = l > 0 ? w[0] : nullptr;
-            qa.b_ih[l] = (l > 0 && p->has_bias) ? w[2] : nullptr;
-            qa.b_hh[l] = (l > 0 && p->has_bias) ? w[3] : nullptr;
-            qa.xslots[l] = l + 1 < p->L ? T : 2;
-            qa.xbuf[l] = xbuf + off_words;
-            off_words += slot_words * (size_t)qa.xslots[l];
-            qa.tag_base[l] = (unsigned)l * (unsigned)(T + 1);
-            qa.kchp[l] = ps.kchp[l];
-            qa.nbatch[l] = ps.nbatch[l];
+            qa.b_ih[l] = p->has_bias ? w[2] : nullptr;
+            qa.b_hh[l] = p->has_bias ? w[3] : nullptr;
+            qa.xbuf[l] = xw + off_words;
+            off_words += slot_words * (l + 1 < p->L ? (size_t)T : 2);
         }
-        qa.G = G;
+        qa.x = x;
         qa.h0 = h0;
         qa.c0 = c0;
         qa.Y = y;
@@ -953,18 +923,26 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         qa.T = T;
         qa.B = B;
         qa.H = p->H;
-        qa.P = ps.P;
-        qa.BG = ps.BG;
-        qa.NGB = ps.NGB;
-        qa.kch = ps.geom.kch;
-        qa.kchp_max = ps.geom.kchp;
+        qa.I = p->I;
+        qa.P = wsch.P;
+        qa.BG = wsch.BG;
+        qa.NGB = wsch.NGB;
+        qa.kch = (p->H + (p->dtype == LSTM_BF16 ? 31 : 15)) / (p->dtype == LSTM_BF16 ? 32 : 16);
+        qa.ncx0 = wsch.ncx0;
+        qa.map_xcd = wsch.map_xcd;
         qa.poll_sleep = p->poll_sleep;
-        qa.vec = (p->H % per16p == 0) && (!h0 || (uintptr_t)h0 % 16 == 0);
+        qa.pace = (int)((long long)(p->read_pace_ns >= 0 ? p->read_pace_ns : 375) * di.wall_khz / 1000000);
+        const int per16w = p->dtype == LSTM_BF16 ? 8 : 4;
+        // 16-byte fragment loads of W and h0 rows; x rows go through a buffer resource
+        bool vec = (p->H % per16w == 0) && (p->I % per16w == 0) && (!h0 || (uintptr_t)h0 % 16 == 0) &&
+                   (uintptr_t)x % 16 == 0;
         for (int l = 0; l < p->L; ++l)
-            qa.vec = qa.vec && (uintptr_t)qa.whh[l] % 16 == 0 && (!qa.wih[l] || (uintptr_t)qa.wih[l] % 16 == 0);
+            vec = vec && (uintptr_t)qa.whh[l] % 16 == 0 && (uintptr_t)qa.wih[l] % 16 == 0;
+        qa.vec = vec ? 1 : 0;
         qa.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
-        span = span_begin(p, st, 1);
-        if (launch_pipe(qa, ps.tile, ps.geom.smem, p->dtype, st) == hipSuccess) {
+        const int span = span_begin(p, st, 1);
+        // x's fragment loads need 16-byte rows: otherwise the layer-by-layer path
+        if (vec && (size_t)B * p->I * es < ((size_t)1 << 31) && launch_wave(qa, wsch.NT, p->dtype, st) == hipSuccess) {
             span_end(p, span, st, 1);
             if (p->timing) p->acc.calls += 1;
             return LSTM_OK;

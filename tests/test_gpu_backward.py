@@ -76,8 +76,11 @@ def test_backward_matches_oracle(spec):
     h0 = to_dev(inp.h0, bf, dev)
     c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
     y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
-    plain, _ = run_gpu(inp)
-    np.testing.assert_array_equal(y.float().cpu().numpy(), plain[0])  # saving activations changes nothing
+    # saving activations changes nothing: the training forward equals the
+    # layer-by-layer inference forward bit for bit (the layer wavefront, the
+    # inference default for unidirectional stacks, sums in another order)
+    plain, _ = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 0})
+    np.testing.assert_array_equal(y.float().cpu().numpy(), plain[0])
     dy_d = to_dev(dy_b if bf else dy, bf, dev)
     dhn_d = to_dev(dhn_b if bf else dhn, bf, dev)
     dcn_d = torch.from_numpy(dcn).to(dev)
@@ -220,7 +223,8 @@ def test_backward_with_lengths_matches_oracle(spec, mode, rec):
         dy_b, dhn_b = f32_to_bf16_bits(dy), f32_to_bf16_bits(dhn)
         dy, dhn = bf16_bits_to_f32(dy_b), bf16_bits_to_f32(dhn_b)
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
-                 dtype=spec.dtype, recurrence=pkg.LSTM_REC_GEMM if rec == "gemm" else pkg.LSTM_REC_AUTO)
+                 dtype=spec.dtype, recurrence=pkg.LSTM_REC_GEMM if rec == "gemm" else pkg.LSTM_REC_AUTO,
+                 options={pkg.LSTM_OPT_LAYER_PIPE: 0})  # the training forward runs layer by layer
     x = to_dev(inp.x, bf, dev)
     w = [to_dev(p, bf, dev) for p in inp.params]
     h0 = to_dev(inp.h0, bf, dev)

@@ -83,22 +83,23 @@ def test_gemm_step_blocks(spec):
 
 @pytest.mark.parametrize("spec", [
     Spec(24, 64, 2, False, 9, 40, "f32", 501, "normal0.1"),     # two layers, two batch groups
-    Spec(33, 52, 3, False, 7, 19, "f32", 502, "zeros"),         # three layers, ragged H (partial unit slice)
+    Spec(32, 52, 3, False, 7, 19, "f32", 502, "zeros"),         # three layers, ragged H (partial unit slice)
     Spec(40, 96, 4, False, 5, 70, "bf16", 503, "normal0.1"),    # four layers, ragged batch groups
     Spec(16, 40, 2, False, 6, 3, "bf16", 504, "normal0.1", has_bias=False),
     Spec(8, 16, 2, False, 1, 1, "f32", 505, "normal0.1"),       # one step, one row
 ], ids=_id)
-def test_layer_pipeline(spec):
-    """All layers of a unidirectional stack in one pipelined launch
-    (k_rec_pipe), against the oracle and against the layer-by-layer path."""
-    print(f"case {_id(spec)} layer pipe", flush=True)
+def test_layer_wavefront(spec):
+    """All layers of a unidirectional stack in one launch, layer l consuming
+    layer l-1's h_t as it is produced (k_rec_wave), against the oracle and
+    against the layer-by-layer path."""
+    print(f"case {_id(spec)} layer wavefront", flush=True)
     inp = make_inputs(spec)
     ref = run_oracle(inp)
     got, m = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 1})
-    assert "layer-pipe" in m.describe(spec.T, spec.B)
-    assert_parity(got, ref, spec.dtype, "layer pipe")
-    seq, m2 = run_gpu(inp)
-    assert "layer-pipe" not in m2.describe(spec.T, spec.B)
+    assert "wavefront" in m.describe(spec.T, spec.B)
+    assert_parity(got, ref, spec.dtype, "wavefront")
+    seq, m2 = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 0})
+    assert "wavefront" not in m2.describe(spec.T, spec.B)
     assert_parity(seq, ref, spec.dtype, "layer by layer")
 
 
@@ -379,8 +380,12 @@ def test_full_l2_in256_h512_b64_f32_hoisted_projection_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [5, 40], options={pkg.LSTM_OPT_FUSE_INPUT: 0})
 
 
-def test_full_l2_in256_h512_b64_f32_layer_pipeline_sampled_rows():
+def test_full_l2_in256_h512_b64_f32_wavefront_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [1, 32, 62], options={pkg.LSTM_OPT_LAYER_PIPE: 1})
+
+
+def test_full_l2_in256_h512_b64_f32_layer_by_layer_sampled_rows():
+    _full("l2_in256_h512_t128_b64_f32", [2, 33, 61], options={pkg.LSTM_OPT_LAYER_PIPE: 0})
 
 
 def test_full_l2_in256_h512_b64_f32_lengths_sampled_rows():
