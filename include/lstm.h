@@ -118,6 +118,10 @@ typedef enum {
     LSTM_OPT_FUSE_INPUT = 11, /* 1 (default): a layer whose recurrence runs as one persistent launch and
                                 whose W_ih share fits in registers computes x_t W_ih^T + b_ih + b_hh inside
                                 that launch (no projection GEMM, G unused); 0: always hoist the projection */
+    LSTM_OPT_SMALL_BATCH = 13, /* 1 (default): an LSTM layer with B <= 16 whose W_hh fits the registers of
+                                one XCD's 32 CUs (H <= 1024 bf16 / 512 fp32, whole 16-byte rows) runs each
+                                direction's recurrence on one XCD, after a hoisted projection; 0: the
+                                general recurrence (time-major inference only, as the wavefront) */
     LSTM_OPT_BATCH_FIRST = 12 /* 0 (default): x is [T, B, input_size] and y is [T, B, D*H]; 1: x is
                                 [B, T, input_size] and y is [B, T, D*H] ("batch_first" of the trace page's
                                 op signature, Step 3).  h0, c0, h_n, c_n stay [L*D, B, H].  A layout

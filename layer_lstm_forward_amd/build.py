@@ -13,7 +13,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["lstm_api.cpp", "kernels.hip", "rec_f32.hip", "rec_bf16.hip", "rec_bf16_wide.hip", "backward.hip",
-           "pack.hip", "noalloc.hip", "rec_wave.hip"]
+           "pack.hip", "noalloc.hip", "rec_wave.hip", "rec_xcd.hip"]
 # Packed-fp32 VALU ops stay off: the device code uses plain fp32 arithmetic.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

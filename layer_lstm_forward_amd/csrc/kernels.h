@@ -101,6 +101,15 @@ struct WaveArgs {
     int poll_sleep, pace, vec;
     long long timeout_ticks;
 };
+// Small-batch recurrence (rec_xcd.hip): one layer, B <= 16 rows, direction d's
+// 32-unit workgroups on XCD d (a launch of 8 P workgroups of 512 threads, id
+// % 8 = XCD); hoisted projection G; W_hh in registers.  Shapes: K <= 8 waves
+// x 4 chunks (H <= 1024 bf16 / 512 fp32), at most 32 workgroups per direction.
+bool xcd_shape_ok(int H, int B, int D, int dtype);
+int xcd_workgroups(int H);
+hipError_t xcd_max_coresident(int dtype, int *blocks_per_cu);
+hipError_t launch_xcd(const RecArgs &a, int dtype, hipStream_t s);
+
 // The wavefront applies when W_hh's K fits 4 waves x 8 chunks, layer 0's
 // input width fits 8 chunks per wave (ncx0: its chunks per wave), and H and
 // the input width are multiples of 16 bytes.

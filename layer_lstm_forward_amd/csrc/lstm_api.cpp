@@ -28,6 +28,7 @@ struct lstm_plan {
     int layer_pipe;    // 1 (default): run a unidirectional stack's layers in one wavefront launch when it fits
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
+    int small_batch;   // 1: B <= 16 layers run each direction's recurrence on one XCD (rec_xcd.hip)
     int mode;          // LSTM_MODE_*
     int NG;            // gate blocks of H rows: 4 (LSTM), 3 (GRU), 1 (RNN)
     // training dropout between layers (lstm_set_dropout)
@@ -486,6 +487,21 @@ bool choose_wave(const lstm_plan *p, int B, int dev, WaveSched *out) {
     return false;
 }
 
+// The small-batch recurrence (rec_xcd.hip): time-major LSTM inference with
+// B <= 16 whose W_hh fits one XCD's registers, all its workgroups co-resident.
+bool use_xcd(const lstm_plan *p, int B, int dev) {
+    if (!p->small_batch || p->mode != LSTM_MODE_LSTM || p->batch_first ||
+        !(p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT) || p->rec_tile != 0 ||
+        !xcd_shape_ok(p->H, B, p->D, p->dtype))
+        return false;
+    const DevInfo di = dev_info(dev);
+    int bpc = 0;
+    const bool ok = di.ok && xcd_max_coresident(p->dtype, &bpc) == hipSuccess && bpc > 0 &&
+                    (long long)bpc * di.cus >= 8LL * xcd_workgroups(p->H) && di.cus >= 256;
+    (void)hipGetLastError();
+    return ok;
+}
+
 hipEvent_t take_event(lstm_plan *p) {
     if (!p->pool.empty()) {
         hipEvent_t e = p->pool.back();
@@ -602,6 +618,7 @@ lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidd
     p->layer_pipe = 1;
     p->fuse_input = 1;
     p->batch_first = 0;
+    p->small_batch = 1;
     p->mode = mode;
     p->NG = mode == LSTM_MODE_LSTM ? 4 : mode == LSTM_MODE_GRU ? 3 : 1;
     p->dropout = 0.0;
@@ -692,6 +709,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
             p->batch_first = value;
             return LSTM_OK;
+        case LSTM_OPT_SMALL_BATCH:
+            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            p->small_batch = value;
+            return LSTM_OK;
         case LSTM_OPT_READ_PACE:
             if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
             p->read_pace_ns = value;
@@ -760,6 +781,12 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
                       "map_xcd=%d w_hh=regs xproj=%s",
                       dt, ws.NT, ws.U, ws.P, ws.BG, ws.NGB, p->L, ws.wgs, ws.map_xcd,
                       p->L == 2 ? "fused,fused" : p->L == 3 ? "fused,fused,fused" : "fused,fused,fused,fused");
+        return LSTM_OK;
+    }
+    if (!mode_persistent && use_xcd(p, B, dev)) {
+        std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_xcd<%s> mode=small-batch units=32 workgroups=%d per direction "
+                      "(one XCD each) w_hh=regs xproj=hoisted",
+                      proj, dt, dt, xcd_workgroups(p->H));
         return LSTM_OK;
     }
     if (!s.persistent && gemm_step_shape_ok(p)) {
@@ -954,6 +981,8 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     if (launch_fill_u32(status, lay.sync_bytes / sizeof(unsigned), 0u, st) != hipSuccess) return LSTM_ERR_LAUNCH;
 
     const int per16 = p->dtype == LSTM_BF16 ? 8 : 4;
+    // small batches: each direction's recurrence on one XCD, after a hoisted projection
+    const bool small = !padded && !dlen && !reserve && use_xcd(p, B, dev);
     // Exchange tags are one bit per word: bit p of xpar is the parity of the
     // writes exchange buffer p has received so far in this call.  A k_rec
     // layer writes buffer s & 1 at every step s < T - 1.
@@ -973,7 +1002,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         const void *wih[2] = {nullptr, nullptr};
         for (int d = 0; d < p->D; ++d) wih[d] = wts[(size_t)(l * p->D + d) * wper];
         // the GRU needs x W_in^T apart from W_hn h (reset product): never fused
-        int ncx = p->mode == LSTM_MODE_GRU ? 0 : fused_chunks(p, sch, T, B, in_l, X, wih, di);
+        int ncx = p->mode == LSTM_MODE_GRU || small ? 0 : fused_chunks(p, sch, T, B, in_l, X, wih, di);
 
         // hoisted projection G = X W_ih^T + b_ih + b_hh (skipped when fused)
         auto project = [&]() -> bool {
@@ -1050,6 +1079,17 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         for (int d = 0; d < p->D; ++d) ra.vec = ra.vec && ((uintptr_t)ra.whh[d] % 16 == 0);
         ra.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
         int span = span_begin(p, st, 1);
+        if (small) {
+            RecArgs xa = ra;
+            xa.P = xcd_workgroups(p->H);
+            xa.pace = (int)((long long)(p->read_pace_ns >= 0 ? p->read_pace_ns : 200) * di.wall_khz / 1000000);
+            if (launch_xcd(xa, p->dtype, st) == hipSuccess) {
+                span_end(p, span, st, 1);
+                xpar ^= layer_writes;
+                continue;
+            }
+            (void)hipGetLastError();  // refused (nothing ran): the general recurrence below
+        }
         bool stepped = !sch.persistent;
         if (sch.persistent) {
             ra.s_begin = 0;

@@ -124,6 +124,28 @@ def test_fused_input_projection(spec):
     assert_parity(hoisted, ref, spec.dtype, "hoisted")
 
 
+@pytest.mark.parametrize("spec", [
+    Spec(64, 1024, 1, False, 9, 1, "bf16", 651, "zeros"),        # the latency-bound workload's shape, short
+    Spec(64, 1024, 1, True, 7, 4, "bf16", 652, "normal0.1"),     # both directions: one XCD each
+    Spec(40, 40, 2, False, 6, 16, "bf16", 653, "normal0.1"),     # partial unit slice, a full 16-row tile
+    Spec(24, 512, 2, True, 5, 3, "f32", 654, "normal0.1"),       # fp32 at its widest K
+    Spec(8, 16, 1, False, 5, 1, "f32", 655, "zeros"),            # one workgroup per direction
+], ids=_id)
+def test_small_batch_one_xcd(spec):
+    """Batches of at most 16 rows: each direction's recurrence on the 32 CUs of
+    one XCD (k_rec_xcd), against the oracle and against the general path."""
+    print(f"case {_id(spec)} small batch", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    lbl = {pkg.LSTM_OPT_LAYER_PIPE: 0}  # a unidirectional stack would otherwise take the layer wavefront
+    got, m = run_gpu(inp, options=lbl)
+    assert "small-batch" in m.describe(spec.T, spec.B)
+    assert_parity(got, ref, spec.dtype, "one XCD")
+    gen, m2 = run_gpu(inp, options={**lbl, pkg.LSTM_OPT_SMALL_BATCH: 0})
+    assert "small-batch" not in m2.describe(spec.T, spec.B)
+    assert_parity(gen, ref, spec.dtype, "general")
+
+
 LENGTH_SPECS = [
     Spec(24, 64, 2, False, 9, 40, "f32", 701, "normal0.1"),      # fused projection
     Spec(37, 52, 2, True, 9, 19, "f32", 702, "normal0.1"),       # ragged H and I, both directions
