@@ -162,19 +162,20 @@ def summarize_profile(path, command):
 
 
 def kernel_source_hash(kernel):
-    """sha256 of the sources of `kernel` (its .hip file and the shared device
-    headers; "a+b": of each kernel's); a stored counter profile is valid only
-    for the sources it was taken from."""
+    """sha256 of the sources of `kernel` (every source file that defines or
+    instantiates it, and the shared device headers; "a+b": of each kernel's);
+    a stored counter profile is valid only for the sources it was taken from."""
     import hashlib
     import re as _re
     csrc = os.path.join(ROOT, "layer_lstm_forward_amd", "csrc")
+    sources = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")) and f not in ("device.h", "kernels.h"))
     files = set()
     for k in kernel.split("+"):
-        for name in ("backward.hip", "kernels.hip"):
+        pat = _re.compile(r"\b" + _re.escape(k.strip()) + r"\s*[(<]")
+        for name in sources:
             with open(os.path.join(csrc, name)) as fh:
-                if _re.search(r"\b" + _re.escape(k.strip()) + r"\s*\(", fh.read()):
+                if pat.search(fh.read()):
                     files.add(name)
-                    break
     h = hashlib.sha256()
     for f in sorted(files) + ["device.h", "kernels.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -232,6 +233,52 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, wo
     return "\n".join(lines)
 
 
+def counter_summary(kernel, workload, csv_paths, command):
+    """Per-dispatch averages of every counter in rocprofv3 counter_collection
+    csv files for the dispatches of `kernel`, with the ratios read from them:
+      mfma_flops        SQ_INSTS_VALU_MFMA_MOPS_{BF,F} x 512 (matrix-core
+                        flops the dispatch executed), beside the algorithm's
+      mfma_busy_per_cu  SQ_VALU_MFMA_BUSY_CYCLES / (dispatch cycles at
+                        2.4 GHz x 256 CUs)
+      lds_conflict      SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      wait_any          SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES"""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(list)
+    durs = {}
+    name = None
+    for path in csv_paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if kernel not in row["Kernel_Name"]:
+                    continue
+                name = row["Kernel_Name"]
+                vals[row["Counter_Name"]].append(float(row["Counter_Value"]))
+                if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                    durs[(path, row["Dispatch_Id"])] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    if name is None:
+        raise SystemExit(f"no dispatch of {kernel} in {csv_paths}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    lines = ["# rocprofv3 counters, averages per dispatch (one dispatch = one launch)",
+             f"# command: {command}", f"# workload: {workload}", f"# kernel: {name[:160]}",
+             f"kernel_source_sha256: {kernel_source_hash(kernel)}"]
+    for k in sorted(avg):
+        lines.append(f"{k}: {avg[k]:.1f} (over {len(vals[k])} dispatches)")
+    dur_ns = sum(durs.values()) / len(durs) if durs else None
+    if dur_ns:
+        lines.append(f"dispatch_us_under_counters: {dur_ns / 1e3:.2f}")
+    mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F", 0.0)
+    if mops:
+        lines.append(f"mfma_flops: {mops * 512:.4g}")
+    if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        lines.append(f"mfma_busy_per_cu: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (dur_ns * 2.4 * 256):.4f}")
+    if avg.get("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"lds_conflict: {avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_LDS_IDX_ACTIVE']:.4f}")
+    if avg.get("SQ_WAVE_CYCLES"):
+        lines.append(f"wait_any: {avg.get('SQ_WAIT_INST_ANY', 0.0) / avg['SQ_WAVE_CYCLES']:.4f}")
+    return "\n".join(lines)
+
+
 def stored_traffic(kernel, workload):
     """traffic_bytes_per_launch from profiles/<kernel>_<workload>_hbm_counters.txt
     if it was taken from the current kernel sources, else None."""
@@ -267,6 +314,10 @@ def main():
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         print(pmc_summary(*sys.argv[2:8], " ".join(sys.argv[8:])))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--counter-summary":
+        # --counter-summary <kernel> <workload> <csv>[,<csv>...] <command text>
+        print(counter_summary(sys.argv[2], sys.argv[3], sys.argv[4].split(","), " ".join(sys.argv[5:])))
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
         copy_calibration(int(sys.argv[2]) if len(sys.argv) > 2 else 256 << 20, 5)
@@ -463,7 +514,7 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
       k_proj*      x [T*B, in_l] + W_ih [D*4H, in_l] read, G [T*B, D*4H] fp32
                    written (mean over layers)
       k_rec        per layer: W_hh [D*4H, H], y [T, B, D*H] written, h0/c0 and
-                   h_n/c_n, and either G read (hoisted) or x and W_ih read
+      k_rec_xcd    h_n/c_n, and either G read (hoisted) or x and W_ih read
                    (fused) (mean over layers)
       k_rec_step   one step: W_hh, G [B, D*4H] fp32, h_{t-1} [B, D*H] read, c
                    read and written, y [B, D*H] written
@@ -482,7 +533,7 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
                 + T * B * D * H * s + L * 2 * D * B * H * (s + 4))
     if kname == "k_rec_step" or (kname == "k_rec" and stepping):
         return D * G4 * H * s + B * D * G4 * 4 + B * D * H * s + 2 * B * D * H * 4 + B * D * H * s
-    if kname == "k_rec":
+    if kname in ("k_rec", "k_rec_xcd"):
         tot = 0.0
         for l in range(L):
             io = (T * B * spec.layer_input(l) * s + D * G4 * spec.layer_input(l) * s
