@@ -236,10 +236,10 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, wo
 def counter_summary(kernel, workload, csv_paths, command):
     """Per-dispatch averages of every counter in rocprofv3 counter_collection
     csv files for the dispatches of `kernel`, with the ratios read from them:
-      mfma_flops        SQ_INSTS_VALU_MFMA_MOPS_{BF,F} x 512 (matrix-core
-                        flops the dispatch executed), beside the algorithm's
-      mfma_busy_per_cu  SQ_VALU_MFMA_BUSY_CYCLES / (dispatch cycles at
-                        2.4 GHz x 256 CUs)
+      mfma_busy         SQ_VALU_MFMA_BUSY_CYCLES / (dispatch cycles at
+                        2.4 GHz x 1024 SIMDs): the matrix pipes' busy fraction
+                        (the counter adds each MFMA instruction's issue cycles,
+                        so this equals achieved / peak matrix flops)
       lds_conflict      SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
       wait_any          SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES"""
     import csv
@@ -261,17 +261,14 @@ def counter_summary(kernel, workload, csv_paths, command):
     avg = {k: sum(v) / len(v) for k, v in vals.items()}
     lines = ["# rocprofv3 counters, averages per dispatch (one dispatch = one launch)",
              f"# command: {command}", f"# workload: {workload}", f"# kernel: {name[:160]}",
-             f"kernel_source_sha256: {kernel_source_hash(kernel)}"]
+             f"kernel_source_sha256: {kernel_source_hash(kernel.rstrip('<'))}"]
     for k in sorted(avg):
         lines.append(f"{k}: {avg[k]:.1f} (over {len(vals[k])} dispatches)")
     dur_ns = sum(durs.values()) / len(durs) if durs else None
     if dur_ns:
         lines.append(f"dispatch_us_under_counters: {dur_ns / 1e3:.2f}")
-    mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F", 0.0)
-    if mops:
-        lines.append(f"mfma_flops: {mops * 512:.4g}")
     if dur_ns and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-        lines.append(f"mfma_busy_per_cu: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (dur_ns * 2.4 * 256):.4f}")
+        lines.append(f"mfma_busy: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (dur_ns * 2.4 * 1024):.4f}")
     if avg.get("SQ_LDS_IDX_ACTIVE"):
         lines.append(f"lds_conflict: {avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_LDS_IDX_ACTIVE']:.4f}")
     if avg.get("SQ_WAVE_CYCLES"):
