@@ -327,7 +327,10 @@ def main():
     ap.add_argument("--recurrence", choices=["auto", "step", "persistent"], default="auto")
     ap.add_argument("--rec-tile", type=int, default=0)
     ap.add_argument("--proj-tile", type=int, default=0, help="LSTM_OPT_PROJ_TILE (0 automatic)")
-    ap.add_argument("--layer-pipe", action="store_true", help="LSTM_OPT_LAYER_PIPE = 1")
+    ap.add_argument("--layer-pipe", type=int, choices=[0, 1], default=None,
+                    help="LSTM_OPT_LAYER_PIPE (default: the library's, the layer wavefront where it applies)")
+    ap.add_argument("--small-batch", type=int, choices=[0, 1], default=None,
+                    help="LSTM_OPT_SMALL_BATCH (default: the library's, one XCD per direction where it applies)")
     ap.add_argument("--read-pace", type=int, default=-1, help="LSTM_OPT_READ_PACE in ns (-1: the default)")
     ap.add_argument("--partial-buffers", type=int, default=0)
     ap.add_argument("--poll-sleep", type=int, default=-1)
@@ -387,8 +390,10 @@ def main():
         opts[pkg.LSTM_OPT_POLL_SLEEP] = args.poll_sleep
     if args.proj_tile:
         opts[pkg.LSTM_OPT_PROJ_TILE] = args.proj_tile
-    if args.layer_pipe:
-        opts[pkg.LSTM_OPT_LAYER_PIPE] = 1
+    if args.layer_pipe is not None:
+        opts[pkg.LSTM_OPT_LAYER_PIPE] = args.layer_pipe
+    if args.small_batch is not None:
+        opts[pkg.LSTM_OPT_SMALL_BATCH] = args.small_batch
     if args.read_pace >= 0:
         opts[pkg.LSTM_OPT_READ_PACE] = args.read_pace
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
