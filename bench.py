@@ -331,6 +331,9 @@ def main():
                     help="LSTM_OPT_LAYER_PIPE (default: the library's, the layer wavefront where it applies)")
     ap.add_argument("--small-batch", type=int, choices=[0, 1], default=None,
                     help="LSTM_OPT_SMALL_BATCH (default: the library's, one XCD per direction where it applies)")
+    ap.add_argument("--resident", type=int, choices=[0, 1, 2], default=None,
+                    help="LSTM_OPT_RESIDENT (default: the library's, W_hh held across the chip where a layer "
+                         "would otherwise step)")
     ap.add_argument("--read-pace", type=int, default=-1, help="LSTM_OPT_READ_PACE in ns (-1: the default)")
     ap.add_argument("--partial-buffers", type=int, default=0)
     ap.add_argument("--poll-sleep", type=int, default=-1)
@@ -394,6 +397,8 @@ def main():
         opts[pkg.LSTM_OPT_LAYER_PIPE] = args.layer_pipe
     if args.small_batch is not None:
         opts[pkg.LSTM_OPT_SMALL_BATCH] = args.small_batch
+    if args.resident is not None:
+        opts[pkg.LSTM_OPT_RESIDENT] = args.resident
     if args.read_pace >= 0:
         opts[pkg.LSTM_OPT_READ_PACE] = args.read_pace
     m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, bias=spec.has_bias,
@@ -517,7 +522,7 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
                    written (mean over layers)
       k_rec        per layer: W_hh [D*4H, H], y [T, B, D*H] written, h0/c0 and
       k_rec_xcd    h_n/c_n, and either G read (hoisted) or x and W_ih read
-                   (fused) (mean over layers)
+      k_rec_res    (fused) (mean over layers)
       k_rec_step   one step: W_hh, G [B, D*4H] fp32, h_{t-1} [B, D*H] read, c
                    read and written, y [B, D*H] written
       k_rec_wave   the whole stack: every layer's W_ih and W_hh, x, the top
@@ -535,7 +540,7 @@ def alg_bytes_per_launch(spec, kname, desc, stepping):
                 + T * B * D * H * s + L * 2 * D * B * H * (s + 4))
     if kname == "k_rec_step" or (kname == "k_rec" and stepping):
         return D * G4 * H * s + B * D * G4 * 4 + B * D * H * s + 2 * B * D * H * 4 + B * D * H * s
-    if kname in ("k_rec", "k_rec_xcd"):
+    if kname in ("k_rec", "k_rec_xcd", "k_rec_res"):
         tot = 0.0
         for l in range(L):
             io = (T * B * spec.layer_input(l) * s + D * G4 * spec.layer_input(l) * s

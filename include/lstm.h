@@ -122,6 +122,12 @@ typedef enum {
                                 one XCD's 32 CUs (H <= 1024 bf16 / 512 fp32, whole 16-byte rows) runs each
                                 direction's recurrence on one XCD, after a hoisted projection; 0: the
                                 general recurrence (time-major inference only, as the wavefront) */
+    LSTM_OPT_RESIDENT = 14,    /* 1 (default): a bf16 LSTM layer whose W_hh is too large for the per-layer
+                                persistent recurrence (H one of 256, 512, 1024, 1536, 2048, and
+                                ceil(B/128)*D*H/16 workgroups fitting the chip at once) runs its recurrence
+                                in one launch that holds W_hh once across the chip and exchanges h through
+                                y; 2: whenever the shape allows it; 0: never (one launch per step).
+                                Time-major inference only, without per-row lengths */
     LSTM_OPT_BATCH_FIRST = 12 /* 0 (default): x is [T, B, input_size] and y is [T, B, D*H]; 1: x is
                                 [B, T, input_size] and y is [B, T, D*H] ("batch_first" of the trace page's
                                 op signature, Step 3).  h0, c0, h_n, c_n stay [L*D, B, H].  A layout

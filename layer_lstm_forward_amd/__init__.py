@@ -27,6 +27,7 @@ LSTM_OPT_LAYER_PIPE = 10
 LSTM_OPT_FUSE_INPUT = 11
 LSTM_OPT_BATCH_FIRST = 12
 LSTM_OPT_SMALL_BATCH = 13
+LSTM_OPT_RESIDENT = 14
 STATUS = {0: "LSTM_OK", -1: "LSTM_ERR_ARG", -2: "LSTM_ERR_SHAPE", -3: "LSTM_ERR_DTYPE",
           -4: "LSTM_ERR_DEVICE", -5: "LSTM_ERR_WORKSPACE", -6: "LSTM_ERR_LAUNCH",
           -7: "LSTM_ERR_UNSUPPORTED", -8: "LSTM_ERR_DEVICE_TIMEOUT"}

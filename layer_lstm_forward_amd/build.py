@@ -13,9 +13,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["lstm_api.cpp", "kernels.hip", "rec_f32.hip", "rec_bf16.hip", "rec_bf16_wide.hip", "backward.hip",
-           "pack.hip", "noalloc.hip", "rec_wave.hip", "rec_xcd.hip"]
+           "pack.hip", "noalloc.hip", "rec_wave.hip", "rec_xcd.hip",
+           "rec_res.hip"]
 # Packed-fp32 VALU ops stay off: the device code uses plain fp32 arithmetic.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags.  rec_res.hip keeps W_hh (up to 256 registers a wave) beside
+# its accumulators: with the accumulators in ordinary VGPRs the allocator puts
+# W_hh in the accumulation registers instead of spilling to scratch.
+SOURCE_FLAGS = {"rec_res.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -23,7 +28,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-           "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *lang, "-c", path, "-o", obj]
+           "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -110,6 +110,18 @@ int xcd_workgroups(int H);
 hipError_t xcd_max_coresident(int dtype, int *blocks_per_cu);
 hipError_t launch_xcd(const RecArgs &a, int dtype, hipStream_t s);
 
+// Large-batch recurrence with W_hh held once across the chip and h exchanged
+// through a two-slot ring of tagged words (rec_res.hip).  res_shape_ok:
+// bf16, H one of 256, 512, 1024, 1536, 2048, (ceil(B/128) * D) groups x H/16
+// unit slices <= cus workgroups; it returns the groups, the slices and
+// whether the XCD-aware order applies.  The launch takes NGB = groups,
+// P = slices, map_xcd as returned, and xbuf pointing at res_ring_bytes(H,
+// groups) zeroed bytes.
+bool res_shape_ok(int H, int B, int D, int dtype, int cus, int *groups, int *slices, int *map_xcd);
+size_t res_ring_bytes(int H, int groups);
+hipError_t res_max_coresident(int H, int *blocks_per_cu);
+hipError_t launch_res(const RecArgs &a, hipStream_t s);
+
 // The wavefront applies when W_hh's K fits 4 waves x 8 chunks, layer 0's
 // input width fits 8 chunks per wave (ncx0: its chunks per wave), and H and
 // the input width are multiples of 16 bytes.

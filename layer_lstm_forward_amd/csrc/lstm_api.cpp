@@ -29,6 +29,7 @@ struct lstm_plan {
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
     int small_batch;   // 1: B <= 16 layers run each direction's recurrence on one XCD (rec_xcd.hip)
+    int resident;      // 1: large-batch layers that would step hold W_hh once across the chip (rec_res.hip); 2: always
     int mode;          // LSTM_MODE_*
     int NG;            // gate blocks of H rows: 4 (LSTM), 3 (GRU), 1 (RNN)
     // training dropout between layers (lstm_set_dropout)
@@ -502,6 +503,22 @@ bool use_xcd(const lstm_plan *p, int B, int dev) {
     return ok;
 }
 
+// The large-batch resident recurrence (rec_res.hip): time-major bf16 LSTM
+// inference whose layer would otherwise step (option 1) or always when the
+// shape allows (option 2), every workgroup co-resident.
+bool use_res(const lstm_plan *p, int B, int dev, bool persistent, int *groups, int *slices, int *map_xcd) {
+    if (!p->resident || (p->resident == 1 && persistent) || p->mode != LSTM_MODE_LSTM || p->batch_first ||
+        !(p->rec_mode == LSTM_REC_AUTO || p->rec_mode == LSTM_REC_PERSISTENT) || p->rec_tile != 0)
+        return false;
+    const DevInfo di = dev_info(dev);
+    if (!di.ok || !res_shape_ok(p->H, B, p->D, p->dtype, di.cus, groups, slices, map_xcd)) return false;
+    int bpc = 0;
+    const bool ok = res_max_coresident(p->H, &bpc) == hipSuccess && bpc > 0 &&
+                    (long long)bpc * di.cus >= (long long)*groups * *slices;
+    (void)hipGetLastError();
+    return ok;
+}
+
 hipEvent_t take_event(lstm_plan *p) {
     if (!p->pool.empty()) {
         hipEvent_t e = p->pool.back();
@@ -619,6 +636,7 @@ lstm_status lstm_create_mode(lstm_plan **out, int mode, int input_size, int hidd
     p->fuse_input = 1;
     p->batch_first = 0;
     p->small_batch = 1;
+    p->resident = 1;
     p->mode = mode;
     p->NG = mode == LSTM_MODE_LSTM ? 4 : mode == LSTM_MODE_GRU ? 3 : 1;
     p->dropout = 0.0;
@@ -713,6 +731,10 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
             p->small_batch = value;
             return LSTM_OK;
+        case LSTM_OPT_RESIDENT:
+            if (value < 0 || value > 2) return LSTM_ERR_UNSUPPORTED;
+            p->resident = value;
+            return LSTM_OK;
         case LSTM_OPT_READ_PACE:
             if (value < 0 || value > 100000) return LSTM_ERR_UNSUPPORTED;
             p->read_pace_ns = value;
@@ -787,6 +809,13 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
         std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_xcd<%s> mode=small-batch units=32 workgroups=%d per direction "
                       "(one XCD each) w_hh=regs xproj=hoisted",
                       proj, dt, dt, xcd_workgroups(p->H));
+        return LSTM_OK;
+    }
+    int rg = 0, rs = 0, rmap = 0;
+    if (!mode_persistent && use_res(p, B, dev, s.persistent, &rg, &rs, &rmap)) {
+        std::snprintf(buf, len, "proj=%s<%s>; rec=k_rec_res<%s> mode=resident rows=128 units=16 workgroups=%d "
+                      "map_xcd=%d w_hh=regs h_via=ring xproj=hoisted",
+                      proj, dt, dt, rg * rs, rmap);
         return LSTM_OK;
     }
     if (!s.persistent && gemm_step_shape_ok(p)) {
@@ -983,6 +1012,10 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
     const int per16 = p->dtype == LSTM_BF16 ? 8 : 4;
     // small batches: each direction's recurrence on one XCD, after a hoisted projection
     const bool small = !padded && !dlen && !reserve && use_xcd(p, B, dev);
+    // large batches whose layers would step: W_hh held once across the chip, h through y
+    int res_groups = 0, res_slices = 0, res_map = 0;
+    const bool res = !small && !padded && !dlen && !reserve &&
+                     use_res(p, B, dev, sch.persistent, &res_groups, &res_slices, &res_map);
     // Exchange tags are one bit per word: bit p of xpar is the parity of the
     // writes exchange buffer p has received so far in this call.  A k_rec
     // layer writes buffer s & 1 at every step s < T - 1.
@@ -1002,7 +1035,13 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         const void *wih[2] = {nullptr, nullptr};
         for (int d = 0; d < p->D; ++d) wih[d] = wts[(size_t)(l * p->D + d) * wper];
         // the GRU needs x W_in^T apart from W_hn h (reset product): never fused
-        int ncx = p->mode == LSTM_MODE_GRU || small ? 0 : fused_chunks(p, sch, T, B, in_l, X, wih, di);
+        // (the resident recurrence reads G: the layer hoists its projection)
+        const bool res_layer = res && res_ring_bytes(p->H, res_groups) <= lay.sync_bytes - lay.xbuf &&
+                               (uintptr_t)Y % 16 == 0 &&
+                               (!h0 || ((uintptr_t)h0 + (size_t)l * state_elems * es) % 16 == 0) &&
+                               (uintptr_t)wts[(size_t)(l * p->D) * wper + 1] % 16 == 0 &&
+                               (p->D < 2 || (uintptr_t)wts[(size_t)(l * p->D + 1) * wper + 1] % 16 == 0);
+        int ncx = p->mode == LSTM_MODE_GRU || small || res_layer ? 0 : fused_chunks(p, sch, T, B, in_l, X, wih, di);
 
         // hoisted projection G = X W_ih^T + b_ih + b_hh (skipped when fused)
         auto project = [&]() -> bool {
@@ -1089,6 +1128,32 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
                 continue;
             }
             (void)hipGetLastError();  // refused (nothing ran): the general recurrence below
+        }
+        if (res_layer) {
+            // The kernel's ring lives in the exchange buffer and starts zeroed
+            // (tag 0).  The buffer is zeroed again after it, and the other
+            // kernels' tag sequence restarts (xpar = 0): every word is then tag 0.
+            RecArgs xa = ra;
+            xa.NGB = res_groups;
+            xa.P = res_slices;
+            xa.map_xcd = res_map;
+            unsigned *const xw = reinterpret_cast<unsigned *>(ws + lay.xbuf);
+            const size_t xwords = (lay.sync_bytes - lay.xbuf) / sizeof(unsigned);
+            if (launch_fill_u32(xw, xwords, 0u, st) != hipSuccess) {
+                (void)hipGetLastError();
+                return LSTM_ERR_LAUNCH;
+            }
+            const bool ran = launch_res(xa, st) == hipSuccess;
+            if (!ran) (void)hipGetLastError();  // refused (nothing ran): the general recurrence below
+            if (launch_fill_u32(xw, xwords, 0u, st) != hipSuccess) {
+                (void)hipGetLastError();
+                return LSTM_ERR_LAUNCH;
+            }
+            xpar = 0;
+            if (ran) {
+                span_end(p, span, st, 1);
+                continue;
+            }
         }
         bool stepped = !sch.persistent;
         if (sch.persistent) {

@@ -146,6 +146,53 @@ def test_small_batch_one_xcd(spec):
     assert_parity(gen, ref, spec.dtype, "general")
 
 
+RESIDENT_SPECS = [
+    Spec(40, 256, 2, False, 6, 130, "bf16", 801, "normal0.1"),   # 2 chunks a wave, ragged second row block, two layers
+    Spec(64, 512, 1, True, 5, 200, "bf16", 802, "normal0.1"),    # both directions, 4 row groups of 32 slices
+    Spec(32, 1024, 1, False, 4, 20, "bf16", 803, "zeros"),       # one partial row block
+    Spec(24, 1536, 1, True, 3, 40, "bf16", 805, "normal0.1"),    # 12 chunks a wave, 192 workgroups
+    Spec(16, 2048, 1, False, 3, 130, "bf16", 804, "normal0.1"),  # the H = 2048 shape: every CU, 16 chunks a wave
+]
+
+
+@pytest.mark.parametrize("spec", RESIDENT_SPECS, ids=_id)
+def test_resident_recurrence(spec):
+    """W_hh held once across the chip and h_{t-1} read back from y
+    (k_rec_res), forced on shapes that would otherwise run another
+    recurrence, against the oracle and against the per-step GEMM."""
+    print(f"case {_id(spec)} resident", flush=True)
+    inp = make_inputs(spec)
+    ref = run_oracle(inp)
+    opts = {pkg.LSTM_OPT_LAYER_PIPE: 0, pkg.LSTM_OPT_RESIDENT: 2}
+    got, m = run_gpu(inp, options=opts)
+    assert "resident" in m.describe(spec.T, spec.B)
+    assert_parity(got, ref, spec.dtype, "resident")
+    gem, m2 = run_gpu(inp, recurrence=pkg.LSTM_REC_GEMM, options={pkg.LSTM_OPT_RESIDENT: 0})
+    assert "resident" not in m2.describe(spec.T, spec.B)
+    assert_parity(gem, ref, spec.dtype, "gemm step")
+
+
+def test_resident_large_h0_and_saturation():
+    """The resident recurrence from a caller's h0 of magnitude up to ~10 (read
+    directly at the first step) and with every gate saturated (|h| = 1
+    exactly in y, the words the next step reads)."""
+    from layer_lstm_forward_amd.synth import bf16_bits_to_f32
+    spec = Spec(32, 256, 1, True, 12, 150, "bf16", 806, "normal0.1")
+    opts = {pkg.LSTM_OPT_LAYER_PIPE: 0, pkg.LSTM_OPT_RESIDENT: 2}
+    print("case resident large h0", flush=True)
+    inp = make_inputs(spec)
+    inp.h0 = _scaled(inp.h0, 40.0, True)
+    assert np.max(np.abs(bf16_bits_to_f32(inp.h0))) >= 2.0
+    got, m = run_gpu(inp, options=opts)
+    assert "resident" in m.describe(spec.T, spec.B)
+    assert_parity(got, run_oracle(inp), "bf16", "resident, large h0")
+    print("case resident saturated", flush=True)
+    inp = _saturating(spec)
+    got, m = run_gpu(inp, options=opts)
+    assert np.mean(np.abs(got[0]) == 1.0) > 0.1, "the case should drive h to +-1 exactly"
+    assert_parity(got, run_oracle(inp), "bf16", "resident, saturated")
+
+
 LENGTH_SPECS = [
     Spec(24, 64, 2, False, 9, 40, "f32", 701, "normal0.1"),      # fused projection
     Spec(37, 52, 2, True, 9, 19, "f32", 702, "normal0.1"),       # ragged H and I, both directions
