@@ -77,9 +77,12 @@ def test_backward_matches_oracle(spec):
     c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
     y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
     # saving activations changes nothing: the training forward equals the
-    # layer-by-layer inference forward bit for bit (the layer wavefront, the
-    # inference default for unidirectional stacks, sums in another order)
-    plain, _ = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 0})
+    # layer-by-layer inference forward of the per-layer kernels bit for bit
+    # (the layer wavefront, the one-XCD small-batch kernel and the resident
+    # large-batch kernel, inference defaults where they apply, sum in other
+    # orders)
+    plain, _ = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 0, pkg.LSTM_OPT_SMALL_BATCH: 0,
+                                     pkg.LSTM_OPT_RESIDENT: 0})
     np.testing.assert_array_equal(y.float().cpu().numpy(), plain[0])
     dy_d = to_dev(dy_b if bf else dy, bf, dev)
     dhn_d = to_dev(dhn_b if bf else dhn, bf, dev)
