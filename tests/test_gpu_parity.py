@@ -157,8 +157,8 @@ RESIDENT_SPECS = [
 
 @pytest.mark.parametrize("spec", RESIDENT_SPECS, ids=_id)
 def test_resident_recurrence(spec):
-    """W_hh held once across the chip and h_{t-1} read back from y
-    (k_rec_res), forced on shapes that would otherwise run another
+    """W_hh held once across the chip and h_{t-1} exchanged through a ring
+    of step-tagged words (k_rec_res), forced on shapes that would otherwise run another
     recurrence, against the oracle and against the per-step GEMM."""
     print(f"case {_id(spec)} resident", flush=True)
     inp = make_inputs(spec)
