@@ -225,25 +225,25 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
         return true;
     };
 
+    if (l > 0) issue_words(slot_words(l - 1, 0), cx0, kch, xin);  // step 0's input (checked in the step)
+
     for (int s = 0; s < T; ++s) {
         f32x4 acc[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         bool wave_ok = true;
 
-        // The input product first: x_t (layer 0, already loaded) or layer
-        // l-1's h_t (usually already there: the layer below runs ahead).  Its
-        // W_ih fragments come from LDS one chunk ahead of the products (the
-        // scheduling barriers keep the compiler from fetching them all at
-        // once: registers are scarce with two workgroups per CU).  It also
-        // gives the others' h_{t-1} time to arrive: their reads are issued
-        // after it (issued before it, they reached memory ahead of the data
-        // and the step got slower).
+        // The input product first: x_t (layer 0) or layer l-1's h_t, both
+        // read a step ahead (below).  Layer l-1's words are usually current
+        // by now, since the layer below runs ahead; they are checked here and
+        // re-read if not.  The W_ih fragments come from LDS one chunk ahead
+        // of the products (the scheduling barriers keep the compiler from
+        // fetching them all at once: registers are scarce with two
+        // workgroups per CU).  The product also gives the others' h_{t-1}
+        // time to arrive: their reads are issued after it (issued before it,
+        // they reached memory ahead of the data and the step got slower).
         const uint32_t *xsrc = l > 0 ? slot_words(l - 1, s) : nullptr;
-        if (l > 0) {
-            issue_words(xsrc, cx0, kch, xin);
-            wave_ok = wait_words(xsrc, cx0, kch, 1u, xin);
-        }
+        if (l > 0) wave_ok = wait_words(xsrc, cx0, kch, 1u, xin);
         if (wave_ok) {
             u32x4 wcur[NT], wnext[NT];
 #pragma unroll
@@ -262,7 +262,15 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (l == 0) load_x(s + 1);  // consumed: fetch the next step's x while this one runs
+        // consumed: fetch the next step's input while this one runs
+        if (l == 0) load_x(s + 1);
+        else if (s + 1 < T) issue_words(slot_words(l - 1, s + 1), cx0, kch, xin);
+
+        // From here to the publication of h_t the wave is on its layer's
+        // critical path (every workgroup of the team waits for h_t): it takes
+        // the matrix cores ahead of the other layer's input product, which
+        // can run at any time before that layer's own h arrives.
+        __builtin_amdgcn_s_setprio(2);
 
         // The hidden product: h_{t-1} (h0 at the first step), read once the
         // pace has passed since this workgroup's last publication.
@@ -343,6 +351,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
         }
         __syncthreads();  // the partial sums are reused by the next step
         t_pub = wall_clock64();
+        __builtin_amdgcn_s_setprio(0);
     }
 }
 
