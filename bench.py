@@ -555,8 +555,9 @@ def recurrence_roofline(spec, desc, tm, workload):
     matrix-core time at the dtype's peak (the recurrent products, plus the
     input products when they run inside the recurrent launch), (b) W_hh read
     once per step from where it lives (registers: no bound; LDS at the LDS
-    peak; streamed from HBM by the per-step GEMM kernel) and (c) its HBM
-    traffic (the hoisted G read and y written).  frac = roofline time /
+    peak; streamed from HBM by the per-step GEMM kernel), W_ih likewise for
+    the layer wavefront (read from LDS), and (c) its HBM traffic (the hoisted
+    G read and y written).  frac = roofline time /
     measured time; per_step_us = measured time / sequential step slots."""
     H, B, T, D, L = spec.hidden_size, spec.B, spec.T, spec.D, spec.num_layers
     s = 2 if spec.dtype == "bf16" else 4
@@ -569,7 +570,7 @@ def recurrence_roofline(spec, desc, tm, workload):
     slots = T + L - 1 if pipe else T * L
     if "k_rec_step" in desc or "mode=gemm-step" in desc:
         w_level, w_bw = "hbm", PEAK_HBM_GBS
-    elif "w_hh=lds" in desc or pipe:
+    elif "w_hh=lds" in desc:
         w_level, w_bw = "lds", PEAK_LDS_GBS
     else:
         w_level, w_bw = "registers", None
@@ -578,6 +579,8 @@ def recurrence_roofline(spec, desc, tm, workload):
     terms = {"mfma_us": flops / (PEAK_TFLOPS[spec.dtype] * 1e12) * 1e6,
              "w_hh_us": None if w_bw is None else w_bytes / (w_bw * 1e9) * 1e6,
              "hbm_us": hbm_bytes / (PEAK_HBM_GBS * 1e9) * 1e6}
+    if pipe:  # the wavefront keeps W_hh in registers and reads W_ih from LDS every step
+        terms["w_ih_lds_us"] = T * sum(D * G4 * spec.layer_input(l) * s for l in range(L)) / (PEAK_LDS_GBS * 1e9) * 1e6
     bound = max((k for k in terms if terms[k] is not None), key=lambda k: terms[k])
     t_roof = terms[bound]
     return {"per_step_us": round(rec_ms * 1e3 / slots, 3), "slots": slots, "ms": round(rec_ms, 4),
