@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                     for (int i = 0; i < MTW; ++i) {
                         settle(ci, i);
 #pragma unroll
-                        for (int h = 0; h < NWL; ++h) mine = mine && xc_ok<XF>(wd[ci][i][h], tb);
+                        for (int h = 0; h < NWL; ++h) mine = mine & xc_ok<XF>(wd[ci][i][h], tb);
                     }
                 if (!__all(mine)) {
                     // slow path: back off, then re-read only the fragments that are stale
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
                                     if (stale[ci][i][h]) wd[ci][i][h] = re[ci][i][h];
                                 settle(ci, i);
 #pragma unroll
-                                for (int h = 0; h < NWL; ++h) mine = mine && xc_ok<XF>(wd[ci][i][h], tb);
+                                for (int h = 0; h < NWL; ++h) mine = mine & xc_ok<XF>(wd[ci][i][h], tb);
                             }
                     } while (!__all(mine));
                     if (!wave_ok) break;

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void k_rec_res(RecArgs a) {
                 auto current = [&](const u32x4 (&f)[kResRTP]) {
                     bool ok = true;
 #pragma unroll
-                    for (int i = 0; i < kResRTP; ++i) ok = ok && xc_ok<XF_PAIR>(f[i], tb);
+                    for (int i = 0; i < kResRTP; ++i) ok = ok & xc_ok<XF_PAIR>(f[i], tb);
                     return from_h0 || ok;
                 };
                 u32x4 hf[kResLA + 1][kResRTP];

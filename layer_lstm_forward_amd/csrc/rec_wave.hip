@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
 #pragma unroll
         for (int ci = 0; ci < CB; ++ci) {
             settle(ci);
-            mine = mine && xc_ok<XF>(frag[ci], tb);
+            mine = mine & xc_ok<XF>(frag[ci], tb);
         }
         if (!__all(mine)) {
             unsigned spins = 0;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci) {
                     settle(ci);
-                    mine = mine && xc_ok<XF>(frag[ci], tb);
+                    mine = mine & xc_ok<XF>(frag[ci], tb);
                 }
             } while (!__all(mine));
         }

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
 #pragma unroll
             for (int ci = 0; ci < CPW; ++ci) {
                 settle(ci);
-                mine = mine && xc_ok<XF>(hf[ci], tb);
+                mine = mine & xc_ok<XF>(hf[ci], tb);
             }
             if (!__all(mine)) {
                 unsigned spins = 0;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
 #pragma unroll
                     for (int ci = 0; ci < CPW; ++ci) {
                         settle(ci);
-                        mine = mine && xc_ok<XF>(hf[ci], tb);
+                        mine = mine & xc_ok<XF>(hf[ci], tb);
                     }
                 } while (!__all(mine));
             }
