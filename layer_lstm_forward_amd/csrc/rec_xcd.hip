@@ -101,7 +101,6 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
         float g[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) g[q] = gnext[q];
-        load_g(s + 1, gnext);
 
         f32x4 acc[NT];
 #pragma unroll
@@ -181,6 +180,11 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
                                    xc_pair_value(hf[ci].w)};
             }
         }
+        // The next step's G is requested only now: vector-memory counters
+        // complete in issue order, so loads issued before the h reads would
+        // hold up the check of those reads until they too had returned
+        // (G comes from HBM, h from the exchange, sooner).
+        load_g(s + 1, gnext);
         if (wave_ok && have_h)
 #pragma unroll
             for (int ci = 0; ci < CPW; ++ci)
