@@ -100,10 +100,13 @@ typedef enum {
     LSTM_OPT_POLL_SLEEP = 5, /* 0..1000: back-off (units of 64 clocks) between re-reads of h words */
     /* 6: reserved (no longer accepted) */
     LSTM_OPT_TEAM_ROWS = 7,  /* 0 (default): batch rows per team as the tile holds; n > 0: at most n */
-    LSTM_OPT_PROJ_TILE = 8,  /* projection GEMM: 0 automatic, 1 128x128, 2 256x256, 3 256x256 direct-to-LDS,
+    LSTM_OPT_PROJ_TILE = 8,  /* projection GEMM: 0 automatic (7 where the 256x256 direct-to-LDS tiles
+                                apply), 1 128x128, 2 256x256, 3 256x256 direct-to-LDS,
                                 4 / 5 256x256 direct-to-LDS through a ring of 4 / 5 stages, 6 256x128
-                                through a ring of 3 stages (two workgroups per CU) */
-    LSTM_OPT_READ_PACE = 9,  /* 0..100000 ns (default: 300 to 450 by schedule): delay between a workgroup
+                                through a ring of 3 stages (two workgroups per CU), 7 as 3 with the next
+                                stage's loads interleaved with the products */
+    LSTM_OPT_READ_PACE = 9,  /* 0..100000 ns (default by schedule: 300 to 450 for teams across XCDs, 0 on
+                                one XCD): delay between a workgroup
                                 finishing step t (its h_t published) and its first read of the other
                                 workgroups' h_t; 0 reads as soon as the step ends. A read that reaches
                                 memory before the data costs a retry round trip; results do not depend

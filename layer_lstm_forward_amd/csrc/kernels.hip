@@ -380,6 +380,154 @@ __global__ __launch_bounds__(256) void k_proj_dma(ProjArgs a) {
 }
 
 // ===========================================================================
+// Projection GEMM, k_proj_dma with the next stage's loads spread over the
+// products.  With one wave per SIMD, the issue of a stage's 16 direct-to-LDS
+// loads (and their address arithmetic) in one burst leaves the matrix pipe
+// idle for that time.  Here each lane's load offsets are computed once, a
+// stage is addressed by advancing the buffer resources' base, and the next
+// stage's loads go out in four groups, each behind the four products of one
+// row tile of the stage's first K sub-chunk, where they issue while those
+// products run.  Same tile, LDS layout, operand order and sums as k_proj_dma
+// (its results, bit for bit).  A stage that reaches past K (a ragged last
+// stage) is issued with per-segment checks, as in k_proj_dma.
+// ===========================================================================
+template <class DT>
+__global__ __launch_bounds__(256) void k_proj_il(ProjArgs a) {
+    using S = typename DT::S;
+    constexpr int BM = 256, BN = 256, SEG = 8;
+    constexpr int KS = SEG * DT::PER16;
+    constexpr int STAGE = (BM + BN) * SEG;  // 16-byte segments per stage
+    constexpr unsigned OOR = 0x80000000u;   // past any resource: reads zero
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4 *lds = reinterpret_cast<u32x4 *>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const ProjSplit sp = proj_split(a);
+    const int d = sp.d;
+    const int M = a.M, N = a.N, K = sp.kc, ldw = a.K;
+    int tm, tn;
+    gemm_tile_order(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int es = (int)sizeof(S);
+    const S *X = static_cast<const S *>(a.X) + (size_t)m0 * a.ldx + sp.kb;
+    const S *W = static_cast<const S *>(a.W[d]) + (size_t)n0 * ldw + sp.kb;
+    float *const Gs = a.G + sp.goff;
+    const unsigned xbytes = (unsigned)(((size_t)(min(BM, M - m0) - 1) * a.ldx + K) * es);
+    const unsigned wbytes = (unsigned)(((size_t)(min(BN, N - n0) - 1) * ldw + K) * es);
+
+    // this lane's slot in each 1 KiB block: row (lane / 8) of the block, swizzled segment (lane % 8)
+    const int brow = lane >> 3, pseg = lane & 7;
+    unsigned vx[8], vw[8];  // byte offsets of this lane's 8 segments of a stage (stage 0)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = (w + 4 * i) * 8 + brow;
+        const int lseg = pseg ^ ((row >> 1) & 7);
+        vx[i] = (unsigned)(((size_t)row * a.ldx + lseg * DT::PER16) * es);
+        vw[i] = (unsigned)(((size_t)row * ldw + lseg * DT::PER16) * es);
+    }
+    // every segment of stage kt lies inside K: the resources start at K offset
+    // kt * KS (rows past M or N stay past the shortened resources: ldx, ldw >= K)
+    auto issue_part = [&](int kt, int buf, int part) {
+        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+        const unsigned kb = (unsigned)(kt * KS * es);
+        const __amdgpu_buffer_rsrc_t rx =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(X + (size_t)kt * KS), (short)0, (int)(xbytes - kb), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W + (size_t)kt * KS), (short)0, (int)(wbytes - kb), 0x00020000);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * part + ii, blk = w + 4 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(sa + blk * 64), 16, vx[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(sb + blk * 64), 16, vw[i], 0, 0, 0);
+        }
+    };
+    // a stage reaching past K: each segment checked
+    const __amdgpu_buffer_rsrc_t rx0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(X), (short)0, (int)xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<S *>(W), (short)0, (int)wbytes, 0x00020000);
+    auto issue_checked = [&](int kt, int buf) {
+        u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int blk = w + 4 * i;
+            const int row = blk * 8 + brow;
+            const int lseg = pseg ^ ((row >> 1) & 7);
+            const int k = kt * KS + lseg * DT::PER16;
+            const unsigned ox = k < K ? (unsigned)(((size_t)row * a.ldx + k) * es) : OOR;
+            const unsigned ow = k < K ? (unsigned)(((size_t)row * ldw + k) * es) : OOR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx0, (lds_void_t *)(sa + blk * 64), 16, ox, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw0, (lds_void_t *)(sb + blk * 64), 16, ow, 0, 0, 0);
+        }
+    };
+    auto swz = [](int row, int sg) { return row * SEG + (sg ^ ((row >> 1) & 7)); };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (K + KS - 1) / KS;
+    const int nfull = K / KS;  // stages entirely inside K
+    if (nfull > 0) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) issue_part(0, 0, part);
+    } else {
+        issue_checked(0, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage kt are in LDS
+        __syncthreads();                 // everyone's are, and stage kt-1 is no longer read
+        const bool nxt = kt + 1 < nk, nxt_full = kt + 1 < nfull;
+        if (nxt && !nxt_full) issue_checked(kt + 1, buf ^ 1);
+        const u32x4 *sa = lds + buf * STAGE, *sb = sa + BM * SEG;
+        u32x4 af[2][4], bw[2][4];
+        auto frags = [&](int c, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+            const int sg = 2 * c + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = sa[swz(wm * 128 + 32 * i + (lane & 31), sg)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = sb[swz(wn * 128 + 32 * j + (lane & 31), sg)];
+        };
+        frags(0, af[0], bw[0]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (c + 1 < 4) frags(c + 1, af[(c + 1) & 1], bw[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead in front of the products
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma32_chunk(DT{}, acc[i][j], af[c & 1][i], bw[c & 1][j]);
+                if (c == 0) {
+                    // a quarter of the next stage's loads behind each row tile's products
+                    if (nxt_full) issue_part(kt + 1, buf ^ 1, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+
+    const S *bi = static_cast<const S *>(a.b_ih[d]);
+    const S *bh = static_cast<const S *>(a.b_hh[d]);
+    const size_t ldg = (size_t)a.D * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + 32 * j + (lane & 31);
+        const float bias = (bi && n < N) ? DT::to_f(bi[n]) + (bh ? DT::to_f(bh[n]) : 0.f) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M && n < N) Gs[(size_t)m * ldg + (size_t)d * N + n] = acc[i][j][v] + bias;
+            }
+    }
+}
+
+// ===========================================================================
 // Recurrence, one step as a GEMM.  For layers whose W_hh does not stay on
 // chip, each step is one launch of this kernel: S = h_{t-1} W_hh^T for a block
 // of BM = 32*WM batch rows and 32 hidden units, followed in the same kernel by
@@ -815,6 +963,15 @@ static hipError_t launch_proj_t(const ProjArgs &a, bool big, bool dma, int ring,
     if (big && dma && VEC && ring == 4) return launch_proj_ring<DT, 4, 256>(a, s);
     if (big && dma && VEC && ring == 5) return launch_proj_ring<DT, 5, 256>(a, s);
     if (big && dma && VEC && ring == 6) return launch_proj_ring<DT, 3, 128>(a, s);
+    if (big && dma && VEC && (ring == 7 || ring == 0)) {
+        const void *fn = reinterpret_cast<const void *>(&k_proj_il<DT>);
+        const size_t smem = 2 * (256 + 256) * 8 * 16;
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        dim3 grid(((a.M + 255) / 256) * ((a.N + 255) / 256), 1, zd);
+        hipLaunchKernelGGL((k_proj_il<DT>), grid, dim3(256), smem, s, a);
+        return hipGetLastError();
+    }
     if (big && dma && VEC) {
         const void *fn = reinterpret_cast<const void *>(&k_proj_dma<DT>);
         const size_t smem = 2 * (256 + 256) * 8 * 16;
@@ -847,9 +1004,11 @@ static void proj_choose(int M, int N, int K, int ldx, int D, int dtype, int vari
     *dma = *big && vec && variant != 2 && (size_t)256 * ldx * es < (1u << 31) && (size_t)256 * K * es < (1u << 31);
 }
 
-// the direct-to-LDS ring variant: 4 / 5 stages of 256x256 tiles, 6: three
-// stages of 256x128 tiles (0: the double-buffered k_proj_dma)
-static int proj_ring(int variant) { return variant >= 4 && variant <= 6 ? variant : 0; }
+// the direct-to-LDS variants: 4 / 5 stages of 256x256 tiles, 6: three
+// stages of 256x128 tiles, 7 (and automatic, 0): k_proj_il, the double
+// buffer with its loads interleaved with the products; 3: k_proj_dma, the
+// double buffer with each stage's loads issued together
+static int proj_ring(int variant) { return variant >= 4 && variant <= 7 ? variant : 0; }
 
 int proj_kchunk(int M, int N, int K) {
     const long long tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);
@@ -865,7 +1024,8 @@ const char *proj_kernel_name(int M, int N, int K, int D, int dtype, int variant)
     const int per16 = dtype == DT_BF16 ? 8 : 4;
     bool big, dma;
     proj_choose(M, N, K, K, D, dtype, variant, K % per16 == 0, &big, &dma);
-    return dma ? (proj_ring(variant) ? "k_proj_ring" : "k_proj_dma") : big ? "k_proj_big" : "k_proj";
+    return dma ? (variant == 7 || variant == 0 ? "k_proj_il" : proj_ring(variant) ? "k_proj_ring" : "k_proj_dma")
+               : big ? "k_proj_big" : "k_proj";
 }
 
 hipError_t launch_proj(const ProjArgs &a, int dtype, int variant, hipStream_t s) {

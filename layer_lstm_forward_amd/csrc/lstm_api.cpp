@@ -744,7 +744,7 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             p->team_rows = value;
             return LSTM_OK;
         case LSTM_OPT_PROJ_TILE:
-            if (value < 0 || value > 6) return LSTM_ERR_UNSUPPORTED;
+            if (value < 0 || value > 7) return LSTM_ERR_UNSUPPORTED;
             p->proj_tile = value;
             return LSTM_OK;
         case LSTM_OPT_TIMING:
@@ -1121,7 +1121,8 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         if (small) {
             RecArgs xa = ra;
             xa.P = xcd_workgroups(p->H);
-            xa.pace = (int)((long long)(p->read_pace_ns >= 0 ? p->read_pace_ns : 200) * di.wall_khz / 1000000);
+            // no default pace: on one XCD a stale read costs a short round trip
+            xa.pace = (int)((long long)(p->read_pace_ns >= 0 ? p->read_pace_ns : 0) * di.wall_khz / 1000000);
             if (launch_xcd(xa, p->dtype, st) == hipSuccess) {
                 span_end(p, span, st, 1);
                 xpar ^= layer_writes;

@@ -348,8 +348,8 @@ def test_lengths_all_full_equal_plain_forward():
 
 
 @pytest.mark.parametrize("spec", SMALL[:4] + SMALL[5:7], ids=_id)
-@pytest.mark.parametrize("proj_tile", [1, 2, 3, 4, 5, 6],
-                         ids=["proj128", "proj256", "proj256dma", "ring4", "ring5", "ring3x128"])
+@pytest.mark.parametrize("proj_tile", [1, 2, 3, 4, 5, 6, 7],
+                         ids=["proj128", "proj256", "proj256dma", "ring4", "ring5", "ring3x128", "interleaved"])
 def test_projection_tiles(spec, proj_tile):
     """Both projection GEMM kernels, forced on shapes with ragged M, N and K."""
     print(f"case {_id(spec)} proj tile {proj_tile}", flush=True)
@@ -357,6 +357,23 @@ def test_projection_tiles(spec, proj_tile):
     got, m = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: proj_tile, pkg.LSTM_OPT_FUSE_INPUT: 0})
     ref = run_oracle(inp)
     assert_parity(got, ref, spec.dtype, f"proj tile {proj_tile}")
+
+
+@pytest.mark.parametrize("spec", [Spec(200, 136, 1, True, 9, 37, "bf16", 711, "normal0.1"),   # ragged K: a checked last stage
+                                  Spec(512, 192, 1, False, 40, 13, "bf16", 712, "normal0.1"),  # full stages only
+                                  Spec(96, 72, 1, False, 33, 9, "f32", 713, "normal0.1")], ids=_id)
+def test_interleaved_projection_equals_dma(spec):
+    """The projection with its loads spread over the products (tile 7) does
+    the same products in the same order as the double-buffered one (tile 3):
+    equal bit for bit, and within the oracle's tolerance."""
+    print(f"case {_id(spec)} interleaved projection", flush=True)
+    inp = make_inputs(spec)
+    a, m = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: 7, pkg.LSTM_OPT_FUSE_INPUT: 0, pkg.LSTM_OPT_SMALL_BATCH: 0})
+    assert "k_proj_il" in m.describe(spec.T, spec.B)
+    b, _ = run_gpu(inp, options={pkg.LSTM_OPT_PROJ_TILE: 3, pkg.LSTM_OPT_FUSE_INPUT: 0, pkg.LSTM_OPT_SMALL_BATCH: 0})
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    assert_parity(a, run_oracle(inp), spec.dtype, "interleaved projection")
 
 
 @pytest.mark.parametrize("tile", TILES)
