@@ -196,6 +196,20 @@ __host__ __device__ inline bool xc_ok(const u32x4 &w, unsigned tb) {
     return ((tb ? all : ~any) >> xc_shift(F)) & 1u;
 }
 
+// Sum of the N f32x4 partial sums at p, p + stride, ..., p + (N-1) stride
+// (floats, in LDS), added in index order.  All N reads are issued before the
+// first addition, so the reduction costs one LDS round trip, not N.
+template <int N>
+__device__ inline f32x4 lds_sum_f32x4(const float *p, int stride) {
+    f32x4 v[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = *reinterpret_cast<const f32x4 *>(p + k * stride);
+    f32x4 sum = v[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) sum += v[k];
+    return sum;
+}
+
 // The float at byte offset off of a buffer of nbytes bytes, through a buffer
 // resource: a NULL base (no records) reads 0, without a branch (a branch
 // around a load makes the compiler wait for it where the paths join).

@@ -456,9 +456,7 @@ __global__ __launch_bounds__(256) void k_rec(RecArgs a) {
             S hs = (S)0;
             if (cv[i]) {
                 const float *pp = &part[cm[i] * PSTR + 4 * cu[i]];
-                f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
-#pragma unroll
-                for (int kk = 1; kk < WK; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
+                const f32x4 sum = lds_sum_f32x4<WK>(pp, ROWS * PSTR);
                 float pre[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {

@@ -182,11 +182,13 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
             if (nl < 3) frag[ci].z = tpat;
             if (nl < 4) frag[ci].w = tpat;
         };
+        // (short-circuit form: the branch-free one of the other kernels raises
+        // the register count past two workgroups per CU here, and spills)
         bool mine = true;
 #pragma unroll
         for (int ci = 0; ci < CB; ++ci) {
             settle(ci);
-            mine = mine & xc_ok<XF>(frag[ci], tb);
+            mine = mine && xc_ok<XF>(frag[ci], tb);
         }
         if (!__all(mine)) {
             unsigned spins = 0;
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci) {
                     settle(ci);
-                    mine = mine & xc_ok<XF>(frag[ci], tb);
+                    mine = mine && xc_ok<XF>(frag[ci], tb);
                 }
             } while (!__all(mine));
         }
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
         S hs = (S)0;
         if (cv) {
             const float *pp = &part[cm * PSTR + 4 * cu];
+            // (read one partial at a time: registers are scarce with two workgroups per CU)
             f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
 #pragma unroll
             for (int kk = 1; kk < 4; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);

@@ -205,9 +205,7 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
         S hs = (S)0;
         if (cv) {
             const float *pp = &part[cm * PSTR + 4 * cu];
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
-#pragma unroll
-            for (int kk = 1; kk < kXcdWaves; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
+            const f32x4 sum = lds_sum_f32x4<kXcdWaves>(pp, ROWS * PSTR);
             const float ig = sigmoid_f(sum.x + g[0]);
             const float fg = sigmoid_f(sum.y + g[1]);
             const float gg = tanh_f(sum.z + g[2]);
