@@ -327,7 +327,7 @@ def main():
     ap.add_argument("--recurrence", choices=["auto", "step", "persistent"], default="auto")
     ap.add_argument("--rec-tile", type=int, default=0)
     ap.add_argument("--proj-tile", type=int, default=0, help="LSTM_OPT_PROJ_TILE (0 automatic)")
-    ap.add_argument("--layer-pipe", type=int, choices=[0, 1], default=None,
+    ap.add_argument("--layer-pipe", type=int, choices=[0, 1, 2], default=None,
                     help="LSTM_OPT_LAYER_PIPE (default: the library's, the layer wavefront where it applies)")
     ap.add_argument("--small-batch", type=int, choices=[0, 1], default=None,
                     help="LSTM_OPT_SMALL_BATCH (default: the library's, one XCD per direction where it applies)")

@@ -115,8 +115,10 @@ typedef enum {
                                 layout runs every layer in one persistent launch (the layer wavefront: layer
                                 l consumes layer l-1's h_t as it is produced, two workgroups per CU) when its
                                 tiles fit (H and the input width at most 128 fp32 / 256 bf16 values per wave
-                                and whole 16-byte rows) and all its workgroups are co-resident; 0: layer by
-                                layer.  Not used with per-row lengths or in training. Changes
+                                and whole 16-byte rows) and all its workgroups are co-resident; 2: the same,
+                                with a two-layer stack's layers paired in 512-thread workgroups that step
+                                in lockstep (layer 1 two steps behind; at most 8 units per workgroup);
+                                0: layer by layer.  Not used with per-row lengths or in training. Changes
                                 lstm_workspace_size. */
     LSTM_OPT_FUSE_INPUT = 11, /* 1 (default): a layer whose recurrence runs as one persistent launch and
                                 whose W_ih share fits in registers computes x_t W_ih^T + b_ih + b_hh inside

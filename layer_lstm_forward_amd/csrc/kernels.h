@@ -126,9 +126,10 @@ hipError_t launch_res(const RecArgs &a, hipStream_t s);
 // input width fits 8 chunks per wave (ncx0: its chunks per wave), and H and
 // the input width are multiples of 16 bytes.
 bool wave_shape_ok(int H, int I, int dtype, int *ncx0);
-// nt: 4 nt units per workgroup (1, 2 or 4)
-hipError_t wave_max_coresident(int nt, int dtype, int *blocks_per_cu);
-hipError_t launch_wave(const WaveArgs &a, int nt, int dtype, hipStream_t s);
+// nt: 4 nt units per workgroup (1, 2 or 4); lpw: layers per workgroup (1, or
+// 2 for a two-layer stack: both layers' unit slice in one 512-thread workgroup)
+hipError_t wave_max_coresident(int nt, int dtype, int lpw, int *blocks_per_cu);
+hipError_t launch_wave(const WaveArgs &a, int nt, int dtype, int lpw, hipStream_t s);
 
 // Recurrent tile: 4 waves split (4/WK) ways over batch tiles and WK ways over
 // K; each wave owns MTW 16-row batch tiles; NT 16-column tiles of gate rows

@@ -25,7 +25,8 @@ struct lstm_plan {
     int part_bufs;   // partial-sum buffers requested (1 or 2)
     int poll_sleep;  // back-off between re-reads of stale exchange words
     int read_pace_ns;  // delay between the end of a recurrent step and the first read of the next (-1: by schedule)
-    int layer_pipe;    // 1 (default): run a unidirectional stack's layers in one wavefront launch when it fits
+    int layer_pipe;    // 1 (default): run a unidirectional stack's layers in one wavefront launch when it fits;
+                       // 2: the same with a two-layer stack's layers paired in each workgroup
     int fuse_input;    // 1: compute x_t W_ih^T inside the persistent recurrence when W_ih fits in registers
     int batch_first;   // 1: x and y are [B, T, .] instead of [T, B, .]
     int small_batch;   // 1: B <= 16 layers run each direction's recurrence on one XCD (rec_xcd.hip)
@@ -455,6 +456,7 @@ bool gemm_step_shape_ok(const lstm_plan *p) {
 
 struct WaveSched {
     int NT, U, P, BG, NGB, wgs, ncx0, map_xcd;
+    int lpw;  // layers per workgroup: 1, or 2 (a two-layer stack paired in 512-thread workgroups)
 };
 
 // Wavefront schedule: teams of at most 16 rows, U = 4 NT units per
@@ -472,12 +474,13 @@ bool choose_wave(const lstm_plan *p, int B, int dev, WaveSched *out) {
         w.P = (p->H + w.U - 1) / w.U;
         w.NGB = wave_teams(B);
         w.BG = (B + w.NGB - 1) / w.NGB;
-        w.wgs = p->L * w.NGB * w.P;
+        w.lpw = (p->layer_pipe == 2 && p->L == 2 && nt <= 2) ? 2 : 1;
+        w.wgs = (w.lpw == 2 ? 1 : p->L) * w.NGB * w.P;
         wave_shape_ok(p->H, p->I, p->dtype, &w.ncx0);
         const int per_layer = w.NGB * w.P;
         w.map_xcd = (w.NGB <= 8 && 8 % w.NGB == 0 && per_layer % 8 == 0) ? 1 : 0;
         int bpc = 0;
-        const bool ok = wave_max_coresident(nt, p->dtype, &bpc) == hipSuccess && bpc > 0 &&
+        const bool ok = wave_max_coresident(nt, p->dtype, w.lpw, &bpc) == hipSuccess && bpc > 0 &&
                         (long long)bpc * di.cus >= w.wgs;
         (void)hipGetLastError();
         if (ok) {
@@ -716,7 +719,7 @@ lstm_status lstm_set_option(lstm_plan *p, int option, int value) {
             p->poll_sleep = value;
             return LSTM_OK;
         case LSTM_OPT_LAYER_PIPE:
-            if (value != 0 && value != 1) return LSTM_ERR_UNSUPPORTED;
+            if (value < 0 || value > 2) return LSTM_ERR_UNSUPPORTED;
             p->layer_pipe = value;
             return LSTM_OK;
         case LSTM_OPT_FUSE_INPUT:
@@ -799,9 +802,9 @@ lstm_status lstm_describe(const lstm_plan *p, int T, int B, char *buf, size_t le
     WaveSched ws{};
     if (!mode_persistent && choose_wave(p, B, dev, &ws)) {
         std::snprintf(buf, len,
-                      "rec=k_rec_wave<%s,NT=%d> mode=wavefront U=%d P=%d BG=%d NGB=%d layers=%d workgroups=%d "
-                      "map_xcd=%d w_hh=regs xproj=%s",
-                      dt, ws.NT, ws.U, ws.P, ws.BG, ws.NGB, p->L, ws.wgs, ws.map_xcd,
+                      "rec=k_rec_wave<%s,NT=%d> mode=wavefront U=%d P=%d BG=%d NGB=%d layers=%d layers_per_wg=%d "
+                      "workgroups=%d map_xcd=%d w_hh=regs xproj=%s",
+                      dt, ws.NT, ws.U, ws.P, ws.BG, ws.NGB, p->L, ws.lpw, ws.wgs, ws.map_xcd,
                       p->L == 2 ? "fused,fused" : p->L == 3 ? "fused,fused,fused" : "fused,fused,fused,fused");
         return LSTM_OK;
     }
@@ -998,7 +1001,7 @@ lstm_status forward_impl(lstm_plan *p, const void *x, const int *lengths_h, cons
         qa.timeout_ticks = (long long)di.wall_khz * 1000LL * 5;  // five seconds
         const int span = span_begin(p, st, 1);
         // x's fragment loads need 16-byte rows: otherwise the layer-by-layer path
-        if (vec && (size_t)B * p->I * es < ((size_t)1 << 31) && launch_wave(qa, wsch.NT, p->dtype, st) == hipSuccess) {
+        if (vec && (size_t)B * p->I * es < ((size_t)1 << 31) && launch_wave(qa, wsch.NT, p->dtype, wsch.lpw, st) == hipSuccess) {
             span_end(p, span, st, 1);
             if (p->timing) p->acc.calls += 1;
             return LSTM_OK;

@@ -36,8 +36,13 @@ namespace {
 
 constexpr int kWaveCB = 8;  // K chunks of W_hh (and of a layer's W_ih) per wave: K <= 4 waves x 8 chunks
 
-template <class DT, int NT, int FX>
-__global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
+constexpr int kWaveLag = 2;  // paired layers: layer 1 runs step t in the slot of layer 0's step t + 2
+
+// LPW layers per workgroup: 1 (a workgroup per layer and unit slice), or 2
+// (a two-layer stack's unit slice of both layers in one 512-thread
+// workgroup, stepping in lockstep slots: layer 1 kWaveLag steps behind).
+template <class DT, int NT, int FX, int LPW>
+__global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k_rec_wave(WaveArgs a) {
     using S = typename DT::S;
     constexpr bool BF = sizeof(S) == 2;
     constexpr int XF = BF ? XF_PAIR : XF_F32;  // |h| <= 1 for the LSTM: the pair words are sound
@@ -50,15 +55,20 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
     constexpr int EW = BF ? 2 : 1;  // K values per exchange word
     static_assert(CELLS <= 256, "one cell per thread");
     static_assert(FX >= CB, "a layer above the first multiplies CB chunks of its input per wave");
-    __shared__ float part[4 * ROWS * PSTR];
+    static_assert(LPW == 1 || LPW == 2, "one or two layers per workgroup");
+    __shared__ float part[LPW][4 * ROWS * PSTR];
     __shared__ int s_bad;
     extern __shared__ __align__(16) unsigned char smem[];
-    u32x4 *wxs = reinterpret_cast<u32x4 *>(smem);  // W_ih fragments: [wave][FX chunks][NT][64 lanes]
 
-    const int tid = threadIdx.x, lane = tid & 63, wk = tid >> 6;  // wave wk owns a quarter of K
+    // a layer's 256 threads: wave wk owns a quarter of K
+    const int tid = threadIdx.x & 255, lid = LPW == 2 ? (int)(threadIdx.x >> 8) : 0;
+    const int lane = tid & 63, wk = tid >> 6;
+    // W_ih fragments of this workgroup's layer lid: [wave][FX chunks][NT][64 lanes]
+    u32x4 *wxs = reinterpret_cast<u32x4 *>(smem) + (size_t)lid * 4 * FX * NT * 64;
     // workgroup -> (layer, team, unit slice)
     const int per_layer = a.NGB * a.P;
-    const int l = blockIdx.x / per_layer, lb = blockIdx.x % per_layer;
+    const int l = LPW == 2 ? lid : (int)(blockIdx.x / per_layer);
+    const int lb = LPW == 2 ? (int)blockIdx.x : (int)(blockIdx.x % per_layer);
     int team, p;
     if (a.map_xcd) {  // workgroup ids go round-robin over the 8 XCDs; a team keeps to 8 / NGB of them
         const int X = 8 / a.NGB;
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
             bias[q] = bi ? DT::to_f(bi[r]) + DT::to_f(bh[r]) : 0.f;
         }
     }
-    if (tid == 0) s_bad = 0;
+    if (threadIdx.x == 0) s_bad = 0;
 
     const int mrow = lane & 15;                    // this lane's team row in the 16-row tile
     const int ksub = (lane >> 4) * DT::PER16;      // this lane's K offset inside a chunk
@@ -229,11 +239,17 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
 
     if (l > 0) issue_words(slot_words(l - 1, 0), cx0, kch, xin);  // step 0's input (checked in the step)
 
-    for (int s = 0; s < T; ++s) {
+    // slots: one step of every layer (paired layers: layer l at step sg - l kWaveLag,
+    // idle before its first and after its last step but at every barrier)
+    const int nslots = LPW == 2 ? T + kWaveLag * (L - 1) : T;
+    for (int sg = 0; sg < nslots; ++sg) {
+        const int s = LPW == 2 ? sg - kWaveLag * l : sg;
+        const bool act = s >= 0 && s < T;
+        bool wave_ok = true;
         f32x4 acc[NT];
+        if (act) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bool wave_ok = true;
 
         // The input product first: x_t (layer 0) or layer l-1's h_t, both
         // read a step ahead (below).  Layer l-1's words are usually current
@@ -302,16 +318,18 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) part[(wk * ROWS + 4 * (lane >> 4) + v) * PSTR + j * 16 + (lane & 15)] = acc[j][v];
+            for (int v = 0; v < 4; ++v) part[lid][(wk * ROWS + 4 * (lane >> 4) + v) * PSTR + j * 16 + (lane & 15)] = acc[j][v];
+        }  // act
         if (!wave_ok) s_bad = 1;
         __syncthreads();
         if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+        if (act) {
 
         // gates, cell update, h_t (warp-nn equation block)
         float hv = 0.f;
         S hs = (S)0;
         if (cv) {
-            const float *pp = &part[cm * PSTR + 4 * cu];
+            const float *pp = &part[lid][cm * PSTR + 4 * cu];
             // (read one partial at a time: registers are scarce with two workgroups per CU)
             f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
 #pragma unroll
@@ -352,24 +370,28 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void k_rec_wave(WaveArgs a) {
                 if (a.cn) a.cn[si] = creg;
             }
         }
+        }  // act
         __syncthreads();  // the partial sums are reused by the next step
         t_pub = wall_clock64();
         __builtin_amdgcn_s_setprio(0);
     }
 }
 
-#define LSTM_WAVE_TILES(X) X(1) X(2) X(4)
-
+// Paired layers only with NT <= 2: at NT = 4 two waves per SIMD do not fit
+// the registers.
 template <class DT>
-const void *wave_kernel_ptr(int nt) {
-#define LSTM_W_PTR(nt_)                                                                            \
-    if (nt == nt_) return reinterpret_cast<const void *>(&k_rec_wave<DT, nt_, kWaveCB>);
-    LSTM_WAVE_TILES(LSTM_W_PTR)
-#undef LSTM_W_PTR
+const void *wave_kernel_ptr(int nt, int lpw) {
+    if (nt == 1) return lpw == 2 ? reinterpret_cast<const void *>(&k_rec_wave<DT, 1, kWaveCB, 2>)
+                                 : reinterpret_cast<const void *>(&k_rec_wave<DT, 1, kWaveCB, 1>);
+    if (nt == 2) return lpw == 2 ? reinterpret_cast<const void *>(&k_rec_wave<DT, 2, kWaveCB, 2>)
+                                 : reinterpret_cast<const void *>(&k_rec_wave<DT, 2, kWaveCB, 1>);
+    if (nt == 4 && lpw == 1) return reinterpret_cast<const void *>(&k_rec_wave<DT, 4, kWaveCB, 1>);
     return nullptr;
 }
 
-const void *wave_kernel(int nt, int dtype) { return dtype == DT_BF16 ? wave_kernel_ptr<BF16>(nt) : wave_kernel_ptr<F32>(nt); }
+const void *wave_kernel(int nt, int dtype, int lpw) {
+    return dtype == DT_BF16 ? wave_kernel_ptr<BF16>(nt, lpw) : wave_kernel_ptr<F32>(nt, lpw);
+}
 
 }  // namespace
 
@@ -381,26 +403,26 @@ bool wave_shape_ok(int H, int I, int dtype, int *ncx0) {
     return kch <= 4 * kWaveCB && *ncx0 <= kWaveCB && H % per16 == 0 && I % per16 == 0;
 }
 
-// dynamic LDS of k_rec_wave: the W_ih fragments of its four waves
-static size_t wave_smem(int nt) { return (size_t)4 * kWaveCB * nt * 64 * 16; }
+// dynamic LDS of k_rec_wave: the W_ih fragments of four waves per layer
+static size_t wave_smem(int nt, int lpw) { return (size_t)lpw * 4 * kWaveCB * nt * 64 * 16; }
 
-hipError_t wave_max_coresident(int nt, int dtype, int *blocks_per_cu) {
-    const void *fn = wave_kernel(nt, dtype);
+hipError_t wave_max_coresident(int nt, int dtype, int lpw, int *blocks_per_cu) {
+    const void *fn = wave_kernel(nt, dtype, lpw);
     if (!fn) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wave_smem(nt));
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wave_smem(nt, lpw));
     if (e != hipSuccess) return e;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256, wave_smem(nt));
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, 256 * lpw, wave_smem(nt, lpw));
 }
 
-hipError_t launch_wave(const WaveArgs &a, int nt, int dtype, hipStream_t s) {
-    const void *fn = wave_kernel(nt, dtype);
+hipError_t launch_wave(const WaveArgs &a, int nt, int dtype, int lpw, hipStream_t s) {
+    const void *fn = wave_kernel(nt, dtype, lpw);
     if (!fn) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wave_smem(nt));
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wave_smem(nt, lpw));
     if (e != hipSuccess) return e;
-    dim3 grid(a.L * a.NGB * a.P), block(256);
+    dim3 grid((lpw == 2 ? 1 : a.L) * a.NGB * a.P), block(256 * lpw);
     WaveArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)wave_smem(nt), s);
+    return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)wave_smem(nt, lpw), s);
 }
 
 }  // namespace lstm_amd

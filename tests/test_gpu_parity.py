@@ -101,6 +101,12 @@ def test_layer_wavefront(spec):
     seq, m2 = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 0})
     assert "wavefront" not in m2.describe(spec.T, spec.B)
     assert_parity(seq, ref, spec.dtype, "layer by layer")
+    # a two-layer stack paired in 512-thread workgroups (lockstep slots, layer
+    # 1 two steps behind); deeper stacks keep one workgroup per layer
+    paired, m3 = run_gpu(inp, options={pkg.LSTM_OPT_LAYER_PIPE: 2})
+    desc = m3.describe(spec.T, spec.B)
+    assert "wavefront" in desc and ("layers_per_wg=2" in desc) == (spec.num_layers == 2), desc
+    assert_parity(paired, ref, spec.dtype, "paired wavefront")
 
 
 @pytest.mark.parametrize("spec", [
@@ -468,6 +474,10 @@ def test_full_l2_in256_h512_b64_f32_hoisted_projection_sampled_rows():
 
 def test_full_l2_in256_h512_b64_f32_wavefront_sampled_rows():
     _full("l2_in256_h512_t128_b64_f32", [1, 32, 62], options={pkg.LSTM_OPT_LAYER_PIPE: 1})
+
+
+def test_full_l2_in256_h512_b64_f32_paired_wavefront_sampled_rows():
+    _full("l2_in256_h512_t128_b64_f32", [3, 31, 63], options={pkg.LSTM_OPT_LAYER_PIPE: 2})
 
 
 def test_full_l2_in256_h512_b64_f32_layer_by_layer_sampled_rows():
