@@ -271,8 +271,12 @@ def counter_summary(kernel, workload, csv_paths, command):
         lines.append(f"mfma_busy: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (dur_ns * 2.4 * 1024):.4f}")
     if avg.get("SQ_LDS_IDX_ACTIVE"):
         lines.append(f"lds_conflict: {avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_LDS_IDX_ACTIVE']:.4f}")
-    if avg.get("SQ_WAVE_CYCLES"):
-        lines.append(f"wait_any: {avg.get('SQ_WAIT_INST_ANY', 0.0) / avg['SQ_WAVE_CYCLES']:.4f}")
+    if avg.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in avg:
+        lines.append(f"wait_any: {avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.4f}")
+    if dur_ns and "GRBM_GUI_ACTIVE" in avg:
+        # GRBM_GUI_ACTIVE adds the 8 XCDs' active cycles; per XCD and nanosecond
+        # of the dispatch it approximates the clock (short dispatches overstate it)
+        lines.append(f"grbm_active_ghz_per_xcd: {avg['GRBM_GUI_ACTIVE'] / 8 / dur_ns:.2f}")
     return "\n".join(lines)
 
 
