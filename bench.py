@@ -222,7 +222,7 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, wo
              f"# command: {command}",
              f"# workload: {workload}",
              f"# kernel: {name}",
-             f"kernel_source_sha256: {kernel_source_hash(kernel)}",
+             f"kernel_source_sha256: {kernel_source_hash(kernel.replace('<', ''))}",
              f"copy_calibration: FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB for a 262144 KiB copy "
              f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
              f"FETCH_SIZE_KiB_per_dispatch: {kf:.1f} (over {nf} dispatches)",
