@@ -311,7 +311,8 @@ __global__ __launch_bounds__(256, 1) void k_rec_res(RecArgs a) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+            // the drain flag is read with the partial sums (one LDS round trip)
+            const int bad = s_bad;
             f32x4 sum[4];
 #pragma unroll
             for (int i = 0; i < kResRTP; ++i)
@@ -322,6 +323,7 @@ __global__ __launch_bounds__(256, 1) void k_rec_res(RecArgs a) {
             for (int sl = 0; sl < kResRTP - 1; ++sl)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) sum[q] += part[p][w][sl][q][lane];
+            if (bad) return;  // a wait gave up: leave (every workgroup drains the same way)
 
             // this wave's G loads of this pass are in LDS (it alone reads them):
             // all but the six newest loads (the next pass's) have completed

@@ -36,7 +36,10 @@ namespace {
 
 constexpr int kWaveCB = 8;  // K chunks of W_hh (and of a layer's W_ih) per wave: K <= 4 waves x 8 chunks
 
-constexpr int kWaveLag = 2;  // paired layers: layer 1 runs step t in the slot of layer 0's step t + 2
+constexpr int kWaveLag = 2;
+
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for
+constexpr int kWaitVmem0 = (7 << 4) | (15 << 8);  // paired layers: layer 1 runs step t in the slot of layer 0's step t + 2
 
 // LPW layers per workgroup: 1 (a workgroup per layer and unit slice), or 2
 // (a two-layer stack's unit slice of both layers in one 512-thread
@@ -238,6 +241,10 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
     };
 
     if (l > 0) issue_words(slot_words(l - 1, 0), cx0, kch, xin);  // step 0's input (checked in the step)
+    // Step 0's input has returned before the loop, as every later step's has
+    // at the bottom of the one before it (see below): the top of the step then
+    // carries no wait for memory operations.
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
 
     // slots: one step of every layer (paired layers: layer l at step sg - l kWaveLag,
     // idle before its first and after its last step but at every barrier)
@@ -321,19 +328,24 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
             for (int v = 0; v < 4; ++v) part[lid][(wk * ROWS + 4 * (lane >> 4) + v) * PSTR + j * 16 + (lane & 15)] = acc[j][v];
         }  // act
         if (!wave_ok) s_bad = 1;
+        // Every load of this wave has returned here on the usual path (the h
+        // wait drained them); saying so on every path keeps the compiler from
+        // waiting for the publication stores below at the top of the next
+        // step, where it would otherwise wait for the prefetched input.
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
         __syncthreads();
-        if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+        // The drain flag is read with the partial sums, in the same LDS round
+        // trip, and tested once they are in.
+        const int bad = s_bad;
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (act && cv) sum = lds_sum_f32x4<4>(&part[lid][cm * PSTR + 4 * cu], ROWS * PSTR);
+        if (bad) return;  // a wait gave up: leave (every workgroup drains the same way)
         if (act) {
 
         // gates, cell update, h_t (warp-nn equation block)
         float hv = 0.f;
         S hs = (S)0;
         if (cv) {
-            const float *pp = &part[lid][cm * PSTR + 4 * cu];
-            // (read one partial at a time: registers are scarce with two workgroups per CU)
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
-#pragma unroll
-            for (int kk = 1; kk < 4; ++kk) sum += *reinterpret_cast<const f32x4 *>(pp + kk * ROWS * PSTR);
             const float ig = sigmoid_f(sum.x + bias[0]);
             const float fg = sigmoid_f(sum.y + bias[1]);
             const float gg = tanh_f(sum.z + bias[2]);
