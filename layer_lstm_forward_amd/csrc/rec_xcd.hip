@@ -198,17 +198,14 @@ __global__ __launch_bounds__(512) void k_rec_xcd(RecArgs a) {
             for (int v = 0; v < 4; ++v) part[(wk * ROWS + 4 * (lane >> 4) + v) * PSTR + j * 16 + (lane & 15)] = acc[j][v];
         if (!wave_ok) s_bad = 1;
         __syncthreads();
-        // The drain flag is read with the partial sums, in the same LDS round
-        // trip, and tested once they are in.
-        const int bad = s_bad;
-        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (cv) sum = lds_sum_f32x4<kXcdWaves>(&part[cm * PSTR + 4 * cu], ROWS * PSTR);
-        if (bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+        if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
 
         // gates, cell update, h_t (warp-nn equation block)
         float hv = 0.f;
         S hs = (S)0;
         if (cv) {
+            const float *pp = &part[cm * PSTR + 4 * cu];
+            const f32x4 sum = lds_sum_f32x4<kXcdWaves>(pp, ROWS * PSTR);
             const float ig = sigmoid_f(sum.x + g[0]);
             const float fg = sigmoid_f(sum.y + g[1]);
             const float gg = tanh_f(sum.z + g[2]);
