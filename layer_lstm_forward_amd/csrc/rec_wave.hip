@@ -185,7 +185,15 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
 #pragma unroll
         for (int ci = 0; ci < CB; ++ci) frag[ci] = xload2(xr, word_off(c0, climit, ci));
     };
-    auto wait_words = [&](const uint32_t *src, int c0, int climit, unsigned tb, u32x4 (&frag)[CB]) -> bool {
+    // Whether every word of this wave's fragments of chunks c0 .. c0 + CB is
+    // live (all 16 team rows, every chunk inside climit and H): wave-uniform,
+    // and then no word needs settling, which keeps the per-word lane masks
+    // (loop-invariant, spilled from scalar registers) off the step's path.
+    auto all_live = [&](int c0, int climit) -> bool {
+        return rows == ROWS && c0 + CB <= climit && (c0 + CB) * DT::KC <= H;
+    };
+    const bool live_x = l > 0 && all_live(cx0, kch), live_h = all_live(wk * CB, kch);
+    auto wait_words = [&](const uint32_t *src, int c0, int climit, unsigned tb, bool live, u32x4 (&frag)[CB]) -> bool {
         const __amdgpu_buffer_rsrc_t xr = xcrsrc(src, (unsigned)(region * 4));
         const unsigned tpat = tb << xc_shift(XF);
         auto settle = [&](int ci) {  // a dead word counts as current; its value meets zero W rows
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
         bool mine = true;
 #pragma unroll
         for (int ci = 0; ci < CB; ++ci) {
-            settle(ci);
+            if (!live) settle(ci);
             mine = mine && xc_ok<XF>(frag[ci], tb);
         }
         if (!__all(mine)) {
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
                 mine = true;
 #pragma unroll
                 for (int ci = 0; ci < CB; ++ci) {
-                    settle(ci);
+                    if (!live) settle(ci);
                     mine = mine && xc_ok<XF>(frag[ci], tb);
                 }
             } while (!__all(mine));
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
         // time to arrive: their reads are issued after it (issued before it,
         // they reached memory ahead of the data and the step got slower).
         const uint32_t *xsrc = l > 0 ? slot_words(l - 1, s) : nullptr;
-        if (l > 0) wave_ok = wait_words(xsrc, cx0, kch, 1u, xin);
+        if (l > 0) wave_ok = wait_words(xsrc, cx0, kch, 1u, live_x, xin);
         if (wave_ok) {
             u32x4 wcur[NT], wnext[NT];
 #pragma unroll
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
             if (a.pace > 0)
                 while (wall_clock64() - t_pub < a.pace) __builtin_amdgcn_s_sleep(1);
             issue_words(hsrc, wk * CB, kch, hf);
-            if (wave_ok) wave_ok = wait_words(hsrc, wk * CB, kch, tag_of(l, s - 1), hf);
+            if (wave_ok) wave_ok = wait_words(hsrc, wk * CB, kch, tag_of(l, s - 1), live_h, hf);
         } else if (a.h0) {  // plain loads of h0 (NULL: nothing to multiply)
             const S *hs = static_cast<const S *>(a.h0) + (size_t)l * B * H;
 #pragma unroll
