@@ -398,3 +398,43 @@ def test_full_size_training_sampled_rows(spec, rows):
     _check(cpu(dx)[:, rows], rdx, spec.dtype, "dx")
     _check(cpu(dh0)[:, rows], rdh0, spec.dtype, "dh0")
     _check(cpu(dc0)[:, rows], rdc0, spec.dtype, "dc0")
+
+
+@pytest.mark.parametrize("spec,rows", FULL_TRAIN, ids=lambda v: _id(v) if isinstance(v, Spec) else "")
+def test_full_size_weight_gradients_of_sampled_rows(spec, rows):
+    # The weight and bias gradients sum over every row, so at full size they
+    # are checked through the rows' independence: every row outside `rows`
+    # gets zero dy, dh_n and dc_n, hence zero gradient at every step, and the
+    # full-size launch's weight gradients must then equal the oracle's for
+    # the sampled rows alone.  dx of the zeroed rows must be exactly zero.
+    import torch
+    print(f"case {_id(spec)} full-size weight gradients, rows {rows}", flush=True)
+    inp = make_inputs(spec)
+    assert spec.dtype == "f32"
+    dev = "cuda:0"
+    dy, dhn, dcn = _grads(spec, spec.seed + 7)
+    others = np.setdiff1d(np.arange(spec.B), rows)
+    dy[:, others] = 0.0
+    dhn[:, others] = 0.0
+    dcn[:, others] = 0.0
+    m = pkg.LSTM(spec.input_size, spec.hidden_size, spec.num_layers, spec.bidirectional, dtype=spec.dtype)
+    x = to_dev(inp.x, False, dev)
+    w = [to_dev(p, False, dev) for p in inp.params]
+    h0 = None if inp.h0 is None else to_dev(inp.h0, False, dev)
+    c0 = None if inp.c0 is None else torch.from_numpy(inp.c0).to(dev)
+    y, hn, cn, reserve = m.forward_train(x, w, h0, c0)
+    dx, dh0, dc0, dws = m.backward(x, w, y, reserve, to_dev(dy, False, dev), h0=h0, c0=c0,
+                                   dh_n=to_dev(dhn, False, dev), dc_n=torch.from_numpy(dcn).to(dev))
+    torch.cuda.synchronize()
+    assert m.backward_status() == (0, 0)
+    sub = inp.rows(rows)
+    rdx, _, _, rdws = oracle.lstm_backward(sub.x, sub.params, spec.hidden_size, spec.num_layers,
+                                           spec.bidirectional, np.ascontiguousarray(dy[:, rows]), h0=sub.h0,
+                                           c0=sub.c0, dh_n=np.ascontiguousarray(dhn[:, rows]),
+                                           dc_n=np.ascontiguousarray(dcn[:, rows]), bf16=False)
+    cpu = lambda t: t.float().cpu().numpy()  # noqa: E731
+    _check(cpu(dx)[:, rows], rdx, spec.dtype, "dx")
+    assert np.all(cpu(dx)[:, others] == 0.0)
+    assert len(dws) == len(rdws)
+    for k, (g, r) in enumerate(zip(dws, rdws)):
+        _check(cpu(g), r, spec.dtype, f"dweights[{k}]")
