@@ -87,6 +87,10 @@ def test_gemm_step_blocks(spec):
     Spec(40, 96, 4, False, 5, 70, "bf16", 503, "normal0.1"),    # four layers, ragged batch groups
     Spec(16, 40, 2, False, 6, 3, "bf16", 504, "normal0.1", has_bias=False),
     Spec(8, 16, 2, False, 1, 1, "f32", 505, "normal0.1"),       # one step, one row
+    # waves whose exchange fragments are all live (they skip the per-word
+    # settling) beside partial waves and a ragged last team, in one launch
+    Spec(128, 400, 2, False, 6, 40, "f32", 506, "normal0.1"),
+    Spec(64, 1024, 2, False, 4, 20, "bf16", 507, "normal0.1"),
 ], ids=_id)
 def test_layer_wavefront(spec):
     """All layers of a unidirectional stack in one launch, layer l consuming
