@@ -64,7 +64,9 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
     extern __shared__ __align__(16) unsigned char smem[];
 
     // a layer's 256 threads: wave wk owns a quarter of K
-    const int tid = threadIdx.x & 255, lid = LPW == 2 ? (int)(threadIdx.x >> 8) : 0;
+    // (the layer of a wave is the same for all its lanes: said so, so that it
+    // stays in scalar registers and everything derived from it is uniform)
+    const int tid = threadIdx.x & 255, lid = LPW == 2 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8)) : 0;
     const int lane = tid & 63, wk = tid >> 6;
     // W_ih fragments of this workgroup's layer lid: [wave][FX chunks][NT][64 lanes]
     u32x4 *wxs = reinterpret_cast<u32x4 *>(smem) + (size_t)lid * 4 * FX * NT * 64;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
     // time step; dead rows and chunks read zeros), or layer l-1's h_t from
     // its exchange words.
     u32x4 xin[FX];
-    auto load_x = [&](int step) {
+    auto load_x = [&](int step) __attribute__((always_inline)) {
         const int st = step < T ? step : T - 1;
         const int tx = __builtin_amdgcn_readfirstlane(st);
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
     auto word_off = [&](int c0, int climit, int ci) -> unsigned {
         return nlive(c0, climit, ci) > 0 ? frag_off(c0 + ci) : 0x7FFFFFF0u;
     };
-    auto issue_words = [&](const uint32_t *src, int c0, int climit, u32x4 (&frag)[CB]) {
+    auto issue_words = [&](const uint32_t *src, int c0, int climit, u32x4 (&frag)[CB]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t xr = xcrsrc(src, (unsigned)(region * 4));
 #pragma unroll
         for (int ci = 0; ci < CB; ++ci) frag[ci] = xload2(xr, word_off(c0, climit, ci));
@@ -193,10 +195,11 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
         return rows == ROWS && c0 + CB <= climit && (c0 + CB) * DT::KC <= H;
     };
     const bool live_x = l > 0 && all_live(cx0, kch), live_h = all_live(wk * CB, kch);
-    auto wait_words = [&](const uint32_t *src, int c0, int climit, unsigned tb, bool live, u32x4 (&frag)[CB]) -> bool {
+    auto wait_words = [&](const uint32_t *src, int c0, int climit, unsigned tb, bool live, u32x4 (&frag)[CB])
+        __attribute__((always_inline)) -> bool {
         const __amdgpu_buffer_rsrc_t xr = xcrsrc(src, (unsigned)(region * 4));
         const unsigned tpat = tb << xc_shift(XF);
-        auto settle = [&](int ci) {  // a dead word counts as current; its value meets zero W rows
+        auto settle = [&](int ci) __attribute__((always_inline)) {  // a dead word counts as current; its value meets zero W rows
             const int nl = nlive(c0, climit, ci);
             if (nl < 1) frag[ci].x = tpat;
             if (nl < 2) frag[ci].y = tpat;
@@ -253,6 +256,154 @@ __global__ __launch_bounds__(256 * LPW, LPW == 2 ? 1 : (NT <= 2 ? 2 : 1)) void k
     // at the bottom of the one before it (see below): the top of the step then
     // carries no wait for memory operations.
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+
+    if constexpr (LPW == 2) {
+        // Paired layers, three phases a slot, so that the two layers' critical
+        // sections (h wait, recurrent product, epilogue, publication) never
+        // compete for the matrix pipes: layer 0 runs its recurrent product in
+        // phase 0, its epilogue in phase 1 and its next step's input product in
+        // phase 2; layer 1 (kWaveLag steps behind, so that its input, layer 0's
+        // h_t, is at least a slot old) its input product in phase 0, its
+        // recurrent product in phase 1 and its epilogue in phase 2.  Each
+        // layer's h is then published a phase or two before the team reads it.
+        f32x4 acc[NT];
+        long long t_pub2 = 0;
+        // acc = x_s W_ih^T (x_s: layer 0's input, or layer 0's h_s for layer 1);
+        // the next step's input is requested behind it
+        auto input_task = [&](int st) __attribute__((always_inline)) -> bool {
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (l > 0) ok = wait_words(slot_words(l - 1, st), cx0, kch, 1u, live_x, xin);
+            if (ok) {
+                u32x4 wcur[NT], wnext[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) wcur[j] = wx(0, j);
+#pragma unroll
+                for (int cx = 0; cx < FX; ++cx) {
+                    if (cx < ncx) {
+                        if (cx + 1 < FX)
+#pragma unroll
+                            for (int j = 0; j < NT; ++j) wnext[j] = wx(cx + 1, j);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[j] = mma_chunk(DT{}, acc[j], xin[cx], wcur[j]);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) wcur[j] = wnext[j];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (l == 0) load_x(st + 1);
+            else if (st + 1 < T) issue_words(slot_words(l - 1, st + 1), cx0, kch, xin);
+            return ok;
+        };
+        // acc += h_{s-1} W_hh^T at raised priority; the four K quarters' sums to LDS
+        auto crit_task = [&](int st) __attribute__((always_inline)) -> bool {
+            __builtin_amdgcn_s_setprio(2);
+            bool ok = true;
+            u32x4 hf[CB];
+            if (st > 0) {
+                if (a.pace > 0)
+                    while (wall_clock64() - t_pub2 < a.pace) __builtin_amdgcn_s_sleep(1);
+                issue_words(slot_words(l, st - 1), wk * CB, kch, hf);
+                ok = wait_words(slot_words(l, st - 1), wk * CB, kch, tag_of(l, st - 1), live_h, hf);
+            } else if (a.h0) {
+                const S *hs = static_cast<const S *>(a.h0) + (size_t)l * B * H;
+#pragma unroll
+                for (int ci = 0; ci < CB; ++ci) {
+                    const int k = (wk * CB + ci) * DT::KC + ksub;
+                    hf[ci] = (row_ok && k < H) ? load_frag<DT>(hs + (size_t)(b0 + mrow) * H, k, H, a.vec != 0)
+                                               : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            if (ok && (st > 0 || a.h0))
+#pragma unroll
+                for (int ci = 0; ci < CB; ++ci)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[j] = mma_chunk(DT{}, acc[j], hf[ci], wreg[ci][j]);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    part[lid][(wk * ROWS + 4 * (lane >> 4) + v) * PSTR + j * 16 + (lane & 15)] = acc[j][v];
+            return ok;
+        };
+        // gates, cell update, h_t (warp-nn equation block), publication
+        auto epi_task = [&](int st) __attribute__((always_inline)) {
+            // every load of this wave has returned (its h wait drained them):
+            // said so that the stores below are never waited for with the
+            // next input
+            __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+            float hv = 0.f;
+            S hsv = (S)0;
+            if (cv) {
+                const f32x4 sum = lds_sum_f32x4<4>(&part[lid][cm * PSTR + 4 * cu], ROWS * PSTR);
+                const float ig = sigmoid_f(sum.x + bias[0]);
+                const float fg = sigmoid_f(sum.y + bias[1]);
+                const float gg = tanh_f(sum.z + bias[2]);
+                const float og = sigmoid_f(sum.w + bias[3]);
+                creg = fg * creg + ig * gg;
+                hv = og * tanh_f(creg);
+                hsv = DT::from_f(hv);
+            }
+            const bool publish = !last || st + 1 < T;
+            uint32_t *xo = slot_words(l, st);
+            const unsigned tb_out = tag_of(l, st);
+            const int jj = j0 + cu;
+            if constexpr (BF) {
+                const uint32_t mine_bits = (uint32_t)(uint16_t)hsv;
+                const uint32_t nb_bits = (uint32_t)__shfl_xor((int)mine_bits, 1);
+                if (publish && cv && (cu & 1) == 0) {
+                    const int ch = jj >> 5, g = (jj >> 3) & 3, e = (jj >> 1) & 3;
+                    const uint32_t hi = cu + 1 < units ? nb_bits : 0u;
+                    xcstore(xo + ((size_t)ch * 64 + 16 * g + cm) * 4 + e,
+                            xc_word_pair((uint16_t)mine_bits, (uint16_t)hi, tb_out));
+                }
+            } else if (publish && cv) {
+                const int ch = jj >> 4, g = (jj >> 2) & 3, e = jj & 3;
+                xcstore(xo + ((size_t)ch * 64 + 16 * g + cm) * 4 + e, xc_word_f32(__float_as_uint(hv), tb_out));
+            }
+            if (cv) {
+                if (last) static_cast<S *>(a.Y)[((size_t)st * B + b0 + cm) * H + jj] = hsv;
+                if (st == T - 1) {
+                    const size_t si = ((size_t)l * B + b0 + cm) * H + jj;
+                    if (a.hn) static_cast<S *>(a.hn)[si] = hsv;
+                    if (a.cn) a.cn[si] = creg;
+                }
+            }
+            t_pub2 = wall_clock64();
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        if (l == 0) input_task(0);  // layer 0's first input product, ahead of the first slot
+        const int nslots2 = T + kWaveLag;
+        for (int sg = 0; sg < nslots2; ++sg) {
+            const int st = sg - kWaveLag * l;
+            const bool act = st >= 0 && st < T;
+            bool ok = true;
+            // phase 0: layer 0 critical, layer 1 input
+            if (act) ok = l == 0 ? crit_task(st) : input_task(st);
+            if (!ok) s_bad = 1;
+            __syncthreads();
+            if (s_bad) return;  // a wait gave up: leave (every workgroup drains the same way)
+            // phase 1: layer 0 epilogue, layer 1 critical
+            if (act) {
+                if (l == 0) epi_task(st);
+                else ok = crit_task(st);
+            }
+            if (!ok) s_bad = 1;
+            __syncthreads();
+            if (s_bad) return;
+            // phase 2: layer 0 next input, layer 1 epilogue
+            if (l == 0) {
+                if (act && st + 1 < T) input_task(st + 1);
+            } else if (act) {
+                epi_task(st);
+            }
+            __syncthreads();  // the partial sums are reused in the next slot
+        }
+        return;
+    }
 
     // slots: one step of every layer (paired layers: layer l at step sg - l kWaveLag,
     // idle before its first and after its last step but at every barrier)
